@@ -1,0 +1,248 @@
+"""CPU oracle for MXFP8 quantization, scale rearrangement and block-scaled GEMM.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it; the library in
+``mxfp8_block_scaled_08_amd`` never does and shares no code with it.
+
+The arithmetic lives in ``oracle/mx_oracle.c`` (plain scalar C, double
+precision); this module only marshals numpy arrays into it.  The sources it
+follows are named in the header of that file: the MXFP8 RL paper "End-to-End
+MXFP8 Reinforcement Learning on Blackwell" (Figure 1, Table 6, Table 10) for
+what the path computes, and the OCP MX v1.0 shared-scale rule for the bytes.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB, build_oracle
+
+_lib = None
+
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i64 = ctypes.c_int64
+
+
+def lib():
+    """Load (building on first use if absent) the oracle's shared library."""
+    global _lib
+    if _lib is None:
+        path = LIB
+        if not os.path.exists(path):
+            path = build_oracle()
+        L = ctypes.CDLL(path)
+        L.oracle_bf16_to_double.restype = ctypes.c_double
+        L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        L.oracle_e4m3_decode.restype = ctypes.c_double
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+        L.oracle_scale_code.restype = ctypes.c_uint8
+        L.oracle_scale_code.argtypes = [ctypes.c_double]
+        L.oracle_e8m0_decode.restype = ctypes.c_double
+        L.oracle_e8m0_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_swizzled_bytes.restype = _i64
+        L.oracle_swizzled_bytes.argtypes = [_i64, _i64]
+        L.oracle_swizzle_offset.restype = _i64
+        L.oracle_swizzle_offset.argtypes = [_i64, _i64, _i64]
+        L.oracle_dequant.restype = ctypes.c_double
+        L.oracle_dequant.argtypes = [ctypes.c_uint8, ctypes.c_uint8]
+        L.oracle_e4m3_encode_array.argtypes = [_f64p, _i64, _u8p]
+        L.oracle_e4m3_decode_array.argtypes = [_u8p, _i64, _f64p]
+        L.oracle_scale_code_array.argtypes = [_f64p, _i64, _u8p]
+        L.oracle_quantize_rowwise.argtypes = [_u16p, _i64, _i64, _i64, _u8p, _i64, _u8p, _i64]
+        L.oracle_quantize_colwise.argtypes = [_u16p, _i64, _i64, _i64, _u8p, _i64, _u8p, _i64]
+        L.oracle_scale_swizzle.argtypes = [_u8p, _i64, _i64, _i64, _u8p]
+        L.oracle_scale_unswizzle.argtypes = [_u8p, _i64, _i64, _u8p, _i64]
+        L.oracle_dequantize_rowwise.argtypes = [_u8p, _i64, _i64, _i64, _u8p, _i64, _f64p]
+        L.oracle_gemm.argtypes = [_i64, _i64, _i64, _u8p, _i64, _u8p, _i64, _u8p, _i64, _u8p,
+                                  _i64, _f64p, _f64p]
+        L.oracle_gemm_sampled.argtypes = [_i64, _i64p, _i64p, _i64, _u8p, _i64, _u8p, _i64,
+                                          _u8p, _i64, _u8p, _i64, _f64p, _f64p]
+        L.oracle_grouped_gemm_sampled.argtypes = [_i64, _i64p, _i64p, _i64, _i64p, _i64, _i64,
+                                                  _u8p, _i64, _u8p, _i64, _u8p, _i64, _u8p,
+                                                  _i64, _f64p, _f64p]
+        _lib = L
+    return _lib
+
+
+def _p(a, typ):
+    return a.ctypes.data_as(typ)
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+# ---- scalars -------------------------------------------------------------
+
+def bf16_to_double(bits: int) -> float:
+    return lib().oracle_bf16_to_double(bits)
+
+
+def e4m3_decode(code: int) -> float:
+    return lib().oracle_e4m3_decode(code)
+
+
+def e4m3_encode(t: float) -> int:
+    return lib().oracle_e4m3_encode(t)
+
+
+def scale_code(amax: float) -> int:
+    return lib().oracle_scale_code(amax)
+
+
+def e8m0_decode(code: int) -> float:
+    return lib().oracle_e8m0_decode(code)
+
+
+def dequant(q: int, c: int) -> float:
+    return lib().oracle_dequant(q, c)
+
+
+# ---- arrays ----------------------------------------------------------------
+
+def e4m3_encode_array(t) -> np.ndarray:
+    t = _c(t, np.float64)
+    out = np.empty(t.shape, np.uint8)
+    lib().oracle_e4m3_encode_array(_p(t, _f64p), t.size, _p(out, _u8p))
+    return out
+
+
+def e4m3_decode_array(q) -> np.ndarray:
+    q = _c(q, np.uint8)
+    out = np.empty(q.shape, np.float64)
+    lib().oracle_e4m3_decode_array(_p(q, _u8p), q.size, _p(out, _f64p))
+    return out
+
+
+def scale_code_array(amax) -> np.ndarray:
+    a = _c(amax, np.float64)
+    out = np.empty(a.shape, np.uint8)
+    lib().oracle_scale_code_array(_p(a, _f64p), a.size, _p(out, _u8p))
+    return out
+
+
+def quantize_rowwise(x_bits):
+    """x_bits: uint16 [rows, cols] of BF16 bit patterns -> (q [rows, cols], s [rows, cols/32])."""
+    x = _c(x_bits, np.uint16)
+    rows, cols = x.shape
+    assert cols % 32 == 0
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((rows, cols // 32), np.uint8)
+    lib().oracle_quantize_rowwise(_p(x, _u16p), rows, cols, cols, _p(q, _u8p), cols,
+                                  _p(s, _u8p), cols // 32)
+    return q, s
+
+
+def quantize_colwise(x_bits):
+    """x_bits: uint16 [rows, cols] -> (qt [cols, rows], st [cols, rows/32])."""
+    x = _c(x_bits, np.uint16)
+    rows, cols = x.shape
+    assert rows % 32 == 0
+    qt = np.empty((cols, rows), np.uint8)
+    st = np.empty((cols, rows // 32), np.uint8)
+    lib().oracle_quantize_colwise(_p(x, _u16p), rows, cols, cols, _p(qt, _u8p), rows,
+                                  _p(st, _u8p), rows // 32)
+    return qt, st
+
+
+def swizzled_bytes(rows: int, kblocks: int) -> int:
+    return lib().oracle_swizzled_bytes(rows, kblocks)
+
+
+def swizzle_offset(row: int, blk: int, kblocks: int) -> int:
+    return lib().oracle_swizzle_offset(row, blk, kblocks)
+
+
+def scale_swizzle(s) -> np.ndarray:
+    s = _c(s, np.uint8)
+    rows, kb = s.shape
+    out = np.empty(swizzled_bytes(rows, kb), np.uint8)
+    lib().oracle_scale_swizzle(_p(s, _u8p), rows, kb, kb, _p(out, _u8p))
+    return out
+
+
+def scale_unswizzle(buf, rows: int, kblocks: int) -> np.ndarray:
+    buf = _c(buf, np.uint8)
+    assert buf.size >= swizzled_bytes(rows, kblocks)
+    s = np.empty((rows, kblocks), np.uint8)
+    lib().oracle_scale_unswizzle(_p(buf, _u8p), rows, kblocks, _p(s, _u8p), kblocks)
+    return s
+
+
+def dequantize_rowwise(q, s) -> np.ndarray:
+    q = _c(q, np.uint8)
+    s = _c(s, np.uint8)
+    rows, cols = q.shape
+    out = np.empty((rows, cols), np.float64)
+    lib().oracle_dequantize_rowwise(_p(q, _u8p), rows, cols, cols, _p(s, _u8p), s.shape[1],
+                                    _p(out, _f64p))
+    return out
+
+
+def gemm(qa, sa, qb, sb):
+    """C = deq(A) deq(B)^T and Bnd = |deq(A)| |deq(B)|^T, both float64 [M, N].
+
+    qa [M, K], sa [M, K/32], qb [N, K], sb [N, K/32], plain (unrearranged) scales."""
+    qa, sa, qb, sb = (_c(a, np.uint8) for a in (qa, sa, qb, sb))
+    M, K = qa.shape
+    N = qb.shape[0]
+    assert qb.shape[1] == K and sa.shape == (M, K // 32) and sb.shape == (N, K // 32)
+    c = np.empty((M, N), np.float64)
+    bnd = np.empty((M, N), np.float64)
+    lib().oracle_gemm(M, N, K, _p(qa, _u8p), K, _p(sa, _u8p), K // 32, _p(qb, _u8p), K,
+                      _p(sb, _u8p), K // 32, _p(c, _f64p), _p(bnd, _f64p))
+    return c, bnd
+
+
+def gemm_sampled(rows, cols, qa, sa, qb, sb):
+    """Entries (rows[e], cols[e]) of deq(A) deq(B)^T, with their bounds."""
+    qa, sa, qb, sb = (_c(a, np.uint8) for a in (qa, sa, qb, sb))
+    rows = _c(rows, np.int64)
+    cols = _c(cols, np.int64)
+    K = qa.shape[1]
+    assert rows.shape == cols.shape
+    assert rows.size == 0 or (rows.min() >= 0 and rows.max() < qa.shape[0])
+    assert cols.size == 0 or (cols.min() >= 0 and cols.max() < qb.shape[0])
+    c = np.empty(rows.size, np.float64)
+    bnd = np.empty(rows.size, np.float64)
+    lib().oracle_gemm_sampled(rows.size, _p(rows, _i64p), _p(cols, _i64p), K, _p(qa, _u8p), K,
+                              _p(sa, _u8p), K // 32, _p(qb, _u8p), K, _p(sb, _u8p), K // 32,
+                              _p(c, _f64p), _p(bnd, _f64p))
+    return c, bnd
+
+
+def grouped_gemm_sampled(rows, cols, offsets, qa, sa, qb, sb):
+    """Per-expert product: row i in [offsets[g], offsets[g+1]) uses expert g.
+
+    qa [M_total, K], sa [M_total, K/32], qb [G, N, K], sb [G, N, K/32]."""
+    qa, sa, qb, sb = (_c(a, np.uint8) for a in (qa, sa, qb, sb))
+    rows = _c(rows, np.int64)
+    cols = _c(cols, np.int64)
+    offsets = _c(offsets, np.int64)
+    G, N, K = qb.shape
+    assert offsets.size == G + 1 and offsets[0] == 0 and offsets[-1] == qa.shape[0]
+    assert rows.size == 0 or (rows.min() >= 0 and rows.max() < qa.shape[0])
+    assert cols.size == 0 or (cols.min() >= 0 and cols.max() < N)
+    c = np.empty(rows.size, np.float64)
+    bnd = np.empty(rows.size, np.float64)
+    lib().oracle_grouped_gemm_sampled(rows.size, _p(rows, _i64p), _p(cols, _i64p), G,
+                                      _p(offsets, _i64p), N, K, _p(qa, _u8p), K, _p(sa, _u8p),
+                                      K // 32, _p(qb, _u8p), K, _p(sb, _u8p), K // 32,
+                                      _p(c, _f64p), _p(bnd, _f64p))
+    return c, bnd
+
+
+def grouped_gemm(offsets, qa, sa, qb, sb):
+    """Full per-expert product (small sizes): float64 [M_total, N] and its bound."""
+    G, N, K = np.asarray(qb).shape
+    M = np.asarray(qa).shape[0]
+    rows = np.repeat(np.arange(M, dtype=np.int64), N)
+    cols = np.tile(np.arange(N, dtype=np.int64), M)
+    c, bnd = grouped_gemm_sampled(rows, cols, offsets, qa, sa, qb, sb)
+    return c.reshape(M, N), bnd.reshape(M, N)
