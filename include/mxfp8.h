@@ -1,0 +1,197 @@
+/*
+ * mxfp8.h -- C ABI of the MI355X (gfx950) MXFP8 hot-path library, libmxfp8.so.
+ *
+ * The library implements the data-parallel hot path of an MXFP8 learner and
+ * sampler as described in "End-to-End MXFP8 Reinforcement Learning on
+ * Blackwell" (Figure 1: MXFP8 GEMMs over BF16 master weights, weights
+ * quantized with the learner's own quantizer at every synchronization;
+ * Table 6: the GEMM, "MXFP8 quantization" and "scale rearrangement" kernel
+ * categories; Table 10 rows F3/F4/F6: derived scale layouts and expert
+ * layouts that must be rebuilt from the current weights, scales that are
+ * E8M0 exponents only):
+ *
+ *   mx_quantize_rowwise   BF16 -> E4M3 + E8M0, 32-element blocks along rows
+ *   mx_quantize_colwise   BF16 -> E4M3 + E8M0, 32-element blocks down columns
+ *   mx_scale_swizzle      E8M0 [rows][kblocks] -> the GEMM's scale layout
+ *   mx_gemm               C = deq(A) . deq(B)^T, FP32 accumulation
+ *   mx_grouped_gemm       the same per MoE expert over row groups
+ *
+ * Number format (OCP Microscaling Formats (MX) v1.0, MXFP8 E4M3):
+ *   element  E4M3 ("E4M3FN"): bias 7, largest finite 448 (0x7E), NaN 0x7F/0xFF,
+ *            subnormals m * 2^-9, no infinities.
+ *   scale    E8M0: code c in 0..254 means 2^(c-127); 0xFF is NaN.
+ *   block    32 consecutive elements along the quantized dimension.
+ *   rule     amax = max |v| over the block; c = floor(log2(amax)) - 8 + 127
+ *            clamped to [0, 254] (8 = largest E4M3 exponent); every element
+ *            is v / 2^(c-127) rounded to nearest, ties to even, magnitudes
+ *            above 448 clamped to 448, E4M3 subnormals kept, a negative value
+ *            that rounds to zero stays -0 (0x80).
+ *   special  an all-zero block gets c = 0x00; a block holding NaN or Inf gets
+ *            c = 0xFF and every element 0x7F.
+ *   Results are deterministic: the same input gives the same bytes, on every
+ *   call (the condition that synchronized weights equal the learner's forward
+ *   weights byte for byte, paper abstract and Table 11 "byte comparison").
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless stated; the caller owns all
+ *     buffers (allocated e.g. with torch).  The library allocates nothing,
+ *     keeps no pointer after returning and holds no derived state, so no
+ *     cached layout can go stale.
+ *   - Work is enqueued on `stream` (a hipStream_t cast to void*; NULL is the
+ *     null stream).  No call synchronizes the host or reads device memory
+ *     from the host; calls are capturable in a HIP graph.
+ *   - Every argument is validated before anything is launched: on error no
+ *     output byte is written and a status other than MX_OK is returned;
+ *     mx_last_error() then gives a message naming the argument.  Launch
+ *     failures return MX_ERR_HIP.  Faults inside kernels surface at the
+ *     caller's next synchronization (HIP semantics).
+ *   - Element counts and leading dimensions are in elements of the buffer's
+ *     own type (BF16 = 2 bytes, E4M3/E8M0 = 1 byte, FP32 = 4 bytes).
+ *   - Zero-sized problems (rows == 0, cols == 0, M == 0 or N == 0) return
+ *     MX_OK and launch nothing.
+ *   - Calls on different streams may run concurrently; the library has no
+ *     shared mutable state apart from the thread-local error message.
+ */
+#ifndef MXFP8_H
+#define MXFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXFP8_ABI_VERSION 1
+
+typedef enum mx_status {
+    MX_OK = 0,
+    MX_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad enum, ld too small  */
+    MX_ERR_SHAPE = 2,       /* a dimension breaks the 32-element block structure    */
+    MX_ERR_ALIGN = 3,       /* a pointer or leading dimension breaks 16-byte rows   */
+    MX_ERR_OVERLAP = 4,     /* an output overlaps an input or another output        */
+    MX_ERR_UNSUPPORTED = 5, /* valid MX shape this build has no kernel for          */
+    MX_ERR_HIP = 6          /* the HIP runtime refused a launch                     */
+} mx_status;
+
+typedef enum mx_dtype {
+    MX_BF16 = 0, /* output rounded to nearest even from the FP32 accumulator */
+    MX_F32 = 1
+} mx_dtype;
+
+/* Version of this header's ABI (MXFP8_ABI_VERSION). */
+int mx_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char *mx_status_string(int status);
+
+/* Thread-local message describing the last non-MX_OK status returned on the
+ * calling thread ("" if none).  Valid until the next call on that thread. */
+const char *mx_last_error(void);
+
+/*
+ * Row-wise quantization (one 1x32 block per 32 consecutive elements of a row):
+ *   x  BF16  [rows][ld_x]  input, row-major, cols used per row
+ *   q  E4M3  [rows][ld_q]  output element codes
+ *   s  E8M0  [rows][ld_s]  output scale codes, cols/32 used per row
+ * Requirements: cols % 32 == 0 (else MX_ERR_SHAPE); ld_x >= cols, ld_q >= cols,
+ * ld_s >= cols/32; x and q 16-byte aligned with ld_x % 8 == 0 and
+ * ld_q % 16 == 0 (else MX_ERR_ALIGN); q and s must not overlap x or each other.
+ * This is the operand of a forward GEMM (K along the rows).
+ */
+mx_status mx_quantize_rowwise(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                              void *q, int64_t ld_q, void *s, int64_t ld_s, void *stream);
+
+/*
+ * Column-wise quantization (one 32x1 block per 32 consecutive elements of a
+ * column), written TRANSPOSED so that every GEMM operand is K-contiguous:
+ *   x   BF16  [rows][ld_x]   input, row-major
+ *   qt  E4M3  [cols][ld_qt]  output: qt[j][i] encodes x[i][j]
+ *   st  E8M0  [cols][ld_st]  output: st[j][b] is the scale of x[32b..32b+31][j]
+ * Equivalent to mx_quantize_rowwise of x^T.  Requirements: rows % 32 == 0 and
+ * cols % 8 == 0 (else MX_ERR_SHAPE); ld_x >= cols, ld_qt >= rows,
+ * ld_st >= rows/32; x and qt 16-byte aligned with ld_x % 8 == 0 and
+ * ld_qt % 16 == 0 (else MX_ERR_ALIGN); no overlap.  These are the operands of
+ * the backward GEMMs (dgrad's weight, wgrad's activations and gradients).
+ */
+mx_status mx_quantize_colwise(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                              void *qt, int64_t ld_qt, void *st, int64_t ld_st, void *stream);
+
+/*
+ * Size in bytes of the rearranged scale buffer for a [rows][kblocks] scale
+ * tensor: ceil(rows/32) * ceil(kblocks/8) * 256.  Host-only, no device work.
+ * Returns 0 for rows <= 0 or kblocks <= 0.
+ */
+int64_t mx_scale_swizzled_bytes(int64_t rows, int64_t kblocks);
+
+/*
+ * Scale rearrangement ("scale rearrangement" in the paper's Table 6; the
+ * derived scale copy of Table 10 row F3).  Layout of s_swz, defined by this
+ * library and read directly by the GEMM's matrix-core lanes:
+ *   tiles of 32 rows x 8 k-blocks = 256 bytes; with KT = ceil(kblocks/8),
+ *   tile (rt, kt) starts at byte (rt*KT + kt) * 256; inside it the scale of
+ *   (row 32*rt + r, block 8*kt + 2*t + h), r in 0..31, t in 0..3, h in 0..1,
+ *   is byte (32*h + r)*4 + t.  So the 4-byte word w of a tile holds, for
+ *   row r = w % 32, the scales of blocks 8kt+h, 8kt+2+h, 8kt+4+h, 8kt+6+h
+ *   with h = w / 32: one word per matrix-core lane per 256 K.
+ *   Every byte not covered by a scale is 0x7F (scale 1.0).
+ *   s      E8M0 [rows][ld_s], kblocks used per row (ld_s >= kblocks)
+ *   s_swz  mx_scale_swizzled_bytes(rows, kblocks) bytes, 4-byte aligned;
+ *          every byte is written.
+ * The rearranged copy is a pure function of s: it must be rebuilt whenever
+ * s changes (a stale copy silently corrupts every product that uses it).
+ */
+mx_status mx_scale_swizzle(const void *s, int64_t rows, int64_t kblocks, int64_t ld_s,
+                           void *s_swz, void *stream);
+
+/*
+ * Dense block-scaled GEMM ("MXFP8 GEMMs" of the learner, paper Figure 1 and
+ * Table 6):
+ *   C[i][j] = sum_k deq(A)[i][k] * deq(B)[j][k],   i < M, j < N, k < K
+ * with deq(q)[i][k] = E4M3(q[i][k]) * 2^(s[i][k/32] - 127), accumulated in
+ * FP32 and written as BF16 (round to nearest even) or FP32.
+ *   a_q      E4M3 [M][ld_a]   row-wise quantized A (K contiguous)
+ *   a_s_swz  rearranged scales of A: mx_scale_swizzle of its [M][K/32] scales
+ *   b_q      E4M3 [N][ld_b]   B stored as [N][K] (K contiguous), e.g. a
+ *            weight [out][in] for a forward product, or column-wise
+ *            quantized operands for the backward products
+ *   b_s_swz  rearranged scales of B ([N][K/32] before rearrangement)
+ *   c        [M][ld_c] of c_dtype (MX_BF16 or MX_F32)
+ * Requirements: K % 32 == 0 (else MX_ERR_SHAPE) and K % 128 == 0 (else
+ * MX_ERR_UNSUPPORTED); M, N >= 0 arbitrary; a_q, b_q 16-byte aligned with
+ * ld_a % 16 == 0, ld_b % 16 == 0; scale buffers 4-byte aligned; c aligned to
+ * its element size (else MX_ERR_ALIGN); ld_a, ld_b >= K, ld_c >= N; c must
+ * not overlap an input.  No split-K: each output is one FP32 accumulation.
+ */
+mx_status mx_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t ld_a,
+                  const void *a_s_swz, const void *b_q, int64_t ld_b, const void *b_s_swz,
+                  void *c, int64_t ld_c, int c_dtype, void *stream);
+
+/*
+ * Grouped (per-expert) block-scaled GEMM for MoE layers (paper Table 2:
+ * Qwen3-30B-A3B, 128 experts, top-8; Table 10 row F4: the expert layout must
+ * follow the current weights).  Rows of A are sorted by expert:
+ *   for g < num_groups and group_offsets[g] <= i < group_offsets[g+1]:
+ *   C[i][j] = sum_k deq(A)[i][k] * deq(B_g)[j][k]
+ *   group_offsets  DEVICE int64 [num_groups + 1], nondecreasing, [0] == 0,
+ *                  [num_groups] == M_total; empty groups are allowed
+ *   a_q      E4M3 [M_total][ld_a], a_s_swz: rearranged [M_total][K/32] scales
+ *            (one buffer over all rows; groups need not start on 32-row tiles)
+ *   b_q      E4M3 [num_groups][N][K] contiguous (expert g at g*N*K)
+ *   b_s_swz  num_groups rearranged [N][K/32] scale buffers back to back,
+ *            expert g at g * mx_scale_swizzled_bytes(N, K/32)
+ *   c        [M_total][ld_c] of c_dtype
+ * Same requirements as mx_gemm, plus num_groups >= 1.  The offsets live on
+ * the device and are not read by the host; offsets that break the stated
+ * properties give unspecified (but in-bounds) results.
+ */
+mx_status mx_grouped_gemm(int64_t num_groups, int64_t M_total, int64_t N, int64_t K,
+                          const int64_t *group_offsets, const void *a_q, int64_t ld_a,
+                          const void *a_s_swz, const void *b_q, const void *b_s_swz,
+                          void *c, int64_t ld_c, int c_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP8_H */

@@ -1,0 +1,249 @@
+"""MI355X (gfx950) MXFP8 hot path: quantize, scale rearrangement, block-scaled GEMM.
+
+A thin Python binding over the C ABI of ``libmxfp8.so`` (declared in
+``include/mxfp8.h``).  Every function here only marshals torch tensors into
+pointers, sizes and the current HIP stream; all computation runs in the
+library's HIP kernels.  If the shared library is missing, ``load()`` raises:
+there is no fallback path.
+
+The operations are those of the MXFP8 learner/sampler hot path in
+"End-to-End MXFP8 Reinforcement Learning on Blackwell" (Figure 1: quantize
+the weights with the learner's quantizer, MXFP8 GEMMs; Table 6: GEMM,
+quantization and scale-rearrangement kernels; Table 2: dense Qwen3-8B and
+the 128-expert Qwen3-30B-A3B MoE).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "MxError", "load", "lib_path", "mx_abi_version", "mx_status_string", "mx_last_error", "mx_quantize_rowwise",
+    "mx_quantize_colwise", "mx_scale_swizzled_bytes", "mx_scale_swizzle", "mx_gemm",
+    "mx_grouped_gemm", "MX_OK", "MX_ERR_INVALID_ARG", "MX_ERR_SHAPE", "MX_ERR_ALIGN",
+    "MX_ERR_OVERLAP", "MX_ERR_UNSUPPORTED", "MX_ERR_HIP", "MX_BF16", "MX_F32",
+]
+
+MX_OK, MX_ERR_INVALID_ARG, MX_ERR_SHAPE, MX_ERR_ALIGN = 0, 1, 2, 3
+MX_ERR_OVERLAP, MX_ERR_UNSUPPORTED, MX_ERR_HIP = 4, 5, 6
+MX_BF16, MX_F32 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmxfp8.so")
+_lib: Optional[ctypes.CDLL] = None
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+
+class MxError(RuntimeError):
+    """A non-MX_OK status from the library, with its message."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        self.status = status
+        super().__init__(f"{fn} -> {_status_name(status)}: {msg}")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libmxfp8.so (built by ``__graft_entry__.build()``); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} not found: build it first (python -c 'import __graft_entry__ as g; "
+            "g.build()'); there is no CPU fallback")
+    L = ctypes.CDLL(_LIB_PATH)
+    L.mx_abi_version.restype = ctypes.c_int
+    L.mx_abi_version.argtypes = []
+    L.mx_status_string.restype = ctypes.c_char_p
+    L.mx_status_string.argtypes = [ctypes.c_int]
+    L.mx_last_error.restype = ctypes.c_char_p
+    L.mx_last_error.argtypes = []
+    L.mx_scale_swizzled_bytes.restype = _i64
+    L.mx_scale_swizzled_bytes.argtypes = [_i64, _i64]
+    for name in ("mx_quantize_rowwise", "mx_quantize_colwise"):
+        f = getattr(L, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp]
+    L.mx_scale_swizzle.restype = ctypes.c_int
+    L.mx_scale_swizzle.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp]
+    L.mx_gemm.restype = ctypes.c_int
+    L.mx_gemm.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
+                          ctypes.c_int, _vp]
+    L.mx_grouped_gemm.restype = ctypes.c_int
+    L.mx_grouped_gemm.argtypes = [_i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp,
+                                  _i64, ctypes.c_int, _vp]
+    _lib = L
+    return L
+
+
+def _status_name(st: int) -> str:
+    return load().mx_status_string(st).decode()
+
+
+def _check(fn: str, st: int) -> None:
+    if st != MX_OK:
+        raise MxError(fn, st, load().mx_last_error().decode())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _ld(t: torch.Tensor, name: str) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D row-major view")
+    return t.stride(0)
+
+
+_BYTE_VIEWS = tuple(getattr(torch, n) for n in ("float8_e4m3fn", "float8_e8m0fnu")
+                    if hasattr(torch, n))
+
+
+def _u8(t: torch.Tensor) -> torch.Tensor:
+    # E4M3 and E8M0 buffers are bytes at the ABI; accept float8 views too
+    if t.dtype in _BYTE_VIEWS:
+        return t.view(torch.uint8)
+    return t
+
+
+# ---------------------------------------------------------------------------
+
+
+def mx_abi_version() -> int:
+    return load().mx_abi_version()
+
+
+def mx_status_string(status: int) -> str:
+    return load().mx_status_string(status).decode()
+
+
+def mx_last_error() -> str:
+    """Message of the last non-MX_OK status returned on this thread."""
+    return load().mx_last_error().decode()
+
+
+def mx_scale_swizzled_bytes(rows: int, kblocks: int) -> int:
+    return load().mx_scale_swizzled_bytes(rows, kblocks)
+
+
+def mx_quantize_rowwise(x: torch.Tensor, q: Optional[torch.Tensor] = None,
+                        s: Optional[torch.Tensor] = None,
+                        stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """BF16 x[rows][cols] -> (q uint8 [rows][cols] E4M3, s uint8 [rows][cols/32] E8M0)."""
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    q, s = _u8(q), _u8(s)
+    st = load().mx_quantize_rowwise(_dev(x, "x", torch.bfloat16), rows, cols, _ld(x, "x"),
+                                    _dev(q, "q", torch.uint8), _ld(q, "q"),
+                                    _dev(s, "s", torch.uint8), _ld(s, "s"), _stream(stream))
+    _check("mx_quantize_rowwise", st)
+    return q, s
+
+
+def mx_quantize_colwise(x: torch.Tensor, qt: Optional[torch.Tensor] = None,
+                        st_: Optional[torch.Tensor] = None,
+                        stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """BF16 x[rows][cols] -> (qt uint8 [cols][rows], st uint8 [cols][rows/32]), transposed."""
+    rows, cols = x.shape
+    if qt is None:
+        qt = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    if st_ is None:
+        st_ = torch.empty((cols, rows // 32), dtype=torch.uint8, device=x.device)
+    qt, st_ = _u8(qt), _u8(st_)
+    st = load().mx_quantize_colwise(_dev(x, "x", torch.bfloat16), rows, cols, _ld(x, "x"),
+                                    _dev(qt, "qt", torch.uint8), _ld(qt, "qt"),
+                                    _dev(st_, "st", torch.uint8), _ld(st_, "st"),
+                                    _stream(stream))
+    _check("mx_quantize_colwise", st)
+    return qt, st_
+
+
+def mx_scale_swizzle(s: torch.Tensor, out: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """E8M0 s[rows][kblocks] -> the GEMM's rearranged scale buffer (uint8, 1-D)."""
+    s = _u8(s)
+    rows, kb = s.shape
+    n = mx_scale_swizzled_bytes(rows, kb)
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=s.device)
+    if out.numel() < n:
+        raise ValueError(f"out holds {out.numel()} bytes, needs {n}")
+    st = load().mx_scale_swizzle(_dev(s, "s", torch.uint8), rows, kb, _ld(s, "s"),
+                                 _dev(out, "out", torch.uint8), _stream(stream))
+    _check("mx_scale_swizzle", st)
+    return out
+
+
+_OUT = {torch.bfloat16: MX_BF16, torch.float32: MX_F32}
+
+
+def mx_gemm(a_q: torch.Tensor, a_s_swz: torch.Tensor, b_q: torch.Tensor,
+            b_s_swz: torch.Tensor, c: Optional[torch.Tensor] = None,
+            out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+    """C[M][N] = deq(A)[M][K] . deq(B)[N][K]^T (both operands K-contiguous)."""
+    a_q, b_q = _u8(a_q), _u8(b_q)
+    M, K = a_q.shape
+    N = b_q.shape[0]
+    if b_q.shape[1] != K:
+        raise ValueError(f"K mismatch: A {tuple(a_q.shape)} B {tuple(b_q.shape)}")
+    if c is None:
+        c = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
+    if c.dtype not in _OUT:
+        raise ValueError("c must be bfloat16 or float32")
+    st = load().mx_gemm(M, N, K, _dev(a_q, "a_q", torch.uint8), _ld(a_q, "a_q"),
+                        _dev(a_s_swz, "a_s_swz", torch.uint8), _dev(b_q, "b_q", torch.uint8),
+                        _ld(b_q, "b_q"), _dev(b_s_swz, "b_s_swz", torch.uint8),
+                        _dev(c, "c"), _ld(c, "c"), _OUT[c.dtype], _stream(stream))
+    _check("mx_gemm", st)
+    return c
+
+
+def mx_grouped_gemm(group_offsets: torch.Tensor, a_q: torch.Tensor, a_s_swz: torch.Tensor,
+                    b_q: torch.Tensor, b_s_swz: torch.Tensor, c: Optional[torch.Tensor] = None,
+                    out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+    """Per-expert C: rows [off[g], off[g+1]) of A times B_g^T, B as [G][N][K]."""
+    a_q, b_q = _u8(a_q), _u8(b_q)
+    M, K = a_q.shape
+    G, N, Kb = b_q.shape
+    if Kb != K:
+        raise ValueError(f"K mismatch: A {tuple(a_q.shape)} B {tuple(b_q.shape)}")
+    if not b_q.is_contiguous():
+        raise ValueError("b_q must be contiguous [G][N][K]")
+    if group_offsets.dtype != torch.int64 or group_offsets.numel() != G + 1:
+        raise ValueError("group_offsets must be int64 with G+1 entries")
+    if c is None:
+        c = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
+    if c.dtype not in _OUT:
+        raise ValueError("c must be bfloat16 or float32")
+    st = load().mx_grouped_gemm(G, M, N, K, _dev(group_offsets, "group_offsets"),
+                                _dev(a_q, "a_q", torch.uint8), _ld(a_q, "a_q"),
+                                _dev(a_s_swz, "a_s_swz", torch.uint8),
+                                _dev(b_q, "b_q", torch.uint8),
+                                _dev(b_s_swz, "b_s_swz", torch.uint8), _dev(c, "c"),
+                                _ld(c, "c"), _OUT[c.dtype], _stream(stream))
+    _check("mx_grouped_gemm", st)
+    return c

@@ -1,0 +1,273 @@
+// C ABI of libmxfp8.so (declared in include/mxfp8.h): argument validation,
+// status reporting, and dispatch to the HIP launchers.
+//
+// Every entry point validates all of its arguments before it touches HIP, so
+// an invalid call writes nothing and returns a status naming the problem
+// (the paper "End-to-End MXFP8 Reinforcement Learning on Blackwell" found
+// five of its seven weight-sync failures silent, Table 10; errors here are
+// loud).  Nothing here allocates, synchronizes or reads device memory.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/mxfp8.h"
+#include "mx_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mx_status fail(mx_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+mx_status ok()
+{
+    g_err[0] = '\0';
+    return MX_OK;
+}
+
+mx_status hip_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(MX_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// [p, p + n) and [q, q + m) overlap (n, m in bytes, both > 0)
+bool overlap(const void *p, int64_t n, const void *q, int64_t m)
+{
+    const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+    return n > 0 && m > 0 && a < b + (uintptr_t)m && b < a + (uintptr_t)n;
+}
+
+// byte extent of a row-major [rows][ld] buffer whose rows use `used` elements
+int64_t extent(int64_t rows, int64_t used, int64_t ld, int64_t elem)
+{
+    if (rows <= 0 || used <= 0)
+        return 0;
+    return ((rows - 1) * ld + used) * elem;
+}
+
+int64_t swz_bytes(int64_t rows, int64_t kb)
+{
+    if (rows <= 0 || kb <= 0)
+        return 0;
+    return ((rows + 31) / 32) * ((kb + 7) / 8) * 256;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mx_abi_version(void) { return MXFP8_ABI_VERSION; }
+
+const char *mx_status_string(int status)
+{
+    switch (status) {
+    case MX_OK: return "MX_OK";
+    case MX_ERR_INVALID_ARG: return "MX_ERR_INVALID_ARG";
+    case MX_ERR_SHAPE: return "MX_ERR_SHAPE";
+    case MX_ERR_ALIGN: return "MX_ERR_ALIGN";
+    case MX_ERR_OVERLAP: return "MX_ERR_OVERLAP";
+    case MX_ERR_UNSUPPORTED: return "MX_ERR_UNSUPPORTED";
+    case MX_ERR_HIP: return "MX_ERR_HIP";
+    default: return "MX_ERR_UNKNOWN";
+    }
+}
+
+const char *mx_last_error(void) { return g_err; }
+
+int64_t mx_scale_swizzled_bytes(int64_t rows, int64_t kblocks) { return swz_bytes(rows, kblocks); }
+
+mx_status mx_quantize_rowwise(const void *x, int64_t rows, int64_t cols, int64_t ld_x, void *q,
+                              int64_t ld_q, void *s, int64_t ld_s, void *stream)
+{
+    const char *fn = "mx_quantize_rowwise";
+    if (rows < 0 || cols < 0)
+        return fail(MX_ERR_INVALID_ARG, "%s: negative size rows=%lld cols=%lld", fn,
+                    (long long)rows, (long long)cols);
+    if (cols % 32 != 0)
+        return fail(MX_ERR_SHAPE, "%s: cols=%lld is not a multiple of the 32-element block", fn,
+                    (long long)cols);
+    if (ld_x < cols || ld_q < cols || ld_s < cols / 32)
+        return fail(MX_ERR_INVALID_ARG,
+                    "%s: leading dimension too small (ld_x=%lld ld_q=%lld ld_s=%lld, cols=%lld)",
+                    fn, (long long)ld_x, (long long)ld_q, (long long)ld_s, (long long)cols);
+    if (rows == 0 || cols == 0)
+        return ok();
+    if (!x || !q || !s)
+        return fail(MX_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!aligned(x, 16) || !aligned(q, 16) || ld_x % 8 != 0 || ld_q % 16 != 0)
+        return fail(MX_ERR_ALIGN, "%s: x and q need 16-byte aligned rows (ld_x %% 8, ld_q %% 16)",
+                    fn);
+    const int64_t ex = extent(rows, cols, ld_x, 2), eq = extent(rows, cols, ld_q, 1),
+                  es = extent(rows, cols / 32, ld_s, 1);
+    if (overlap(x, ex, q, eq) || overlap(x, ex, s, es) || overlap(q, eq, s, es))
+        return fail(MX_ERR_OVERLAP, "%s: input and outputs overlap", fn);
+    return hip_status(mx::launch_quantize_rowwise(x, rows, cols, ld_x, q, ld_q, s, ld_s,
+                                                  (hipStream_t)stream),
+                      fn);
+}
+
+mx_status mx_quantize_colwise(const void *x, int64_t rows, int64_t cols, int64_t ld_x, void *qt,
+                              int64_t ld_qt, void *st, int64_t ld_st, void *stream)
+{
+    const char *fn = "mx_quantize_colwise";
+    if (rows < 0 || cols < 0)
+        return fail(MX_ERR_INVALID_ARG, "%s: negative size rows=%lld cols=%lld", fn,
+                    (long long)rows, (long long)cols);
+    if (rows % 32 != 0)
+        return fail(MX_ERR_SHAPE, "%s: rows=%lld is not a multiple of the 32-element block", fn,
+                    (long long)rows);
+    if (cols % 8 != 0)
+        return fail(MX_ERR_SHAPE, "%s: cols=%lld is not a multiple of 8", fn, (long long)cols);
+    if (ld_x < cols || ld_qt < rows || ld_st < rows / 32)
+        return fail(MX_ERR_INVALID_ARG,
+                    "%s: leading dimension too small (ld_x=%lld ld_qt=%lld ld_st=%lld)", fn,
+                    (long long)ld_x, (long long)ld_qt, (long long)ld_st);
+    if (rows == 0 || cols == 0)
+        return ok();
+    if (!x || !qt || !st)
+        return fail(MX_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!aligned(x, 16) || !aligned(qt, 16) || ld_x % 8 != 0 || ld_qt % 16 != 0)
+        return fail(MX_ERR_ALIGN,
+                    "%s: x and qt need 16-byte aligned rows (ld_x %% 8, ld_qt %% 16)", fn);
+    const int64_t ex = extent(rows, cols, ld_x, 2), eq = extent(cols, rows, ld_qt, 1),
+                  es = extent(cols, rows / 32, ld_st, 1);
+    if (overlap(x, ex, qt, eq) || overlap(x, ex, st, es) || overlap(qt, eq, st, es))
+        return fail(MX_ERR_OVERLAP, "%s: input and outputs overlap", fn);
+    return hip_status(mx::launch_quantize_colwise(x, rows, cols, ld_x, qt, ld_qt, st, ld_st,
+                                                  (hipStream_t)stream),
+                      fn);
+}
+
+mx_status mx_scale_swizzle(const void *s, int64_t rows, int64_t kblocks, int64_t ld_s,
+                           void *s_swz, void *stream)
+{
+    const char *fn = "mx_scale_swizzle";
+    if (rows < 0 || kblocks < 0)
+        return fail(MX_ERR_INVALID_ARG, "%s: negative size", fn);
+    if (ld_s < kblocks)
+        return fail(MX_ERR_INVALID_ARG, "%s: ld_s=%lld < kblocks=%lld", fn, (long long)ld_s,
+                    (long long)kblocks);
+    if (rows == 0 || kblocks == 0)
+        return ok();
+    if (!s || !s_swz)
+        return fail(MX_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!aligned(s_swz, 4))
+        return fail(MX_ERR_ALIGN, "%s: s_swz must be 4-byte aligned", fn);
+    if (overlap(s, extent(rows, kblocks, ld_s, 1), s_swz, swz_bytes(rows, kblocks)))
+        return fail(MX_ERR_OVERLAP, "%s: input and output overlap", fn);
+    return hip_status(mx::launch_scale_swizzle(s, rows, kblocks, ld_s, s_swz, (hipStream_t)stream),
+                      fn);
+}
+
+static mx_status check_gemm_common(const char *fn, int64_t M, int64_t N, int64_t K,
+                                   const void *a_q, int64_t ld_a, const void *a_s,
+                                   const void *b_q, int64_t ld_b, const void *b_s, void *c,
+                                   int64_t ld_c, int c_dtype)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return fail(MX_ERR_INVALID_ARG, "%s: negative size M=%lld N=%lld K=%lld", fn,
+                    (long long)M, (long long)N, (long long)K);
+    if (c_dtype != MX_BF16 && c_dtype != MX_F32)
+        return fail(MX_ERR_INVALID_ARG, "%s: c_dtype=%d is neither MX_BF16 nor MX_F32", fn,
+                    c_dtype);
+    if (K % 32 != 0 || K == 0)
+        return fail(MX_ERR_SHAPE, "%s: K=%lld must be a positive multiple of 32", fn,
+                    (long long)K);
+    if (K % 128 != 0)
+        return fail(MX_ERR_UNSUPPORTED, "%s: K=%lld: this build needs K %% 128 == 0", fn,
+                    (long long)K);
+    if (ld_a < K || ld_b < K || ld_c < N)
+        return fail(MX_ERR_INVALID_ARG,
+                    "%s: leading dimension too small (ld_a=%lld ld_b=%lld ld_c=%lld)", fn,
+                    (long long)ld_a, (long long)ld_b, (long long)ld_c);
+    if (M == 0 || N == 0)
+        return MX_OK;
+    if (!a_q || !a_s || !b_q || !b_s || !c)
+        return fail(MX_ERR_INVALID_ARG, "%s: null pointer", fn);
+    const uintptr_t ce = c_dtype == MX_BF16 ? 2 : 4;
+    if (!aligned(a_q, 16) || !aligned(b_q, 16) || ld_a % 16 != 0 || ld_b % 16 != 0 ||
+        !aligned(a_s, 4) || !aligned(b_s, 4) || !aligned(c, ce))
+        return fail(MX_ERR_ALIGN,
+                    "%s: operands need 16-byte aligned rows, scales 4-byte alignment, C its "
+                    "element size",
+                    fn);
+    // Row offsets inside a 256-row tile and offsets into a rearranged scale
+    // buffer are formed in 32 bits.
+    if ((int64_t)256 * ld_a >= ((int64_t)1 << 31) || (int64_t)256 * ld_b >= ((int64_t)1 << 31))
+        return fail(MX_ERR_UNSUPPORTED, "%s: leading dimension too large for this build", fn);
+    if (swz_bytes(M, K / 32) >= ((int64_t)1 << 32) || swz_bytes(N, K / 32) >= ((int64_t)1 << 32))
+        return fail(MX_ERR_UNSUPPORTED, "%s: operand too large for this build", fn);
+    return MX_OK;
+}
+
+mx_status mx_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t ld_a,
+                  const void *a_s_swz, const void *b_q, int64_t ld_b, const void *b_s_swz,
+                  void *c, int64_t ld_c, int c_dtype, void *stream)
+{
+    const char *fn = "mx_gemm";
+    mx_status st =
+        check_gemm_common(fn, M, N, K, a_q, ld_a, a_s_swz, b_q, ld_b, b_s_swz, c, ld_c, c_dtype);
+    if (st != MX_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return ok();
+    const int64_t ce = c_dtype == MX_BF16 ? 2 : 4;
+    const int64_t ec = extent(M, N, ld_c, ce);
+    if (overlap(c, ec, a_q, extent(M, K, ld_a, 1)) || overlap(c, ec, b_q, extent(N, K, ld_b, 1)) ||
+        overlap(c, ec, a_s_swz, swz_bytes(M, K / 32)) ||
+        overlap(c, ec, b_s_swz, swz_bytes(N, K / 32)))
+        return fail(MX_ERR_OVERLAP, "%s: C overlaps an input", fn);
+    return hip_status(mx::launch_gemm(M, N, K, a_q, ld_a, a_s_swz, b_q, ld_b, b_s_swz, c, ld_c,
+                                      c_dtype, (hipStream_t)stream),
+                      fn);
+}
+
+mx_status mx_grouped_gemm(int64_t num_groups, int64_t M_total, int64_t N, int64_t K,
+                          const int64_t *group_offsets, const void *a_q, int64_t ld_a,
+                          const void *a_s_swz, const void *b_q, const void *b_s_swz, void *c,
+                          int64_t ld_c, int c_dtype, void *stream)
+{
+    const char *fn = "mx_grouped_gemm";
+    if (num_groups < 1)
+        return fail(MX_ERR_INVALID_ARG, "%s: num_groups=%lld < 1", fn, (long long)num_groups);
+    if (num_groups > (1 << 20))
+        return fail(MX_ERR_UNSUPPORTED, "%s: num_groups=%lld too large", fn,
+                    (long long)num_groups);
+    mx_status st = check_gemm_common(fn, M_total, N, K, a_q, ld_a, a_s_swz, b_q, K, b_s_swz, c,
+                                     ld_c, c_dtype);
+    if (st != MX_OK)
+        return st;
+    if (M_total == 0 || N == 0)
+        return ok();
+    if (!group_offsets)
+        return fail(MX_ERR_INVALID_ARG, "%s: null group_offsets", fn);
+    if (!aligned(group_offsets, 8))
+        return fail(MX_ERR_ALIGN, "%s: group_offsets must be 8-byte aligned", fn);
+    const int64_t ce = c_dtype == MX_BF16 ? 2 : 4;
+    const int64_t ec = extent(M_total, N, ld_c, ce);
+    const int64_t eb = num_groups * N * K;
+    const int64_t ebs = num_groups * swz_bytes(N, K / 32);
+    if (overlap(c, ec, a_q, extent(M_total, K, ld_a, 1)) || overlap(c, ec, b_q, eb) ||
+        overlap(c, ec, a_s_swz, swz_bytes(M_total, K / 32)) || overlap(c, ec, b_s_swz, ebs) ||
+        overlap(c, ec, group_offsets, (num_groups + 1) * 8))
+        return fail(MX_ERR_OVERLAP, "%s: C overlaps an input", fn);
+    return hip_status(mx::launch_grouped_gemm(num_groups, M_total, N, K, group_offsets, a_q, ld_a,
+                                              a_s_swz, b_q, b_s_swz, c, ld_c, c_dtype,
+                                              (hipStream_t)stream),
+                      fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,154 @@
+"""CPU checks of the C ABI: the library loads without a GPU, exports every
+declared entry point, and rejects invalid arguments before touching HIP.
+
+No call here reaches a kernel: every call is either a host-only query or an
+argument error (fake non-null pointers are never dereferenced, because
+validation returns first).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp8_block_scaled_08_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp8.h")
+
+FAKE = 0x10000  # 64 KiB-aligned fake device address; never dereferenced
+FAKE2 = 0x40000000
+FAKE3 = 0x80000000
+FAKE4 = 0xC0000000
+STREAM = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mx_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = mx.load()
+    names = declared_functions()
+    assert {"mx_quantize_rowwise", "mx_quantize_colwise", "mx_scale_swizzle", "mx_gemm",
+            "mx_grouped_gemm", "mx_scale_swizzled_bytes"} <= set(names)
+    raw = ctypes.CDLL(mx.lib_path())
+    for n in names:
+        assert hasattr(raw, n), f"{n} declared in include/mxfp8.h but not exported"
+        assert hasattr(mx, n), f"{n} has no Python binding of the same name"
+    assert L.mx_abi_version() == 1
+
+
+def test_status_strings():
+    L = mx.load()
+    for code, name in [(0, "MX_OK"), (1, "MX_ERR_INVALID_ARG"), (2, "MX_ERR_SHAPE"),
+                       (3, "MX_ERR_ALIGN"), (4, "MX_ERR_OVERLAP"), (5, "MX_ERR_UNSUPPORTED"),
+                       (6, "MX_ERR_HIP")]:
+        assert L.mx_status_string(code).decode() == name
+    assert L.mx_status_string(99).decode() == "MX_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("rows,kb", [(0, 8), (1, 1), (32, 8), (33, 9), (4096, 128), (163840, 64),
+                                     (12288, 768)])
+def test_swizzled_bytes(rows, kb):
+    expect = 0 if rows == 0 else ((rows + 31) // 32) * ((kb + 7) // 8) * 256
+    assert mx.mx_scale_swizzled_bytes(rows, kb) == expect
+
+
+def _err(L):
+    return L.mx_last_error().decode()
+
+
+def test_quantize_rowwise_validation():
+    L = mx.load()
+    f = L.mx_quantize_rowwise
+    assert f(FAKE, 4, 48, 48, FAKE2, 48, FAKE3, 2, STREAM) == mx.MX_ERR_SHAPE
+    assert "cols=48" in _err(L)
+    assert f(FAKE, -1, 64, 64, FAKE2, 64, FAKE3, 2, STREAM) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE, 4, 64, 32, FAKE2, 64, FAKE3, 2, STREAM) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE, 4, 64, 64, FAKE2, 64, FAKE3, 1, STREAM) == mx.MX_ERR_INVALID_ARG
+    assert f(0, 4, 64, 64, FAKE2, 64, FAKE3, 2, STREAM) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE + 2, 4, 64, 64, FAKE2, 64, FAKE3, 2, STREAM) == mx.MX_ERR_ALIGN
+    assert f(FAKE, 4, 64, 68, FAKE2, 64, FAKE3, 2, STREAM) == mx.MX_ERR_ALIGN
+    assert f(FAKE, 4, 64, 64, FAKE2, 72, FAKE3, 2, STREAM) == mx.MX_ERR_ALIGN
+    # q inside x
+    assert f(FAKE, 4, 64, 64, FAKE + 64, 64, FAKE3, 2, STREAM) == mx.MX_ERR_OVERLAP
+    # s inside q
+    assert f(FAKE, 4, 64, 64, FAKE2, 64, FAKE2 + 100, 2, STREAM) == mx.MX_ERR_OVERLAP
+    # empty problems are a no-op that succeeds (nothing launched)
+    assert f(FAKE, 0, 64, 64, FAKE2, 64, FAKE3, 2, STREAM) == mx.MX_OK
+    assert f(FAKE, 7, 0, 0, FAKE2, 0, FAKE3, 0, STREAM) == mx.MX_OK
+
+
+def test_quantize_colwise_validation():
+    L = mx.load()
+    f = L.mx_quantize_colwise
+    assert f(FAKE, 48, 64, 64, FAKE2, 48, FAKE3, 1, STREAM) == mx.MX_ERR_SHAPE
+    assert f(FAKE, 64, 60, 64, FAKE2, 64, FAKE3, 2, STREAM) == mx.MX_ERR_SHAPE
+    assert f(FAKE, 64, 64, 64, FAKE2, 32, FAKE3, 2, STREAM) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE, 64, 64, 64, FAKE2, 64, FAKE3, 1, STREAM) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE, 64, 64, 64, FAKE2 + 8, 64, FAKE3, 2, STREAM) == mx.MX_ERR_ALIGN
+    assert f(FAKE, 64, 64, 64, FAKE + 4096, 64, FAKE3, 2, STREAM) == mx.MX_ERR_OVERLAP
+    assert f(FAKE, 0, 64, 64, FAKE2, 0, FAKE3, 0, STREAM) == mx.MX_OK
+
+
+def test_swizzle_validation():
+    L = mx.load()
+    f = L.mx_scale_swizzle
+    assert f(FAKE, 64, 8, 4, FAKE2, STREAM) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE, 64, 8, 8, FAKE2 + 2, STREAM) == mx.MX_ERR_ALIGN
+    assert f(FAKE, 64, 8, 8, FAKE + 16, STREAM) == mx.MX_ERR_OVERLAP
+    assert f(0, 64, 8, 8, FAKE2, STREAM) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE, 0, 8, 8, FAKE2, STREAM) == mx.MX_OK
+
+
+def test_gemm_validation():
+    L = mx.load()
+    g = L.mx_gemm
+    ok_args = dict(M=64, N=64, K=256, a=FAKE, lda=256, sa=FAKE2, b=FAKE3, ldb=256, sb=FAKE4,
+                   c=FAKE4 + (1 << 20), ldc=64, dt=mx.MX_BF16)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return g(a["M"], a["N"], a["K"], a["a"], a["lda"], a["sa"], a["b"], a["ldb"], a["sb"],
+                 a["c"], a["ldc"], a["dt"], STREAM)
+
+    assert call(K=96) == mx.MX_ERR_UNSUPPORTED
+    assert call(K=100, lda=112, ldb=112) == mx.MX_ERR_SHAPE
+    assert call(K=0) == mx.MX_ERR_SHAPE
+    assert call(dt=7) == mx.MX_ERR_INVALID_ARG
+    assert call(M=-1) == mx.MX_ERR_INVALID_ARG
+    assert call(lda=128) == mx.MX_ERR_INVALID_ARG
+    assert call(ldc=32) == mx.MX_ERR_INVALID_ARG
+    assert call(a=FAKE + 8) == mx.MX_ERR_ALIGN
+    assert call(lda=264) == mx.MX_ERR_ALIGN
+    assert call(sa=FAKE2 + 2) == mx.MX_ERR_ALIGN
+    assert call(c=FAKE4 + (1 << 20) + 1) == mx.MX_ERR_ALIGN
+    assert call(sb=0) == mx.MX_ERR_INVALID_ARG
+    assert call(c=FAKE + 128) == mx.MX_ERR_OVERLAP
+    assert call(M=0) == mx.MX_OK
+    assert call(N=0) == mx.MX_OK
+
+
+def test_grouped_gemm_validation():
+    L = mx.load()
+    f = L.mx_grouped_gemm
+    base = (4, 100, 64, 256, FAKE4 + (1 << 22), FAKE, 256, FAKE2, FAKE3, FAKE4,
+            FAKE4 + (1 << 20), 64, mx.MX_BF16, STREAM)
+    assert f(*base[:0], 0, *base[1:]) == mx.MX_ERR_INVALID_ARG
+    assert f(*base[:4], 0, *base[5:]) == mx.MX_ERR_INVALID_ARG  # null offsets
+    assert f(*base[:4], FAKE4 + (1 << 22) + 4, *base[5:]) == mx.MX_ERR_ALIGN
+    assert f(*base[:3], 96, *base[4:]) == mx.MX_ERR_UNSUPPORTED
+    # C on top of the offsets array
+    assert f(*base[:10], FAKE4 + (1 << 22) - 64, *base[11:]) == mx.MX_ERR_OVERLAP
+    assert f(*base[:1], 0, *base[2:]) == mx.MX_OK
+
+
+def test_python_binding_fails_loudly_without_device_tensors():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mx.mx_quantize_rowwise(x, q=torch.zeros(4, 64, dtype=torch.uint8),
+                               s=torch.zeros(4, 2, dtype=torch.uint8), stream=0)

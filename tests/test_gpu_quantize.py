@@ -1,0 +1,185 @@
+"""GPU parity of the quantizers and the scale rearrangement against the oracle.
+
+Bar: bit-exact bytes (codes and scales), every byte of every output.  The
+E4M3/E8M0 rule is the one pinned in tests/test_oracle_pins.py.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import mxsynth
+import oracle
+from gpu_util import bf16_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _golden_x():
+    from test_oracle_pins import GOLDEN_BLOCKS
+    return np.array([b["x"] for b in GOLDEN_BLOCKS], np.uint16)
+
+
+def test_golden_blocks_rowwise_and_colwise(gpu_lib):
+    mx = gpu_lib
+    x = _golden_x()  # [7][32]
+    xt = mxsynth.from_bits(x)
+    q, s = mx.mx_quantize_rowwise(bf16_dev(xt))
+    oq, os_ = oracle.quantize_rowwise(x)
+    assert np.array_equal(q.cpu().numpy(), oq)
+    assert np.array_equal(s.cpu().numpy(), os_)
+    # the same blocks down columns: x^T is [32][7] -> pad columns to a multiple of 8
+    xc = np.zeros((32, 8), np.uint16)
+    xc[:, :7] = x.T
+    qt, st = mx.mx_quantize_colwise(bf16_dev(mxsynth.from_bits(xc)))
+    oqt, ost = oracle.quantize_colwise(xc)
+    assert np.array_equal(qt.cpu().numpy(), oqt) and np.array_equal(st.cpu().numpy(), ost)
+
+
+def _exhaustive_blocks():
+    """Blocks whose first element fixes the scale code c (amax = largest BF16 of
+    binade c + 8, or of binade <= 8 for c = 0) and whose other 31 elements run
+    over every finite BF16 of magnitude <= amax, both signs: every (element,
+    scale) pair the quantizer can meet."""
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    fin = allb[((allb >> 7) & 0xFF) != 0xFF]
+    mag = fin & 0x7FFF
+    rows = []
+    for c in range(0, 247):
+        e_amax = c + 8
+        amax = np.uint16((e_amax << 7) | 0x7F)
+        els = fin[mag <= amax]
+        n = (els.size + 30) // 31
+        pad = np.zeros(n * 31, np.uint16)
+        pad[:els.size] = els
+        blk = np.concatenate([np.full((n, 1), amax, np.uint16), pad.reshape(n, 31)], axis=1)
+        rows.append(blk)
+    return np.concatenate(rows, 0)
+
+
+def test_exhaustive_encoder_table_on_device(gpu_lib):
+    """All reachable (BF16 element, scale code) pairs: ~16 M elements."""
+    mx = gpu_lib
+    blocks = _exhaustive_blocks()            # [nblk][32]
+    nblk = blocks.shape[0]
+    rows = 64
+    nrow_blocks = (nblk + rows - 1) // rows
+    x = np.zeros((nrow_blocks * rows, 32), np.uint16)
+    x[:nblk] = blocks
+    x = x.reshape(nrow_blocks, rows * 32)    # row-major: each row holds 64 blocks
+    q, s = mx.mx_quantize_rowwise(bf16_dev(mxsynth.from_bits(x)))
+    oq, os_ = oracle.quantize_rowwise(x)
+    gq = q.cpu().numpy()
+    bad = np.argwhere(gq != oq)
+    assert bad.size == 0, f"{len(bad)} code mismatches, first at {bad[0]}: " \
+                          f"x={x[tuple(bad[0])]:#06x} got {gq[tuple(bad[0])]:#04x} " \
+                          f"ref {oq[tuple(bad[0])]:#04x}"
+    assert np.array_equal(s.cpu().numpy(), os_)
+    assert set(np.unique(os_).tolist()) == set(range(0, 247))
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (3, 96), (128, 256), (257, 4096), (33, 12288)])
+def test_rowwise_shapes(gpu_lib, rows, cols):
+    mx = gpu_lib
+    x = mxsynth.normal_bf16((rows, cols), 1.0, rows * 7 + cols, 0.01, 100.0)
+    q, s = mx.mx_quantize_rowwise(bf16_dev(x))
+    oq, os_ = oracle.quantize_rowwise(mxsynth.bits(x))
+    assert np.array_equal(q.cpu().numpy(), oq) and np.array_equal(s.cpu().numpy(), os_)
+
+
+def test_rowwise_strided_and_byte_views(gpu_lib):
+    """Leading dimensions larger than the row (a column slice of a wider tensor)."""
+    mx = gpu_lib
+    big = mxsynth.normal_bf16((40, 512), 0.02, 11, 0.001, 20.0)
+    xs = bf16_dev(big)[:, 128:384]                     # ld_x = 512
+    qbuf = torch.full((40, 320), 0xAB, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((40, 12), 0xCD, dtype=torch.uint8, device="cuda")
+    q, s = mx.mx_quantize_rowwise(xs, q=qbuf[:, :256], s=sbuf[:, :8])
+    oq, os_ = oracle.quantize_rowwise(mxsynth.bits(big[:, 128:384].contiguous()))
+    assert np.array_equal(q.cpu().numpy(), oq) and np.array_equal(s.cpu().numpy(), os_)
+    # bytes outside the used window are untouched
+    assert (qbuf[:, 256:] == 0xAB).all() and (sbuf[:, 8:] == 0xCD).all()
+
+
+@pytest.mark.parametrize("rows,cols", [(32, 8), (64, 24), (128, 256), (160, 264), (4096, 1024),
+                                       (96, 4104)])
+def test_colwise_shapes(gpu_lib, rows, cols):
+    mx = gpu_lib
+    x = mxsynth.normal_bf16((rows, cols), 1e-3, rows * 13 + cols, 0.01, 50.0)
+    qt, st = mx.mx_quantize_colwise(bf16_dev(x))
+    oqt, ost = oracle.quantize_colwise(mxsynth.bits(x))
+    assert np.array_equal(qt.cpu().numpy(), oqt) and np.array_equal(st.cpu().numpy(), ost)
+
+
+def test_colwise_strided_output(gpu_lib):
+    mx = gpu_lib
+    x = mxsynth.normal_bf16((64, 48), 1.0, 5)
+    qbuf = torch.full((48, 80), 0x11, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((48, 5), 0x22, dtype=torch.uint8, device="cuda")
+    qt, st = mx.mx_quantize_colwise(bf16_dev(x), qt=qbuf[:, :64], st_=sbuf[:, :2])
+    oqt, ost = oracle.quantize_colwise(mxsynth.bits(x))
+    assert np.array_equal(qt.cpu().numpy(), oqt) and np.array_equal(st.cpu().numpy(), ost)
+    assert (qbuf[:, 64:] == 0x11).all() and (sbuf[:, 2:] == 0x22).all()
+
+
+def test_tiny_config_bytes(gpu_lib):
+    mx = gpu_lib
+    A, B = mxsynth.tiny()
+    qa, sa = mx.mx_quantize_rowwise(bf16_dev(A))
+    qbt, sbt = mx.mx_quantize_colwise(bf16_dev(B))
+    oqa, osa = oracle.quantize_rowwise(mxsynth.bits(A))
+    oqb, osb = oracle.quantize_colwise(mxsynth.bits(B))
+    for g, o in ((qa, oqa), (sa, osa), (qbt, oqb), (sbt, osb)):
+        assert np.array_equal(g.cpu().numpy(), o)
+
+
+def test_determinism_repeat_calls(gpu_lib):
+    """Byte-for-byte: the same weights quantize to the same bytes on every call."""
+    mx = gpu_lib
+    w = bf16_dev(mxsynth.normal_bf16((1024, 4096), 0.02, 77, 0.001, 20.0))
+    q1, s1 = mx.mx_quantize_rowwise(w)
+    t1, u1 = mx.mx_quantize_colwise(w)
+    for _ in range(3):
+        q2, s2 = mx.mx_quantize_rowwise(w)
+        t2, u2 = mx.mx_quantize_colwise(w)
+        assert torch.equal(q1, q2) and torch.equal(s1, s2)
+        assert torch.equal(t1, t2) and torch.equal(u1, u2)
+
+
+def test_nan_inf_blocks(gpu_lib):
+    mx = gpu_lib
+    x = mxsynth.bits(mxsynth.normal_bf16((64, 64), 1.0, 3))
+    x[3, 5] = 0x7FC0   # NaN
+    x[40, 33] = 0xFF80  # -Inf
+    x[10, 40] = 0x7F80  # +Inf
+    xt = bf16_dev(mxsynth.from_bits(x))
+    q, s = mx.mx_quantize_rowwise(xt)
+    oq, os_ = oracle.quantize_rowwise(x)
+    assert np.array_equal(q.cpu().numpy(), oq) and np.array_equal(s.cpu().numpy(), os_)
+    qt, st = mx.mx_quantize_colwise(xt)
+    oqt, ost = oracle.quantize_colwise(x)
+    assert np.array_equal(qt.cpu().numpy(), oqt) and np.array_equal(st.cpu().numpy(), ost)
+    assert (os_ == 0xFF).sum() == 3
+
+
+# ---------------------------------------------------------------------------
+# scale rearrangement
+
+
+@pytest.mark.parametrize("rows,kb", [(1, 1), (32, 8), (33, 9), (128, 8), (100, 24), (4096, 384),
+                                     (4101, 77)])
+def test_swizzle_matches_oracle(gpu_lib, rows, kb):
+    mx = gpu_lib
+    rng = np.random.default_rng(rows * 31 + kb)
+    s = rng.integers(0, 255, size=(rows, kb), dtype=np.uint8)
+    out = mx.mx_scale_swizzle(to_dev(s))
+    assert np.array_equal(out.cpu().numpy(), oracle.scale_swizzle(s))
+
+
+def test_swizzle_strided_input(gpu_lib):
+    mx = gpu_lib
+    rng = np.random.default_rng(9)
+    s = rng.integers(0, 255, size=(70, 40), dtype=np.uint8)
+    out = mx.mx_scale_swizzle(to_dev(s)[:, 3:30])
+    assert np.array_equal(out.cpu().numpy(), oracle.scale_swizzle(s[:, 3:30].copy()))
