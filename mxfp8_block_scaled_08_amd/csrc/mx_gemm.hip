@@ -6,13 +6,18 @@
 // they run on the matrix cores: v_mfma_scale_f32_32x32x64_f8f6f4 multiplies
 // 32x64 E4M3 by 64x32 E4M3 with one E8M0 scale per lane and FP32 accumulate.
 //
-// Matrix-core operand layout (32x32x64, E4M3): lane l = 32h + r supplies 32
-// consecutive K bytes [32h, 32h+32) of row r, and one scale byte that applies
-// to exactly those 32 values -- one MX block.  The rearranged scale layout
-// (mx_scale_swizzle) gives each lane one 4-byte word per 256 K: byte t is the
-// scale of k-step t's block for that lane.  The instruction always reads
-// byte 0 of its scale operand on this target, so the kernel shifts byte t
-// down instead of relying on the byte-select field.
+// Matrix-core operand layout (32x32x64, E4M3), measured on gfx950: lane
+// l = 32h + r holds 32 bytes of row r; its bytes 0-15 belong to the
+// instruction's first 32-element K block and bytes 16-31 to the second, and
+// the scale of block x for row r is taken from lane 32x + r.  So lane (h, r)
+// loads the 16-byte chunks h and 2 + h of each 64-K step: MX block 2s + x
+// of step s is split over the two lane groups (16 bytes each) in byte half
+// x, and its E8M0 scale sits in lane 32x + r.  The rearranged scale layout
+// (mx_scale_swizzle) gives lane 32x + r one 4-byte word per 256 K whose byte
+// t is the scale of block 8kt + 2t + x: exactly the scale that lane must
+// supply at k-step t.  The instruction always reads byte 0 of its scale
+// operand on this target, so the kernel shifts byte t down instead of relying
+// on the byte-select field.
 //
 // Roles are swapped so the accumulator layout suits row-major C: the B tile
 // (N rows) feeds the instruction's first operand and the A tile (M rows) its
@@ -243,12 +248,13 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
         sb_off[i] = (uint32_t)((row >> 5) * KT256 * 256 + (h * 32 + (row & 31)) * 4);
     }
 
-    // ---- per-lane LDS read offsets of the matrix-core fragments.  Rows of
-    // the sub-tiles are 32 apart, which leaves chunk_perm unchanged, so one
-    // offset serves all four (plus i * 32 rows); the second 16-byte chunk of
-    // a lane's 32 bytes is the first one's slot XOR 1.
-    const uint32_t la0 = (uint32_t)((wm * 128 + r32) * BK + (((2 * h) ^ chunk_perm(r32)) * 16));
-    const uint32_t lb0 = (uint32_t)((wn * 128 + r32) * BK + (((2 * h) ^ chunk_perm(r32)) * 16));
+    // ---- per-lane LDS read offsets of the matrix-core fragments: chunk h
+    // (bytes 0-15 of the operand) and chunk 2 + h (bytes 16-31) of the lane's
+    // row.  Rows of the sub-tiles are 32 apart, which leaves chunk_perm
+    // unchanged, so one offset serves all four (plus i * 32 rows); chunk 2 + h
+    // sits in slot (h ^ perm) ^ 2, i.e. at the first offset XOR 32.
+    const uint32_t la0 = (uint32_t)((wm * 128 + r32) * BK + ((h ^ chunk_perm(r32)) * 16));
+    const uint32_t lb0 = (uint32_t)((wn * 128 + r32) * BK + ((h ^ chunk_perm(r32)) * 16));
 
     v16f acc[TN][TM];
 #pragma unroll
@@ -266,14 +272,14 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
 #pragma unroll
         for (int i = 0; i < TM; i++) {
             const uint4 lo = *reinterpret_cast<const uint4 *>(A_ + la0 + i * 32 * BK);
-            const uint4 hi = *reinterpret_cast<const uint4 *>(A_ + ((la0 + i * 32 * BK) ^ 16));
+            const uint4 hi = *reinterpret_cast<const uint4 *>(A_ + ((la0 + i * 32 * BK) ^ 32));
             xa[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
 #pragma unroll
         for (int i = 0; i < TN; i++) {
             const uint4 lo = *reinterpret_cast<const uint4 *>(B_ + lb0 + i * 32 * BK);
-            const uint4 hi = *reinterpret_cast<const uint4 *>(B_ + ((lb0 + i * 32 * BK) ^ 16));
+            const uint4 hi = *reinterpret_cast<const uint4 *>(B_ + ((lb0 + i * 32 * BK) ^ 32));
             xb[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }

@@ -1,0 +1,145 @@
+"""Full-size parity on the five workloads (Qwen3-8B / Qwen3-30B-A3B layer shapes).
+
+Quantized bytes and rearranged scales are compared with the oracle byte for
+byte over every element; GEMM outputs on sampled entries (random positions
+plus rows/columns along the edges of C) against the oracle's double-precision
+entries, with the derived tolerance of tests/gpu_util.py.  The launches are
+the same ones bench.py times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mxsynth
+import oracle
+from gpu_util import (check_sampled, check_sampled_grouped, oracle_colwise_par,
+                      oracle_rowwise_par, sample_entries)
+
+pytestmark = pytest.mark.gpu
+
+
+def _eq(gpu: torch.Tensor, ref: np.ndarray, what: str):
+    g = gpu.cpu().numpy()
+    assert g.shape == ref.shape, (what, g.shape, ref.shape)
+    bad = np.argwhere(g != ref)
+    assert bad.size == 0, f"{what}: {len(bad)} bytes differ, first at {tuple(bad[0])}"
+
+
+def _swz_eq(mx, s_gpu: torch.Tensor, s_ref: np.ndarray, what: str):
+    _eq(mx.mx_scale_swizzle(s_gpu), oracle.scale_swizzle(s_ref), what + " rearranged")
+
+
+@pytest.fixture(scope="module")
+def layer():
+    return mxsynth.weight_sync()
+
+
+def test_weight_sync_qwen3_8b_layer(gpu_lib, layer):
+    """Row-wise + column-wise MXFP8 and scale rearrangement of every weight."""
+    mx = gpu_lib
+    for name, w in layer.items():
+        wb = mxsynth.bits(w)
+        wd = w.cuda()
+        q, s = mx.mx_quantize_rowwise(wd)
+        oq, os_ = oracle_rowwise_par(wb)
+        _eq(q, oq, f"{name} rowwise q")
+        _eq(s, os_, f"{name} rowwise s")
+        _swz_eq(mx, s, os_, f"{name} rowwise")
+        qt, st = mx.mx_quantize_colwise(wd)
+        oqt, ost = oracle_colwise_par(wb)
+        _eq(qt, oqt, f"{name} colwise q")
+        _eq(st, ost, f"{name} colwise s")
+        _swz_eq(mx, st, ost, f"{name} colwise")
+        del q, s, qt, st
+
+
+def test_dense_forward_m4608(gpu_lib, layer):
+    mx = gpu_lib
+    xh, xi = mxsynth.dense_fwd_activations()
+    W = mxsynth.dense_fwd_weights(layer)
+    inputs = {"qkv": xh, "o": xh, "gate_up": xh, "down": xi}
+    quant = {}
+    for key, x in (("xh", xh), ("xi", xi)):
+        q, s = mx.mx_quantize_rowwise(x.cuda())
+        oq, os_ = oracle_rowwise_par(mxsynth.bits(x))
+        _eq(q, oq, f"{key} q")
+        _eq(s, os_, f"{key} s")
+        quant[key] = (q, s, oq, os_)
+    rng = np.random.default_rng(3)
+    for spec in mxsynth.DENSE_FWD_GEMMS:
+        q, s, oq, os_ = quant["xh" if inputs[spec.name] is xh else "xi"]
+        wq, ws = mx.mx_quantize_rowwise(W[spec.name].cuda())
+        owq, ows = oracle_rowwise_par(mxsynth.bits(W[spec.name]))
+        _eq(wq, owq, f"{spec.name} weight q")
+        C = mx.mx_gemm(q, mx.mx_scale_swizzle(s), wq, mx.mx_scale_swizzle(ws),
+                       out_dtype=torch.bfloat16)
+        assert C.shape == (spec.M, spec.N)
+        rows, cols = sample_entries(rng, spec.M, spec.N)
+        check_sampled(C, rows, cols, oq, os_, owq, ows, f"fwd {spec.name}")
+        del C, wq, ws
+
+
+def test_dense_backward_gate_up(gpu_lib, layer):
+    """dgrad = rowwise(dY) . colwise(W)^T ; wgrad = colwise(dY) . colwise(X)^T."""
+    mx = gpu_lib
+    dy, x = mxsynth.dense_bwd_inputs()
+    W = mxsynth.dense_fwd_weights(layer)["gate_up"]            # [24576][4096]
+    dyb, xb, wb = mxsynth.bits(dy), mxsynth.bits(x), mxsynth.bits(W)
+    dyd = dy.cuda()
+    rng = np.random.default_rng(4)
+    # dgrad: M = 12288 tokens, N = 4096, K = 24576
+    q, s = mx.mx_quantize_rowwise(dyd)
+    oq, os_ = oracle_rowwise_par(dyb)
+    _eq(q, oq, "dY rowwise q")
+    _eq(s, os_, "dY rowwise s")
+    wqt, wst = mx.mx_quantize_colwise(W.cuda())
+    owqt, owst = oracle_colwise_par(wb)
+    _eq(wqt, owqt, "W colwise q")
+    _eq(wst, owst, "W colwise s")
+    C = mx.mx_gemm(q, mx.mx_scale_swizzle(s), wqt, mx.mx_scale_swizzle(wst),
+                   out_dtype=torch.bfloat16)
+    rows, cols = sample_entries(rng, 12288, 4096)
+    check_sampled(C, rows, cols, oq, os_, owqt, owst, "dgrad")
+    del C, q, s, wqt, wst
+    # wgrad: M = 24576, N = 4096, K = 12288 tokens
+    dqt, dst = mx.mx_quantize_colwise(dyd)
+    odqt, odst = oracle_colwise_par(dyb)
+    _eq(dqt, odqt, "dY colwise q")
+    _eq(dst, odst, "dY colwise s")
+    xqt, xst = mx.mx_quantize_colwise(x.cuda())
+    oxqt, oxst = oracle_colwise_par(xb)
+    _eq(xqt, oxqt, "X colwise q")
+    _eq(xst, oxst, "X colwise s")
+    C = mx.mx_gemm(dqt, mx.mx_scale_swizzle(dst), xqt, mx.mx_scale_swizzle(xst),
+                   out_dtype=torch.bfloat16)
+    rows, cols = sample_entries(rng, 24576, 4096)
+    check_sampled(C, rows, cols, odqt, odst, oxqt, oxst, "wgrad")
+
+
+def test_moe_grouped_qwen3_30b_a3b(gpu_lib):
+    mx = gpu_lib
+    rows_per, a_gu, a_dn, w_gu, w_dn = mxsynth.moe_inputs()
+    off = mxsynth.offsets_from_rows(rows_per)
+    offd = torch.from_numpy(off).cuda()
+    rng = np.random.default_rng(5)
+    for name, a, w in (("gate_up", a_gu, w_gu), ("down", a_dn, w_dn)):
+        G, N, K = w.shape
+        q, s = mx.mx_quantize_rowwise(a.cuda())
+        oq, os_ = oracle_rowwise_par(mxsynth.bits(a))
+        _eq(q, oq, f"{name} A q")
+        _eq(s, os_, f"{name} A s")
+        wflat = w.reshape(G * N, K)
+        wq, ws = mx.mx_quantize_rowwise(wflat.cuda())
+        owq, ows = oracle_rowwise_par(mxsynth.bits(wflat))
+        _eq(wq, owq, f"{name} W q")
+        b_swz = torch.cat([mx.mx_scale_swizzle(ws[g * N:(g + 1) * N]) for g in range(G)])
+        C = mx.mx_grouped_gemm(offd, q, mx.mx_scale_swizzle(s), wq.view(G, N, K), b_swz,
+                               out_dtype=torch.bfloat16)
+        # every expert: its first and last row, plus random rows; random columns
+        firsts = off[:-1][rows_per > 0]
+        lasts = off[1:][rows_per > 0] - 1
+        rr = np.concatenate([firsts, lasts, rng.integers(0, int(off[-1]), size=1024)])
+        cc = rng.integers(0, N, size=rr.size)
+        check_sampled_grouped(C, rr, cc, off, oq, os_, owq.reshape(G, N, K),
+                              ows.reshape(G, N, K // 32), f"moe {name}")
+        del C, q, s, wq, ws
