@@ -1,0 +1,360 @@
+"""Benchmark of the MXFP8 hot path on one MI355X (gfx950).
+
+One step is one pass of the whole hot path over one Qwen3 layer's worth of
+synthetic input ("End-to-End MXFP8 Reinforcement Learning on Blackwell":
+Figure 1 for the path, Table 2 for the models and token counts, Table 7 for
+the ~4.5k-token dense break-even that sets M = 4608):
+
+  1. weight sync of a Qwen3-8B decoder layer: row-wise and column-wise MXFP8
+     quantization of q, k, v, o, gate, up, down, plus scale rearrangement;
+  2. dense forward at 4608 tokens: quantize X_h, X_i row-wise, rearrange,
+     GEMMs qkv / o / gate_up / down against the row-wise weights of step 1;
+  3. dense backward of gate_up at 12288 tokens: dY row-wise and column-wise,
+     X column-wise; dgrad = dY . W (column-wise weights of step 1) and
+     wgrad = dY^T . X;
+  4. Qwen3-30B-A3B MoE layer: 20480 tokens x top-8 = 163840 routed rows over
+     128 experts with Zipf(1.1) loads; quantize activations and expert
+     weights row-wise, rearrange, grouped GEMMs gate_up and down.
+
+Inputs are drawn once on the device (seeded, same distributions as the
+parity tests' CPU draws) and stay resident in HBM; the timed region holds
+only the library's kernels.  Prints ONE JSON line.
+"""
+import argparse
+import json
+import os
+import platform
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, 8 TB/s
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 / MXFP8 matrix peak, 5.0 PFLOP/s
+QUANT_BYTES_PER_ELEMENT = 2 + 1 + 1 / 32  # BF16 in, E4M3 out, E8M0 per 32
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events around launches on the current stream, summed per category."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pending = []
+        self.totals = {}
+        self.counts = {}
+
+    def __call__(self, cat, fn, *a, **kw):
+        t = self.torch
+        s = t.cuda.Event(enable_timing=True)
+        e = t.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn(*a, **kw)
+        e.record()
+        self.pending.append((cat, s, e))
+        return out
+
+    def collect(self):
+        for cat, s, e in self.pending:
+            self.totals[cat] = self.totals.get(cat, 0.0) + s.elapsed_time(e)
+            self.counts[cat] = self.counts.get(cat, 0) + 1
+        self.pending = []
+
+
+def build_workload(mx, torch, mxsynth):
+    dev = "cuda"
+    W = mxsynth.weight_sync(device=dev)
+    xh, xi = mxsynth.dense_fwd_activations(device=dev)
+    dy, xb = mxsynth.dense_bwd_inputs(device=dev)
+    rows_per, a_gu, a_dn, w_gu, w_dn = mxsynth.moe_inputs(device=dev)
+    off = torch.from_numpy(mxsynth.offsets_from_rows(rows_per)).to(dev)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    swz = mx.mx_scale_swizzled_bytes
+
+    o = {}
+    # weight sync outputs: row-wise into the fused forward operands, column-wise
+    # into the fused backward operand of gate_up
+    o["qkv_q"] = torch.empty(6144, 4096, **u8)
+    o["qkv_s"] = torch.empty(6144, 128, **u8)
+    o["o_q"], o["o_s"] = torch.empty(4096, 4096, **u8), torch.empty(4096, 128, **u8)
+    o["gu_q"] = torch.empty(24576, 4096, **u8)
+    o["gu_s"] = torch.empty(24576, 128, **u8)
+    o["dn_q"], o["dn_s"] = torch.empty(4096, 12288, **u8), torch.empty(4096, 384, **u8)
+    o["guT_q"] = torch.empty(4096, 24576, **u8)
+    o["guT_s"] = torch.empty(4096, 768, **u8)
+    o["colT"] = {n: (torch.empty(W[n].shape[1], W[n].shape[0], **u8),
+                     torch.empty(W[n].shape[1], W[n].shape[0] // 32, **u8))
+                 for n in ("q", "k", "v", "o", "down")}
+    for name, (r, c) in (("qkv", (6144, 4096)), ("o", (4096, 4096)), ("gu", (24576, 4096)),
+                         ("dn", (4096, 12288)), ("guT", (4096, 24576))):
+        o[name + "_swz"] = torch.empty(swz(r, c // 32), **u8)
+    o["colT_swz"] = {n: torch.empty(swz(W[n].shape[1], W[n].shape[0] // 32), **u8)
+                     for n in o["colT"]}
+    # activations
+    for name, x in (("xh", xh), ("xi", xi)):
+        o[name + "_q"] = torch.empty(x.shape, **u8)
+        o[name + "_s"] = torch.empty(x.shape[0], x.shape[1] // 32, **u8)
+        o[name + "_swz"] = torch.empty(swz(x.shape[0], x.shape[1] // 32), **u8)
+    o["dy_q"], o["dy_s"] = torch.empty(12288, 24576, **u8), torch.empty(12288, 768, **u8)
+    o["dy_swz"] = torch.empty(swz(12288, 768), **u8)
+    o["dyT_q"], o["dyT_s"] = torch.empty(24576, 12288, **u8), torch.empty(24576, 384, **u8)
+    o["dyT_swz"] = torch.empty(swz(24576, 384), **u8)
+    o["xT_q"], o["xT_s"] = torch.empty(4096, 12288, **u8), torch.empty(4096, 384, **u8)
+    o["xT_swz"] = torch.empty(swz(4096, 384), **u8)
+    M = int(off[-1].item())
+    for name, a, w in (("mgu", a_gu, w_gu), ("mdn", a_dn, w_dn)):
+        G, N, K = w.shape
+        o[name + "_aq"] = torch.empty(M, K, **u8)
+        o[name + "_as"] = torch.empty(M, K // 32, **u8)
+        o[name + "_aswz"] = torch.empty(swz(M, K // 32), **u8)
+        o[name + "_wq"] = torch.empty(G * N, K, **u8)
+        o[name + "_ws"] = torch.empty(G * N, K // 32, **u8)
+        o[name + "_wswz"] = torch.empty(swz(G * N, K // 32), **u8)
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    o["C_qkv"] = torch.empty(4608, 6144, **bf)
+    o["C_o"] = torch.empty(4608, 4096, **bf)
+    o["C_gu"] = torch.empty(4608, 24576, **bf)
+    o["C_dn"] = torch.empty(4608, 4096, **bf)
+    o["C_dgrad"] = torch.empty(12288, 4096, **bf)
+    o["C_wgrad"] = torch.empty(24576, 4096, **bf)
+    o["C_mgu"] = torch.empty(M, 1536, **bf)
+    o["C_mdn"] = torch.empty(M, 2048, **bf)
+    inputs = dict(W=W, xh=xh, xi=xi, dy=dy, x=xb, off=off, a_gu=a_gu, a_dn=a_dn,
+                  w_gu=w_gu, w_dn=w_dn, M=M)
+    return inputs, o
+
+
+def step(mx, I, o, T):
+    """One pass of the hot path; T(category, fn, ...) times each launch."""
+    W = I["W"]
+    rq, cq, sw = mx.mx_quantize_rowwise, mx.mx_quantize_colwise, mx.mx_scale_swizzle
+    # 1. weight sync: row-wise into the fused forward operands
+    T("quant_row", rq, W["q"], o["qkv_q"][0:4096], o["qkv_s"][0:4096])
+    T("quant_row", rq, W["k"], o["qkv_q"][4096:5120], o["qkv_s"][4096:5120])
+    T("quant_row", rq, W["v"], o["qkv_q"][5120:6144], o["qkv_s"][5120:6144])
+    T("quant_row", rq, W["o"], o["o_q"], o["o_s"])
+    T("quant_row", rq, W["gate"], o["gu_q"][0:12288], o["gu_s"][0:12288])
+    T("quant_row", rq, W["up"], o["gu_q"][12288:24576], o["gu_s"][12288:24576])
+    T("quant_row", rq, W["down"], o["dn_q"], o["dn_s"])
+    #    column-wise: gate and up side by side into the backward operand of gate_up
+    T("quant_col", cq, W["gate"], o["guT_q"][:, 0:12288], o["guT_s"][:, 0:384])
+    T("quant_col", cq, W["up"], o["guT_q"][:, 12288:24576], o["guT_s"][:, 384:768])
+    for n, (qt, st) in o["colT"].items():
+        T("quant_col", cq, W[n], qt, st)
+    for name in ("qkv", "o", "gu", "dn", "guT"):
+        T("swizzle", sw, o[name + "_s"], o[name + "_swz"])
+    for n, (qt, st) in o["colT"].items():
+        T("swizzle", sw, st, o["colT_swz"][n])
+    # 2. dense forward, M = 4608
+    for name in ("xh", "xi"):
+        T("quant_row", rq, I[name], o[name + "_q"], o[name + "_s"])
+        T("swizzle", sw, o[name + "_s"], o[name + "_swz"])
+    g = mx.mx_gemm
+    T("gemm", g, o["xh_q"], o["xh_swz"], o["qkv_q"], o["qkv_swz"], c=o["C_qkv"])
+    T("gemm", g, o["xh_q"], o["xh_swz"], o["o_q"], o["o_swz"], c=o["C_o"])
+    T("gemm", g, o["xh_q"], o["xh_swz"], o["gu_q"], o["gu_swz"], c=o["C_gu"])
+    T("gemm", g, o["xi_q"], o["xi_swz"], o["dn_q"], o["dn_swz"], c=o["C_dn"])
+    # 3. dense backward of gate_up, 12288 tokens
+    T("quant_row", rq, I["dy"], o["dy_q"], o["dy_s"])
+    T("quant_col", cq, I["dy"], o["dyT_q"], o["dyT_s"])
+    T("quant_col", cq, I["x"], o["xT_q"], o["xT_s"])
+    for name in ("dy", "dyT", "xT"):
+        T("swizzle", sw, o[name + "_s"], o[name + "_swz"])
+    T("gemm", g, o["dy_q"], o["dy_swz"], o["guT_q"], o["guT_swz"], c=o["C_dgrad"])
+    T("gemm", g, o["dyT_q"], o["dyT_swz"], o["xT_q"], o["xT_swz"], c=o["C_wgrad"])
+    # 4. MoE layer, grouped per expert
+    for name, a, w in (("mgu", I["a_gu"], I["w_gu"]), ("mdn", I["a_dn"], I["w_dn"])):
+        G, N, K = w.shape
+        T("quant_row", rq, w.view(G * N, K), o[name + "_wq"], o[name + "_ws"])
+        T("swizzle", sw, o[name + "_ws"], o[name + "_wswz"])
+        T("quant_row", rq, a, o[name + "_aq"], o[name + "_as"])
+        T("swizzle", sw, o[name + "_as"], o[name + "_aswz"])
+        T("grouped_gemm", mx.mx_grouped_gemm, I["off"], o[name + "_aq"], o[name + "_aswz"],
+          o[name + "_wq"].view(G, N, K), o[name + "_wswz"], c=o["C_" + name])
+
+
+def work_per_step(I):
+    """Algorithmic work of one step: elements quantized per orientation, scale
+    bytes rearranged, GEMM FLOPs (dense and grouped)."""
+    W = I["W"]
+    row_el = sum(w.numel() for w in W.values())                  # weight sync row-wise
+    col_el = sum(w.numel() for w in W.values())                  # weight sync column-wise
+    row_el += I["xh"].numel() + I["xi"].numel()                  # forward activations
+    row_el += I["dy"].numel()                                    # dgrad operand
+    col_el += I["dy"].numel() + I["x"].numel()                   # wgrad operands
+    row_el += I["w_gu"].numel() + I["w_dn"].numel() + I["a_gu"].numel() + I["a_dn"].numel()
+    M = I["M"]
+    dense = (2 * 4608 * 6144 * 4096 + 2 * 4608 * 4096 * 4096 + 2 * 4608 * 24576 * 4096
+             + 2 * 4608 * 4096 * 12288 + 2 * 12288 * 4096 * 24576 + 2 * 24576 * 4096 * 12288)
+    grouped = 2 * M * 1536 * 2048 + 2 * M * 2048 * 768
+    return row_el, col_el, dense, grouped
+
+
+def cpu_baseline(torch, mxsynth, row_el, col_el, flops):
+    """The CPU oracle (single-threaded C, as it stands) on a bounded sample of
+    the same workload, extrapolated to the step's work in the metric's unit."""
+    import numpy as np
+    import oracle
+
+    t0 = time.perf_counter()
+    w = mxsynth.normal_bf16((1024, 4096), 0.02, 2004, 0.001, 20.0)
+    wb = mxsynth.bits(w)
+    t = time.perf_counter()
+    n_q = 0
+    while time.perf_counter() - t < 4.0:
+        oracle.quantize_rowwise(wb)
+        oracle.quantize_colwise(wb)
+        n_q += 1
+    q_time = time.perf_counter() - t
+    q_rate = n_q * wb.size / q_time * 2          # element-orientations per second
+    xh = mxsynth.channel_outliers_bf16(64, 4096, 1.0, 3000, 0.005, 50.0)
+    qa, sa = oracle.quantize_rowwise(mxsynth.bits(xh))
+    qb, sb = oracle.quantize_rowwise(mxsynth.bits(
+        mxsynth.normal_bf16((512, 4096), 0.02, 2000, 0.001, 20.0)))
+    t = time.perf_counter()
+    n_g = 0
+    rows = np.repeat(np.arange(64), 512)
+    cols = np.tile(np.arange(512), 64)
+    while time.perf_counter() - t < 8.0:
+        oracle.gemm_sampled(rows, cols, qa, sa, qb, sb)
+        n_g += 1
+    g_time = time.perf_counter() - t
+    g_rate = n_g * 2 * 64 * 512 * 4096 / g_time  # FLOP/s
+    step_s = (row_el + col_el) / q_rate + flops / g_rate
+    return {
+        "value": flops / step_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"row+column quantize of a 1024x4096 weight ({n_q} passes, {q_time:.1f} s: "
+                   f"{q_rate / 1e6:.1f} M element-orientations/s) and FP64 GEMM of a 64x512x4096 "
+                   f"slice of the forward qkv product ({n_g} passes, {g_time:.1f} s: "
+                   f"{g_rate / 1e9:.3f} GFLOP/s); step time extrapolated to the full step "
+                   f"({step_s:.0f} s), single thread"),
+        "wall_s": round(time.perf_counter() - t0, 1),
+        "host_cpu": platform.processor() or platform.machine(),
+        "host_nproc": os.cpu_count(),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the MXFP8 hot "
+              "path here is a single-GPU library with no collectives", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mxfp8_block_scaled_08_amd as mx
+    import mxsynth
+
+    mx.load()
+    torch.cuda.set_device(0)
+    I, o = build_workload(mx, torch, mxsynth)
+    torch.cuda.synchronize()
+
+    noop = lambda cat, fn, *a, **kw: fn(*a, **kw)
+    for _ in range(args.warmup):
+        step(mx, I, o, noop)
+    torch.cuda.synchronize()
+
+    T = Timer(torch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step(mx, I, o, T)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    T.collect()
+    gpu_ms = start.elapsed_time(end)
+    ms_per_step = gpu_ms / args.steps
+
+    row_el, col_el, dense, grouped = work_per_step(I)
+    flops = dense + grouped
+    K = args.steps
+    q_bytes = (row_el + col_el) * QUANT_BYTES_PER_ELEMENT
+    qt = (T.totals.get("quant_row", 0) + T.totals.get("quant_col", 0)) / K  # ms
+    gemm_ms = T.totals["gemm"] / K
+    ggemm_ms = T.totals["grouped_gemm"] / K
+    ops = {
+        "quantize_rowwise": {"ms": T.totals["quant_row"] / K,
+                             "GB/s": row_el * QUANT_BYTES_PER_ELEMENT / (T.totals["quant_row"] / K) / 1e6},
+        "quantize_colwise": {"ms": T.totals["quant_col"] / K,
+                             "GB/s": col_el * QUANT_BYTES_PER_ELEMENT / (T.totals["quant_col"] / K) / 1e6},
+        "scale_swizzle": {"ms": T.totals["swizzle"] / K, "launches": T.counts["swizzle"] // K},
+        "dense_gemm": {"ms": gemm_ms, "TFLOP/s": dense / gemm_ms / 1e9},
+        "grouped_gemm": {"ms": ggemm_ms, "TFLOP/s": grouped / ggemm_ms / 1e9},
+    }
+    for k, v in ops.items():
+        if "GB/s" in v:
+            v["frac_hbm_peak"] = v["GB/s"] / HBM_PEAK_GBPS
+        if "TFLOP/s" in v:
+            v["frac_mfma_peak"] = v["TFLOP/s"] / MFMA_FP8_PEAK_TFLOPS
+        for kk in list(v):
+            if isinstance(v[kk], float):
+                v[kk] = round(v[kk], 4)
+    dense_tflops = dense / gemm_ms / 1e9
+    result = {
+        "metric": "MXFP8 GEMM TFLOP/s + quantize GB/s vs MI355X peaks, Qwen3 layer shapes",
+        "value": round(flops / ms_per_step / 1e9, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8-e4m3 (E8M0 block scales, FP32 accumulate, BF16 out)",
+        "data": "synthetic (seeded device draws; Qwen3-8B / Qwen3-30B-A3B layer shapes)",
+        "config": {
+            "workload": ("qwen3-layer-pass: weight-sync row+column MXFP8 quantize of one "
+                         "Qwen3-8B layer; dense fwd M=4608 (qkv, o, gate_up, down); dense bwd "
+                         "gate_up dgrad 12288x4096x24576 + wgrad 24576x4096x12288; Qwen3-30B-A3B "
+                         "MoE grouped gate_up/down, 163840 rows, 128 experts, Zipf(1.1)"),
+            "gemm_flop_per_step": flops,
+            "quantized_elements_per_step": row_el + col_el,
+            "parallelism": "single GPU",
+        },
+        "value_definition": "total GEMM FLOP of the step / wall time of the whole step "
+                            "(quantize, rearrangement and GEMMs, HIP events)",
+        "quantize_GBps": round(q_bytes / qt / 1e6, 1),
+        "quantize_frac_hbm_peak": round(q_bytes / qt / 1e6 / HBM_PEAK_GBPS, 4),
+        "gemm_TFLOPs": round((dense + grouped) / (gemm_ms + ggemm_ms) / 1e9, 1),
+        "gemm_frac_mfma_peak": round((dense + grouped) / (gemm_ms + ggemm_ms) / 1e9
+                                     / MFMA_FP8_PEAK_TFLOPS, 4),
+        "ops": ops,
+        "roofline": {
+            "kernel": "mx_gemm_kernel<dense, BF16 out>",
+            "bound": "mfma",
+            "achieved": round(dense_tflops, 1),
+            "peak": MFMA_FP8_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(dense_tflops / MFMA_FP8_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "launches_per_step": T.counts["gemm"] // K,
+            "avg_launch_ms": round(gemm_ms / (T.counts["gemm"] // K), 4),
+        },
+        "wall_s_timed_region": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(torch, mxsynth, row_el, col_el, flops)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

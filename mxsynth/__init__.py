@@ -30,33 +30,37 @@ import torch
 # primitive draws
 
 
-def _gen(seed: int) -> torch.Generator:
-    g = torch.Generator(device="cpu")
+def _gen(seed: int, device="cpu") -> torch.Generator:
+    g = torch.Generator(device=device)
     g.manual_seed(seed)
     return g
 
 
 def normal_bf16(shape, std: float, seed: int, outlier_frac: float = 0.0,
-                outlier_mul: float = 1.0) -> torch.Tensor:
-    """N(0, std) with a fraction of elements (chosen without replacement) multiplied."""
-    g = _gen(seed)
-    x = torch.randn(*shape, generator=g, dtype=torch.float32) * std
+                outlier_mul: float = 1.0, device="cpu") -> torch.Tensor:
+    """N(0, std) with a fraction of elements (chosen without replacement) multiplied.
+
+    ``device`` picks where the generator runs: the CPU stream is the one the
+    parity tests use; a device stream draws the same distribution faster but
+    not the same numbers."""
+    g = _gen(seed, device)
+    x = torch.randn(*shape, generator=g, dtype=torch.float32, device=device) * std
     n = x.numel()
     k = int(round(outlier_frac * n))
     if k > 0:
-        idx = torch.randperm(n, generator=g)[:k]
+        idx = torch.randperm(n, generator=g, device=device)[:k]
         x.view(-1)[idx] *= outlier_mul
     return x.to(torch.bfloat16)
 
 
 def channel_outliers_bf16(rows: int, cols: int, std: float, seed: int, frac: float,
-                          mul: float) -> torch.Tensor:
+                          mul: float, device="cpu") -> torch.Tensor:
     """Activations N(0, std) whose ``frac`` of whole columns (channels) are multiplied."""
-    g = _gen(seed)
-    x = torch.randn(rows, cols, generator=g, dtype=torch.float32) * std
+    g = _gen(seed, device)
+    x = torch.randn(rows, cols, generator=g, dtype=torch.float32, device=device) * std
     k = int(round(frac * cols))
     if k > 0:
-        ch = torch.randperm(cols, generator=g)[:k]
+        ch = torch.randperm(cols, generator=g, device=device)[:k]
         x[:, ch] *= mul
     return x.to(torch.bfloat16)
 
@@ -167,17 +171,17 @@ def tiny(seed: int = 0):
     return A.to(torch.bfloat16), B.to(torch.bfloat16)
 
 
-def weight_sync(cfg_seed: int = 2000) -> Dict[str, torch.Tensor]:
+def weight_sync(cfg_seed: int = 2000, device="cpu") -> Dict[str, torch.Tensor]:
     """One Qwen3-8B decoder layer's BF16 weights ~ N(0, 0.02), 0.1% of elements x20."""
-    return {name: normal_bf16(shape, 0.02, cfg_seed + i, 0.001, 20.0)
+    return {name: normal_bf16(shape, 0.02, cfg_seed + i, 0.001, 20.0, device)
             for i, (name, shape) in enumerate(QWEN3_8B_WEIGHTS)}
 
 
-def dense_fwd_activations(seed: int = 3000):
+def dense_fwd_activations(seed: int = 3000, device="cpu"):
     """X_h[4608x4096] (input of qkv, o, gate_up) and X_i[4608x12288] (input of down),
     N(0,1) with 0.5% of channels x50."""
-    xh = channel_outliers_bf16(DENSE_FWD_TOKENS, 4096, 1.0, seed, 0.005, 50.0)
-    xi = channel_outliers_bf16(DENSE_FWD_TOKENS, 12288, 1.0, seed + 1, 0.005, 50.0)
+    xh = channel_outliers_bf16(DENSE_FWD_TOKENS, 4096, 1.0, seed, 0.005, 50.0, device)
+    xi = channel_outliers_bf16(DENSE_FWD_TOKENS, 12288, 1.0, seed + 1, 0.005, 50.0, device)
     return xh, xi
 
 
@@ -187,15 +191,15 @@ def dense_fwd_weights(w: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:
             "gate_up": torch.cat([w["gate"], w["up"]], 0), "down": w["down"]}
 
 
-def dense_bwd_inputs(seed: int = 4000):
+def dense_bwd_inputs(seed: int = 4000, device="cpu"):
     """dY[12288x24576] ~ N(0, 1e-3) (gradient of the gate_up output) and the
     layer input X[12288x4096] drawn like the forward activations."""
-    dy = normal_bf16((DENSE_BWD_TOKENS, 24576), 1e-3, seed)
-    x = channel_outliers_bf16(DENSE_BWD_TOKENS, 4096, 1.0, seed + 1, 0.005, 50.0)
+    dy = normal_bf16((DENSE_BWD_TOKENS, 24576), 1e-3, seed, device=device)
+    x = channel_outliers_bf16(DENSE_BWD_TOKENS, 4096, 1.0, seed + 1, 0.005, 50.0, device)
     return dy, x
 
 
-def moe_inputs(seed: int = 5000):
+def moe_inputs(seed: int = 5000, device="cpu"):
     """Qwen3-30B-A3B MoE layer: routed rows sorted by expert.
 
     Returns (rows_per_expert[128], A_gu[163840x2048], A_dn[163840x768],
@@ -203,10 +207,10 @@ def moe_inputs(seed: int = 5000):
     weights N(0, 0.02)."""
     rows = zipf_expert_rows(MOE_TOKENS, MOE_EXPERTS, MOE_TOPK, 1.1)
     m = int(rows.sum())
-    a_gu = normal_bf16((m, MOE_HIDDEN), 1.0, seed)
-    a_dn = normal_bf16((m, MOE_FFN), 1.0, seed + 1)
-    w_gu = normal_bf16((MOE_EXPERTS, 2 * MOE_FFN, MOE_HIDDEN), 0.02, seed + 2)
-    w_dn = normal_bf16((MOE_EXPERTS, MOE_HIDDEN, MOE_FFN), 0.02, seed + 3)
+    a_gu = normal_bf16((m, MOE_HIDDEN), 1.0, seed, device=device)
+    a_dn = normal_bf16((m, MOE_FFN), 1.0, seed + 1, device=device)
+    w_gu = normal_bf16((MOE_EXPERTS, 2 * MOE_FFN, MOE_HIDDEN), 0.02, seed + 2, device=device)
+    w_dn = normal_bf16((MOE_EXPERTS, MOE_HIDDEN, MOE_FFN), 0.02, seed + 3, device=device)
     return rows, a_gu, a_dn, w_gu, w_dn
 
 
