@@ -32,8 +32,12 @@
 // three stages stay in flight while the matrix cores work on the fourth.
 // Each load instruction writes 1 KiB of LDS linearly by lane, so the lane's
 // global address picks which 16-byte chunk lands where: the four chunks of a
-// 64-byte row are XOR-permuted by ((row >> 1) ^ (row >> 3)) & 3 so that the
-// matrix-core reads of consecutive rows fall in distinct LDS banks.  The
+// 64-byte row are XOR-permuted by (row >> 3) & 3.  A 16-byte LDS read is
+// serviced 16 lanes at a time, in the lane groups {0-3, 12-15, 20-27} and
+// {4-11, 16-19, 28-31} of each half-wave (measured with in-bounds probes and
+// the LDS bank-conflict counter), each cycle covering 64 banks = 256 bytes.
+// Within a group the four rows with equal row % 4 differ in bits 3-4, so the
+// permutation gives every lane of a group its own 16-byte bank slot.  The
 // fragments of stage k+1 are read from LDS while the matrix cores run stage k.
 #include "mx_device.h"
 #include "mx_launch.h"
@@ -68,7 +72,7 @@ struct GemmParams {
     int vec_store;
 };
 
-__device__ __forceinline__ int chunk_perm(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int chunk_perm(int row) { return (row >> 3) & 3; }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
 {
@@ -85,6 +89,19 @@ typedef void __attribute__((address_space(3))) *lptr_t;
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
 #define MX_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+// Workgroup barrier for the LDS ring.  __syncthreads() would also wait for
+// every outstanding vector-memory load (its release fence must cover the LDS
+// writes of the direct-to-LDS loads), draining the whole pipeline each step.
+// Here each wave waits only for its own LDS reads (so a buffer can be
+// refilled) and the loads of the stage about to be read were already waited
+// for with MX_WAIT_VMCNT; the "memory" clobber keeps the compiler from moving
+// LDS accesses across the barrier.
+__device__ __forceinline__ void lds_ring_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+}
 
 // Vector-memory operations a wave issues per stage of DMA, and the scale
 // words it loads per 256-K group (both 8 here, so every count below is a
@@ -309,7 +326,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
         else
             MX_WAIT_VMCNT(0);
     }
-    __syncthreads();
+    lds_ring_barrier();
     v8i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
     read_frags(0, fa0, fb0);
 
@@ -332,7 +349,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                 else                                                                         \
                     MX_WAIT_VMCNT(0);                                                        \
             }                                                                                \
-            __syncthreads();                                                                 \
+            lds_ring_barrier();                                                              \
             if ((POS) == 0 && it + 4 < KIT) {                                                \
                 const int64_t kw = (int64_t)((it + 4) >> 2) * 256;                           \
                 _Pragma("unroll") for (int i = 0; i < TM; i++)                               \
