@@ -52,13 +52,18 @@ __global__ __launch_bounds__(QR_THREADS) void quantize_rowwise_kernel(
             int64_t u = base + (int64_t)i * QR_THREADS;
             // units is a multiple of 4 and u % 4 == lane % 4, so a quad is
             // either entirely in range or entirely out of it.
-            uint32_t m = max_mag_x8(v[i]);
+            const uint4 &w = v[i];
+            uint32_t m = pk_max_u16(pk_max_u16(mag2(w.x), mag2(w.y)), pk_max_u16(mag2(w.z), mag2(w.w)));
+            m = max(m & 0xFFFFu, m >> 16);
             m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false)); // [1,0,3,2]
             m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false)); // [2,3,0,1]
             if (u >= units)
                 continue;
-            uint32_t c = scale_code(m);
-            uint2 out = e4m3_x8(v[i], (int)c, c == 0xFFu);
+            const uint32_t c = scale_code(m);
+            const float sc = cvt_scale(c);
+            uint2 out;
+            out.x = nan_block_select(cvt_x4(w.x, w.y, sc), c);
+            out.y = nan_block_select(cvt_x4(w.z, w.w, sc), c);
             int64_t qo, so;
             if (CONTIG) {
                 qo = u * 8;
@@ -77,79 +82,79 @@ __global__ __launch_bounds__(QR_THREADS) void quantize_rowwise_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Column-wise: a workgroup quantizes a tile of 128 rows x 256 columns.  The
-// tile is read with 16-byte row-contiguous loads into LDS; then thread j owns
-// column j of the tile, reads its 128 values down the column (consecutive
-// lanes read consecutive LDS halfwords: no bank conflicts), and writes the
-// four 32-element blocks as 128 contiguous bytes of the transposed output
-// row qt[col][...] plus four scale bytes.
+// Column-wise: a block is 32 consecutive rows of one column, and the output is
+// transposed (qt[col][row], st[col][row / 32]).  No LDS: each wave covers a
+// 128-row x 64-column tile; lane = 16 * rb + 8 * half + cg owns columns
+// c0 .. c0+7 (cg selects the 8-column group) and rows 16 * half .. +15 of row
+// block rb.  Every load is a 16-byte vector of 8 columns (eight lanes read one
+// 128-byte line of a row).  The lane's packed per-column maxima over its 16
+// rows are combined with the other half of the block by a DPP rotation of 8
+// within each 16-lane row (lane ^ 8).  v_perm pairs two rows of one column in
+// a word for the scaled conversion, so the lane's 16 codes of a column form
+// one 16-byte store, and the eight lanes of a column write one full 128-byte
+// line of qt.  Four waves side by side make a 128 x 256 workgroup tile.
 
 constexpr int QC_THREADS = 256;
-constexpr int QC_ROWS = 128;
-constexpr int QC_COLS = 256;
+constexpr int QC_TILE_R = 128;
+constexpr int QC_TILE_C = 256;
 
 __global__ __launch_bounds__(QC_THREADS) void quantize_colwise_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t *__restrict__ qt, int64_t ld_qt, uint8_t *__restrict__ st, int64_t ld_st,
     int64_t tiles_c)
 {
-    __shared__ uint16_t tile[QC_ROWS][QC_COLS];
-    const int64_t tr = blockIdx.x / tiles_c;
-    const int64_t tc = blockIdx.x - tr * tiles_c;
-    const int64_t r0 = tr * QC_ROWS, c0 = tc * QC_COLS;
-    const int nrows = (int)min((int64_t)QC_ROWS, rows - r0);  // multiple of 32
-    const int ncols = (int)min((int64_t)QC_COLS, cols - c0);  // multiple of 8
-    const int tid = threadIdx.x;
-
-    // load: 8 rows x 256 columns per pass, 16 passes
-    {
-        const int col8 = tid & 31;
-        const int rsub = tid >> 5;
-        uint4 v[QC_ROWS / 8];
+    const int lane = threadIdx.x & 63;
+    const int cg = lane & 7, half = (lane >> 3) & 1, rb = lane >> 4;
+    const int64_t tr = blockIdx.x / tiles_c, tc = blockIdx.x - tr * tiles_c;
+    const int64_t c0 = tc * QC_TILE_C + (threadIdx.x >> 6) * 64 + cg * 8;
+    const int64_t r0 = tr * QC_TILE_R + rb * 32 + half * 16;
+    // rows % 32 == 0 and cols % 8 == 0: a lane's rows and columns are either
+    // all in range or all out of it, and both halves of a block agree.
+    const bool active = c0 < cols && r0 < rows;
+    // Lanes out of range read rows 0..15 of column group 0 (present whenever
+    // the grid is not empty) and store nothing; their DPP partner lane ^ 8 is
+    // out of range too, so those values never reach a stored block.
+    const uint16_t *src = x + (active ? r0 * ld_x + c0 : 0);
+    uint4 v[16];
 #pragma unroll
-        for (int p = 0; p < QC_ROWS / 8; p++) {
-            int r = p * 8 + rsub;
-            if (r < nrows && col8 * 8 < ncols)
-                v[p] = *reinterpret_cast<const uint4 *>(x + (r0 + r) * ld_x + c0 + col8 * 8);
-            else
-                v[p] = make_uint4(0, 0, 0, 0);
-        }
+    for (int i = 0; i < 16; i++)
+        v[i] = *reinterpret_cast<const uint4 *>(src + i * ld_x);
+    // packed maxima of columns (0,1), (2,3), (4,5), (6,7)
+    uint32_t m[4] = {0, 0, 0, 0};
 #pragma unroll
-        for (int p = 0; p < QC_ROWS / 8; p++)
-            *reinterpret_cast<uint4 *>(&tile[p * 8 + rsub][col8 * 8]) = v[p];
+    for (int i = 0; i < 16; i++) {
+        m[0] = pk_max_u16(m[0], mag2(v[i].x));
+        m[1] = pk_max_u16(m[1], mag2(v[i].y));
+        m[2] = pk_max_u16(m[2], mag2(v[i].z));
+        m[3] = pk_max_u16(m[3], mag2(v[i].w));
     }
-    __syncthreads();
-
-    const int j = tid;
-    if (j >= ncols)
+#pragma unroll
+    for (int k = 0; k < 4; k++)  // row_ror:8 - the other half of the block
+        m[k] = pk_max_u16(m[k], (uint32_t)__builtin_amdgcn_mov_dpp((int)m[k], 0x128, 0xF, 0xF, false));
+    if (!active)
         return;
-    uint8_t *qrow = qt + (c0 + j) * ld_qt + r0;
-    uint8_t *srow = st + (c0 + j) * ld_st + r0 / 32;
-    for (int b = 0; b < nrows / 32; b++) {
-        uint32_t w[16];
-        uint32_t m = 0;
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-            uint32_t lo = tile[32 * b + 2 * i][j];
-            uint32_t hi = tile[32 * b + 2 * i + 1][j];
-            w[i] = lo | (hi << 16);
-            m = max(m, max(lo & 0x7FFFu, hi & 0x7FFFu));
+    for (int j = 0; j < 8; j++) {
+        const uint32_t c = scale_code((m[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+        const float sc = cvt_scale(c);
+        // bytes 0,1 (column j even) or 2,3 (odd) of the row pair's words
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const uint4 &a = v[4 * k], &b = v[4 * k + 1], &cc = v[4 * k + 2], &d = v[4 * k + 3];
+            const int wi = j >> 1;
+            const uint32_t wa = wi == 0 ? a.x : wi == 1 ? a.y : wi == 2 ? a.z : a.w;
+            const uint32_t wb = wi == 0 ? b.x : wi == 1 ? b.y : wi == 2 ? b.z : b.w;
+            const uint32_t wc = wi == 0 ? cc.x : wi == 1 ? cc.y : wi == 2 ? cc.z : cc.w;
+            const uint32_t wd = wi == 0 ? d.x : wi == 1 ? d.y : wi == 2 ? d.z : d.w;
+            const uint32_t p01 = __builtin_amdgcn_perm(wb, wa, sel);  // rows 4k, 4k+1
+            const uint32_t p23 = __builtin_amdgcn_perm(wd, wc, sel);  // rows 4k+2, 4k+3
+            o[k] = nan_block_select(cvt_x4(p01, p23, sc), c);
         }
-        uint32_t c = scale_code(m);
-        uint32_t o[8];
-        if (c == 0xFFu) {
-#pragma unroll
-            for (int i = 0; i < 8; i++)
-                o[i] = 0x7F7F7F7Fu;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; i++)
-                o[i] = e4m3_pair(w[2 * i], (int)c) | (e4m3_pair(w[2 * i + 1], (int)c) << 16);
-        }
-        uint4 *dst = reinterpret_cast<uint4 *>(qrow + 32 * b);
-        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-        srow[b] = (uint8_t)c;
+        *reinterpret_cast<uint4 *>(qt + (c0 + j) * ld_qt + r0) = make_uint4(o[0], o[1], o[2], o[3]);
+        if (half == 0)
+            st[(c0 + j) * ld_st + (r0 >> 5)] = (uint8_t)c;
     }
 }
 
@@ -212,11 +217,11 @@ hipError_t launch_quantize_colwise(const void *x, int64_t rows, int64_t cols, in
                                    void *qt, int64_t ld_qt, void *st, int64_t ld_st,
                                    hipStream_t stream)
 {
-    int64_t tiles_r = (rows + QC_ROWS - 1) / QC_ROWS;
-    int64_t tiles_c = (cols + QC_COLS - 1) / QC_COLS;
-    hipLaunchKernelGGL(quantize_colwise_kernel, dim3((unsigned)(tiles_r * tiles_c)),
-                       dim3(QC_THREADS), 0, stream, (const uint16_t *)x, rows, cols, ld_x,
-                       (uint8_t *)qt, ld_qt, (uint8_t *)st, ld_st, tiles_c);
+    const int64_t tiles_c = (cols + QC_TILE_C - 1) / QC_TILE_C;
+    const int64_t blocks = ((rows + QC_TILE_R - 1) / QC_TILE_R) * tiles_c;
+    hipLaunchKernelGGL(quantize_colwise_kernel, dim3((unsigned)blocks), dim3(QC_THREADS), 0,
+                       stream, (const uint16_t *)x, rows, cols, ld_x, (uint8_t *)qt, ld_qt,
+                       (uint8_t *)st, ld_st, tiles_c);
     return hipGetLastError();
 }
 

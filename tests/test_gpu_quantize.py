@@ -58,25 +58,58 @@ def _exhaustive_blocks():
     return np.concatenate(rows, 0)
 
 
-def test_exhaustive_encoder_table_on_device(gpu_lib):
-    """All reachable (BF16 element, scale code) pairs: ~16 M elements."""
-    mx = gpu_lib
-    blocks = _exhaustive_blocks()            # [nblk][32]
+def _assert_codes(got: torch.Tensor, ref: np.ndarray, x: np.ndarray, what: str):
+    g = got.cpu().numpy()
+    bad = np.argwhere(g != ref)
+    assert bad.size == 0, (f"{what}: {len(bad)} mismatches, first at {tuple(bad[0])}: "
+                           f"x={x[tuple(bad[0])]:#06x} got {g[tuple(bad[0])]:#04x} "
+                           f"ref {ref[tuple(bad[0])]:#04x}")
+
+
+def _blocks_to_matrix(blocks: np.ndarray) -> np.ndarray:
+    """[nblk][32] -> [R][2048] (64 blocks per row, R a multiple of 8, zero padded)."""
     nblk = blocks.shape[0]
-    rows = 64
-    nrow_blocks = (nblk + rows - 1) // rows
-    x = np.zeros((nrow_blocks * rows, 32), np.uint16)
+    R = -(-nblk // 64)
+    R = -(-R // 8) * 8
+    x = np.zeros((R * 64, 32), np.uint16)
     x[:nblk] = blocks
-    x = x.reshape(nrow_blocks, rows * 32)    # row-major: each row holds 64 blocks
+    return x.reshape(R, 2048)
+
+
+def _check_both_orientations(mx, x: np.ndarray, what: str):
+    """Row-wise on x, and column-wise on x^T, whose column blocks are the row blocks of x."""
     q, s = mx.mx_quantize_rowwise(bf16_dev(mxsynth.from_bits(x)))
     oq, os_ = oracle.quantize_rowwise(x)
-    gq = q.cpu().numpy()
-    bad = np.argwhere(gq != oq)
-    assert bad.size == 0, f"{len(bad)} code mismatches, first at {bad[0]}: " \
-                          f"x={x[tuple(bad[0])]:#06x} got {gq[tuple(bad[0])]:#04x} " \
-                          f"ref {oq[tuple(bad[0])]:#04x}"
-    assert np.array_equal(s.cpu().numpy(), os_)
+    _assert_codes(q, oq, x, what + " rowwise codes")
+    _assert_codes(s, os_, np.zeros_like(os_, np.uint16), what + " rowwise scales")
+    xt = np.ascontiguousarray(x.T)
+    qt, st = mx.mx_quantize_colwise(bf16_dev(mxsynth.from_bits(xt)))
+    oqt, ost = oracle.quantize_colwise(xt)
+    _assert_codes(qt, oqt, x, what + " colwise codes")
+    _assert_codes(st, ost, np.zeros_like(ost, np.uint16), what + " colwise scales")
+    return os_
+
+
+def test_exhaustive_encoder_table_on_device(gpu_lib):
+    """All reachable (BF16 element, scale code) pairs, ~9 M elements, both kernels."""
+    x = _blocks_to_matrix(_exhaustive_blocks())
+    os_ = _check_both_orientations(gpu_lib, x, "exhaustive")
     assert set(np.unique(os_).tolist()) == set(range(0, 247))
+
+
+def test_every_block_maximum(gpu_lib):
+    """Every magnitude pattern 0..0x7FFF as a block maximum (NaN and Inf included),
+    at a position and sign that vary with the pattern; the other elements are
+    smaller magnitudes of alternating sign."""
+    p = np.arange(0x8000, dtype=np.int64)
+    i = np.arange(32, dtype=np.int64)
+    blocks = (p[:, None] * i[None, :]) // 32                       # magnitudes below p
+    blocks[p, p % 32] = p                                          # the maximum itself
+    sign = ((p[:, None] + i[None, :]) & 1) << 15
+    x = _blocks_to_matrix((blocks | sign).astype(np.uint16))
+    os_ = _check_both_orientations(gpu_lib, x, "block maxima")
+    assert (os_ == 0xFF).sum() == 0x8000 - 0x7F80                  # every Inf/NaN block
+    assert (os_ == 0).sum() >= 8 << 7                              # all tiny maxima clamp to 0
 
 
 @pytest.mark.parametrize("rows,cols", [(1, 32), (3, 96), (128, 256), (257, 4096), (33, 12288)])
