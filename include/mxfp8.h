@@ -161,7 +161,11 @@ mx_status mx_scale_swizzle(const void *s, int64_t rows, int64_t kblocks, int64_t
  * MX_ERR_UNSUPPORTED); M, N >= 0 arbitrary; a_q, b_q 16-byte aligned with
  * ld_a % 16 == 0, ld_b % 16 == 0; scale buffers 4-byte aligned; c aligned to
  * its element size (else MX_ERR_ALIGN); ld_a, ld_b >= K, ld_c >= N; c must
- * not overlap an input.  No split-K: each output is one FP32 accumulation.
+ * not overlap an input.  Offsets inside a 256-row tile and inside a
+ * rearranged scale buffer are 32-bit: 256 * ld_a, 256 * ld_b and
+ * 256 * ld_c * (element size of C) must stay below 2^31 and each rearranged
+ * scale buffer below 4 GiB (else MX_ERR_UNSUPPORTED).  No split-K: each
+ * output is one FP32 accumulation.
  */
 mx_status mx_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t ld_a,
                   const void *a_s_swz, const void *b_q, int64_t ld_b, const void *b_s_swz,

@@ -204,9 +204,10 @@ static mx_status check_gemm_common(const char *fn, int64_t M, int64_t N, int64_t
                     "%s: operands need 16-byte aligned rows, scales 4-byte alignment, C its "
                     "element size",
                     fn);
-    // Row offsets inside a 256-row tile and offsets into a rearranged scale
-    // buffer are formed in 32 bits.
-    if ((int64_t)256 * ld_a >= ((int64_t)1 << 31) || (int64_t)256 * ld_b >= ((int64_t)1 << 31))
+    // Row offsets inside a 256-row tile (of A, B and C) and offsets into a
+    // rearranged scale buffer are formed in 32 bits.
+    if ((int64_t)256 * ld_a >= ((int64_t)1 << 31) || (int64_t)256 * ld_b >= ((int64_t)1 << 31) ||
+        (int64_t)256 * ld_c * (int64_t)ce >= ((int64_t)1 << 31))
         return fail(MX_ERR_UNSUPPORTED, "%s: leading dimension too large for this build", fn);
     if (swz_bytes(M, K / 32) >= ((int64_t)1 << 32) || swz_bytes(N, K / 32) >= ((int64_t)1 << 32))
         return fail(MX_ERR_UNSUPPORTED, "%s: operand too large for this build", fn);

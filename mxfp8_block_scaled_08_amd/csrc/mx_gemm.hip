@@ -45,6 +45,8 @@
 #include "mx_device.h"
 #include "mx_launch.h"
 
+#include <algorithm>
+
 namespace mx {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -53,7 +55,6 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int GM_THREADS = 256;
 constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int STAGES = 2;
 constexpr int TM = 4, TN = 4;      // 32x32 sub-tiles per wave along M and N
 constexpr int GROUP_M = 4;         // tile-rows walked together for L2 reuse
 constexpr int STAGE_BYTES = BM * BK;  // one operand, one stage (32 KiB)
@@ -79,13 +80,12 @@ struct GemmParams {
 
 __device__ __forceinline__ int chunk_perm(int row) { return (row >> 1) & 7; }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+// Two FP32 -> packed BF16 (low half first), round to nearest even: one
+// v_cvt_pk_bf16_f32 on this target (NaN stays NaN).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
-        return 0x7FC0u;
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t{lo, hi}), bf16x2_t));
 }
 
 typedef const void __attribute__((address_space(1))) *gptr_t;
@@ -93,11 +93,31 @@ typedef void __attribute__((address_space(3))) *lptr_t;
 
 // Buffer resource for a byte range: uniform base and size in SGPRs, so each
 // lane supplies only a 32-bit offset.  Word 3 selects 32-bit data format
-// (what untyped buffer loads on gfx9-family targets expect).  Loads whose
-// per-lane offset falls outside the range return zeros instead of faulting.
+// (what untyped buffer loads on gfx9-family targets expect).  Accesses whose
+// per-lane offset falls outside the range read zero or are dropped.  Callers
+// pass values that every lane holds alike; reading them from the first lane
+// says so to the compiler, which would otherwise wrap each access in a loop
+// over the distinct values it cannot rule out.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void *base, uint32_t bytes)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    void *ub = (void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, 0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                             0x00020000);
+}
+
+// Values every lane holds alike, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform(int64_t x)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+template <typename T> __device__ __forceinline__ const T *uniform(const T *x)
+{
+    return reinterpret_cast<const T *>(uniform((int64_t)(uintptr_t)x));
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -117,111 +137,218 @@ __device__ __forceinline__ void lds_ring_barrier()
     asm volatile("s_barrier" ::: "memory");
 }
 
+// Coordinates of one 256x256 output tile.
+struct Tile {
+    int64_t m0, n0, m_end;
+    const uint8_t *b, *bs;  // B operand and its rearranged scales (per expert when grouped)
+};
+
+constexpr int GROUP_TABLE = 1024;  // experts whose tile table fits in LDS
+
 template <bool GROUPED, int CT>
 __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t sA[STAGES][STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t sB[STAGES][STAGE_BYTES];
-    // per wave: the TM + TN scale words of each lane for one 256-K group
-    __shared__ __attribute__((aligned(1024))) uint32_t sS[4][TM + TN][64];
-    __shared__ int64_t s_grp[3];
+    __shared__ __attribute__((aligned(1024))) uint8_t sA[2][STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sB[2][STAGE_BYTES];
+    // per wave: the 32-row scale tiles of one 256-K group that hold its A rows
+    // (up to five: 2 KiB) and B rows (four: 1 KiB)
+    __shared__ __attribute__((aligned(1024))) uint8_t sS[4][3072];
+    // grouped: per expert g, its first m-tile number and its clamped row range
+    __shared__ int s_pref[GROUPED ? GROUP_TABLE + 1 : 1];
+    __shared__ int s_lo[GROUPED ? GROUP_TABLE : 1], s_hi[GROUPED ? GROUP_TABLE : 1];
+    __shared__ int s_wsum[4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
+    const int h = lane >> 5;
+    const int r32 = lane & 31;
+    const int64_t N = p.N;
+    const int64_t KT256 = (p.K + 255) / 256;  // scale words per 32-row tile
+    const int KIT = (int)(p.K / BK);
+    const int KITP = (KIT + 1) & ~1;  // stages per tile, padded to whole 256-K groups
 
-    int64_t m0, n0, m_end;
-    const uint8_t *B = p.b;
-    const uint8_t *BS = p.bs;
-
+    // ---- tile enumeration
+    const bool table = !GROUPED || (p.G <= GROUP_TABLE && p.M < ((int64_t)1 << 31));
+    int64_t ntiles;
     if (!GROUPED) {
-        int64_t pid = blockIdx.x;
-        const int64_t num = gridDim.x;
-        // consecutive workgroups are dealt to the 8 XCDs in turn: renumber so
-        // each XCD walks a contiguous range of tiles (shared L2 panels)
-        if ((num & 7) == 0)
-            pid = (pid & 7) * (num >> 3) + (pid >> 3);
-        const int64_t per_group = GROUP_M * p.tiles_n;
-        const int64_t grp = pid / per_group;
-        const int64_t first_m = grp * GROUP_M;
-        const int64_t gm = min(p.tiles_m - first_m, (int64_t)GROUP_M);
-        const int64_t in = pid - grp * per_group;
-        m0 = (first_m + in % gm) * BM;
-        n0 = (in / gm) * BN;
-        m_end = p.M;
+        ntiles = p.tiles_m * p.tiles_n;
+    } else if (table) {
+        // each thread takes a contiguous run of experts; block-wide exclusive
+        // scan of their m-tile counts (ceil(rows / BM))
+        const int G = (int)p.G;
+        const int per = (G + GM_THREADS - 1) / GM_THREADS;
+        const int g0 = tid * per, g1 = min(g0 + per, G);
+        int sum = 0;
+        for (int g = g0; g < g1; g++) {
+            const int64_t lo = min(max(p.offsets[g], (int64_t)0), p.M);
+            const int64_t hi = min(max(p.offsets[g + 1], lo), p.M);
+            s_lo[g] = (int)lo;
+            s_hi[g] = (int)hi;
+            sum += (int)((hi - lo + BM - 1) / BM);
+        }
+        int incl = sum;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int o = __shfl_up(incl, d, 64);
+            if (lane >= d)
+                incl += o;
+        }
+        if (lane == 63)
+            s_wsum[wave] = incl;
+        __syncthreads();
+        int run = incl - sum;
+        for (int w = 0; w < wave; w++)
+            run += s_wsum[w];
+        for (int g = g0; g < g1; g++) {
+            s_pref[g] = run;
+            run += (s_hi[g] - s_lo[g] + BM - 1) / BM;
+        }
+        if (tid == GM_THREADS - 1)
+            s_pref[G] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+        __syncthreads();
+        ntiles = (int64_t)s_pref[G] * p.tiles_n;
     } else {
-        // tile (m-tile id, n-tile): find the expert whose rows hold m-tile id
-        const int64_t mt_id = blockIdx.x / p.tiles_n;
-        const int64_t tn = blockIdx.x - mt_id * p.tiles_n;
-        n0 = tn * BN;
-        if (wave == 0) {
-            int64_t running = 0;
-            for (int64_t g0 = 0; g0 < p.G; g0 += 64) {
-                const int64_t g = g0 + lane;
+        // too many experts for the table: count with a wave-wide scan over
+        // global memory (every wave computes the same total)
+        int64_t run = 0;
+        for (int64_t gb = 0; gb < p.G; gb += 64) {
+            const int64_t g = gb + lane;
+            int64_t cnt = 0;
+            if (g < p.G) {
+                const int64_t lo = min(max(p.offsets[g], (int64_t)0), p.M);
+                const int64_t hi = min(max(p.offsets[g + 1], lo), p.M);
+                cnt = (hi - lo + BM - 1) / BM;
+            }
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int64_t o = __shfl_xor(cnt, d, 64);
+                cnt += o;
+            }
+            run += cnt;
+        }
+        ntiles = run * p.tiles_n;
+    }
+    // Workgroups are dealt to the 8 XCDs in turn (workgroup b runs on XCD
+    // b % 8), and each XCD has its own L2: give XCD x a contiguous eighth of
+    // the tiles, walked by its workgroups in step, so that tiles running
+    // together on one XCD share A and B panels.
+    int64_t t_first, t_step, t_end;
+    if (gridDim.x % 8 == 0) {
+        const int64_t x = blockIdx.x & 7, per_xcd = (ntiles + 7) / 8;
+        t_first = x * per_xcd + (blockIdx.x >> 3);
+        t_step = gridDim.x >> 3;
+        t_end = min((x + 1) * per_xcd, ntiles);
+    } else {
+        t_first = blockIdx.x;
+        t_step = gridDim.x;
+        t_end = ntiles;
+    }
+    const int64_t my_tiles = t_first < t_end ? (t_end - t_first + t_step - 1) / t_step : 0;
+    if (my_tiles == 0)
+        return;
+
+    // tile number -> coordinates
+    int g_cur = 0;  // grouped: experts are met in increasing order
+    auto coords = [&](int64_t pid) -> Tile {
+        Tile c;
+        if (!GROUPED) {
+            const int64_t per_group = GROUP_M * p.tiles_n;
+            const int64_t grp = pid / per_group;
+            const int64_t first_m = grp * GROUP_M;
+            const int64_t gm = min(p.tiles_m - first_m, (int64_t)GROUP_M);
+            const int64_t in = pid - grp * per_group;
+            c.m0 = (first_m + in % gm) * BM;
+            c.n0 = (in / gm) * BN;
+            c.m_end = p.M;
+            c.b = p.b;
+            c.bs = p.bs;
+            return c;
+        }
+        const int64_t mt = pid / p.tiles_n;
+        c.n0 = (pid - mt * p.tiles_n) * BN;
+        int64_t g;
+        if (table) {
+            // first expert whose tiles end beyond mt, searching forward from
+            // the last one found (a workgroup's tiles come in increasing
+            // order); pid < ntiles guarantees a hit, and the loop is bounded
+            // either way
+            const int G = (int)p.G;
+            if ((int64_t)s_pref[g_cur] > mt)
+                g_cur = 0;
+            int found = -1;
+            for (int gb = g_cur; gb < G && found < 0; gb += 64) {
+                const int gg = gb + lane;
+                const uint64_t m = __ballot(gg < G && (int64_t)s_pref[gg + 1] > mt);
+                if (m)
+                    found = gb + __builtin_ctzll(m);
+            }
+            g_cur = found < 0 ? G - 1 : found;
+            g = g_cur;
+            c.m0 = s_lo[g] + (mt - s_pref[g]) * BM;
+            c.m_end = s_hi[g];
+        } else {
+            int64_t run = 0;
+            g = -1;
+            for (int64_t gb = 0; gb < p.G && g < 0; gb += 64) {
+                const int64_t gg = gb + lane;
                 int64_t lo = 0, hi = 0;
-                if (g < p.G) {
-                    lo = min(max(p.offsets[g], (int64_t)0), p.M);
-                    hi = min(max(p.offsets[g + 1], lo), p.M);
+                if (gg < p.G) {
+                    lo = min(max(p.offsets[gg], (int64_t)0), p.M);
+                    hi = min(max(p.offsets[gg + 1], lo), p.M);
                 }
                 const int64_t cnt = (hi - lo + BM - 1) / BM;
                 int64_t incl = cnt;
 #pragma unroll
                 for (int d = 1; d < 64; d <<= 1) {
-                    int64_t o = __shfl_up(incl, d, 64);
+                    const int64_t o = __shfl_up(incl, d, 64);
                     if (lane >= d)
                         incl += o;
                 }
-                const int64_t excl = running + incl - cnt;
-                if (cnt > 0 && mt_id >= excl && mt_id < excl + cnt) {
-                    s_grp[0] = g;
-                    s_grp[1] = lo + (mt_id - excl) * BM;
-                    s_grp[2] = hi;
+                const int64_t excl = run + incl - cnt;
+                const uint64_t m = __ballot(cnt > 0 && mt >= excl && mt < excl + cnt);
+                if (m) {
+                    const int src = __builtin_ctzll(m);
+                    g = gb + src;
+                    c.m0 = __shfl(lo + (mt - excl) * BM, src, 64);
+                    c.m_end = __shfl(hi, src, 64);
                 }
-                running += __shfl(incl, 63, 64);
+                run += __shfl(incl, 63, 64);
             }
-            if (lane == 0 && mt_id >= running)
-                s_grp[0] = -1;
         }
-        __syncthreads();
-        const int64_t g = s_grp[0];
-        if (g < 0)
-            return;
-        m0 = s_grp[1];
-        m_end = s_grp[2];
-        B = p.b + g * p.b_group_stride;
-        BS = p.bs + g * p.bs_group_stride;
-    }
-
-    const int64_t N = p.N;
-    const int64_t KT256 = (p.K + 255) / 256;  // scale words per 32-row tile
-    const int KIT = (int)(p.K / BK);
+        c.m0 = uniform(c.m0);
+        c.m_end = uniform(c.m_end);
+        g = uniform(g);
+        c.b = p.b + g * p.b_group_stride;
+        c.bs = p.bs + g * p.bs_group_stride;
+        return c;
+    };
 
     // ---- direct-to-LDS plan.  Instruction i of this wave fills LDS rows
     // 8*(8*wave + i) .. +8 of a stage; lane -> row + lane/8, slot lane%8,
-    // fetching global chunk slot ^ perm(row) of that row.
-    const uint8_t *a_tile = p.a + m0 * p.ld_a;
-    const uint8_t *b_tile = B + n0 * p.ld_b;
-    const uint32_t a_tile_bytes = (uint32_t)(min(m_end - m0, (int64_t)BM) * p.ld_a);
-    const uint32_t b_tile_bytes = (uint32_t)(min(N - n0, (int64_t)BN) * p.ld_b);
+    // fetching global chunk slot ^ perm(row) of that row.  Rows past the
+    // operand (or past the expert, which are never stored) need no clamp:
+    // the tile's buffer range ends at the operand's last row and reads
+    // beyond it return zero.
     uint32_t a_src[DMA_PER_WAVE], b_src[DMA_PER_WAVE];
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; i++) {
         const int row = 8 * (DMA_PER_WAVE * wave + i) + (lane >> 3);
         const int chunk = (lane & 7) ^ chunk_perm(row);
-        const int64_t ra = min(m0 + row, m_end - 1) - m0;
-        const int64_t rb = min(n0 + row, N - 1) - n0;
-        a_src[i] = (uint32_t)(ra * p.ld_a + chunk * 16);
-        b_src[i] = (uint32_t)(rb * p.ld_b + chunk * 16);
+        a_src[i] = (uint32_t)(row * p.ld_a + chunk * 16);
+        b_src[i] = (uint32_t)(row * p.ld_b + chunk * 16);
     }
     const uint32_t lds_a0 = (uint32_t)(uintptr_t)&sA[0][0];
     const uint32_t lds_b0 = (uint32_t)(uintptr_t)&sB[0][0];
-    // Loads of stage st into buffer buf.  A stage past the end (live false)
-    // gets an empty range: its loads move no data and write zeros into a
-    // buffer nobody reads again, which keeps the main loop branch-free.
-    auto dma_stage = [&](int st, int buf, bool live) {
-        const __amdgpu_buffer_rsrc_t ra = byte_range(a_tile, live ? a_tile_bytes : 0u);
-        const __amdgpu_buffer_rsrc_t rb = byte_range(b_tile, live ? b_tile_bytes : 0u);
+    // Loads of stage st of tile T into buffer buf.  A stage past the end or a
+    // padding stage (live false) gets an empty range: its loads move no data
+    // and write zeros, which keeps the main loop branch-free.
+    auto dma_stage = [&](const Tile &T, int st, int buf, bool live) {
+        const uint32_t ab = (uint32_t)(min(p.M - T.m0, (int64_t)BM) * p.ld_a);
+        const uint32_t bb = (uint32_t)(min(N - T.n0, (int64_t)BN) * p.ld_b);
+        const __amdgpu_buffer_rsrc_t ra = byte_range(p.a + T.m0 * p.ld_a, live ? ab : 0u);
+        const __amdgpu_buffer_rsrc_t rb = byte_range(T.b + T.n0 * p.ld_b, live ? bb : 0u);
         const uint32_t koff = (uint32_t)st * BK;  // scalar offset, added after the range check
 #pragma unroll
         for (int i = 0; i < DMA_PER_WAVE; i++) {
@@ -233,46 +360,48 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
         }
     };
 
-    // ---- per-lane scale words.  The lane's row is r32 within every 32-row
-    // sub-tile; sub-tiles are 32 rows apart, i.e. one scale tile (KT256 * 256
-    // bytes) apart.  Each 256-K group's words travel through LDS: one 4-byte
-    // direct-to-LDS load per sub-tile puts lane l's word at word l of the
-    // wave's region, and the lane reads it back when the group starts.  Rows
-    // past the operand fall outside the resource's range and read zero.
-    const int h = lane >> 5;
-    const int r32 = lane & 31;
-    uint32_t sa_off[TM], sb_off[TN];
-#pragma unroll
-    for (int i = 0; i < TM; i++) {
-        const int64_t row = m0 + wm * 128 + i * 32 + r32;
-        sa_off[i] = (uint32_t)((row >> 5) * KT256 * 256 + (h * 32 + (row & 31)) * 4);
-    }
-#pragma unroll
-    for (int i = 0; i < TN; i++) {
-        const int64_t row = n0 + wn * 128 + i * 32 + r32;
-        sb_off[i] = (uint32_t)((row >> 5) * KT256 * 256 + (h * 32 + (row & 31)) * 4);
-    }
-    const uint32_t lds_s0 = (uint32_t)(uintptr_t)&sS[wave][0][0];
-    auto dma_scales = [&](int group, bool live) {
-        const __amdgpu_buffer_rsrc_t rsa = byte_range(p.as, live ? p.as_bytes : 0u);
-        const __amdgpu_buffer_rsrc_t rsb = byte_range(BS, live ? p.bs_bytes : 0u);
-        const uint32_t kw = (uint32_t)group * 256;
-#pragma unroll
-        for (int i = 0; i < TM; i++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lptr_t)(uintptr_t)(lds_s0 + 256 * i), 4,
-                                                     sa_off[i], kw, 0, 0);
-#pragma unroll
-        for (int i = 0; i < TN; i++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lptr_t)(uintptr_t)(lds_s0 + 256 * (TM + i)),
-                                                     4, sb_off[i], kw, 0, 0);
+    // ---- scale words.  A group's word for a row sits in the row's 32-row
+    // scale tile (256 bytes per tile and group; tiles KT256 * 256 bytes
+    // apart).  The wave's 128 A rows lie in at most five consecutive tiles
+    // (four when the tile's first row is a multiple of 32, always so for B),
+    // so three 16-byte-per-lane direct-to-LDS loads bring a group's words:
+    // lane l fetches 16 bytes of tile l / 16 (the second A load covers tile 4
+    // with lanes 0-15; the other lanes are out of range and write zeros).
+    // The lane then reads its own word of sub-tile i from LDS at a per-tile
+    // base plus i * 256.  Rows past the operand fall outside the resource's
+    // range and read zero.
+    const uint32_t lds_s = (uint32_t)(uintptr_t)&sS[wave][0];
+    const int64_t stile = KT256 * 256;  // bytes per 32-row scale tile
+    const uint32_t s_v4 = (uint32_t)((lane >> 4) * stile + (lane & 15) * 16);
+    const uint32_t s_v1 = lane < 16 ? (uint32_t)(4 * stile + lane * 16) : 0xFFFFFFF0u;
+    // offset of the lane's A word of sub-tile 0 in the wave's region for
+    // tile T (sub-tile i adds i * 256; B words sit at 2048 + i * 256 + lane * 4)
+    auto scale_lanes = [&](const Tile &T) -> uint32_t {
+        const int x = (int)(T.m0 & 31) + r32;
+        return (uint32_t)((x >> 5) * 256 + (h * 32 + (x & 31)) * 4);
     };
-    auto read_scales = [&](uint32_t *xa, uint32_t *xb) {
+    auto dma_scales = [&](const Tile &T, int group, bool live) {
+        const int64_t a_base = ((T.m0 + wm * 128) >> 5) * stile;
+        const int64_t b_base = ((T.n0 + wn * 128) >> 5) * stile;
+        const uint32_t a_bytes = live && a_base < p.as_bytes ? (uint32_t)(p.as_bytes - a_base) : 0u;
+        const uint32_t b_bytes = live && b_base < p.bs_bytes ? (uint32_t)(p.bs_bytes - b_base) : 0u;
+        const __amdgpu_buffer_rsrc_t rsa = byte_range(p.as + (live ? a_base : 0), a_bytes);
+        const __amdgpu_buffer_rsrc_t rsb = byte_range(T.bs + (live ? b_base : 0), b_bytes);
+        const uint32_t kw = (uint32_t)group * 256;  // scalar offset, within the row's scale tile
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lptr_t)(uintptr_t)lds_s, 16, s_v4, kw, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lptr_t)(uintptr_t)(lds_s + 1024), 16, s_v1,
+                                                 kw, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lptr_t)(uintptr_t)(lds_s + 2048), 16, s_v4,
+                                                 kw, 0, 0);
+    };
+    constexpr int SCALE_LOADS = 3;
+    auto read_scales = [&](uint32_t a_rd_s, uint32_t *xa, uint32_t *xb) {
 #pragma unroll
         for (int i = 0; i < TM; i++)
-            xa[i] = sS[wave][i][lane];
+            xa[i] = *reinterpret_cast<const uint32_t *>(&sS[wave][a_rd_s + i * 256]);
 #pragma unroll
         for (int i = 0; i < TN; i++)
-            xb[i] = sS[wave][TM + i][lane];
+            xb[i] = *reinterpret_cast<const uint32_t *>(&sS[wave][2048 + i * 256 + lane * 4]);
     };
 
     // ---- per-lane LDS read offsets of the matrix-core fragments.  At step
@@ -280,8 +409,8 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     // operand) and chunk 4s + 2 + h (bytes 16-31) of its row.  Rows of the
     // sub-tiles are 32 apart, which leaves chunk_perm unchanged, and the chunk
     // bits are disjoint, so the four chunks sit at the step-0 offset XOR
-    // 64s + 32t.  One register per (s, t) and operand; sub-tile and buffer
-    // are immediate offsets of the LDS read.
+    // 64s + 32t.  One register per (s, t) and operand; the sub-tile is an
+    // immediate offset of the LDS read.
     uint32_t a_rd[4], b_rd[4];
     {
         const uint32_t la0 = (uint32_t)((wm * 128 + r32) * BK + ((h ^ chunk_perm(r32)) * 16));
@@ -292,16 +421,6 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             b_rd[x] = lb0 ^ (32u * x);
         }
     }
-
-    v16f acc[TN][TM];
-#pragma unroll
-    for (int i = 0; i < TN; i++)
-#pragma unroll
-        for (int j = 0; j < TM; j++)
-#pragma unroll
-            for (int v = 0; v < 16; v++)
-                acc[i][j][v] = 0.0f;
-
     auto read_frags = [&](int buf, int step, v8i *xa, v8i *xb) {
         const uint8_t *A_ = &sA[buf][0];
         const uint8_t *B_ = &sB[buf][0];
@@ -319,119 +438,221 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
         }
     };
 
-    // ---- prologue: scale words of the first 256 K, stages 0 and 1 in flight
-    dma_scales(0, true);
-    dma_stage(0, 0, true);
-    dma_stage(1, 1, KIT > 1);
+    v16f acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; i++)
+#pragma unroll
+        for (int j = 0; j < TM; j++)
+#pragma unroll
+            for (int v = 0; v < 16; v++)
+                acc[i][j][v] = 0.0f;
+
+    // per-lane offsets of C within a tile: row wm*128 + j*32 + r32, columns
+    // from wn*128 + 4h (the sub-tile and register group add immediates)
+    constexpr int CE = CT == 0 ? 2 : 4;  // bytes per C element
+    uint32_t c_off[TM];
+#pragma unroll
+    for (int j = 0; j < TM; j++)
+        c_off[j] = (uint32_t)(((wm * 128 + j * 32 + r32) * p.ld_c + wn * 128 + 4 * h) * CE);
+
+    // ---- the workgroup's stages: tiles t_first, + t_step, ..., KITP
+    // stages each, numbered continuously so the pipeline runs across tiles
+    const int64_t total = my_tiles * KITP;
+    Tile cur = coords(t_first);
+    uint32_t cur_srd = scale_lanes(cur);
+
+    // prologue: scale words of the first group, stages 0 and 1 in flight
+    dma_scales(cur, 0, true);
+    dma_stage(cur, 0, 0, true);
+    dma_stage(cur, 1, 1, 1 < KIT);
     MX_WAIT_VMCNT(2 * DMA_PER_WAVE);  // stage 1's loads may still be in flight
     lds_ring_barrier();
     uint32_t wa[TM], wb[TN];
-    read_scales(wa, wb);
+    read_scales(cur_srd, wa, wb);
     v8i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
     read_frags(0, 0, fa0, fb0);
 
-#define MX_MFMA_STEP(FA, FB, SHIFT)                                                          \
-    _Pragma("unroll") for (int i = 0; i < TN; i++) {                                         \
+#define MX_MFMA_STEP(FA, FB, SHIFT, I0, I1)                                                  \
+    _Pragma("unroll") for (int i = (I0); i < (I1); i++) {                                    \
         const int sbv = (int)(wb[i] >> (SHIFT));                                             \
         _Pragma("unroll") for (int j = 0; j < TM; j++)                                       \
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                     \
                 FB[i], FA[j], acc[i][j], 0, 0, 0, sbv, 0, (int)(wa[j] >> (SHIFT)));          \
     }
 
-    // Stage st uses buffer st & 1 and scale bytes 2*(st & 1) and 2*(st & 1) + 1
-    // of the current 256-K words.  On entry the step-0 fragments are in
-    // fa0/fb0.  First half: read step 1's fragments while step 0 runs (one
-    // LDS read between consecutive matrix-core instructions).  Then wait until
-    // this wave's loads of stage st+1 have landed and every wave is done with
-    // buffer st & 1.  Second half, while step 1 runs: read the scale words
-    // staged in LDS, issue the loads of stage st+2 into buffer st & 1 (after
-    // the scale words of group (st+2)/2), and read stage st+1's step-0
-    // fragments from the other buffer.  The scale words read on a group's
-    // last stage (odd st) belong to the next group and replace the current
-    // ones; on an even stage the read races the new loads and is discarded.
+    // Stage gs uses buffer gs & 1 and scale bytes 2*(gs & 1) and 2*(gs & 1)+1
+    // of the current 256-K words (a tile has an even number of stages, so
+    // parity within the tile and overall agree).  On entry the step-0
+    // fragments are in fa0/fb0 and the loads of stage gs+1 are in flight.
+    //   1. Step 0 runs while step 1's fragments are read (one LDS read
+    //      between consecutive matrix-core instructions).
+    //   2. Barrier: every wave is done with buffer gs & 1.  Half of step 1
+    //      runs while the loads of stage gs+2 (and the scale words of its
+    //      group) are issued into that buffer.
+    //   3. Wait until this wave's loads of stage gs+1 have landed (all but
+    //      the loads just issued: vector-memory operations retire in issue
+    //      order) and barrier, so every wave's have.  The other half of step
+    //      1 runs while stage gs+1's step-0 fragments and the scale words of
+    //      the next group are read.  Those words are kept on a group's last
+    //      stage (odd gs), when they belong to the group of stage gs+1; on
+    //      an even stage they are being rewritten and are discarded.  An odd
+    //      stage reloads the words of its own group, which leaves the bytes
+    //      unchanged.
     // Past the end the loads are empty and the fragment reads unused, so the
-    // body has no branches and the interleaving below applies to all of it.
-    for (int st = 0; st < KIT; st++) {
-        const int buf = st & 1;
-        const int shift = 16 * buf;
-        read_frags(buf, 1, fa1, fb1);
-        MX_MFMA_STEP(fa0, fb0, shift)
+    // body has no branches.  After a tile's last stage its accumulators are
+    // stored and cleared.
+    int64_t gs = 0;  // stages run so far (all tiles)
+    for (int64_t k = 0; k < my_tiles; k++) {
+        // the tile after this one (loaded during this tile's last two stages)
+        const Tile nxt = k + 1 < my_tiles ? coords(t_first + (k + 1) * t_step) : cur;
+        const uint32_t nxt_srd = scale_lanes(nxt);
+        for (int st = 0; st < KITP; st++, gs++) {
+            const int buf = (int)(gs & 1);
+            const int shift = 16 * buf;
+            // 1.
+            read_frags(buf, 1, fa1, fb1);
+            MX_MFMA_STEP(fa0, fb0, shift, 0, TN)
 #pragma unroll
-        for (int q = 0; q < TM * TN; q++) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // matrix core
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            for (int q = 0; q < TM * TN; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // matrix core
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            lds_ring_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            // 2. stage gs + 2: stage st + 2 of this tile, or the next tile's first two
+            const bool same = st + 2 < KITP;
+            const int st2 = same ? st + 2 : st + 2 - KITP;
+            const Tile ld = same ? cur : nxt;
+            const bool live = gs + 2 < total;
+            const bool live_group = ((gs + 2) & ~(int64_t)1) < total;  // the group's first stage
+            dma_scales(ld, st2 >> 1, live_group);
+            dma_stage(ld, st2, buf, live && st2 < KIT);
+            MX_MFMA_STEP(fa1, fb1, shift + 8, 0, TN / 2)
+#pragma unroll
+            for (int q = 0; q < 3; q++) {  // 8 matrix-core, 19 loads
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x010, 3, 1);
+            }
+#pragma unroll
+            for (int q = 0; q < 5; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x010, 2, 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // 3.
+            MX_WAIT_VMCNT(2 * DMA_PER_WAVE + SCALE_LOADS);
+            asm volatile("s_barrier" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            uint32_t na[TM], nb[TN];
+            read_scales(st + 1 < KITP ? cur_srd : nxt_srd, na, nb);
+            read_frags(buf ^ 1, 0, fa0, fb0);
+            MX_MFMA_STEP(fa1, fb1, shift + 8, TN / 2, TN)
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);  // scale words
+#pragma unroll
+            for (int q = 0; q < TM * TN / 2; q++) {  // 8 matrix-core, 16 LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // the selects wait for the words: keep them last
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+                wa[i] = buf ? na[i] : wa[i];
+#pragma unroll
+            for (int i = 0; i < TN; i++)
+                wb[i] = buf ? nb[i] : wb[i];
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        MX_WAIT_VMCNT(0);
-        lds_ring_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        uint32_t na[TM], nb[TN];
-        read_scales(na, nb);
-        const bool live = st + 2 < KIT;
-        dma_scales((st + 2) >> 1, live);
-        dma_stage(st + 2, buf, live);
-        read_frags(buf ^ 1, 0, fa0, fb0);
-        MX_MFMA_STEP(fa1, fb1, shift + 8)
-        __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 1);  // scale words
-#pragma unroll
-        for (int q = 0; q < TM * TN / 2; q++) {  // 16 matrix-core, 24 loads, 16 LDS reads
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x010, 2, 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x010, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-        }
-#pragma unroll
-        for (int i = 0; i < TM; i++)
-            wa[i] = buf ? na[i] : wa[i];
-#pragma unroll
-        for (int i = 0; i < TN; i++)
-            wb[i] = buf ? nb[i] : wb[i];
-    }
-    MX_WAIT_VMCNT(0);  // no load may still write LDS when the workgroup ends
-#undef MX_MFMA_STEP
 
-    // ---- epilogue: lane holds C[m][n..n+3] for each register group
+        // ---- epilogue: lane holds C[m][n..n+3] for each register group
+        if (p.vec_store && cur.n0 + BN <= N) {
+            // whole-width tile: buffer stores relative to the tile's first
+            // element; the range ends after the tile's last valid row, so the
+            // stores of rows past it (past M, or past the expert) are dropped
+            const uint32_t rows_valid = (uint32_t)min(cur.m_end - cur.m0, (int64_t)BM);
+            const __amdgpu_buffer_rsrc_t rc =
+                byte_range((const uint8_t *)p.c + (cur.m0 * p.ld_c + cur.n0) * CE,
+                           rows_valid * (uint32_t)(p.ld_c * CE));
 #pragma unroll
-    for (int i = 0; i < TN; i++) {
+            for (int i = 0; i < TN; i++) {
 #pragma unroll
-        for (int j = 0; j < TM; j++) {
-            const int64_t m = m0 + wm * 128 + j * 32 + r32;
-            if (m >= m_end)
-                continue;
+                for (int j = 0; j < TM; j++) {
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const int64_t n = n0 + wn * 128 + i * 32 + 8 * q + 4 * h;
-                const float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
-                const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-                if (CT == 0) {
-                    uint16_t *crow = reinterpret_cast<uint16_t *>(p.c) + m * p.ld_c;
-                    if (p.vec_store && n + 3 < N) {
-                        uint2 w;
-                        w.x = f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16);
-                        w.y = f32_to_bf16_rne(v2) | (f32_to_bf16_rne(v3) << 16);
-                        *reinterpret_cast<uint2 *>(crow + n) = w;
-                    } else {
-                        if (n + 0 < N) crow[n + 0] = (uint16_t)f32_to_bf16_rne(v0);
-                        if (n + 1 < N) crow[n + 1] = (uint16_t)f32_to_bf16_rne(v1);
-                        if (n + 2 < N) crow[n + 2] = (uint16_t)f32_to_bf16_rne(v2);
-                        if (n + 3 < N) crow[n + 3] = (uint16_t)f32_to_bf16_rne(v3);
+                    for (int q = 0; q < 4; q++) {
+                        const float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
+                        const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+                        const uint32_t off = c_off[j] + (uint32_t)((i * 32 + 8 * q) * CE);
+                        if (CT == 0) {
+                            typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+                            __builtin_amdgcn_raw_buffer_store_b64(
+                                u2_t{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)}, rc, off, 0, 0);
+                        } else {
+                            typedef float f4_t __attribute__((ext_vector_type(4)));
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                __builtin_bit_cast(v4i, f4_t{v0, v1, v2, v3}), rc, off, 0, 0);
+                        }
                     }
-                } else {
-                    float *crow = reinterpret_cast<float *>(p.c) + m * p.ld_c;
-                    if (p.vec_store && n + 3 < N) {
-                        *reinterpret_cast<float4 *>(crow + n) = make_float4(v0, v1, v2, v3);
-                    } else {
-                        if (n + 0 < N) crow[n + 0] = v0;
-                        if (n + 1 < N) crow[n + 1] = v1;
-                        if (n + 2 < N) crow[n + 2] = v2;
-                        if (n + 3 < N) crow[n + 3] = v3;
+#pragma unroll
+                    for (int v = 0; v < 16; v++)
+                        acc[i][j][v] = 0.0f;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < TN; i++) {
+#pragma unroll
+                for (int j = 0; j < TM; j++) {
+                    const int64_t m = cur.m0 + wm * 128 + j * 32 + r32;
+                    if (m < cur.m_end) {
+#pragma unroll
+                        for (int q = 0; q < 4; q++) {
+                            const int64_t n = cur.n0 + wn * 128 + i * 32 + 8 * q + 4 * h;
+                            const float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
+                            const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+                            if (CT == 0) {
+                                uint16_t *crow = reinterpret_cast<uint16_t *>(p.c) + m * p.ld_c;
+                                const uint32_t w0 = pack_bf16x2(v0, v1), w1 = pack_bf16x2(v2, v3);
+                                if (p.vec_store && n + 3 < N) {
+                                    *reinterpret_cast<uint2 *>(crow + n) = make_uint2(w0, w1);
+                                } else {
+                                    if (n + 0 < N) crow[n + 0] = (uint16_t)w0;
+                                    if (n + 1 < N) crow[n + 1] = (uint16_t)(w0 >> 16);
+                                    if (n + 2 < N) crow[n + 2] = (uint16_t)w1;
+                                    if (n + 3 < N) crow[n + 3] = (uint16_t)(w1 >> 16);
+                                }
+                            } else {
+                                float *crow = reinterpret_cast<float *>(p.c) + m * p.ld_c;
+                                if (p.vec_store && n + 3 < N) {
+                                    *reinterpret_cast<float4 *>(crow + n) = make_float4(v0, v1, v2, v3);
+                                } else {
+                                    if (n + 0 < N) crow[n + 0] = v0;
+                                    if (n + 1 < N) crow[n + 1] = v1;
+                                    if (n + 2 < N) crow[n + 2] = v2;
+                                    if (n + 3 < N) crow[n + 3] = v3;
+                                }
+                            }
+                        }
                     }
+#pragma unroll
+                    for (int v = 0; v < 16; v++)
+                        acc[i][j][v] = 0.0f;
                 }
             }
         }
+        cur = nxt;
+        cur_srd = nxt_srd;
+        // re-read the next stage's step-0 fragments, so that the copy read in
+        // the last stage need not stay live across the stores
+        read_frags((int)(gs & 1), 0, fa0, fb0);
     }
+#undef MX_MFMA_STEP
+    MX_WAIT_VMCNT(0);  // no load may still write LDS when the workgroup ends
+}
+
+static int vec_ok(const void *c, int64_t ld_c, int c_dtype)
+{
+    const uintptr_t align = c_dtype == 0 ? 8 : 16;
+    return ((uintptr_t)c % align == 0) && (ld_c % 4 == 0);
 }
 
 // Bytes of a rearranged scale buffer: 32-row x 8-block tiles of 256 bytes.
@@ -440,10 +661,22 @@ static int64_t scale_bytes(int64_t rows, int64_t K)
     return ((rows + 31) / 32) * ((K / 32 + 7) / 8) * 256;
 }
 
-static int vec_ok(const void *c, int64_t ld_c, int c_dtype)
+// Compute units of the current device (one persistent workgroup each: the
+// kernel's LDS admits one workgroup per CU).
+static int cu_count()
 {
-    const uintptr_t align = c_dtype == 0 ? 8 : 16;
-    return ((uintptr_t)c % align == 0) && (ld_c % 4 == 0);
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
 }
 
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t ld_a,
@@ -467,7 +700,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t
     p.as_bytes = (uint32_t)scale_bytes(M, K);
     p.bs_bytes = (uint32_t)scale_bytes(N, K);
     p.vec_store = vec_ok(c, ld_c, c_dtype);
-    const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
+    const unsigned grid = (unsigned)std::min<int64_t>(p.tiles_m * p.tiles_n, cu_count());
     if (c_dtype == 0)
         hipLaunchKernelGGL((mx_gemm_kernel<false, 0>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
     else
@@ -498,11 +731,11 @@ hipError_t launch_grouped_gemm(int64_t G, int64_t M_total, int64_t N, int64_t K,
     p.bs_group_stride = scale_bytes(N, K);
     p.as_bytes = (uint32_t)scale_bytes(M_total, K);
     p.bs_bytes = (uint32_t)p.bs_group_stride;
-    // upper bound on sum_g ceil(m_g / BM): every group adds at most one partial tile
-    p.tiles_m = (M_total + BM - 1) / BM + G;
     p.tiles_n = (N + BN - 1) / BN;
     p.vec_store = vec_ok(c, ld_c, c_dtype);
-    const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
+    // the tile count depends on the device-side offsets: one workgroup per CU,
+    // each walking the tiles the kernel enumerates
+    const unsigned grid = (unsigned)cu_count();
     if (c_dtype == 0)
         hipLaunchKernelGGL((mx_gemm_kernel<true, 0>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
     else
