@@ -42,7 +42,37 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only copy BYTES between two device buffers (a plain copy of known "
+                         "size, for scaling the HBM byte counters) and exit")
     return ap.parse_args()
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "dense_gemm_hbm_traffic.md")
+GEMM_SOURCE = os.path.join(ROOT, "mxfp8_block_scaled_08_amd", "csrc", "mx_gemm.hip")
+
+
+def measured_traffic():
+    """HBM bytes per dense-GEMM launch from the committed counter summary, or
+    None when the summary is missing or was taken on another kernel source
+    (the summary records the source's SHA-256)."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+        src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel source sha256") != src:
+        return None
+    try:
+        return int(fields["HBM bytes per launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 class Timer:
@@ -255,6 +285,17 @@ def main():
         sys.exit(2)
     import torch
 
+    if args.copy_calibration:
+        torch.cuda.set_device(0)
+        n = args.copy_calibration
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}))
+        return
+
     import mxfp8_block_scaled_08_amd as mx
     import mxsynth
 
@@ -345,7 +386,7 @@ def main():
             "peak": MFMA_FP8_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(dense_tflops / MFMA_FP8_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "launches_per_step": T.counts["gemm"] // K,
             "avg_launch_ms": round(gemm_ms / (T.counts["gemm"] // K), 4),
         },
