@@ -341,17 +341,19 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     }
     const uint32_t lds_a0 = (uint32_t)(uintptr_t)&sA[0][0];
     const uint32_t lds_b0 = (uint32_t)(uintptr_t)&sB[0][0];
-    // Loads of stage st of tile T into buffer buf.  A stage past the end or a
-    // padding stage (live false) gets an empty range: its loads move no data
-    // and write zeros, which keeps the main loop branch-free.
-    auto dma_stage = [&](const Tile &T, int st, int buf, bool live) {
+    // Loads of stage st of tile T into buffer buf, in two halves (rows of
+    // instructions 0-3 and 4-7) so they can be issued at two points of a
+    // stage.  A stage past the end or a padding stage (live false) gets an
+    // empty range: its loads move no data and write zeros, which keeps the
+    // main loop branch-free.
+    auto dma_stage = [&](const Tile &T, int st, int buf, bool live, int half) {
         const uint32_t ab = (uint32_t)(min(p.M - T.m0, (int64_t)BM) * p.ld_a);
         const uint32_t bb = (uint32_t)(min(N - T.n0, (int64_t)BN) * p.ld_b);
         const __amdgpu_buffer_rsrc_t ra = byte_range(p.a + T.m0 * p.ld_a, live ? ab : 0u);
         const __amdgpu_buffer_rsrc_t rb = byte_range(T.b + T.n0 * p.ld_b, live ? bb : 0u);
         const uint32_t koff = (uint32_t)st * BK;  // scalar offset, added after the range check
 #pragma unroll
-        for (int i = 0; i < DMA_PER_WAVE; i++) {
+        for (int i = half * (DMA_PER_WAVE / 2); i < (half + 1) * (DMA_PER_WAVE / 2); i++) {
             const uint32_t off = (uint32_t)(buf * STAGE_BYTES + 1024 * (DMA_PER_WAVE * wave + i));
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lptr_t)(uintptr_t)(lds_a0 + off), 16,
                                                      a_src[i], koff, 0, 0);
@@ -463,8 +465,10 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
 
     // prologue: scale words of the first group, stages 0 and 1 in flight
     dma_scales(cur, 0, true);
-    dma_stage(cur, 0, 0, true);
-    dma_stage(cur, 1, 1, 1 < KIT);
+    dma_stage(cur, 0, 0, true, 0);
+    dma_stage(cur, 0, 0, true, 1);
+    dma_stage(cur, 1, 1, 1 < KIT, 0);
+    dma_stage(cur, 1, 1, 1 < KIT, 1);
     MX_WAIT_VMCNT(2 * DMA_PER_WAVE);  // stage 1's loads may still be in flight
     lds_ring_barrier();
     uint32_t wa[TM], wb[TN];
@@ -485,19 +489,24 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     // parity within the tile and overall agree).  On entry the step-0
     // fragments are in fa0/fb0 and the loads of stage gs+1 are in flight.
     //   1. Step 0 runs while step 1's fragments are read (one LDS read
-    //      between consecutive matrix-core instructions).
+    //      between consecutive matrix-core instructions) and the scale words
+    //      of stage gs+2's group are requested.
     //   2. Barrier: every wave is done with buffer gs & 1.  Half of step 1
-    //      runs while the loads of stage gs+2 (and the scale words of its
-    //      group) are issued into that buffer.
+    //      runs while the first half of stage gs+2's loads goes into that
+    //      buffer.
     //   3. Wait until this wave's loads of stage gs+1 have landed (all but
-    //      the loads just issued: vector-memory operations retire in issue
-    //      order) and barrier, so every wave's have.  The other half of step
-    //      1 runs while stage gs+1's step-0 fragments and the scale words of
+    //      the 11 issued since its last one: vector-memory operations retire
+    //      in issue order) and barrier, so every wave's have.  The other half
+    //      of step 1 runs while the second half of stage gs+2's loads is
+    //      issued and stage gs+1's step-0 fragments and the scale words of
     //      the next group are read.  Those words are kept on a group's last
-    //      stage (odd gs), when they belong to the group of stage gs+1; on
-    //      an even stage they are being rewritten and are discarded.  An odd
+    //      stage (odd gs), when they belong to the group of stage gs+1; on an
+    //      even stage they are being rewritten and are discarded.  An odd
     //      stage reloads the words of its own group, which leaves the bytes
     //      unchanged.
+    // Spreading the loads over the stage keeps fewer of them waiting on the
+    // L1's outstanding-miss capacity at once: a load that cannot be accepted
+    // stalls the wave, and with it the matrix-core instructions behind it.
     // Past the end the loads are empty and the fragment reads unused, so the
     // body has no branches.  After a tile's last stage its accumulators are
     // stored and cleared.
@@ -509,49 +518,53 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
         for (int st = 0; st < KITP; st++, gs++) {
             const int buf = (int)(gs & 1);
             const int shift = 16 * buf;
-            // 1.
-            read_frags(buf, 1, fa1, fb1);
-            MX_MFMA_STEP(fa0, fb0, shift, 0, TN)
-#pragma unroll
-            for (int q = 0; q < TM * TN; q++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // matrix core
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            lds_ring_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-            // 2. stage gs + 2: stage st + 2 of this tile, or the next tile's first two
+            // stage gs + 2: stage st + 2 of this tile, or the next tile's first two
             const bool same = st + 2 < KITP;
             const int st2 = same ? st + 2 : st + 2 - KITP;
             const Tile ld = same ? cur : nxt;
             const bool live = gs + 2 < total;
             const bool live_group = ((gs + 2) & ~(int64_t)1) < total;  // the group's first stage
+            // 1.
+            read_frags(buf, 1, fa1, fb1);
             dma_scales(ld, st2 >> 1, live_group);
-            dma_stage(ld, st2, buf, live && st2 < KIT);
-            MX_MFMA_STEP(fa1, fb1, shift + 8, 0, TN / 2)
+            MX_MFMA_STEP(fa0, fb0, shift, 0, TN)
 #pragma unroll
-            for (int q = 0; q < 3; q++) {  // 8 matrix-core, 19 loads
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-                __builtin_amdgcn_sched_group_barrier(0x010, 3, 1);
+            for (int q = 0; q < 3; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // matrix core
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // scale load
             }
 #pragma unroll
-            for (int q = 0; q < 5; q++) {
+            for (int q = 0; q < TM * TN - 3; q++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            lds_ring_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            // 2.
+            dma_stage(ld, st2, buf, live && st2 < KIT, 0);
+            MX_MFMA_STEP(fa1, fb1, shift + 8, 0, TN / 2)
+#pragma unroll
+            for (int q = 0; q < 8; q++) {  // 8 matrix-core, 8 loads
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-                __builtin_amdgcn_sched_group_barrier(0x010, 2, 1);
+                __builtin_amdgcn_sched_group_barrier(0x010, 1, 1);
             }
             __builtin_amdgcn_sched_barrier(0);
             // 3.
-            MX_WAIT_VMCNT(2 * DMA_PER_WAVE + SCALE_LOADS);
+            MX_WAIT_VMCNT(DMA_PER_WAVE + SCALE_LOADS);
             asm volatile("s_barrier" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
             uint32_t na[TM], nb[TN];
             read_scales(st + 1 < KITP ? cur_srd : nxt_srd, na, nb);
+            dma_stage(ld, st2, buf, live && st2 < KIT, 1);
             read_frags(buf ^ 1, 0, fa0, fb0);
             MX_MFMA_STEP(fa1, fb1, shift + 8, TN / 2, TN)
             __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);  // scale words
 #pragma unroll
-            for (int q = 0; q < TM * TN / 2; q++) {  // 8 matrix-core, 16 LDS reads
+            for (int q = 0; q < 8; q++) {  // 8 matrix-core, 8 loads, 16 LDS reads
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+                __builtin_amdgcn_sched_group_barrier(0x010, 1, 2);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
             }
             __builtin_amdgcn_sched_barrier(0);  // the selects wait for the words: keep them last
