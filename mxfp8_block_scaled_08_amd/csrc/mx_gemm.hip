@@ -75,7 +75,8 @@ struct GemmParams {
     int64_t G;
     int64_t b_group_stride, bs_group_stride;
     uint32_t as_bytes, bs_bytes;  // rearranged scale bytes of A (all rows) and of one B
-    int vec_store;
+    int vec_store;  // C rows allow 4-element vector stores
+    int vec16;      // BF16 C: rows allow 16-byte stores (8 elements)
 };
 
 __device__ __forceinline__ int chunk_perm(int row) { return (row >> 1) & 7; }
@@ -452,10 +453,12 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     // per-lane offsets of C within a tile: row wm*128 + j*32 + r32, columns
     // from wn*128 + 4h (the sub-tile and register group add immediates)
     constexpr int CE = CT == 0 ? 2 : 4;  // bytes per C element
+    // (BF16 C is stored 8 columns per lane after a half-wave exchange, so its
+    // lane column is wn*128 + 8h)
     uint32_t c_off[TM];
 #pragma unroll
     for (int j = 0; j < TM; j++)
-        c_off[j] = (uint32_t)(((wm * 128 + j * 32 + r32) * p.ld_c + wn * 128 + 4 * h) * CE);
+        c_off[j] = (uint32_t)(((wm * 128 + j * 32 + r32) * p.ld_c + wn * 128 + (CT == 0 ? 8 : 4) * h) * CE);
 
     // ---- the workgroup's stages: tiles t_first, + t_step, ..., KITP
     // stages each, numbered continuously so the pipeline runs across tiles
@@ -578,7 +581,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
         }
 
         // ---- epilogue: lane holds C[m][n..n+3] for each register group
-        if (p.vec_store && cur.n0 + BN <= N) {
+        if ((CT == 0 ? p.vec16 : p.vec_store) && cur.n0 + BN <= N) {
             // whole-width tile: buffer stores relative to the tile's first
             // element; the range ends after the tile's last valid row, so the
             // stores of rows past it (past M, or past the expert) are dropped
@@ -590,19 +593,43 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             for (int i = 0; i < TN; i++) {
 #pragma unroll
                 for (int j = 0; j < TM; j++) {
+                    if (CT == 0) {
+                        // Register group q of lane (h, r) holds columns 8q + 4h .. +3
+                        // of row r.  Swapping group 1 of the lower half-wave with
+                        // group 0 of the upper one (v_permlane32_swap) leaves lane r
+                        // with columns 0-7 in groups (0, 1) and lane 32 + r with
+                        // columns 8-15; groups (2, 3) likewise give 16-23 / 24-31.
+                        uint32_t w[4][2];
 #pragma unroll
-                    for (int q = 0; q < 4; q++) {
-                        const float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
-                        const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-                        const uint32_t off = c_off[j] + (uint32_t)((i * 32 + 8 * q) * CE);
-                        if (CT == 0) {
-                            typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
-                            __builtin_amdgcn_raw_buffer_store_b64(
-                                u2_t{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)}, rc, off, 0, 0);
-                        } else {
+                        for (int q = 0; q < 4; q++) {
+                            w[q][0] = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
+                            w[q][1] = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                        }
+#pragma unroll
+                        for (int q = 0; q < 4; q += 2) {
+#pragma unroll
+                            for (int d = 0; d < 2; d++) {
+                                const auto sw = __builtin_amdgcn_permlane32_swap(w[q][d], w[q + 1][d],
+                                                                                 false, false);
+                                w[q][d] = sw[0];
+                                w[q + 1][d] = sw[1];
+                            }
+                        }
+                        const uint32_t off = c_off[j] + (uint32_t)(i * 32 * CE);
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            v4i{(int)w[0][0], (int)w[0][1], (int)w[1][0], (int)w[1][1]}, rc, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            v4i{(int)w[2][0], (int)w[2][1], (int)w[3][0], (int)w[3][1]}, rc,
+                            off + 16 * CE, 0, 0);
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; q++) {
                             typedef float f4_t __attribute__((ext_vector_type(4)));
+                            const f4_t v{acc[i][j][4 * q + 0], acc[i][j][4 * q + 1],
+                                         acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
                             __builtin_amdgcn_raw_buffer_store_b128(
-                                __builtin_bit_cast(v4i, f4_t{v0, v1, v2, v3}), rc, off, 0, 0);
+                                __builtin_bit_cast(v4i, v), rc, c_off[j] + (uint32_t)((i * 32 + 8 * q) * CE),
+                                0, 0);
                         }
                     }
 #pragma unroll
@@ -668,6 +695,11 @@ static int vec_ok(const void *c, int64_t ld_c, int c_dtype)
     return ((uintptr_t)c % align == 0) && (ld_c % 4 == 0);
 }
 
+static int vec16_ok(const void *c, int64_t ld_c, int c_dtype)
+{
+    return c_dtype == 0 && ((uintptr_t)c % 16 == 0) && (ld_c % 8 == 0);
+}
+
 // Bytes of a rearranged scale buffer: 32-row x 8-block tiles of 256 bytes.
 static int64_t scale_bytes(int64_t rows, int64_t K)
 {
@@ -713,6 +745,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t
     p.as_bytes = (uint32_t)scale_bytes(M, K);
     p.bs_bytes = (uint32_t)scale_bytes(N, K);
     p.vec_store = vec_ok(c, ld_c, c_dtype);
+    p.vec16 = vec16_ok(c, ld_c, c_dtype);
     const unsigned grid = (unsigned)std::min<int64_t>(p.tiles_m * p.tiles_n, cu_count());
     if (c_dtype == 0)
         hipLaunchKernelGGL((mx_gemm_kernel<false, 0>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
@@ -746,6 +779,7 @@ hipError_t launch_grouped_gemm(int64_t G, int64_t M_total, int64_t N, int64_t K,
     p.bs_bytes = (uint32_t)p.bs_group_stride;
     p.tiles_n = (N + BN - 1) / BN;
     p.vec_store = vec_ok(c, ld_c, c_dtype);
+    p.vec16 = vec16_ok(c, ld_c, c_dtype);
     // the tile count depends on the device-side offsets: one workgroup per CU,
     // each walking the tiles the kernel enumerates
     const unsigned grid = (unsigned)cu_count();
