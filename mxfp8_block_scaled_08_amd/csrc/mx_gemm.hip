@@ -453,12 +453,22 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     // per-lane offsets of C within a tile: row wm*128 + j*32 + r32, columns
     // from wn*128 + 4h (the sub-tile and register group add immediates)
     constexpr int CE = CT == 0 ? 2 : 4;  // bytes per C element
-    // (BF16 C is stored 8 columns per lane after a half-wave exchange, so its
-    // lane column is wn*128 + 8h)
-    uint32_t c_off[TM];
+    // BF16 C is stored after two lane exchanges (see the epilogue): lane l
+    // writes 8 columns (chunk k = ((l >> 5) & 1) | (((l >> 4) & 1) << 1)) of
+    // row l & 15 of a 16-row half of the sub-tile, one base per half.
+    uint32_t c_off[TM], c_off_hi[TM];
 #pragma unroll
-    for (int j = 0; j < TM; j++)
-        c_off[j] = (uint32_t)(((wm * 128 + j * 32 + r32) * p.ld_c + wn * 128 + (CT == 0 ? 8 : 4) * h) * CE);
+    for (int j = 0; j < TM; j++) {
+        if (CT == 0) {
+            const int row = wm * 128 + j * 32 + (lane & 15);
+            const int chunk = ((lane >> 5) & 1) | (((lane >> 4) & 1) << 1);
+            c_off[j] = (uint32_t)((row * p.ld_c + wn * 128 + chunk * 8) * CE);
+            c_off_hi[j] = (uint32_t)(((row + 16) * p.ld_c + wn * 128 + chunk * 8) * CE);
+        } else {
+            c_off[j] = (uint32_t)(((wm * 128 + j * 32 + r32) * p.ld_c + wn * 128 + 4 * h) * CE);
+            c_off_hi[j] = 0;
+        }
+    }
 
     // ---- the workgroup's stages: tiles t_first, + t_step, ..., KITP
     // stages each, numbered continuously so the pipeline runs across tiles
@@ -595,10 +605,14 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                 for (int j = 0; j < TM; j++) {
                     if (CT == 0) {
                         // Register group q of lane (h, r) holds columns 8q + 4h .. +3
-                        // of row r.  Swapping group 1 of the lower half-wave with
-                        // group 0 of the upper one (v_permlane32_swap) leaves lane r
-                        // with columns 0-7 in groups (0, 1) and lane 32 + r with
-                        // columns 8-15; groups (2, 3) likewise give 16-23 / 24-31.
+                        // of row r (r = lane & 31) as two packed words.  Swapping
+                        // group 1 of the lower half-wave with group 0 of the upper
+                        // one (v_permlane32_swap), and group 3 with group 2, leaves
+                        // lane (h, r) with 16-byte chunks h (columns 8h..8h+7) in
+                        // s1 and 2 + h in s2.  Swapping the odd 16-lane rows of s1
+                        // with the even ones of s2 (v_permlane16_swap) then gathers
+                        // all four chunks of rows 0-15 in s1 and of rows 16-31 in
+                        // s2: one store writes 64 contiguous bytes of 16 rows.
                         uint32_t w[4][2];
 #pragma unroll
                         for (int q = 0; q < 4; q++) {
@@ -615,12 +629,19 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                                 w[q + 1][d] = sw[1];
                             }
                         }
-                        const uint32_t off = c_off[j] + (uint32_t)(i * 32 * CE);
+                        uint32_t s1[4] = {w[0][0], w[0][1], w[1][0], w[1][1]};
+                        uint32_t s2[4] = {w[2][0], w[2][1], w[3][0], w[3][1]};
+#pragma unroll
+                        for (int d = 0; d < 4; d++) {
+                            const auto sw = __builtin_amdgcn_permlane16_swap(s1[d], s2[d], false, false);
+                            s1[d] = sw[0];
+                            s2[d] = sw[1];
+                        }
+                        const uint32_t col = (uint32_t)(i * 32 * CE);
                         __builtin_amdgcn_raw_buffer_store_b128(
-                            v4i{(int)w[0][0], (int)w[0][1], (int)w[1][0], (int)w[1][1]}, rc, off, 0, 0);
+                            v4i{(int)s1[0], (int)s1[1], (int)s1[2], (int)s1[3]}, rc, c_off[j] + col, 0, 0);
                         __builtin_amdgcn_raw_buffer_store_b128(
-                            v4i{(int)w[2][0], (int)w[2][1], (int)w[3][0], (int)w[3][1]}, rc,
-                            off + 16 * CE, 0, 0);
+                            v4i{(int)s2[0], (int)s2[1], (int)s2[2], (int)s2[3]}, rc, c_off_hi[j] + col, 0, 0);
                     } else {
 #pragma unroll
                         for (int q = 0; q < 4; q++) {
