@@ -159,31 +159,56 @@ __global__ __launch_bounds__(QC_THREADS) void quantize_colwise_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Scale rearrangement: one thread writes one 4-byte word of the GEMM layout
-// (word w of tile (rt, kt) holds, for row 32rt + w%32, the scales of blocks
-// 8kt + h, +2, +4, +6 with h = w/32), padding with 0x7F.
+// Scale rearrangement.  A half-wave takes one 32-row tile row rt and a run of
+// up to SW_KT consecutive 256-K groups kt; lane r owns row 32rt + r.  Per
+// group the lane reads the row's 8 scale bytes (blocks 8kt .. 8kt+7) as one
+// 8-byte load and splits them with v_perm into the word of lane slot r
+// (blocks 8kt, +2, +4, +6) and of slot 32 + r (blocks 8kt+1, +3, +5, +7); the
+// 32 lanes then write each 128-byte half of the tile with one store each.
+// Rows past the tensor and blocks past kblocks are the 0x7F padding.  The
+// 8-byte path needs 8-byte aligned scale rows; otherwise bytes are read one
+// at a time.
 
 constexpr int SW_THREADS = 256;
+constexpr int SW_KT = 4;  // 256-K groups per half-wave
 
+template <bool ALIGNED8>
 __global__ __launch_bounds__(SW_THREADS) void scale_swizzle_kernel(
     const uint8_t *__restrict__ s, int64_t rows, int64_t kblocks, int64_t ld_s,
-    uint32_t *__restrict__ out, int64_t words, int64_t KT)
+    uint32_t *__restrict__ out, int64_t KT, int64_t runs, int64_t halves)
 {
-    for (int64_t d = (int64_t)blockIdx.x * SW_THREADS + threadIdx.x; d < words;
-         d += (int64_t)gridDim.x * SW_THREADS) {
-        int64_t tile = d >> 6;
-        int lane = (int)(d & 63);
-        int h = lane >> 5, r = lane & 31;
-        int64_t rt = tile / KT, kt = tile - rt * KT;
-        int64_t row = rt * 32 + r;
-        uint32_t word = 0;
+    const int64_t hw = ((int64_t)blockIdx.x * SW_THREADS + threadIdx.x) >> 5;
+    if (hw >= halves)
+        return;
+    const int r = threadIdx.x & 31;
+    const int64_t rt = hw / runs;
+    const int64_t kt0 = (hw - rt * runs) * SW_KT;
+    const int64_t row = rt * 32 + r;
+    const bool row_ok = row < rows;
+    const uint8_t *srow = s + (row_ok ? row : 0) * ld_s;
 #pragma unroll
-        for (int t = 0; t < 4; t++) {
-            int64_t blk = kt * 8 + 2 * t + h;
-            uint32_t byte = (row < rows && blk < kblocks) ? s[row * ld_s + blk] : 0x7Fu;
-            word |= byte << (8 * t);
+    for (int u = 0; u < SW_KT; u++) {
+        const int64_t kt = kt0 + u;
+        if (kt >= KT)
+            break;
+        uint32_t lo = 0x7F7F7F7Fu, hi = 0x7F7F7F7Fu;
+        if (row_ok) {
+            if (ALIGNED8 && 8 * kt + 8 <= kblocks) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(srow + 8 * kt);
+                lo = v.x;
+                hi = v.y;
+            } else {
+                uint32_t b[8];
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    b[e] = 8 * kt + e < kblocks ? srow[8 * kt + e] : 0x7Fu;
+                lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+                hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+            }
         }
-        out[d] = word;
+        uint32_t *tile = out + (rt * KT + kt) * 64;
+        tile[r] = __builtin_amdgcn_perm(hi, lo, 0x06040200u);       // blocks 0, 2, 4, 6
+        tile[32 + r] = __builtin_amdgcn_perm(hi, lo, 0x07050301u);  // blocks 1, 3, 5, 7
     }
 }
 
@@ -228,13 +253,19 @@ hipError_t launch_quantize_colwise(const void *x, int64_t rows, int64_t cols, in
 hipError_t launch_scale_swizzle(const void *s, int64_t rows, int64_t kblocks, int64_t ld_s,
                                 void *s_swz, hipStream_t stream)
 {
-    int64_t KT = (kblocks + 7) / 8;
-    int64_t words = ((rows + 31) / 32) * KT * 64;
-    int64_t blocks = (words + SW_THREADS - 1) / SW_THREADS;
-    if (blocks > 65536)
-        blocks = 65536;
-    hipLaunchKernelGGL(scale_swizzle_kernel, dim3((unsigned)blocks), dim3(SW_THREADS), 0, stream,
-                       (const uint8_t *)s, rows, kblocks, ld_s, (uint32_t *)s_swz, words, KT);
+    const int64_t KT = (kblocks + 7) / 8;
+    const int64_t runs = (KT + SW_KT - 1) / SW_KT;
+    const int64_t halves = ((rows + 31) / 32) * runs;
+    const int64_t blocks = (halves * 32 + SW_THREADS - 1) / SW_THREADS;
+    const bool aligned8 = ((uintptr_t)s % 8 == 0) && (ld_s % 8 == 0);
+    if (aligned8)
+        hipLaunchKernelGGL(scale_swizzle_kernel<true>, dim3((unsigned)blocks), dim3(SW_THREADS), 0,
+                           stream, (const uint8_t *)s, rows, kblocks, ld_s, (uint32_t *)s_swz, KT,
+                           runs, halves);
+    else
+        hipLaunchKernelGGL(scale_swizzle_kernel<false>, dim3((unsigned)blocks), dim3(SW_THREADS), 0,
+                           stream, (const uint8_t *)s, rows, kblocks, ld_s, (uint32_t *)s_swz, KT,
+                           runs, halves);
     return hipGetLastError();
 }
 
