@@ -125,6 +125,16 @@ template <typename T> __device__ __forceinline__ const T *uniform(const T *x)
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
 #define MX_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
+// The same wait with its bound picked by a wave-uniform value: at most
+// RELAXED operations outstanding when sel is zero, else at most STRICT
+// (RELAXED >= STRICT; the zero path jumps over the strict wait).
+#define MX_WAIT_VMCNT_SEL(sel, RELAXED, STRICT)                                                   \
+    asm volatile("s_cmp_eq_u32 %0, 0\n\t"                                                       \
+                 "s_cbranch_scc1 .Lmx_vm_relaxed%=\n\t"                                         \
+                 "s_waitcnt vmcnt(%2)\n"                                                         \
+                 ".Lmx_vm_relaxed%=:\n\t"                                                       \
+                 "s_waitcnt vmcnt(%1)" ::"s"(sel), "n"(RELAXED), "n"(STRICT) : "memory", "scc")
+
 // Workgroup barrier for the LDS ring.  __syncthreads() would also wait for
 // every outstanding vector-memory load (its release fence must cover the LDS
 // writes of the direct-to-LDS loads), draining the whole pipeline each step.
@@ -398,6 +408,9 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                                                  kw, 0, 0);
     };
     constexpr int SCALE_LOADS = 3;
+    constexpr int EPILOGUE_STORES = 2 * TM * TN;  // BF16 C, whole-width tile
+    static_assert(TN % 2 == 0, "BF16 stores pair adjacent sub-tiles");
+    static_assert(DMA_PER_WAVE + SCALE_LOADS + EPILOGUE_STORES <= 63, "vmcnt holds at most 63");
     auto read_scales = [&](uint32_t a_rd_s, uint32_t *xa, uint32_t *xb) {
 #pragma unroll
         for (int i = 0; i < TM; i++)
@@ -453,17 +466,18 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     // per-lane offsets of C within a tile: row wm*128 + j*32 + r32, columns
     // from wn*128 + 4h (the sub-tile and register group add immediates)
     constexpr int CE = CT == 0 ? 2 : 4;  // bytes per C element
-    // BF16 C is stored after two lane exchanges (see the epilogue): lane l
-    // writes 8 columns (chunk k = ((l >> 5) & 1) | (((l >> 4) & 1) << 1)) of
-    // row l & 15 of a 16-row half of the sub-tile, one base per half.
+    // BF16 C is stored after three lane exchanges (see the epilogue): lane l
+    // writes 8 columns, chunk k = ((l >> 5) & 1) | (((l >> 4) & 1) << 1) of
+    // sub-tile pair half (l >> 3) & 1, of row l & 7 of an 8-row quarter of the
+    // pair's 32-row band; one base for rows 0-7 and one for rows 16-23.
     uint32_t c_off[TM], c_off_hi[TM];
 #pragma unroll
     for (int j = 0; j < TM; j++) {
         if (CT == 0) {
-            const int row = wm * 128 + j * 32 + (lane & 15);
-            const int chunk = ((lane >> 5) & 1) | (((lane >> 4) & 1) << 1);
-            c_off[j] = (uint32_t)((row * p.ld_c + wn * 128 + chunk * 8) * CE);
-            c_off_hi[j] = (uint32_t)(((row + 16) * p.ld_c + wn * 128 + chunk * 8) * CE);
+            const int row = wm * 128 + j * 32 + (lane & 7);
+            const int col = wn * 128 + ((lane >> 3) & 1) * 32 + (((lane >> 5) & 1) | (((lane >> 4) & 1) << 1)) * 8;
+            c_off[j] = (uint32_t)((row * p.ld_c + col) * CE);
+            c_off_hi[j] = (uint32_t)(((row + 16) * p.ld_c + col) * CE);
         } else {
             c_off[j] = (uint32_t)(((wm * 128 + j * 32 + r32) * p.ld_c + wn * 128 + 4 * h) * CE);
             c_off_hi[j] = 0;
@@ -482,7 +496,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     dma_stage(cur, 0, 0, true, 1);
     dma_stage(cur, 1, 1, 1 < KIT, 0);
     dma_stage(cur, 1, 1, 1 < KIT, 1);
-    MX_WAIT_VMCNT(2 * DMA_PER_WAVE);  // stage 1's loads may still be in flight
+    MX_WAIT_VMCNT(0);  // stages 0 and 1 (the first stage's wait is the relaxed one)
     lds_ring_barrier();
     uint32_t wa[TM], wb[TN];
     read_scales(cur_srd, wa, wb);
@@ -524,6 +538,14 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     // body has no branches.  After a tile's last stage its accumulators are
     // stored and cleared.
     int64_t gs = 0;  // stages run so far (all tiles)
+    // The first stage of a tile waits for loads issued before the previous
+    // tile's stores.  Vector-memory operations retire in issue order, so its
+    // wait allows EPILOGUE_STORES more outstanding operations: the stores
+    // drain while that stage's matrix-core work runs, and only the second
+    // stage's wait (for loads issued after them) includes them.  That bound
+    // is exact after the BF16 whole-width stores and conservative after the
+    // FP32 ones (more stores); the other epilogue, and the prologue before
+    // the first tile, wait for all of the wave's operations instead.
     for (int64_t k = 0; k < my_tiles; k++) {
         // the tile after this one (loaded during this tile's last two stages)
         const Tile nxt = k + 1 < my_tiles ? coords(t_first + (k + 1) * t_step) : cur;
@@ -565,7 +587,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             }
             __builtin_amdgcn_sched_barrier(0);
             // 3.
-            MX_WAIT_VMCNT(DMA_PER_WAVE + SCALE_LOADS);
+            MX_WAIT_VMCNT_SEL(st, DMA_PER_WAVE + SCALE_LOADS + EPILOGUE_STORES, DMA_PER_WAVE + SCALE_LOADS);
             asm volatile("s_barrier" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
             uint32_t na[TM], nb[TN];
@@ -599,20 +621,29 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             const __amdgpu_buffer_rsrc_t rc =
                 byte_range((const uint8_t *)p.c + (cur.m0 * p.ld_c + cur.n0) * CE,
                            rows_valid * (uint32_t)(p.ld_c * CE));
-#pragma unroll
-            for (int i = 0; i < TN; i++) {
+            if (CT == 0) {
+                // Register group q of lane (h, r) holds columns 8q + 4h .. +3 of
+                // row r (r = lane & 31) as two packed words.  Swapping group 1 of
+                // the lower half-wave with group 0 of the upper one
+                // (v_permlane32_swap), and group 3 with group 2, leaves lane
+                // (h, r) with 16-byte chunks h (columns 8h..8h+7) in s1 and 2 + h
+                // in s2.  Swapping the odd 16-lane rows of s1 with the even ones of
+                // s2 (v_permlane16_swap) then gathers all four chunks of rows 0-15
+                // in s1 and of rows 16-31 in s2, lane l holding row l & 15.  Last,
+                // within each 16-lane row, lanes 8-15 of sub-tile i trade with
+                // lanes 0-7 of sub-tile i + 1 (DPP row shifts by 8, bank-masked):
+                // then one store writes whole 128-byte lines, 64 bytes of each of
+                // the two sub-tiles, of 8 rows.
+                // The stores are non-temporal.  C is never read back here, and
+                // with the default policy each round of tiles' output fills the
+                // L2 and evicts the operand panels that the next round reuses;
+                // streaming whole lines keeps them resident.
+                const uint32_t row8 = (uint32_t)(8 * p.ld_c * CE);
 #pragma unroll
                 for (int j = 0; j < TM; j++) {
-                    if (CT == 0) {
-                        // Register group q of lane (h, r) holds columns 8q + 4h .. +3
-                        // of row r (r = lane & 31) as two packed words.  Swapping
-                        // group 1 of the lower half-wave with group 0 of the upper
-                        // one (v_permlane32_swap), and group 3 with group 2, leaves
-                        // lane (h, r) with 16-byte chunks h (columns 8h..8h+7) in
-                        // s1 and 2 + h in s2.  Swapping the odd 16-lane rows of s1
-                        // with the even ones of s2 (v_permlane16_swap) then gathers
-                        // all four chunks of rows 0-15 in s1 and of rows 16-31 in
-                        // s2: one store writes 64 contiguous bytes of 16 rows.
+                    uint32_t s1[TN][4], s2[TN][4];
+#pragma unroll
+                    for (int i = 0; i < TN; i++) {
                         uint32_t w[4][2];
 #pragma unroll
                         for (int q = 0; q < 4; q++) {
@@ -629,20 +660,50 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                                 w[q + 1][d] = sw[1];
                             }
                         }
-                        uint32_t s1[4] = {w[0][0], w[0][1], w[1][0], w[1][1]};
-                        uint32_t s2[4] = {w[2][0], w[2][1], w[3][0], w[3][1]};
+                        const uint32_t t1[4] = {w[0][0], w[0][1], w[1][0], w[1][1]};
+                        const uint32_t t2[4] = {w[2][0], w[2][1], w[3][0], w[3][1]};
 #pragma unroll
                         for (int d = 0; d < 4; d++) {
-                            const auto sw = __builtin_amdgcn_permlane16_swap(s1[d], s2[d], false, false);
-                            s1[d] = sw[0];
-                            s2[d] = sw[1];
+                            const auto sw = __builtin_amdgcn_permlane16_swap(t1[d], t2[d], false, false);
+                            s1[i][d] = sw[0];
+                            s2[i][d] = sw[1];
+                        }
+#pragma unroll
+                        for (int v = 0; v < 16; v++)
+                            acc[i][j][v] = 0.0f;
+                    }
+#pragma unroll
+                    for (int i = 0; i < TN; i += 2) {
+                        // row_shr:8 into lanes 8-15 (banks 2, 3), row_shl:8 into lanes 0-7
+                        uint32_t x1[4], y1[4], x2[4], y2[4];
+#pragma unroll
+                        for (int d = 0; d < 4; d++) {
+                            x1[d] = (uint32_t)__builtin_amdgcn_update_dpp((int)s1[i][d], (int)s1[i + 1][d],
+                                                                          0x118, 0xF, 0xC, false);
+                            y1[d] = (uint32_t)__builtin_amdgcn_update_dpp((int)s1[i + 1][d], (int)s1[i][d],
+                                                                          0x108, 0xF, 0x3, false);
+                            x2[d] = (uint32_t)__builtin_amdgcn_update_dpp((int)s2[i][d], (int)s2[i + 1][d],
+                                                                          0x118, 0xF, 0xC, false);
+                            y2[d] = (uint32_t)__builtin_amdgcn_update_dpp((int)s2[i + 1][d], (int)s2[i][d],
+                                                                          0x108, 0xF, 0x3, false);
                         }
                         const uint32_t col = (uint32_t)(i * 32 * CE);
-                        __builtin_amdgcn_raw_buffer_store_b128(
-                            v4i{(int)s1[0], (int)s1[1], (int)s1[2], (int)s1[3]}, rc, c_off[j] + col, 0, 0);
-                        __builtin_amdgcn_raw_buffer_store_b128(
-                            v4i{(int)s2[0], (int)s2[1], (int)s2[2], (int)s2[3]}, rc, c_off_hi[j] + col, 0, 0);
-                    } else {
+                        constexpr int NT = 2;  // cache policy: non-temporal
+                        __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]},
+                                                               rc, c_off[j] + col, 0, NT);
+                        __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)y1[0], (int)y1[1], (int)y1[2], (int)y1[3]},
+                                                               rc, c_off[j] + row8 + col, 0, NT);
+                        __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)x2[0], (int)x2[1], (int)x2[2], (int)x2[3]},
+                                                               rc, c_off_hi[j] + col, 0, NT);
+                        __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)y2[0], (int)y2[1], (int)y2[2], (int)y2[3]},
+                                                               rc, c_off_hi[j] + row8 + col, 0, NT);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < TN; i++) {
+#pragma unroll
+                    for (int j = 0; j < TM; j++) {
 #pragma unroll
                         for (int q = 0; q < 4; q++) {
                             typedef float f4_t __attribute__((ext_vector_type(4)));
@@ -652,10 +713,10 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                                 __builtin_bit_cast(v4i, v), rc, c_off[j] + (uint32_t)((i * 32 + 8 * q) * CE),
                                 0, 0);
                         }
-                    }
 #pragma unroll
-                    for (int v = 0; v < 16; v++)
-                        acc[i][j][v] = 0.0f;
+                        for (int v = 0; v < 16; v++)
+                            acc[i][j][v] = 0.0f;
+                    }
                 }
             }
         } else {
@@ -699,6 +760,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                         acc[i][j][v] = 0.0f;
                 }
             }
+            MX_WAIT_VMCNT(0);  // a varying number of stores: the next wait cannot count them
         }
         cur = nxt;
         cur_srd = nxt_srd;
