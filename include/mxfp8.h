@@ -34,9 +34,10 @@
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless stated; the caller owns all
- *     buffers (allocated e.g. with torch).  The library allocates nothing,
- *     keeps no pointer after returning and holds no derived state, so no
- *     cached layout can go stale.
+ *     buffers (allocated e.g. with torch).  Apart from mx_gemm's
+ *     stream-ordered split workspace (see there) the library allocates
+ *     nothing; it keeps no pointer after returning and holds no derived
+ *     state, so no cached layout can go stale.
  *   - Work is enqueued on `stream` (a hipStream_t cast to void*; NULL is the
  *     null stream).  No call synchronizes the host or reads device memory
  *     from the host; calls are capturable in a HIP graph.
@@ -50,7 +51,8 @@
  *   - Zero-sized problems (rows == 0, cols == 0, M == 0 or N == 0) return
  *     MX_OK and launch nothing.
  *   - Calls on different streams may run concurrently; the library has no
- *     shared mutable state apart from the thread-local error message.
+ *     shared mutable state apart from the thread-local error message and
+ *     mx_gemm's per-device workspace pool (stream-ordered allocations).
  */
 #ifndef MXFP8_H
 #define MXFP8_H
@@ -164,8 +166,18 @@ mx_status mx_scale_swizzle(const void *s, int64_t rows, int64_t kblocks, int64_t
  * not overlap an input.  Offsets inside a 256-row tile and inside a
  * rearranged scale buffer are 32-bit: 256 * ld_a, 256 * ld_b and
  * 256 * ld_c * (element size of C) must stay below 2^31 and each rearranged
- * scale buffer below 4 GiB (else MX_ERR_UNSUPPORTED).  No split-K: each
- * output is one FP32 accumulation.
+ * scale buffer below 4 GiB (else MX_ERR_UNSUPPORTED).
+ * Work: 256x256 output tiles on persistent workgroups, one per compute unit.
+ * When the tile count leaves a partial last round and C is BF16 with
+ * full-width tiles (N % 256 == 0, c 16-byte aligned, ld_c % 8 == 0), each
+ * leftover tile is split along K into S ranges of whole 256-K groups: every
+ * range accumulates in FP32, and the S FP32 partial sums are added in range
+ * order before the single rounding to BF16.  S depends only on M, N, K and
+ * the device's compute-unit count, so results are deterministic per shape
+ * and device.  The split takes a workspace of S * 256 KiB per leftover tile
+ * (at most 64 MiB) as a stream-ordered allocation from a memory pool the
+ * library creates per device and keeps for reuse; if that allocation fails
+ * the call runs unsplit (same results up to the summation order).
  */
 mx_status mx_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t ld_a,
                   const void *a_s_swz, const void *b_q, int64_t ld_b, const void *b_s_swz,

@@ -46,6 +46,8 @@
 #include "mx_launch.h"
 
 #include <algorithm>
+#include <cmath>
+#include <mutex>
 
 namespace mx {
 
@@ -77,6 +79,14 @@ struct GemmParams {
     uint32_t as_bytes, bs_bytes;  // rearranged scale bytes of A (all rows) and of one B
     int vec_store;  // C rows allow 4-element vector stores
     int vec16;      // BF16 C: rows allow 16-byte stores (8 elements)
+    // Split tail (dense only): tiles dp_tiles .. dp_tiles + split_tiles - 1
+    // are each cut into split_s K ranges of whole 256-K groups, one workgroup
+    // per range.  Each range writes its FP32 partial tile to ws (slot
+    // tile * split_s + range, BM * BN floats); split_reduce_kernel then sums
+    // the slots of each tile in range order and writes C.
+    int64_t dp_tiles;
+    int split_tiles, split_s;
+    float *ws;
 };
 
 __device__ __forceinline__ int chunk_perm(int row) { return (row >> 1) & 7; }
@@ -148,15 +158,20 @@ __device__ __forceinline__ void lds_ring_barrier()
     asm volatile("s_barrier" ::: "memory");
 }
 
-// Coordinates of one 256x256 output tile.
+// Coordinates of one 256x256 output tile, and the stages of it a unit of
+// work covers: ns stages from stage kb (both even: whole 256-K groups).
 struct Tile {
     int64_t m0, n0, m_end;
     const uint8_t *b, *bs;  // B operand and its rearranged scales (per expert when grouped)
+    int kb, ns;
+    int sp;  // split-tail slot (tile * split_s + range), or -1 for a whole tile
 };
 
 constexpr int GROUP_TABLE = 1024;  // experts whose tile table fits in LDS
 
-template <bool GROUPED, int CT>
+// SPLIT: the launch has a split tail (dense, BF16 C only).  A separate
+// instantiation, since carrying that path costs the other launches 1-4 %.
+template <bool GROUPED, int CT, bool SPLIT>
 __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t sA[2][STAGE_BYTES];
@@ -245,19 +260,31 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     // b % 8), and each XCD has its own L2: give XCD x a contiguous eighth of
     // the tiles, walked by its workgroups in step, so that tiles running
     // together on one XCD share A and B panels.
+    // A split tail's units are dealt the same way: XCD x takes a contiguous
+    // eighth of them, so the K ranges of one tile run on one XCD.
+    const int64_t whole = GROUPED ? ntiles : p.dp_tiles;
     int64_t t_first, t_step, t_end;
     if (gridDim.x % 8 == 0) {
-        const int64_t x = blockIdx.x & 7, per_xcd = (ntiles + 7) / 8;
+        const int64_t x = blockIdx.x & 7, per_xcd = (whole + 7) / 8;
         t_first = x * per_xcd + (blockIdx.x >> 3);
         t_step = gridDim.x >> 3;
-        t_end = min((x + 1) * per_xcd, ntiles);
+        t_end = min((x + 1) * per_xcd, whole);
     } else {
         t_first = blockIdx.x;
         t_step = gridDim.x;
-        t_end = ntiles;
+        t_end = whole;
     }
     const int64_t my_tiles = t_first < t_end ? (t_end - t_first + t_step - 1) / t_step : 0;
-    if (my_tiles == 0)
+    int split_u = -1;  // this workgroup's split-tail unit
+    if (SPLIT) {
+        const int64_t u = gridDim.x % 8 == 0 ? (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3)
+                                             : (int64_t)blockIdx.x;
+        if (u < (int64_t)p.split_tiles * p.split_s)
+            split_u = (int)u;
+    }
+    const int has_split = split_u >= 0 ? 1 : 0;
+    const int64_t my_units = my_tiles + has_split;
+    if (my_units == 0)
         return;
 
     // tile number -> coordinates
@@ -335,6 +362,25 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
         c.bs = p.bs + g * p.bs_group_stride;
         return c;
     };
+    // unit k of this workgroup: its split-tail unit first, then whole tiles
+    auto unit = [&](int64_t k) -> Tile {
+        if (SPLIT && has_split && k == 0) {
+            const int r = split_u / p.split_s, sidx = split_u - r * p.split_s;
+            Tile c = coords(p.dp_tiles + r);
+            const int KG = KITP / 2;  // 256-K groups
+            const int g0 = (int)((int64_t)sidx * KG / p.split_s);
+            const int g1 = (int)((int64_t)(sidx + 1) * KG / p.split_s);
+            c.kb = 2 * g0;
+            c.ns = 2 * (g1 - g0);
+            c.sp = split_u;
+            return c;
+        }
+        Tile c = coords(t_first + (k - has_split) * t_step);
+        c.kb = 0;
+        c.ns = KITP;
+        c.sp = -1;
+        return c;
+    };
 
     // ---- direct-to-LDS plan.  Instruction i of this wave fills LDS rows
     // 8*(8*wave + i) .. +8 of a stage; lane -> row + lane/8, slot lane%8,
@@ -362,7 +408,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
         const uint32_t bb = (uint32_t)(min(N - T.n0, (int64_t)BN) * p.ld_b);
         const __amdgpu_buffer_rsrc_t ra = byte_range(p.a + T.m0 * p.ld_a, live ? ab : 0u);
         const __amdgpu_buffer_rsrc_t rb = byte_range(T.b + T.n0 * p.ld_b, live ? bb : 0u);
-        const uint32_t koff = (uint32_t)st * BK;  // scalar offset, added after the range check
+        const uint32_t koff = (uint32_t)(T.kb + st) * BK;  // scalar offset, added after the range check
 #pragma unroll
         for (int i = half * (DMA_PER_WAVE / 2); i < (half + 1) * (DMA_PER_WAVE / 2); i++) {
             const uint32_t off = (uint32_t)(buf * STAGE_BYTES + 1024 * (DMA_PER_WAVE * wave + i));
@@ -484,18 +530,18 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
         }
     }
 
-    // ---- the workgroup's stages: tiles t_first, + t_step, ..., KITP
-    // stages each, numbered continuously so the pipeline runs across tiles
-    const int64_t total = my_tiles * KITP;
-    Tile cur = coords(t_first);
+    // ---- the workgroup's stages: its units' stages numbered continuously,
+    // so the pipeline runs across units
+    Tile cur = unit(0);
+    const int64_t total = (my_units - has_split) * KITP + (has_split ? cur.ns : 0);
     uint32_t cur_srd = scale_lanes(cur);
 
     // prologue: scale words of the first group, stages 0 and 1 in flight
-    dma_scales(cur, 0, true);
-    dma_stage(cur, 0, 0, true, 0);
-    dma_stage(cur, 0, 0, true, 1);
-    dma_stage(cur, 1, 1, 1 < KIT, 0);
-    dma_stage(cur, 1, 1, 1 < KIT, 1);
+    dma_scales(cur, cur.kb >> 1, true);
+    dma_stage(cur, 0, 0, cur.kb < KIT, 0);
+    dma_stage(cur, 0, 0, cur.kb < KIT, 1);
+    dma_stage(cur, 1, 1, cur.kb + 1 < KIT, 0);
+    dma_stage(cur, 1, 1, cur.kb + 1 < KIT, 1);
     MX_WAIT_VMCNT(0);  // stages 0 and 1 (the first stage's wait is the relaxed one)
     lds_ring_barrier();
     uint32_t wa[TM], wb[TN];
@@ -510,6 +556,83 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                     \
                 FB[i], FA[j], acc[i][j], 0, 0, 0, sbv, 0, (int)(wa[j] >> (SHIFT)));          \
     }
+
+    // BF16 stores of one 32-row band j of the wave's C, sub-tile i in x[i].
+    // Register group q of lane (h, r) holds columns 8q + 4h .. +3 of
+    // row r (r = lane & 31) as two packed words.  Swapping group 1 of
+    // the lower half-wave with group 0 of the upper one
+    // (v_permlane32_swap), and group 3 with group 2, leaves lane
+    // (h, r) with 16-byte chunks h (columns 8h..8h+7) in s1 and 2 + h
+    // in s2.  Swapping the odd 16-lane rows of s1 with the even ones of
+    // s2 (v_permlane16_swap) then gathers all four chunks of rows 0-15
+    // in s1 and of rows 16-31 in s2, lane l holding row l & 15.  Last,
+    // within each 16-lane row, lanes 8-15 of sub-tile i trade with
+    // lanes 0-7 of sub-tile i + 1 (DPP row shifts by 8, bank-masked):
+    // then one store writes whole 128-byte lines, 64 bytes of each of
+    // the two sub-tiles, of 8 rows.
+    // The stores are non-temporal.  C is never read back here, and
+    // with the default policy each round of tiles' output fills the
+    // L2 and evicts the operand panels that the next round reuses;
+    // streaming whole lines keeps them resident.
+    auto store_band = [&](const __amdgpu_buffer_rsrc_t &rc, int j, const v16f *x) {
+        const uint32_t row8 = (uint32_t)(8 * p.ld_c * CE);
+        {
+            uint32_t s1[TN][4], s2[TN][4];
+#pragma unroll
+            for (int i = 0; i < TN; i++) {
+                uint32_t w[4][2];
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    w[q][0] = pack_bf16x2(x[i][4 * q + 0], x[i][4 * q + 1]);
+                    w[q][1] = pack_bf16x2(x[i][4 * q + 2], x[i][4 * q + 3]);
+                }
+#pragma unroll
+                for (int q = 0; q < 4; q += 2) {
+#pragma unroll
+                    for (int d = 0; d < 2; d++) {
+                        const auto sw = __builtin_amdgcn_permlane32_swap(w[q][d], w[q + 1][d],
+                                                                         false, false);
+                        w[q][d] = sw[0];
+                        w[q + 1][d] = sw[1];
+                    }
+                }
+                const uint32_t t1[4] = {w[0][0], w[0][1], w[1][0], w[1][1]};
+                const uint32_t t2[4] = {w[2][0], w[2][1], w[3][0], w[3][1]};
+#pragma unroll
+                for (int d = 0; d < 4; d++) {
+                    const auto sw = __builtin_amdgcn_permlane16_swap(t1[d], t2[d], false, false);
+                    s1[i][d] = sw[0];
+                    s2[i][d] = sw[1];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < TN; i += 2) {
+                // row_shr:8 into lanes 8-15 (banks 2, 3), row_shl:8 into lanes 0-7
+                uint32_t x1[4], y1[4], x2[4], y2[4];
+#pragma unroll
+                for (int d = 0; d < 4; d++) {
+                    x1[d] = (uint32_t)__builtin_amdgcn_update_dpp((int)s1[i][d], (int)s1[i + 1][d],
+                                                                  0x118, 0xF, 0xC, false);
+                    y1[d] = (uint32_t)__builtin_amdgcn_update_dpp((int)s1[i + 1][d], (int)s1[i][d],
+                                                                  0x108, 0xF, 0x3, false);
+                    x2[d] = (uint32_t)__builtin_amdgcn_update_dpp((int)s2[i][d], (int)s2[i + 1][d],
+                                                                  0x118, 0xF, 0xC, false);
+                    y2[d] = (uint32_t)__builtin_amdgcn_update_dpp((int)s2[i + 1][d], (int)s2[i][d],
+                                                                  0x108, 0xF, 0x3, false);
+                }
+                const uint32_t col = (uint32_t)(i * 32 * CE);
+                constexpr int NT = 2;  // cache policy: non-temporal
+                __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]},
+                                                       rc, c_off[j] + col, 0, NT);
+                __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)y1[0], (int)y1[1], (int)y1[2], (int)y1[3]},
+                                                       rc, c_off[j] + row8 + col, 0, NT);
+                __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)x2[0], (int)x2[1], (int)x2[2], (int)x2[3]},
+                                                       rc, c_off_hi[j] + col, 0, NT);
+                __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)y2[0], (int)y2[1], (int)y2[2], (int)y2[3]},
+                                                       rc, c_off_hi[j] + row8 + col, 0, NT);
+            }
+        }
+    };
 
     // Stage gs uses buffer gs & 1 and scale bytes 2*(gs & 1) and 2*(gs & 1)+1
     // of the current 256-K words (a tile has an even number of stages, so
@@ -546,22 +669,22 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     // is exact after the BF16 whole-width stores and conservative after the
     // FP32 ones (more stores); the other epilogue, and the prologue before
     // the first tile, wait for all of the wave's operations instead.
-    for (int64_t k = 0; k < my_tiles; k++) {
-        // the tile after this one (loaded during this tile's last two stages)
-        const Tile nxt = k + 1 < my_tiles ? coords(t_first + (k + 1) * t_step) : cur;
+    for (int64_t k = 0; k < my_units; k++) {
+        // the unit after this one (loaded during this unit's last two stages)
+        const Tile nxt = k + 1 < my_units ? unit(k + 1) : cur;
         const uint32_t nxt_srd = scale_lanes(nxt);
-        for (int st = 0; st < KITP; st++, gs++) {
+        for (int st = 0; st < cur.ns; st++, gs++) {
             const int buf = (int)(gs & 1);
             const int shift = 16 * buf;
-            // stage gs + 2: stage st + 2 of this tile, or the next tile's first two
-            const bool same = st + 2 < KITP;
-            const int st2 = same ? st + 2 : st + 2 - KITP;
+            // stage gs + 2: stage st + 2 of this unit, or the next unit's first two
+            const bool same = st + 2 < cur.ns;
+            const int st2 = same ? st + 2 : st + 2 - cur.ns;
             const Tile ld = same ? cur : nxt;
             const bool live = gs + 2 < total;
             const bool live_group = ((gs + 2) & ~(int64_t)1) < total;  // the group's first stage
             // 1.
             read_frags(buf, 1, fa1, fb1);
-            dma_scales(ld, st2 >> 1, live_group);
+            dma_scales(ld, (ld.kb + st2) >> 1, live_group);
             MX_MFMA_STEP(fa0, fb0, shift, 0, TN)
 #pragma unroll
             for (int q = 0; q < 3; q++) {
@@ -578,7 +701,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             lds_ring_barrier();
             __builtin_amdgcn_sched_barrier(0);
             // 2.
-            dma_stage(ld, st2, buf, live && st2 < KIT, 0);
+            dma_stage(ld, st2, buf, live && ld.kb + st2 < KIT, 0);
             MX_MFMA_STEP(fa1, fb1, shift + 8, 0, TN / 2)
 #pragma unroll
             for (int q = 0; q < 8; q++) {  // 8 matrix-core, 8 loads
@@ -591,8 +714,8 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             asm volatile("s_barrier" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
             uint32_t na[TM], nb[TN];
-            read_scales(st + 1 < KITP ? cur_srd : nxt_srd, na, nb);
-            dma_stage(ld, st2, buf, live && st2 < KIT, 1);
+            read_scales(st + 1 < cur.ns ? cur_srd : nxt_srd, na, nb);
+            dma_stage(ld, st2, buf, live && ld.kb + st2 < KIT, 1);
             read_frags(buf ^ 1, 0, fa0, fb0);
             MX_MFMA_STEP(fa1, fb1, shift + 8, TN / 2, TN)
             __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);  // scale words
@@ -612,8 +735,32 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             __builtin_amdgcn_sched_barrier(0);
         }
 
-        // ---- epilogue: lane holds C[m][n..n+3] for each register group
-        if ((CT == 0 ? p.vec16 : p.vec_store) && cur.n0 + BN <= N) {
+        // ---- split-tail unit (BF16 C, whole-width tiles only): its FP32
+        // partial tile goes to its workspace slot, lane-major per sub-tile
+        // and register group (64 lanes x 16 bytes per store, whole lines,
+        // non-temporal: nothing here reads it back)
+        const bool split_unit = SPLIT && cur.sp >= 0;
+        if (split_unit) {
+            const __amdgpu_buffer_rsrc_t rw = byte_range(p.ws, (uint32_t)(p.split_tiles * p.split_s) *
+                                                                   (uint32_t)(BM * BN * 4));
+            const uint32_t base = (uint32_t)cur.sp * (BM * BN * 4) + (uint32_t)(wave * (BM * BN / 4) + lane * 4) * 4;
+#pragma unroll
+            for (int i = 0; i < TN; i++)
+#pragma unroll
+                for (int j = 0; j < TM; j++) {
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        typedef float f4_t __attribute__((ext_vector_type(4)));
+                        const f4_t v{acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                     acc[i][j][4 * q + 3]};
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), rw,
+                                                               base + (uint32_t)(((i * TM + j) * 4 + q) * 1024), 0, 2);
+                    }
+#pragma unroll
+                    for (int v = 0; v < 16; v++)
+                        acc[i][j][v] = 0.0f;
+                }
+        } else         if ((CT == 0 ? p.vec16 : p.vec_store) && cur.n0 + BN <= N) {
             // whole-width tile: buffer stores relative to the tile's first
             // element; the range ends after the tile's last valid row, so the
             // stores of rows past it (past M, or past the expert) are dropped
@@ -622,82 +769,18 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                 byte_range((const uint8_t *)p.c + (cur.m0 * p.ld_c + cur.n0) * CE,
                            rows_valid * (uint32_t)(p.ld_c * CE));
             if (CT == 0) {
-                // Register group q of lane (h, r) holds columns 8q + 4h .. +3 of
-                // row r (r = lane & 31) as two packed words.  Swapping group 1 of
-                // the lower half-wave with group 0 of the upper one
-                // (v_permlane32_swap), and group 3 with group 2, leaves lane
-                // (h, r) with 16-byte chunks h (columns 8h..8h+7) in s1 and 2 + h
-                // in s2.  Swapping the odd 16-lane rows of s1 with the even ones of
-                // s2 (v_permlane16_swap) then gathers all four chunks of rows 0-15
-                // in s1 and of rows 16-31 in s2, lane l holding row l & 15.  Last,
-                // within each 16-lane row, lanes 8-15 of sub-tile i trade with
-                // lanes 0-7 of sub-tile i + 1 (DPP row shifts by 8, bank-masked):
-                // then one store writes whole 128-byte lines, 64 bytes of each of
-                // the two sub-tiles, of 8 rows.
-                // The stores are non-temporal.  C is never read back here, and
-                // with the default policy each round of tiles' output fills the
-                // L2 and evicts the operand panels that the next round reuses;
-                // streaming whole lines keeps them resident.
-                const uint32_t row8 = (uint32_t)(8 * p.ld_c * CE);
 #pragma unroll
                 for (int j = 0; j < TM; j++) {
-                    uint32_t s1[TN][4], s2[TN][4];
+                    v16f x[TN];
 #pragma unroll
-                    for (int i = 0; i < TN; i++) {
-                        uint32_t w[4][2];
+                    for (int i = 0; i < TN; i++)
+                        x[i] = acc[i][j];
+                    store_band(rc, j, x);
 #pragma unroll
-                        for (int q = 0; q < 4; q++) {
-                            w[q][0] = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
-                            w[q][1] = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-                        }
-#pragma unroll
-                        for (int q = 0; q < 4; q += 2) {
-#pragma unroll
-                            for (int d = 0; d < 2; d++) {
-                                const auto sw = __builtin_amdgcn_permlane32_swap(w[q][d], w[q + 1][d],
-                                                                                 false, false);
-                                w[q][d] = sw[0];
-                                w[q + 1][d] = sw[1];
-                            }
-                        }
-                        const uint32_t t1[4] = {w[0][0], w[0][1], w[1][0], w[1][1]};
-                        const uint32_t t2[4] = {w[2][0], w[2][1], w[3][0], w[3][1]};
-#pragma unroll
-                        for (int d = 0; d < 4; d++) {
-                            const auto sw = __builtin_amdgcn_permlane16_swap(t1[d], t2[d], false, false);
-                            s1[i][d] = sw[0];
-                            s2[i][d] = sw[1];
-                        }
+                    for (int i = 0; i < TN; i++)
 #pragma unroll
                         for (int v = 0; v < 16; v++)
                             acc[i][j][v] = 0.0f;
-                    }
-#pragma unroll
-                    for (int i = 0; i < TN; i += 2) {
-                        // row_shr:8 into lanes 8-15 (banks 2, 3), row_shl:8 into lanes 0-7
-                        uint32_t x1[4], y1[4], x2[4], y2[4];
-#pragma unroll
-                        for (int d = 0; d < 4; d++) {
-                            x1[d] = (uint32_t)__builtin_amdgcn_update_dpp((int)s1[i][d], (int)s1[i + 1][d],
-                                                                          0x118, 0xF, 0xC, false);
-                            y1[d] = (uint32_t)__builtin_amdgcn_update_dpp((int)s1[i + 1][d], (int)s1[i][d],
-                                                                          0x108, 0xF, 0x3, false);
-                            x2[d] = (uint32_t)__builtin_amdgcn_update_dpp((int)s2[i][d], (int)s2[i + 1][d],
-                                                                          0x118, 0xF, 0xC, false);
-                            y2[d] = (uint32_t)__builtin_amdgcn_update_dpp((int)s2[i + 1][d], (int)s2[i][d],
-                                                                          0x108, 0xF, 0x3, false);
-                        }
-                        const uint32_t col = (uint32_t)(i * 32 * CE);
-                        constexpr int NT = 2;  // cache policy: non-temporal
-                        __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]},
-                                                               rc, c_off[j] + col, 0, NT);
-                        __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)y1[0], (int)y1[1], (int)y1[2], (int)y1[3]},
-                                                               rc, c_off[j] + row8 + col, 0, NT);
-                        __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)x2[0], (int)x2[1], (int)x2[2], (int)x2[3]},
-                                                               rc, c_off_hi[j] + col, 0, NT);
-                        __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)y2[0], (int)y2[1], (int)y2[2], (int)y2[3]},
-                                                               rc, c_off_hi[j] + row8 + col, 0, NT);
-                    }
                 }
             } else {
 #pragma unroll
@@ -762,6 +845,8 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             }
             MX_WAIT_VMCNT(0);  // a varying number of stores: the next wait cannot count them
         }
+        // (a split-tail unit issues 64 stores, more than the next unit's
+        // relaxed first wait allows, so that wait still covers its loads)
         cur = nxt;
         cur_srd = nxt_srd;
         // re-read the next stage's step-0 fragments, so that the copy read in
@@ -807,6 +892,74 @@ static int cu_count()
     return cache[dev];
 }
 
+// Stream-ordered workspace of the split tail: a memory pool per device that
+// keeps freed blocks for reuse (release threshold at its maximum), so after
+// the first call an allocation costs no driver round trip.  The pool is the
+// library's own; the device's default pool is left as the caller set it.
+static hipMemPool_t split_pool()
+{
+    static std::mutex mu;
+    static hipMemPool_t pools[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (pools[dev] == nullptr) {
+        hipMemPoolProps props{};
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        if (hipMemPoolCreate(&pool, &props) != hipSuccess)
+            return nullptr;
+        uint64_t keep = ~(uint64_t)0;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        pools[dev] = pool;
+    }
+    return pools[dev];
+}
+
+// Sums of the split tail: thread t of tile r's 16384 takes float4 t of the
+// tile's slots (the partial-tile layout above: wave, sub-tile (i, j),
+// register group q, lane), adds the split_s slots in range order and writes
+// the four BF16 of C they hold, row wm*128 + 32j + (lane & 31), columns
+// wn*128 + 32i + 8q + 4(lane >> 5) .. +3.
+__global__ __launch_bounds__(256) void split_reduce_kernel(GemmParams p)
+{
+    const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int r = (int)(gt >> 14);
+    const int t = (int)(gt & 16383);
+    if (r >= p.split_tiles)
+        return;
+    const int wave = t >> 12, idx = (t >> 6) & 63, lane = t & 63;
+    const int q = idx & 3, j = (idx >> 2) & 3, i = idx >> 4;
+    const int row = (wave & 1) * 128 + j * 32 + (lane & 31);
+    const int col = (wave >> 1) * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
+    // tile dp_tiles + r: the kernel's tile order (GROUP_M tile-rows at a time)
+    const int64_t pid = p.dp_tiles + r;
+    const int64_t per_group = GROUP_M * p.tiles_n;
+    const int64_t grp = pid / per_group;
+    const int64_t first_m = grp * GROUP_M;
+    const int64_t gm = min(p.tiles_m - first_m, (int64_t)GROUP_M);
+    const int64_t in = pid - grp * per_group;
+    const int64_t m = (first_m + in % gm) * BM + row;
+    const int64_t n = (in / gm) * BN + col;
+    if (m >= p.M)
+        return;
+    const float4 *src = reinterpret_cast<const float4 *>(p.ws) + (int64_t)r * p.split_s * (BM * BN / 4) + t;
+    float4 a = src[0];
+    for (int sidx = 1; sidx < p.split_s; sidx++) {
+        const float4 b = src[(int64_t)sidx * (BM * BN / 4)];
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+    }
+    *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.c) + m * p.ld_c + n) =
+        make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
+}
+
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t ld_a,
                        const void *a_s, const void *b_q, int64_t ld_b, const void *b_s,
                        void *c, int64_t ld_c, int c_dtype, hipStream_t stream)
@@ -829,12 +982,56 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t
     p.bs_bytes = (uint32_t)scale_bytes(N, K);
     p.vec_store = vec_ok(c, ld_c, c_dtype);
     p.vec16 = vec16_ok(c, ld_c, c_dtype);
-    const unsigned grid = (unsigned)std::min<int64_t>(p.tiles_m * p.tiles_n, cu_count());
-    if (c_dtype == 0)
-        hipLaunchKernelGGL((mx_gemm_kernel<false, 0>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
+    const int64_t tiles = p.tiles_m * p.tiles_n;
+    const int64_t cus = cu_count();
+    p.dp_tiles = tiles;
+    unsigned grid = (unsigned)std::min<int64_t>(tiles, cus);
+    // Split tail.  With T tiles on P compute units the last R = T mod P
+    // tiles form a partial round that leaves most units idle.  Cut each of
+    // them into S K ranges (at most P / R, at most one per 256-K group), one
+    // workgroup per range: the round then costs about 1/S of a tile, plus
+    // writing and summing R * S partial tiles of 256 KiB.  A tile costs
+    // ~1.7 us per 128-K stage and summing one partial ~0.065 us, so
+    // S ~ sqrt(26 * stages / R) balances the two.  Only BF16 C stored by
+    // whole-line stores (every tile full width) is split; without the
+    // workspace the call runs unsplit.
+    void *ws = nullptr;
+    const int64_t groups = (K / BK + 1) / 2;
+    const int64_t rem = tiles % cus;
+    if (rem > 0 && groups >= 2 && c_dtype == 0 && p.vec16 && N % BN == 0) {
+        const int64_t balance = std::max<int64_t>(2, (int64_t)std::sqrt(26.0 * 2 * groups / (double)rem));
+        const int64_t S = std::min<int64_t>(std::min<int64_t>(cus / rem, groups), balance);
+        hipMemPool_t pool = S >= 2 ? split_pool() : nullptr;
+        const size_t part_bytes = (size_t)(rem * S) * (BM * BN * sizeof(float));
+        if (pool != nullptr && hipMallocFromPoolAsync(&ws, part_bytes, pool, stream) == hipSuccess) {
+            p.dp_tiles = tiles - rem;
+            p.split_tiles = (int)rem;
+            p.split_s = (int)S;
+            p.ws = (float *)ws;
+            grid = (unsigned)std::max<int64_t>(std::min<int64_t>(p.dp_tiles, cus), rem * S);
+        } else {
+            ws = nullptr;
+            (void)hipGetLastError();  // a failed allocation leaves the unsplit schedule
+        }
+    }
+    if (ws != nullptr)
+        hipLaunchKernelGGL((mx_gemm_kernel<false, 0, true>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
+    else if (c_dtype == 0)
+        hipLaunchKernelGGL((mx_gemm_kernel<false, 0, false>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
     else
-        hipLaunchKernelGGL((mx_gemm_kernel<false, 1>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
-    return hipGetLastError();
+        hipLaunchKernelGGL((mx_gemm_kernel<false, 1, false>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
+    hipError_t err = hipGetLastError();
+    if (ws != nullptr) {
+        if (err == hipSuccess) {
+            hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)(p.split_tiles * (BM * BN / 4 / 256))),
+                               dim3(256), 0, stream, p);
+            err = hipGetLastError();
+        }
+        const hipError_t fe = hipFreeAsync(ws, stream);
+        if (err == hipSuccess)
+            err = fe;
+    }
+    return err;
 }
 
 hipError_t launch_grouped_gemm(int64_t G, int64_t M_total, int64_t N, int64_t K,
@@ -867,9 +1064,9 @@ hipError_t launch_grouped_gemm(int64_t G, int64_t M_total, int64_t N, int64_t K,
     // each walking the tiles the kernel enumerates
     const unsigned grid = (unsigned)cu_count();
     if (c_dtype == 0)
-        hipLaunchKernelGGL((mx_gemm_kernel<true, 0>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
+        hipLaunchKernelGGL((mx_gemm_kernel<true, 0, false>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
     else
-        hipLaunchKernelGGL((mx_gemm_kernel<true, 1>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
+        hipLaunchKernelGGL((mx_gemm_kernel<true, 1, false>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
     return hipGetLastError();
 }
 

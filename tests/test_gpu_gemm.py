@@ -136,6 +136,40 @@ def test_stale_swizzled_scales_detected(gpu_lib):
     assert_gemm_close(C_fresh, r, "fresh")
 
 
+@pytest.mark.parametrize("M,N,K", [(700, 768, 512), (512, 512, 2048), (300, 256, 1280),
+                                   (256, 512, 1152), (33, 256, 4096)])
+def test_split_tail_matches_oracle(gpu_lib, M, N, K):
+    """Tile counts that leave a partial round of workgroups: the leftover
+    tiles are cut into K ranges of whole 256-K groups (2 to 8 ranges here,
+    one group per range for K = 1280, the padded half group for K = 1152)
+    whose FP32 partial tiles are summed by the last range to finish."""
+    mx = gpu_lib
+    rng = np.random.default_rng(M + N + K)
+    qa, sa = random_mx_operand(rng, M, K)
+    qb, sb = random_mx_operand(rng, N, K)
+    C = _run(mx, qa, sa, qb, sb, torch.bfloat16)
+    assert_gemm_close(C, gemm_ref(qa, sa, qb, sb), f"split tail {M}x{N}x{K}")
+    assert torch.equal(C, _run(mx, qa, sa, qb, sb, torch.bfloat16))
+
+
+def test_split_tail_after_full_rounds(gpu_lib):
+    """272 tiles on 256 compute units: one whole tile per workgroup, then the
+    last 16 tiles split in two K ranges; sampled outputs, the split rows
+    (the last 256-row band) sampled densely."""
+    from gpu_util import check_sampled, sample_entries
+    mx = gpu_lib
+    M, N, K = 4352, 4096, 512
+    rng = np.random.default_rng(272)
+    qa, sa = random_mx_operand(rng, M, K)
+    qb, sb = random_mx_operand(rng, N, K)
+    C = _run(mx, qa, sa, qb, sb, torch.bfloat16)
+    rows, cols = sample_entries(rng, M, N)
+    rows = np.concatenate([rows, rng.integers(M - 256, M, size=2048)])
+    cols = np.concatenate([cols, rng.integers(0, N, size=2048)])
+    check_sampled(C, rows, cols, qa, sa, qb, sb, "split tail after a full round")
+    assert torch.equal(C, _run(mx, qa, sa, qb, sb, torch.bfloat16))
+
+
 def test_gemm_deterministic(gpu_lib):
     mx = gpu_lib
     rng = np.random.default_rng(21)
