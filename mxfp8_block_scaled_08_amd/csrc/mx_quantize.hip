@@ -93,19 +93,46 @@ __global__ __launch_bounds__(QR_THREADS) void quantize_rowwise_kernel(
 // a word for the scaled conversion, so the lane's 16 codes of a column form
 // one 16-byte store, and the eight lanes of a column write one full 128-byte
 // line of qt.  Four waves side by side make a 128 x 256 workgroup tile.
+//
+// Tile order.  Workgroup b runs on XCD b mod 8.  For a wide matrix (at least
+// QC_WIDE column tiles) XCD x takes a contiguous range of tiles numbered in
+// groups of QC_GROUP_R tile-rows (tile-row fastest), so the tiles it runs
+// together form a compact block: long contiguous runs of both the rows of x
+// it reads and the rows of qt it writes (12288 x 24576: 4.3 -> 4.9 TB/s).
+// Otherwise tiles go in row-major order, which gives XCD x the column tiles
+// c = x (mod 8): for a tall matrix of few column tiles each XCD then writes
+// whole rows of qt in sequence (196608 x 2048: 4.95 TB/s against 4.6 with
+// the grouped order).
 
 constexpr int QC_THREADS = 256;
 constexpr int QC_TILE_R = 128;
 constexpr int QC_TILE_C = 256;
+constexpr int QC_WIDE = 32;
+constexpr int QC_GROUP_R = 32;
 
 __global__ __launch_bounds__(QC_THREADS) void quantize_colwise_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t *__restrict__ qt, int64_t ld_qt, uint8_t *__restrict__ st, int64_t ld_st,
-    int64_t tiles_c)
+    int64_t tiles_r, int64_t tiles_c)
 {
     const int lane = threadIdx.x & 63;
     const int cg = lane & 7, half = (lane >> 3) & 1, rb = lane >> 4;
-    const int64_t tr = blockIdx.x / tiles_c, tc = blockIdx.x - tr * tiles_c;
+    int64_t tr, tc;
+    if (tiles_c >= QC_WIDE) {
+        // the grid is a multiple of 8; numbers past the last tile do nothing
+        const int64_t t = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+        if (t >= tiles_r * tiles_c)
+            return;
+        const int64_t per_group = QC_GROUP_R * tiles_c;
+        const int64_t grp = t / per_group, first = grp * QC_GROUP_R;
+        const int64_t gr = min(tiles_r - first, (int64_t)QC_GROUP_R);
+        const int64_t in = t - grp * per_group;
+        tr = first + in % gr;
+        tc = in / gr;
+    } else {
+        tr = blockIdx.x / tiles_c;
+        tc = blockIdx.x - tr * tiles_c;
+    }
     const int64_t c0 = tc * QC_TILE_C + (threadIdx.x >> 6) * 64 + cg * 8;
     const int64_t r0 = tr * QC_TILE_R + rb * 32 + half * 16;
     // rows % 32 == 0 and cols % 8 == 0: a lane's rows and columns are either
@@ -243,10 +270,13 @@ hipError_t launch_quantize_colwise(const void *x, int64_t rows, int64_t cols, in
                                    hipStream_t stream)
 {
     const int64_t tiles_c = (cols + QC_TILE_C - 1) / QC_TILE_C;
-    const int64_t blocks = ((rows + QC_TILE_R - 1) / QC_TILE_R) * tiles_c;
+    const int64_t tiles_r = (rows + QC_TILE_R - 1) / QC_TILE_R;
+    int64_t blocks = tiles_r * tiles_c;
+    if (tiles_c >= QC_WIDE)
+        blocks = (blocks + 7) / 8 * 8;
     hipLaunchKernelGGL(quantize_colwise_kernel, dim3((unsigned)blocks), dim3(QC_THREADS), 0,
                        stream, (const uint16_t *)x, rows, cols, ld_x, (uint8_t *)qt, ld_qt,
-                       (uint8_t *)st, ld_st, tiles_c);
+                       (uint8_t *)st, ld_st, tiles_r, tiles_c);
     return hipGetLastError();
 }
 

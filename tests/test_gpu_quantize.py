@@ -136,7 +136,10 @@ def test_rowwise_strided_and_byte_views(gpu_lib):
 
 
 @pytest.mark.parametrize("rows,cols", [(32, 8), (64, 24), (128, 256), (160, 264), (4096, 1024),
-                                       (96, 4104)])
+                                       (96, 4104),
+                                       # 32+ column tiles: the grouped, per-XCD tile order, with
+                                       # a ragged last tile-row group and a grid padded to 8
+                                       (1184, 8200), (4224, 8192), (32, 16384)])
 def test_colwise_shapes(gpu_lib, rows, cols):
     mx = gpu_lib
     x = mxsynth.normal_bf16((rows, cols), 1e-3, rows * 13 + cols, 0.01, 50.0)
