@@ -13,6 +13,8 @@
  *   mx_quantize_rowwise   BF16 -> E4M3 + E8M0, 32-element blocks along rows
  *   mx_quantize_colwise   BF16 -> E4M3 + E8M0, 32-element blocks down columns
  *   mx_scale_swizzle      E8M0 [rows][kblocks] -> the GEMM's scale layout
+ *   mx_quantize_dual      both orientations from one read, scales already in
+ *                         the GEMM's layout
  *   mx_gemm               C = deq(A) . deq(B)^T, FP32 accumulation
  *   mx_grouped_gemm       the same per MoE expert over row groups
  *
@@ -64,7 +66,7 @@
 extern "C" {
 #endif
 
-#define MXFP8_ABI_VERSION 1
+#define MXFP8_ABI_VERSION 2
 
 typedef enum mx_status {
     MX_OK = 0,
@@ -145,6 +147,40 @@ int64_t mx_scale_swizzled_bytes(int64_t rows, int64_t kblocks);
  */
 mx_status mx_scale_swizzle(const void *s, int64_t rows, int64_t kblocks, int64_t ld_s,
                            void *s_swz, void *stream);
+
+/*
+ * Row-wise and column-wise quantization of the same tensor in one pass, with
+ * both scale sets written directly in the rearranged layout of
+ * mx_scale_swizzle.  The pages time "MXFP8 quantization" and "scale
+ * rearrangement" as separate kernel categories of the learner (Table 6); a
+ * weight needed by both the forward and the backward products is read once
+ * here instead of twice, and no rearrangement pass follows.
+ *   x       BF16 [rows][ld_x]
+ *   q       E4M3 [rows][ld_q]   = mx_quantize_rowwise's q
+ *   s_swz   the row-wise scales ([rows][cols/32]) rearranged: tile (rt, kt)
+ *           (rows 32rt.., blocks 8kt..) at byte offset (rt*s_tiles + kt)*256
+ *   qt      E4M3 [cols][ld_qt]  = mx_quantize_colwise's qt
+ *   st_swz  the column-wise scales ([cols][rows/32]) rearranged: tile
+ *           (rt, kt) at byte offset (rt*st_tiles + kt)*256
+ * With s_tiles = ceil(cols/256) and st_tiles = ceil(rows/256) the two
+ * buffers equal mx_scale_swizzle of mx_quantize_rowwise's s and
+ * mx_quantize_colwise's st, byte for byte (mx_scale_swizzled_bytes(rows,
+ * cols/32) and (cols, rows/32) bytes).  A larger tiles-per-row count, with
+ * the pointer advanced to the block's first tile, writes into the rearranged
+ * buffer of a larger operand: rows that follow other rows (rt offset), or K
+ * ranges that follow others (kt offset; then every call but the last along
+ * K needs a multiple of 256 in that direction, since a call writes whole
+ * tiles, 0x7F past its own blocks).
+ * Requirements: rows % 32 == 0 and cols % 32 == 0 (else MX_ERR_SHAPE);
+ * ld_x >= cols, ld_q >= cols, ld_qt >= rows, s_tiles >= ceil(cols/256),
+ * st_tiles >= ceil(rows/256) (else MX_ERR_INVALID_ARG); x, q, qt 16-byte
+ * aligned with ld_x % 8, ld_q % 16, ld_qt % 16 == 0 and s_swz, st_swz 4-byte
+ * aligned (else MX_ERR_ALIGN); no two of the five buffers overlap (else
+ * MX_ERR_OVERLAP).
+ */
+mx_status mx_quantize_dual(const void *x, int64_t rows, int64_t cols, int64_t ld_x, void *q,
+                           int64_t ld_q, void *s_swz, int64_t s_tiles, void *qt, int64_t ld_qt,
+                           void *st_swz, int64_t st_tiles, void *stream);
 
 /*
  * Dense block-scaled GEMM ("MXFP8 GEMMs" of the learner, paper Figure 1 and

@@ -75,6 +75,9 @@ def load() -> ctypes.CDLL:
         f.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp]
     L.mx_scale_swizzle.restype = ctypes.c_int
     L.mx_scale_swizzle.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp]
+    L.mx_quantize_dual.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                                   _i64, _vp]
+    L.mx_quantize_dual.restype = ctypes.c_int
     L.mx_gemm.restype = ctypes.c_int
     L.mx_gemm.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
                           ctypes.c_int, _vp]
@@ -196,6 +199,37 @@ def mx_scale_swizzle(s: torch.Tensor, out: Optional[torch.Tensor] = None,
                                  _dev(out, "out", torch.uint8), _stream(stream))
     _check("mx_scale_swizzle", st)
     return out
+
+
+def mx_quantize_dual(x: torch.Tensor, q: Optional[torch.Tensor] = None,
+                     s_swz: Optional[torch.Tensor] = None, qt: Optional[torch.Tensor] = None,
+                     st_swz: Optional[torch.Tensor] = None, s_tiles: Optional[int] = None,
+                     st_tiles: Optional[int] = None, stream=None):
+    """BF16 x[rows][cols] -> (q [rows][cols], s_swz, qt [cols][rows], st_swz): both
+    orientations, scales in the GEMM's rearranged layout (see mx_quantize_dual in
+    the header for s_tiles / st_tiles and writing into a larger buffer)."""
+    rows, cols = x.shape
+    dev = x.device
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if qt is None:
+        qt = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+    if s_tiles is None:
+        s_tiles = (cols // 32 + 7) // 8
+    if st_tiles is None:
+        st_tiles = (rows // 32 + 7) // 8
+    if s_swz is None:
+        s_swz = torch.empty(mx_scale_swizzled_bytes(rows, cols // 32), dtype=torch.uint8, device=dev)
+    if st_swz is None:
+        st_swz = torch.empty(mx_scale_swizzled_bytes(cols, rows // 32), dtype=torch.uint8, device=dev)
+    q, qt, s_swz, st_swz = _u8(q), _u8(qt), _u8(s_swz), _u8(st_swz)
+    st = load().mx_quantize_dual(_dev(x, "x", torch.bfloat16), rows, cols, _ld(x, "x"),
+                                 _dev(q, "q", torch.uint8), _ld(q, "q"),
+                                 _dev(s_swz, "s_swz", torch.uint8), s_tiles,
+                                 _dev(qt, "qt", torch.uint8), _ld(qt, "qt"),
+                                 _dev(st_swz, "st_swz", torch.uint8), st_tiles, _stream(stream))
+    _check("mx_quantize_dual", st)
+    return q, s_swz, qt, st_swz
 
 
 _OUT = {torch.bfloat16: MX_BF16, torch.float32: MX_F32}

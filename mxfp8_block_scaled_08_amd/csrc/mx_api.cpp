@@ -151,6 +151,55 @@ mx_status mx_quantize_colwise(const void *x, int64_t rows, int64_t cols, int64_t
                       fn);
 }
 
+mx_status mx_quantize_dual(const void *x, int64_t rows, int64_t cols, int64_t ld_x, void *q,
+                           int64_t ld_q, void *s_swz, int64_t s_tiles, void *qt, int64_t ld_qt,
+                           void *st_swz, int64_t st_tiles, void *stream)
+{
+    const char *fn = "mx_quantize_dual";
+    if (rows < 0 || cols < 0)
+        return fail(MX_ERR_INVALID_ARG, "%s: negative size rows=%lld cols=%lld", fn,
+                    (long long)rows, (long long)cols);
+    if (rows % 32 != 0 || cols % 32 != 0)
+        return fail(MX_ERR_SHAPE, "%s: rows=%lld and cols=%lld must be multiples of the 32-element block",
+                    fn, (long long)rows, (long long)cols);
+    if (ld_x < cols || ld_q < cols || ld_qt < rows)
+        return fail(MX_ERR_INVALID_ARG,
+                    "%s: leading dimension too small (ld_x=%lld ld_q=%lld ld_qt=%lld)", fn,
+                    (long long)ld_x, (long long)ld_q, (long long)ld_qt);
+    const int64_t kt_row = (cols / 32 + 7) / 8, kt_col = (rows / 32 + 7) / 8;
+    if (s_tiles < kt_row || st_tiles < kt_col)
+        return fail(MX_ERR_INVALID_ARG,
+                    "%s: tiles per rearranged row too small (s_tiles=%lld < %lld or st_tiles=%lld < %lld)",
+                    fn, (long long)s_tiles, (long long)kt_row, (long long)st_tiles, (long long)kt_col);
+    if (rows == 0 || cols == 0)
+        return ok();
+    if (!x || !q || !s_swz || !qt || !st_swz)
+        return fail(MX_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(qt, 16) || ld_x % 8 != 0 || ld_q % 16 != 0 ||
+        ld_qt % 16 != 0)
+        return fail(MX_ERR_ALIGN,
+                    "%s: x, q and qt need 16-byte aligned rows (ld_x %% 8, ld_q %% 16, ld_qt %% 16)", fn);
+    if (!aligned(s_swz, 4) || !aligned(st_swz, 4))
+        return fail(MX_ERR_ALIGN, "%s: s_swz and st_swz must be 4-byte aligned", fn);
+    // byte extents: the rearranged outputs span their last tile row's tiles
+    const int64_t ex = extent(rows, cols, ld_x, 2), eq = extent(rows, cols, ld_q, 1),
+                  eqt = extent(cols, rows, ld_qt, 1);
+    const int64_t es = ((rows / 32 - 1) * s_tiles + kt_row) * 256,
+                  est = ((cols / 32 - 1) * st_tiles + kt_col) * 256;
+    const void *outs[4] = {q, s_swz, qt, st_swz};
+    const int64_t lens[4] = {eq, es, eqt, est};
+    for (int i = 0; i < 4; i++) {
+        if (overlap(x, ex, outs[i], lens[i]))
+            return fail(MX_ERR_OVERLAP, "%s: input and an output overlap", fn);
+        for (int j = i + 1; j < 4; j++)
+            if (overlap(outs[i], lens[i], outs[j], lens[j]))
+                return fail(MX_ERR_OVERLAP, "%s: two outputs overlap", fn);
+    }
+    return hip_status(mx::launch_quantize_dual(x, rows, cols, ld_x, q, ld_q, s_swz, s_tiles, qt,
+                                               ld_qt, st_swz, st_tiles, (hipStream_t)stream),
+                      fn);
+}
+
 mx_status mx_scale_swizzle(const void *s, int64_t rows, int64_t kblocks, int64_t ld_s,
                            void *s_swz, void *stream)
 {

@@ -186,6 +186,144 @@ __global__ __launch_bounds__(QC_THREADS) void quantize_colwise_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Both orientations in one pass, scales straight into the rearranged layout
+// (the weight-sync pair: the row-wise operand of the forward product and the
+// column-wise one of the backward product from one read of the BF16 weight).
+// A 512-thread workgroup takes a 256 x 256 tile as 2 x 4 waves of the
+// column-wise kernel's 128 x 64 wave tile, so the column-wise half is that
+// kernel's.  Row-wise, lane (rb, half, cg) holds 8 columns of 16 rows; the
+// four lanes cg & ~3 .. | 3 of a row hold one 32-column block, whose maximum
+// they combine by two DPP quad exchanges; each lane converts its 8 elements
+// of each row and stores them (8 bytes; 256 contiguous bytes per row per
+// workgroup).  The tile's scales are exactly 8 rearranged 256-byte tiles per
+// orientation (256 rows x 8 blocks row-wise, 256 columns x 8 blocks
+// column-wise): the codes are placed in LDS at their rearranged positions
+// (byte (32h + r) * 4 + t of tile r / 32 for block 2t + h, the layout of
+// mx_scale_swizzle), the rest left 0x7F, and each thread then stores one
+// word of each, 256 contiguous bytes per tile.
+
+constexpr int QD_THREADS = 512;
+constexpr int QD_TILE = 256;
+
+__global__ __launch_bounds__(QD_THREADS) void quantize_dual_kernel(
+    const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    uint8_t *__restrict__ q, int64_t ld_q, uint8_t *__restrict__ s_swz, int64_t s_tiles,
+    uint8_t *__restrict__ qt, int64_t ld_qt, uint8_t *__restrict__ st_swz, int64_t st_tiles,
+    int64_t tiles_r, int64_t tiles_c)
+{
+    __shared__ uint32_t lds_s[8 * 64];   // row-wise scales: 8 rearranged tiles
+    __shared__ uint32_t lds_st[8 * 64];  // column-wise scales: 8 rearranged tiles
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wr = wave >> 2, wc = wave & 3;
+    const int cg = lane & 7, half = (lane >> 3) & 1, rb = lane >> 4;
+    int64_t tr, tc;
+    if (tiles_c >= QC_WIDE) {
+        const int64_t t = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+        if (t >= tiles_r * tiles_c)
+            return;
+        const int64_t per_group = QC_GROUP_R * tiles_c;
+        const int64_t grp = t / per_group, first = grp * QC_GROUP_R;
+        const int64_t gr = min(tiles_r - first, (int64_t)QC_GROUP_R);
+        const int64_t in = t - grp * per_group;
+        tr = first + in % gr;
+        tc = in / gr;
+    } else {
+        tr = blockIdx.x / tiles_c;
+        tc = blockIdx.x - tr * tiles_c;
+    }
+    const int64_t R0 = tr * QD_TILE, C0 = tc * QD_TILE;
+    const int64_t c0 = C0 + wc * 64 + cg * 8;
+    const int64_t r0 = R0 + wr * 128 + rb * 32 + half * 16;
+    // rows % 32 == 0 and cols % 32 == 0: a lane's rows and columns are all in
+    // range or all out, and so are its DPP partners (the other half of its
+    // column block, the other lanes of its row block)
+    const bool active = c0 < cols && r0 < rows;
+    lds_s[tid] = 0x7F7F7F7Fu;
+    lds_st[tid] = 0x7F7F7F7Fu;
+    const uint16_t *src = x + (active ? r0 * ld_x + c0 : 0);
+    uint4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++)
+        v[i] = *reinterpret_cast<const uint4 *>(src + i * ld_x);
+    uint32_t m[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        m[0] = pk_max_u16(m[0], mag2(v[i].x));
+        m[1] = pk_max_u16(m[1], mag2(v[i].y));
+        m[2] = pk_max_u16(m[2], mag2(v[i].z));
+        m[3] = pk_max_u16(m[3], mag2(v[i].w));
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k++)  // row_ror:8 - the other half of the column block
+        m[k] = pk_max_u16(m[k], (uint32_t)__builtin_amdgcn_mov_dpp((int)m[k], 0x128, 0xF, 0xF, false));
+    // row-wise block maxima: the lane's 8 columns, then its quad (quad_perm
+    // [1,0,3,2] and [2,3,0,1])
+    uint32_t rmax[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const uint32_t w = pk_max_u16(pk_max_u16(mag2(v[i].x), mag2(v[i].y)),
+                                      pk_max_u16(mag2(v[i].z), mag2(v[i].w)));
+        uint32_t a = max(w & 0xFFFFu, w >> 16);
+        a = max(a, (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0xB1, 0xF, 0xF, false));
+        a = max(a, (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0x4E, 0xF, 0xF, false));
+        rmax[i] = a;
+    }
+    __syncthreads();  // the 0x7F fill precedes every scale byte
+    uint8_t *bs = reinterpret_cast<uint8_t *>(lds_s);
+    uint8_t *bst = reinterpret_cast<uint8_t *>(lds_st);
+    if (active) {
+        // column-wise, as quantize_colwise_kernel
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const uint32_t c = scale_code((m[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+            const float sc = cvt_scale(c);
+            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+            uint32_t o[4];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const uint4 &a = v[4 * k], &b = v[4 * k + 1], &cc = v[4 * k + 2], &d = v[4 * k + 3];
+                const int wi = j >> 1;
+                const uint32_t wa = wi == 0 ? a.x : wi == 1 ? a.y : wi == 2 ? a.z : a.w;
+                const uint32_t wb = wi == 0 ? b.x : wi == 1 ? b.y : wi == 2 ? b.z : b.w;
+                const uint32_t wcw = wi == 0 ? cc.x : wi == 1 ? cc.y : wi == 2 ? cc.z : cc.w;
+                const uint32_t wd = wi == 0 ? d.x : wi == 1 ? d.y : wi == 2 ? d.z : d.w;
+                const uint32_t p01 = __builtin_amdgcn_perm(wb, wa, sel);
+                const uint32_t p23 = __builtin_amdgcn_perm(wd, wcw, sel);
+                o[k] = nan_block_select(cvt_x4(p01, p23, sc), c);
+            }
+            *reinterpret_cast<uint4 *>(qt + (c0 + j) * ld_qt + r0) = make_uint4(o[0], o[1], o[2], o[3]);
+            if (half == 0) {
+                // rearranged row = column wc*64 + cg*8 + j of the tile, block wr*4 + rb
+                const int col = wc * 64 + cg * 8 + j, blk = wr * 4 + rb;
+                bst[(col >> 5) * 256 + (32 * (blk & 1) + (col & 31)) * 4 + (blk >> 1)] = (uint8_t)c;
+            }
+        }
+        // row-wise
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const uint32_t c = scale_code(rmax[i]);
+            const float sc = cvt_scale(c);
+            const uint32_t o0 = nan_block_select(cvt_x4(v[i].x, v[i].y, sc), c);
+            const uint32_t o1 = nan_block_select(cvt_x4(v[i].z, v[i].w, sc), c);
+            *reinterpret_cast<uint2 *>(q + (r0 + i) * ld_q + c0) = make_uint2(o0, o1);
+            if ((cg & 3) == 0) {
+                // rearranged row = tile row wr*128 + rb*32 + half*16 + i, block wc*2 + cg/4
+                const int row = wr * 128 + rb * 32 + half * 16 + i, blk = wc * 2 + (cg >> 2);
+                bs[(row >> 5) * 256 + (32 * (blk & 1) + (row & 31)) * 4 + (blk >> 1)] = (uint8_t)c;
+            }
+        }
+    }
+    __syncthreads();
+    // thread -> word tid & 63 of rearranged tile tid >> 6 (its 32-row tile
+    // row of each orientation; the tile's 8 blocks are this tile's 256-K group)
+    const int t = tid >> 6, w = tid & 63;
+    if (R0 + 32 * t < rows)
+        reinterpret_cast<uint32_t *>(s_swz + ((R0 / 32 + t) * s_tiles + C0 / 256) * 256)[w] = lds_s[tid];
+    if (C0 + 32 * t < cols)
+        reinterpret_cast<uint32_t *>(st_swz + ((C0 / 32 + t) * st_tiles + R0 / 256) * 256)[w] = lds_st[tid];
+}
+
 // Scale rearrangement.  A half-wave takes one 32-row tile row rt and a run of
 // up to SW_KT consecutive 256-K groups kt; lane r owns row 32rt + r.  Per
 // group the lane reads the row's 8 scale bytes (blocks 8kt .. 8kt+7) as one
@@ -277,6 +415,21 @@ hipError_t launch_quantize_colwise(const void *x, int64_t rows, int64_t cols, in
     hipLaunchKernelGGL(quantize_colwise_kernel, dim3((unsigned)blocks), dim3(QC_THREADS), 0,
                        stream, (const uint16_t *)x, rows, cols, ld_x, (uint8_t *)qt, ld_qt,
                        (uint8_t *)st, ld_st, tiles_r, tiles_c);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_dual(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                                void *q, int64_t ld_q, void *s_swz, int64_t s_tiles, void *qt,
+                                int64_t ld_qt, void *st_swz, int64_t st_tiles, hipStream_t stream)
+{
+    const int64_t tiles_r = (rows + QD_TILE - 1) / QD_TILE;
+    const int64_t tiles_c = (cols + QD_TILE - 1) / QD_TILE;
+    int64_t blocks = tiles_r * tiles_c;
+    if (tiles_c >= QC_WIDE)
+        blocks = (blocks + 7) / 8 * 8;
+    hipLaunchKernelGGL(quantize_dual_kernel, dim3((unsigned)blocks), dim3(QD_THREADS), 0, stream,
+                       (const uint16_t *)x, rows, cols, ld_x, (uint8_t *)q, ld_q, (uint8_t *)s_swz,
+                       s_tiles, (uint8_t *)qt, ld_qt, (uint8_t *)st_swz, st_tiles, tiles_r, tiles_c);
     return hipGetLastError();
 }
 

@@ -33,12 +33,12 @@ def test_library_loads_and_exports_every_declared_symbol():
     L = mx.load()
     names = declared_functions()
     assert {"mx_quantize_rowwise", "mx_quantize_colwise", "mx_scale_swizzle", "mx_gemm",
-            "mx_grouped_gemm", "mx_scale_swizzled_bytes"} <= set(names)
+            "mx_grouped_gemm", "mx_scale_swizzled_bytes", "mx_quantize_dual"} <= set(names)
     raw = ctypes.CDLL(mx.lib_path())
     for n in names:
         assert hasattr(raw, n), f"{n} declared in include/mxfp8.h but not exported"
         assert hasattr(mx, n), f"{n} has no Python binding of the same name"
-    assert L.mx_abi_version() == 1
+    assert L.mx_abi_version() == 2
 
 
 def test_status_strings():
@@ -92,6 +92,39 @@ def test_quantize_colwise_validation():
     assert f(FAKE, 64, 64, 64, FAKE2 + 8, 64, FAKE3, 2, STREAM) == mx.MX_ERR_ALIGN
     assert f(FAKE, 64, 64, 64, FAKE + 4096, 64, FAKE3, 2, STREAM) == mx.MX_ERR_OVERLAP
     assert f(FAKE, 0, 64, 64, FAKE2, 0, FAKE3, 0, STREAM) == mx.MX_OK
+
+
+def test_quantize_dual_validation():
+    L = mx.load()
+    f = L.mx_quantize_dual
+    FAKE5, FAKE6 = 0x100000000, 0x140000000
+    # x[64][64]: q at FAKE2, s_swz at FAKE3 (2 tiles), qt at FAKE5, st_swz at FAKE6 (2 tiles)
+    good = [FAKE, 64, 64, 64, FAKE2, 64, FAKE3, 1, FAKE5, 64, FAKE6, 1, STREAM]
+
+    def call(**kw):
+        a = list(good)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a1=48) == mx.MX_ERR_SHAPE           # rows % 32
+    assert call(a2=48, a3=48, a5=48) == mx.MX_ERR_SHAPE  # cols % 32
+    assert call(a1=-32) == mx.MX_ERR_INVALID_ARG
+    assert call(a3=32) == mx.MX_ERR_INVALID_ARG      # ld_x < cols
+    assert call(a5=32) == mx.MX_ERR_INVALID_ARG      # ld_q < cols
+    assert call(a9=32) == mx.MX_ERR_INVALID_ARG      # ld_qt < rows
+    assert call(a2=512, a3=512, a5=512, a7=1) == mx.MX_ERR_INVALID_ARG  # s_tiles < ceil(512/256)
+    assert call(a1=512, a9=512, a11=1) == mx.MX_ERR_INVALID_ARG         # st_tiles < ceil(512/256)
+    assert "tiles" in _err(L)
+    assert call(a4=0) == mx.MX_ERR_INVALID_ARG       # null q
+    assert call(a0=FAKE + 2) == mx.MX_ERR_ALIGN
+    assert call(a8=FAKE5 + 8) == mx.MX_ERR_ALIGN
+    assert call(a6=FAKE3 + 2) == mx.MX_ERR_ALIGN
+    assert call(a9=72) == mx.MX_ERR_ALIGN            # ld_qt % 16
+    assert call(a4=FAKE + 128) == mx.MX_ERR_OVERLAP  # q inside x
+    assert call(a10=FAKE5 + 256) == mx.MX_ERR_OVERLAP  # st_swz inside qt
+    assert call(a6=FAKE2 + 64) == mx.MX_ERR_OVERLAP  # s_swz inside q
+    assert call(a1=0) == mx.MX_OK
+    assert call(a2=0, a3=0, a5=0) == mx.MX_OK
 
 
 def test_swizzle_validation():
