@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, 8 TB/s
 MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 / MXFP8 matrix peak, 5.0 PFLOP/s
 QUANT_BYTES_PER_ELEMENT = 2 + 1 + 1 / 32  # BF16 in, E4M3 out, E8M0 per 32
+DUAL_BYTES_PER_ELEMENT = 2 + 2 * (1 + 1 / 32)  # one BF16 read, both orientations out
 
 
 def parse():
@@ -168,23 +169,26 @@ def step(mx, I, o, T):
     """One pass of the hot path; T(category, fn, ...) times each launch."""
     W = I["W"]
     rq, cq, sw = mx.mx_quantize_rowwise, mx.mx_quantize_colwise, mx.mx_scale_swizzle
-    # 1. weight sync: row-wise into the fused forward operands
-    T("quant_row", rq, W["q"], o["qkv_q"][0:4096], o["qkv_s"][0:4096])
-    T("quant_row", rq, W["k"], o["qkv_q"][4096:5120], o["qkv_s"][4096:5120])
-    T("quant_row", rq, W["v"], o["qkv_q"][5120:6144], o["qkv_s"][5120:6144])
-    T("quant_row", rq, W["o"], o["o_q"], o["o_s"])
-    T("quant_row", rq, W["gate"], o["gu_q"][0:12288], o["gu_s"][0:12288])
-    T("quant_row", rq, W["up"], o["gu_q"][12288:24576], o["gu_s"][12288:24576])
-    T("quant_row", rq, W["down"], o["dn_q"], o["dn_s"])
-    #    column-wise: gate and up side by side into the backward operand of gate_up
-    T("quant_col", cq, W["gate"], o["guT_q"][:, 0:12288], o["guT_s"][:, 0:384])
-    T("quant_col", cq, W["up"], o["guT_q"][:, 12288:24576], o["guT_s"][:, 384:768])
-    for n, (qt, st) in o["colT"].items():
-        T("quant_col", cq, W[n], qt, st)
-    for name in ("qkv", "o", "gu", "dn", "guT"):
-        T("swizzle", sw, o[name + "_s"], o[name + "_swz"])
-    for n, (qt, st) in o["colT"].items():
-        T("swizzle", sw, st, o["colT_swz"][n])
+    # 1. weight sync: both orientations of every weight in one pass each, the
+    #    row-wise codes into the fused forward operands (q, k, v stacked; gate,
+    #    up stacked) and the column-wise ones into the backward operands (gate
+    #    and up side by side along K), scales straight into the GEMM layout
+    dq = mx.mx_quantize_dual
+    t16 = 4096 // 256  # rearranged tiles per row of a K = 4096 operand
+    for name, r0, r1 in (("q", 0, 4096), ("k", 4096, 5120), ("v", 5120, 6144)):
+        qt, _ = o["colT"][name]
+        T("quant_dual", dq, W[name], q=o["qkv_q"][r0:r1],
+          s_swz=o["qkv_swz"][(r0 // 32) * t16 * 256:], s_tiles=t16, qt=qt,
+          st_swz=o["colT_swz"][name])
+    T("quant_dual", dq, W["o"], q=o["o_q"], s_swz=o["o_swz"], qt=o["colT"]["o"][0],
+      st_swz=o["colT_swz"]["o"])
+    for name, r0, r1 in (("gate", 0, 12288), ("up", 12288, 24576)):
+        T("quant_dual", dq, W[name], q=o["gu_q"][r0:r1],
+          s_swz=o["gu_swz"][(r0 // 32) * t16 * 256:], s_tiles=t16,
+          qt=o["guT_q"][:, r0:r1], st_swz=o["guT_swz"][(r0 // 256) * 256:],
+          st_tiles=24576 // 256)
+    T("quant_dual", dq, W["down"], q=o["dn_q"], s_swz=o["dn_swz"], qt=o["colT"]["down"][0],
+      st_swz=o["colT_swz"]["down"])
     # 2. dense forward, M = 4608
     for name in ("xh", "xi"):
         T("quant_row", rq, I[name], o[name + "_q"], o[name + "_s"])
@@ -195,11 +199,10 @@ def step(mx, I, o, T):
     T("gemm", g, o["xh_q"], o["xh_swz"], o["gu_q"], o["gu_swz"], c=o["C_gu"])
     T("gemm", g, o["xi_q"], o["xi_swz"], o["dn_q"], o["dn_swz"], c=o["C_dn"])
     # 3. dense backward of gate_up, 12288 tokens
-    T("quant_row", rq, I["dy"], o["dy_q"], o["dy_s"])
-    T("quant_col", cq, I["dy"], o["dyT_q"], o["dyT_s"])
+    T("quant_dual", dq, I["dy"], q=o["dy_q"], s_swz=o["dy_swz"], qt=o["dyT_q"],
+      st_swz=o["dyT_swz"])
     T("quant_col", cq, I["x"], o["xT_q"], o["xT_s"])
-    for name in ("dy", "dyT", "xT"):
-        T("swizzle", sw, o[name + "_s"], o[name + "_swz"])
+    T("swizzle", sw, o["xT_s"], o["xT_swz"])
     T("gemm", g, o["dy_q"], o["dy_swz"], o["guT_q"], o["guT_swz"], c=o["C_dgrad"])
     T("gemm", g, o["dyT_q"], o["dyT_swz"], o["xT_q"], o["xT_swz"], c=o["C_wgrad"])
     # 4. MoE layer, grouped per expert
@@ -214,20 +217,20 @@ def step(mx, I, o, T):
 
 
 def work_per_step(I):
-    """Algorithmic work of one step: elements quantized per orientation, scale
-    bytes rearranged, GEMM FLOPs (dense and grouped)."""
+    """Algorithmic work of one step: elements quantized per orientation (those
+    quantized in both orientations by one dual pass counted in each), GEMM
+    FLOPs (dense and grouped)."""
     W = I["W"]
-    row_el = sum(w.numel() for w in W.values())                  # weight sync row-wise
-    col_el = sum(w.numel() for w in W.values())                  # weight sync column-wise
-    row_el += I["xh"].numel() + I["xi"].numel()                  # forward activations
-    row_el += I["dy"].numel()                                    # dgrad operand
-    col_el += I["dy"].numel() + I["x"].numel()                   # wgrad operands
+    dual_el = sum(w.numel() for w in W.values())                 # weight sync, both
+    dual_el += I["dy"].numel()                                   # dgrad + wgrad operand
+    row_el = dual_el + I["xh"].numel() + I["xi"].numel()         # + forward activations
     row_el += I["w_gu"].numel() + I["w_dn"].numel() + I["a_gu"].numel() + I["a_dn"].numel()
+    col_el = dual_el + I["x"].numel()                            # + wgrad activation operand
     M = I["M"]
     dense = (2 * 4608 * 6144 * 4096 + 2 * 4608 * 4096 * 4096 + 2 * 4608 * 24576 * 4096
              + 2 * 4608 * 4096 * 12288 + 2 * 12288 * 4096 * 24576 + 2 * 24576 * 4096 * 12288)
     grouped = 2 * M * 1536 * 2048 + 2 * M * 2048 * 768
-    return row_el, col_el, dense, grouped
+    return row_el, col_el, dual_el, dense, grouped
 
 
 def cpu_baseline(torch, mxsynth, row_el, col_el, flops):
@@ -324,18 +327,23 @@ def main():
     gpu_ms = start.elapsed_time(end)
     ms_per_step = gpu_ms / args.steps
 
-    row_el, col_el, dense, grouped = work_per_step(I)
+    row_el, col_el, dual_el, dense, grouped = work_per_step(I)
     flops = dense + grouped
     K = args.steps
-    q_bytes = (row_el + col_el) * QUANT_BYTES_PER_ELEMENT
-    qt = (T.totals.get("quant_row", 0) + T.totals.get("quant_col", 0)) / K  # ms
+    row_only, col_only = row_el - dual_el, col_el - dual_el
+    q_bytes = ((row_only + col_only) * QUANT_BYTES_PER_ELEMENT
+               + dual_el * DUAL_BYTES_PER_ELEMENT)
+    qt = (T.totals.get("quant_row", 0) + T.totals.get("quant_col", 0)
+          + T.totals.get("quant_dual", 0)) / K  # ms
     gemm_ms = T.totals["gemm"] / K
     ggemm_ms = T.totals["grouped_gemm"] / K
     ops = {
         "quantize_rowwise": {"ms": T.totals["quant_row"] / K,
-                             "GB/s": row_el * QUANT_BYTES_PER_ELEMENT / (T.totals["quant_row"] / K) / 1e6},
+                             "GB/s": row_only * QUANT_BYTES_PER_ELEMENT / (T.totals["quant_row"] / K) / 1e6},
         "quantize_colwise": {"ms": T.totals["quant_col"] / K,
-                             "GB/s": col_el * QUANT_BYTES_PER_ELEMENT / (T.totals["quant_col"] / K) / 1e6},
+                             "GB/s": col_only * QUANT_BYTES_PER_ELEMENT / (T.totals["quant_col"] / K) / 1e6},
+        "quantize_dual": {"ms": T.totals["quant_dual"] / K,
+                          "GB/s": dual_el * DUAL_BYTES_PER_ELEMENT / (T.totals["quant_dual"] / K) / 1e6},
         "scale_swizzle": {"ms": T.totals["swizzle"] / K, "launches": T.counts["swizzle"] // K},
         "dense_gemm": {"ms": gemm_ms, "TFLOP/s": dense / gemm_ms / 1e9},
         "grouped_gemm": {"ms": ggemm_ms, "TFLOP/s": grouped / ggemm_ms / 1e9},
@@ -364,7 +372,7 @@ def main():
         "data": "synthetic (seeded device draws; Qwen3-8B / Qwen3-30B-A3B layer shapes)",
         "config": {
             "workload": ("qwen3-layer-pass: weight-sync row+column MXFP8 quantize of one "
-                         "Qwen3-8B layer; dense fwd M=4608 (qkv, o, gate_up, down); dense bwd "
+                         "Qwen3-8B layer (one dual pass per weight); dense fwd M=4608 (qkv, o, gate_up, down); dense bwd "
                          "gate_up dgrad 12288x4096x24576 + wgrad 24576x4096x12288; Qwen3-30B-A3B "
                          "MoE grouped gate_up/down, 163840 rows, 128 experts, Zipf(1.1)"),
             "gemm_flop_per_step": flops,
