@@ -175,20 +175,19 @@ def step(mx, I, o, T):
     #    and up side by side along K), scales straight into the GEMM layout
     dq = mx.mx_quantize_dual
     t16 = 4096 // 256  # rearranged tiles per row of a K = 4096 operand
+    jobs = []
     for name, r0, r1 in (("q", 0, 4096), ("k", 4096, 5120), ("v", 5120, 6144)):
-        qt, _ = o["colT"][name]
-        T("quant_dual", dq, W[name], q=o["qkv_q"][r0:r1],
-          s_swz=o["qkv_swz"][(r0 // 32) * t16 * 256:], s_tiles=t16, qt=qt,
-          st_swz=o["colT_swz"][name])
-    T("quant_dual", dq, W["o"], q=o["o_q"], s_swz=o["o_swz"], qt=o["colT"]["o"][0],
-      st_swz=o["colT_swz"]["o"])
+        jobs.append(dict(x=W[name], q=o["qkv_q"][r0:r1], s_swz=o["qkv_swz"][(r0 // 32) * t16 * 256:],
+                         s_tiles=t16, qt=o["colT"][name][0], st_swz=o["colT_swz"][name]))
+    jobs.append(dict(x=W["o"], q=o["o_q"], s_swz=o["o_swz"], qt=o["colT"]["o"][0],
+                     st_swz=o["colT_swz"]["o"]))
     for name, r0, r1 in (("gate", 0, 12288), ("up", 12288, 24576)):
-        T("quant_dual", dq, W[name], q=o["gu_q"][r0:r1],
-          s_swz=o["gu_swz"][(r0 // 32) * t16 * 256:], s_tiles=t16,
-          qt=o["guT_q"][:, r0:r1], st_swz=o["guT_swz"][(r0 // 256) * 256:],
-          st_tiles=24576 // 256)
-    T("quant_dual", dq, W["down"], q=o["dn_q"], s_swz=o["dn_swz"], qt=o["colT"]["down"][0],
-      st_swz=o["colT_swz"]["down"])
+        jobs.append(dict(x=W[name], q=o["gu_q"][r0:r1], s_swz=o["gu_swz"][(r0 // 32) * t16 * 256:],
+                         s_tiles=t16, qt=o["guT_q"][:, r0:r1],
+                         st_swz=o["guT_swz"][(r0 // 256) * 256:], st_tiles=24576 // 256))
+    jobs.append(dict(x=W["down"], q=o["dn_q"], s_swz=o["dn_swz"], qt=o["colT"]["down"][0],
+                     st_swz=o["colT_swz"]["down"]))
+    T("quant_dual", mx.mx_quantize_dual_batch, jobs)
     # 2. dense forward, M = 4608
     for name in ("xh", "xi"):
         T("quant_row", rq, I[name], o[name + "_q"], o[name + "_s"])

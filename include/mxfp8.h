@@ -14,7 +14,8 @@
  *   mx_quantize_colwise   BF16 -> E4M3 + E8M0, 32-element blocks down columns
  *   mx_scale_swizzle      E8M0 [rows][kblocks] -> the GEMM's scale layout
  *   mx_quantize_dual      both orientations from one read, scales already in
- *                         the GEMM's layout
+ *                         the GEMM's layout (mx_quantize_dual_batch: several
+ *                         tensors in one launch)
  *   mx_gemm               C = deq(A) . deq(B)^T, FP32 accumulation
  *   mx_grouped_gemm       the same per MoE expert over row groups
  *
@@ -181,6 +182,32 @@ mx_status mx_scale_swizzle(const void *s, int64_t rows, int64_t kblocks, int64_t
 mx_status mx_quantize_dual(const void *x, int64_t rows, int64_t cols, int64_t ld_x, void *q,
                            int64_t ld_q, void *s_swz, int64_t s_tiles, void *qt, int64_t ld_qt,
                            void *st_swz, int64_t st_tiles, void *stream);
+
+/*
+ * Several mx_quantize_dual jobs in one launch (e.g. every weight of a layer
+ * at a synchronization), so that small tensors share the chip instead of
+ * each launching a partial wave.  jobs is a HOST array of n_jobs (0..16)
+ * descriptors, read before the call returns; each job has the meaning and
+ * requirements of mx_quantize_dual's arguments and is validated before
+ * anything is launched (messages name the job).  A job's input must not
+ * overlap another job's codes (else MX_ERR_OVERLAP).  Jobs may write
+ * disjoint parts of one output buffer (stacked or side-by-side operands);
+ * overlapping writes by two jobs give unspecified bytes there.
+ */
+#define MX_DUAL_MAX_JOBS 16
+typedef struct mx_dual_job {
+    const void *x;
+    int64_t rows, cols, ld_x;
+    void *q;
+    int64_t ld_q;
+    void *s_swz;
+    int64_t s_tiles;
+    void *qt;
+    int64_t ld_qt;
+    void *st_swz;
+    int64_t st_tiles;
+} mx_dual_job;
+mx_status mx_quantize_dual_batch(const mx_dual_job *jobs, int n_jobs, void *stream);
 
 /*
  * Dense block-scaled GEMM ("MXFP8 GEMMs" of the learner, paper Figure 1 and

@@ -78,6 +78,8 @@ def load() -> ctypes.CDLL:
     L.mx_quantize_dual.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
                                    _i64, _vp]
     L.mx_quantize_dual.restype = ctypes.c_int
+    L.mx_quantize_dual_batch.argtypes = [ctypes.c_void_p, ctypes.c_int, _vp]
+    L.mx_quantize_dual_batch.restype = ctypes.c_int
     L.mx_gemm.restype = ctypes.c_int
     L.mx_gemm.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
                           ctypes.c_int, _vp]
@@ -230,6 +232,34 @@ def mx_quantize_dual(x: torch.Tensor, q: Optional[torch.Tensor] = None,
                                  _dev(st_swz, "st_swz", torch.uint8), st_tiles, _stream(stream))
     _check("mx_quantize_dual", st)
     return q, s_swz, qt, st_swz
+
+
+class _DualJob(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("ld_x", ctypes.c_int64), ("q", ctypes.c_void_p), ("ld_q", ctypes.c_int64),
+                ("s_swz", ctypes.c_void_p), ("s_tiles", ctypes.c_int64),
+                ("qt", ctypes.c_void_p), ("ld_qt", ctypes.c_int64),
+                ("st_swz", ctypes.c_void_p), ("st_tiles", ctypes.c_int64)]
+
+
+def mx_quantize_dual_batch(jobs, stream=None) -> None:
+    """Several dual quantizations in one launch.  jobs: a sequence of dicts with
+    the device tensors x, q, s_swz, qt, st_swz and optionally s_tiles / st_tiles
+    (the meaning of mx_quantize_dual's arguments); outputs are written in place."""
+    arr = (_DualJob * max(len(jobs), 1))()
+    for i, j in enumerate(jobs):
+        x = j["x"]
+        rows, cols = x.shape
+        q, s_swz, qt, st_swz = (_u8(j[k]) for k in ("q", "s_swz", "qt", "st_swz"))
+        arr[i] = _DualJob(_dev(x, "x", torch.bfloat16), rows, cols, _ld(x, "x"),
+                          _dev(q, "q", torch.uint8), _ld(q, "q"),
+                          _dev(s_swz, "s_swz", torch.uint8),
+                          j.get("s_tiles", (cols // 32 + 7) // 8),
+                          _dev(qt, "qt", torch.uint8), _ld(qt, "qt"),
+                          _dev(st_swz, "st_swz", torch.uint8),
+                          j.get("st_tiles", (rows // 32 + 7) // 8))
+    st = load().mx_quantize_dual_batch(ctypes.cast(arr, ctypes.c_void_p), len(jobs), _stream(stream))
+    _check("mx_quantize_dual_batch", st)
 
 
 _OUT = {torch.bfloat16: MX_BF16, torch.float32: MX_F32}

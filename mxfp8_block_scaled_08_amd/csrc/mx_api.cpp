@@ -151,53 +151,106 @@ mx_status mx_quantize_colwise(const void *x, int64_t rows, int64_t cols, int64_t
                       fn);
 }
 
+// Checks of one dual-quantization job; `who` names it in messages.
+static mx_status check_dual_job(const char *who, const mx_dual_job &j)
+{
+    const int64_t rows = j.rows, cols = j.cols;
+    if (rows < 0 || cols < 0)
+        return fail(MX_ERR_INVALID_ARG, "%s: negative size rows=%lld cols=%lld", who,
+                    (long long)rows, (long long)cols);
+    if (rows % 32 != 0 || cols % 32 != 0)
+        return fail(MX_ERR_SHAPE, "%s: rows=%lld and cols=%lld must be multiples of the 32-element block",
+                    who, (long long)rows, (long long)cols);
+    if (j.ld_x < cols || j.ld_q < cols || j.ld_qt < rows)
+        return fail(MX_ERR_INVALID_ARG,
+                    "%s: leading dimension too small (ld_x=%lld ld_q=%lld ld_qt=%lld)", who,
+                    (long long)j.ld_x, (long long)j.ld_q, (long long)j.ld_qt);
+    const int64_t kt_row = (cols / 32 + 7) / 8, kt_col = (rows / 32 + 7) / 8;
+    if (j.s_tiles < kt_row || j.st_tiles < kt_col)
+        return fail(MX_ERR_INVALID_ARG,
+                    "%s: tiles per rearranged row too small (s_tiles=%lld < %lld or st_tiles=%lld < %lld)",
+                    who, (long long)j.s_tiles, (long long)kt_row, (long long)j.st_tiles, (long long)kt_col);
+    if (rows == 0 || cols == 0)
+        return MX_OK;
+    if (!j.x || !j.q || !j.s_swz || !j.qt || !j.st_swz)
+        return fail(MX_ERR_INVALID_ARG, "%s: null pointer", who);
+    if (!aligned(j.x, 16) || !aligned(j.q, 16) || !aligned(j.qt, 16) || j.ld_x % 8 != 0 ||
+        j.ld_q % 16 != 0 || j.ld_qt % 16 != 0)
+        return fail(MX_ERR_ALIGN,
+                    "%s: x, q and qt need 16-byte aligned rows (ld_x %% 8, ld_q %% 16, ld_qt %% 16)", who);
+    if (!aligned(j.s_swz, 4) || !aligned(j.st_swz, 4))
+        return fail(MX_ERR_ALIGN, "%s: s_swz and st_swz must be 4-byte aligned", who);
+    // byte extents: the rearranged outputs span their last tile row's tiles
+    const int64_t ex = extent(rows, cols, j.ld_x, 2), eq = extent(rows, cols, j.ld_q, 1),
+                  eqt = extent(cols, rows, j.ld_qt, 1);
+    const int64_t es = ((rows / 32 - 1) * j.s_tiles + kt_row) * 256,
+                  est = ((cols / 32 - 1) * j.st_tiles + kt_col) * 256;
+    const void *outs[4] = {j.q, j.s_swz, j.qt, j.st_swz};
+    const int64_t lens[4] = {eq, es, eqt, est};
+    for (int i = 0; i < 4; i++) {
+        if (overlap(j.x, ex, outs[i], lens[i]))
+            return fail(MX_ERR_OVERLAP, "%s: input and an output overlap", who);
+        for (int k = i + 1; k < 4; k++)
+            if (overlap(outs[i], lens[i], outs[k], lens[k]))
+                return fail(MX_ERR_OVERLAP, "%s: two outputs overlap", who);
+    }
+    return MX_OK;
+}
+
+static mx::DualJob to_job(const mx_dual_job &j)
+{
+    return mx::DualJob{j.x, j.rows, j.cols, j.ld_x, j.q, j.ld_q, j.s_swz, j.s_tiles,
+                       j.qt, j.ld_qt, j.st_swz, j.st_tiles};
+}
+
 mx_status mx_quantize_dual(const void *x, int64_t rows, int64_t cols, int64_t ld_x, void *q,
                            int64_t ld_q, void *s_swz, int64_t s_tiles, void *qt, int64_t ld_qt,
                            void *st_swz, int64_t st_tiles, void *stream)
 {
     const char *fn = "mx_quantize_dual";
-    if (rows < 0 || cols < 0)
-        return fail(MX_ERR_INVALID_ARG, "%s: negative size rows=%lld cols=%lld", fn,
-                    (long long)rows, (long long)cols);
-    if (rows % 32 != 0 || cols % 32 != 0)
-        return fail(MX_ERR_SHAPE, "%s: rows=%lld and cols=%lld must be multiples of the 32-element block",
-                    fn, (long long)rows, (long long)cols);
-    if (ld_x < cols || ld_q < cols || ld_qt < rows)
-        return fail(MX_ERR_INVALID_ARG,
-                    "%s: leading dimension too small (ld_x=%lld ld_q=%lld ld_qt=%lld)", fn,
-                    (long long)ld_x, (long long)ld_q, (long long)ld_qt);
-    const int64_t kt_row = (cols / 32 + 7) / 8, kt_col = (rows / 32 + 7) / 8;
-    if (s_tiles < kt_row || st_tiles < kt_col)
-        return fail(MX_ERR_INVALID_ARG,
-                    "%s: tiles per rearranged row too small (s_tiles=%lld < %lld or st_tiles=%lld < %lld)",
-                    fn, (long long)s_tiles, (long long)kt_row, (long long)st_tiles, (long long)kt_col);
+    const mx_dual_job j{x, rows, cols, ld_x, q, ld_q, s_swz, s_tiles, qt, ld_qt, st_swz, st_tiles};
+    const mx_status st = check_dual_job(fn, j);
+    if (st != MX_OK)
+        return st;
     if (rows == 0 || cols == 0)
         return ok();
-    if (!x || !q || !s_swz || !qt || !st_swz)
-        return fail(MX_ERR_INVALID_ARG, "%s: null pointer", fn);
-    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(qt, 16) || ld_x % 8 != 0 || ld_q % 16 != 0 ||
-        ld_qt % 16 != 0)
-        return fail(MX_ERR_ALIGN,
-                    "%s: x, q and qt need 16-byte aligned rows (ld_x %% 8, ld_q %% 16, ld_qt %% 16)", fn);
-    if (!aligned(s_swz, 4) || !aligned(st_swz, 4))
-        return fail(MX_ERR_ALIGN, "%s: s_swz and st_swz must be 4-byte aligned", fn);
-    // byte extents: the rearranged outputs span their last tile row's tiles
-    const int64_t ex = extent(rows, cols, ld_x, 2), eq = extent(rows, cols, ld_q, 1),
-                  eqt = extent(cols, rows, ld_qt, 1);
-    const int64_t es = ((rows / 32 - 1) * s_tiles + kt_row) * 256,
-                  est = ((cols / 32 - 1) * st_tiles + kt_col) * 256;
-    const void *outs[4] = {q, s_swz, qt, st_swz};
-    const int64_t lens[4] = {eq, es, eqt, est};
-    for (int i = 0; i < 4; i++) {
-        if (overlap(x, ex, outs[i], lens[i]))
-            return fail(MX_ERR_OVERLAP, "%s: input and an output overlap", fn);
-        for (int j = i + 1; j < 4; j++)
-            if (overlap(outs[i], lens[i], outs[j], lens[j]))
-                return fail(MX_ERR_OVERLAP, "%s: two outputs overlap", fn);
+    const mx::DualJob dj = to_job(j);
+    return hip_status(mx::launch_quantize_dual(&dj, 1, (hipStream_t)stream), fn);
+}
+
+mx_status mx_quantize_dual_batch(const mx_dual_job *jobs, int n_jobs, void *stream)
+{
+    const char *fn = "mx_quantize_dual_batch";
+    if (n_jobs < 0 || n_jobs > MX_DUAL_MAX_JOBS)
+        return fail(MX_ERR_INVALID_ARG, "%s: n_jobs=%d outside 0..%d", fn, n_jobs, MX_DUAL_MAX_JOBS);
+    if (n_jobs == 0)
+        return ok();
+    if (!jobs)
+        return fail(MX_ERR_INVALID_ARG, "%s: null job array", fn);
+    mx::DualJob dj[MX_DUAL_MAX_JOBS];
+    int n = 0;
+    for (int i = 0; i < n_jobs; i++) {
+        char who[96];
+        snprintf(who, sizeof who, "%s: job %d", fn, i);
+        const mx_status st = check_dual_job(who, jobs[i]);
+        if (st != MX_OK)
+            return st;
+        // a job's input must not be written by another job
+        for (int k = 0; k < n_jobs; k++) {
+            if (k == i || jobs[k].rows <= 0 || jobs[k].cols <= 0 || jobs[i].rows <= 0 || jobs[i].cols <= 0)
+                continue;
+            const mx_dual_job &a = jobs[i], &b = jobs[k];
+            const int64_t ex = extent(a.rows, a.cols, a.ld_x, 2);
+            if (overlap(a.x, ex, b.q, extent(b.rows, b.cols, b.ld_q, 1)) ||
+                overlap(a.x, ex, b.qt, extent(b.cols, b.rows, b.ld_qt, 1)))
+                return fail(MX_ERR_OVERLAP, "%s: job %d's input overlaps job %d's codes", fn, i, k);
+        }
+        if (jobs[i].rows > 0 && jobs[i].cols > 0)
+            dj[n++] = to_job(jobs[i]);
     }
-    return hip_status(mx::launch_quantize_dual(x, rows, cols, ld_x, q, ld_q, s_swz, s_tiles, qt,
-                                               ld_qt, st_swz, st_tiles, (hipStream_t)stream),
-                      fn);
+    if (n == 0)
+        return ok();
+    return hip_status(mx::launch_quantize_dual(dj, n, (hipStream_t)stream), fn);
 }
 
 mx_status mx_scale_swizzle(const void *s, int64_t rows, int64_t kblocks, int64_t ld_s,

@@ -16,11 +16,25 @@ hipError_t launch_quantize_colwise(const void *x, int64_t rows, int64_t cols, in
                                    void *qt, int64_t ld_qt, void *st, int64_t ld_st,
                                    hipStream_t stream);
 
-// s_swz / st_swz: tile (0, 0) of this call's rearranged scales; tile (rt, kt)
-// at + (rt * s_tiles + kt) * 256 (st_tiles likewise).
-hipError_t launch_quantize_dual(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
-                                void *q, int64_t ld_q, void *s_swz, int64_t s_tiles, void *qt,
-                                int64_t ld_qt, void *st_swz, int64_t st_tiles, hipStream_t stream);
+// One tensor of a dual (row-wise + column-wise) quantization.  s_swz /
+// st_swz: tile (0, 0) of its rearranged scales; tile (rt, kt) at
+// + (rt * s_tiles + kt) * 256 (st_tiles likewise).
+struct DualJob {
+    const void *x;
+    int64_t rows, cols, ld_x;
+    void *q;
+    int64_t ld_q;
+    void *s_swz;
+    int64_t s_tiles;
+    void *qt;
+    int64_t ld_qt;
+    void *st_swz;
+    int64_t st_tiles;
+};
+constexpr int QD_MAX_JOBS = 16;
+
+// n in 1..QD_MAX_JOBS jobs, one launch; empty jobs are allowed.
+hipError_t launch_quantize_dual(const DualJob *jobs, int n, hipStream_t stream);
 
 hipError_t launch_scale_swizzle(const void *s, int64_t rows, int64_t kblocks, int64_t ld_s,
                                 void *s_swz, hipStream_t stream);

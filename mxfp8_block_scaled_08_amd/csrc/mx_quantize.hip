@@ -205,21 +205,39 @@ __global__ __launch_bounds__(QC_THREADS) void quantize_colwise_kernel(
 constexpr int QD_THREADS = 512;
 constexpr int QD_TILE = 256;
 
-__global__ __launch_bounds__(QD_THREADS) void quantize_dual_kernel(
-    const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
-    uint8_t *__restrict__ q, int64_t ld_q, uint8_t *__restrict__ s_swz, int64_t s_tiles,
-    uint8_t *__restrict__ qt, int64_t ld_qt, uint8_t *__restrict__ st_swz, int64_t st_tiles,
-    int64_t tiles_r, int64_t tiles_c)
+// Several tensors in one launch (a layer's weights): job j takes blocks
+// first[j] .. first[j+1] - 1, each job's count a multiple of 8 when it uses
+// the per-XCD order, so a block's XCD is still its number mod 8.
+struct DualBatch {
+    DualJob job[QD_MAX_JOBS];
+    int64_t first[QD_MAX_JOBS + 1];
+    int n;
+};
+
+__global__ __launch_bounds__(QD_THREADS) void quantize_dual_kernel(DualBatch B)
 {
     __shared__ uint32_t lds_s[8 * 64];   // row-wise scales: 8 rearranged tiles
     __shared__ uint32_t lds_st[8 * 64];  // column-wise scales: 8 rearranged tiles
+    int jb = 0;
+    while (jb + 1 < B.n && (int64_t)blockIdx.x >= B.first[jb + 1])
+        jb++;
+    const DualJob &J = B.job[jb];
+    const uint16_t *__restrict__ x = (const uint16_t *)J.x;
+    const int64_t rows = J.rows, cols = J.cols, ld_x = J.ld_x;
+    uint8_t *__restrict__ q = (uint8_t *)J.q;
+    uint8_t *__restrict__ s_swz = (uint8_t *)J.s_swz;
+    uint8_t *__restrict__ qt = (uint8_t *)J.qt;
+    uint8_t *__restrict__ st_swz = (uint8_t *)J.st_swz;
+    const int64_t ld_q = J.ld_q, s_tiles = J.s_tiles, ld_qt = J.ld_qt, st_tiles = J.st_tiles;
+    const int64_t tiles_r = (rows + QD_TILE - 1) / QD_TILE, tiles_c = (cols + QD_TILE - 1) / QD_TILE;
+    const int64_t b = (int64_t)blockIdx.x - B.first[jb], nb = B.first[jb + 1] - B.first[jb];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 2, wc = wave & 3;
     const int cg = lane & 7, half = (lane >> 3) & 1, rb = lane >> 4;
     int64_t tr, tc;
     if (tiles_c >= QC_WIDE) {
-        const int64_t t = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+        const int64_t t = (b & 7) * (nb >> 3) + (b >> 3);
         if (t >= tiles_r * tiles_c)
             return;
         const int64_t per_group = QC_GROUP_R * tiles_c;
@@ -229,8 +247,8 @@ __global__ __launch_bounds__(QD_THREADS) void quantize_dual_kernel(
         tr = first + in % gr;
         tc = in / gr;
     } else {
-        tr = blockIdx.x / tiles_c;
-        tc = blockIdx.x - tr * tiles_c;
+        tr = b / tiles_c;
+        tc = b - tr * tiles_c;
     }
     const int64_t R0 = tr * QD_TILE, C0 = tc * QD_TILE;
     const int64_t c0 = C0 + wc * 64 + cg * 8;
@@ -418,18 +436,25 @@ hipError_t launch_quantize_colwise(const void *x, int64_t rows, int64_t cols, in
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_dual(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
-                                void *q, int64_t ld_q, void *s_swz, int64_t s_tiles, void *qt,
-                                int64_t ld_qt, void *st_swz, int64_t st_tiles, hipStream_t stream)
+hipError_t launch_quantize_dual(const DualJob *jobs, int n, hipStream_t stream)
 {
-    const int64_t tiles_r = (rows + QD_TILE - 1) / QD_TILE;
-    const int64_t tiles_c = (cols + QD_TILE - 1) / QD_TILE;
-    int64_t blocks = tiles_r * tiles_c;
-    if (tiles_c >= QC_WIDE)
-        blocks = (blocks + 7) / 8 * 8;
-    hipLaunchKernelGGL(quantize_dual_kernel, dim3((unsigned)blocks), dim3(QD_THREADS), 0, stream,
-                       (const uint16_t *)x, rows, cols, ld_x, (uint8_t *)q, ld_q, (uint8_t *)s_swz,
-                       s_tiles, (uint8_t *)qt, ld_qt, (uint8_t *)st_swz, st_tiles, tiles_r, tiles_c);
+    DualBatch B{};
+    B.n = n;
+    int64_t blocks = 0;
+    for (int j = 0; j < n; j++) {
+        B.job[j] = jobs[j];
+        B.first[j] = blocks;
+        const int64_t tiles_r = (jobs[j].rows + QD_TILE - 1) / QD_TILE;
+        const int64_t tiles_c = (jobs[j].cols + QD_TILE - 1) / QD_TILE;
+        int64_t nb = tiles_r * tiles_c;
+        if (tiles_c >= QC_WIDE)
+            nb = (nb + 7) / 8 * 8;
+        blocks += nb;
+    }
+    B.first[n] = blocks;
+    if (blocks == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(quantize_dual_kernel, dim3((unsigned)blocks), dim3(QD_THREADS), 0, stream, B);
     return hipGetLastError();
 }
 

@@ -127,6 +127,34 @@ def test_quantize_dual_validation():
     assert call(a2=0, a3=0, a5=0) == mx.MX_OK
 
 
+def test_quantize_dual_batch_validation():
+    L = mx.load()
+    f = L.mx_quantize_dual_batch
+    J = mx._DualJob
+    good = (FAKE, 64, 64, 64, FAKE2, 64, FAKE3, 1, 0x100000000, 64, 0x140000000, 1)
+    arr = (J * 3)(J(*good), J(*good), J(*good))
+    assert f(ctypes.cast(arr, ctypes.c_void_p), 17, STREAM) == mx.MX_ERR_INVALID_ARG
+    assert f(ctypes.cast(arr, ctypes.c_void_p), -1, STREAM) == mx.MX_ERR_INVALID_ARG
+    assert f(None, 2, STREAM) == mx.MX_ERR_INVALID_ARG
+    assert f(None, 0, STREAM) == mx.MX_OK
+    bad = list(good)
+    bad[1] = 48                                      # rows % 32 in job 1
+    arr[1] = J(*bad)
+    assert f(ctypes.cast(arr, ctypes.c_void_p), 3, STREAM) == mx.MX_ERR_SHAPE
+    assert "job 1" in _err(L)
+    arr[1] = J(*good)
+    other = list(good)
+    other[0] = 0x180000000                           # job 2 reads ...
+    other[4] = FAKE + 64                             # ... and writes its codes into job 0's input
+    arr[2] = J(*other)
+    assert f(ctypes.cast(arr, ctypes.c_void_p), 3, STREAM) == mx.MX_ERR_OVERLAP
+    assert "job 0" in _err(L) or "job 2" in _err(L)
+    empty = list(good)
+    empty[1] = 0
+    arr[0] = arr[1] = arr[2] = J(*empty)
+    assert f(ctypes.cast(arr, ctypes.c_void_p), 3, STREAM) == mx.MX_OK
+
+
 def test_swizzle_validation():
     L = mx.load()
     f = L.mx_scale_swizzle

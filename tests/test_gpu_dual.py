@@ -91,3 +91,51 @@ def test_dual_into_concatenated_operands(gpu_lib):
     for got, ref, name in zip((q, s_swz, qt, st_swz), _ref(np.concatenate([x1, x2], 0)),
                               ("q", "s_swz", "qt", "st_swz")):
         _eq(got, ref, f"stacked {name}")
+
+
+def test_dual_batch_matches_oracle(gpu_lib):
+    """A layer's worth of jobs in one launch: different shapes (one of them wide
+    enough for the per-XCD tile order, one a quarter of the chip), two of them
+    writing the halves of stacked and side-by-side operands, and an empty job."""
+    mx = gpu_lib
+    dev = "cuda"
+    shapes = {"a": (256, 512), "b": (1024, 256), "c": (96, 8224), "g": (512, 288), "u": (256, 288)}
+    X = {k: mxsynth.bits(mxsynth.normal_bf16(v, 1.0 + i, 40 + i)) for i, (k, v) in enumerate(shapes.items())}
+    outs = {}
+    jobs = []
+    for k in ("a", "b", "c"):
+        r, c = shapes[k]
+        o = dict(x=bf16_dev(mxsynth.from_bits(X[k])),
+                 q=torch.empty((r, c), dtype=torch.uint8, device=dev),
+                 s_swz=torch.empty((mx.mx_scale_swizzled_bytes(r, c // 32),), dtype=torch.uint8, device=dev),
+                 qt=torch.empty((c, r), dtype=torch.uint8, device=dev),
+                 st_swz=torch.empty((mx.mx_scale_swizzled_bytes(c, r // 32),), dtype=torch.uint8, device=dev))
+        outs[k] = o
+        jobs.append(o)
+    # g and u: stacked rows (forward operand), side by side along K (backward operand)
+    R, C = 512 + 256, 288
+    kts, ktst = (C // 32 + 7) // 8, (R // 32 + 7) // 8
+    fused = dict(q=torch.empty((R, C), dtype=torch.uint8, device=dev),
+                 s_swz=torch.full((mx.mx_scale_swizzled_bytes(R, C // 32),), 0xEE, dtype=torch.uint8, device=dev),
+                 qt=torch.empty((C, R), dtype=torch.uint8, device=dev),
+                 st_swz=torch.full((mx.mx_scale_swizzled_bytes(C, R // 32),), 0xEE, dtype=torch.uint8, device=dev))
+    for k, r0, r1 in (("g", 0, 512), ("u", 512, 768)):
+        jobs.append(dict(x=bf16_dev(mxsynth.from_bits(X[k])), q=fused["q"][r0:r1],
+                         s_swz=fused["s_swz"][(r0 // 32) * kts * 256:], s_tiles=kts,
+                         qt=fused["qt"][:, r0:r1], st_swz=fused["st_swz"][(r0 // 256) * 256:],
+                         st_tiles=ktst))
+    e = torch.empty((0, 64), dtype=torch.bfloat16, device=dev)
+    jobs.append(dict(x=e, q=torch.empty((0, 64), dtype=torch.uint8, device=dev),
+                     s_swz=torch.empty((4,), dtype=torch.uint8, device=dev),
+                     qt=torch.empty((64, 0), dtype=torch.uint8, device=dev),
+                     st_swz=torch.empty((4,), dtype=torch.uint8, device=dev)))
+    mx.mx_quantize_dual_batch(jobs)
+    for k in ("a", "b", "c"):
+        o = outs[k]
+        for got, ref, name in zip((o["q"], o["s_swz"], o["qt"], o["st_swz"]), _ref(X[k]),
+                                  ("q", "s_swz", "qt", "st_swz")):
+            _eq(got, ref, f"batch {k} {name}")
+    for got, ref, name in zip((fused["q"], fused["s_swz"], fused["qt"], fused["st_swz"]),
+                              _ref(np.concatenate([X["g"], X["u"]], 0)),
+                              ("q", "s_swz", "qt", "st_swz")):
+        _eq(got, ref, f"batch stacked {name}")
