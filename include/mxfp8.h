@@ -18,6 +18,8 @@
  *                         tensors in one launch)
  *   mx_gemm               C = deq(A) . deq(B)^T, FP32 accumulation
  *   mx_grouped_gemm       the same per MoE expert over row groups
+ *   mx_moe_dispatch       rows sorted by expert, gathered and quantized
+ *   mx_moe_combine        expert outputs weighted and summed per token
  *
  * Number format (OCP Microscaling Formats (MX) v1.0, MXFP8 E4M3):
  *   element  E4M3 ("E4M3FN"): bias 7, largest finite 448 (0x7E), NaN 0x7F/0xFF,
@@ -208,6 +210,62 @@ typedef struct mx_dual_job {
     int64_t st_tiles;
 } mx_dual_job;
 mx_status mx_quantize_dual_batch(const mx_dual_job *jobs, int n_jobs, void *stream);
+
+/*
+ * MoE dispatch: the routed rows sorted by expert, gathered and quantized
+ * row-wise as the grouped GEMM's A operand (paper Table 2: Qwen3-30B-A3B,
+ * 128 experts, 8 routed per token; its expert GEMMs run per expert on rows
+ * sorted by expert).
+ *   x          BF16 [tokens][ld_x], the layer input
+ *   topk_ids   DEVICE int32 [tokens][topk]: assignment a = t*topk + j sends
+ *              token t to expert topk_ids[t][j]; ids outside
+ *              [0, num_experts) are not routed
+ *   offsets    DEVICE int64 [num_experts + 1] out: expert g's rows are
+ *              [offsets[g], offsets[g+1]); offsets[num_experts] = routed rows
+ *   src_token  DEVICE int32 [tokens*topk] out: token of permuted row i
+ *              (rows below the routed count)
+ *   slot       DEVICE int32 [tokens*topk] out: permuted row of assignment a,
+ *              -1 if not routed
+ *   q          E4M3 [tokens*topk][ld_q] out: row i = mx_quantize_rowwise of
+ *              x[src_token[i]] (routed rows only)
+ *   s_swz      its scales in the rearranged layout of mx_scale_swizzle for a
+ *              [tokens*topk][hidden/32] scale tensor (routed rows only)
+ * Order: assignment a goes to row offsets[e] + the number of earlier
+ * assignments (smaller a) to the same expert e, i.e. a stable sort by expert:
+ * the same routing always gives the same bytes.  offsets, src_token, slot,
+ * q and s_swz feed mx_grouped_gemm (A = q, a_s_swz = s_swz, group_offsets =
+ * offsets, M_total = tokens*topk: rows past the routed count belong to no
+ * expert).
+ * Requirements: tokens >= 1, topk >= 1, num_experts in 1..1024 (else
+ * MX_ERR_INVALID_ARG / MX_ERR_UNSUPPORTED), hidden % 32 == 0 (else
+ * MX_ERR_SHAPE) and hidden % 256 == 0 (else MX_ERR_UNSUPPORTED),
+ * tokens*topk < 2^30; x and q 16-byte aligned rows (ld_x % 8, ld_q % 16),
+ * index arrays naturally aligned (else MX_ERR_ALIGN); outputs overlap
+ * nothing (else MX_ERR_OVERLAP).  Uses a stream-ordered workspace of
+ * 4 * num_experts bytes per 256 assignments from the library's pool.
+ */
+mx_status mx_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
+                          const int32_t *topk_ids, int64_t topk, int64_t num_experts,
+                          int64_t *offsets, int32_t *src_token, int32_t *slot, void *q, int64_t ld_q,
+                          void *s_swz, void *stream);
+
+/*
+ * MoE combine: each token's expert outputs weighted and summed back in token
+ * order, undoing mx_moe_dispatch's permutation.
+ *   y        BF16 [tokens*topk][ld_y]: per permuted row, its expert's output
+ *   slot     DEVICE int32 [tokens*topk] from mx_moe_dispatch
+ *   weights  DEVICE float [tokens][topk]: the routing weights
+ *   out      BF16 [tokens][ld_out]: out[t] = sum over j (in order 0..topk-1,
+ *            skipping slot -1) of weights[t][j] * y[slot[t*topk + j]],
+ *            FP32 fused multiply-adds, rounded once to BF16 (nearest even)
+ * Requirements: hidden % 8 == 0 (else MX_ERR_SHAPE); y and out 16-byte
+ * aligned rows with ld % 8 == 0 (else MX_ERR_ALIGN); out overlaps neither y
+ * nor the routing (else MX_ERR_OVERLAP).  Slots outside [0, tokens*topk)
+ * contribute nothing.
+ */
+mx_status mx_moe_combine(const void *y, int64_t tokens, int64_t hidden, int64_t ld_y,
+                         const int32_t *slot, const float *weights, int64_t topk, void *out,
+                         int64_t ld_out, void *stream);
 
 /*
  * Dense block-scaled GEMM ("MXFP8 GEMMs" of the learner, paper Figure 1 and

@@ -80,6 +80,11 @@ def load() -> ctypes.CDLL:
     L.mx_quantize_dual.restype = ctypes.c_int
     L.mx_quantize_dual_batch.argtypes = [ctypes.c_void_p, ctypes.c_int, _vp]
     L.mx_quantize_dual_batch.restype = ctypes.c_int
+    L.mx_moe_dispatch.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64,
+                                  _vp, _vp]
+    L.mx_moe_dispatch.restype = ctypes.c_int
+    L.mx_moe_combine.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp]
+    L.mx_moe_combine.restype = ctypes.c_int
     L.mx_gemm.restype = ctypes.c_int
     L.mx_gemm.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
                           ctypes.c_int, _vp]
@@ -260,6 +265,47 @@ def mx_quantize_dual_batch(jobs, stream=None) -> None:
                           j.get("st_tiles", (rows // 32 + 7) // 8))
     st = load().mx_quantize_dual_batch(ctypes.cast(arr, ctypes.c_void_p), len(jobs), _stream(stream))
     _check("mx_quantize_dual_batch", st)
+
+
+def mx_moe_dispatch(x: torch.Tensor, topk_ids: torch.Tensor, num_experts: int, stream=None):
+    """Sort the routed rows by expert, gather and quantize them row-wise.
+
+    x BF16 [tokens][hidden], topk_ids int32 [tokens][topk] -> (offsets int64
+    [num_experts+1], src_token int32 [tokens*topk], slot int32 [tokens*topk],
+    q uint8 [tokens*topk][hidden], s_swz uint8: rearranged scales)."""
+    tokens, hidden = x.shape
+    if topk_ids.dim() != 2 or topk_ids.shape[0] != tokens or not topk_ids.is_contiguous():
+        raise ValueError("topk_ids must be a contiguous [tokens][topk] tensor")
+    topk = topk_ids.shape[1]
+    n = tokens * topk
+    dev = x.device
+    offsets = torch.empty(num_experts + 1, dtype=torch.int64, device=dev)
+    src = torch.empty(n, dtype=torch.int32, device=dev)
+    slot = torch.empty(n, dtype=torch.int32, device=dev)
+    q = torch.empty((n, hidden), dtype=torch.uint8, device=dev)
+    s_swz = torch.empty(mx_scale_swizzled_bytes(n, hidden // 32), dtype=torch.uint8, device=dev)
+    st = load().mx_moe_dispatch(_dev(x, "x", torch.bfloat16), tokens, hidden, _ld(x, "x"),
+                                _dev(topk_ids, "topk_ids", torch.int32), topk, num_experts,
+                                _dev(offsets, "offsets"), _dev(src, "src"), _dev(slot, "slot"),
+                                _dev(q, "q"), _ld(q, "q"), _dev(s_swz, "s_swz"), _stream(stream))
+    _check("mx_moe_dispatch", st)
+    return offsets, src, slot, q, s_swz
+
+
+def mx_moe_combine(y: torch.Tensor, slot: torch.Tensor, weights: torch.Tensor,
+                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out[t] = sum_j weights[t][j] * y[slot[t*topk + j]] (BF16 [tokens][hidden])."""
+    tokens, topk = weights.shape
+    hidden = y.shape[1]
+    if out is None:
+        out = torch.empty((tokens, hidden), dtype=torch.bfloat16, device=y.device)
+    if not (slot.is_contiguous() and weights.is_contiguous()):
+        raise ValueError("slot and weights must be contiguous")
+    st = load().mx_moe_combine(_dev(y, "y", torch.bfloat16), tokens, hidden, _ld(y, "y"),
+                               _dev(slot, "slot", torch.int32), _dev(weights, "weights", torch.float32),
+                               topk, _dev(out, "out", torch.bfloat16), _ld(out, "out"), _stream(stream))
+    _check("mx_moe_combine", st)
+    return out
 
 
 _OUT = {torch.bfloat16: MX_BF16, torch.float32: MX_F32}

@@ -253,6 +253,82 @@ mx_status mx_quantize_dual_batch(const mx_dual_job *jobs, int n_jobs, void *stre
     return hip_status(mx::launch_quantize_dual(dj, n, (hipStream_t)stream), fn);
 }
 
+mx_status mx_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
+                          const int32_t *topk_ids, int64_t topk, int64_t num_experts,
+                          int64_t *offsets, int32_t *src_token, int32_t *slot, void *q, int64_t ld_q,
+                          void *s_swz, void *stream)
+{
+    const char *fn = "mx_moe_dispatch";
+    if (tokens < 0 || hidden < 0 || topk < 1 || num_experts < 1)
+        return fail(MX_ERR_INVALID_ARG, "%s: need tokens, hidden >= 0, topk, num_experts >= 1", fn);
+    if (hidden % 32 != 0)
+        return fail(MX_ERR_SHAPE, "%s: hidden=%lld is not a multiple of the 32-element block", fn,
+                    (long long)hidden);
+    if (hidden % 256 != 0)
+        return fail(MX_ERR_UNSUPPORTED, "%s: hidden=%lld: this build needs hidden %% 256 == 0", fn,
+                    (long long)hidden);
+    if (num_experts > mx::MOE_MAX_EXPERTS)
+        return fail(MX_ERR_UNSUPPORTED, "%s: num_experts=%lld > %d", fn, (long long)num_experts,
+                    mx::MOE_MAX_EXPERTS);
+    if (tokens * topk >= ((int64_t)1 << 31) / 2)
+        return fail(MX_ERR_UNSUPPORTED, "%s: tokens * topk must stay below 2^30", fn);
+    if (ld_x < hidden || ld_q < hidden)
+        return fail(MX_ERR_INVALID_ARG, "%s: leading dimension too small (ld_x=%lld ld_q=%lld)", fn,
+                    (long long)ld_x, (long long)ld_q);
+    if (!offsets)
+        return fail(MX_ERR_INVALID_ARG, "%s: null offsets", fn);
+    if (tokens == 0 || hidden == 0) {
+        // nothing routed: offsets all zero would need a device write; refuse
+        // instead of leaving them unwritten
+        return fail(MX_ERR_INVALID_ARG, "%s: tokens and hidden must be positive", fn);
+    }
+    if (!x || !topk_ids || !src_token || !slot || !q || !s_swz)
+        return fail(MX_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!aligned(x, 16) || !aligned(q, 16) || ld_x % 8 != 0 || ld_q % 16 != 0)
+        return fail(MX_ERR_ALIGN, "%s: x and q need 16-byte aligned rows (ld_x %% 8, ld_q %% 16)", fn);
+    if (!aligned(topk_ids, 4) || !aligned(src_token, 4) || !aligned(slot, 4) || !aligned(offsets, 8))
+        return fail(MX_ERR_ALIGN, "%s: index arrays need their natural alignment", fn);
+    const int64_t n = tokens * topk;
+    const void *bufs[7] = {x, topk_ids, offsets, src_token, slot, q, s_swz};
+    const int64_t lens[7] = {extent(tokens, hidden, ld_x, 2), n * 4, (num_experts + 1) * 8, n * 4, n * 4,
+                             extent(n, hidden, ld_q, 1), swz_bytes(n, hidden / 32)};
+    for (int i = 0; i < 7; i++)
+        for (int k = i + 1; k < 7; k++)
+            if ((i >= 2 || k >= 2) && overlap(bufs[i], lens[i], bufs[k], lens[k]))
+                return fail(MX_ERR_OVERLAP, "%s: buffers %d and %d overlap", fn, i, k);
+    return hip_status(mx::launch_moe_dispatch(x, tokens, hidden, ld_x, topk_ids, topk, num_experts,
+                                              offsets, src_token, slot, q, ld_q, s_swz,
+                                              (hipStream_t)stream),
+                      fn);
+}
+
+mx_status mx_moe_combine(const void *y, int64_t tokens, int64_t hidden, int64_t ld_y,
+                         const int32_t *slot, const float *weights, int64_t topk, void *out,
+                         int64_t ld_out, void *stream)
+{
+    const char *fn = "mx_moe_combine";
+    if (tokens < 0 || hidden < 0 || topk < 1)
+        return fail(MX_ERR_INVALID_ARG, "%s: need tokens, hidden >= 0, topk >= 1", fn);
+    if (hidden % 8 != 0)
+        return fail(MX_ERR_SHAPE, "%s: hidden=%lld is not a multiple of 8", fn, (long long)hidden);
+    if (ld_y < hidden || ld_out < hidden)
+        return fail(MX_ERR_INVALID_ARG, "%s: leading dimension too small", fn);
+    if (tokens == 0 || hidden == 0)
+        return ok();
+    if (!y || !slot || !weights || !out)
+        return fail(MX_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!aligned(y, 16) || !aligned(out, 16) || ld_y % 8 != 0 || ld_out % 8 != 0 || !aligned(slot, 4) ||
+        !aligned(weights, 4))
+        return fail(MX_ERR_ALIGN, "%s: y and out need 16-byte aligned rows (ld %% 8)", fn);
+    const int64_t eo = extent(tokens, hidden, ld_out, 2);
+    if (overlap(out, eo, slot, tokens * topk * 4) || overlap(out, eo, weights, tokens * topk * 4) ||
+        overlap(out, eo, y, extent(tokens * topk, hidden, ld_y, 2)))
+        return fail(MX_ERR_OVERLAP, "%s: out overlaps y or the routing", fn);
+    return hip_status(mx::launch_moe_combine(y, tokens, hidden, ld_y, slot, weights, topk, out, ld_out,
+                                             (hipStream_t)stream),
+                      fn);
+}
+
 mx_status mx_scale_swizzle(const void *s, int64_t rows, int64_t kblocks, int64_t ld_s,
                            void *s_swz, void *stream)
 {

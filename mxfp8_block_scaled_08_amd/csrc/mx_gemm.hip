@@ -892,11 +892,12 @@ static int cu_count()
     return cache[dev];
 }
 
-// Stream-ordered workspace of the split tail: a memory pool per device that
-// keeps freed blocks for reuse (release threshold at its maximum), so after
-// the first call an allocation costs no driver round trip.  The pool is the
-// library's own; the device's default pool is left as the caller set it.
-static hipMemPool_t split_pool()
+// Stream-ordered workspace (the split tail, the MoE permutation's counts): a
+// memory pool per device that keeps freed blocks for reuse (release
+// threshold at its maximum), so after the first call an allocation costs no
+// driver round trip.  The pool is the library's own; the device's default
+// pool is left as the caller set it.
+hipMemPool_t workspace_pool()
 {
     static std::mutex mu;
     static hipMemPool_t pools[64];
@@ -1001,7 +1002,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t
     if (rem > 0 && groups >= 2 && c_dtype == 0 && p.vec16 && N % BN == 0) {
         const int64_t balance = std::max<int64_t>(2, (int64_t)std::sqrt(26.0 * 2 * groups / (double)rem));
         const int64_t S = std::min<int64_t>(std::min<int64_t>(cus / rem, groups), balance);
-        hipMemPool_t pool = S >= 2 ? split_pool() : nullptr;
+        hipMemPool_t pool = S >= 2 ? workspace_pool() : nullptr;
         const size_t part_bytes = (size_t)(rem * S) * (BM * BN * sizeof(float));
         if (pool != nullptr && hipMallocFromPoolAsync(&ws, part_bytes, pool, stream) == hipSuccess) {
             p.dp_tiles = tiles - rem;

@@ -49,4 +49,22 @@ hipError_t launch_grouped_gemm(int64_t G, int64_t M_total, int64_t N, int64_t K,
                                const void *a_s, const void *b_q, const void *b_s, void *c,
                                int64_t ld_c, int c_dtype, hipStream_t stream);
 
+// The library's stream-ordered workspace pool of the current device (null
+// if it cannot be created).
+hipMemPool_t workspace_pool();
+
+// MoE dispatch: stable order of the routed (token, expert) assignments by
+// expert, then the permuted rows gathered and quantized row-wise, scales in
+// the rearranged layout.  G <= MOE_MAX_EXPERTS, hidden % 256 == 0.
+constexpr int MOE_MAX_EXPERTS = 1024;
+hipError_t launch_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
+                               const int32_t *topk_ids, int64_t topk, int64_t experts,
+                               int64_t *offsets, int32_t *src_token, int32_t *slot, void *q,
+                               int64_t ld_q, void *s_swz, hipStream_t stream);
+
+// MoE combine: out[t] = sum_j weights[t][j] * y[slot[t][j]] (slots < 0 skipped).
+hipError_t launch_moe_combine(const void *y, int64_t tokens, int64_t hidden, int64_t ld_y,
+                              const int32_t *slot, const float *weights, int64_t topk, void *out,
+                              int64_t ld_out, hipStream_t stream);
+
 }  // namespace mx

@@ -1,0 +1,237 @@
+// MoE token dispatch and combine around the grouped GEMM (gfx950).
+//
+// The MoE layers of "End-to-End MXFP8 Reinforcement Learning on Blackwell"
+// (Table 2: Qwen3-30B-A3B, 128 experts, 8 routed per token) run the expert
+// GEMMs on rows sorted by expert.  Dispatch builds that order and the GEMM's
+// A operand in one pass over the activations; combine undoes it.
+//
+// Order.  Assignment a = t * topk + j (token t, its j-th expert) is placed at
+// row offsets[e] + (number of earlier assignments to the same expert e): a
+// stable sort by expert, so the result depends only on the routing.  Three
+// small kernels compute it without atomics on the result: per chunk of 256
+// assignments an LDS histogram of experts (LDS atomics only count, so the
+// counts are exact); per expert a scan over the chunks plus the experts'
+// exclusive scan (the offsets); per assignment its rank among the earlier
+// assignments of its chunk with the same expert, from the chunk's experts in
+// LDS.  Expert ids outside [0, experts) are not routed (slot -1).
+//
+// Gather + quantize.  Row i of the permuted operand is the quantized row of
+// token src_token[i]: the row-wise kernel's lane layout (8 BF16 per lane,
+// four lanes per 32-element block, DPP quad maximum, CDNA4's scaled
+// conversion) with the source row looked up per unit, and each block's scale
+// byte stored at its place in the GEMM's rearranged layout.
+#include "mx_device.h"
+#include "mx_launch.h"
+
+#include <algorithm>
+
+namespace mx {
+
+constexpr int MOE_CHUNK = 256;
+
+__global__ __launch_bounds__(MOE_CHUNK) void moe_count_kernel(const int32_t *__restrict__ ids, int64_t n,
+                                                               int experts, int32_t *__restrict__ counts)
+{
+    __shared__ int hist[MOE_MAX_EXPERTS];
+    for (int g = threadIdx.x; g < experts; g += MOE_CHUNK)
+        hist[g] = 0;
+    __syncthreads();
+    const int64_t a = (int64_t)blockIdx.x * MOE_CHUNK + threadIdx.x;
+    if (a < n) {
+        const int e = ids[a];
+        if (e >= 0 && e < experts)
+            atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+    for (int g = threadIdx.x; g < experts; g += MOE_CHUNK)
+        counts[(int64_t)blockIdx.x * experts + g] = hist[g];
+}
+
+// One workgroup: thread g scans expert g's column of chunk counts into chunk
+// bases, then the experts' totals are scanned into the offsets and added.
+__global__ __launch_bounds__(MOE_MAX_EXPERTS) void moe_scan_kernel(int32_t *__restrict__ counts, int64_t chunks,
+                                                                   int experts, int64_t *__restrict__ offsets)
+{
+    __shared__ int64_t total[MOE_MAX_EXPERTS];
+    const int g = threadIdx.x;
+    int64_t run = 0;
+    if (g < experts) {
+        for (int64_t c = 0; c < chunks; c++) {
+            const int32_t t = counts[c * experts + g];
+            counts[c * experts + g] = (int32_t)run;
+            run += t;
+        }
+        total[g] = run;
+    }
+    __syncthreads();
+    if (g == 0) {
+        int64_t acc = 0;
+        for (int e = 0; e < experts; e++) {
+            const int64_t t = total[e];
+            total[e] = acc;
+            offsets[e] = acc;
+            acc += t;
+        }
+        offsets[experts] = acc;
+    }
+    __syncthreads();
+    if (g < experts) {
+        const int32_t base = (int32_t)total[g];
+        for (int64_t c = 0; c < chunks; c++)
+            counts[c * experts + g] += base;
+    }
+}
+
+__global__ __launch_bounds__(MOE_CHUNK) void moe_place_kernel(const int32_t *__restrict__ ids, int64_t n,
+                                                               int topk, int experts,
+                                                               const int32_t *__restrict__ base,
+                                                               int32_t *__restrict__ src_token,
+                                                               int32_t *__restrict__ slot)
+{
+    __shared__ int ex[MOE_CHUNK];
+    const int i = threadIdx.x;
+    const int64_t a = (int64_t)blockIdx.x * MOE_CHUNK + i;
+    int e = -1;
+    if (a < n) {
+        e = ids[a];
+        if (e < 0 || e >= experts)
+            e = -1;
+    }
+    ex[i] = e;
+    __syncthreads();
+    if (a >= n)
+        return;
+    if (e < 0) {
+        slot[a] = -1;
+        return;
+    }
+    int rank = 0;
+    for (int j = 0; j < i; j++)
+        rank += ex[j] == e;
+    const int32_t p = base[(int64_t)blockIdx.x * experts + e] + rank;
+    slot[a] = p;
+    src_token[p] = (int32_t)(a / topk);
+}
+
+constexpr int MOE_Q_THREADS = 256;
+
+// Unit u = 8 consecutive elements of permuted row u / upr; rows at or past
+// offsets[experts] (the routed count) are not written.
+__global__ __launch_bounds__(MOE_Q_THREADS) void moe_gather_quantize_kernel(
+    const uint16_t *__restrict__ x, int64_t ld_x, const int32_t *__restrict__ src_token,
+    const int64_t *__restrict__ routed_end, uint8_t *__restrict__ q, int64_t ld_q,
+    uint8_t *__restrict__ s_swz, int64_t units, uint32_t upr, int64_t kt)
+{
+    const int64_t routed = *routed_end;
+    for (int64_t u = (int64_t)blockIdx.x * MOE_Q_THREADS + threadIdx.x; u - (threadIdx.x & 3) < units;
+         u += (int64_t)gridDim.x * MOE_Q_THREADS) {
+        // upr is a multiple of 32, so a quad shares its row
+        const int64_t row = u / upr;
+        const int64_t cu = u - row * upr;
+        const bool live = u < units && row < routed;
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (live) {
+            const int64_t t = src_token[row];
+            w = *reinterpret_cast<const uint4 *>(x + t * ld_x + cu * 8);
+        }
+        uint32_t m = pk_max_u16(pk_max_u16(mag2(w.x), mag2(w.y)), pk_max_u16(mag2(w.z), mag2(w.w)));
+        m = max(m & 0xFFFFu, m >> 16);
+        m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+        m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+        if (!live)
+            continue;
+        const uint32_t c = scale_code(m);
+        const float sc = cvt_scale(c);
+        uint2 out;
+        out.x = nan_block_select(cvt_x4(w.x, w.y, sc), c);
+        out.y = nan_block_select(cvt_x4(w.z, w.w, sc), c);
+        *reinterpret_cast<uint2 *>(q + row * ld_q + cu * 8) = out;
+        if ((threadIdx.x & 3) == 0) {
+            const int64_t b = cu >> 2;  // 32-element block of the row
+            s_swz[((row >> 5) * kt + (b >> 3)) * 256 + (32 * (b & 1) + (row & 31)) * 4 + ((b & 7) >> 1)] =
+                (uint8_t)c;
+        }
+    }
+}
+
+hipError_t launch_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
+                               const int32_t *topk_ids, int64_t topk, int64_t experts,
+                               int64_t *offsets, int32_t *src_token, int32_t *slot, void *q,
+                               int64_t ld_q, void *s_swz, hipStream_t stream)
+{
+    const int64_t n = tokens * topk;
+    const int64_t chunks = (n + MOE_CHUNK - 1) / MOE_CHUNK;
+    hipMemPool_t pool = workspace_pool();
+    if (pool == nullptr)
+        return hipErrorOutOfMemory;
+    void *ws = nullptr;
+    hipError_t e = hipMallocFromPoolAsync(&ws, (size_t)(chunks * experts) * sizeof(int32_t), pool, stream);
+    if (e != hipSuccess)
+        return e;
+    int32_t *counts = (int32_t *)ws;
+    hipLaunchKernelGGL(moe_count_kernel, dim3((unsigned)chunks), dim3(MOE_CHUNK), 0, stream, topk_ids, n,
+                       (int)experts, counts);
+    hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, stream, counts, chunks,
+                       (int)experts, offsets);
+    hipLaunchKernelGGL(moe_place_kernel, dim3((unsigned)chunks), dim3(MOE_CHUNK), 0, stream, topk_ids, n,
+                       (int)topk, (int)experts, counts, src_token, slot);
+    const uint32_t upr = (uint32_t)(hidden / 8);
+    const int64_t units = n * upr;
+    const int64_t per_pass = (int64_t)MOE_Q_THREADS;
+    const int64_t blocks = std::min<int64_t>((units + per_pass - 1) / per_pass, 65536);
+    hipLaunchKernelGGL(moe_gather_quantize_kernel, dim3((unsigned)blocks), dim3(MOE_Q_THREADS), 0, stream,
+                       (const uint16_t *)x, ld_x, src_token, offsets + experts, (uint8_t *)q, ld_q,
+                       (uint8_t *)s_swz, units, upr, (hidden / 32 + 7) / 8);
+    e = hipGetLastError();
+    const hipError_t fe = hipFreeAsync(ws, stream);
+    return e != hipSuccess ? e : fe;
+}
+
+// Combine: thread -> 8 consecutive columns of one token; the token's slots in
+// order j = 0..topk-1, FP32 sums of weight * value, BF16 (nearest even) out.
+// Slots outside [0, tokens * topk) contribute nothing.
+__global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t *__restrict__ y, int64_t ld_y,
+                                                          const int32_t *__restrict__ slot,
+                                                          const float *__restrict__ weights, int topk,
+                                                          uint16_t *__restrict__ out, int64_t ld_out,
+                                                          int64_t units, uint32_t upr, int64_t rows_y)
+{
+    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += (int64_t)gridDim.x * 256) {
+        const int64_t t = u / upr;
+        const int64_t cu = u - t * upr;
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int j = 0; j < topk; j++) {
+            const int32_t p = slot[t * topk + j];
+            if (p < 0 || p >= rows_y)  // unrouted, or not a row of y
+                continue;
+            const float w = weights[t * topk + j];
+            const uint4 v = *reinterpret_cast<const uint4 *>(y + (int64_t)p * ld_y + cu * 8);
+            const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                acc[2 * k] = fmaf(w, __builtin_bit_cast(float, wd[k] << 16), acc[2 * k]);
+                acc[2 * k + 1] = fmaf(w, __builtin_bit_cast(float, wd[k] & 0xFFFF0000u), acc[2 * k + 1]);
+            }
+        }
+        typedef float f2_t __attribute__((ext_vector_type(2)));
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+            o[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t{acc[2 * k], acc[2 * k + 1]}), bf16x2_t));
+        *reinterpret_cast<uint4 *>(out + t * ld_out + cu * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+hipError_t launch_moe_combine(const void *y, int64_t tokens, int64_t hidden, int64_t ld_y,
+                              const int32_t *slot, const float *weights, int64_t topk, void *out,
+                              int64_t ld_out, hipStream_t stream)
+{
+    const uint32_t upr = (uint32_t)(hidden / 8);
+    const int64_t units = tokens * upr;
+    const int64_t blocks = std::min<int64_t>((units + 255) / 256, 65536);
+    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const uint16_t *)y,
+                       ld_y, slot, weights, (int)topk, (uint16_t *)out, ld_out, units, upr, tokens * topk);
+    return hipGetLastError();
+}
+
+}  // namespace mx

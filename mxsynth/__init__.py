@@ -221,3 +221,27 @@ WORKLOADS = {
     "dense_bwd": "Qwen3-8B gate_up dgrad (12288x4096x24576) and wgrad (24576x4096x12288)",
     "moe": "Qwen3-30B-A3B grouped gate_up/down, 128 experts, top-8, Zipf(1.1) loads",
 }
+
+
+def moe_routing(seed: int = 5100, num_tokens: int = MOE_TOKENS, num_experts: int = MOE_EXPERTS,
+                top_k: int = MOE_TOPK, exponent: float = 1.1):
+    """Top-k routing with the per-expert row counts of zipf_expert_rows.
+
+    Returns (topk_ids int32 [num_tokens][top_k], weights float32 [num_tokens]
+    [top_k]).  Expert e's rows[e] assignments go to distinct tokens (the
+    experts' slots, laid out expert by expert, are dealt to tokens round-robin,
+    and no expert holds more than num_tokens rows); tokens and the order of
+    each token's experts are then shuffled.  Weights are positive and sum to
+    1 per token (a softmax over seeded logits)."""
+    rows = zipf_expert_rows(num_tokens, num_experts, top_k, exponent)
+    flat = np.repeat(np.arange(num_experts, dtype=np.int32), rows)
+    grid = np.empty((num_tokens, top_k), np.int32)
+    i = np.arange(flat.size)
+    grid[i % num_tokens, i // num_tokens] = flat
+    rng = np.random.default_rng(seed)
+    grid = grid[rng.permutation(num_tokens)]
+    grid = np.take_along_axis(grid, np.argsort(rng.random(grid.shape), axis=1), axis=1)
+    logits = rng.normal(0.0, 1.0, size=grid.shape)
+    w = np.exp(logits - logits.max(axis=1, keepdims=True))
+    w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+    return grid, w

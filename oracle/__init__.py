@@ -246,3 +246,51 @@ def grouped_gemm(offsets, qa, sa, qb, sb):
     cols = np.tile(np.arange(N, dtype=np.int64), M)
     c, bnd = grouped_gemm_sampled(rows, cols, offsets, qa, sa, qb, sb)
     return c.reshape(M, N), bnd.reshape(M, N)
+
+
+def moe_dispatch(topk_ids, num_experts: int):
+    """Rows sorted by expert, stably: the MoE layer's expert GEMMs run per expert
+    on rows sorted by expert ("End-to-End MXFP8 Reinforcement Learning on
+    Blackwell", Table 2: 128 experts, 8 routed per token).  Assignment
+    a = t*topk + j sends token t to expert e = topk_ids[t][j]; ids outside
+    [0, num_experts) are not routed.  Assignment a lands on row offsets[e] +
+    (number of assignments a' < a to the same expert).
+
+    Returns (offsets int64 [G+1], src_token int32 [n]: token of each row, -1
+    past the routed count, slot int32 [n]: row of each assignment, -1 if not
+    routed); n = tokens * topk."""
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    tokens, topk = ids.shape
+    e = ids.reshape(-1)
+    n = e.size
+    valid = (e >= 0) & (e < num_experts)
+    offsets = np.zeros(num_experts + 1, np.int64)
+    offsets[1:] = np.cumsum(np.bincount(e[valid], minlength=num_experts))
+    # a stable sort by expert (library sort as one step); unrouted ones last
+    order = np.argsort(np.where(valid, e, num_experts), kind="stable")
+    routed = int(valid.sum())
+    slot = np.full(n, -1, np.int32)
+    slot[order[:routed]] = np.arange(routed, dtype=np.int32)
+    src = np.full(n, -1, np.int32)
+    src[:routed] = (order[:routed] // topk).astype(np.int32)
+    return offsets, src, slot
+
+
+def moe_combine(y_bits, slot, weights):
+    """out[t] = sum_j weights[t][j] * y[slot[t*topk + j]] in float64, skipping
+    slots outside [0, rows of y); y given as BF16 bit patterns [n][hidden]."""
+    y = np.asarray(y_bits, np.uint16).astype(np.uint32) << 16
+    y = y.view(np.float32).astype(np.float64)
+    w = np.asarray(weights, np.float32).astype(np.float64)
+    tokens, topk = w.shape
+    slot = np.asarray(slot, np.int64).reshape(tokens, topk)
+    out = np.zeros((tokens, y.shape[1]), np.float64)
+    bnd = np.zeros_like(out)
+    for j in range(topk):
+        p = slot[:, j]
+        ok = (p >= 0) & (p < y.shape[0])
+        rows = y[np.where(ok, p, 0)]
+        term = np.where(ok[:, None], w[:, j:j + 1] * rows, 0.0)
+        out += term
+        bnd += np.abs(term)
+    return out, bnd
