@@ -65,6 +65,12 @@ def lib():
         L.oracle_grouped_gemm_sampled.argtypes = [_i64, _i64p, _i64p, _i64, _i64p, _i64, _i64,
                                                   _u8p, _i64, _u8p, _i64, _u8p, _i64, _u8p,
                                                   _i64, _f64p, _f64p]
+        L.oracle_grouped_pad_offsets.argtypes = [_i64, _i64p, _i64p]
+        L.oracle_quantize_colwise_grouped.argtypes = [_u16p, _i64, _i64, _i64, _i64p, _i64p,
+                                                      _u8p, _i64, _u8p, _i64]
+        L.oracle_grouped_wgrad_sampled.argtypes = [_i64, _i64p, _i64p, _i64p, _i64p, _u8p, _i64,
+                                                   _u8p, _i64, _u8p, _i64, _u8p, _i64, _f64p,
+                                                   _f64p]
         _lib = L
     return _lib
 
@@ -294,3 +300,83 @@ def moe_combine(y_bits, slot, weights):
         out += term
         bnd += np.abs(term)
     return out, bnd
+
+
+# ---- MoE backward ----------------------------------------------------------
+# The expert weight gradient dW_g = dY_g^T X_g of the update_actor stage
+# ("End-to-End MXFP8 Reinforcement Learning on Blackwell", Table 8; Table 2
+# for the 128-expert top-8 model) contracts over the expert's own token rows,
+# with both operands quantized column-wise in 32-row blocks that never hold
+# rows of two experts.  Layout: expert g's rows become columns
+# [pad[g], pad[g+1]) of the transposed operand, each range max(256, m_g
+# rounded up to 256) long, the rows past m_g taken as zeros.
+
+
+def grouped_pad_offsets(offsets) -> np.ndarray:
+    """pad int64 [G+1]: pad[0] = 0, pad[g+1] = pad[g] + max(256, ceil(m_g/256)*256)."""
+    offsets = _c(offsets, np.int64)
+    G = offsets.size - 1
+    pad = np.empty(G + 1, np.int64)
+    lib().oracle_grouped_pad_offsets(G, _p(offsets, _i64p), _p(pad, _i64p))
+    return pad
+
+
+def grouped_k_capacity(rows_total: int, G: int) -> int:
+    """A column count that holds pad[G] for any split of rows_total rows into G
+    experts: each range exceeds its m_g by at most 256."""
+    return (rows_total + 255) // 256 * 256 + 256 * G
+
+
+def quantize_colwise_grouped(x_bits, offsets, k_cap: int):
+    """x_bits uint16 [rows_total, cols], rows sorted by expert ->
+    (qt uint8 [cols, k_cap], st uint8 [cols, k_cap/32], pad int64 [G+1]).
+    Expert g's column-wise blocks of its own rows land in columns
+    [pad[g], pad[g+1]); columns past pad[G] are zero here (the library
+    leaves them unwritten)."""
+    x = _c(x_bits, np.uint16)
+    offsets = _c(offsets, np.int64)
+    rows, cols = x.shape
+    G = offsets.size - 1
+    assert offsets[0] == 0 and offsets[-1] == rows and (np.diff(offsets) >= 0).all()
+    pad = grouped_pad_offsets(offsets)
+    assert k_cap % 256 == 0 and pad[-1] <= k_cap
+    qt = np.zeros((cols, k_cap), np.uint8)
+    st = np.zeros((cols, k_cap // 32), np.uint8)
+    if rows == 0:
+        x = np.zeros((1, cols), np.uint16)  # a valid pointer; no row is read
+    lib().oracle_quantize_colwise_grouped(_p(x, _u16p), cols, cols, G, _p(offsets, _i64p),
+                                          _p(pad, _i64p), _p(qt, _u8p), k_cap, _p(st, _u8p),
+                                          k_cap // 32)
+    return qt, st, pad
+
+
+def grouped_wgrad_sampled(groups, rows, cols, pad, qa, sa, qb, sb):
+    """Entries C_g[rows[e]][cols[e]] (g = groups[e]) of the per-expert product
+    C_g = deq(A)[:, pad[g]:pad[g+1]] deq(B)[:, pad[g]:pad[g+1]]^T, with bounds.
+    qa [M, Kc], sa [M, Kc/32], qb [N, Kc], sb [N, Kc/32]."""
+    qa, sa, qb, sb = (_c(a, np.uint8) for a in (qa, sa, qb, sb))
+    groups, rows, cols, pad = (_c(a, np.int64) for a in (groups, rows, cols, pad))
+    Kc = qa.shape[1]
+    assert qb.shape[1] == Kc and sa.shape[1] == Kc // 32 and sb.shape[1] == Kc // 32
+    assert groups.shape == rows.shape == cols.shape
+    assert pad[-1] <= Kc and (pad % 32 == 0).all()
+    assert rows.size == 0 or (rows.min() >= 0 and rows.max() < qa.shape[0])
+    assert cols.size == 0 or (cols.min() >= 0 and cols.max() < qb.shape[0])
+    assert groups.size == 0 or (groups.min() >= 0 and groups.max() < pad.size - 1)
+    c = np.empty(rows.size, np.float64)
+    bnd = np.empty(rows.size, np.float64)
+    lib().oracle_grouped_wgrad_sampled(rows.size, _p(groups, _i64p), _p(rows, _i64p),
+                                       _p(cols, _i64p), _p(pad, _i64p), _p(qa, _u8p), Kc,
+                                       _p(sa, _u8p), Kc // 32, _p(qb, _u8p), Kc, _p(sb, _u8p),
+                                       Kc // 32, _p(c, _f64p), _p(bnd, _f64p))
+    return c, bnd
+
+
+def grouped_wgrad(pad, qa, sa, qb, sb):
+    """Every entry (small sizes): float64 [G, M, N] and its bound."""
+    pad = _c(pad, np.int64)
+    G = pad.size - 1
+    M, N = np.asarray(qa).shape[0], np.asarray(qb).shape[0]
+    g, i, j = np.meshgrid(np.arange(G), np.arange(M), np.arange(N), indexing="ij")
+    c, bnd = grouped_wgrad_sampled(g.ravel(), i.ravel(), j.ravel(), pad, qa, sa, qb, sb)
+    return c.reshape(G, M, N), bnd.reshape(G, M, N)

@@ -316,3 +316,71 @@ void oracle_dequantize_rowwise(const uint8_t *q, int64_t rows, int64_t cols, int
         for (k = 0; k < cols; k++)
             out[r * cols + k] = oracle_dequant(q[r * ld_q + k], s[r * ld_s + k / 32]);
 }
+
+/* ---- MoE backward: per-expert column-wise operands and weight gradients --
+ * The update_actor stage of the MoE learner (paper Table 8; Table 2 for the
+ * 128-expert, top-8 model) needs each expert's weight gradient
+ * dW_g = dY_g^T X_g, a contraction over that expert's token rows only.  Both
+ * operands are quantized column-wise in 32-row blocks, and a block may not
+ * hold rows of two experts.  Layout (ours): expert g's rows
+ * [offsets[g], offsets[g+1]) become columns [pad[g], pad[g+1]) of the
+ * transposed operand, with pad[0] = 0 and
+ * pad[g+1] = pad[g] + max(256, m_g rounded up to a multiple of 256); the
+ * columns past the expert's m_g rows hold zero codes (zero rows appended,
+ * which leave every block maximum unchanged). */
+
+void oracle_grouped_pad_offsets(int64_t G, const int64_t *offsets, int64_t *pad)
+{
+    int64_t g, m, len;
+    pad[0] = 0;
+    for (g = 0; g < G; g++) {
+        m = offsets[g + 1] - offsets[g];
+        len = ((m + 255) / 256) * 256;
+        if (len < 256)
+            len = 256;
+        pad[g + 1] = pad[g] + len;
+    }
+}
+
+/* x[rows_total][ld_x] BF16, rows sorted by expert -> qt[cols][ld_qt] and
+ * st[cols][ld_st] (plain scales, one per 32 columns of qt), columns laid out
+ * by pad (from oracle_grouped_pad_offsets).  Columns past pad[G] are left
+ * untouched. */
+void oracle_quantize_colwise_grouped(const uint16_t *x, int64_t cols, int64_t ld_x, int64_t G,
+                                     const int64_t *offsets, const int64_t *pad, uint8_t *qt,
+                                     int64_t ld_qt, uint8_t *st, int64_t ld_st)
+{
+    int64_t g, c, b, i, row;
+    uint16_t v[32];
+    for (g = 0; g < G; g++)
+        for (c = 0; c < cols; c++)
+            for (b = 0; b < (pad[g + 1] - pad[g]) / 32; b++) {
+                for (i = 0; i < 32; i++) {
+                    row = offsets[g] + 32 * b + i;
+                    v[i] = row < offsets[g + 1] ? x[row * ld_x + c] : 0x0000; /* +0.0 */
+                }
+                oracle_quantize_block(v, 1, qt + c * ld_qt + pad[g] + 32 * b, 1,
+                                      st + c * ld_st + pad[g] / 32 + b);
+            }
+}
+
+/* Selected entries of the per-expert weight gradient: entry e is
+ * C_g[rows[e]][cols[e]] with g = groups[e], i.e.
+ * sum over k in [pad[g], pad[g+1]) of deqA[row][k] * deqB[col][k]
+ * (A = qa[M][ld_a], B = qb[N][ld_b], plain scales one per 32 of k). */
+void oracle_grouped_wgrad_sampled(int64_t n, const int64_t *groups, const int64_t *rows,
+                                  const int64_t *cols, const int64_t *pad, const uint8_t *qa,
+                                  int64_t ld_a, const uint8_t *sa, int64_t ld_sa,
+                                  const uint8_t *qb, int64_t ld_b, const uint8_t *sb,
+                                  int64_t ld_sb, double *c, double *bnd)
+{
+    int64_t e, g, lo, len;
+    for (e = 0; e < n; e++) {
+        g = groups[e];
+        lo = pad[g];
+        len = pad[g + 1] - lo;
+        oracle_gemm_entry(len, qa + rows[e] * ld_a + lo, sa + rows[e] * ld_sa + lo / 32,
+                          qb + cols[e] * ld_b + lo, sb + cols[e] * ld_sb + lo / 32, c + e,
+                          bnd + e);
+    }
+}
