@@ -13,8 +13,14 @@ the ~4.5k-token dense break-even that sets M = 4608):
      X column-wise; dgrad = dY . W (column-wise weights of step 1) and
      wgrad = dY^T . X;
   4. Qwen3-30B-A3B MoE layer: 20480 tokens x top-8 = 163840 routed rows over
-     128 experts with Zipf(1.1) loads; quantize activations and expert
-     weights row-wise, rearrange, grouped GEMMs gate_up and down.
+     128 experts with Zipf(1.1) loads; expert weights quantized in both
+     orientations (one dual pass over all experts), activations row-wise,
+     grouped GEMMs gate_up and down;
+  5. the same MoE layer's expert backward (Table 8's update_actor): per
+     projection, dY row-wise for the data gradient dX = dY . W_g (grouped over
+     rows, column-wise expert weights of step 4), dY and the forward input
+     column-wise per expert into 256-aligned column ranges for the weight
+     gradient dW_g = dY_g^T X_g (grouped over each expert's token range).
 
 Inputs are drawn once on the device (seeded, same distributions as the
 parity tests' CPU draws) and stay resident in HBM; the timed region holds
@@ -108,6 +114,7 @@ def build_workload(mx, torch, mxsynth):
     xh, xi = mxsynth.dense_fwd_activations(device=dev)
     dy, xb = mxsynth.dense_bwd_inputs(device=dev)
     rows_per, a_gu, a_dn, w_gu, w_dn = mxsynth.moe_inputs(device=dev)
+    dy_gu, dy_dn = mxsynth.moe_bwd_grads(device=dev)
     off = torch.from_numpy(mxsynth.offsets_from_rows(rows_per)).to(dev)
     u8 = dict(dtype=torch.uint8, device=dev)
     swz = mx.mx_scale_swizzled_bytes
@@ -143,14 +150,30 @@ def build_workload(mx, torch, mxsynth):
     o["xT_q"], o["xT_s"] = torch.empty(4096, 12288, **u8), torch.empty(4096, 384, **u8)
     o["xT_swz"] = torch.empty(swz(4096, 384), **u8)
     M = int(off[-1].item())
-    for name, a, w in (("mgu", a_gu, w_gu), ("mdn", a_dn, w_dn)):
+    G = w_gu.shape[0]
+    k_cap = mx.mx_grouped_k_capacity(M, G)
+    for name, a, w, dyp in (("mgu", a_gu, w_gu, dy_gu), ("mdn", a_dn, w_dn, dy_dn)):
         G, N, K = w.shape
         o[name + "_aq"] = torch.empty(M, K, **u8)
         o[name + "_as"] = torch.empty(M, K // 32, **u8)
         o[name + "_aswz"] = torch.empty(swz(M, K // 32), **u8)
-        o[name + "_wq"] = torch.empty(G * N, K, **u8)
-        o[name + "_ws"] = torch.empty(G * N, K // 32, **u8)
-        o[name + "_wswz"] = torch.empty(swz(G * N, K // 32), **u8)
+        # expert weights, both orientations: [G][N][K] and [G][K][N], scales
+        # rearranged per expert, back to back
+        o[name + "_wq"] = torch.empty(G, N, K, **u8)
+        o[name + "_wswz"] = torch.empty(G * swz(N, K // 32), **u8)
+        o[name + "_wqt"] = torch.empty(G, K, N, **u8)
+        o[name + "_wstswz"] = torch.empty(G * swz(K, N // 32), **u8)
+        # backward: dY [M][N] row-wise (data gradient), dY and the forward
+        # input column-wise per expert (weight gradient)
+        o[name + "_dyq"] = torch.empty(M, N, **u8)
+        o[name + "_dys"] = torch.empty(M, N // 32, **u8)
+        o[name + "_dyswz"] = torch.empty(swz(M, N // 32), **u8)
+        o[name + "_dyT"] = torch.empty(N, k_cap, **u8)
+        o[name + "_dyTswz"] = torch.empty(swz(N, k_cap // 32), **u8)
+        o[name + "_xT"] = torch.empty(K, k_cap, **u8)
+        o[name + "_xTswz"] = torch.empty(swz(K, k_cap // 32), **u8)
+        o[name + "_pad"] = torch.empty(G + 1, dtype=torch.int64, device=dev)
+        o[name + "_pad2"] = torch.empty(G + 1, dtype=torch.int64, device=dev)
     bf = dict(dtype=torch.bfloat16, device=dev)
     o["C_qkv"] = torch.empty(4608, 6144, **bf)
     o["C_o"] = torch.empty(4608, 4096, **bf)
@@ -160,8 +183,12 @@ def build_workload(mx, torch, mxsynth):
     o["C_wgrad"] = torch.empty(24576, 4096, **bf)
     o["C_mgu"] = torch.empty(M, 1536, **bf)
     o["C_mdn"] = torch.empty(M, 2048, **bf)
+    o["dX_mgu"] = torch.empty(M, 2048, **bf)
+    o["dX_mdn"] = torch.empty(M, 768, **bf)
+    o["dW_mgu"] = torch.empty(G, 1536, 2048, **bf)
+    o["dW_mdn"] = torch.empty(G, 2048, 768, **bf)
     inputs = dict(W=W, xh=xh, xi=xi, dy=dy, x=xb, off=off, a_gu=a_gu, a_dn=a_dn,
-                  w_gu=w_gu, w_dn=w_dn, M=M)
+                  w_gu=w_gu, w_dn=w_dn, dy_gu=dy_gu, dy_dn=dy_dn, M=M, k_cap=k_cap)
     return inputs, o
 
 
@@ -206,13 +233,26 @@ def step(mx, I, o, T):
     T("gemm", g, o["dyT_q"], o["dyT_swz"], o["xT_q"], o["xT_swz"], c=o["C_wgrad"])
     # 4. MoE layer, grouped per expert
     for name, a, w in (("mgu", I["a_gu"], I["w_gu"]), ("mdn", I["a_dn"], I["w_dn"])):
-        G, N, K = w.shape
-        T("quant_row", rq, w.view(G * N, K), o[name + "_wq"], o[name + "_ws"])
-        T("swizzle", sw, o[name + "_ws"], o[name + "_wswz"])
+        T("quant_dual", mx.mx_quantize_dual_experts, w, q=o[name + "_wq"], s_swz=o[name + "_wswz"],
+          qt=o[name + "_wqt"], st_swz=o[name + "_wstswz"])
         T("quant_row", rq, a, o[name + "_aq"], o[name + "_as"])
         T("swizzle", sw, o[name + "_as"], o[name + "_aswz"])
         T("grouped_gemm", mx.mx_grouped_gemm, I["off"], o[name + "_aq"], o[name + "_aswz"],
-          o[name + "_wq"].view(G, N, K), o[name + "_wswz"], c=o["C_" + name])
+          o[name + "_wq"], o[name + "_wswz"], c=o["C_" + name])
+    # 5. MoE expert backward: data gradient grouped over rows, weight gradient
+    #    grouped over each expert's token range
+    k_cap = I["k_cap"]
+    for name, a, dyp in (("mgu", I["a_gu"], I["dy_gu"]), ("mdn", I["a_dn"], I["dy_dn"])):
+        T("quant_row", rq, dyp, o[name + "_dyq"], o[name + "_dys"])
+        T("swizzle", sw, o[name + "_dys"], o[name + "_dyswz"])
+        T("grouped_gemm", mx.mx_grouped_gemm, I["off"], o[name + "_dyq"], o[name + "_dyswz"],
+          o[name + "_wqt"], o[name + "_wstswz"], c=o["dX_" + name])
+        T("quant_col_grouped", mx.mx_quantize_colwise_grouped, dyp, I["off"], k_cap=k_cap,
+          qt=o[name + "_dyT"], st_swz=o[name + "_dyTswz"], pad_offsets=o[name + "_pad"])
+        T("quant_col_grouped", mx.mx_quantize_colwise_grouped, a, I["off"], k_cap=k_cap,
+          qt=o[name + "_xT"], st_swz=o[name + "_xTswz"], pad_offsets=o[name + "_pad2"])
+        T("grouped_wgrad", mx.mx_grouped_gemm_wgrad, o[name + "_pad"], o[name + "_dyT"],
+          o[name + "_dyTswz"], o[name + "_xT"], o[name + "_xTswz"], c=o["dW_" + name])
 
 
 def work_per_step(I):
@@ -222,14 +262,21 @@ def work_per_step(I):
     W = I["W"]
     dual_el = sum(w.numel() for w in W.values())                 # weight sync, both
     dual_el += I["dy"].numel()                                   # dgrad + wgrad operand
+    dual_el += I["w_gu"].numel() + I["w_dn"].numel()             # MoE expert weights
     row_el = dual_el + I["xh"].numel() + I["xi"].numel()         # + forward activations
-    row_el += I["w_gu"].numel() + I["w_dn"].numel() + I["a_gu"].numel() + I["a_dn"].numel()
+    row_el += I["a_gu"].numel() + I["a_dn"].numel()              # + MoE activations
+    row_el += I["dy_gu"].numel() + I["dy_dn"].numel()            # + MoE output gradients
     col_el = dual_el + I["x"].numel()                            # + wgrad activation operand
+    # per-expert column-wise operands of the MoE weight gradients
+    colg_el = (I["dy_gu"].numel() + I["dy_dn"].numel() + I["a_gu"].numel()
+               + I["a_dn"].numel())
     M = I["M"]
     dense = (2 * 4608 * 6144 * 4096 + 2 * 4608 * 4096 * 4096 + 2 * 4608 * 24576 * 4096
              + 2 * 4608 * 4096 * 12288 + 2 * 12288 * 4096 * 24576 + 2 * 24576 * 4096 * 12288)
-    grouped = 2 * M * 1536 * 2048 + 2 * M * 2048 * 768
-    return row_el, col_el, dual_el, dense, grouped
+    grouped = 2 * (2 * M * 1536 * 2048 + 2 * M * 2048 * 768)   # forward + data gradient
+    wgrad = 2 * M * 1536 * 2048 + 2 * M * 2048 * 768
+    return dict(row_el=row_el, col_el=col_el, dual_el=dual_el, colg_el=colg_el, dense=dense,
+                grouped=grouped, wgrad=wgrad)
 
 
 def cpu_baseline(torch, mxsynth, row_el, col_el, flops):
@@ -326,16 +373,19 @@ def main():
     gpu_ms = start.elapsed_time(end)
     ms_per_step = gpu_ms / args.steps
 
-    row_el, col_el, dual_el, dense, grouped = work_per_step(I)
-    flops = dense + grouped
+    w = work_per_step(I)
+    row_el, col_el, dual_el, colg_el = w["row_el"], w["col_el"], w["dual_el"], w["colg_el"]
+    dense, grouped, wgrad = w["dense"], w["grouped"], w["wgrad"]
+    flops = dense + grouped + wgrad
     K = args.steps
     row_only, col_only = row_el - dual_el, col_el - dual_el
-    q_bytes = ((row_only + col_only) * QUANT_BYTES_PER_ELEMENT
+    q_bytes = ((row_only + col_only + colg_el) * QUANT_BYTES_PER_ELEMENT
                + dual_el * DUAL_BYTES_PER_ELEMENT)
     qt = (T.totals.get("quant_row", 0) + T.totals.get("quant_col", 0)
-          + T.totals.get("quant_dual", 0)) / K  # ms
+          + T.totals.get("quant_dual", 0) + T.totals.get("quant_col_grouped", 0)) / K  # ms
     gemm_ms = T.totals["gemm"] / K
     ggemm_ms = T.totals["grouped_gemm"] / K
+    wg_ms = T.totals["grouped_wgrad"] / K
     ops = {
         "quantize_rowwise": {"ms": T.totals["quant_row"] / K,
                              "GB/s": row_only * QUANT_BYTES_PER_ELEMENT / (T.totals["quant_row"] / K) / 1e6},
@@ -344,8 +394,12 @@ def main():
         "quantize_dual": {"ms": T.totals["quant_dual"] / K,
                           "GB/s": dual_el * DUAL_BYTES_PER_ELEMENT / (T.totals["quant_dual"] / K) / 1e6},
         "scale_swizzle": {"ms": T.totals["swizzle"] / K, "launches": T.counts["swizzle"] // K},
+        "quantize_colwise_grouped": {
+            "ms": T.totals["quant_col_grouped"] / K,
+            "GB/s": colg_el * QUANT_BYTES_PER_ELEMENT / (T.totals["quant_col_grouped"] / K) / 1e6},
         "dense_gemm": {"ms": gemm_ms, "TFLOP/s": dense / gemm_ms / 1e9},
         "grouped_gemm": {"ms": ggemm_ms, "TFLOP/s": grouped / ggemm_ms / 1e9},
+        "grouped_wgrad": {"ms": wg_ms, "TFLOP/s": wgrad / wg_ms / 1e9},
     }
     for k, v in ops.items():
         if "GB/s" in v:
@@ -373,17 +427,19 @@ def main():
             "workload": ("qwen3-layer-pass: weight-sync row+column MXFP8 quantize of one "
                          "Qwen3-8B layer (one dual pass per weight); dense fwd M=4608 (qkv, o, gate_up, down); dense bwd "
                          "gate_up dgrad 12288x4096x24576 + wgrad 24576x4096x12288; Qwen3-30B-A3B "
-                         "MoE grouped gate_up/down, 163840 rows, 128 experts, Zipf(1.1)"),
+                         "MoE grouped gate_up/down, 163840 rows, 128 experts, Zipf(1.1), forward "
+                         "and expert backward (data gradient grouped over rows, weight gradient "
+                         "grouped over each expert's token range)"),
             "gemm_flop_per_step": flops,
-            "quantized_elements_per_step": row_el + col_el,
+            "quantized_elements_per_step": row_el + col_el + colg_el,
             "parallelism": "single GPU",
         },
         "value_definition": "total GEMM FLOP of the step / wall time of the whole step "
                             "(quantize, rearrangement and GEMMs, HIP events)",
         "quantize_GBps": round(q_bytes / qt / 1e6, 1),
         "quantize_frac_hbm_peak": round(q_bytes / qt / 1e6 / HBM_PEAK_GBPS, 4),
-        "gemm_TFLOPs": round((dense + grouped) / (gemm_ms + ggemm_ms) / 1e9, 1),
-        "gemm_frac_mfma_peak": round((dense + grouped) / (gemm_ms + ggemm_ms) / 1e9
+        "gemm_TFLOPs": round(flops / (gemm_ms + ggemm_ms + wg_ms) / 1e9, 1),
+        "gemm_frac_mfma_peak": round(flops / (gemm_ms + ggemm_ms + wg_ms) / 1e9
                                      / MFMA_FP8_PEAK_TFLOPS, 4),
         "ops": ops,
         "roofline": {
@@ -400,7 +456,7 @@ def main():
         "wall_s_timed_region": round(wall, 3),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(torch, mxsynth, row_el, col_el, flops)
+        result["cpu_baseline"] = cpu_baseline(torch, mxsynth, row_el, col_el + colg_el, flops)
     print(json.dumps(result))
 
 

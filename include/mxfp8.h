@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define MXFP8_ABI_VERSION 2
+#define MXFP8_ABI_VERSION 3
 
 typedef enum mx_status {
     MX_OK = 0,
@@ -212,6 +212,29 @@ typedef struct mx_dual_job {
 mx_status mx_quantize_dual_batch(const mx_dual_job *jobs, int n_jobs, void *stream);
 
 /*
+ * The weight synchronization of a MoE layer's experts (paper Table 2:
+ * Qwen3-30B-A3B, 128 experts; abstract and Table 11: the synchronized
+ * weights must equal the learner's FP8 weights byte for byte): mx_quantize_dual
+ * of every expert of a stacked weight in one launch.
+ *   x       BF16 [num_experts][rows][cols] contiguous
+ *   q       E4M3 [num_experts][rows][cols]: expert e = mx_quantize_rowwise's q
+ *   s_swz   num_experts rearranged [rows][cols/32] scale buffers back to back,
+ *           expert e at e * mx_scale_swizzled_bytes(rows, cols/32)
+ *   qt      E4M3 [num_experts][cols][rows]: expert e = mx_quantize_colwise's qt
+ *   st_swz  num_experts rearranged [cols][rows/32] buffers back to back,
+ *           expert e at e * mx_scale_swizzled_bytes(cols, rows/32)
+ * (q, s_swz) is mx_grouped_gemm's B for the forward product over rows
+ * (N = rows, K = cols), and (qt, st_swz) its B for the data gradient
+ * (N = cols, K = rows).  Every expert's bytes equal mx_quantize_dual's.
+ * Requirements: num_experts >= 0 (else MX_ERR_INVALID_ARG); rows % 32 == 0
+ * and cols % 32 == 0 (else MX_ERR_SHAPE); x, q, qt 16-byte aligned, the
+ * scale buffers 4-byte aligned (else MX_ERR_ALIGN); no two of the five
+ * stacks overlap (else MX_ERR_OVERLAP).
+ */
+mx_status mx_quantize_dual_experts(const void *x, int64_t num_experts, int64_t rows, int64_t cols,
+                                   void *q, void *s_swz, void *qt, void *st_swz, void *stream);
+
+/*
  * MoE dispatch: the routed rows sorted by expert, gathered and quantized
  * row-wise as the grouped GEMM's A operand (paper Table 2: Qwen3-30B-A3B,
  * 128 experts, 8 routed per token; its expert GEMMs run per expert on rows
@@ -326,6 +349,72 @@ mx_status mx_grouped_gemm(int64_t num_groups, int64_t M_total, int64_t N, int64_
                           const int64_t *group_offsets, const void *a_q, int64_t ld_a,
                           const void *a_s_swz, const void *b_q, const void *b_s_swz,
                           void *c, int64_t ld_c, int c_dtype, void *stream);
+
+/*
+ * MoE weight gradient, operand side.  In the update_actor stage of the MoE
+ * learner (paper Table 8; Table 2: Qwen3-30B-A3B, 128 experts, top-8) each
+ * expert's weight gradient dW_g = dY_g^T X_g contracts over that expert's own
+ * token rows, with dY and X quantized column-wise; a 32-row block must not
+ * hold rows of two experts.  This call quantizes x column-wise per expert:
+ *   x              BF16 [rows_total][ld_x], rows sorted by expert
+ *   group_offsets  DEVICE int64 [num_groups + 1]: expert g's rows are
+ *                  [group_offsets[g], group_offsets[g+1]) (mx_moe_dispatch's
+ *                  offsets); read on the device only
+ *   pad_offsets    DEVICE int64 [num_groups + 1] out: pad[0] = 0,
+ *                  pad[g+1] = pad[g] + max(256, m_g rounded up to 256),
+ *                  m_g = group_offsets[g+1] - group_offsets[g]
+ *   qt             E4M3 [cols][ld_qt] out: column pad[g] + i of row j is
+ *                  the column-wise code of x[group_offsets[g] + i][j] for
+ *                  i < m_g, in 32-row blocks counted from the expert's first
+ *                  row; columns pad[g] + m_g .. pad[g+1]-1 are zero codes
+ *                  (rows of zeros appended to the expert)
+ *   st_swz         the scales of qt ([cols][k_cap/32], one per 32 columns)
+ *                  in the rearranged layout of mx_scale_swizzle
+ *                  (mx_scale_swizzled_bytes(cols, k_cap/32) bytes); blocks of
+ *                  appended zeros only have scale 0
+ * Columns from pad[num_groups] to k_cap and their scale tiles are not
+ * written.  k_cap must be at least mx_grouped_k_capacity(rows_total,
+ * num_groups), a bound on pad[num_groups] for any split of the rows.  The
+ * outputs feed mx_grouped_gemm_wgrad (k_offsets = pad_offsets).
+ * Requirements: rows_total >= 0, cols >= 1, num_groups in 1..1024 (else
+ * MX_ERR_INVALID_ARG / MX_ERR_UNSUPPORTED); cols % 32 == 0 (else
+ * MX_ERR_SHAPE); k_cap % 256 == 0, k_cap >= the capacity, ld_x >= cols,
+ * ld_qt >= k_cap (else MX_ERR_INVALID_ARG; x may be null when rows_total is
+ * 0); x and qt 16-byte aligned rows
+ * (ld_x % 8, ld_qt % 16), st_swz 4 bytes, the offsets 8 bytes (else
+ * MX_ERR_ALIGN); outputs overlap nothing (else MX_ERR_OVERLAP).  Offsets
+ * that are not nondecreasing within [0, rows_total] are clamped into it
+ * (unspecified but in-bounds results).
+ */
+int64_t mx_grouped_k_capacity(int64_t rows_total, int64_t num_groups);
+mx_status mx_quantize_colwise_grouped(const void *x, int64_t rows_total, int64_t cols, int64_t ld_x,
+                                      const int64_t *group_offsets, int64_t num_groups,
+                                      int64_t *pad_offsets, void *qt, int64_t ld_qt, int64_t k_cap,
+                                      void *st_swz, void *stream);
+
+/*
+ * MoE weight gradient, product side (paper Table 8, update_actor; Table 2):
+ *   for g < num_groups, with r_g = [k_offsets[g], k_offsets[g+1]):
+ *   C_g[i][j] = sum over k in r_g of deq(A)[i][k] * deq(B)[j][k]
+ *   A  E4M3 [M][ld_a] + rearranged [M][k_cap/32] scales (e.g. dY's
+ *      mx_quantize_colwise_grouped output: M = dY's columns)
+ *   B  E4M3 [N][ld_b] + rearranged [N][k_cap/32] scales (X's output)
+ *   c  [num_groups][M][ld_c] of c_dtype: C_g at c + g * M * ld_c
+ *   k_offsets  DEVICE int64 [num_groups + 1], multiples of 256 with every
+ *              range at least 256 long (mx_quantize_colwise_grouped's
+ *              pad_offsets); other values are clamped so that each range is
+ *              at least one 256-column group inside [0, k_cap) (unspecified
+ *              but in-bounds results)
+ * An expert with no rows contracts its appended zeros: C_g = 0.  Tiles are
+ * dealt longest range first over persistent workgroups.
+ * Requirements: those of mx_gemm with K = k_cap, plus k_cap % 256 == 0 (else
+ * MX_ERR_SHAPE), num_groups in 1..1024 (else MX_ERR_INVALID_ARG /
+ * MX_ERR_UNSUPPORTED); C overlaps no input (else MX_ERR_OVERLAP).
+ */
+mx_status mx_grouped_gemm_wgrad(int64_t num_groups, int64_t M, int64_t N, int64_t k_cap,
+                                const int64_t *k_offsets, const void *a_q, int64_t ld_a,
+                                const void *a_s_swz, const void *b_q, int64_t ld_b,
+                                const void *b_s_swz, void *c, int64_t ld_c, int c_dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,9 @@ import torch
 __all__ = [
     "MxError", "load", "lib_path", "mx_abi_version", "mx_status_string", "mx_last_error", "mx_quantize_rowwise",
     "mx_quantize_colwise", "mx_scale_swizzled_bytes", "mx_scale_swizzle", "mx_gemm",
-    "mx_grouped_gemm", "MX_OK", "MX_ERR_INVALID_ARG", "MX_ERR_SHAPE", "MX_ERR_ALIGN",
+    "mx_grouped_gemm", "mx_quantize_dual", "mx_quantize_dual_batch", "mx_quantize_dual_experts",
+    "mx_moe_dispatch", "mx_moe_combine", "mx_grouped_k_capacity", "mx_quantize_colwise_grouped",
+    "mx_grouped_gemm_wgrad", "MX_OK", "MX_ERR_INVALID_ARG", "MX_ERR_SHAPE", "MX_ERR_ALIGN",
     "MX_ERR_OVERLAP", "MX_ERR_UNSUPPORTED", "MX_ERR_HIP", "MX_BF16", "MX_F32",
 ]
 
@@ -91,6 +93,16 @@ def load() -> ctypes.CDLL:
     L.mx_grouped_gemm.restype = ctypes.c_int
     L.mx_grouped_gemm.argtypes = [_i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp,
                                   _i64, ctypes.c_int, _vp]
+    L.mx_quantize_dual_experts.restype = ctypes.c_int
+    L.mx_quantize_dual_experts.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]
+    L.mx_grouped_k_capacity.restype = _i64
+    L.mx_grouped_k_capacity.argtypes = [_i64, _i64]
+    L.mx_quantize_colwise_grouped.restype = ctypes.c_int
+    L.mx_quantize_colwise_grouped.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64,
+                                              _i64, _vp, _vp]
+    L.mx_grouped_gemm_wgrad.restype = ctypes.c_int
+    L.mx_grouped_gemm_wgrad.argtypes = [_i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
+                                        _vp, _vp, _i64, ctypes.c_int, _vp]
     _lib = L
     return L
 
@@ -356,4 +368,101 @@ def mx_grouped_gemm(group_offsets: torch.Tensor, a_q: torch.Tensor, a_s_swz: tor
                                 _dev(b_s_swz, "b_s_swz", torch.uint8), _dev(c, "c"),
                                 _ld(c, "c"), _OUT[c.dtype], _stream(stream))
     _check("mx_grouped_gemm", st)
+    return c
+
+
+def mx_quantize_dual_experts(w: torch.Tensor, q: Optional[torch.Tensor] = None,
+                             s_swz: Optional[torch.Tensor] = None, qt: Optional[torch.Tensor] = None,
+                             st_swz: Optional[torch.Tensor] = None, stream=None):
+    """Stacked expert weights w [G][N][K] (BF16) -> (q [G][N][K], s_swz, qt [G][K][N],
+    st_swz): each expert quantized row-wise and column-wise in one launch, its
+    rearranged scales back to back (expert g at g * mx_scale_swizzled_bytes of
+    one expert), the layouts mx_grouped_gemm takes for B."""
+    G, N, K = w.shape
+    dev = w.device
+    if not w.is_contiguous():
+        raise ValueError("w must be a contiguous [G][N][K] stack")
+    if q is None:
+        q = torch.empty((G, N, K), dtype=torch.uint8, device=dev)
+    if qt is None:
+        qt = torch.empty((G, K, N), dtype=torch.uint8, device=dev)
+    if s_swz is None:
+        s_swz = torch.empty(G * mx_scale_swizzled_bytes(N, K // 32), dtype=torch.uint8, device=dev)
+    if st_swz is None:
+        st_swz = torch.empty(G * mx_scale_swizzled_bytes(K, N // 32), dtype=torch.uint8, device=dev)
+    q, qt, s_swz, st_swz = _u8(q), _u8(qt), _u8(s_swz), _u8(st_swz)
+    for t, name in ((q, "q"), (qt, "qt")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    st = load().mx_quantize_dual_experts(_dev(w, "w", torch.bfloat16), G, N, K,
+                                         _dev(q, "q", torch.uint8), _dev(s_swz, "s_swz", torch.uint8),
+                                         _dev(qt, "qt", torch.uint8),
+                                         _dev(st_swz, "st_swz", torch.uint8), _stream(stream))
+    _check("mx_quantize_dual_experts", st)
+    return q, s_swz, qt, st_swz
+
+
+def mx_grouped_k_capacity(rows_total: int, num_groups: int) -> int:
+    """Columns that hold every expert's 256-aligned range for any split of the rows."""
+    return load().mx_grouped_k_capacity(rows_total, num_groups)
+
+
+def mx_quantize_colwise_grouped(x: torch.Tensor, group_offsets: torch.Tensor,
+                                k_cap: Optional[int] = None, qt: Optional[torch.Tensor] = None,
+                                st_swz: Optional[torch.Tensor] = None,
+                                pad_offsets: Optional[torch.Tensor] = None, stream=None):
+    """x [rows][cols] BF16, rows sorted by expert -> (qt [cols][k_cap], st_swz,
+    pad_offsets int64 [G+1]): per-expert column-wise quantization into 256-aligned
+    column ranges (see mx_quantize_colwise_grouped in the header)."""
+    rows, cols = x.shape
+    G = group_offsets.numel() - 1
+    if group_offsets.dtype != torch.int64 or G < 1:
+        raise ValueError("group_offsets must be int64 with G+1 entries, G >= 1")
+    if k_cap is None:
+        k_cap = mx_grouped_k_capacity(rows, G)
+    dev = x.device
+    if qt is None:
+        qt = torch.empty((cols, k_cap), dtype=torch.uint8, device=dev)
+    if st_swz is None:
+        st_swz = torch.empty(mx_scale_swizzled_bytes(cols, k_cap // 32), dtype=torch.uint8,
+                             device=dev)
+    if pad_offsets is None:
+        pad_offsets = torch.empty(G + 1, dtype=torch.int64, device=dev)
+    qt, st_swz = _u8(qt), _u8(st_swz)
+    st = load().mx_quantize_colwise_grouped(_dev(x, "x", torch.bfloat16), rows, cols, _ld(x, "x"),
+                                            _dev(group_offsets, "group_offsets", torch.int64), G,
+                                            _dev(pad_offsets, "pad_offsets", torch.int64),
+                                            _dev(qt, "qt", torch.uint8), _ld(qt, "qt"), k_cap,
+                                            _dev(st_swz, "st_swz", torch.uint8), _stream(stream))
+    _check("mx_quantize_colwise_grouped", st)
+    return qt, st_swz, pad_offsets
+
+
+def mx_grouped_gemm_wgrad(k_offsets: torch.Tensor, a_q: torch.Tensor, a_s_swz: torch.Tensor,
+                          b_q: torch.Tensor, b_s_swz: torch.Tensor, c: Optional[torch.Tensor] = None,
+                          out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+    """C [G][M][N]: C_g = A[:, r_g] B[:, r_g]^T over the column ranges
+    r_g = [k_offsets[g], k_offsets[g+1]) (the per-expert weight gradient)."""
+    a_q, b_q = _u8(a_q), _u8(b_q)
+    M, K = a_q.shape
+    N, Kb = b_q.shape
+    if Kb != K:
+        raise ValueError(f"K mismatch: A {tuple(a_q.shape)} B {tuple(b_q.shape)}")
+    G = k_offsets.numel() - 1
+    if k_offsets.dtype != torch.int64 or G < 1:
+        raise ValueError("k_offsets must be int64 with G+1 entries, G >= 1")
+    if c is None:
+        c = torch.empty((G, M, N), dtype=out_dtype, device=a_q.device)
+    if c.dtype not in _OUT:
+        raise ValueError("c must be bfloat16 or float32")
+    if c.dim() != 3 or c.shape[0] != G or c.shape[1] != M or c.stride(2) != 1 or \
+            c.stride(0) != M * c.stride(1):
+        raise ValueError("c must be [G][M][ld_c] with row-major experts back to back")
+    st = load().mx_grouped_gemm_wgrad(G, M, N, K, _dev(k_offsets, "k_offsets", torch.int64),
+                                      _dev(a_q, "a_q", torch.uint8), _ld(a_q, "a_q"),
+                                      _dev(a_s_swz, "a_s_swz", torch.uint8),
+                                      _dev(b_q, "b_q", torch.uint8), _ld(b_q, "b_q"),
+                                      _dev(b_s_swz, "b_s_swz", torch.uint8), _dev(c, "c"),
+                                      c.stride(1), _OUT[c.dtype], _stream(stream))
+    _check("mx_grouped_gemm_wgrad", st)
     return c

@@ -200,7 +200,7 @@ static mx_status check_dual_job(const char *who, const mx_dual_job &j)
 static mx::DualJob to_job(const mx_dual_job &j)
 {
     return mx::DualJob{j.x, j.rows, j.cols, j.ld_x, j.q, j.ld_q, j.s_swz, j.s_tiles,
-                       j.qt, j.ld_qt, j.st_swz, j.st_tiles};
+                       j.qt, j.ld_qt, j.st_swz, j.st_tiles, 1, 0, 0, 0, 0, 0};
 }
 
 mx_status mx_quantize_dual(const void *x, int64_t rows, int64_t cols, int64_t ld_x, void *q,
@@ -253,6 +253,45 @@ mx_status mx_quantize_dual_batch(const mx_dual_job *jobs, int n_jobs, void *stre
     return hip_status(mx::launch_quantize_dual(dj, n, (hipStream_t)stream), fn);
 }
 
+mx_status mx_quantize_dual_experts(const void *x, int64_t num_experts, int64_t rows, int64_t cols,
+                                   void *q, void *s_swz, void *qt, void *st_swz, void *stream)
+{
+    const char *fn = "mx_quantize_dual_experts";
+    if (num_experts < 0)
+        return fail(MX_ERR_INVALID_ARG, "%s: num_experts=%lld < 0", fn, (long long)num_experts);
+    if (num_experts > (1 << 20))
+        return fail(MX_ERR_UNSUPPORTED, "%s: num_experts=%lld too large", fn, (long long)num_experts);
+    // one expert's job: contiguous [rows][cols] in, [rows][cols] and [cols][rows] out
+    const int64_t s_tiles = (cols / 32 + 7) / 8, st_tiles = (rows / 32 + 7) / 8;
+    const mx_dual_job j{x, rows, cols, cols, q, cols, s_swz, s_tiles, qt, rows, st_swz, st_tiles};
+    const mx_status st = check_dual_job(fn, j);
+    if (st != MX_OK)
+        return st;
+    if (num_experts == 0 || rows == 0 || cols == 0)
+        return ok();
+    const int64_t n = rows * cols, sb = swz_bytes(rows, cols / 32), stb = swz_bytes(cols, rows / 32);
+    if (n * num_experts >= ((int64_t)1 << 40))
+        return fail(MX_ERR_UNSUPPORTED, "%s: stack too large", fn);
+    // the whole stacks: the input against every output, the outputs pairwise
+    const void *bufs[5] = {x, q, s_swz, qt, st_swz};
+    const int64_t lens[5] = {2 * n * num_experts, n * num_experts, sb * num_experts, n * num_experts,
+                             stb * num_experts};
+    for (int i = 0; i < 5; i++)
+        for (int k = i + 1; k < 5; k++)
+            if (overlap(bufs[i], lens[i], bufs[k], lens[k]))
+                return fail(MX_ERR_OVERLAP, "%s: buffers %d and %d overlap", fn, i, k);
+    mx::DualJob dj = to_job(j);
+    dj.count = num_experts;
+    dj.x_stride = n;
+    dj.q_stride = n;
+    dj.s_stride = sb;
+    dj.qt_stride = n;
+    dj.st_stride = stb;
+    if (num_experts * ((rows + 255) / 256) * ((cols + 255) / 256 + 7) >= ((int64_t)1 << 31))
+        return fail(MX_ERR_UNSUPPORTED, "%s: too many blocks for one launch", fn);
+    return hip_status(mx::launch_quantize_dual(&dj, 1, (hipStream_t)stream), fn);
+}
+
 mx_status mx_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
                           const int32_t *topk_ids, int64_t topk, int64_t num_experts,
                           int64_t *offsets, int32_t *src_token, int32_t *slot, void *q, int64_t ld_q,
@@ -299,6 +338,57 @@ mx_status mx_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t
     return hip_status(mx::launch_moe_dispatch(x, tokens, hidden, ld_x, topk_ids, topk, num_experts,
                                               offsets, src_token, slot, q, ld_q, s_swz,
                                               (hipStream_t)stream),
+                      fn);
+}
+
+int64_t mx_grouped_k_capacity(int64_t rows_total, int64_t num_groups)
+{
+    if (rows_total < 0 || num_groups < 1)
+        return 0;
+    return (rows_total + 255) / 256 * 256 + 256 * num_groups;
+}
+
+mx_status mx_quantize_colwise_grouped(const void *x, int64_t rows_total, int64_t cols, int64_t ld_x,
+                                      const int64_t *group_offsets, int64_t num_groups,
+                                      int64_t *pad_offsets, void *qt, int64_t ld_qt, int64_t k_cap,
+                                      void *st_swz, void *stream)
+{
+    const char *fn = "mx_quantize_colwise_grouped";
+    if (rows_total < 0 || cols < 1 || num_groups < 1)
+        return fail(MX_ERR_INVALID_ARG, "%s: need rows_total >= 0, cols >= 1, num_groups >= 1", fn);
+    if (num_groups > mx::MOE_MAX_EXPERTS)
+        return fail(MX_ERR_UNSUPPORTED, "%s: num_groups=%lld > %d", fn, (long long)num_groups,
+                    mx::MOE_MAX_EXPERTS);
+    if (cols % 32 != 0)
+        return fail(MX_ERR_SHAPE, "%s: cols=%lld is not a multiple of 32", fn, (long long)cols);
+    if (k_cap % 256 != 0 || k_cap < mx_grouped_k_capacity(rows_total, num_groups))
+        return fail(MX_ERR_INVALID_ARG,
+                    "%s: k_cap=%lld must be a multiple of 256 and at least "
+                    "mx_grouped_k_capacity(rows_total, num_groups) = %lld",
+                    fn, (long long)k_cap, (long long)mx_grouped_k_capacity(rows_total, num_groups));
+    if (ld_x < cols || ld_qt < k_cap)
+        return fail(MX_ERR_INVALID_ARG, "%s: leading dimension too small (ld_x=%lld ld_qt=%lld)", fn,
+                    (long long)ld_x, (long long)ld_qt);
+    if ((!x && rows_total > 0) || !group_offsets || !pad_offsets || !qt || !st_swz)
+        return fail(MX_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!aligned(x, 16) || ld_x % 8 != 0 || !aligned(qt, 16) || ld_qt % 16 != 0 || !aligned(st_swz, 4) ||
+        !aligned(group_offsets, 8) || !aligned(pad_offsets, 8))
+        return fail(MX_ERR_ALIGN,
+                    "%s: x and qt need 16-byte aligned rows (ld_x %% 8, ld_qt %% 16), st_swz 4 bytes, "
+                    "the offsets 8 bytes",
+                    fn);
+    if (k_cap / 256 * ((cols + 255) / 256) >= ((int64_t)1 << 31))
+        return fail(MX_ERR_UNSUPPORTED, "%s: operand too large for this build", fn);
+    const void *bufs[5] = {x, group_offsets, pad_offsets, qt, st_swz};
+    const int64_t lens[5] = {rows_total > 0 ? extent(rows_total, cols, ld_x, 2) : 0, (num_groups + 1) * 8,
+                             (num_groups + 1) * 8, extent(cols, k_cap, ld_qt, 1), swz_bytes(cols, k_cap / 32)};
+    for (int i = 0; i < 5; i++)
+        for (int k = i + 1; k < 5; k++)
+            if ((i >= 2 || k >= 2) && overlap(bufs[i], lens[i], bufs[k], lens[k]))
+                return fail(MX_ERR_OVERLAP, "%s: buffers %d and %d overlap", fn, i, k);
+    return hip_status(mx::launch_quantize_colwise_grouped(x, rows_total, cols, ld_x, group_offsets,
+                                                          num_groups, pad_offsets, qt, ld_qt, k_cap,
+                                                          st_swz, (hipStream_t)stream),
                       fn);
 }
 
@@ -446,6 +536,43 @@ mx_status mx_grouped_gemm(int64_t num_groups, int64_t M_total, int64_t N, int64_
     return hip_status(mx::launch_grouped_gemm(num_groups, M_total, N, K, group_offsets, a_q, ld_a,
                                               a_s_swz, b_q, b_s_swz, c, ld_c, c_dtype,
                                               (hipStream_t)stream),
+                      fn);
+}
+
+mx_status mx_grouped_gemm_wgrad(int64_t num_groups, int64_t M, int64_t N, int64_t k_cap,
+                                const int64_t *k_offsets, const void *a_q, int64_t ld_a,
+                                const void *a_s_swz, const void *b_q, int64_t ld_b,
+                                const void *b_s_swz, void *c, int64_t ld_c, int c_dtype, void *stream)
+{
+    const char *fn = "mx_grouped_gemm_wgrad";
+    if (num_groups < 1)
+        return fail(MX_ERR_INVALID_ARG, "%s: num_groups=%lld < 1", fn, (long long)num_groups);
+    if (num_groups > mx::MOE_MAX_EXPERTS)
+        return fail(MX_ERR_UNSUPPORTED, "%s: num_groups=%lld > %d", fn, (long long)num_groups,
+                    mx::MOE_MAX_EXPERTS);
+    mx_status st = check_gemm_common(fn, M, N, k_cap, a_q, ld_a, a_s_swz, b_q, ld_b, b_s_swz, c, ld_c,
+                                     c_dtype);
+    if (st != MX_OK)
+        return st;
+    if (k_cap % 256 != 0)
+        return fail(MX_ERR_SHAPE, "%s: k_cap=%lld must be a multiple of 256", fn, (long long)k_cap);
+    if (M == 0 || N == 0)
+        return ok();
+    if (!k_offsets)
+        return fail(MX_ERR_INVALID_ARG, "%s: null k_offsets", fn);
+    if (!aligned(k_offsets, 8))
+        return fail(MX_ERR_ALIGN, "%s: k_offsets must be 8-byte aligned", fn);
+    const int64_t ce = c_dtype == MX_BF16 ? 2 : 4;
+    if ((num_groups * M) * ld_c >= ((int64_t)1 << 62) / ce)
+        return fail(MX_ERR_UNSUPPORTED, "%s: C too large", fn);
+    const int64_t ec = extent(num_groups * M, N, ld_c, ce);
+    if (overlap(c, ec, a_q, extent(M, k_cap, ld_a, 1)) || overlap(c, ec, b_q, extent(N, k_cap, ld_b, 1)) ||
+        overlap(c, ec, a_s_swz, swz_bytes(M, k_cap / 32)) || overlap(c, ec, b_s_swz, swz_bytes(N, k_cap / 32)) ||
+        overlap(c, ec, k_offsets, (num_groups + 1) * 8))
+        return fail(MX_ERR_OVERLAP, "%s: C overlaps an input", fn);
+    return hip_status(mx::launch_grouped_gemm_wgrad(num_groups, M, N, k_cap, k_offsets, a_q, ld_a, a_s_swz,
+                                                    b_q, ld_b, b_s_swz, c, ld_c, c_dtype,
+                                                    (hipStream_t)stream),
                       fn);
 }
 

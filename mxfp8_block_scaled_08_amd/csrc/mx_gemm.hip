@@ -162,6 +162,7 @@ __device__ __forceinline__ void lds_ring_barrier()
 // work covers: ns stages from stage kb (both even: whole 256-K groups).
 struct Tile {
     int64_t m0, n0, m_end;
+    int64_t c_row;  // K-grouped: the row of C holding the tile's first row (g * M + m0)
     const uint8_t *b, *bs;  // B operand and its rearranged scales (per expert when grouped)
     int kb, ns;
     int sp;  // split-tail slot (tile * split_s + range), or -1 for a whole tile
@@ -169,19 +170,28 @@ struct Tile {
 
 constexpr int GROUP_TABLE = 1024;  // experts whose tile table fits in LDS
 
+// MODE: 0 dense; 1 grouped along M (rows of A sorted by expert, expert g's
+// rows multiply B_g); 2 grouped along K (the per-expert weight gradient:
+// expert g contracts the K range [offsets[g], offsets[g+1]) of A and B, both
+// 256-aligned, into its own C_g = C + g * M * ld_c).
 // SPLIT: the launch has a split tail (dense, BF16 C only).  A separate
 // instantiation, since carrying that path costs the other launches 1-4 %.
-template <bool GROUPED, int CT, bool SPLIT>
+template <int MODE, int CT, bool SPLIT>
 __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
 {
+    constexpr bool GROUPED = MODE == 1;
+    constexpr bool KGROUPED = MODE == 2;
     __shared__ __attribute__((aligned(1024))) uint8_t sA[2][STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t sB[2][STAGE_BYTES];
     // per wave: the 32-row scale tiles of one 256-K group that hold its A rows
     // (up to five: 2 KiB) and B rows (four: 1 KiB)
     __shared__ __attribute__((aligned(1024))) uint8_t sS[4][3072];
     // grouped: per expert g, its first m-tile number and its clamped row range
-    __shared__ int s_pref[GROUPED ? GROUP_TABLE + 1 : 1];
-    __shared__ int s_lo[GROUPED ? GROUP_TABLE : 1], s_hi[GROUPED ? GROUP_TABLE : 1];
+    // K-grouped: per expert g its stage range [s_lo[g], s_hi[g]), and s_pref[r]
+    // the expert of rank r by decreasing stage count
+    constexpr bool TABLE = GROUPED || KGROUPED;
+    __shared__ int s_pref[TABLE ? GROUP_TABLE + 1 : 1];
+    __shared__ int s_lo[TABLE ? GROUP_TABLE : 1], s_hi[TABLE ? GROUP_TABLE : 1];
     __shared__ int s_wsum[4];
 
     const int tid = threadIdx.x;
@@ -198,7 +208,37 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     // ---- tile enumeration
     const bool table = !GROUPED || (p.G <= GROUP_TABLE && p.M < ((int64_t)1 << 31));
     int64_t ntiles;
-    if (!GROUPED) {
+    if (KGROUPED) {
+        // Stage ranges, clamped so that every expert has at least one 256-K
+        // group inside [0, K) whatever the offsets hold (for offsets that are
+        // 256-aligned and at least 256 apart, as mx_quantize_colwise_grouped
+        // writes them, the clamps change nothing).  An expert with no rows
+        // then contracts its zero padding and writes a zero C_g.
+        const int G = (int)p.G;
+        const int KG = (int)(p.K / 256);
+        for (int g = tid; g < G; g += GM_THREADS) {
+            const int64_t lo = min(max(p.offsets[g], (int64_t)0), p.K);
+            const int64_t hi = min(max(p.offsets[g + 1], lo), p.K);
+            const int glo = min((int)(lo / 256), KG - 1);
+            const int ghi = min(max((int)((hi + 255) / 256), glo + 1), KG);
+            s_lo[g] = 2 * glo;
+            s_hi[g] = 2 * ghi;
+        }
+        __syncthreads();
+        // rank by decreasing stage count (ties by expert number): tiles are
+        // dealt longest first
+        for (int g = tid; g < G; g += GM_THREADS) {
+            const int ns = s_hi[g] - s_lo[g];
+            int rank = 0;
+            for (int h = 0; h < G; h++) {
+                const int nh = s_hi[h] - s_lo[h];
+                rank += (nh > ns || (nh == ns && h < g)) ? 1 : 0;
+            }
+            s_pref[rank] = g;
+        }
+        __syncthreads();
+        ntiles = p.G * p.tiles_m * p.tiles_n;
+    } else if (!GROUPED) {
         ntiles = p.tiles_m * p.tiles_n;
     } else if (table) {
         // each thread takes a contiguous run of experts; block-wide exclusive
@@ -262,7 +302,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     // together on one XCD share A and B panels.
     // A split tail's units are dealt the same way: XCD x takes a contiguous
     // eighth of them, so the K ranges of one tile run on one XCD.
-    const int64_t whole = GROUPED ? ntiles : p.dp_tiles;
+    const int64_t whole = TABLE ? ntiles : p.dp_tiles;
     int64_t t_first, t_step, t_end;
     if (gridDim.x % 8 == 0) {
         const int64_t x = blockIdx.x & 7, per_xcd = (whole + 7) / 8;
@@ -274,7 +314,21 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
         t_step = gridDim.x;
         t_end = whole;
     }
-    const int64_t my_tiles = t_first < t_end ? (t_end - t_first + t_step - 1) / t_step : 0;
+    int64_t my_tiles = t_first < t_end ? (t_end - t_first + t_step - 1) / t_step : 0;
+    // K-grouped: tiles in rank order (an expert's tiles together, longest
+    // experts first) are dealt in rounds of P = gridDim.x, alternately
+    // forwards and backwards, to virtual slots v; slot v runs on workgroup
+    // (v mod P/8) * 8 + v / (P/8), so consecutive slots, which take
+    // neighbouring tiles of one expert, share an XCD and its L2.
+    const int64_t P = gridDim.x;
+    int64_t vslot = blockIdx.x;
+    if (KGROUPED) {
+        if (P % 8 == 0)
+            vslot = (int64_t)(blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3);
+        const int64_t full = ntiles / P, rem = ntiles - full * P;
+        const int64_t pos_last = (full & 1) ? P - 1 - vslot : vslot;
+        my_tiles = full + (pos_last < rem ? 1 : 0);
+    }
     int split_u = -1;  // this workgroup's split-tail unit
     if (SPLIT) {
         const int64_t u = gridDim.x % 8 == 0 ? (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3)
@@ -291,6 +345,26 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     int g_cur = 0;  // grouped: experts are met in increasing order
     auto coords = [&](int64_t pid) -> Tile {
         Tile c;
+        if (KGROUPED) {
+            const int64_t per_expert = p.tiles_m * p.tiles_n;
+            const int64_t r = pid / per_expert;
+            const int g = __builtin_amdgcn_readfirstlane(s_pref[r]);
+            const int64_t t = pid - r * per_expert;
+            const int64_t per_group = GROUP_M * p.tiles_n;
+            const int64_t grp = t / per_group;
+            const int64_t first_m = grp * GROUP_M;
+            const int64_t gm = min(p.tiles_m - first_m, (int64_t)GROUP_M);
+            const int64_t in = t - grp * per_group;
+            c.m0 = (first_m + in % gm) * BM;
+            c.n0 = (in / gm) * BN;
+            c.m_end = p.M;
+            c.c_row = (int64_t)g * p.M + c.m0;
+            c.b = p.b;
+            c.bs = p.bs;
+            c.kb = __builtin_amdgcn_readfirstlane(s_lo[g]);
+            c.ns = __builtin_amdgcn_readfirstlane(s_hi[g]) - c.kb;
+            return c;
+        }
         if (!GROUPED) {
             const int64_t per_group = GROUP_M * p.tiles_n;
             const int64_t grp = pid / per_group;
@@ -373,6 +447,12 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             c.kb = 2 * g0;
             c.ns = 2 * (g1 - g0);
             c.sp = split_u;
+            return c;
+        }
+        if (KGROUPED) {
+            const int64_t pos = (k & 1) ? P - 1 - vslot : vslot;
+            Tile c = coords(k * P + pos);
+            c.sp = -1;
             return c;
         }
         Tile c = coords(t_first + (k - has_split) * t_step);
@@ -533,7 +613,12 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     // ---- the workgroup's stages: its units' stages numbered continuously,
     // so the pipeline runs across units
     Tile cur = unit(0);
-    const int64_t total = (my_units - has_split) * KITP + (has_split ? cur.ns : 0);
+    int64_t total = (my_units - has_split) * KITP + (has_split ? cur.ns : 0);
+    if (KGROUPED) {
+        total = 0;
+        for (int64_t k = 0; k < my_units; k++)
+            total += unit(k).ns;
+    }
     uint32_t cur_srd = scale_lanes(cur);
 
     // prologue: scale words of the first group, stages 0 and 1 in flight
@@ -765,8 +850,9 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             // element; the range ends after the tile's last valid row, so the
             // stores of rows past it (past M, or past the expert) are dropped
             const uint32_t rows_valid = (uint32_t)min(cur.m_end - cur.m0, (int64_t)BM);
+            const int64_t c_row = KGROUPED ? cur.c_row : cur.m0;
             const __amdgpu_buffer_rsrc_t rc =
-                byte_range((const uint8_t *)p.c + (cur.m0 * p.ld_c + cur.n0) * CE,
+                byte_range((const uint8_t *)p.c + (c_row * p.ld_c + cur.n0) * CE,
                            rows_valid * (uint32_t)(p.ld_c * CE));
             if (CT == 0) {
 #pragma unroll
@@ -808,6 +894,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
 #pragma unroll
                 for (int j = 0; j < TM; j++) {
                     const int64_t m = cur.m0 + wm * 128 + j * 32 + r32;
+                    const int64_t mc = m + (KGROUPED ? cur.c_row - cur.m0 : 0);  // row of C
                     if (m < cur.m_end) {
 #pragma unroll
                         for (int q = 0; q < 4; q++) {
@@ -815,7 +902,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                             const float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
                             const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
                             if (CT == 0) {
-                                uint16_t *crow = reinterpret_cast<uint16_t *>(p.c) + m * p.ld_c;
+                                uint16_t *crow = reinterpret_cast<uint16_t *>(p.c) + mc * p.ld_c;
                                 const uint32_t w0 = pack_bf16x2(v0, v1), w1 = pack_bf16x2(v2, v3);
                                 if (p.vec_store && n + 3 < N) {
                                     *reinterpret_cast<uint2 *>(crow + n) = make_uint2(w0, w1);
@@ -826,7 +913,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                                     if (n + 3 < N) crow[n + 3] = (uint16_t)(w1 >> 16);
                                 }
                             } else {
-                                float *crow = reinterpret_cast<float *>(p.c) + m * p.ld_c;
+                                float *crow = reinterpret_cast<float *>(p.c) + mc * p.ld_c;
                                 if (p.vec_store && n + 3 < N) {
                                     *reinterpret_cast<float4 *>(crow + n) = make_float4(v0, v1, v2, v3);
                                 } else {
@@ -1016,11 +1103,11 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t
         }
     }
     if (ws != nullptr)
-        hipLaunchKernelGGL((mx_gemm_kernel<false, 0, true>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
+        hipLaunchKernelGGL((mx_gemm_kernel<0, 0, true>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
     else if (c_dtype == 0)
-        hipLaunchKernelGGL((mx_gemm_kernel<false, 0, false>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
+        hipLaunchKernelGGL((mx_gemm_kernel<0, 0, false>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
     else
-        hipLaunchKernelGGL((mx_gemm_kernel<false, 1, false>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
+        hipLaunchKernelGGL((mx_gemm_kernel<0, 1, false>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
     hipError_t err = hipGetLastError();
     if (ws != nullptr) {
         if (err == hipSuccess) {
@@ -1065,9 +1152,44 @@ hipError_t launch_grouped_gemm(int64_t G, int64_t M_total, int64_t N, int64_t K,
     // each walking the tiles the kernel enumerates
     const unsigned grid = (unsigned)cu_count();
     if (c_dtype == 0)
-        hipLaunchKernelGGL((mx_gemm_kernel<true, 0, false>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
+        hipLaunchKernelGGL((mx_gemm_kernel<1, 0, false>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
     else
-        hipLaunchKernelGGL((mx_gemm_kernel<true, 1, false>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
+        hipLaunchKernelGGL((mx_gemm_kernel<1, 1, false>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_wgrad(int64_t G, int64_t M, int64_t N, int64_t K,
+                                     const int64_t *k_offsets, const void *a_q, int64_t ld_a,
+                                     const void *a_s, const void *b_q, int64_t ld_b,
+                                     const void *b_s, void *c, int64_t ld_c, int c_dtype,
+                                     hipStream_t stream)
+{
+    GemmParams p{};
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.a = (const uint8_t *)a_q;
+    p.ld_a = ld_a;
+    p.as = (const uint8_t *)a_s;
+    p.b = (const uint8_t *)b_q;
+    p.ld_b = ld_b;
+    p.bs = (const uint8_t *)b_s;
+    p.c = c;
+    p.ld_c = ld_c;
+    p.offsets = k_offsets;
+    p.G = G;
+    p.tiles_m = (M + BM - 1) / BM;
+    p.tiles_n = (N + BN - 1) / BN;
+    p.as_bytes = (uint32_t)scale_bytes(M, K);
+    p.bs_bytes = (uint32_t)scale_bytes(N, K);
+    p.vec_store = vec_ok(c, ld_c, c_dtype);
+    p.vec16 = vec16_ok(c, ld_c, c_dtype);
+    const int64_t tiles = G * p.tiles_m * p.tiles_n;
+    const unsigned grid = (unsigned)std::min<int64_t>(tiles, cu_count());
+    if (c_dtype == 0)
+        hipLaunchKernelGGL((mx_gemm_kernel<2, 0, false>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
+    else
+        hipLaunchKernelGGL((mx_gemm_kernel<2, 1, false>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
     return hipGetLastError();
 }
 

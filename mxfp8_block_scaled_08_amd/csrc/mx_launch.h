@@ -30,6 +30,10 @@ struct DualJob {
     int64_t ld_qt;
     void *st_swz;
     int64_t st_tiles;
+    // count tensors of this shape, tensor i at x + i * x_stride elements and
+    // its outputs at the given byte strides (stacked expert weights)
+    int64_t count;
+    int64_t x_stride, q_stride, s_stride, qt_stride, st_stride;
 };
 constexpr int QD_MAX_JOBS = 16;
 
@@ -66,5 +70,23 @@ hipError_t launch_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, in
 hipError_t launch_moe_combine(const void *y, int64_t tokens, int64_t hidden, int64_t ld_y,
                               const int32_t *slot, const float *weights, int64_t topk, void *out,
                               int64_t ld_out, hipStream_t stream);
+
+// Per-expert column-wise quantization into 256-aligned column ranges (the
+// MoE weight gradient's operands): the ranges' start offsets into pad, then
+// the codes and rearranged scales.  G <= MOE_MAX_EXPERTS, cols % 32 == 0,
+// k_cap % 256 == 0 and at least the capacity for rows and G.
+hipError_t launch_quantize_colwise_grouped(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                                          const int64_t *offsets, int64_t G, int64_t *pad,
+                                          void *qt, int64_t ld_qt, int64_t k_cap, void *st_swz,
+                                          hipStream_t stream);
+
+// Per-expert product along K: C_g = A[:, r_g] . B[:, r_g]^T for the column
+// ranges r_g = [k_offsets[g], k_offsets[g+1]), C_g at c + g * M * ld_c.
+// K % 256 == 0, G <= MOE_MAX_EXPERTS.
+hipError_t launch_grouped_gemm_wgrad(int64_t G, int64_t M, int64_t N, int64_t K,
+                                     const int64_t *k_offsets, const void *a_q, int64_t ld_a,
+                                     const void *a_s, const void *b_q, int64_t ld_b,
+                                     const void *b_s, void *c, int64_t ld_c, int c_dtype,
+                                     hipStream_t stream);
 
 }  // namespace mx

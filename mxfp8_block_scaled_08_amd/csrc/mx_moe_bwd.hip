@@ -1,0 +1,183 @@
+// Per-expert column-wise quantization for the MoE weight gradient (gfx950).
+//
+// The update_actor stage of the MoE learner in "End-to-End MXFP8
+// Reinforcement Learning on Blackwell" (Table 8; Table 2 for Qwen3-30B-A3B,
+// 128 experts, top-8) needs each expert's weight gradient dW_g = dY_g^T X_g:
+// a contraction over that expert's token rows only.  Its operands are the
+// column-wise quantized dY and X, and a 32-row block must not hold rows of two
+// experts.  Layout: expert g's rows [offsets[g], offsets[g+1]) become columns
+// [pad[g], pad[g+1]) of the transposed operand, each range max(256, m_g
+// rounded up to 256) columns long so that every range is a whole number of
+// the GEMM's 256-K scale groups; the columns past an expert's rows hold zero
+// codes (zero rows appended: they leave every block maximum unchanged) and
+// the blocks made only of them get scale code 0.
+//
+// pad_offsets_kernel: one workgroup, thread g takes expert g; a block-wide
+// scan of the range lengths.  The offsets are clamped into [0, rows] and made
+// nondecreasing first, and the results at k_cap, so any offsets give
+// in-bounds ranges.
+//
+// quantize_colwise_grouped_kernel: a 512-thread workgroup takes 256 columns
+// of the padded operand (one expert's, since every range is 256-aligned) by
+// 256 of x's columns, as 2 x 4 waves of 128 padded rows x 64 columns: the
+// column-wise lane layout of the dual quantizer (lane = 32-row block, half,
+// 8-column group; 16 rows x 8 columns per lane; the halves of a block meet
+// through one DPP rotation; v_perm pairs two rows of a column for the scaled
+// conversion).  A lane loads only the rows that exist in its expert (the
+// others are zero) and stores 16 codes of each of its 8 columns.  The scale
+// bytes go to LDS at their rearranged positions, and each thread stores one
+// word: 8 whole 256-byte tiles of the rearranged layout per workgroup.
+#include "mx_device.h"
+#include "mx_launch.h"
+
+namespace mx {
+
+constexpr int QG_THREADS = 512;
+constexpr int QG_TILE = 256;
+
+__global__ __launch_bounds__(MOE_MAX_EXPERTS) void pad_offsets_kernel(const int64_t *__restrict__ offsets,
+                                                                      int G, int64_t rows, int64_t k_cap,
+                                                                      int64_t *__restrict__ pad)
+{
+    __shared__ int64_t wsum[MOE_MAX_EXPERTS / 64];
+    const int g = threadIdx.x, lane = g & 63, wave = g >> 6;
+    int64_t len = 0;
+    if (g < G) {
+        const int64_t lo = min(max(offsets[g], (int64_t)0), rows);
+        const int64_t hi = min(max(offsets[g + 1], lo), rows);
+        len = max((int64_t)QG_TILE, (hi - lo + QG_TILE - 1) / QG_TILE * QG_TILE);
+    }
+    int64_t incl = len;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int64_t o = __shfl_up(incl, d, 64);
+        if (lane >= d)
+            incl += o;
+    }
+    if (lane == 63)
+        wsum[wave] = incl;
+    __syncthreads();
+    int64_t base = 0;
+    for (int w = 0; w < wave; w++)
+        base += wsum[w];
+    if (g < G)
+        pad[g] = min(base + incl - len, k_cap);
+    if (g == G - 1)
+        pad[G] = min(base + incl, k_cap);
+}
+
+__global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
+    const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
+    const int64_t *__restrict__ offsets, const int64_t *__restrict__ pad, int G,
+    uint8_t *__restrict__ qt, int64_t ld_qt, uint8_t *__restrict__ st_swz, int64_t st_tiles,
+    int64_t tiles_c)
+{
+    __shared__ uint32_t lds_st[8 * 64];
+    const int64_t tr = blockIdx.x / tiles_c, tc = blockIdx.x - tr * tiles_c;
+    const int64_t P0 = tr * QG_TILE;  // first padded column (row of the padded operand)
+    if (P0 >= pad[G])
+        return;  // past the last expert's range: nothing to write
+    // the expert whose range holds P0: the last g with pad[g] <= P0
+    int lo = 0, hi = G;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pad[mid] <= P0)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    const int g = lo;
+    const int64_t glo = min(max(offsets[g], (int64_t)0), rows);
+    const int64_t ghi = min(max(offsets[g + 1], glo), rows);
+    const int64_t src0 = glo + (P0 - pad[g]);
+    const int valid = (int)min(max(ghi - src0, (int64_t)0), (int64_t)QG_TILE);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wr = wave >> 2, wc = wave & 3;
+    const int cg = lane & 7, half = (lane >> 3) & 1, rb = lane >> 4;
+    const int64_t C0 = tc * QG_TILE;
+    const int64_t c0 = C0 + wc * 64 + cg * 8;
+    const int rl0 = wr * 128 + rb * 32 + half * 16;  // the lane's first row within the tile
+    // cols % 32 == 0: a lane's 8 columns are all in range or all out, and so
+    // are those of its DPP partner (the other half of its block)
+    const bool active = c0 < cols;
+    lds_st[tid] = 0x7F7F7F7Fu;
+    uint4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        if (active && rl0 + i < valid)
+            v[i] = *reinterpret_cast<const uint4 *>(x + (src0 + rl0 + i) * ld_x + c0);
+        else
+            v[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    uint32_t m[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        m[0] = pk_max_u16(m[0], mag2(v[i].x));
+        m[1] = pk_max_u16(m[1], mag2(v[i].y));
+        m[2] = pk_max_u16(m[2], mag2(v[i].z));
+        m[3] = pk_max_u16(m[3], mag2(v[i].w));
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k++)  // row_ror:8 - the other half of the column block
+        m[k] = pk_max_u16(m[k], (uint32_t)__builtin_amdgcn_mov_dpp((int)m[k], 0x128, 0xF, 0xF, false));
+    __syncthreads();  // the 0x7F fill precedes every scale byte
+    uint8_t *bst = reinterpret_cast<uint8_t *>(lds_st);
+    if (active) {
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const uint32_t c = scale_code((m[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+            const float sc = cvt_scale(c);
+            // bytes 0,1 (column j even) or 2,3 (odd) of the row pair's words
+            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+            uint32_t o[4];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const uint4 &a = v[4 * k], &b = v[4 * k + 1], &cc = v[4 * k + 2], &d = v[4 * k + 3];
+                const int wi = j >> 1;
+                const uint32_t wa = wi == 0 ? a.x : wi == 1 ? a.y : wi == 2 ? a.z : a.w;
+                const uint32_t wb = wi == 0 ? b.x : wi == 1 ? b.y : wi == 2 ? b.z : b.w;
+                const uint32_t wcw = wi == 0 ? cc.x : wi == 1 ? cc.y : wi == 2 ? cc.z : cc.w;
+                const uint32_t wd = wi == 0 ? d.x : wi == 1 ? d.y : wi == 2 ? d.z : d.w;
+                const uint32_t p01 = __builtin_amdgcn_perm(wb, wa, sel);   // rows 4k, 4k+1
+                const uint32_t p23 = __builtin_amdgcn_perm(wd, wcw, sel);  // rows 4k+2, 4k+3
+                o[k] = nan_block_select(cvt_x4(p01, p23, sc), c);
+            }
+            *reinterpret_cast<uint4 *>(qt + (c0 + j) * ld_qt + P0 + rl0) = make_uint4(o[0], o[1], o[2], o[3]);
+            if (half == 0) {
+                // rearranged row = column wc*64 + cg*8 + j of the tile, block wr*4 + rb
+                const int col = wc * 64 + cg * 8 + j, blk = wr * 4 + rb;
+                bst[(col >> 5) * 256 + (32 * (blk & 1) + (col & 31)) * 4 + (blk >> 1)] = (uint8_t)c;
+            }
+        }
+    }
+    __syncthreads();
+    // thread -> word tid & 63 of the rearranged tile of 32-column row tid >> 6
+    const int t = tid >> 6, w = tid & 63;
+    if (C0 + 32 * t < cols)
+        reinterpret_cast<uint32_t *>(st_swz + ((C0 / 32 + t) * st_tiles + tr) * 256)[w] = lds_st[tid];
+}
+
+hipError_t launch_quantize_colwise_grouped(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                                          const int64_t *offsets, int64_t G, int64_t *pad,
+                                          void *qt, int64_t ld_qt, int64_t k_cap, void *st_swz,
+                                          hipStream_t stream)
+{
+    hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, stream, offsets, (int)G,
+                       rows, k_cap, pad);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    const int64_t tiles_c = (cols + QG_TILE - 1) / QG_TILE;
+    const int64_t tiles_r = k_cap / QG_TILE;
+    const int64_t blocks = tiles_r * tiles_c;
+    if (blocks == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(quantize_colwise_grouped_kernel, dim3((unsigned)blocks), dim3(QG_THREADS), 0, stream,
+                       (const uint16_t *)x, rows, cols, ld_x, offsets, (const int64_t *)pad, (int)G,
+                       (uint8_t *)qt, ld_qt, (uint8_t *)st_swz, k_cap / QG_TILE, tiles_c);
+    return hipGetLastError();
+}
+
+}  // namespace mx

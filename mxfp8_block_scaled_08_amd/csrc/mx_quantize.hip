@@ -206,8 +206,10 @@ constexpr int QD_THREADS = 512;
 constexpr int QD_TILE = 256;
 
 // Several tensors in one launch (a layer's weights): job j takes blocks
-// first[j] .. first[j+1] - 1, each job's count a multiple of 8 when it uses
-// the per-XCD order, so a block's XCD is still its number mod 8.
+// first[j] .. first[j+1] - 1, each tensor's count a multiple of 8 when it uses
+// the per-XCD order, so a block's XCD is still its number mod 8.  A job may
+// stand for several tensors of one shape at fixed strides (stacked expert
+// weights): tensor i takes the i-th equal run of the job's blocks.
 struct DualBatch {
     DualJob job[QD_MAX_JOBS];
     int64_t first[QD_MAX_JOBS + 1];
@@ -222,15 +224,19 @@ __global__ __launch_bounds__(QD_THREADS) void quantize_dual_kernel(DualBatch B)
     while (jb + 1 < B.n && (int64_t)blockIdx.x >= B.first[jb + 1])
         jb++;
     const DualJob &J = B.job[jb];
-    const uint16_t *__restrict__ x = (const uint16_t *)J.x;
+    // a job of count tensors takes count equal runs of nb blocks
+    const int64_t nb = (B.first[jb + 1] - B.first[jb]) / J.count;
+    int64_t b = (int64_t)blockIdx.x - B.first[jb];
+    const int64_t item = b / nb;
+    b -= item * nb;
+    const uint16_t *__restrict__ x = (const uint16_t *)J.x + item * J.x_stride;
     const int64_t rows = J.rows, cols = J.cols, ld_x = J.ld_x;
-    uint8_t *__restrict__ q = (uint8_t *)J.q;
-    uint8_t *__restrict__ s_swz = (uint8_t *)J.s_swz;
-    uint8_t *__restrict__ qt = (uint8_t *)J.qt;
-    uint8_t *__restrict__ st_swz = (uint8_t *)J.st_swz;
+    uint8_t *__restrict__ q = (uint8_t *)J.q + item * J.q_stride;
+    uint8_t *__restrict__ s_swz = (uint8_t *)J.s_swz + item * J.s_stride;
+    uint8_t *__restrict__ qt = (uint8_t *)J.qt + item * J.qt_stride;
+    uint8_t *__restrict__ st_swz = (uint8_t *)J.st_swz + item * J.st_stride;
     const int64_t ld_q = J.ld_q, s_tiles = J.s_tiles, ld_qt = J.ld_qt, st_tiles = J.st_tiles;
     const int64_t tiles_r = (rows + QD_TILE - 1) / QD_TILE, tiles_c = (cols + QD_TILE - 1) / QD_TILE;
-    const int64_t b = (int64_t)blockIdx.x - B.first[jb], nb = B.first[jb + 1] - B.first[jb];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 2, wc = wave & 3;
@@ -449,7 +455,7 @@ hipError_t launch_quantize_dual(const DualJob *jobs, int n, hipStream_t stream)
         int64_t nb = tiles_r * tiles_c;
         if (tiles_c >= QC_WIDE)
             nb = (nb + 7) / 8 * 8;
-        blocks += nb;
+        blocks += nb * jobs[j].count;
     }
     B.first[n] = blocks;
     if (blocks == 0)

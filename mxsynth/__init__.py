@@ -214,12 +214,24 @@ def moe_inputs(seed: int = 5000, device="cpu"):
     return rows, a_gu, a_dn, w_gu, w_dn
 
 
+def moe_bwd_grads(seed: int = 5200, device="cpu"):
+    """Gradients of the Qwen3-30B-A3B MoE layer's expert outputs, rows sorted by
+    expert like moe_inputs: dY_gu[163840x1536] (gate_up output) and
+    dY_dn[163840x2048] (down output), BF16 N(0, 1e-3) like the dense backward."""
+    m = int(zipf_expert_rows(MOE_TOKENS, MOE_EXPERTS, MOE_TOPK, 1.1).sum())
+    dy_gu = normal_bf16((m, 2 * MOE_FFN), 1e-3, seed, device=device)
+    dy_dn = normal_bf16((m, MOE_HIDDEN), 1e-3, seed + 1, device=device)
+    return dy_gu, dy_dn
+
+
 WORKLOADS = {
     "tiny": "A[128x256] row-wise, B[256x256] column-wise, mx_gemm 128x256x256 BF16 out",
     "weight_sync": "row-wise + column-wise MXFP8 + scale rearrangement of one Qwen3-8B layer",
     "dense_fwd": "Qwen3-8B linears at M=4608: qkv, o, gate_up, down",
     "dense_bwd": "Qwen3-8B gate_up dgrad (12288x4096x24576) and wgrad (24576x4096x12288)",
     "moe": "Qwen3-30B-A3B grouped gate_up/down, 128 experts, top-8, Zipf(1.1) loads",
+    "moe_bwd": "Qwen3-30B-A3B expert backward: per-expert dgrad (grouped over rows) and "
+               "wgrad (grouped over each expert's token range) of gate_up and down",
 }
 
 

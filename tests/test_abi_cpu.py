@@ -38,7 +38,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for n in names:
         assert hasattr(raw, n), f"{n} declared in include/mxfp8.h but not exported"
         assert hasattr(mx, n), f"{n} has no Python binding of the same name"
-    assert L.mx_abi_version() == 2
+    assert L.mx_abi_version() == 3
 
 
 def test_status_strings():
@@ -213,3 +213,79 @@ def test_python_binding_fails_loudly_without_device_tensors():
     with pytest.raises(ValueError):
         mx.mx_quantize_rowwise(x, q=torch.zeros(4, 64, dtype=torch.uint8),
                                s=torch.zeros(4, 2, dtype=torch.uint8), stream=0)
+
+
+def test_grouped_k_capacity():
+    L = mx.load()
+    assert L.mx_grouped_k_capacity(163840, 128) == 163840 + 256 * 128
+    assert L.mx_grouped_k_capacity(1, 1) == 512
+    assert L.mx_grouped_k_capacity(0, 3) == 768
+    assert L.mx_grouped_k_capacity(-1, 3) == 0 and L.mx_grouped_k_capacity(5, 0) == 0
+
+
+def test_quantize_colwise_grouped_validation():
+    L = mx.load()
+    f = L.mx_quantize_colwise_grouped
+    cap = L.mx_grouped_k_capacity(1000, 4)           # 1024 + 1024
+    # x, offsets, pad, qt, st_swz
+    args = lambda **kw: [kw.get("x", FAKE), kw.get("rows", 1000), kw.get("cols", 64),
+                         kw.get("ld_x", 64), kw.get("off", FAKE2), kw.get("G", 4),
+                         kw.get("pad", FAKE2 + 4096), kw.get("qt", FAKE3), kw.get("ld_qt", cap),
+                         kw.get("k_cap", cap), kw.get("st", FAKE4), STREAM]
+    assert f(*args(cols=48)) == mx.MX_ERR_SHAPE
+    assert f(*args(G=0)) == mx.MX_ERR_INVALID_ARG
+    assert f(*args(G=1025)) == mx.MX_ERR_UNSUPPORTED
+    assert f(*args(k_cap=cap - 256, ld_qt=cap)) == mx.MX_ERR_INVALID_ARG
+    assert "mx_grouped_k_capacity" in _err(L)
+    assert f(*args(k_cap=cap + 32, ld_qt=cap + 32)) == mx.MX_ERR_INVALID_ARG
+    assert f(*args(ld_qt=cap - 16)) == mx.MX_ERR_INVALID_ARG
+    assert f(*args(ld_x=32)) == mx.MX_ERR_INVALID_ARG
+    assert f(*args(pad=0)) == mx.MX_ERR_INVALID_ARG
+    assert f(*args(x=FAKE + 2)) == mx.MX_ERR_ALIGN
+    assert f(*args(ld_qt=cap + 8)) == mx.MX_ERR_ALIGN
+    assert f(*args(pad=FAKE2 + 4100)) == mx.MX_ERR_ALIGN
+    # the padded offsets written over the group offsets; scales inside the codes
+    assert f(*args(pad=FAKE2 + 8)) == mx.MX_ERR_OVERLAP
+    assert f(*args(st=FAKE3 + 64)) == mx.MX_ERR_OVERLAP
+
+
+def test_grouped_gemm_wgrad_validation():
+    L = mx.load()
+    f = L.mx_grouped_gemm_wgrad
+    # G, M, N, k_cap, k_offsets, a_q, ld_a, a_s, b_q, ld_b, b_s, c, ld_c, dtype
+    args = lambda **kw: [kw.get("G", 4), kw.get("M", 256), kw.get("N", 128), kw.get("K", 2048),
+                         kw.get("off", FAKE), kw.get("a", FAKE2), kw.get("ld_a", 2048),
+                         kw.get("a_s", FAKE2 + (1 << 24)), kw.get("b", FAKE3),
+                         kw.get("ld_b", 2048), kw.get("b_s", FAKE3 + (1 << 24)),
+                         kw.get("c", FAKE4), kw.get("ld_c", 128), kw.get("dt", mx.MX_BF16), STREAM]
+    assert f(*args(G=0)) == mx.MX_ERR_INVALID_ARG
+    assert f(*args(G=2000)) == mx.MX_ERR_UNSUPPORTED
+    assert f(*args(K=2048 + 128, ld_a=2304, ld_b=2304)) == mx.MX_ERR_SHAPE
+    assert "multiple of 256" in _err(L)
+    assert f(*args(K=2000)) == mx.MX_ERR_SHAPE
+    assert f(*args(off=0)) == mx.MX_ERR_INVALID_ARG
+    assert f(*args(off=FAKE + 4)) == mx.MX_ERR_ALIGN
+    assert f(*args(ld_c=100)) == mx.MX_ERR_INVALID_ARG
+    assert f(*args(dt=7)) == mx.MX_ERR_INVALID_ARG
+    # C over A's codes
+    assert f(*args(c=FAKE2 + 4096)) == mx.MX_ERR_OVERLAP
+    # C (4 experts x 256 rows) reaching the offsets
+    assert f(*args(off=FAKE4 + 1000)) == mx.MX_ERR_OVERLAP
+    # empty products succeed without a launch
+    assert f(*args(M=0)) == mx.MX_OK
+
+
+def test_quantize_dual_experts_validation():
+    L = mx.load()
+    f = L.mx_quantize_dual_experts
+    # x, G, rows, cols, q, s_swz, qt, st_swz
+    assert f(FAKE, -1, 64, 64, FAKE2, FAKE3, FAKE4, FAKE4 + (1 << 20), STREAM) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE, 4, 48, 64, FAKE2, FAKE3, FAKE4, FAKE4 + (1 << 20), STREAM) == mx.MX_ERR_SHAPE
+    assert f(FAKE + 8, 4, 64, 64, FAKE2, FAKE3, FAKE4, FAKE4 + (1 << 20), STREAM) == mx.MX_ERR_ALIGN
+    assert f(FAKE, 4, 64, 64, FAKE2, FAKE3 + 2, FAKE4, FAKE4 + (1 << 20), STREAM) == mx.MX_ERR_ALIGN
+    assert f(0, 4, 64, 64, FAKE2, FAKE3, FAKE4, FAKE4 + (1 << 20), STREAM) == mx.MX_ERR_INVALID_ARG
+    # the fourth expert's codes (64x64 each) run into s_swz placed 3 experts after q
+    assert f(FAKE, 4, 64, 64, FAKE2, FAKE2 + 3 * 4096, FAKE4, FAKE4 + (1 << 20), STREAM) == mx.MX_ERR_OVERLAP
+    # qt stack over the input stack (4 x 64 x 64 BF16 = 32 KiB)
+    assert f(FAKE, 4, 64, 64, FAKE2, FAKE3, FAKE + 30000, FAKE4 + (1 << 20), STREAM) == mx.MX_ERR_OVERLAP
+    assert f(FAKE, 0, 64, 64, FAKE2, FAKE3, FAKE4, FAKE4 + (1 << 20), STREAM) == mx.MX_OK

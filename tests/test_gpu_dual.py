@@ -139,3 +139,23 @@ def test_dual_batch_matches_oracle(gpu_lib):
                               _ref(np.concatenate([X["g"], X["u"]], 0)),
                               ("q", "s_swz", "qt", "st_swz")):
         _eq(got, ref, f"batch stacked {name}")
+
+
+@pytest.mark.parametrize("G,rows,cols", [(1, 32, 32), (5, 96, 64), (3, 288, 320), (2, 256, 8224),
+                                         (17, 1536, 256)])
+def test_dual_experts_matches_oracle(gpu_lib, G, rows, cols):
+    """Stacked expert weights in one launch: every expert's four outputs equal
+    the oracle's, at the expert's place in each stack."""
+    mx = gpu_lib
+    w = mxsynth.normal_bf16((G, rows, cols), 0.02, seed=900 + G, outlier_frac=0.001)
+    q, s_swz, qt, st_swz = mx.mx_quantize_dual_experts(w.cuda())
+    torch.cuda.synchronize()
+    sb = mx.mx_scale_swizzled_bytes(rows, cols // 32)
+    stb = mx.mx_scale_swizzled_bytes(cols, rows // 32)
+    assert s_swz.numel() == G * sb and st_swz.numel() == G * stb
+    for g in range(G):
+        oq, os_swz, oqt, ost_swz = _ref(mxsynth.bits(w[g]))
+        _eq(q[g], oq, f"expert {g} q")
+        _eq(s_swz[g * sb:(g + 1) * sb], os_swz, f"expert {g} s_swz")
+        _eq(qt[g], oqt, f"expert {g} qt")
+        _eq(st_swz[g * stb:(g + 1) * stb], ost_swz, f"expert {g} st_swz")

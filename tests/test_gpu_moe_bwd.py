@@ -1,0 +1,235 @@
+"""GPU parity of the MoE backward products against the oracle.
+
+The expert weight gradient dW_g = dY_g^T X_g ("End-to-End MXFP8 Reinforcement
+Learning on Blackwell", Table 8: update_actor; Table 2: Qwen3-30B-A3B, 128
+experts, top-8) runs as mx_quantize_colwise_grouped of dY and X (per-expert
+column-wise blocks in 256-aligned column ranges) followed by
+mx_grouped_gemm_wgrad; the data gradient dX = dY . W_g per expert is
+mx_grouped_gemm with the column-wise expert weights of
+mx_quantize_dual_experts.  Quantized bytes are compared bit for bit; GEMM
+outputs against the oracle's double-precision entries within the derived
+tolerance of tests/gpu_util.py (FP32 accumulation bar plus the matrix cores'
+8-product window term, plus one BF16 ulp for BF16 output).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mxsynth
+import oracle
+from gpu_util import (GemmRef, _pool_map, assert_gemm_close, check_sampled_grouped,
+                      oracle_colwise_par, window_bound_full, window_bound_pairs)
+
+pytestmark = pytest.mark.gpu
+
+
+def _offsets(sizes):
+    return np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+
+
+def _grouped_oracle_par(xb, off, k_cap, chunk=256):
+    """oracle.quantize_colwise_grouped split over column chunks (threads)."""
+    cols = xb.shape[1]
+    parts = _pool_map(lambda c0: oracle.quantize_colwise_grouped(
+        np.ascontiguousarray(xb[:, c0:c0 + chunk]), off, k_cap), range(0, cols, chunk))
+    return (np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]),
+            parts[0][2])
+
+
+def _check_grouped_quant(mx, x, off, what, sentinel=True):
+    """Run the grouped quantizer on x (CPU BF16) and compare with the oracle:
+    pad offsets, codes up to pad[G], rearranged scale tiles up to pad[G], and
+    (sentinel) nothing written past pad[G].  Returns GPU and oracle outputs."""
+    rows, cols = x.shape
+    G = len(off) - 1
+    k_cap = mx.mx_grouped_k_capacity(rows, G)
+    xb = mxsynth.bits(x)
+    oqt, ost, opad = _grouped_oracle_par(xb, off, k_cap)
+    qt = torch.full((cols, k_cap), 0xAB, dtype=torch.uint8, device="cuda")
+    st_swz = torch.full((mx.mx_scale_swizzled_bytes(cols, k_cap // 32),), 0xCD, dtype=torch.uint8,
+                        device="cuda")
+    _, _, pad = mx.mx_quantize_colwise_grouped(x.cuda(), torch.from_numpy(off).cuda(), k_cap=k_cap,
+                                               qt=qt, st_swz=st_swz)
+    torch.cuda.synchronize()
+    pad_h = pad.cpu().numpy()
+    assert np.array_equal(pad_h, opad), f"{what}: pad offsets {pad_h} vs {opad}"
+    pend = int(opad[-1])
+    g = qt.cpu().numpy()
+    bad = np.argwhere(g[:, :pend] != oqt[:, :pend])
+    assert bad.size == 0, f"{what}: {len(bad)} codes differ, first at {tuple(bad[0])}"
+    if sentinel:
+        assert (g[:, pend:] == 0xAB).all(), f"{what}: columns past pad[G] were written"
+    KT = k_cap // 256
+    RT = (cols + 31) // 32
+    swz = st_swz.cpu().numpy().reshape(RT, KT, 256)
+    oswz = oracle.scale_swizzle(ost).reshape(RT, KT, 256)
+    bad = np.argwhere(swz[:, :pend // 256] != oswz[:, :pend // 256])
+    assert bad.size == 0, f"{what}: {len(bad)} rearranged scale bytes differ, first at {tuple(bad[0])}"
+    if sentinel:
+        assert (swz[:, pend // 256:] == 0xCD).all(), f"{what}: scale tiles past pad[G] were written"
+    return qt, st_swz, pad, oqt, ost, opad
+
+
+@pytest.mark.parametrize("sizes,cols", [
+    ([37], 32),
+    ([0, 37, 256, 300, 5], 64),
+    ([0, 0, 0, 1], 288),
+    ([513, 0, 255, 256, 257, 1, 0], 256),
+    ([1000] * 3 + [0] * 5 + [31], 96),
+])
+def test_colwise_grouped_matches_oracle(gpu_lib, sizes, cols):
+    off = _offsets(sizes)
+    x = mxsynth.normal_bf16((int(off[-1]), cols), 1.0, seed=100 + len(sizes), outlier_frac=0.01)
+    _check_grouped_quant(gpu_lib, x, off, f"sizes={sizes} cols={cols}")
+
+
+def test_colwise_grouped_no_rows(gpu_lib):
+    """Every expert empty: each range is 256 zero columns with scale 0."""
+    mx = gpu_lib
+    off = np.zeros(4, np.int64)
+    x = torch.zeros((1, 64), dtype=torch.bfloat16)[:0]
+    qt, st_swz, pad = mx.mx_quantize_colwise_grouped(x.cuda(), torch.from_numpy(off).cuda())
+    torch.cuda.synchronize()
+    assert pad.cpu().tolist() == [0, 256, 512, 768]
+    assert (qt[:, :768].cpu() == 0).all()
+    swz = st_swz.cpu().numpy().reshape(2, -1, 256)
+    assert (swz[:, :3] == 0).all()
+
+
+def _wgrad_ref(pad, qa, sa, qb, sb):
+    """Oracle C [G][M][N] plus the window term per expert range."""
+    ref, bnd = oracle.grouped_wgrad(pad, qa, sa, qb, sb)
+    hw = np.zeros_like(ref)
+    da, db = oracle.dequantize_rowwise(qa, sa), oracle.dequantize_rowwise(qb, sb)
+    for g in range(len(pad) - 1):
+        lo, hi = int(pad[g]), int(pad[g + 1])
+        hw[g] = window_bound_full(da[:, lo:hi], db[:, lo:hi])
+    return ref, bnd, hw
+
+
+@pytest.mark.parametrize("sizes,M,N,dtype", [
+    ([37], 32, 32, torch.bfloat16),
+    ([0, 37, 256, 300, 5], 96, 224, torch.bfloat16),
+    ([700, 0, 1, 513], 288, 256, torch.float32),
+    ([100] * 9, 256, 512, torch.bfloat16),
+    ([2000, 3, 0, 600], 64, 544, torch.float32),
+])
+def test_wgrad_matches_oracle(gpu_lib, sizes, M, N, dtype):
+    mx = gpu_lib
+    off = _offsets(sizes)
+    T = int(off[-1])
+    dy = mxsynth.normal_bf16((T, M), 1e-3, seed=200 + M, outlier_frac=0.01)
+    x = mxsynth.normal_bf16((T, N), 1.0, seed=300 + N, outlier_frac=0.01)
+    qa, sa_swz, pad, oqa, osa, opad = _check_grouped_quant(mx, dy, off, "dY", sentinel=False)
+    qb, sb_swz, _, oqb, osb, _ = _check_grouped_quant(mx, x, off, "X", sentinel=False)
+    C = mx.mx_grouped_gemm_wgrad(pad, qa, sa_swz, qb, sb_swz, out_dtype=dtype)
+    torch.cuda.synchronize()
+    assert C.shape == (len(sizes), M, N)
+    ref, bnd, hw = _wgrad_ref(opad, oqa, osa, oqb, osb)
+    stats = assert_gemm_close(C.reshape(-1, N), GemmRef(ref.reshape(-1, N), bnd.reshape(-1, N),
+                                                        hw.reshape(-1, N)), f"wgrad {sizes}")
+    for g, m in enumerate(sizes):
+        if m == 0:
+            assert (C[g] == 0).all(), f"expert {g} has no rows but a nonzero gradient"
+    print(f"wgrad {sizes} {M}x{N}: {stats['within_stated']}/{stats['n']} within the stated bar")
+
+
+def test_wgrad_repeatable_and_offsets_change_only_their_expert(gpu_lib):
+    """Same inputs give the same bytes; moving rows between two experts
+    changes only those two experts' gradients."""
+    mx = gpu_lib
+    sizes = [300, 200, 500, 24]
+    off = _offsets(sizes)
+    T, M, N = int(off[-1]), 128, 256
+    dy = mxsynth.normal_bf16((T, M), 1e-3, seed=41).cuda()
+    x = mxsynth.normal_bf16((T, N), 1.0, seed=42).cuda()
+
+    def run(o):
+        od = torch.from_numpy(o).cuda()
+        qa, sa, pad = mx.mx_quantize_colwise_grouped(dy, od)
+        qb, sb, _ = mx.mx_quantize_colwise_grouped(x, od)
+        return mx.mx_grouped_gemm_wgrad(pad, qa, sa, qb, sb)
+
+    c1, c2 = run(off), run(off)
+    assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
+    off2 = off.copy()
+    off2[2] += 64          # 64 rows move from expert 2 to expert 1
+    c3 = run(off2)
+    same = [torch.equal(c1[g].view(torch.int16), c3[g].view(torch.int16)) for g in range(4)]
+    assert same == [True, False, False, True]
+
+
+def test_moe_backward_qwen3_30b_a3b(gpu_lib):
+    """Full size: 163840 routed rows over 128 experts with Zipf(1.1) loads.
+    Per projection, the grouped column-wise quantization of dY and of the
+    forward input (bytes exact over every column range), the weight gradient
+    on sampled entries of every expert, and the data gradient through the
+    column-wise expert weights on sampled rows of every expert."""
+    mx = gpu_lib
+    rows_per, a_gu, a_dn, w_gu, w_dn = mxsynth.moe_inputs()
+    dy_gu, dy_dn = mxsynth.moe_bwd_grads()
+    off = mxsynth.offsets_from_rows(rows_per)
+    offd = torch.from_numpy(off).cuda()
+    G = len(rows_per)
+    rng = np.random.default_rng(6)
+    # (name, dY [T][Nout], forward input X [T][Kin], W [G][Nout][Kin])
+    for name, dy, x, w in (("gate_up", dy_gu, a_gu, w_gu), ("down", dy_dn, a_dn, w_dn)):
+        print(f"moe bwd {name}: quantize", flush=True)
+        qa, sa, pad, oqa, osa, opad = _check_grouped_quant(mx, dy, off, f"{name} dY", sentinel=False)
+        qb, sb, _, oqb, osb, _ = _check_grouped_quant(mx, x, off, f"{name} X", sentinel=False)
+        Nout, Kin = w.shape[1], w.shape[2]
+        print(f"moe bwd {name}: wgrad {G}x{Nout}x{Kin}", flush=True)
+        C = mx.mx_grouped_gemm_wgrad(pad, qa, sa, qb, sb, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        # every expert: 16 random entries plus its corners
+        gs, rs, cs = [], [], []
+        for g in range(G):
+            r = np.concatenate([rng.integers(0, Nout, 16), [0, Nout - 1, 0, Nout - 1]])
+            c = np.concatenate([rng.integers(0, Kin, 16), [0, Kin - 1, Kin - 1, 0]])
+            gs.append(np.full(r.size, g))
+            rs.append(r)
+            cs.append(c)
+        gs, rs, cs = np.concatenate(gs), np.concatenate(rs), np.concatenate(cs)
+        ref, bnd = oracle.grouped_wgrad_sampled(gs, rs, cs, opad, oqa, osa, oqb, osb)
+        hw = np.empty_like(ref)
+        for g in range(G):
+            sel = gs == g
+            lo, hi = int(opad[g]), int(opad[g + 1])
+            da = oracle.dequantize_rowwise(oqa[rs[sel], lo:hi], osa[rs[sel], lo // 32:hi // 32])
+            db = oracle.dequantize_rowwise(oqb[cs[sel], lo:hi], osb[cs[sel], lo // 32:hi // 32])
+            hw[sel] = window_bound_pairs(da, db)
+        got = C[torch.from_numpy(gs).cuda(), torch.from_numpy(rs).cuda(), torch.from_numpy(cs).cuda()]
+        st = assert_gemm_close(got[None, :], GemmRef(ref[None], bnd[None], hw[None]), f"{name} wgrad")
+        print(f"moe bwd {name} wgrad: {st['within_stated']}/{st['n']} within the stated bar", flush=True)
+        del C, qa, sa, qb, sb, oqa, oqb
+
+        # data gradient: dX = dY . W_g, B = column-wise W_g ([Kin][Nout] per expert)
+        print(f"moe bwd {name}: dgrad", flush=True)
+        _, _, wqt, wst_swz = mx.mx_quantize_dual_experts(w.cuda())
+        wb = mxsynth.bits(w)
+        parts = _pool_map(lambda g: oracle.quantize_colwise(wb[g]), range(G))
+        owqt = np.stack([p[0] for p in parts])
+        owst = np.stack([p[1] for p in parts])
+        got_qt = wqt.cpu().numpy()
+        assert np.array_equal(got_qt, owqt), f"{name}: column-wise expert weights differ"
+        stb = mx.mx_scale_swizzled_bytes(Kin, Nout // 32)
+        oswz = np.concatenate([oracle.scale_swizzle(owst[g]) for g in range(G)])
+        assert np.array_equal(wst_swz.cpu().numpy(), oswz), f"{name}: expert weight scales differ"
+        assert wst_swz.numel() == G * stb
+        dq, ds = mx.mx_quantize_rowwise(dy.cuda())
+        odq, ods = mxsynth_rowwise(dy)
+        assert np.array_equal(dq.cpu().numpy(), odq) and np.array_equal(ds.cpu().numpy(), ods)
+        D = mx.mx_grouped_gemm(offd, dq, mx.mx_scale_swizzle(ds), wqt, wst_swz,
+                               out_dtype=torch.bfloat16)
+        firsts = off[:-1][rows_per > 0]
+        lasts = off[1:][rows_per > 0] - 1
+        rows = np.concatenate([firsts, lasts, rng.integers(0, int(off[-1]), 1024)])
+        cols = rng.integers(0, Kin, rows.size)
+        st = check_sampled_grouped(D, rows, cols, off, odq, ods, owqt, owst, f"{name} dgrad")
+        print(f"moe bwd {name} dgrad: {st['within_stated']}/{st['n']} within the stated bar", flush=True)
+        del D, dq, ds, wqt, wst_swz
+
+
+def mxsynth_rowwise(x):
+    from gpu_util import oracle_rowwise_par
+    return oracle_rowwise_par(mxsynth.bits(x))
