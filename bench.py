@@ -55,7 +55,7 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "dense_gemm_hbm_traffic.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_hbm_traffic_qwen3_layer.md")
 GEMM_SOURCE = os.path.join(ROOT, "mxfp8_block_scaled_08_amd", "csrc", "mx_gemm.hip")
 
 
