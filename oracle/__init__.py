@@ -66,6 +66,11 @@ def lib():
                                                   _u8p, _i64, _u8p, _i64, _u8p, _i64, _u8p,
                                                   _i64, _f64p, _f64p]
         L.oracle_grouped_pad_offsets.argtypes = [_i64, _i64p, _i64p]
+        L.oracle_swiglu_f64.restype = ctypes.c_double
+        L.oracle_swiglu_f64.argtypes = [ctypes.c_double, ctypes.c_double]
+        L.oracle_double_to_bf16.restype = ctypes.c_uint16
+        L.oracle_double_to_bf16.argtypes = [ctypes.c_double]
+        L.oracle_swiglu_bf16.argtypes = [_u16p, _i64, _i64, _i64, _u16p]
         L.oracle_quantize_colwise_grouped.argtypes = [_u16p, _i64, _i64, _i64, _i64p, _i64p,
                                                       _u8p, _i64, _u8p, _i64]
         L.oracle_grouped_wgrad_sampled.argtypes = [_i64, _i64p, _i64p, _i64p, _i64p, _u8p, _i64,
@@ -380,3 +385,39 @@ def grouped_wgrad(pad, qa, sa, qb, sb):
     g, i, j = np.meshgrid(np.arange(G), np.arange(M), np.arange(N), indexing="ij")
     c, bnd = grouped_wgrad_sampled(g.ravel(), i.ravel(), j.ravel(), pad, qa, sa, qb, sb)
     return c.reshape(G, M, N), bnd.reshape(G, M, N)
+
+
+# ---- SwiGLU between the MoE expert projections --------------------------
+# Qwen3's expert MLP ("End-to-End MXFP8 Reinforcement Learning on Blackwell",
+# Table 2: Qwen3-30B-A3B) feeds the down projection with h = silu(g) * u,
+# silu(g) = g / (1 + exp(-g)); g and u are the gate and up halves of the
+# gate_up product.  Activations are BF16 (Figure 1), so h is rounded once to
+# BF16 and then quantized row-wise as the down projection's A operand.
+
+
+def swiglu_f64(g: float, u: float) -> float:
+    return lib().oracle_swiglu_f64(g, u)
+
+
+def double_to_bf16(v: float) -> int:
+    """Nearest BF16 bit pattern (ties to even), one rounding from double."""
+    return lib().oracle_double_to_bf16(v)
+
+
+def swiglu_bf16(gu_bits):
+    """gu_bits uint16 [rows, 2F] (gate | up) -> h uint16 [rows, F] (BF16 bits)."""
+    gu = _c(gu_bits, np.uint16)
+    rows, F2 = gu.shape
+    assert F2 % 2 == 0
+    F = F2 // 2
+    h = np.empty((rows, F), np.uint16)
+    if rows:
+        lib().oracle_swiglu_bf16(_p(gu, _u16p), rows, F, F2, _p(h, _u16p))
+    return h
+
+
+def swiglu_quantize(gu_bits):
+    """SwiGLU then row-wise MXFP8: (h [rows, F] BF16 bits, q [rows, F], s [rows, F/32])."""
+    h = swiglu_bf16(gu_bits)
+    q, s = quantize_rowwise(h)
+    return h, q, s

@@ -384,3 +384,59 @@ void oracle_grouped_wgrad_sampled(int64_t n, const int64_t *groups, const int64_
                           bnd + e);
     }
 }
+
+/* ---- SwiGLU between the MoE expert projections ---------------------------
+ * Qwen3's expert MLP (paper Table 2: Qwen3-30B-A3B) feeds the down
+ * projection with h = silu(g) * u, silu(g) = g / (1 + exp(-g)), where g and u
+ * are the gate and up halves of the gate_up product.  The learner keeps
+ * activations in BF16 (paper Figure 1: BF16 activations quantized to MXFP8
+ * before each MXFP8 GEMM), so h is rounded once to BF16 (nearest, ties to
+ * even) and then quantized row-wise like any GEMM input. */
+
+double oracle_swiglu_f64(double g, double u)
+{
+    return g * u / (1.0 + exp(-g));
+}
+
+/* double -> BF16 bit pattern, round to nearest, ties to even, one rounding:
+ * 8 significant bits for normal results, multiples of 2^-133 below 2^-126,
+ * +-Inf from 2^128 * (1 - 2^-9) up; NaN stays NaN. */
+uint16_t oracle_double_to_bf16(double v)
+{
+    double a, q;
+    int e;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    if (isnan(v))
+        return 0x7FC0;
+    a = fabs(v);
+    if (a == 0.0)
+        return sign;
+    frexp(a, &e); /* a = m * 2^e, m in [0.5, 1) */
+    if (e - 1 >= -126)
+        q = ldexp(rint(ldexp(a, 8 - e)), e - 8);   /* 8 significant bits */
+    else
+        q = ldexp(rint(ldexp(a, 133)), -133);      /* subnormal spacing 2^-133 */
+    if (q >= ldexp(1.0, 128))
+        return sign | 0x7F80;
+    if (q == 0.0)
+        return sign;
+    /* q is exactly a BF16 value: read its fields */
+    frexp(q, &e);
+    if (e - 1 >= -126) {
+        uint16_t E = (uint16_t)(e - 1 + 127);
+        uint16_t M = (uint16_t)(ldexp(q, 8 - e) - 128.0);
+        return sign | (uint16_t)(E << 7) | M;
+    }
+    return sign | (uint16_t)ldexp(q, 133);
+}
+
+/* gu[rows][ld_gu]: columns [0, F) the gate g, [F, 2F) the up u (BF16) ->
+ * h[rows][F] BF16 bit patterns. */
+void oracle_swiglu_bf16(const uint16_t *gu, int64_t rows, int64_t F, int64_t ld_gu, uint16_t *h)
+{
+    int64_t r, j;
+    for (r = 0; r < rows; r++)
+        for (j = 0; j < F; j++)
+            h[r * F + j] = oracle_double_to_bf16(oracle_swiglu_f64(
+                oracle_bf16_to_double(gu[r * ld_gu + j]), oracle_bf16_to_double(gu[r * ld_gu + F + j])));
+}
