@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define MXFP8_ABI_VERSION 3
+#define MXFP8_ABI_VERSION 4
 
 typedef enum mx_status {
     MX_OK = 0,
@@ -271,6 +271,31 @@ mx_status mx_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t
                           const int32_t *topk_ids, int64_t topk, int64_t num_experts,
                           int64_t *offsets, int32_t *src_token, int32_t *slot, void *q, int64_t ld_q,
                           void *s_swz, void *stream);
+
+/*
+ * The SwiGLU between the MoE expert projections (Qwen3's expert MLP; paper
+ * Table 2: Qwen3-30B-A3B) fused with the row-wise quantization of its output,
+ * the down projection's A operand (paper Figure 1: BF16 activations quantized
+ * to MXFP8 before each MXFP8 GEMM):
+ *   gu     BF16 [rows][ld_gu], the gate_up product: columns [0, F) the gate g,
+ *          [F, 2F) the up projection u
+ *   h      BF16 [rows][ld_h] out, or null: h = silu(g) * u rounded once to
+ *          BF16 (nearest, ties to even), silu(g) = g / (1 + exp(-g)); computed
+ *          in FP32 (the sigmoid from exp(-|g|)), so h is the correctly rounded
+ *          BF16 value or, within a few FP32 ulps of a BF16 rounding midpoint,
+ *          its neighbour
+ *   q      E4M3 [rows][ld_q] out = mx_quantize_rowwise of h
+ *   s_swz  its scales in the rearranged layout of mx_scale_swizzle for a
+ *          [rows][F/32] scale tensor (the rows past `rows` in the last 32-row
+ *          tile are not written)
+ * Requirements: rows, F >= 0 (else MX_ERR_INVALID_ARG); F % 32 == 0 (else
+ * MX_ERR_SHAPE) and F % 256 == 0 (else MX_ERR_UNSUPPORTED); ld_gu >= 2F,
+ * ld_q >= F, ld_h >= F (else MX_ERR_INVALID_ARG); gu, h, q 16-byte aligned
+ * rows (ld_gu % 8, ld_h % 8, ld_q % 16; else MX_ERR_ALIGN); no two buffers
+ * overlap (else MX_ERR_OVERLAP).
+ */
+mx_status mx_swiglu_quantize(const void *gu, int64_t rows, int64_t F, int64_t ld_gu, void *h, int64_t ld_h,
+                             void *q, int64_t ld_q, void *s_swz, void *stream);
 
 /*
  * MoE combine: each token's expert outputs weighted and summed back in token

@@ -25,7 +25,7 @@ __all__ = [
     "mx_quantize_colwise", "mx_scale_swizzled_bytes", "mx_scale_swizzle", "mx_gemm",
     "mx_grouped_gemm", "mx_quantize_dual", "mx_quantize_dual_batch", "mx_quantize_dual_experts",
     "mx_moe_dispatch", "mx_moe_combine", "mx_grouped_k_capacity", "mx_quantize_colwise_grouped",
-    "mx_grouped_gemm_wgrad", "MX_OK", "MX_ERR_INVALID_ARG", "MX_ERR_SHAPE", "MX_ERR_ALIGN",
+    "mx_grouped_gemm_wgrad", "mx_swiglu_quantize", "MX_OK", "MX_ERR_INVALID_ARG", "MX_ERR_SHAPE", "MX_ERR_ALIGN",
     "MX_ERR_OVERLAP", "MX_ERR_UNSUPPORTED", "MX_ERR_HIP", "MX_BF16", "MX_F32",
 ]
 
@@ -93,6 +93,8 @@ def load() -> ctypes.CDLL:
     L.mx_grouped_gemm.restype = ctypes.c_int
     L.mx_grouped_gemm.argtypes = [_i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp,
                                   _i64, ctypes.c_int, _vp]
+    L.mx_swiglu_quantize.restype = ctypes.c_int
+    L.mx_swiglu_quantize.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]
     L.mx_quantize_dual_experts.restype = ctypes.c_int
     L.mx_quantize_dual_experts.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]
     L.mx_grouped_k_capacity.restype = _i64
@@ -466,3 +468,27 @@ def mx_grouped_gemm_wgrad(k_offsets: torch.Tensor, a_q: torch.Tensor, a_s_swz: t
                                       c.stride(1), _OUT[c.dtype], _stream(stream))
     _check("mx_grouped_gemm_wgrad", st)
     return c
+
+
+def mx_swiglu_quantize(gu: torch.Tensor, q: Optional[torch.Tensor] = None,
+                       s_swz: Optional[torch.Tensor] = None, h: Optional[torch.Tensor] = None,
+                       want_h: bool = False, stream=None):
+    """gu [rows][2F] BF16 (gate | up) -> (q [rows][F], s_swz, h or None): SwiGLU,
+    rounded to BF16, quantized row-wise with scales in the GEMM layout."""
+    rows, F2 = gu.shape
+    F = F2 // 2
+    dev = gu.device
+    if q is None:
+        q = torch.empty((rows, F), dtype=torch.uint8, device=dev)
+    if s_swz is None:
+        s_swz = torch.empty(mx_scale_swizzled_bytes(rows, F // 32), dtype=torch.uint8, device=dev)
+    if h is None and want_h:
+        h = torch.empty((rows, F), dtype=torch.bfloat16, device=dev)
+    q, s_swz = _u8(q), _u8(s_swz)
+    st = load().mx_swiglu_quantize(_dev(gu, "gu", torch.bfloat16), rows, F, _ld(gu, "gu"),
+                                   _dev(h, "h", torch.bfloat16) if h is not None else None,
+                                   _ld(h, "h") if h is not None else 0,
+                                   _dev(q, "q", torch.uint8), _ld(q, "q"),
+                                   _dev(s_swz, "s_swz", torch.uint8), _stream(stream))
+    _check("mx_swiglu_quantize", st)
+    return q, s_swz, h

@@ -392,6 +392,40 @@ mx_status mx_quantize_colwise_grouped(const void *x, int64_t rows_total, int64_t
                       fn);
 }
 
+mx_status mx_swiglu_quantize(const void *gu, int64_t rows, int64_t F, int64_t ld_gu, void *h, int64_t ld_h,
+                             void *q, int64_t ld_q, void *s_swz, void *stream)
+{
+    const char *fn = "mx_swiglu_quantize";
+    if (rows < 0 || F < 0)
+        return fail(MX_ERR_INVALID_ARG, "%s: negative size rows=%lld F=%lld", fn, (long long)rows, (long long)F);
+    if (F % 32 != 0)
+        return fail(MX_ERR_SHAPE, "%s: F=%lld is not a multiple of the 32-element block", fn, (long long)F);
+    if (F % 256 != 0)
+        return fail(MX_ERR_UNSUPPORTED, "%s: F=%lld: this build needs F %% 256 == 0", fn, (long long)F);
+    if (ld_gu < 2 * F || ld_q < F || (h && ld_h < F))
+        return fail(MX_ERR_INVALID_ARG, "%s: leading dimension too small (ld_gu=%lld ld_h=%lld ld_q=%lld)", fn,
+                    (long long)ld_gu, (long long)ld_h, (long long)ld_q);
+    if (rows == 0 || F == 0)
+        return ok();
+    if (!gu || !q || !s_swz)
+        return fail(MX_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!aligned(gu, 16) || ld_gu % 8 != 0 || !aligned(q, 16) || ld_q % 16 != 0 ||
+        (h && (!aligned(h, 16) || ld_h % 8 != 0)))
+        return fail(MX_ERR_ALIGN, "%s: gu, h and q need 16-byte aligned rows (ld_gu %% 8, ld_h %% 8, ld_q %% 16)",
+                    fn);
+    if (rows * (F / 8) >= ((int64_t)1 << 40))
+        return fail(MX_ERR_UNSUPPORTED, "%s: too large", fn);
+    const void *bufs[4] = {gu, h, q, s_swz};
+    const int64_t lens[4] = {extent(rows, 2 * F, ld_gu, 2), h ? extent(rows, F, ld_h, 2) : 0,
+                             extent(rows, F, ld_q, 1), swz_bytes(rows, F / 32)};
+    for (int i = 0; i < 4; i++)
+        for (int k = i + 1; k < 4; k++)
+            if (overlap(bufs[i], lens[i], bufs[k], lens[k]))
+                return fail(MX_ERR_OVERLAP, "%s: buffers %d and %d overlap", fn, i, k);
+    return hip_status(mx::launch_swiglu_quantize(gu, rows, F, ld_gu, h, ld_h, q, ld_q, s_swz, (hipStream_t)stream),
+                      fn);
+}
+
 mx_status mx_moe_combine(const void *y, int64_t tokens, int64_t hidden, int64_t ld_y,
                          const int32_t *slot, const float *weights, int64_t topk, void *out,
                          int64_t ld_out, void *stream)

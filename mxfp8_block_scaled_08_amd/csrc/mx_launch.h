@@ -89,4 +89,10 @@ hipError_t launch_grouped_gemm_wgrad(int64_t G, int64_t M, int64_t N, int64_t K,
                                      const void *b_s, void *c, int64_t ld_c, int c_dtype,
                                      hipStream_t stream);
 
+// SwiGLU of gu's halves ([0, F) gate, [F, 2F) up) fused with the row-wise
+// quantization of the BF16 result; h (BF16 [rows][ld_h]) stored when not
+// null.  F % 256 == 0.
+hipError_t launch_swiglu_quantize(const void *gu, int64_t rows, int64_t F, int64_t ld_gu, void *h,
+                                  int64_t ld_h, void *q, int64_t ld_q, void *s_swz, hipStream_t stream);
+
 }  // namespace mx

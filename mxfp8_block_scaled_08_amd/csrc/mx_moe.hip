@@ -234,4 +234,81 @@ hipError_t launch_moe_combine(const void *y, int64_t tokens, int64_t hidden, int
     return hipGetLastError();
 }
 
+// SwiGLU between the expert projections, fused with the row-wise
+// quantization of its output (the down projection's A operand).  Unit u = 8
+// consecutive outputs of row u / upr: one 16-byte load of the gate half and
+// one of the up half, h = g * sigmoid(g) * u in FP32 with the sigmoid taken
+// from exp(-|g|) (no overflow for any g), rounded to BF16 by the hardware's
+// nearest-even conversion; then the row-wise quantizer's quad layout (four
+// lanes per 32-element block, DPP quad maximum, scaled conversion) and the
+// scale byte stored at its rearranged position.  h itself is stored too when
+// asked for.
+__global__ __launch_bounds__(256) void swiglu_quantize_kernel(
+    const uint16_t *__restrict__ gu, int64_t ld_gu, int64_t F, uint16_t *__restrict__ h, int64_t ld_h,
+    uint8_t *__restrict__ q, int64_t ld_q, uint8_t *__restrict__ s_swz, int64_t units, uint32_t upr,
+    int64_t kt)
+{
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u - (threadIdx.x & 3) < units;
+         u += (int64_t)gridDim.x * 256) {
+        // upr is a multiple of 4, so a quad shares its row
+        const int64_t row = u / upr;
+        const int64_t cu = u - row * upr;
+        const bool live = u < units;
+        uint4 gw = make_uint4(0, 0, 0, 0), uw = make_uint4(0, 0, 0, 0);
+        if (live) {
+            gw = *reinterpret_cast<const uint4 *>(gu + row * ld_gu + cu * 8);
+            uw = *reinterpret_cast<const uint4 *>(gu + row * ld_gu + F + cu * 8);
+        }
+        const uint32_t gs[4] = {gw.x, gw.y, gw.z, gw.w}, us[4] = {uw.x, uw.y, uw.z, uw.w};
+        uint32_t hw[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            float hv[2];
+#pragma unroll
+            for (int e = 0; e < 2; e++) {
+                const float g = __builtin_bit_cast(float, e ? (gs[k] & 0xFFFF0000u) : (gs[k] << 16));
+                const float v = __builtin_bit_cast(float, e ? (us[k] & 0xFFFF0000u) : (us[k] << 16));
+                const float t = expf(-fabsf(g));  // the library exp: subnormal results kept
+                const float sig = (g >= 0.0f ? 1.0f : t) / (1.0f + t);
+                hv[e] = g * sig * v;
+            }
+            hw[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t{hv[0], hv[1]}), bf16x2_t));
+        }
+        if (live && h != nullptr)
+            *reinterpret_cast<uint4 *>(h + row * ld_h + cu * 8) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        uint32_t m = pk_max_u16(pk_max_u16(mag2(hw[0]), mag2(hw[1])), pk_max_u16(mag2(hw[2]), mag2(hw[3])));
+        m = max(m & 0xFFFFu, m >> 16);
+        m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+        m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+        if (!live)
+            continue;
+        const uint32_t c = scale_code(m);
+        const float sc = cvt_scale(c);
+        uint2 out;
+        out.x = nan_block_select(cvt_x4(hw[0], hw[1], sc), c);
+        out.y = nan_block_select(cvt_x4(hw[2], hw[3], sc), c);
+        *reinterpret_cast<uint2 *>(q + row * ld_q + cu * 8) = out;
+        if ((threadIdx.x & 3) == 0) {
+            const int64_t b = cu >> 2;  // 32-element block of the row
+            s_swz[((row >> 5) * kt + (b >> 3)) * 256 + (32 * (b & 1) + (row & 31)) * 4 + ((b & 7) >> 1)] =
+                (uint8_t)c;
+        }
+    }
+}
+
+hipError_t launch_swiglu_quantize(const void *gu, int64_t rows, int64_t F, int64_t ld_gu, void *h,
+                                  int64_t ld_h, void *q, int64_t ld_q, void *s_swz, hipStream_t stream)
+{
+    const uint32_t upr = (uint32_t)(F / 8);
+    const int64_t units = rows * upr;
+    const int64_t blocks = std::min<int64_t>((units + 255) / 256, 65536);
+    if (blocks == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(swiglu_quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const uint16_t *)gu, ld_gu, F, (uint16_t *)h, ld_h, (uint8_t *)q, ld_q,
+                       (uint8_t *)s_swz, units, upr, (F / 32 + 7) / 8);
+    return hipGetLastError();
+}
+
 }  // namespace mx

@@ -38,7 +38,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for n in names:
         assert hasattr(raw, n), f"{n} declared in include/mxfp8.h but not exported"
         assert hasattr(mx, n), f"{n} has no Python binding of the same name"
-    assert L.mx_abi_version() == 3
+    assert L.mx_abi_version() == 4
 
 
 def test_status_strings():
@@ -289,3 +289,24 @@ def test_quantize_dual_experts_validation():
     # qt stack over the input stack (4 x 64 x 64 BF16 = 32 KiB)
     assert f(FAKE, 4, 64, 64, FAKE2, FAKE3, FAKE + 30000, FAKE4 + (1 << 20), STREAM) == mx.MX_ERR_OVERLAP
     assert f(FAKE, 0, 64, 64, FAKE2, FAKE3, FAKE4, FAKE4 + (1 << 20), STREAM) == mx.MX_OK
+
+
+def test_swiglu_quantize_validation():
+    L = mx.load()
+    f = L.mx_swiglu_quantize
+    # gu, rows, F, ld_gu, h, ld_h, q, ld_q, s_swz
+    ok_args = [FAKE, 64, 768, 1536, FAKE2, 768, FAKE3, 768, FAKE4]
+    a = list(ok_args); a[2] = 48; a[3] = 96
+    assert f(*a, STREAM) == mx.MX_ERR_SHAPE
+    a = list(ok_args); a[2] = 288; a[3] = 576
+    assert f(*a, STREAM) == mx.MX_ERR_UNSUPPORTED
+    a = list(ok_args); a[3] = 1000
+    assert f(*a, STREAM) == mx.MX_ERR_INVALID_ARG
+    a = list(ok_args); a[0] = FAKE + 8
+    assert f(*a, STREAM) == mx.MX_ERR_ALIGN
+    a = list(ok_args); a[6] = 0
+    assert f(*a, STREAM) == mx.MX_ERR_INVALID_ARG
+    a = list(ok_args); a[6] = FAKE + 4096      # q inside gu
+    assert f(*a, STREAM) == mx.MX_ERR_OVERLAP
+    a = list(ok_args); a[1] = 0
+    assert f(*a, STREAM) == mx.MX_OK

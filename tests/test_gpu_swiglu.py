@@ -1,0 +1,88 @@
+"""GPU parity of the fused SwiGLU + row-wise quantization (mx_swiglu_quantize).
+
+The oracle computes h = silu(g) u in double and rounds once to BF16; the
+kernel computes in FP32, so its BF16 h is the oracle's or, within a few FP32
+ulps of a BF16 rounding midpoint, the neighbouring BF16 value (both are
+correct roundings of values inside FP32's error of the exact h).  What is
+unique is compared exactly: every block whose 32 h values equal the oracle's
+must have the oracle's scale byte and codes.  A block holding a neighbour
+value must still satisfy the quantizer's properties against the oracle's h:
+scale within one step, every code within one E4M3 step of the oracle's code.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mxsynth
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _gu(rows, F, seed):
+    g = mxsynth.normal_bf16((rows, 2 * F), 1.0, seed=seed, outlier_frac=0.01)
+    b = mxsynth.bits(g).copy()
+    if rows and F:
+        rng = np.random.default_rng(seed)
+        # gate values far out on both sides, zeros, and negative zeros
+        for v in (0xC2C8, 0x4248, 0x0000, 0x8000, 0xC1A0, 0x42B2, 0xC2B2):   # -100, 50, 0, -0, -20, 89, -89
+            r, c = rng.integers(0, rows, 8), rng.integers(0, F, 8)
+            b[r, c] = v
+    return b
+
+
+def _check(mx, rows, F, seed, what):
+    gb = _gu(rows, F, seed)
+    gu = mxsynth.from_bits(gb).cuda()
+    q, s_swz, h = mx.mx_swiglu_quantize(gu, want_h=True)
+    torch.cuda.synchronize()
+    oh, oq, os_ = oracle.swiglu_quantize(gb)
+    hg = h.cpu().view(torch.int16).numpy().view(np.uint16)
+    # h: the oracle's pattern or its neighbour of the same sign
+    diff = hg != oh
+    if diff.any():
+        a, b = hg[diff].astype(np.int32), oh[diff].astype(np.int32)
+        same_sign = (a & 0x8000) == (b & 0x8000)
+        near = same_sign & (np.abs(a - b) == 1)
+        zeros = ((a & 0x7FFF) == 0) & ((b & 0x7FFF) == 0)
+        assert (near | zeros).all(), f"{what}: h differs by more than one BF16 step at {np.argwhere(diff)[:5]}"
+    # codes and scales: exact on blocks whose h matches
+    qg = q.cpu().numpy()
+    sg = oracle.scale_unswizzle(s_swz.cpu().numpy(), rows, F // 32)
+    blk_same = ~diff.reshape(rows, F // 32, 32).any(axis=2)
+    assert np.array_equal(sg[blk_same], os_[blk_same]), f"{what}: scales differ on matching blocks"
+    qb, oqb = qg.reshape(rows, F // 32, 32), oq.reshape(rows, F // 32, 32)
+    assert np.array_equal(qb[blk_same], oqb[blk_same]), f"{what}: codes differ on matching blocks"
+    # other blocks: properties against the oracle
+    if (~blk_same).any():
+        assert (np.abs(sg[~blk_same].astype(int) - os_[~blk_same].astype(int)) <= 1).all()
+        dq = oracle.e4m3_decode_array(qb[~blk_same]) * np.ldexp(1.0, sg[~blk_same].astype(int) - 127)[:, None]
+        do = oracle.e4m3_decode_array(oqb[~blk_same]) * np.ldexp(1.0, os_[~blk_same].astype(int) - 127)[:, None]
+        step = np.ldexp(1.0, np.maximum(sg[~blk_same], os_[~blk_same]).astype(int) - 127 + 5)[:, None]
+        assert (np.abs(dq - do) <= step).all()
+    return int(diff.sum()), int((~blk_same).sum()), diff.size
+
+
+@pytest.mark.parametrize("rows,F", [(1, 256), (37, 768), (256, 256), (1000, 1024), (4099, 768)])
+def test_swiglu_quantize_matches_oracle(gpu_lib, rows, F):
+    nd, nb, n = _check(gpu_lib, rows, F, 10 + rows, f"{rows}x{F}")
+    print(f"{rows}x{F}: {nd} of {n} h values are the neighbouring BF16, {nb} blocks")
+
+
+def test_swiglu_without_h_and_empty(gpu_lib):
+    mx = gpu_lib
+    gb = _gu(64, 256, 3)
+    gu = mxsynth.from_bits(gb).cuda()
+    q1, s1, _ = mx.mx_swiglu_quantize(gu, want_h=True)
+    q2, s2, h2 = mx.mx_swiglu_quantize(gu)
+    torch.cuda.synchronize()
+    assert h2 is None and torch.equal(q1, q2) and torch.equal(s1, s2)
+    q0, s0, _ = mx.mx_swiglu_quantize(gu[:0])
+    assert q0.numel() == 0
+
+
+def test_swiglu_qwen3_moe_rows(gpu_lib):
+    """The Qwen3-30B-A3B expert MLP's width (F = 768) over all 163840 routed rows."""
+    nd, nb, n = _check(gpu_lib, 163840, 768, 77, "moe 163840x768")
+    assert nd <= n * 1e-3, f"{nd} neighbour values of {n}: more than FP32 rounding explains"
+    print(f"163840x768: {nd} of {n} h values are the neighbouring BF16 ({nb} blocks)")
