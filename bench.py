@@ -14,13 +14,16 @@ the ~4.5k-token dense break-even that sets M = 4608):
      wgrad = dY^T . X;
   4. Qwen3-30B-A3B MoE layer: 20480 tokens x top-8 = 163840 routed rows over
      128 experts with Zipf(1.1) loads; expert weights quantized in both
-     orientations (one dual pass over all experts), activations row-wise,
-     grouped GEMMs gate_up and down;
+     orientations (one dual pass over all experts); dispatch (rows sorted by
+     expert, gathered and quantized), grouped gate_up, SwiGLU fused with the
+     quantization of its output, grouped down, weighted combine;
   5. the same MoE layer's expert backward (Table 8's update_actor): per
      projection, dY row-wise for the data gradient dX = dY . W_g (grouped over
      rows, column-wise expert weights of step 4), dY and the forward input
      column-wise per expert into 256-aligned column ranges for the weight
-     gradient dW_g = dY_g^T X_g (grouped over each expert's token range).
+     gradient dW_g = dY_g^T X_g (grouped over each expert's token range).  The
+     forward input of down is step 4's SwiGLU output; that of gate_up, the
+     expert-sorted BF16 rows, and the two dY are synthetic of their shapes.
 
 Inputs are drawn once on the device (seeded, same distributions as the
 parity tests' CPU draws) and stay resident in HBM; the timed region holds
@@ -116,6 +119,10 @@ def build_workload(mx, torch, mxsynth):
     rows_per, a_gu, a_dn, w_gu, w_dn = mxsynth.moe_inputs(device=dev)
     dy_gu, dy_dn = mxsynth.moe_bwd_grads(device=dev)
     off = torch.from_numpy(mxsynth.offsets_from_rows(rows_per)).to(dev)
+    ids, rw = mxsynth.moe_routing()
+    x_tok = mxsynth.normal_bf16((ids.shape[0], w_gu.shape[2]), 1.0, 5300, device=dev)
+    ids = torch.from_numpy(ids).to(dev).contiguous()
+    rw = torch.from_numpy(rw).to(dev).contiguous()
     u8 = dict(dtype=torch.uint8, device=dev)
     swz = mx.mx_scale_swizzled_bytes
 
@@ -187,8 +194,19 @@ def build_workload(mx, torch, mxsynth):
     o["dX_mdn"] = torch.empty(M, 768, **bf)
     o["dW_mgu"] = torch.empty(G, 1536, 2048, **bf)
     o["dW_mdn"] = torch.empty(G, 2048, 768, **bf)
+    # MoE forward through dispatch, SwiGLU and combine
+    n_assign = ids.numel()
+    o["moff"] = torch.empty(G + 1, dtype=torch.int64, device=dev)
+    o["msrc"] = torch.empty(n_assign, dtype=torch.int32, device=dev)
+    o["mslot"] = torch.empty(n_assign, dtype=torch.int32, device=dev)
+    o["h"] = torch.empty(M, 768, **bf)
+    o["hq"] = torch.empty(M, 768, **u8)
+    o["hswz"] = torch.empty(swz(M, 768 // 32), **u8)
+    o["moe_out"] = torch.empty(ids.shape[0], 2048, **bf)
+    assert n_assign == M
     inputs = dict(W=W, xh=xh, xi=xi, dy=dy, x=xb, off=off, a_gu=a_gu, a_dn=a_dn,
-                  w_gu=w_gu, w_dn=w_dn, dy_gu=dy_gu, dy_dn=dy_dn, M=M, k_cap=k_cap)
+                  w_gu=w_gu, w_dn=w_dn, dy_gu=dy_gu, dy_dn=dy_dn, M=M, k_cap=k_cap,
+                  x_tok=x_tok, ids=ids, rw=rw)
     return inputs, o
 
 
@@ -231,18 +249,23 @@ def step(mx, I, o, T):
     T("swizzle", sw, o["xT_s"], o["xT_swz"])
     T("gemm", g, o["dy_q"], o["dy_swz"], o["guT_q"], o["guT_swz"], c=o["C_dgrad"])
     T("gemm", g, o["dyT_q"], o["dyT_swz"], o["xT_q"], o["xT_swz"], c=o["C_wgrad"])
-    # 4. MoE layer, grouped per expert
-    for name, a, w in (("mgu", I["a_gu"], I["w_gu"]), ("mdn", I["a_dn"], I["w_dn"])):
+    # 4. MoE layer: expert weights in both orientations, dispatch, gate_up,
+    #    SwiGLU + quantize, down, combine
+    for name, w in (("mgu", I["w_gu"]), ("mdn", I["w_dn"])):
         T("quant_dual", mx.mx_quantize_dual_experts, w, q=o[name + "_wq"], s_swz=o[name + "_wswz"],
           qt=o[name + "_wqt"], st_swz=o[name + "_wstswz"])
-        T("quant_row", rq, a, o[name + "_aq"], o[name + "_as"])
-        T("swizzle", sw, o[name + "_as"], o[name + "_aswz"])
-        T("grouped_gemm", mx.mx_grouped_gemm, I["off"], o[name + "_aq"], o[name + "_aswz"],
-          o[name + "_wq"], o[name + "_wswz"], c=o["C_" + name])
+    T("moe_dispatch", mx.mx_moe_dispatch, I["x_tok"], I["ids"], I["w_gu"].shape[0],
+      offsets=o["moff"], src=o["msrc"], slot=o["mslot"], q=o["mgu_aq"], s_swz=o["mgu_aswz"])
+    T("grouped_gemm", mx.mx_grouped_gemm, o["moff"], o["mgu_aq"], o["mgu_aswz"], o["mgu_wq"],
+      o["mgu_wswz"], c=o["C_mgu"])
+    T("swiglu", mx.mx_swiglu_quantize, o["C_mgu"], q=o["hq"], s_swz=o["hswz"], h=o["h"])
+    T("grouped_gemm", mx.mx_grouped_gemm, o["moff"], o["hq"], o["hswz"], o["mdn_wq"],
+      o["mdn_wswz"], c=o["C_mdn"])
+    T("moe_combine", mx.mx_moe_combine, o["C_mdn"], o["mslot"], I["rw"], out=o["moe_out"])
     # 5. MoE expert backward: data gradient grouped over rows, weight gradient
     #    grouped over each expert's token range
     k_cap = I["k_cap"]
-    for name, a, dyp in (("mgu", I["a_gu"], I["dy_gu"]), ("mdn", I["a_dn"], I["dy_dn"])):
+    for name, a, dyp in (("mgu", I["a_gu"], I["dy_gu"]), ("mdn", o["h"], I["dy_dn"])):
         T("quant_row", rq, dyp, o[name + "_dyq"], o[name + "_dys"])
         T("swizzle", sw, o[name + "_dys"], o[name + "_dyswz"])
         T("grouped_gemm", mx.mx_grouped_gemm, I["off"], o[name + "_dyq"], o[name + "_dyswz"],
@@ -264,7 +287,6 @@ def work_per_step(I):
     dual_el += I["dy"].numel()                                   # dgrad + wgrad operand
     dual_el += I["w_gu"].numel() + I["w_dn"].numel()             # MoE expert weights
     row_el = dual_el + I["xh"].numel() + I["xi"].numel()         # + forward activations
-    row_el += I["a_gu"].numel() + I["a_dn"].numel()              # + MoE activations
     row_el += I["dy_gu"].numel() + I["dy_dn"].numel()            # + MoE output gradients
     col_el = dual_el + I["x"].numel()                            # + wgrad activation operand
     # per-expert column-wise operands of the MoE weight gradients
@@ -275,8 +297,12 @@ def work_per_step(I):
              + 2 * 4608 * 4096 * 12288 + 2 * 12288 * 4096 * 24576 + 2 * 24576 * 4096 * 12288)
     grouped = 2 * (2 * M * 1536 * 2048 + 2 * M * 2048 * 768)   # forward + data gradient
     wgrad = 2 * M * 1536 * 2048 + 2 * M * 2048 * 768
+    disp_el = M * 2048           # routed rows gathered and quantized
+    swiglu_el = M * 768          # SwiGLU outputs, quantized
+    comb_el = I["x_tok"].numel()  # combined outputs
     return dict(row_el=row_el, col_el=col_el, dual_el=dual_el, colg_el=colg_el, dense=dense,
-                grouped=grouped, wgrad=wgrad)
+                grouped=grouped, wgrad=wgrad, disp_el=disp_el, swiglu_el=swiglu_el,
+                comb_el=comb_el, topk=I["ids"].shape[1])
 
 
 def cpu_baseline(torch, mxsynth, row_el, col_el, flops):
@@ -394,6 +420,15 @@ def main():
         "quantize_dual": {"ms": T.totals["quant_dual"] / K,
                           "GB/s": dual_el * DUAL_BYTES_PER_ELEMENT / (T.totals["quant_dual"] / K) / 1e6},
         "scale_swizzle": {"ms": T.totals["swizzle"] / K, "launches": T.counts["swizzle"] // K},
+        "moe_dispatch": {
+            "ms": T.totals["moe_dispatch"] / K,
+            "GB/s": w["disp_el"] * QUANT_BYTES_PER_ELEMENT / (T.totals["moe_dispatch"] / K) / 1e6},
+        "swiglu_quantize": {
+            "ms": T.totals["swiglu"] / K,
+            "GB/s": w["swiglu_el"] * (4 + 2 + QUANT_BYTES_PER_ELEMENT - 2) / (T.totals["swiglu"] / K) / 1e6},
+        "moe_combine": {
+            "ms": T.totals["moe_combine"] / K,
+            "GB/s": w["comb_el"] * (2 * w["topk"] + 2) / (T.totals["moe_combine"] / K) / 1e6},
         "quantize_colwise_grouped": {
             "ms": T.totals["quant_col_grouped"] / K,
             "GB/s": colg_el * QUANT_BYTES_PER_ELEMENT / (T.totals["quant_col_grouped"] / K) / 1e6},

@@ -39,13 +39,19 @@
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless stated; the caller owns all
- *     buffers (allocated e.g. with torch).  Apart from mx_gemm's
- *     stream-ordered split workspace (see there) the library allocates
- *     nothing; it keeps no pointer after returning and holds no derived
- *     state, so no cached layout can go stale.
+ *     buffers (allocated e.g. with torch).  Apart from one workspace per
+ *     (device, stream) (below) the library allocates nothing; it keeps no
+ *     pointer to caller memory after returning and holds no derived state,
+ *     so no cached layout can go stale.
+ *   - Workspace: mx_gemm with a split tail and mx_moe_dispatch use a device
+ *     buffer kept per (device, stream) for the life of the process.  The
+ *     first such call on a stream allocates it (hipMalloc), and a call that
+ *     needs more than it holds waits for that stream and replaces it; every
+ *     other call reuses it without any host-side wait.  Make the first of
+ *     these calls on a stream outside HIP graph capture.
  *   - Work is enqueued on `stream` (a hipStream_t cast to void*; NULL is the
- *     null stream).  No call synchronizes the host or reads device memory
- *     from the host; calls are capturable in a HIP graph.
+ *     null stream).  Apart from the workspace set-up above no call
+ *     synchronizes the host or reads device memory from the host.
  *   - Every argument is validated before anything is launched: on error no
  *     output byte is written and a status other than MX_OK is returned;
  *     mx_last_error() then gives a message naming the argument.  Launch
@@ -57,7 +63,7 @@
  *     MX_OK and launch nothing.
  *   - Calls on different streams may run concurrently; the library has no
  *     shared mutable state apart from the thread-local error message and
- *     mx_gemm's per-device workspace pool (stream-ordered allocations).
+ *     the per-stream workspaces (each used only by work on its stream).
  */
 #ifndef MXFP8_H
 #define MXFP8_H
@@ -264,8 +270,8 @@ mx_status mx_quantize_dual_experts(const void *x, int64_t num_experts, int64_t r
  * MX_ERR_SHAPE) and hidden % 256 == 0 (else MX_ERR_UNSUPPORTED),
  * tokens*topk < 2^30; x and q 16-byte aligned rows (ld_x % 8, ld_q % 16),
  * index arrays naturally aligned (else MX_ERR_ALIGN); outputs overlap
- * nothing (else MX_ERR_OVERLAP).  Uses a stream-ordered workspace of
- * 4 * num_experts bytes per 256 assignments from the library's pool.
+ * nothing (else MX_ERR_OVERLAP).  Uses 4 * num_experts bytes per 256
+ * assignments of the stream's workspace (see the conventions above).
  */
 mx_status mx_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
                           const int32_t *topk_ids, int64_t topk, int64_t num_experts,
@@ -343,10 +349,10 @@ mx_status mx_moe_combine(const void *y, int64_t tokens, int64_t hidden, int64_t 
  * range accumulates in FP32, and the S FP32 partial sums are added in range
  * order before the single rounding to BF16.  S depends only on M, N, K and
  * the device's compute-unit count, so results are deterministic per shape
- * and device.  The split takes a workspace of S * 256 KiB per leftover tile
- * (at most 64 MiB) as a stream-ordered allocation from a memory pool the
- * library creates per device and keeps for reuse; if that allocation fails
- * the call runs unsplit (same results up to the summation order).
+ * and device.  The split takes S * 256 KiB per leftover tile (at most
+ * 64 MiB) of the stream's workspace (see the conventions above); if it
+ * cannot be allocated the call runs unsplit (same results up to the
+ * summation order).
  */
 mx_status mx_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t ld_a,
                   const void *a_s_swz, const void *b_q, int64_t ld_b, const void *b_s_swz,

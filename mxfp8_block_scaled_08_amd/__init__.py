@@ -281,23 +281,34 @@ def mx_quantize_dual_batch(jobs, stream=None) -> None:
     _check("mx_quantize_dual_batch", st)
 
 
-def mx_moe_dispatch(x: torch.Tensor, topk_ids: torch.Tensor, num_experts: int, stream=None):
+def mx_moe_dispatch(x: torch.Tensor, topk_ids: torch.Tensor, num_experts: int,
+                    offsets: Optional[torch.Tensor] = None, src: Optional[torch.Tensor] = None,
+                    slot: Optional[torch.Tensor] = None, q: Optional[torch.Tensor] = None,
+                    s_swz: Optional[torch.Tensor] = None, stream=None):
     """Sort the routed rows by expert, gather and quantize them row-wise.
 
     x BF16 [tokens][hidden], topk_ids int32 [tokens][topk] -> (offsets int64
     [num_experts+1], src_token int32 [tokens*topk], slot int32 [tokens*topk],
-    q uint8 [tokens*topk][hidden], s_swz uint8: rearranged scales)."""
+    q uint8 [tokens*topk][hidden], s_swz uint8: rearranged scales); outputs
+    passed in are written in place."""
     tokens, hidden = x.shape
     if topk_ids.dim() != 2 or topk_ids.shape[0] != tokens or not topk_ids.is_contiguous():
         raise ValueError("topk_ids must be a contiguous [tokens][topk] tensor")
     topk = topk_ids.shape[1]
     n = tokens * topk
     dev = x.device
-    offsets = torch.empty(num_experts + 1, dtype=torch.int64, device=dev)
-    src = torch.empty(n, dtype=torch.int32, device=dev)
-    slot = torch.empty(n, dtype=torch.int32, device=dev)
-    q = torch.empty((n, hidden), dtype=torch.uint8, device=dev)
-    s_swz = torch.empty(mx_scale_swizzled_bytes(n, hidden // 32), dtype=torch.uint8, device=dev)
+    if offsets is None:
+        offsets = torch.empty(num_experts + 1, dtype=torch.int64, device=dev)
+    if src is None:
+        src = torch.empty(n, dtype=torch.int32, device=dev)
+    if slot is None:
+        slot = torch.empty(n, dtype=torch.int32, device=dev)
+    if q is None:
+        q = torch.empty((n, hidden), dtype=torch.uint8, device=dev)
+    if s_swz is None:
+        s_swz = torch.empty(mx_scale_swizzled_bytes(n, hidden // 32), dtype=torch.uint8, device=dev)
+    if offsets.numel() != num_experts + 1 or src.numel() != n or slot.numel() != n:
+        raise ValueError("offsets, src and slot must have num_experts+1, n and n entries")
     st = load().mx_moe_dispatch(_dev(x, "x", torch.bfloat16), tokens, hidden, _ld(x, "x"),
                                 _dev(topk_ids, "topk_ids", torch.int32), topk, num_experts,
                                 _dev(offsets, "offsets"), _dev(src, "src"), _dev(slot, "slot"),

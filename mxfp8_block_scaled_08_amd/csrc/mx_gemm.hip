@@ -48,6 +48,7 @@
 #include <algorithm>
 #include <cmath>
 #include <mutex>
+#include <vector>
 
 namespace mx {
 
@@ -979,33 +980,57 @@ static int cu_count()
     return cache[dev];
 }
 
-// Stream-ordered workspace (the split tail, the MoE permutation's counts): a
-// memory pool per device that keeps freed blocks for reuse (release
-// threshold at its maximum), so after the first call an allocation costs no
-// driver round trip.  The pool is the library's own; the device's default
-// pool is left as the caller set it.
-hipMemPool_t workspace_pool()
+// Workspace (the split tail's partial tiles, the MoE permutation's counts):
+// one device buffer per (device, stream), allocated on first use and grown
+// when a call needs more, kept until the process ends.  Work on one stream
+// runs in order, so successive calls on a stream can share its buffer; calls
+// on different streams get different buffers.  A stream-ordered pool
+// allocation per call was tried first: on this runtime it blocked the host
+// until the stream caught up, which left the GPU idle behind every such call.
+// Growing waits for the stream (the old buffer may still be in use) before
+// freeing; allocation and growth happen outside graph capture only if the
+// first call on a stream is made outside it.
+void *stream_workspace(hipStream_t stream, size_t bytes)
 {
+    struct Entry {
+        int dev;
+        hipStream_t stream;
+        void *ptr;
+        size_t bytes;
+    };
     static std::mutex mu;
-    static hipMemPool_t pools[64];
+    static std::vector<Entry> cache;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    if (hipGetDevice(&dev) != hipSuccess)
         return nullptr;
     std::lock_guard<std::mutex> lock(mu);
-    if (pools[dev] == nullptr) {
-        hipMemPoolProps props{};
-        props.allocType = hipMemAllocationTypePinned;
-        props.handleTypes = hipMemHandleTypeNone;
-        props.location.type = hipMemLocationTypeDevice;
-        props.location.id = dev;
-        hipMemPool_t pool = nullptr;
-        if (hipMemPoolCreate(&pool, &props) != hipSuccess)
+    for (Entry &e : cache) {
+        if (e.dev != dev || e.stream != stream)
+            continue;
+        if (e.bytes >= bytes)
+            return e.ptr;
+        if (hipStreamSynchronize(stream) != hipSuccess)
             return nullptr;
-        uint64_t keep = ~(uint64_t)0;
-        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
-        pools[dev] = pool;
+        (void)hipFree(e.ptr);
+        e.ptr = nullptr;
+        e.bytes = 0;
+        const size_t want = std::max(bytes, (size_t)1 << 20);
+        if (hipMalloc(&e.ptr, want) != hipSuccess) {
+            (void)hipGetLastError();
+            e.ptr = nullptr;
+            return nullptr;
+        }
+        e.bytes = want;
+        return e.ptr;
     }
-    return pools[dev];
+    void *ptr = nullptr;
+    const size_t want = std::max(bytes, (size_t)1 << 20);
+    if (hipMalloc(&ptr, want) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    cache.push_back(Entry{dev, stream, ptr, want});
+    return ptr;
 }
 
 // Sums of the split tail: thread t of tile r's 16384 takes float4 t of the
@@ -1089,18 +1114,16 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t
     if (rem > 0 && groups >= 2 && c_dtype == 0 && p.vec16 && N % BN == 0) {
         const int64_t balance = std::max<int64_t>(2, (int64_t)std::sqrt(26.0 * 2 * groups / (double)rem));
         const int64_t S = std::min<int64_t>(std::min<int64_t>(cus / rem, groups), balance);
-        hipMemPool_t pool = S >= 2 ? workspace_pool() : nullptr;
         const size_t part_bytes = (size_t)(rem * S) * (BM * BN * sizeof(float));
-        if (pool != nullptr && hipMallocFromPoolAsync(&ws, part_bytes, pool, stream) == hipSuccess) {
+        ws = S >= 2 ? stream_workspace(stream, part_bytes) : nullptr;
+        if (ws != nullptr) {
             p.dp_tiles = tiles - rem;
             p.split_tiles = (int)rem;
             p.split_s = (int)S;
             p.ws = (float *)ws;
             grid = (unsigned)std::max<int64_t>(std::min<int64_t>(p.dp_tiles, cus), rem * S);
-        } else {
-            ws = nullptr;
-            (void)hipGetLastError();  // a failed allocation leaves the unsplit schedule
         }
+        // (without a workspace the call runs unsplit)
     }
     if (ws != nullptr)
         hipLaunchKernelGGL((mx_gemm_kernel<0, 0, true>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
@@ -1115,9 +1138,6 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t
                                dim3(256), 0, stream, p);
             err = hipGetLastError();
         }
-        const hipError_t fe = hipFreeAsync(ws, stream);
-        if (err == hipSuccess)
-            err = fe;
     }
     return err;
 }

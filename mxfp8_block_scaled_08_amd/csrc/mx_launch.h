@@ -53,9 +53,10 @@ hipError_t launch_grouped_gemm(int64_t G, int64_t M_total, int64_t N, int64_t K,
                                const void *a_s, const void *b_q, const void *b_s, void *c,
                                int64_t ld_c, int c_dtype, hipStream_t stream);
 
-// The library's stream-ordered workspace pool of the current device (null
-// if it cannot be created).
-hipMemPool_t workspace_pool();
+// The current device's workspace for work on `stream`, at least `bytes`
+// long (null if it cannot be allocated): one buffer per (device, stream),
+// kept for reuse by later calls on that stream.
+void *stream_workspace(hipStream_t stream, size_t bytes);
 
 // MoE dispatch: stable order of the routed (token, expert) assignments by
 // expert, then the permuted rows gathered and quantized row-wise, scales in

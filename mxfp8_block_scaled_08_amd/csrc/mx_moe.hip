@@ -13,7 +13,8 @@
 // counts are exact); per expert a scan over the chunks plus the experts'
 // exclusive scan (the offsets); per assignment its rank among the earlier
 // assignments of its chunk with the same expert, from the chunk's experts in
-// LDS.  Expert ids outside [0, experts) are not routed (slot -1).
+// LDS.  The scan runs as one workgroup per expert over its chunks, then one
+// over the experts' totals.  Expert ids outside [0, experts) are not routed (slot -1).
 //
 // Gather + quantize.  Row i of the permuted operand is the quantized row of
 // token src_token[i]: the row-wise kernel's lane layout (8 BF16 per lane,
@@ -47,44 +48,76 @@ __global__ __launch_bounds__(MOE_CHUNK) void moe_count_kernel(const int32_t *__r
         counts[(int64_t)blockIdx.x * experts + g] = hist[g];
 }
 
-// One workgroup: thread g scans expert g's column of chunk counts into chunk
-// bases, then the experts' totals are scanned into the offsets and added.
-__global__ __launch_bounds__(MOE_MAX_EXPERTS) void moe_scan_kernel(int32_t *__restrict__ counts, int64_t chunks,
-                                                                   int experts, int64_t *__restrict__ offsets)
+// Per expert g (one workgroup each): exclusive scan of its column of chunk
+// counts, in place, so counts[c][g] becomes the number of g's assignments in
+// chunks before c; the column's total goes to offsets[g].  Thread t takes a
+// contiguous run of chunks; the runs' sums are scanned across the workgroup.
+constexpr int MOE_SCAN_THREADS = 256;
+
+__global__ __launch_bounds__(MOE_SCAN_THREADS) void moe_scan_chunks_kernel(int32_t *__restrict__ counts,
+                                                                         int64_t chunks, int experts,
+                                                                         int64_t *__restrict__ totals)
 {
-    __shared__ int64_t total[MOE_MAX_EXPERTS];
-    const int g = threadIdx.x;
-    int64_t run = 0;
-    if (g < experts) {
-        for (int64_t c = 0; c < chunks; c++) {
-            const int32_t t = counts[c * experts + g];
-            counts[c * experts + g] = (int32_t)run;
-            run += t;
-        }
-        total[g] = run;
+    __shared__ int64_t wsum[MOE_SCAN_THREADS / 64];
+    const int g = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t per = (chunks + MOE_SCAN_THREADS - 1) / MOE_SCAN_THREADS;
+    const int64_t c0 = min((int64_t)t * per, chunks), c1 = min(c0 + per, chunks);
+    int64_t sum = 0;
+    for (int64_t c = c0; c < c1; c++)
+        sum += counts[c * experts + g];
+    int64_t incl = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int64_t o = __shfl_up(incl, d, 64);
+        if (lane >= d)
+            incl += o;
     }
+    if (lane == 63)
+        wsum[wave] = incl;
     __syncthreads();
-    if (g == 0) {
-        int64_t acc = 0;
-        for (int e = 0; e < experts; e++) {
-            const int64_t t = total[e];
-            total[e] = acc;
-            offsets[e] = acc;
-            acc += t;
-        }
-        offsets[experts] = acc;
+    int64_t run = incl - sum;
+    for (int w = 0; w < wave; w++)
+        run += wsum[w];
+    for (int64_t c = c0; c < c1; c++) {
+        const int32_t v = counts[c * experts + g];
+        counts[c * experts + g] = (int32_t)run;
+        run += v;
     }
+    if (t == MOE_SCAN_THREADS - 1)
+        totals[g] = run;
+}
+
+// One workgroup: the experts' totals (in offsets[0..experts-1]) scanned into
+// the offsets, offsets[experts] = the routed count.
+__global__ __launch_bounds__(MOE_MAX_EXPERTS) void moe_scan_experts_kernel(int experts,
+                                                                          int64_t *__restrict__ offsets)
+{
+    __shared__ int64_t wsum[MOE_MAX_EXPERTS / 64];
+    const int g = threadIdx.x, lane = g & 63, wave = g >> 6;
+    const int64_t v = g < experts ? offsets[g] : 0;
+    int64_t incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int64_t o = __shfl_up(incl, d, 64);
+        if (lane >= d)
+            incl += o;
+    }
+    if (lane == 63)
+        wsum[wave] = incl;
     __syncthreads();
-    if (g < experts) {
-        const int32_t base = (int32_t)total[g];
-        for (int64_t c = 0; c < chunks; c++)
-            counts[c * experts + g] += base;
-    }
+    int64_t base = 0;
+    for (int w = 0; w < wave; w++)
+        base += wsum[w];
+    if (g < experts)
+        offsets[g] = base + incl - v;
+    if (g == experts - 1)
+        offsets[experts] = base + incl;
 }
 
 __global__ __launch_bounds__(MOE_CHUNK) void moe_place_kernel(const int32_t *__restrict__ ids, int64_t n,
                                                                int topk, int experts,
                                                                const int32_t *__restrict__ base,
+                                                               const int64_t *__restrict__ offsets,
                                                                int32_t *__restrict__ src_token,
                                                                int32_t *__restrict__ slot)
 {
@@ -108,7 +141,7 @@ __global__ __launch_bounds__(MOE_CHUNK) void moe_place_kernel(const int32_t *__r
     int rank = 0;
     for (int j = 0; j < i; j++)
         rank += ex[j] == e;
-    const int32_t p = base[(int64_t)blockIdx.x * experts + e] + rank;
+    const int32_t p = (int32_t)offsets[e] + base[(int64_t)blockIdx.x * experts + e] + rank;
     slot[a] = p;
     src_token[p] = (int32_t)(a / topk);
 }
@@ -161,20 +194,18 @@ hipError_t launch_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, in
 {
     const int64_t n = tokens * topk;
     const int64_t chunks = (n + MOE_CHUNK - 1) / MOE_CHUNK;
-    hipMemPool_t pool = workspace_pool();
-    if (pool == nullptr)
+    void *ws = stream_workspace(stream, (size_t)(chunks * experts) * sizeof(int32_t));
+    if (ws == nullptr)
         return hipErrorOutOfMemory;
-    void *ws = nullptr;
-    hipError_t e = hipMallocFromPoolAsync(&ws, (size_t)(chunks * experts) * sizeof(int32_t), pool, stream);
-    if (e != hipSuccess)
-        return e;
     int32_t *counts = (int32_t *)ws;
     hipLaunchKernelGGL(moe_count_kernel, dim3((unsigned)chunks), dim3(MOE_CHUNK), 0, stream, topk_ids, n,
                        (int)experts, counts);
-    hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, stream, counts, chunks,
-                       (int)experts, offsets);
+    hipLaunchKernelGGL(moe_scan_chunks_kernel, dim3((unsigned)experts), dim3(MOE_SCAN_THREADS), 0, stream,
+                       counts, chunks, (int)experts, offsets);
+    hipLaunchKernelGGL(moe_scan_experts_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, stream, (int)experts,
+                       offsets);
     hipLaunchKernelGGL(moe_place_kernel, dim3((unsigned)chunks), dim3(MOE_CHUNK), 0, stream, topk_ids, n,
-                       (int)topk, (int)experts, counts, src_token, slot);
+                       (int)topk, (int)experts, counts, (const int64_t *)offsets, src_token, slot);
     const uint32_t upr = (uint32_t)(hidden / 8);
     const int64_t units = n * upr;
     const int64_t per_pass = (int64_t)MOE_Q_THREADS;
@@ -182,9 +213,7 @@ hipError_t launch_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, in
     hipLaunchKernelGGL(moe_gather_quantize_kernel, dim3((unsigned)blocks), dim3(MOE_Q_THREADS), 0, stream,
                        (const uint16_t *)x, ld_x, src_token, offsets + experts, (uint8_t *)q, ld_q,
                        (uint8_t *)s_swz, units, upr, (hidden / 32 + 7) / 8);
-    e = hipGetLastError();
-    const hipError_t fe = hipFreeAsync(ws, stream);
-    return e != hipSuccess ? e : fe;
+    return hipGetLastError();
 }
 
 // Combine: thread -> 8 consecutive columns of one token; the token's slots in
