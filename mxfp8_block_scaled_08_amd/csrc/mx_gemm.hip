@@ -47,6 +47,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <climits>
 #include <mutex>
 #include <vector>
 
@@ -88,6 +89,9 @@ struct GemmParams {
     int64_t dp_tiles;
     int split_tiles, split_s;
     float *ws;
+    // K-grouped: the tile counter the workgroups take tiles from after their
+    // first (zero at launch)
+    int *counter;
 };
 
 __device__ __forceinline__ int chunk_perm(int row) { return (row >> 1) & 7; }
@@ -194,6 +198,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     __shared__ int s_pref[TABLE ? GROUP_TABLE + 1 : 1];
     __shared__ int s_lo[TABLE ? GROUP_TABLE : 1], s_hi[TABLE ? GROUP_TABLE : 1];
     __shared__ int s_wsum[4];
+    __shared__ int64_t s_next[KGROUPED ? 2 : 1];  // K-grouped: tiles taken ahead
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -317,18 +322,26 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     }
     int64_t my_tiles = t_first < t_end ? (t_end - t_first + t_step - 1) / t_step : 0;
     // K-grouped: tiles in rank order (an expert's tiles together, longest
-    // experts first) are dealt in rounds of P = gridDim.x, alternately
-    // forwards and backwards, to virtual slots v; slot v runs on workgroup
-    // (v mod P/8) * 8 + v / (P/8), so consecutive slots, which take
-    // neighbouring tiles of one expert, share an XCD and its L2.
+    // experts first).  Tile v of the first P = gridDim.x goes to virtual slot
+    // v, which runs on workgroup (v mod P/8) * 8 + v / (P/8), so neighbouring
+    // tiles of one expert share an XCD and its L2.  After that a workgroup
+    // takes the next tile in rank order from a counter when it is two tiles
+    // from needing it (its next two tiles must be known: the loads of a
+    // tile's first stages run during the previous tile), so the longest
+    // remaining tiles go to the workgroups that free up first.
     const int64_t P = gridDim.x;
     int64_t vslot = blockIdx.x;
+    int64_t t_nxt = 0;  // K-grouped: the tile after the current one
     if (KGROUPED) {
         if (P % 8 == 0)
             vslot = (int64_t)(blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3);
-        const int64_t full = ntiles / P, rem = ntiles - full * P;
-        const int64_t pos_last = (full & 1) ? P - 1 - vslot : vslot;
-        my_tiles = full + (pos_last < rem ? 1 : 0);
+        my_tiles = INT64_MAX;  // ended by the loop once no tile is left
+        if (tid == 0) {
+            s_next[1] = P + __hip_atomic_fetch_add(p.counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_next[0] = P + __hip_atomic_fetch_add(p.counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        t_nxt = uniform(s_next[1]);
     }
     int split_u = -1;  // this workgroup's split-tail unit
     if (SPLIT) {
@@ -450,9 +463,8 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             c.sp = split_u;
             return c;
         }
-        if (KGROUPED) {
-            const int64_t pos = (k & 1) ? P - 1 - vslot : vslot;
-            Tile c = coords(k * P + pos);
+        if (KGROUPED) {  // the first unit only; later ones come from the counter
+            Tile c = coords(vslot);
             c.sp = -1;
             return c;
         }
@@ -614,12 +626,8 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     // ---- the workgroup's stages: its units' stages numbered continuously,
     // so the pipeline runs across units
     Tile cur = unit(0);
-    int64_t total = (my_units - has_split) * KITP + (has_split ? cur.ns : 0);
-    if (KGROUPED) {
-        total = 0;
-        for (int64_t k = 0; k < my_units; k++)
-            total += unit(k).ns;
-    }
+    // (K-grouped: unknown in advance and not used)
+    const int64_t total = KGROUPED ? 0 : (my_units - has_split) * KITP + (has_split ? cur.ns : 0);
     uint32_t cur_srd = scale_lanes(cur);
 
     // prologue: scale words of the first group, stages 0 and 1 in flight
@@ -757,7 +765,15 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     // the first tile, wait for all of the wave's operations instead.
     for (int64_t k = 0; k < my_units; k++) {
         // the unit after this one (loaded during this unit's last two stages)
-        const Tile nxt = k + 1 < my_units ? unit(k + 1) : cur;
+        bool nxt_ok;
+        Tile nxt;
+        if (KGROUPED) {
+            nxt_ok = t_nxt < ntiles;
+            nxt = nxt_ok ? coords(t_nxt) : cur;
+        } else {
+            nxt_ok = k + 1 < my_units;
+            nxt = nxt_ok ? unit(k + 1) : cur;
+        }
         const uint32_t nxt_srd = scale_lanes(nxt);
         for (int st = 0; st < cur.ns; st++, gs++) {
             const int buf = (int)(gs & 1);
@@ -766,8 +782,9 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             const bool same = st + 2 < cur.ns;
             const int st2 = same ? st + 2 : st + 2 - cur.ns;
             const Tile ld = same ? cur : nxt;
-            const bool live = gs + 2 < total;
-            const bool live_group = ((gs + 2) & ~(int64_t)1) < total;  // the group's first stage
+            const bool live = KGROUPED ? (same || nxt_ok) : gs + 2 < total;
+            // the group's first stage (K-grouped: units are whole 256-K groups)
+            const bool live_group = KGROUPED ? live : ((gs + 2) & ~(int64_t)1) < total;
             // 1.
             read_frags(buf, 1, fa1, fb1);
             dma_scales(ld, (ld.kb + st2) >> 1, live_group);
@@ -821,6 +838,11 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             __builtin_amdgcn_sched_barrier(0);
         }
 
+        // K-grouped: take the tile of unit k + 3 (its slot was last read at the
+        // end of unit k - 1, before this unit's barriers)
+        if (KGROUPED && tid == 0)
+            s_next[(k + 1) & 1] =
+                P + __hip_atomic_fetch_add(p.counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // ---- split-tail unit (BF16 C, whole-width tiles only): its FP32
         // partial tile goes to its workspace slot, lane-major per sub-tile
         // and register group (64 lanes x 16 bytes per store, whole lines,
@@ -935,6 +957,11 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
         }
         // (a split-tail unit issues 64 stores, more than the next unit's
         // relaxed first wait allows, so that wait still covers its loads)
+        if (KGROUPED) {
+            if (!nxt_ok)
+                break;
+            t_nxt = uniform(s_next[k & 1]);  // the tile of unit k + 2
+        }
         cur = nxt;
         cur_srd = nxt_srd;
         // re-read the next stage's step-0 fragments, so that the copy read in
@@ -1178,6 +1205,12 @@ hipError_t launch_grouped_gemm(int64_t G, int64_t M_total, int64_t N, int64_t K,
     return hipGetLastError();
 }
 
+__global__ void zero_counter_kernel(int *counter)
+{
+    if (threadIdx.x == 0)
+        *counter = 0;
+}
+
 hipError_t launch_grouped_gemm_wgrad(int64_t G, int64_t M, int64_t N, int64_t K,
                                      const int64_t *k_offsets, const void *a_q, int64_t ld_a,
                                      const void *a_s, const void *b_q, int64_t ld_b,
@@ -1206,6 +1239,10 @@ hipError_t launch_grouped_gemm_wgrad(int64_t G, int64_t M, int64_t N, int64_t K,
     p.vec16 = vec16_ok(c, ld_c, c_dtype);
     const int64_t tiles = G * p.tiles_m * p.tiles_n;
     const unsigned grid = (unsigned)std::min<int64_t>(tiles, cu_count());
+    p.counter = (int *)stream_workspace(stream, 256);
+    if (p.counter == nullptr)
+        return hipErrorOutOfMemory;
+    hipLaunchKernelGGL(zero_counter_kernel, dim3(1), dim3(64), 0, stream, p.counter);
     if (c_dtype == 0)
         hipLaunchKernelGGL((mx_gemm_kernel<2, 0, false>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
     else
