@@ -161,9 +161,6 @@ def build_workload(mx, torch, mxsynth):
     k_cap = mx.mx_grouped_k_capacity(M, G)
     for name, a, w, dyp in (("mgu", a_gu, w_gu, dy_gu), ("mdn", a_dn, w_dn, dy_dn)):
         G, N, K = w.shape
-        o[name + "_aq"] = torch.empty(M, K, **u8)
-        o[name + "_as"] = torch.empty(M, K // 32, **u8)
-        o[name + "_aswz"] = torch.empty(swz(M, K // 32), **u8)
         # expert weights, both orientations: [G][N][K] and [G][K][N], scales
         # rearranged per expert, back to back
         o[name + "_wq"] = torch.empty(G, N, K, **u8)
@@ -197,6 +194,8 @@ def build_workload(mx, torch, mxsynth):
     # MoE forward through dispatch, SwiGLU and combine
     n_assign = ids.numel()
     o["moff"] = torch.empty(G + 1, dtype=torch.int64, device=dev)
+    o["xq"] = torch.empty(M, 2048, **u8)                 # dispatched rows, quantized
+    o["xswz"] = torch.empty(swz(M, 2048 // 32), **u8)
     o["msrc"] = torch.empty(n_assign, dtype=torch.int32, device=dev)
     o["mslot"] = torch.empty(n_assign, dtype=torch.int32, device=dev)
     o["h"] = torch.empty(M, 768, **bf)
@@ -235,8 +234,7 @@ def step(mx, I, o, T):
     T("quant_dual", mx.mx_quantize_dual_batch, jobs)
     # 2. dense forward, M = 4608
     for name in ("xh", "xi"):
-        T("quant_row", rq, I[name], o[name + "_q"], o[name + "_s"])
-        T("swizzle", sw, o[name + "_s"], o[name + "_swz"])
+        T("quant_row", mx.mx_quantize_rowwise_swz, I[name], q=o[name + "_q"], s_swz=o[name + "_swz"])
     g = mx.mx_gemm
     T("gemm", g, o["xh_q"], o["xh_swz"], o["qkv_q"], o["qkv_swz"], c=o["C_qkv"])
     T("gemm", g, o["xh_q"], o["xh_swz"], o["o_q"], o["o_swz"], c=o["C_o"])
@@ -255,8 +253,8 @@ def step(mx, I, o, T):
         T("quant_dual", mx.mx_quantize_dual_experts, w, q=o[name + "_wq"], s_swz=o[name + "_wswz"],
           qt=o[name + "_wqt"], st_swz=o[name + "_wstswz"])
     T("moe_dispatch", mx.mx_moe_dispatch, I["x_tok"], I["ids"], I["w_gu"].shape[0],
-      offsets=o["moff"], src=o["msrc"], slot=o["mslot"], q=o["mgu_aq"], s_swz=o["mgu_aswz"])
-    T("grouped_gemm", mx.mx_grouped_gemm, o["moff"], o["mgu_aq"], o["mgu_aswz"], o["mgu_wq"],
+      offsets=o["moff"], src=o["msrc"], slot=o["mslot"], q=o["xq"], s_swz=o["xswz"])
+    T("grouped_gemm", mx.mx_grouped_gemm, o["moff"], o["xq"], o["xswz"], o["mgu_wq"],
       o["mgu_wswz"], c=o["C_mgu"])
     T("swiglu", mx.mx_swiglu_quantize, o["C_mgu"], q=o["hq"], s_swz=o["hswz"], h=o["h"])
     T("grouped_gemm", mx.mx_grouped_gemm, o["moff"], o["hq"], o["hswz"], o["mdn_wq"],
@@ -266,8 +264,7 @@ def step(mx, I, o, T):
     #    grouped over each expert's token range
     k_cap = I["k_cap"]
     for name, a, dyp in (("mgu", I["a_gu"], I["dy_gu"]), ("mdn", o["h"], I["dy_dn"])):
-        T("quant_row", rq, dyp, o[name + "_dyq"], o[name + "_dys"])
-        T("swizzle", sw, o[name + "_dys"], o[name + "_dyswz"])
+        T("quant_row", mx.mx_quantize_rowwise_swz, dyp, q=o[name + "_dyq"], s_swz=o[name + "_dyswz"])
         T("grouped_gemm", mx.mx_grouped_gemm, I["off"], o[name + "_dyq"], o[name + "_dyswz"],
           o[name + "_wqt"], o[name + "_wstswz"], c=o["dX_" + name])
         T("quant_col_grouped", mx.mx_quantize_colwise_grouped, dyp, I["off"], k_cap=k_cap,

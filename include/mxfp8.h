@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define MXFP8_ABI_VERSION 4
+#define MXFP8_ABI_VERSION 5
 
 typedef enum mx_status {
     MX_OK = 0,
@@ -114,6 +114,28 @@ const char *mx_last_error(void);
  */
 mx_status mx_quantize_rowwise(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
                               void *q, int64_t ld_q, void *s, int64_t ld_s, void *stream);
+
+/*
+ * Row-wise quantization with the scales written straight into the GEMM's
+ * rearranged layout (what mx_quantize_rowwise followed by mx_scale_swizzle
+ * gives, in one pass: the activations' "MXFP8 quantization" and "scale
+ * rearrangement" of the paper's Table 6 fused).
+ *   q      = mx_quantize_rowwise's q
+ *   s_swz  tile (rt, kt) of the rearranged scales (rows 32rt.., blocks 8kt..)
+ *          at byte offset (rt * s_tiles + kt) * 256; with s_tiles =
+ *          cols / 256 the buffer equals mx_scale_swizzle of the row-wise
+ *          scales except that the padding rows of the last 32-row tile (rows
+ *          past `rows`) are not written.  A larger s_tiles, with s_swz
+ *          advanced to the block's first tile, writes into the rearranged
+ *          buffer of a larger operand (as mx_quantize_dual).
+ * Requirements: rows, cols >= 0 (else MX_ERR_INVALID_ARG); cols % 32 == 0
+ * (else MX_ERR_SHAPE) and cols % 256 == 0 (else MX_ERR_UNSUPPORTED);
+ * ld_x >= cols, ld_q >= cols, s_tiles >= cols / 256 (else
+ * MX_ERR_INVALID_ARG); x 16-byte aligned rows (ld_x % 8), q 8-byte (ld_q % 8)
+ * (else MX_ERR_ALIGN); no overlap (else MX_ERR_OVERLAP).
+ */
+mx_status mx_quantize_rowwise_swz(const void *x, int64_t rows, int64_t cols, int64_t ld_x, void *q,
+                                  int64_t ld_q, void *s_swz, int64_t s_tiles, void *stream);
 
 /*
  * Column-wise quantization (one 32x1 block per 32 consecutive elements of a

@@ -25,7 +25,7 @@ __all__ = [
     "mx_quantize_colwise", "mx_scale_swizzled_bytes", "mx_scale_swizzle", "mx_gemm",
     "mx_grouped_gemm", "mx_quantize_dual", "mx_quantize_dual_batch", "mx_quantize_dual_experts",
     "mx_moe_dispatch", "mx_moe_combine", "mx_grouped_k_capacity", "mx_quantize_colwise_grouped",
-    "mx_grouped_gemm_wgrad", "mx_swiglu_quantize", "MX_OK", "MX_ERR_INVALID_ARG", "MX_ERR_SHAPE", "MX_ERR_ALIGN",
+    "mx_grouped_gemm_wgrad", "mx_swiglu_quantize", "mx_quantize_rowwise_swz", "MX_OK", "MX_ERR_INVALID_ARG", "MX_ERR_SHAPE", "MX_ERR_ALIGN",
     "MX_ERR_OVERLAP", "MX_ERR_UNSUPPORTED", "MX_ERR_HIP", "MX_BF16", "MX_F32",
 ]
 
@@ -93,6 +93,8 @@ def load() -> ctypes.CDLL:
     L.mx_grouped_gemm.restype = ctypes.c_int
     L.mx_grouped_gemm.argtypes = [_i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp,
                                   _i64, ctypes.c_int, _vp]
+    L.mx_quantize_rowwise_swz.restype = ctypes.c_int
+    L.mx_quantize_rowwise_swz.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp]
     L.mx_swiglu_quantize.restype = ctypes.c_int
     L.mx_swiglu_quantize.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]
     L.mx_quantize_dual_experts.restype = ctypes.c_int
@@ -503,3 +505,24 @@ def mx_swiglu_quantize(gu: torch.Tensor, q: Optional[torch.Tensor] = None,
                                    _dev(s_swz, "s_swz", torch.uint8), _stream(stream))
     _check("mx_swiglu_quantize", st)
     return q, s_swz, h
+
+
+def mx_quantize_rowwise_swz(x: torch.Tensor, q: Optional[torch.Tensor] = None,
+                            s_swz: Optional[torch.Tensor] = None, s_tiles: Optional[int] = None,
+                            stream=None):
+    """BF16 x[rows][cols] -> (q [rows][cols], s_swz): row-wise MXFP8 with the scales
+    stored in the GEMM's rearranged layout in the same pass."""
+    rows, cols = x.shape
+    dev = x.device
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if s_tiles is None:
+        s_tiles = cols // 256
+    if s_swz is None:
+        s_swz = torch.empty(mx_scale_swizzled_bytes(rows, cols // 32), dtype=torch.uint8, device=dev)
+    q, s_swz = _u8(q), _u8(s_swz)
+    st = load().mx_quantize_rowwise_swz(_dev(x, "x", torch.bfloat16), rows, cols, _ld(x, "x"),
+                                        _dev(q, "q", torch.uint8), _ld(q, "q"),
+                                        _dev(s_swz, "s_swz", torch.uint8), s_tiles, _stream(stream))
+    _check("mx_quantize_rowwise_swz", st)
+    return q, s_swz

@@ -119,6 +119,37 @@ mx_status mx_quantize_rowwise(const void *x, int64_t rows, int64_t cols, int64_t
                       fn);
 }
 
+mx_status mx_quantize_rowwise_swz(const void *x, int64_t rows, int64_t cols, int64_t ld_x, void *q,
+                                  int64_t ld_q, void *s_swz, int64_t s_tiles, void *stream)
+{
+    const char *fn = "mx_quantize_rowwise_swz";
+    if (rows < 0 || cols < 0)
+        return fail(MX_ERR_INVALID_ARG, "%s: negative size rows=%lld cols=%lld", fn, (long long)rows,
+                    (long long)cols);
+    if (cols % 32 != 0)
+        return fail(MX_ERR_SHAPE, "%s: cols=%lld is not a multiple of the 32-element block", fn,
+                    (long long)cols);
+    if (cols % 256 != 0)
+        return fail(MX_ERR_UNSUPPORTED, "%s: cols=%lld: this build needs cols %% 256 == 0", fn,
+                    (long long)cols);
+    if (ld_x < cols || ld_q < cols || s_tiles < cols / 256)
+        return fail(MX_ERR_INVALID_ARG, "%s: ld_x=%lld, ld_q=%lld or s_tiles=%lld too small", fn,
+                    (long long)ld_x, (long long)ld_q, (long long)s_tiles);
+    if (rows == 0 || cols == 0)
+        return ok();
+    if (!x || !q || !s_swz)
+        return fail(MX_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!aligned(x, 16) || !aligned(q, 8) || ld_x % 8 != 0 || ld_q % 8 != 0)
+        return fail(MX_ERR_ALIGN, "%s: x needs 16-byte aligned rows (ld_x %% 8), q 8-byte (ld_q %% 8)", fn);
+    const int64_t ex = extent(rows, cols, ld_x, 2), eq = extent(rows, cols, ld_q, 1);
+    const int64_t es = (((rows + 31) / 32 - 1) * s_tiles + cols / 256) * 256;
+    if (overlap(x, ex, q, eq) || overlap(x, ex, s_swz, es) || overlap(q, eq, s_swz, es))
+        return fail(MX_ERR_OVERLAP, "%s: input and outputs must not overlap", fn);
+    return hip_status(mx::launch_quantize_rowwise_swz(x, rows, cols, ld_x, q, ld_q, s_swz, s_tiles,
+                                                      (hipStream_t)stream),
+                      fn);
+}
+
 mx_status mx_quantize_colwise(const void *x, int64_t rows, int64_t cols, int64_t ld_x, void *qt,
                               int64_t ld_qt, void *st, int64_t ld_st, void *stream)
 {

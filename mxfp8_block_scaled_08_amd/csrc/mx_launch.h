@@ -12,6 +12,12 @@ hipError_t launch_quantize_rowwise(const void *x, int64_t rows, int64_t cols, in
                                    void *q, int64_t ld_q, void *s, int64_t ld_s,
                                    hipStream_t stream);
 
+// Row-wise with the scales stored in the rearranged layout (tile (rt, kt)
+// at s_swz + (rt * s_tiles + kt) * 256); cols % 256 == 0.
+hipError_t launch_quantize_rowwise_swz(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                                       void *q, int64_t ld_q, void *s_swz, int64_t s_tiles,
+                                       hipStream_t stream);
+
 hipError_t launch_quantize_colwise(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
                                    void *qt, int64_t ld_qt, void *st, int64_t ld_st,
                                    hipStream_t stream);

@@ -17,12 +17,14 @@ namespace mx {
 // quad-permute steps; lane 0 of the quad stores the scale byte.  Every wave
 // reads 1 KiB contiguous per load and writes 512 B of codes per store.
 // UNROLL independent units per lane keep enough loads in flight to cover
-// HBM latency.
+// HBM latency.  SWZ: the scale byte goes straight to its place in the GEMM's
+// rearranged layout (ld_s then holds the tiles per 32-row tile row), which
+// saves the separate rearrangement pass.
 
 constexpr int QR_THREADS = 256;
 constexpr int QR_UNROLL = 4;
 
-template <bool CONTIG>
+template <bool CONTIG, bool SWZ>
 __global__ __launch_bounds__(QR_THREADS) void quantize_rowwise_kernel(
     const uint16_t *__restrict__ x, int64_t ld_x, uint8_t *__restrict__ q, int64_t ld_q,
     uint8_t *__restrict__ s, int64_t ld_s, int64_t units, uint32_t units_per_row)
@@ -65,14 +67,19 @@ __global__ __launch_bounds__(QR_THREADS) void quantize_rowwise_kernel(
             out.x = nan_block_select(cvt_x4(w.x, w.y, sc), c);
             out.y = nan_block_select(cvt_x4(w.z, w.w, sc), c);
             int64_t qo, so;
-            if (CONTIG) {
+            if (CONTIG && !SWZ) {
                 qo = u * 8;
                 so = u >> 2;
             } else {
                 int64_t row = u / units_per_row;
                 int64_t cu = u - row * units_per_row;
-                qo = row * ld_q + cu * 8;
-                so = row * ld_s + (cu >> 2);
+                qo = CONTIG ? u * 8 : row * ld_q + cu * 8;
+                if (SWZ) {
+                    const int64_t b = cu >> 2;  // 32-element block of the row
+                    so = ((row >> 5) * ld_s + (b >> 3)) * 256 + (32 * (b & 1) + (row & 31)) * 4 + ((b & 7) >> 1);
+                } else {
+                    so = row * ld_s + (cu >> 2);
+                }
             }
             *reinterpret_cast<uint2 *>(q + qo) = out;
             if ((threadIdx.x & 3) == 0)
@@ -417,13 +424,36 @@ hipError_t launch_quantize_rowwise(const void *x, int64_t rows, int64_t cols, in
         blocks = max_blocks;
     bool contig = (ld_x == cols) && (ld_q == cols) && (ld_s == cols / 32);
     if (contig)
-        hipLaunchKernelGGL(quantize_rowwise_kernel<true>, dim3((unsigned)blocks), dim3(QR_THREADS),
+        hipLaunchKernelGGL((quantize_rowwise_kernel<true, false>), dim3((unsigned)blocks), dim3(QR_THREADS),
                            0, stream, (const uint16_t *)x, ld_x, (uint8_t *)q, ld_q, (uint8_t *)s,
                            ld_s, units, upr);
     else
-        hipLaunchKernelGGL(quantize_rowwise_kernel<false>, dim3((unsigned)blocks),
+        hipLaunchKernelGGL((quantize_rowwise_kernel<false, false>), dim3((unsigned)blocks),
                            dim3(QR_THREADS), 0, stream, (const uint16_t *)x, ld_x, (uint8_t *)q,
                            ld_q, (uint8_t *)s, ld_s, units, upr);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_rowwise_swz(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                                       void *q, int64_t ld_q, void *s_swz, int64_t s_tiles,
+                                       hipStream_t stream)
+{
+    int64_t units = rows * (cols / 8);
+    uint32_t upr = (uint32_t)(cols / 8);
+    int64_t per_block = (int64_t)QR_THREADS * QR_UNROLL;
+    int64_t blocks = (units + per_block - 1) / per_block;
+    int64_t max_blocks = 256 * 8 * 4;
+    if (blocks > max_blocks)
+        blocks = max_blocks;
+    bool contig = (ld_x == cols) && (ld_q == cols);
+    if (contig)
+        hipLaunchKernelGGL((quantize_rowwise_kernel<true, true>), dim3((unsigned)blocks), dim3(QR_THREADS),
+                           0, stream, (const uint16_t *)x, ld_x, (uint8_t *)q, ld_q, (uint8_t *)s_swz,
+                           s_tiles, units, upr);
+    else
+        hipLaunchKernelGGL((quantize_rowwise_kernel<false, true>), dim3((unsigned)blocks),
+                           dim3(QR_THREADS), 0, stream, (const uint16_t *)x, ld_x, (uint8_t *)q,
+                           ld_q, (uint8_t *)s_swz, s_tiles, units, upr);
     return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for n in names:
         assert hasattr(raw, n), f"{n} declared in include/mxfp8.h but not exported"
         assert hasattr(mx, n), f"{n} has no Python binding of the same name"
-    assert L.mx_abi_version() == 4
+    assert L.mx_abi_version() == 5
 
 
 def test_status_strings():
@@ -310,3 +310,17 @@ def test_swiglu_quantize_validation():
     assert f(*a, STREAM) == mx.MX_ERR_OVERLAP
     a = list(ok_args); a[1] = 0
     assert f(*a, STREAM) == mx.MX_OK
+
+
+def test_quantize_rowwise_swz_validation():
+    L = mx.load()
+    f = L.mx_quantize_rowwise_swz
+    # x, rows, cols, ld_x, q, ld_q, s_swz, s_tiles
+    assert f(FAKE, 64, 48, 48, FAKE2, 48, FAKE3, 1, STREAM) == mx.MX_ERR_SHAPE
+    assert f(FAKE, 64, 288, 288, FAKE2, 288, FAKE3, 2, STREAM) == mx.MX_ERR_UNSUPPORTED
+    assert f(FAKE, 64, 512, 512, FAKE2, 512, FAKE3, 1, STREAM) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE, -1, 512, 512, FAKE2, 512, FAKE3, 2, STREAM) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE + 8, 64, 512, 512, FAKE2, 512, FAKE3, 2, STREAM) == mx.MX_ERR_ALIGN
+    assert f(FAKE, 64, 512, 512, FAKE + 1024, 512, FAKE3, 2, STREAM) == mx.MX_ERR_OVERLAP
+    assert f(0, 64, 512, 512, FAKE2, 512, FAKE3, 2, STREAM) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE, 0, 512, 512, FAKE2, 512, FAKE3, 2, STREAM) == mx.MX_OK

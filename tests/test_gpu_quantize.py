@@ -219,3 +219,44 @@ def test_swizzle_strided_input(gpu_lib):
     s = rng.integers(0, 255, size=(70, 40), dtype=np.uint8)
     out = mx.mx_scale_swizzle(to_dev(s)[:, 3:30])
     assert np.array_equal(out.cpu().numpy(), oracle.scale_swizzle(s[:, 3:30].copy()))
+
+
+@pytest.mark.parametrize("rows,cols", [(32, 256), (37, 512), (4608, 4096), (1000, 12288), (163840, 768)])
+def test_rowwise_swz_matches_oracle(gpu_lib, rows, cols):
+    """Row-wise codes and the rearranged scales in one pass: the codes equal
+    the oracle's, every written scale byte sits where the oracle's
+    rearrangement puts it (rows past the tensor in the last 32-row tile are
+    padding the call does not write)."""
+    import mxsynth
+    mx = gpu_lib
+    x = mxsynth.normal_bf16((rows, cols), 1.0, seed=rows + cols, outlier_frac=0.005)
+    xb = mxsynth.bits(x)
+    q, s_swz = mx.mx_quantize_rowwise_swz(x.cuda())
+    torch.cuda.synchronize()
+    from gpu_util import oracle_rowwise_par
+    oq, os_ = oracle_rowwise_par(xb)
+    assert np.array_equal(q.cpu().numpy(), oq)
+    got = s_swz.cpu().numpy()
+    if rows % 32 == 0:
+        assert np.array_equal(got, oracle.scale_swizzle(os_))
+    else:
+        assert np.array_equal(oracle.scale_unswizzle(got, rows, cols // 32), os_)
+
+
+def test_rowwise_swz_into_larger_operand(gpu_lib):
+    """Two tensors side by side along K (s_tiles of the larger operand): the
+    result equals quantizing the concatenation."""
+    import mxsynth
+    mx = gpu_lib
+    a = mxsynth.normal_bf16((64, 512), 1.0, seed=5)
+    b = mxsynth.normal_bf16((64, 256), 1.0, seed=6)
+    cat = torch.cat([a, b], dim=1)
+    kt = 768 // 256
+    q = torch.empty(64, 768, dtype=torch.uint8, device="cuda")
+    s_swz = torch.full((mx.mx_scale_swizzled_bytes(64, 24),), 0xEE, dtype=torch.uint8, device="cuda")
+    mx.mx_quantize_rowwise_swz(a.cuda(), q=q[:, :512], s_swz=s_swz, s_tiles=kt)
+    mx.mx_quantize_rowwise_swz(b.cuda(), q=q[:, 512:], s_swz=s_swz[2 * 256:], s_tiles=kt)
+    torch.cuda.synchronize()
+    oq, os_ = oracle.quantize_rowwise(mxsynth.bits(cat))
+    assert np.array_equal(q.cpu().numpy(), oq)
+    assert np.array_equal(s_swz.cpu().numpy(), oracle.scale_swizzle(os_))
