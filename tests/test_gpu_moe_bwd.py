@@ -233,3 +233,37 @@ def test_moe_backward_qwen3_30b_a3b(gpu_lib):
 def mxsynth_rowwise(x):
     from gpu_util import oracle_rowwise_par
     return oracle_rowwise_par(mxsynth.bits(x))
+
+
+def test_offsets_outside_the_stated_properties_stay_in_bounds(gpu_lib):
+    """Offsets that are not nondecreasing within [0, rows] (and pad offsets
+    that are not 256-aligned) give unspecified results but run to completion
+    inside the buffers: the quantizer clamps the offsets into [0, rows] and
+    makes the ranges nondecreasing, the GEMM clamps every range to at least
+    one 256-column group inside [0, k_cap).  Checked here: both calls
+    complete, the quantizer's ranges are 256-aligned, nondecreasing and end
+    at most at k_cap, bytes past the buffers' ends are untouched, and the
+    product is finite."""
+    mx = gpu_lib
+    rows, cols, G = 1000, 64, 4
+    x = mxsynth.normal_bf16((rows, cols), 1.0, seed=55).cuda()
+    off = torch.tensor([0, 500, 100, 5000, -7], dtype=torch.int64, device="cuda")
+    k_cap = mx.mx_grouped_k_capacity(rows, G)
+    guard = 4096
+    qt_buf = torch.full((cols * k_cap + guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    qt = qt_buf[:cols * k_cap].view(cols, k_cap)
+    swz_n = mx.mx_scale_swizzled_bytes(cols, k_cap // 32)
+    st_buf = torch.full((swz_n + guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    _, _, pad = mx.mx_quantize_colwise_grouped(x, off, k_cap=k_cap, qt=qt, st_swz=st_buf[:swz_n])
+    torch.cuda.synchronize()
+    p = pad.cpu().numpy()
+    assert p[0] == 0 and (np.diff(p) >= 0).all() and (p % 256 == 0).all() and p[-1] <= k_cap
+    assert (qt_buf[cols * k_cap:].cpu() == 0x5A).all() and (st_buf[swz_n:].cpu() == 0x5A).all()
+    # a product over ranges that are neither aligned nor ordered
+    bad = torch.tensor([0, 300, 100, 10 ** 9, -256], dtype=torch.int64, device="cuda")
+    c_buf = torch.full((G * cols * cols + guard,), 7.0, dtype=torch.float32, device="cuda")
+    c = c_buf[:G * cols * cols].view(G, cols, cols)
+    mx.mx_grouped_gemm_wgrad(bad, qt, st_buf[:swz_n], qt, st_buf[:swz_n], c=c)
+    torch.cuda.synchronize()
+    assert torch.isfinite(c).all()
+    assert (c_buf[G * cols * cols:] == 7.0).all()
