@@ -75,18 +75,17 @@ __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
     __shared__ uint32_t lds_st[8 * 64];
     const int64_t tr = blockIdx.x / tiles_c, tc = blockIdx.x - tr * tiles_c;
     const int64_t P0 = tr * QG_TILE;  // first padded column (row of the padded operand)
-    if (P0 >= pad[G])
+    // The expert whose range holds P0 is the last g with pad[g] <= P0; the
+    // ranges are nondecreasing and pad[0] = 0, so g = #{j in 1..G : pad[j] <=
+    // P0}.  Every thread tests up to two entries (G <= 1024) and the
+    // workgroup counts them: one round of loads instead of a dependent
+    // binary search.  g == G means P0 is past the last range.
+    int hits = 0;
+    for (int j = (int)threadIdx.x + 1; j <= G; j += QG_THREADS)
+        hits += pad[j] <= P0 ? 1 : 0;
+    const int g = __syncthreads_count(hits >= 1) + __syncthreads_count(hits >= 2);
+    if (g >= G)
         return;  // past the last expert's range: nothing to write
-    // the expert whose range holds P0: the last g with pad[g] <= P0
-    int lo = 0, hi = G;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (pad[mid] <= P0)
-            lo = mid;
-        else
-            hi = mid;
-    }
-    const int g = lo;
     const int64_t glo = min(max(offsets[g], (int64_t)0), rows);
     const int64_t ghi = min(max(offsets[g + 1], glo), rows);
     const int64_t src0 = glo + (P0 - pad[g]);
