@@ -266,11 +266,13 @@ def step(mx, I, o, T):
     #    grouped over each expert's token range
     k_cap = I["k_cap"]
     for name, a, dyp in (("mgu", I["a_gu"], I["dy_gu"]), ("mdn", o["h"], I["dy_dn"])):
-        T("quant_row", mx.mx_quantize_rowwise_swz, dyp, q=o[name + "_dyq"], s_swz=o[name + "_dyswz"])
+        # dY row-wise (data gradient) and per expert column-wise (weight
+        # gradient) from one read
+        T("quant_dual_grouped", mx.mx_quantize_dual_grouped, dyp, I["off"], k_cap=k_cap,
+          q=o[name + "_dyq"], s_swz=o[name + "_dyswz"], qt=o[name + "_dyT"], st_swz=o[name + "_dyTswz"],
+          pad_offsets=o[name + "_pad"])
         T("grouped_gemm", mx.mx_grouped_gemm, I["off"], o[name + "_dyq"], o[name + "_dyswz"],
           o[name + "_wqt"], o[name + "_wstswz"], c=o["dX_" + name])
-        T("quant_col_grouped", mx.mx_quantize_colwise_grouped, dyp, I["off"], k_cap=k_cap,
-          qt=o[name + "_dyT"], st_swz=o[name + "_dyTswz"], pad_offsets=o[name + "_pad"])
         T("quant_col_grouped", mx.mx_quantize_colwise_grouped, a, I["off"], k_cap=k_cap,
           qt=o[name + "_xT"], st_swz=o[name + "_xTswz"], pad_offsets=o[name + "_pad2"])
         T("grouped_wgrad", mx.mx_grouped_gemm_wgrad, o[name + "_pad"], o[name + "_dyT"],
@@ -286,11 +288,11 @@ def work_per_step(I):
     dual_el += I["dy"].numel()                                   # dgrad + wgrad operand
     dual_el += I["w_gu"].numel() + I["w_dn"].numel()             # MoE expert weights
     row_el = dual_el + I["xh"].numel() + I["xi"].numel()         # + forward activations
-    row_el += I["dy_gu"].numel() + I["dy_dn"].numel()            # + MoE output gradients
     col_el = dual_el + I["x"].numel()                            # + wgrad activation operand
     # per-expert column-wise operands of the MoE weight gradients
-    colg_el = (I["dy_gu"].numel() + I["dy_dn"].numel() + I["a_gu"].numel()
-               + I["a_dn"].numel())
+    colg_el = I["a_gu"].numel() + I["a_dn"].numel()
+    # MoE output gradients: row-wise and per-expert column-wise from one read
+    dualg_el = I["dy_gu"].numel() + I["dy_dn"].numel()
     M = I["M"]
     dense = (2 * 4608 * 6144 * 4096 + 2 * 4608 * 4096 * 4096 + 2 * 4608 * 24576 * 4096
              + 2 * 4608 * 4096 * 12288 + 2 * 12288 * 4096 * 24576 + 2 * 24576 * 4096 * 12288)
@@ -299,7 +301,8 @@ def work_per_step(I):
     disp_el = M * 2048           # routed rows gathered and quantized
     swiglu_el = M * 768          # SwiGLU outputs, quantized
     comb_el = I["x_tok"].numel()  # combined outputs
-    return dict(row_el=row_el, col_el=col_el, dual_el=dual_el, colg_el=colg_el, dense=dense,
+    return dict(row_el=row_el, col_el=col_el, dual_el=dual_el, colg_el=colg_el, dualg_el=dualg_el,
+                dense=dense,
                 grouped=grouped, wgrad=wgrad, disp_el=disp_el, swiglu_el=swiglu_el,
                 comb_el=comb_el, topk=I["ids"].shape[1])
 
@@ -446,14 +449,16 @@ def main():
 
     w = work_per_step(I)
     row_el, col_el, dual_el, colg_el = w["row_el"], w["col_el"], w["dual_el"], w["colg_el"]
+    dualg_el = w["dualg_el"]
     dense, grouped, wgrad = w["dense"], w["grouped"], w["wgrad"]
     flops = dense + grouped + wgrad
     K = args.steps
     row_only, col_only = row_el - dual_el, col_el - dual_el
     q_bytes = ((row_only + col_only + colg_el) * QUANT_BYTES_PER_ELEMENT
-               + dual_el * DUAL_BYTES_PER_ELEMENT)
+               + (dual_el + dualg_el) * DUAL_BYTES_PER_ELEMENT)
     qt = (T.totals.get("quant_row", 0) + T.totals.get("quant_col", 0)
-          + T.totals.get("quant_dual", 0) + T.totals.get("quant_col_grouped", 0)) / K  # ms
+          + T.totals.get("quant_dual", 0) + T.totals.get("quant_col_grouped", 0)
+          + T.totals.get("quant_dual_grouped", 0)) / K  # ms
     gemm_ms = T.totals["gemm"] / K
     ggemm_ms = T.totals["grouped_gemm"] / K
     wg_ms = T.totals["grouped_wgrad"] / K
@@ -474,6 +479,9 @@ def main():
         "moe_combine": {
             "ms": T.totals["moe_combine"] / K,
             "GB/s": w["comb_el"] * (2 * w["topk"] + 2) / (T.totals["moe_combine"] / K) / 1e6},
+        "quantize_dual_grouped": {
+            "ms": T.totals["quant_dual_grouped"] / K,
+            "GB/s": dualg_el * DUAL_BYTES_PER_ELEMENT / (T.totals["quant_dual_grouped"] / K) / 1e6},
         "quantize_colwise_grouped": {
             "ms": T.totals["quant_col_grouped"] / K,
             "GB/s": colg_el * QUANT_BYTES_PER_ELEMENT / (T.totals["quant_col_grouped"] / K) / 1e6},
@@ -514,7 +522,7 @@ def main():
                          "and expert backward (data gradient grouped over rows, weight gradient "
                          "grouped over each expert's token range)"),
             "gemm_flop_per_step": flops,
-            "quantized_elements_per_step": row_el + col_el + colg_el,
+            "quantized_elements_per_step": row_el + col_el + colg_el + 2 * dualg_el,
             "parallelism": "single GPU",
         },
         "value_definition": "total GEMM FLOP of the step / wall time of the whole step "
@@ -541,7 +549,8 @@ def main():
     if graph is not None:
         result["graph"] = graph
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(torch, mxsynth, row_el, col_el + colg_el, flops)
+        result["cpu_baseline"] = cpu_baseline(torch, mxsynth, row_el + dualg_el, col_el + colg_el + dualg_el,
+                                              flops)
     print(json.dumps(result))
 
 

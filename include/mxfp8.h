@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define MXFP8_ABI_VERSION 5
+#define MXFP8_ABI_VERSION 6
 
 typedef enum mx_status {
     MX_OK = 0,
@@ -444,6 +444,27 @@ mx_status mx_quantize_colwise_grouped(const void *x, int64_t rows_total, int64_t
                                       const int64_t *group_offsets, int64_t num_groups,
                                       int64_t *pad_offsets, void *qt, int64_t ld_qt, int64_t k_cap,
                                       void *st_swz, void *stream);
+
+/*
+ * Both operands a MoE expert backward needs from its output gradient, from one
+ * read (paper Table 8, update_actor; Table 2): the row-wise quantization of
+ * every row (the data gradient dX = dY . W_g, mx_grouped_gemm's A) and the
+ * per-expert column-wise quantization of mx_quantize_colwise_grouped (the
+ * weight gradient's A).  Arguments and outputs as mx_quantize_colwise_grouped,
+ * plus
+ *   q      E4M3 [rows_total][ld_q] out = mx_quantize_rowwise of x
+ *   s_swz  its scales in the rearranged layout of mx_scale_swizzle for a
+ *          [rows_total][cols/32] scale tensor (the padding rows of the last
+ *          32-row tile are not written)
+ * Requirements: those of mx_quantize_colwise_grouped, plus cols % 256 == 0
+ * (else MX_ERR_UNSUPPORTED), ld_q >= cols (else MX_ERR_INVALID_ARG), q 8-byte
+ * aligned rows with ld_q % 8 == 0 (else MX_ERR_ALIGN), q and s_swz overlap
+ * nothing (else MX_ERR_OVERLAP).
+ */
+mx_status mx_quantize_dual_grouped(const void *x, int64_t rows_total, int64_t cols, int64_t ld_x,
+                                   const int64_t *group_offsets, int64_t num_groups, int64_t *pad_offsets,
+                                   void *q, int64_t ld_q, void *s_swz, void *qt, int64_t ld_qt, int64_t k_cap,
+                                   void *st_swz, void *stream);
 
 /*
  * MoE weight gradient, product side (paper Table 8, update_actor; Table 2):

@@ -423,6 +423,55 @@ mx_status mx_quantize_colwise_grouped(const void *x, int64_t rows_total, int64_t
                       fn);
 }
 
+mx_status mx_quantize_dual_grouped(const void *x, int64_t rows_total, int64_t cols, int64_t ld_x,
+                                   const int64_t *group_offsets, int64_t num_groups, int64_t *pad_offsets,
+                                   void *q, int64_t ld_q, void *s_swz, void *qt, int64_t ld_qt, int64_t k_cap,
+                                   void *st_swz, void *stream)
+{
+    const char *fn = "mx_quantize_dual_grouped";
+    if (rows_total < 0 || cols < 1 || num_groups < 1)
+        return fail(MX_ERR_INVALID_ARG, "%s: need rows_total >= 0, cols >= 1, num_groups >= 1", fn);
+    if (num_groups > mx::MOE_MAX_EXPERTS)
+        return fail(MX_ERR_UNSUPPORTED, "%s: num_groups=%lld > %d", fn, (long long)num_groups,
+                    mx::MOE_MAX_EXPERTS);
+    if (cols % 32 != 0)
+        return fail(MX_ERR_SHAPE, "%s: cols=%lld is not a multiple of 32", fn, (long long)cols);
+    if (cols % 256 != 0)
+        return fail(MX_ERR_UNSUPPORTED, "%s: cols=%lld: this build needs cols %% 256 == 0", fn, (long long)cols);
+    if (k_cap % 256 != 0 || k_cap < mx_grouped_k_capacity(rows_total, num_groups))
+        return fail(MX_ERR_INVALID_ARG,
+                    "%s: k_cap=%lld must be a multiple of 256 and at least "
+                    "mx_grouped_k_capacity(rows_total, num_groups) = %lld",
+                    fn, (long long)k_cap, (long long)mx_grouped_k_capacity(rows_total, num_groups));
+    if (ld_x < cols || ld_qt < k_cap || ld_q < cols)
+        return fail(MX_ERR_INVALID_ARG, "%s: leading dimension too small (ld_x=%lld ld_q=%lld ld_qt=%lld)", fn,
+                    (long long)ld_x, (long long)ld_q, (long long)ld_qt);
+    if ((!x && rows_total > 0) || (!q && rows_total > 0) || (!s_swz && rows_total > 0) || !group_offsets ||
+        !pad_offsets || !qt || !st_swz)
+        return fail(MX_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!aligned(x, 16) || ld_x % 8 != 0 || !aligned(qt, 16) || ld_qt % 16 != 0 || !aligned(st_swz, 4) ||
+        !aligned(q, 8) || ld_q % 8 != 0 || !aligned(group_offsets, 8) || !aligned(pad_offsets, 8))
+        return fail(MX_ERR_ALIGN,
+                    "%s: x and qt need 16-byte aligned rows (ld_x %% 8, ld_qt %% 16), q 8-byte (ld_q %% 8), "
+                    "st_swz 4 bytes, the offsets 8 bytes",
+                    fn);
+    if (k_cap / 256 * ((cols + 255) / 256) >= ((int64_t)1 << 31))
+        return fail(MX_ERR_UNSUPPORTED, "%s: operand too large for this build", fn);
+    const void *bufs[7] = {x, group_offsets, pad_offsets, qt, st_swz, q, s_swz};
+    const int64_t lens[7] = {rows_total > 0 ? extent(rows_total, cols, ld_x, 2) : 0, (num_groups + 1) * 8,
+                             (num_groups + 1) * 8, extent(cols, k_cap, ld_qt, 1), swz_bytes(cols, k_cap / 32),
+                             extent(rows_total, cols, ld_q, 1), swz_bytes(rows_total, cols / 32)};
+    for (int i = 0; i < 7; i++)
+        for (int k = i + 1; k < 7; k++)
+            if ((i >= 2 || k >= 2) && overlap(bufs[i], lens[i], bufs[k], lens[k]))
+                return fail(MX_ERR_OVERLAP, "%s: buffers %d and %d overlap", fn, i, k);
+    return hip_status(mx::launch_quantize_colwise_grouped(x, rows_total, cols, ld_x, group_offsets, num_groups,
+                                                          pad_offsets, qt, ld_qt, k_cap, st_swz,
+                                                          (hipStream_t)stream, rows_total > 0 ? q : nullptr,
+                                                          ld_q, s_swz),
+                      fn);
+}
+
 mx_status mx_swiglu_quantize(const void *gu, int64_t rows, int64_t F, int64_t ld_gu, void *h, int64_t ld_h,
                              void *q, int64_t ld_q, void *s_swz, void *stream)
 {

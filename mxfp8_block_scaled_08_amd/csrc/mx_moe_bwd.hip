@@ -66,11 +66,18 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void pad_offsets_kernel(const int6
         pad[G] = min(base + incl, k_cap);
 }
 
+// ROW: also the row-wise quantization of the same rows from the same loads
+// (the data gradient's operand): the row-wise blocks of a lane's 16 rows
+// combine over its 4-lane quad as in the dual quantizer; each existing row's
+// 8 codes go to q at the row's own place and its scale byte to the row's
+// place in the rearranged layout (rows of an expert start anywhere, so these
+// are byte stores rather than whole tiles).
+template <bool ROW>
 __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     const int64_t *__restrict__ offsets, const int64_t *__restrict__ pad, int G,
     uint8_t *__restrict__ qt, int64_t ld_qt, uint8_t *__restrict__ st_swz, int64_t st_tiles,
-    int64_t tiles_c)
+    int64_t tiles_c, uint8_t *__restrict__ q, int64_t ld_q, uint8_t *__restrict__ s_swz, int64_t s_tiles)
 {
     __shared__ uint32_t lds_st[8 * 64];
     const int64_t tr = blockIdx.x / tiles_c, tc = blockIdx.x - tr * tiles_c;
@@ -121,6 +128,31 @@ __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
 #pragma unroll
     for (int k = 0; k < 4; k++)  // row_ror:8 - the other half of the column block
         m[k] = pk_max_u16(m[k], (uint32_t)__builtin_amdgcn_mov_dpp((int)m[k], 0x128, 0xF, 0xF, false));
+    if (ROW) {
+        // row-wise: the lane's 8 columns of each row, then its quad (the
+        // 32-column block), quad_perm [1,0,3,2] and [2,3,0,1]
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const uint32_t w = pk_max_u16(pk_max_u16(mag2(v[i].x), mag2(v[i].y)),
+                                          pk_max_u16(mag2(v[i].z), mag2(v[i].w)));
+            uint32_t a = max(w & 0xFFFFu, w >> 16);
+            a = max(a, (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0xB1, 0xF, 0xF, false));
+            a = max(a, (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0x4E, 0xF, 0xF, false));
+            if (active && rl0 + i < valid) {
+                const uint32_t c = scale_code(a);
+                const float sc = cvt_scale(c);
+                const int64_t row = src0 + rl0 + i;
+                const uint32_t o0 = nan_block_select(cvt_x4(v[i].x, v[i].y, sc), c);
+                const uint32_t o1 = nan_block_select(cvt_x4(v[i].z, v[i].w, sc), c);
+                *reinterpret_cast<uint2 *>(q + row * ld_q + c0) = make_uint2(o0, o1);
+                if ((cg & 3) == 0) {
+                    const int64_t b = c0 >> 5;  // 32-column block of the row
+                    s_swz[((row >> 5) * s_tiles + (b >> 3)) * 256 + (32 * (b & 1) + (row & 31)) * 4 +
+                          ((b & 7) >> 1)] = (uint8_t)c;
+                }
+            }
+        }
+    }
     __syncthreads();  // the 0x7F fill precedes every scale byte
     uint8_t *bst = reinterpret_cast<uint8_t *>(lds_st);
     if (active) {
@@ -161,7 +193,7 @@ __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
 hipError_t launch_quantize_colwise_grouped(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
                                           const int64_t *offsets, int64_t G, int64_t *pad,
                                           void *qt, int64_t ld_qt, int64_t k_cap, void *st_swz,
-                                          hipStream_t stream)
+                                          hipStream_t stream, void *q, int64_t ld_q, void *s_swz)
 {
     hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, stream, offsets, (int)G,
                        rows, k_cap, pad);
@@ -173,9 +205,16 @@ hipError_t launch_quantize_colwise_grouped(const void *x, int64_t rows, int64_t 
     const int64_t blocks = tiles_r * tiles_c;
     if (blocks == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(quantize_colwise_grouped_kernel, dim3((unsigned)blocks), dim3(QG_THREADS), 0, stream,
-                       (const uint16_t *)x, rows, cols, ld_x, offsets, (const int64_t *)pad, (int)G,
-                       (uint8_t *)qt, ld_qt, (uint8_t *)st_swz, k_cap / QG_TILE, tiles_c);
+    if (q != nullptr)
+        hipLaunchKernelGGL((quantize_colwise_grouped_kernel<true>), dim3((unsigned)blocks), dim3(QG_THREADS), 0,
+                           stream, (const uint16_t *)x, rows, cols, ld_x, offsets, (const int64_t *)pad, (int)G,
+                           (uint8_t *)qt, ld_qt, (uint8_t *)st_swz, k_cap / QG_TILE, tiles_c, (uint8_t *)q, ld_q,
+                           (uint8_t *)s_swz, cols / 256);
+    else
+        hipLaunchKernelGGL((quantize_colwise_grouped_kernel<false>), dim3((unsigned)blocks), dim3(QG_THREADS), 0,
+                           stream, (const uint16_t *)x, rows, cols, ld_x, offsets, (const int64_t *)pad, (int)G,
+                           (uint8_t *)qt, ld_qt, (uint8_t *)st_swz, k_cap / QG_TILE, tiles_c, nullptr,
+                           (int64_t)0, nullptr, (int64_t)0);
     return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for n in names:
         assert hasattr(raw, n), f"{n} declared in include/mxfp8.h but not exported"
         assert hasattr(mx, n), f"{n} has no Python binding of the same name"
-    assert L.mx_abi_version() == 5
+    assert L.mx_abi_version() == 6
 
 
 def test_status_strings():
@@ -324,3 +324,21 @@ def test_quantize_rowwise_swz_validation():
     assert f(FAKE, 64, 512, 512, FAKE + 1024, 512, FAKE3, 2, STREAM) == mx.MX_ERR_OVERLAP
     assert f(0, 64, 512, 512, FAKE2, 512, FAKE3, 2, STREAM) == mx.MX_ERR_INVALID_ARG
     assert f(FAKE, 0, 512, 512, FAKE2, 512, FAKE3, 2, STREAM) == mx.MX_OK
+
+
+def test_quantize_dual_grouped_validation():
+    L = mx.load()
+    f = L.mx_quantize_dual_grouped
+    cap = L.mx_grouped_k_capacity(1000, 4)
+    # x, rows, cols, ld_x, offsets, G, pad, q, ld_q, s_swz, qt, ld_qt, k_cap, st_swz
+    base = dict(x=FAKE, rows=1000, cols=256, ld_x=256, off=FAKE2, G=4, pad=FAKE2 + 4096, q=FAKE3,
+                ld_q=256, s=FAKE3 + (1 << 24), qt=FAKE4, ld_qt=cap, k_cap=cap, st=FAKE4 + (1 << 24))
+    order = ["x", "rows", "cols", "ld_x", "off", "G", "pad", "q", "ld_q", "s", "qt", "ld_qt", "k_cap", "st"]
+    call = lambda **kw: f(*[kw.get(k, base[k]) for k in order], STREAM)
+    assert call(cols=288, ld_x=288, ld_q=288) == mx.MX_ERR_UNSUPPORTED
+    assert call(cols=48, ld_x=48, ld_q=48) == mx.MX_ERR_SHAPE
+    assert call(ld_q=128) == mx.MX_ERR_INVALID_ARG
+    assert call(q=0) == mx.MX_ERR_INVALID_ARG
+    assert call(q=FAKE3 + 4) == mx.MX_ERR_ALIGN
+    assert call(s=FAKE3 + 1000) == mx.MX_ERR_OVERLAP        # row-wise scales inside the codes
+    assert call(k_cap=cap - 256, ld_qt=cap) == mx.MX_ERR_INVALID_ARG

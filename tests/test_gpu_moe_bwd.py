@@ -201,7 +201,8 @@ def test_moe_backward_qwen3_30b_a3b(gpu_lib):
         got = C[torch.from_numpy(gs).cuda(), torch.from_numpy(rs).cuda(), torch.from_numpy(cs).cuda()]
         st = assert_gemm_close(got[None, :], GemmRef(ref[None], bnd[None], hw[None]), f"{name} wgrad")
         print(f"moe bwd {name} wgrad: {st['within_stated']}/{st['n']} within the stated bar", flush=True)
-        del C, qa, sa, qb, sb, oqa, oqb
+        oqa_dy, oswz_dy = oqa, oracle.scale_swizzle(osa)
+        del C, qa, sa, qb, sb, oqb
 
         # data gradient: dX = dY . W_g, B = column-wise W_g ([Kin][Nout] per expert)
         print(f"moe bwd {name}: dgrad", flush=True)
@@ -216,18 +217,27 @@ def test_moe_backward_qwen3_30b_a3b(gpu_lib):
         oswz = np.concatenate([oracle.scale_swizzle(owst[g]) for g in range(G)])
         assert np.array_equal(wst_swz.cpu().numpy(), oswz), f"{name}: expert weight scales differ"
         assert wst_swz.numel() == G * stb
-        dq, ds = mx.mx_quantize_rowwise(dy.cuda())
+        # dY row-wise and per-expert column-wise from one read
+        dq, ds_swz, dqt, dst_swz, dpad = mx.mx_quantize_dual_grouped(dy.cuda(), offd)
         odq, ods = mxsynth_rowwise(dy)
-        assert np.array_equal(dq.cpu().numpy(), odq) and np.array_equal(ds.cpu().numpy(), ods)
-        D = mx.mx_grouped_gemm(offd, dq, mx.mx_scale_swizzle(ds), wqt, wst_swz,
-                               out_dtype=torch.bfloat16)
+        assert np.array_equal(dq.cpu().numpy(), odq), f"{name}: dual grouped row-wise codes differ"
+        assert np.array_equal(ds_swz.cpu().numpy(), oracle.scale_swizzle(ods))
+        assert np.array_equal(dpad.cpu().numpy(), opad)
+        pend = int(opad[-1])
+        assert np.array_equal(dqt.cpu().numpy()[:, :pend], oqa_dy[:, :pend]), \
+            f"{name}: dual grouped column-wise codes differ"
+        KT = dqt.shape[1] // 256
+        assert np.array_equal(dst_swz.cpu().numpy().reshape(-1, KT, 256)[:, :pend // 256],
+                              oswz_dy.reshape(-1, KT, 256)[:, :pend // 256])
+        del dqt, dst_swz
+        D = mx.mx_grouped_gemm(offd, dq, ds_swz, wqt, wst_swz, out_dtype=torch.bfloat16)
         firsts = off[:-1][rows_per > 0]
         lasts = off[1:][rows_per > 0] - 1
         rows = np.concatenate([firsts, lasts, rng.integers(0, int(off[-1]), 1024)])
         cols = rng.integers(0, Kin, rows.size)
         st = check_sampled_grouped(D, rows, cols, off, odq, ods, owqt, owst, f"{name} dgrad")
         print(f"moe bwd {name} dgrad: {st['within_stated']}/{st['n']} within the stated bar", flush=True)
-        del D, dq, ds, wqt, wst_swz
+        del D, dq, ds_swz, wqt, wst_swz, oqa_dy, oswz_dy
 
 
 def mxsynth_rowwise(x):
@@ -267,3 +277,27 @@ def test_offsets_outside_the_stated_properties_stay_in_bounds(gpu_lib):
     torch.cuda.synchronize()
     assert torch.isfinite(c).all()
     assert (c_buf[G * cols * cols:] == 7.0).all()
+
+
+@pytest.mark.parametrize("sizes,cols", [([37], 256), ([0, 37, 256, 300, 5], 512), ([513, 0, 255, 1, 31], 768)])
+def test_dual_grouped_matches_oracle(gpu_lib, sizes, cols):
+    """Row-wise (every row, scales rearranged) and per-expert column-wise
+    quantization from one read: each output equals its oracle."""
+    mx = gpu_lib
+    off = _offsets(sizes)
+    rows = int(off[-1])
+    x = mxsynth.normal_bf16((rows, cols), 1.0, seed=600 + rows, outlier_frac=0.01)
+    xb = mxsynth.bits(x)
+    q, s_swz, qt, st_swz, pad = mx.mx_quantize_dual_grouped(x.cuda(), torch.from_numpy(off).cuda())
+    torch.cuda.synchronize()
+    oq, os_ = oracle.quantize_rowwise(xb)
+    assert np.array_equal(q.cpu().numpy(), oq)
+    assert np.array_equal(oracle.scale_unswizzle(s_swz.cpu().numpy(), rows, cols // 32), os_)
+    k_cap = qt.shape[1]
+    oqt, ost, opad = oracle.quantize_colwise_grouped(xb, off, k_cap)
+    assert np.array_equal(pad.cpu().numpy(), opad)
+    pend = int(opad[-1])
+    assert np.array_equal(qt.cpu().numpy()[:, :pend], oqt[:, :pend])
+    KT = k_cap // 256
+    assert np.array_equal(st_swz.cpu().numpy().reshape(-1, KT, 256)[:, :pend // 256],
+                          oracle.scale_swizzle(ost).reshape(-1, KT, 256)[:, :pend // 256])
