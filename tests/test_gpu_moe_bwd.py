@@ -79,7 +79,7 @@ def _check_grouped_quant(mx, x, off, what, sentinel=True):
 ])
 def test_colwise_grouped_matches_oracle(gpu_lib, sizes, cols):
     off = _offsets(sizes)
-    x = mxsynth.normal_bf16((int(off[-1]), cols), 1.0, seed=100 + len(sizes), outlier_frac=0.01)
+    x = mxsynth.normal_bf16((int(off[-1]), cols), 1.0, seed=100 + len(sizes), outlier_frac=0.01, outlier_mul=100.0)
     _check_grouped_quant(gpu_lib, x, off, f"sizes={sizes} cols={cols}")
 
 
@@ -118,8 +118,8 @@ def test_wgrad_matches_oracle(gpu_lib, sizes, M, N, dtype):
     mx = gpu_lib
     off = _offsets(sizes)
     T = int(off[-1])
-    dy = mxsynth.normal_bf16((T, M), 1e-3, seed=200 + M, outlier_frac=0.01)
-    x = mxsynth.normal_bf16((T, N), 1.0, seed=300 + N, outlier_frac=0.01)
+    dy = mxsynth.normal_bf16((T, M), 1e-3, seed=200 + M, outlier_frac=0.01, outlier_mul=100.0)
+    x = mxsynth.normal_bf16((T, N), 1.0, seed=300 + N, outlier_frac=0.01, outlier_mul=100.0)
     qa, sa_swz, pad, oqa, osa, opad = _check_grouped_quant(mx, dy, off, "dY", sentinel=False)
     qb, sb_swz, _, oqb, osb, _ = _check_grouped_quant(mx, x, off, "X", sentinel=False)
     C = mx.mx_grouped_gemm_wgrad(pad, qa, sa_swz, qb, sb_swz, out_dtype=dtype)
@@ -286,7 +286,7 @@ def test_dual_grouped_matches_oracle(gpu_lib, sizes, cols):
     mx = gpu_lib
     off = _offsets(sizes)
     rows = int(off[-1])
-    x = mxsynth.normal_bf16((rows, cols), 1.0, seed=600 + rows, outlier_frac=0.01)
+    x = mxsynth.normal_bf16((rows, cols), 1.0, seed=600 + rows, outlier_frac=0.01, outlier_mul=100.0)
     xb = mxsynth.bits(x)
     q, s_swz, qt, st_swz, pad = mx.mx_quantize_dual_grouped(x.cuda(), torch.from_numpy(off).cuda())
     torch.cuda.synchronize()

@@ -229,7 +229,7 @@ def test_rowwise_swz_matches_oracle(gpu_lib, rows, cols):
     padding the call does not write)."""
     import mxsynth
     mx = gpu_lib
-    x = mxsynth.normal_bf16((rows, cols), 1.0, seed=rows + cols, outlier_frac=0.005)
+    x = mxsynth.normal_bf16((rows, cols), 1.0, seed=rows + cols, outlier_frac=0.005, outlier_mul=50.0)
     xb = mxsynth.bits(x)
     q, s_swz = mx.mx_quantize_rowwise_swz(x.cuda())
     torch.cuda.synchronize()

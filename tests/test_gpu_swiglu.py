@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _gu(rows, F, seed):
-    g = mxsynth.normal_bf16((rows, 2 * F), 1.0, seed=seed, outlier_frac=0.01)
+    g = mxsynth.normal_bf16((rows, 2 * F), 1.0, seed=seed, outlier_frac=0.01, outlier_mul=100.0)
     b = mxsynth.bits(g).copy()
     if rows and F:
         rng = np.random.default_rng(seed)
