@@ -214,7 +214,7 @@ def build_workload(mx, torch, mxsynth):
 def step(mx, I, o, T):
     """One pass of the hot path; T(category, fn, ...) times each launch."""
     W = I["W"]
-    rq, cq, sw = mx.mx_quantize_rowwise, mx.mx_quantize_colwise, mx.mx_scale_swizzle
+    cq, sw = mx.mx_quantize_colwise, mx.mx_scale_swizzle
     # 1. weight sync: both orientations of every weight in one pass each, the
     #    row-wise codes into the fused forward operands (q, k, v stacked; gate,
     #    up stacked) and the column-wise ones into the backward operands (gate
