@@ -457,9 +457,9 @@ mx_status mx_quantize_colwise_grouped(const void *x, int64_t rows_total, int64_t
  *          [rows_total][cols/32] scale tensor (the padding rows of the last
  *          32-row tile are not written)
  * Requirements: those of mx_quantize_colwise_grouped, plus cols % 256 == 0
- * (else MX_ERR_UNSUPPORTED), ld_q >= cols (else MX_ERR_INVALID_ARG), q 8-byte
- * aligned rows with ld_q % 8 == 0 (else MX_ERR_ALIGN), q and s_swz overlap
- * nothing (else MX_ERR_OVERLAP).
+ * (else MX_ERR_UNSUPPORTED), ld_q >= cols (else MX_ERR_INVALID_ARG), q
+ * 16-byte aligned rows with ld_q % 16 == 0 and s_swz 4-byte aligned (else
+ * MX_ERR_ALIGN), q and s_swz overlap nothing (else MX_ERR_OVERLAP).
  */
 mx_status mx_quantize_dual_grouped(const void *x, int64_t rows_total, int64_t cols, int64_t ld_x,
                                    const int64_t *group_offsets, int64_t num_groups, int64_t *pad_offsets,

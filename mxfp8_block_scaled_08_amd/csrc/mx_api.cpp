@@ -450,10 +450,11 @@ mx_status mx_quantize_dual_grouped(const void *x, int64_t rows_total, int64_t co
         !pad_offsets || !qt || !st_swz)
         return fail(MX_ERR_INVALID_ARG, "%s: null pointer", fn);
     if (!aligned(x, 16) || ld_x % 8 != 0 || !aligned(qt, 16) || ld_qt % 16 != 0 || !aligned(st_swz, 4) ||
-        !aligned(q, 8) || ld_q % 8 != 0 || !aligned(group_offsets, 8) || !aligned(pad_offsets, 8))
+        !aligned(q, 16) || ld_q % 16 != 0 || !aligned(s_swz, 4) || !aligned(group_offsets, 8) ||
+        !aligned(pad_offsets, 8))
         return fail(MX_ERR_ALIGN,
-                    "%s: x and qt need 16-byte aligned rows (ld_x %% 8, ld_qt %% 16), q 8-byte (ld_q %% 8), "
-                    "st_swz 4 bytes, the offsets 8 bytes",
+                    "%s: x, q and qt need 16-byte aligned rows (ld_x %% 8, ld_q %% 16, ld_qt %% 16), "
+                    "s_swz and st_swz 4 bytes, the offsets 8 bytes",
                     fn);
     if (k_cap / 256 * ((cols + 255) / 256) >= ((int64_t)1 << 31))
         return fail(MX_ERR_UNSUPPORTED, "%s: operand too large for this build", fn);

@@ -68,10 +68,12 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void pad_offsets_kernel(const int6
 
 // ROW: also the row-wise quantization of the same rows from the same loads
 // (the data gradient's operand): the row-wise blocks of a lane's 16 rows
-// combine over its 4-lane quad as in the dual quantizer; each existing row's
-// 8 codes go to q at the row's own place and its scale byte to the row's
-// place in the rearranged layout (rows of an expert start anywhere, so these
-// are byte stores rather than whole tiles).
+// combine over its 4-lane quad as in the dual quantizer.  The codes and
+// scale bytes are staged in LDS, then written row by row: sixteen threads
+// store a row's 256 codes as two whole 128-byte lines, and one thread a
+// row's eight scale bytes as the two 4-byte words they form in the
+// rearranged layout (rows of an expert start anywhere, so a row's scales do
+// not fill whole tiles).
 template <bool ROW>
 __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
@@ -80,6 +82,8 @@ __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
     int64_t tiles_c, uint8_t *__restrict__ q, int64_t ld_q, uint8_t *__restrict__ s_swz, int64_t s_tiles)
 {
     __shared__ uint32_t lds_st[8 * 64];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_q[ROW ? QG_TILE * QG_TILE : 1];  // row-wise codes
+    __shared__ uint8_t lds_rs[ROW ? QG_TILE * 8 : 1];  // row-wise scale bytes, 8 per row
     const int64_t tr = blockIdx.x / tiles_c, tc = blockIdx.x - tr * tiles_c;
     const int64_t P0 = tr * QG_TILE;  // first padded column (row of the padded operand)
     // The expert whose range holds P0 is the last g with pad[g] <= P0; the
@@ -141,15 +145,12 @@ __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
             if (active && rl0 + i < valid) {
                 const uint32_t c = scale_code(a);
                 const float sc = cvt_scale(c);
-                const int64_t row = src0 + rl0 + i;
                 const uint32_t o0 = nan_block_select(cvt_x4(v[i].x, v[i].y, sc), c);
                 const uint32_t o1 = nan_block_select(cvt_x4(v[i].z, v[i].w, sc), c);
-                *reinterpret_cast<uint2 *>(q + row * ld_q + c0) = make_uint2(o0, o1);
-                if ((cg & 3) == 0) {
-                    const int64_t b = c0 >> 5;  // 32-column block of the row
-                    s_swz[((row >> 5) * s_tiles + (b >> 3)) * 256 + (32 * (b & 1) + (row & 31)) * 4 +
-                          ((b & 7) >> 1)] = (uint8_t)c;
-                }
+                const int cl = wc * 64 + cg * 8;  // the lane's first column within the tile
+                *reinterpret_cast<uint2 *>(&lds_q[(rl0 + i) * QG_TILE + cl]) = make_uint2(o0, o1);
+                if ((cg & 3) == 0)
+                    lds_rs[(rl0 + i) * 8 + (cl >> 5)] = (uint8_t)c;
             }
         }
     }
@@ -184,6 +185,29 @@ __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
         }
     }
     __syncthreads();
+    if (ROW) {
+        // codes: 16 threads per row, 16 bytes each (cols % 256 == 0 here, so
+        // every row of the tile has its 256 columns)
+#pragma unroll
+        for (int k = 0; k < QG_TILE * QG_TILE / 16 / QG_THREADS; k++) {
+            const int idx = tid + k * QG_THREADS;
+            const int r = idx >> 4, ch = idx & 15;
+            if (r < valid)
+                *reinterpret_cast<uint4 *>(q + (src0 + r) * ld_q + C0 + ch * 16) =
+                    *reinterpret_cast<const uint4 *>(&lds_q[r * QG_TILE + ch * 16]);
+        }
+        // scales: blocks 2t + h of the row go to byte t of word h
+        if (tid < QG_TILE && tid < valid) {
+            const int r = tid;
+            const int64_t row = src0 + r;
+            const uint8_t *b = &lds_rs[r * 8];
+            const uint32_t w0 = b[0] | (b[2] << 8) | (b[4] << 16) | ((uint32_t)b[6] << 24);
+            const uint32_t w1 = b[1] | (b[3] << 8) | (b[5] << 16) | ((uint32_t)b[7] << 24);
+            uint32_t *tile = reinterpret_cast<uint32_t *>(s_swz + ((row >> 5) * s_tiles + C0 / 256) * 256);
+            tile[row & 31] = w0;
+            tile[32 + (row & 31)] = w1;
+        }
+    }
     // thread -> word tid & 63 of the rearranged tile of 32-column row tid >> 6
     const int t = tid >> 6, w = tid & 63;
     if (C0 + 32 * t < cols)

@@ -339,6 +339,8 @@ def test_quantize_dual_grouped_validation():
     assert call(cols=48, ld_x=48, ld_q=48) == mx.MX_ERR_SHAPE
     assert call(ld_q=128) == mx.MX_ERR_INVALID_ARG
     assert call(q=0) == mx.MX_ERR_INVALID_ARG
-    assert call(q=FAKE3 + 4) == mx.MX_ERR_ALIGN
+    assert call(q=FAKE3 + 8) == mx.MX_ERR_ALIGN
+    assert call(ld_q=264) == mx.MX_ERR_ALIGN
+    assert call(s=FAKE3 + (1 << 24) + 2) == mx.MX_ERR_ALIGN
     assert call(s=FAKE3 + 1000) == mx.MX_ERR_OVERLAP        # row-wise scales inside the codes
     assert call(k_cap=cap - 256, ld_qt=cap) == mx.MX_ERR_INVALID_ARG
