@@ -29,7 +29,13 @@
  * over all 256 E4M3 codes, exhaustive scale-rule check over every BF16 amax,
  * hand-derived golden blocks, exact rational GEMM on tiny inputs, closed
  * forms, and the invariants the pages rely on (power-of-two scales,
- * byte-for-byte determinism, idempotent re-quantization).
+ * byte-for-byte determinism, idempotent re-quantization).  The MoE pieces
+ * (tests/test_oracle_moe_pins.py, test_oracle_moe_bwd_pins.py,
+ * test_oracle_swiglu_pins.py): dispatch order against a loop definition,
+ * combine by exact special cases, the per-expert column-wise layout against
+ * an element loop and a planted straddling block, the per-expert weight
+ * gradient by exact rational sums and the unquantized product, the double ->
+ * BF16 rounding by brute-force nearest search, silu by closed forms.
  */
 #include <math.h>
 #include <stddef.h>
