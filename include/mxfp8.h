@@ -483,7 +483,8 @@ mx_status mx_quantize_dual_grouped(const void *x, int64_t rows_total, int64_t co
  * dealt longest range first over persistent workgroups.
  * Requirements: those of mx_gemm with K = k_cap, plus k_cap % 256 == 0 (else
  * MX_ERR_SHAPE), num_groups in 1..1024 (else MX_ERR_INVALID_ARG /
- * MX_ERR_UNSUPPORTED); C overlaps no input (else MX_ERR_OVERLAP).
+ * MX_ERR_UNSUPPORTED), fewer than 2^31 256x256 output tiles over all groups
+ * (else MX_ERR_UNSUPPORTED); C overlaps no input (else MX_ERR_OVERLAP).
  */
 mx_status mx_grouped_gemm_wgrad(int64_t num_groups, int64_t M, int64_t N, int64_t k_cap,
                                 const int64_t *k_offsets, const void *a_q, int64_t ld_a,

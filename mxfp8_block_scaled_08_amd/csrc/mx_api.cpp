@@ -680,6 +680,8 @@ mx_status mx_grouped_gemm_wgrad(int64_t num_groups, int64_t M, int64_t N, int64_
     const int64_t ce = c_dtype == MX_BF16 ? 2 : 4;
     if ((num_groups * M) * ld_c >= ((int64_t)1 << 62) / ce)
         return fail(MX_ERR_UNSUPPORTED, "%s: C too large", fn);
+    if (num_groups * ((M + 255) / 256) * ((N + 255) / 256) >= ((int64_t)1 << 31))
+        return fail(MX_ERR_UNSUPPORTED, "%s: more than 2^31 - 1 output tiles", fn);
     const int64_t ec = extent(num_groups * M, N, ld_c, ce);
     if (overlap(c, ec, a_q, extent(M, k_cap, ld_a, 1)) || overlap(c, ec, b_q, extent(N, k_cap, ld_b, 1)) ||
         overlap(c, ec, a_s_swz, swz_bytes(M, k_cap / 32)) || overlap(c, ec, b_s_swz, swz_bytes(N, k_cap / 32)) ||

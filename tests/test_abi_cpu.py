@@ -271,6 +271,11 @@ def test_grouped_gemm_wgrad_validation():
     assert f(*args(c=FAKE2 + 4096)) == mx.MX_ERR_OVERLAP
     # C (4 experts x 256 rows) reaching the offsets
     assert f(*args(off=FAKE4 + 1000)) == mx.MX_ERR_OVERLAP
+    # 2^31 output tiles (1024 experts x 2048 x 1024 tiles): the tile numbers
+    # must fit the kernel's 32-bit tile counter
+    assert f(*args(G=1024, M=1 << 19, N=1 << 18, ld_c=1 << 18, K=256, ld_a=256, ld_b=256)) == \
+        mx.MX_ERR_UNSUPPORTED
+    assert "tiles" in _err(L)
     # empty products succeed without a launch
     assert f(*args(M=0)) == mx.MX_OK
 
