@@ -435,9 +435,10 @@ mx_status mx_grouped_gemm(int64_t num_groups, int64_t M_total, int64_t N, int64_
  * ld_qt >= k_cap (else MX_ERR_INVALID_ARG; x may be null when rows_total is
  * 0); x and qt 16-byte aligned rows
  * (ld_x % 8, ld_qt % 16), st_swz 4 bytes, the offsets 8 bytes (else
- * MX_ERR_ALIGN); outputs overlap nothing (else MX_ERR_OVERLAP).  Offsets
- * that are not nondecreasing within [0, rows_total] are clamped into it
- * (unspecified but in-bounds results).
+ * MX_ERR_ALIGN); ld_x < 2^22 and ld_qt < 2^24 (32-bit offsets within a
+ * 256-row tile; else MX_ERR_UNSUPPORTED); outputs overlap nothing (else
+ * MX_ERR_OVERLAP).  Offsets that are not nondecreasing within
+ * [0, rows_total] are clamped into it (unspecified but in-bounds results).
  */
 int64_t mx_grouped_k_capacity(int64_t rows_total, int64_t num_groups);
 mx_status mx_quantize_colwise_grouped(const void *x, int64_t rows_total, int64_t cols, int64_t ld_x,
@@ -457,7 +458,8 @@ mx_status mx_quantize_colwise_grouped(const void *x, int64_t rows_total, int64_t
  *          [rows_total][cols/32] scale tensor (the padding rows of the last
  *          32-row tile are not written)
  * Requirements: those of mx_quantize_colwise_grouped, plus cols % 256 == 0
- * (else MX_ERR_UNSUPPORTED), ld_q >= cols (else MX_ERR_INVALID_ARG), q
+ * and ld_q < 2^24 (else MX_ERR_UNSUPPORTED), ld_q >= cols (else
+ * MX_ERR_INVALID_ARG), q
  * 16-byte aligned rows with ld_q % 16 == 0 and s_swz 4-byte aligned (else
  * MX_ERR_ALIGN), q and s_swz overlap nothing (else MX_ERR_OVERLAP).
  */

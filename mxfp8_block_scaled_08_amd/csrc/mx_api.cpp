@@ -408,8 +408,9 @@ mx_status mx_quantize_colwise_grouped(const void *x, int64_t rows_total, int64_t
                     "%s: x and qt need 16-byte aligned rows (ld_x %% 8, ld_qt %% 16), st_swz 4 bytes, "
                     "the offsets 8 bytes",
                     fn);
-    if (k_cap / 256 * ((cols + 255) / 256) >= ((int64_t)1 << 31))
-        return fail(MX_ERR_UNSUPPORTED, "%s: operand too large for this build", fn);
+    if (k_cap / 256 * ((cols + 255) / 256) >= ((int64_t)1 << 31) || ld_x >= ((int64_t)1 << 22) ||
+        ld_qt >= ((int64_t)1 << 24))
+        return fail(MX_ERR_UNSUPPORTED, "%s: operand too large for this build (ld_x < 2^22, ld_qt < 2^24)", fn);
     const void *bufs[5] = {x, group_offsets, pad_offsets, qt, st_swz};
     const int64_t lens[5] = {rows_total > 0 ? extent(rows_total, cols, ld_x, 2) : 0, (num_groups + 1) * 8,
                              (num_groups + 1) * 8, extent(cols, k_cap, ld_qt, 1), swz_bytes(cols, k_cap / 32)};
@@ -456,8 +457,10 @@ mx_status mx_quantize_dual_grouped(const void *x, int64_t rows_total, int64_t co
                     "%s: x, q and qt need 16-byte aligned rows (ld_x %% 8, ld_q %% 16, ld_qt %% 16), "
                     "s_swz and st_swz 4 bytes, the offsets 8 bytes",
                     fn);
-    if (k_cap / 256 * ((cols + 255) / 256) >= ((int64_t)1 << 31))
-        return fail(MX_ERR_UNSUPPORTED, "%s: operand too large for this build", fn);
+    if (k_cap / 256 * ((cols + 255) / 256) >= ((int64_t)1 << 31) || ld_x >= ((int64_t)1 << 22) ||
+        ld_qt >= ((int64_t)1 << 24) || ld_q >= ((int64_t)1 << 24))
+        return fail(MX_ERR_UNSUPPORTED,
+                    "%s: operand too large for this build (ld_x < 2^22, ld_q and ld_qt < 2^24)", fn);
     const void *bufs[7] = {x, group_offsets, pad_offsets, qt, st_swz, q, s_swz};
     const int64_t lens[7] = {rows_total > 0 ? extent(rows_total, cols, ld_x, 2) : 0, (num_groups + 1) * 8,
                              (num_groups + 1) * 8, extent(cols, k_cap, ld_qt, 1), swz_bytes(cols, k_cap / 32),

@@ -23,17 +23,35 @@
 // column-wise lane layout of the dual quantizer (lane = 32-row block, half,
 // 8-column group; 16 rows x 8 columns per lane; the halves of a block meet
 // through one DPP rotation; v_perm pairs two rows of a column for the scaled
-// conversion).  A lane loads only the rows that exist in its expert (the
-// others are zero) and stores 16 codes of each of its 8 columns.  The scale
-// bytes go to LDS at their rearranged positions, and each thread stores one
-// word: 8 whole 256-byte tiles of the rearranged layout per workgroup.
+// conversion).  The tile's rows of x are one buffer range, [first row, first
+// row + valid rows), so the loads of rows past the expert's last read zero
+// without a per-row test; a lane stores 16 codes of each of its 8 columns.
+// The scale bytes go to LDS at their rearranged positions, and each thread
+// stores one word: 8 whole 256-byte tiles of the rearranged layout per
+// workgroup.  Registers: the 16 rows a lane holds take 64 VGPRs, and each
+// magnitude feeds the column-wise and the row-wise maxima in the same pass
+// (computed in two passes, all 64 magnitudes stayed live and the row-wise
+// variant needed 147 VGPRs: one workgroup per CU instead of two).
 #include "mx_device.h"
 #include "mx_launch.h"
 
 namespace mx {
 
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
 constexpr int QG_THREADS = 512;
 constexpr int QG_TILE = 256;
+
+// Buffer resource over a byte range (base and size uniform): per-lane 32-bit
+// offsets, and accesses outside [0, bytes) read zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void *base, uint32_t bytes)
+{
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    void *ub = (void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, 0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
 
 __global__ __launch_bounds__(MOE_MAX_EXPERTS) void pad_offsets_kernel(const int64_t *__restrict__ offsets,
                                                                       int G, int64_t rows, int64_t k_cap,
@@ -113,49 +131,53 @@ __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
     // are those of its DPP partner (the other half of its block)
     const bool active = c0 < cols;
     lds_st[tid] = 0x7F7F7F7Fu;
+    // the tile's rows of x, [src0, src0 + valid), as one buffer range: loads
+    // of rows past it (the next expert's, or past x) and of inactive lanes
+    // (offset 2^31, past any range: 256 ld_x * 2 < 2^31) read zero
+    const __amdgpu_buffer_rsrc_t rx = byte_range(x + (valid > 0 ? src0 * ld_x : 0), (uint32_t)(valid * ld_x * 2));
+    const uint32_t voff = active ? (uint32_t)(rl0 * ld_x + c0) * 2u : 0x80000000u;
+    const uint32_t vstep = active ? (uint32_t)ld_x * 2u : 0u;
     uint4 v[16];
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-        if (active && rl0 + i < valid)
-            v[i] = *reinterpret_cast<const uint4 *>(x + (src0 + rl0 + i) * ld_x + c0);
-        else
-            v[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
+    for (int i = 0; i < 16; i++)
+        v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff + i * vstep, 0, 0));
+    // column-wise maxima (per column, the lane's 16 rows) and, with ROW, the
+    // row-wise ones (per row, the lane's 8 columns) in one pass, each
+    // magnitude used by both as soon as it is formed
     uint32_t m[4] = {0, 0, 0, 0};
+    uint32_t rmax[ROW ? 16 : 1];
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-        m[0] = pk_max_u16(m[0], mag2(v[i].x));
-        m[1] = pk_max_u16(m[1], mag2(v[i].y));
-        m[2] = pk_max_u16(m[2], mag2(v[i].z));
-        m[3] = pk_max_u16(m[3], mag2(v[i].w));
+        const uint32_t ax = mag2(v[i].x), ay = mag2(v[i].y), az = mag2(v[i].z), aw = mag2(v[i].w);
+        m[0] = pk_max_u16(m[0], ax);
+        m[1] = pk_max_u16(m[1], ay);
+        m[2] = pk_max_u16(m[2], az);
+        m[3] = pk_max_u16(m[3], aw);
+        if (ROW) {
+            const uint32_t w = pk_max_u16(pk_max_u16(ax, ay), pk_max_u16(az, aw));
+            rmax[i] = max(w & 0xFFFFu, w >> 16);
+        }
     }
 #pragma unroll
     for (int k = 0; k < 4; k++)  // row_ror:8 - the other half of the column block
         m[k] = pk_max_u16(m[k], (uint32_t)__builtin_amdgcn_mov_dpp((int)m[k], 0x128, 0xF, 0xF, false));
     if (ROW) {
-        // row-wise: the lane's 8 columns of each row, then its quad (the
-        // 32-column block), quad_perm [1,0,3,2] and [2,3,0,1]
+        // the row's 32-column block is the lane's quad: quad_perm [1,0,3,2]
+        // and [2,3,0,1]
 #pragma unroll
         for (int i = 0; i < 16; i++) {
-            const uint32_t w = pk_max_u16(pk_max_u16(mag2(v[i].x), mag2(v[i].y)),
-                                          pk_max_u16(mag2(v[i].z), mag2(v[i].w)));
-            uint32_t a = max(w & 0xFFFFu, w >> 16);
+            uint32_t a = rmax[i];
             a = max(a, (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0xB1, 0xF, 0xF, false));
             a = max(a, (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0x4E, 0xF, 0xF, false));
-            if (active && rl0 + i < valid) {
-                const uint32_t c = scale_code(a);
-                const float sc = cvt_scale(c);
-                const uint32_t o0 = nan_block_select(cvt_x4(v[i].x, v[i].y, sc), c);
-                const uint32_t o1 = nan_block_select(cvt_x4(v[i].z, v[i].w, sc), c);
-                const int cl = wc * 64 + cg * 8;  // the lane's first column within the tile
-                *reinterpret_cast<uint2 *>(&lds_q[(rl0 + i) * QG_TILE + cl]) = make_uint2(o0, o1);
-                if ((cg & 3) == 0)
-                    lds_rs[(rl0 + i) * 8 + (cl >> 5)] = (uint8_t)c;
-            }
+            rmax[i] = a;
         }
     }
     __syncthreads();  // the 0x7F fill precedes every scale byte
     uint8_t *bst = reinterpret_cast<uint8_t *>(lds_st);
+    // the tile's 256 rows of qt from column P0 (256 ld_qt < 2^32): lane
+    // offset of its first row, column j's row j ld_qt further
+    const __amdgpu_buffer_rsrc_t rq = byte_range(qt + C0 * ld_qt + P0, (uint32_t)(QG_TILE * ld_qt));
+    const uint32_t qoff = (uint32_t)((wc * 64 + cg * 8) * ld_qt + rl0);
     if (active) {
 #pragma unroll
         for (int j = 0; j < 8; j++) {
@@ -176,7 +198,8 @@ __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
                 const uint32_t p23 = __builtin_amdgcn_perm(wd, wcw, sel);  // rows 4k+2, 4k+3
                 o[k] = nan_block_select(cvt_x4(p01, p23, sc), c);
             }
-            *reinterpret_cast<uint4 *>(qt + (c0 + j) * ld_qt + P0 + rl0) = make_uint4(o[0], o[1], o[2], o[3]);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, make_uint4(o[0], o[1], o[2], o[3])), rq,
+                                                   qoff, (int)(j * ld_qt), 0);
             if (half == 0) {
                 // rearranged row = column wc*64 + cg*8 + j of the tile, block wr*4 + rb
                 const int col = wc * 64 + cg * 8 + j, blk = wr * 4 + rb;
@@ -184,17 +207,37 @@ __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
             }
         }
     }
+    if (ROW) {
+        // row-wise codes and scale bytes, staged (every lane is active: cols
+        // % 256 == 0; rows past the valid ones hold zeros and are staged but
+        // not written out)
+        const int cl = wc * 64 + cg * 8;  // the lane's first column within the tile
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const uint32_t c = scale_code(rmax[i]);
+            const float sc = cvt_scale(c);
+            const uint32_t o0 = nan_block_select(cvt_x4(v[i].x, v[i].y, sc), c);
+            const uint32_t o1 = nan_block_select(cvt_x4(v[i].z, v[i].w, sc), c);
+            *reinterpret_cast<uint2 *>(&lds_q[(rl0 + i) * QG_TILE + cl]) = make_uint2(o0, o1);
+            if ((cg & 3) == 0)
+                lds_rs[(rl0 + i) * 8 + (cl >> 5)] = (uint8_t)c;
+        }
+    }
     __syncthreads();
     if (ROW) {
         // codes: 16 threads per row, 16 bytes each (cols % 256 == 0 here, so
         // every row of the tile has its 256 columns)
+        // (one buffer range over rows [src0, src0 + valid): the stores of the
+        // rows past it are dropped; 256 ld_q < 2^32)
+        const __amdgpu_buffer_rsrc_t rr = byte_range(q + (valid > 0 ? src0 * ld_q : 0) + C0,
+                                                     (uint32_t)(valid * ld_q));
 #pragma unroll
         for (int k = 0; k < QG_TILE * QG_TILE / 16 / QG_THREADS; k++) {
             const int idx = tid + k * QG_THREADS;
             const int r = idx >> 4, ch = idx & 15;
-            if (r < valid)
-                *reinterpret_cast<uint4 *>(q + (src0 + r) * ld_q + C0 + ch * 16) =
-                    *reinterpret_cast<const uint4 *>(&lds_q[r * QG_TILE + ch * 16]);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(v4u, *reinterpret_cast<const uint4 *>(&lds_q[r * QG_TILE + ch * 16])), rr,
+                (uint32_t)(r * ld_q + ch * 16), 0, 0);
         }
         // scales: blocks 2t + h of the row go to byte t of word h
         if (tid < QG_TILE && tid < valid) {

@@ -247,6 +247,9 @@ def test_quantize_colwise_grouped_validation():
     # the padded offsets written over the group offsets; scales inside the codes
     assert f(*args(pad=FAKE2 + 8)) == mx.MX_ERR_OVERLAP
     assert f(*args(st=FAKE3 + 64)) == mx.MX_ERR_OVERLAP
+    # 32-bit offsets within a 256-row tile
+    assert f(*args(ld_x=1 << 22)) == mx.MX_ERR_UNSUPPORTED
+    assert f(*args(ld_qt=1 << 24)) == mx.MX_ERR_UNSUPPORTED
 
 
 def test_grouped_gemm_wgrad_validation():
@@ -349,3 +352,5 @@ def test_quantize_dual_grouped_validation():
     assert call(s=FAKE3 + (1 << 24) + 2) == mx.MX_ERR_ALIGN
     assert call(s=FAKE3 + 1000) == mx.MX_ERR_OVERLAP        # row-wise scales inside the codes
     assert call(k_cap=cap - 256, ld_qt=cap) == mx.MX_ERR_INVALID_ARG
+    assert call(ld_q=1 << 24) == mx.MX_ERR_UNSUPPORTED
+    assert call(ld_x=1 << 22) == mx.MX_ERR_UNSUPPORTED
