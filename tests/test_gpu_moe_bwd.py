@@ -301,3 +301,51 @@ def test_dual_grouped_matches_oracle(gpu_lib, sizes, cols):
     KT = k_cap // 256
     assert np.array_equal(st_swz.cpu().numpy().reshape(-1, KT, 256)[:, :pend // 256],
                           oracle.scale_swizzle(ost).reshape(-1, KT, 256)[:, :pend // 256])
+
+
+@pytest.mark.parametrize("row_wise", [False, True])
+def test_grouped_quantizers_strided_views(gpu_lib, row_wise):
+    """x a column slice of a wider BF16 tensor (ld_x > cols), and the codes
+    written into wider operands (ld_q > cols, ld_qt > k_cap): the quantizers
+    address rows through the leading dimensions only, and leave the bytes
+    around the views untouched.  The column-only case takes cols = 96, so
+    the last 256-column tile has lanes past cols (they load and store
+    nothing)."""
+    mx = gpu_lib
+    sizes = [300, 0, 37, 513, 1]
+    off = _offsets(sizes)
+    rows = int(off[-1])
+    cols = 512 if row_wise else 96
+    wide = mxsynth.normal_bf16((rows, cols + 192), 1.0, seed=700 + cols, outlier_frac=0.01,
+                               outlier_mul=50.0).cuda()
+    x = wide[:, 64:64 + cols]
+    assert x.stride(0) == cols + 192
+    xb = mxsynth.bits(x.cpu().contiguous())
+    G = len(sizes)
+    k_cap = mx.mx_grouped_k_capacity(rows, G)
+    qt_wide = torch.full((cols, k_cap + 256), 0xAB, dtype=torch.uint8, device="cuda")
+    qt = qt_wide[:, :k_cap]
+    st_swz = torch.empty(mx.mx_scale_swizzled_bytes(cols, k_cap // 32), dtype=torch.uint8, device="cuda")
+    offd = torch.from_numpy(off).cuda()
+    if row_wise:
+        q_wide = torch.full((rows, cols + 128), 0xEE, dtype=torch.uint8, device="cuda")
+        q = q_wide[:, 128:]
+        _, s_swz, _, _, pad = mx.mx_quantize_dual_grouped(x, offd, k_cap=k_cap, q=q, qt=qt, st_swz=st_swz)
+    else:
+        _, _, pad = mx.mx_quantize_colwise_grouped(x, offd, k_cap=k_cap, qt=qt, st_swz=st_swz)
+    torch.cuda.synchronize()
+    oqt, ost, opad = oracle.quantize_colwise_grouped(xb, off, k_cap)
+    assert np.array_equal(pad.cpu().numpy(), opad)
+    pend = int(opad[-1])
+    g = qt_wide.cpu().numpy()
+    assert np.array_equal(g[:, :pend], oqt[:, :pend])
+    assert (g[:, k_cap:] == 0xAB).all(), "bytes past each qt row's k_cap were written"
+    KT = k_cap // 256
+    assert np.array_equal(st_swz.cpu().numpy().reshape(-1, KT, 256)[:, :pend // 256],
+                          oracle.scale_swizzle(ost).reshape(-1, KT, 256)[:, :pend // 256])
+    if row_wise:
+        oq, os_ = oracle.quantize_rowwise(xb)
+        gq = q_wide.cpu().numpy()
+        assert np.array_equal(gq[:, 128:], oq)
+        assert (gq[:, :128] == 0xEE).all(), "bytes before each q row were written"
+        assert np.array_equal(oracle.scale_unswizzle(s_swz.cpu().numpy(), rows, cols // 32), os_)
