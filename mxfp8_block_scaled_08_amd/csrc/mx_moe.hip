@@ -218,7 +218,21 @@ hipError_t launch_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, in
 
 // Combine: thread -> 8 consecutive columns of one token; the token's slots in
 // order j = 0..topk-1, FP32 sums of weight * value, BF16 (nearest even) out.
-// Slots outside [0, tokens * topk) contribute nothing.
+// Slots outside [0, tokens * topk) contribute nothing.  TOPK > 0 (the top-8
+// routing): the token's slots, weights and rows are all loaded before the
+// sums, so its TOPK row loads are in flight together; the sums are the same
+// fused multiply-adds in the same order as the general path's.
+__device__ __forceinline__ void combine_acc(float (&acc)[8], float w, uint4 v)
+{
+    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        acc[2 * k] = fmaf(w, __builtin_bit_cast(float, wd[k] << 16), acc[2 * k]);
+        acc[2 * k + 1] = fmaf(w, __builtin_bit_cast(float, wd[k] & 0xFFFF0000u), acc[2 * k + 1]);
+    }
+}
+
+template <int TOPK>
 __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t *__restrict__ y, int64_t ld_y,
                                                           const int32_t *__restrict__ slot,
                                                           const float *__restrict__ weights, int topk,
@@ -229,17 +243,32 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t *__rest
         const int64_t t = u / upr;
         const int64_t cu = u - t * upr;
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int j = 0; j < topk; j++) {
-            const int32_t p = slot[t * topk + j];
-            if (p < 0 || p >= rows_y)  // unrouted, or not a row of y
-                continue;
-            const float w = weights[t * topk + j];
-            const uint4 v = *reinterpret_cast<const uint4 *>(y + (int64_t)p * ld_y + cu * 8);
-            const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+        if (TOPK > 0) {
+            constexpr int K = TOPK > 0 ? TOPK : 1;
+            int32_t p[K];
+            float w[K];
+            uint4 v[K];
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
-                acc[2 * k] = fmaf(w, __builtin_bit_cast(float, wd[k] << 16), acc[2 * k]);
-                acc[2 * k + 1] = fmaf(w, __builtin_bit_cast(float, wd[k] & 0xFFFF0000u), acc[2 * k + 1]);
+            for (int j = 0; j < K; j++) {
+                p[j] = slot[t * K + j];
+                w[j] = weights[t * K + j];
+            }
+#pragma unroll
+            for (int j = 0; j < K; j++)
+                v[j] = (p[j] >= 0 && p[j] < rows_y)
+                           ? *reinterpret_cast<const uint4 *>(y + (int64_t)p[j] * ld_y + cu * 8)
+                           : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int j = 0; j < K; j++)
+                if (p[j] >= 0 && p[j] < rows_y)
+                    combine_acc(acc, w[j], v[j]);
+        } else {
+            for (int j = 0; j < topk; j++) {
+                const int32_t p = slot[t * topk + j];
+                if (p < 0 || p >= rows_y)  // unrouted, or not a row of y
+                    continue;
+                combine_acc(acc, weights[t * topk + j],
+                            *reinterpret_cast<const uint4 *>(y + (int64_t)p * ld_y + cu * 8));
             }
         }
         typedef float f2_t __attribute__((ext_vector_type(2)));
@@ -258,8 +287,14 @@ hipError_t launch_moe_combine(const void *y, int64_t tokens, int64_t hidden, int
     const uint32_t upr = (uint32_t)(hidden / 8);
     const int64_t units = tokens * upr;
     const int64_t blocks = std::min<int64_t>((units + 255) / 256, 65536);
-    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const uint16_t *)y,
-                       ld_y, slot, weights, (int)topk, (uint16_t *)out, ld_out, units, upr, tokens * topk);
+    if (topk == 8)
+        hipLaunchKernelGGL(moe_combine_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           (const uint16_t *)y, ld_y, slot, weights, (int)topk, (uint16_t *)out, ld_out, units,
+                           upr, tokens * topk);
+    else
+        hipLaunchKernelGGL(moe_combine_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           (const uint16_t *)y, ld_y, slot, weights, (int)topk, (uint16_t *)out, ld_out, units,
+                           upr, tokens * topk);
     return hipGetLastError();
 }
 
