@@ -77,4 +77,22 @@ __device__ __forceinline__ uint32_t nan_block_select(uint32_t codes, uint32_t c)
     return c == 0xFFu ? 0x7F7F7F7Fu : codes;
 }
 
+typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
+
+// Buffer resource for a byte range: uniform base and size in SGPRs, so each
+// lane supplies only a 32-bit offset.  Word 3 selects 32-bit data format
+// (what untyped buffer accesses on gfx9-family targets expect).  Loads whose
+// per-lane offset falls outside [0, bytes) read zero and such stores are
+// dropped.  Callers pass values that every lane holds alike; reading them
+// from the first lane says so to the compiler, which would otherwise wrap
+// each access in a loop over the distinct values it cannot rule out.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void *base, uint32_t bytes)
+{
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    void *ub = (void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, 0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
 }  // namespace mx

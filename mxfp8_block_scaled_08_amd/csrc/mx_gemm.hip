@@ -107,23 +107,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 typedef const void __attribute__((address_space(1))) *gptr_t;
 typedef void __attribute__((address_space(3))) *lptr_t;
 
-// Buffer resource for a byte range: uniform base and size in SGPRs, so each
-// lane supplies only a 32-bit offset.  Word 3 selects 32-bit data format
-// (what untyped buffer loads on gfx9-family targets expect).  Accesses whose
-// per-lane offset falls outside the range read zero or are dropped.  Callers
-// pass values that every lane holds alike; reading them from the first lane
-// says so to the compiler, which would otherwise wrap each access in a loop
-// over the distinct values it cannot rule out.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void *base, uint32_t bytes)
-{
-    const uint64_t b = (uint64_t)(uintptr_t)base;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-    void *ub = (void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
-    return __builtin_amdgcn_make_buffer_rsrc(ub, 0, (int)__builtin_amdgcn_readfirstlane(bytes),
-                                             0x00020000);
-}
-
 // Values every lane holds alike, moved to scalar registers.
 __device__ __forceinline__ int64_t uniform(int64_t x)
 {

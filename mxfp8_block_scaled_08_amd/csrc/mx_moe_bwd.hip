@@ -37,21 +37,8 @@
 
 namespace mx {
 
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
-
 constexpr int QG_THREADS = 512;
 constexpr int QG_TILE = 256;
-
-// Buffer resource over a byte range (base and size uniform): per-lane 32-bit
-// offsets, and accesses outside [0, bytes) read zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void *base, uint32_t bytes)
-{
-    const uint64_t b = (uint64_t)(uintptr_t)base;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-    void *ub = (void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
-    return __builtin_amdgcn_make_buffer_rsrc(ub, 0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
-}
 
 __global__ __launch_bounds__(MOE_MAX_EXPERTS) void pad_offsets_kernel(const int64_t *__restrict__ offsets,
                                                                       int G, int64_t rows, int64_t k_cap,
@@ -198,7 +185,7 @@ __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
                 const uint32_t p23 = __builtin_amdgcn_perm(wd, wcw, sel);  // rows 4k+2, 4k+3
                 o[k] = nan_block_select(cvt_x4(p01, p23, sc), c);
             }
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, make_uint4(o[0], o[1], o[2], o[3])), rq,
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u_t, make_uint4(o[0], o[1], o[2], o[3])), rq,
                                                    qoff, (int)(j * ld_qt), 0);
             if (half == 0) {
                 // rearranged row = column wc*64 + cg*8 + j of the tile, block wr*4 + rb
@@ -236,7 +223,7 @@ __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
             const int idx = tid + k * QG_THREADS;
             const int r = idx >> 4, ch = idx & 15;
             __builtin_amdgcn_raw_buffer_store_b128(
-                __builtin_bit_cast(v4u, *reinterpret_cast<const uint4 *>(&lds_q[r * QG_TILE + ch * 16])), rr,
+                __builtin_bit_cast(v4u_t, *reinterpret_cast<const uint4 *>(&lds_q[r * QG_TILE + ch * 16])), rr,
                 (uint32_t)(r * ld_q + ch * 16), 0, 0);
         }
         // scales: blocks 2t + h of the row go to byte t of word h
