@@ -64,6 +64,16 @@
  *   - Calls on different streams may run concurrently; the library has no
  *     shared mutable state apart from the thread-local error message and
  *     the per-stream workspaces (each used only by work on its stream).
+ *   - Device-resident offsets (mx_grouped_gemm's group_offsets,
+ *     mx_quantize_colwise_grouped's and mx_quantize_dual_grouped's
+ *     group_offsets, mx_grouped_gemm_wgrad's k_offsets) are not read by the
+ *     host: offsets breaking their stated properties give unspecified but
+ *     in-bounds results.  With the environment variable MX_DEBUG set (to
+ *     anything but "" or "0", read at every call) those entry points first
+ *     check the offsets with a small kernel on `stream`, wait for it, and
+ *     return MX_ERR_INVALID_ARG naming the first bad entry without
+ *     launching anything else.  The wait makes MX_DEBUG unusable inside HIP
+ *     graph capture.
  */
 #ifndef MXFP8_H
 #define MXFP8_H

@@ -8,7 +8,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build", "mxfp8")
 LIB = os.path.join(PKG, "libmxfp8.so")
-SOURCES = ["mx_api.cpp", "mx_quantize.hip", "mx_gemm.hip", "mx_moe.hip", "mx_moe_bwd.hip"]
+SOURCES = ["mx_api.cpp", "mx_quantize.hip", "mx_gemm.hip", "mx_moe.hip", "mx_moe_bwd.hip", "mx_debug.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed FP32 VALU ops.

@@ -5,12 +5,15 @@
 // an invalid call writes nothing and returns a status naming the problem
 // (the paper "End-to-End MXFP8 Reinforcement Learning on Blackwell" found
 // five of its seven weight-sync failures silent, Table 10; errors here are
-// loud).  Nothing here allocates, synchronizes or reads device memory.
+// loud).  Nothing here allocates, synchronizes or reads device memory,
+// except the optional checks of device-resident offsets under MX_DEBUG.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 
 #include "../../include/mxfp8.h"
 #include "mx_launch.h"
@@ -63,6 +66,31 @@ int64_t swz_bytes(int64_t rows, int64_t kb)
     if (rows <= 0 || kb <= 0)
         return 0;
     return ((rows + 31) / 32) * ((kb + 7) / 8) * 256;
+}
+
+// MX_DEBUG set to anything but "" or "0": the grouped entry points check
+// their device offsets before launching (read at every call, so a process
+// can switch it on and off).
+bool debug_checks()
+{
+    const char *e = std::getenv("MX_DEBUG");
+    return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
+}
+
+// The MX_DEBUG offsets check of an entry point: MX_OK, or MX_ERR_INVALID_ARG
+// naming the first bad entry (MX_ERR_HIP if the check itself fails).
+mx_status debug_offsets(const char *fn, const char *what, const int64_t *off, int64_t G, int64_t total,
+                        int64_t align, int64_t min_len, bool first_zero, bool exact_end, void *stream)
+{
+    int64_t bad = -1;
+    const hipError_t e = mx::check_offsets(off, G, total, align, min_len, first_zero, exact_end,
+                                           (hipStream_t)stream, &bad);
+    if (e != hipSuccess)
+        return fail(MX_ERR_HIP, "%s: MX_DEBUG check of %s failed: %s", fn, what, hipGetErrorString(e));
+    if (bad >= 0)
+        return fail(MX_ERR_INVALID_ARG, "%s: %s[%lld] breaks the stated properties (MX_DEBUG check)", fn, what,
+                    (long long)bad);
+    return MX_OK;
 }
 
 }  // namespace
@@ -418,6 +446,12 @@ mx_status mx_quantize_colwise_grouped(const void *x, int64_t rows_total, int64_t
         for (int k = i + 1; k < 5; k++)
             if ((i >= 2 || k >= 2) && overlap(bufs[i], lens[i], bufs[k], lens[k]))
                 return fail(MX_ERR_OVERLAP, "%s: buffers %d and %d overlap", fn, i, k);
+    if (debug_checks()) {
+        const mx_status dst =
+            debug_offsets(fn, "group_offsets", group_offsets, num_groups, rows_total, 1, 0, false, false, stream);
+        if (dst != MX_OK)
+            return dst;
+    }
     return hip_status(mx::launch_quantize_colwise_grouped(x, rows_total, cols, ld_x, group_offsets,
                                                           num_groups, pad_offsets, qt, ld_qt, k_cap,
                                                           st_swz, (hipStream_t)stream),
@@ -469,6 +503,12 @@ mx_status mx_quantize_dual_grouped(const void *x, int64_t rows_total, int64_t co
         for (int k = i + 1; k < 7; k++)
             if ((i >= 2 || k >= 2) && overlap(bufs[i], lens[i], bufs[k], lens[k]))
                 return fail(MX_ERR_OVERLAP, "%s: buffers %d and %d overlap", fn, i, k);
+    if (debug_checks()) {
+        const mx_status dst =
+            debug_offsets(fn, "group_offsets", group_offsets, num_groups, rows_total, 1, 0, false, false, stream);
+        if (dst != MX_OK)
+            return dst;
+    }
     return hip_status(mx::launch_quantize_colwise_grouped(x, rows_total, cols, ld_x, group_offsets, num_groups,
                                                           pad_offsets, qt, ld_qt, k_cap, st_swz,
                                                           (hipStream_t)stream, rows_total > 0 ? q : nullptr,
@@ -651,6 +691,10 @@ mx_status mx_grouped_gemm(int64_t num_groups, int64_t M_total, int64_t N, int64_
         overlap(c, ec, a_s_swz, swz_bytes(M_total, K / 32)) || overlap(c, ec, b_s_swz, ebs) ||
         overlap(c, ec, group_offsets, (num_groups + 1) * 8))
         return fail(MX_ERR_OVERLAP, "%s: C overlaps an input", fn);
+    if (debug_checks() &&
+        (st = debug_offsets(fn, "group_offsets", group_offsets, num_groups, M_total, 1, 0, true, true, stream)) !=
+            MX_OK)
+        return st;
     return hip_status(mx::launch_grouped_gemm(num_groups, M_total, N, K, group_offsets, a_q, ld_a,
                                               a_s_swz, b_q, b_s_swz, c, ld_c, c_dtype,
                                               (hipStream_t)stream),
@@ -690,6 +734,9 @@ mx_status mx_grouped_gemm_wgrad(int64_t num_groups, int64_t M, int64_t N, int64_
         overlap(c, ec, a_s_swz, swz_bytes(M, k_cap / 32)) || overlap(c, ec, b_s_swz, swz_bytes(N, k_cap / 32)) ||
         overlap(c, ec, k_offsets, (num_groups + 1) * 8))
         return fail(MX_ERR_OVERLAP, "%s: C overlaps an input", fn);
+    if (debug_checks() &&
+        (st = debug_offsets(fn, "k_offsets", k_offsets, num_groups, k_cap, 256, 256, false, false, stream)) != MX_OK)
+        return st;
     return hip_status(mx::launch_grouped_gemm_wgrad(num_groups, M, N, k_cap, k_offsets, a_q, ld_a, a_s_swz,
                                                     b_q, ld_b, b_s_swz, c, ld_c, c_dtype,
                                                     (hipStream_t)stream),

@@ -106,4 +106,11 @@ hipError_t launch_grouped_gemm_wgrad(int64_t G, int64_t M, int64_t N, int64_t K,
 hipError_t launch_swiglu_quantize(const void *gu, int64_t rows, int64_t F, int64_t ld_gu, void *h,
                                   int64_t ld_h, void *q, int64_t ld_q, void *s_swz, hipStream_t stream);
 
+// Debug check of device offsets off[0..G] (see mx_debug.hip): waits for the
+// stream, then *first_bad = the first entry breaking the stated properties
+// (in [0, total], multiple of align, ranges at least min_len long,
+// off[0] == 0 if first_zero, off[G] == total if exact_end), or -1.
+hipError_t check_offsets(const int64_t *off, int64_t G, int64_t total, int64_t align, int64_t min_len,
+                         bool first_zero, bool exact_end, hipStream_t stream, int64_t *first_bad);
+
 }  // namespace mx
