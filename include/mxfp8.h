@@ -216,8 +216,9 @@ mx_status mx_scale_swizzle(const void *s, int64_t rows, int64_t kblocks, int64_t
  * ld_x >= cols, ld_q >= cols, ld_qt >= rows, s_tiles >= ceil(cols/256),
  * st_tiles >= ceil(rows/256) (else MX_ERR_INVALID_ARG); x, q, qt 16-byte
  * aligned with ld_x % 8, ld_q % 16, ld_qt % 16 == 0 and s_swz, st_swz 4-byte
- * aligned (else MX_ERR_ALIGN); no two of the five buffers overlap (else
- * MX_ERR_OVERLAP).
+ * aligned (else MX_ERR_ALIGN); ld_q, ld_qt < 2^24 (else MX_ERR_UNSUPPORTED);
+ * no two of the five buffers overlap (else MX_ERR_OVERLAP).  The batched
+ * and stacked-expert forms below check each job the same way.
  */
 mx_status mx_quantize_dual(const void *x, int64_t rows, int64_t cols, int64_t ld_x, void *q,
                            int64_t ld_q, void *s_swz, int64_t s_tiles, void *qt, int64_t ld_qt,

@@ -239,6 +239,8 @@ static mx_status check_dual_job(const char *who, const mx_dual_job &j)
                     "%s: x, q and qt need 16-byte aligned rows (ld_x %% 8, ld_q %% 16, ld_qt %% 16)", who);
     if (!aligned(j.s_swz, 4) || !aligned(j.st_swz, 4))
         return fail(MX_ERR_ALIGN, "%s: s_swz and st_swz must be 4-byte aligned", who);
+    if (j.ld_q >= ((int64_t)1 << 24) || j.ld_qt >= ((int64_t)1 << 24))
+        return fail(MX_ERR_UNSUPPORTED, "%s: ld_q and ld_qt must be below 2^24 (32-bit offsets within a tile)", who);
     // byte extents: the rearranged outputs span their last tile row's tiles
     const int64_t ex = extent(rows, cols, j.ld_x, 2), eq = extent(rows, cols, j.ld_q, 1),
                   eqt = extent(cols, rows, j.ld_qt, 1);

@@ -201,8 +201,9 @@ __global__ __launch_bounds__(QC_THREADS) void quantize_colwise_kernel(
 // kernel's.  Row-wise, lane (rb, half, cg) holds 8 columns of 16 rows; the
 // four lanes cg & ~3 .. | 3 of a row hold one 32-column block, whose maximum
 // they combine by two DPP quad exchanges; each lane converts its 8 elements
-// of each row and stores them (8 bytes; 256 contiguous bytes per row per
-// workgroup).  The tile's scales are exactly 8 rearranged 256-byte tiles per
+// of each row into LDS (8 bytes), and after the workgroup's barrier sixteen
+// threads write each row's 256 codes as two whole 128-byte lines (the
+// lanes' own 8-byte stores left half lines, 5.31 TB/s).  The tile's scales are exactly 8 rearranged 256-byte tiles per
 // orientation (256 rows x 8 blocks row-wise, 256 columns x 8 blocks
 // column-wise): the codes are placed in LDS at their rearranged positions
 // (byte (32h + r) * 4 + t of tile r / 32 for block 2t + h, the layout of
@@ -227,6 +228,7 @@ __global__ __launch_bounds__(QD_THREADS) void quantize_dual_kernel(DualBatch B)
 {
     __shared__ uint32_t lds_s[8 * 64];   // row-wise scales: 8 rearranged tiles
     __shared__ uint32_t lds_st[8 * 64];  // column-wise scales: 8 rearranged tiles
+    __shared__ __attribute__((aligned(16))) uint8_t lds_q[QD_TILE * QD_TILE];  // row-wise codes
     int jb = 0;
     while (jb + 1 < B.n && (int64_t)blockIdx.x >= B.first[jb + 1])
         jb++;
@@ -277,25 +279,29 @@ __global__ __launch_bounds__(QD_THREADS) void quantize_dual_kernel(DualBatch B)
 #pragma unroll
     for (int i = 0; i < 16; i++)
         v[i] = *reinterpret_cast<const uint4 *>(src + i * ld_x);
+    // column-wise maxima (per column, the lane's 16 rows) and row-wise ones
+    // (per row, the lane's 8 columns) in one pass, each magnitude used by
+    // both as soon as it is formed (two passes keep all 64 magnitudes live)
     uint32_t m[4] = {0, 0, 0, 0};
+    uint32_t rmax[16];
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-        m[0] = pk_max_u16(m[0], mag2(v[i].x));
-        m[1] = pk_max_u16(m[1], mag2(v[i].y));
-        m[2] = pk_max_u16(m[2], mag2(v[i].z));
-        m[3] = pk_max_u16(m[3], mag2(v[i].w));
+        const uint32_t ax = mag2(v[i].x), ay = mag2(v[i].y), az = mag2(v[i].z), aw = mag2(v[i].w);
+        m[0] = pk_max_u16(m[0], ax);
+        m[1] = pk_max_u16(m[1], ay);
+        m[2] = pk_max_u16(m[2], az);
+        m[3] = pk_max_u16(m[3], aw);
+        const uint32_t w = pk_max_u16(pk_max_u16(ax, ay), pk_max_u16(az, aw));
+        rmax[i] = max(w & 0xFFFFu, w >> 16);
     }
 #pragma unroll
     for (int k = 0; k < 4; k++)  // row_ror:8 - the other half of the column block
         m[k] = pk_max_u16(m[k], (uint32_t)__builtin_amdgcn_mov_dpp((int)m[k], 0x128, 0xF, 0xF, false));
-    // row-wise block maxima: the lane's 8 columns, then its quad (quad_perm
-    // [1,0,3,2] and [2,3,0,1])
-    uint32_t rmax[16];
+    // a row's 32-column block is the lane's quad: quad_perm [1,0,3,2] and
+    // [2,3,0,1]
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-        const uint32_t w = pk_max_u16(pk_max_u16(mag2(v[i].x), mag2(v[i].y)),
-                                      pk_max_u16(mag2(v[i].z), mag2(v[i].w)));
-        uint32_t a = max(w & 0xFFFFu, w >> 16);
+        uint32_t a = rmax[i];
         a = max(a, (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0xB1, 0xF, 0xF, false));
         a = max(a, (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0x4E, 0xF, 0xF, false));
         rmax[i] = a;
@@ -303,6 +309,10 @@ __global__ __launch_bounds__(QD_THREADS) void quantize_dual_kernel(DualBatch B)
     __syncthreads();  // the 0x7F fill precedes every scale byte
     uint8_t *bs = reinterpret_cast<uint8_t *>(lds_s);
     uint8_t *bst = reinterpret_cast<uint8_t *>(lds_st);
+    // the tile's 256 rows of qt from column R0 as one buffer range (256 ld_qt
+    // < 2^32): column j of the lane is row j ld_qt past its first
+    const __amdgpu_buffer_rsrc_t rq = byte_range(qt + C0 * ld_qt + R0, (uint32_t)(QD_TILE * ld_qt));
+    const uint32_t qoff = (uint32_t)((wc * 64 + cg * 8) * ld_qt + wr * 128 + rb * 32 + half * 16);
     if (active) {
         // column-wise, as quantize_colwise_kernel
 #pragma unroll
@@ -323,7 +333,8 @@ __global__ __launch_bounds__(QD_THREADS) void quantize_dual_kernel(DualBatch B)
                 const uint32_t p23 = __builtin_amdgcn_perm(wd, wcw, sel);
                 o[k] = nan_block_select(cvt_x4(p01, p23, sc), c);
             }
-            *reinterpret_cast<uint4 *>(qt + (c0 + j) * ld_qt + r0) = make_uint4(o[0], o[1], o[2], o[3]);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u_t, make_uint4(o[0], o[1], o[2], o[3])), rq,
+                                                   qoff, (int)(j * ld_qt), 0);
             if (half == 0) {
                 // rearranged row = column wc*64 + cg*8 + j of the tile, block wr*4 + rb
                 const int col = wc * 64 + cg * 8 + j, blk = wr * 4 + rb;
@@ -337,7 +348,8 @@ __global__ __launch_bounds__(QD_THREADS) void quantize_dual_kernel(DualBatch B)
             const float sc = cvt_scale(c);
             const uint32_t o0 = nan_block_select(cvt_x4(v[i].x, v[i].y, sc), c);
             const uint32_t o1 = nan_block_select(cvt_x4(v[i].z, v[i].w, sc), c);
-            *reinterpret_cast<uint2 *>(q + (r0 + i) * ld_q + c0) = make_uint2(o0, o1);
+            *reinterpret_cast<uint2 *>(&lds_q[(wr * 128 + rb * 32 + half * 16 + i) * QD_TILE + wc * 64 + cg * 8]) =
+                make_uint2(o0, o1);
             if ((cg & 3) == 0) {
                 // rearranged row = tile row wr*128 + rb*32 + half*16 + i, block wc*2 + cg/4
                 const int row = wr * 128 + rb * 32 + half * 16 + i, blk = wc * 2 + (cg >> 2);
@@ -346,6 +358,24 @@ __global__ __launch_bounds__(QD_THREADS) void quantize_dual_kernel(DualBatch B)
         }
     }
     __syncthreads();
+    // row-wise codes out of LDS: 16 threads per row of the tile, 16 bytes
+    // each, so every store instruction writes whole 128-byte lines (rows and
+    // columns past the tensor: rows % 32 == 0 and cols % 32 == 0, so a
+    // 16-byte chunk is all inside or all outside)
+    {
+        // (one buffer range over the tile's rows that exist, 256 ld_q < 2^32)
+        const __amdgpu_buffer_rsrc_t rr =
+            byte_range(q + R0 * ld_q + C0, (uint32_t)(min(rows - R0, (int64_t)QD_TILE) * ld_q));
+#pragma unroll
+        for (int k = 0; k < QD_TILE * QD_TILE / 16 / QD_THREADS; k++) {
+            const int idx = tid + k * QD_THREADS;
+            const int r = idx >> 4, ch = idx & 15;
+            if (C0 + ch * 16 < cols)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(v4u_t, *reinterpret_cast<const uint4 *>(&lds_q[r * QD_TILE + ch * 16])), rr,
+                    (uint32_t)(r * ld_q + ch * 16), 0, 0);
+        }
+    }
     // thread -> word tid & 63 of rearranged tile tid >> 6 (its 32-row tile
     // row of each orientation; the tile's 8 blocks are this tile's 256-K group)
     const int t = tid >> 6, w = tid & 63;

@@ -123,6 +123,8 @@ def test_quantize_dual_validation():
     assert call(a4=FAKE + 128) == mx.MX_ERR_OVERLAP  # q inside x
     assert call(a10=FAKE5 + 256) == mx.MX_ERR_OVERLAP  # st_swz inside qt
     assert call(a6=FAKE2 + 64) == mx.MX_ERR_OVERLAP  # s_swz inside q
+    assert call(a5=1 << 24) == mx.MX_ERR_UNSUPPORTED  # 32-bit offsets within a tile
+    assert call(a9=1 << 24) == mx.MX_ERR_UNSUPPORTED
     assert call(a1=0) == mx.MX_OK
     assert call(a2=0, a3=0, a5=0) == mx.MX_OK
 
