@@ -70,6 +70,17 @@ def test_grouped_quantizer_and_wgrad_offsets_checked(gpu_lib, debug_env):
         assert f"group_offsets[{idx}]" in str(e.value), str(e.value)
         torch.cuda.synchronize()
         assert (qt2 == 0x33).all()
+    # the one-read row-wise + per-expert column-wise form checks the same way
+    x2 = mxsynth.normal_bf16((rows, 256), 1.0, seed=42).cuda()
+    q2 = torch.full((rows, 256), 0x44, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mx.MxError) as e:
+        mx.mx_quantize_dual_grouped(x2, torch.tensor([0, 200, 100, rows], dtype=torch.int64, device="cuda"),
+                                    k_cap=k_cap, q=q2)
+    assert "mx_quantize_dual_grouped" in str(e.value) and "group_offsets[1]" in str(e.value), str(e.value)
+    torch.cuda.synchronize()
+    assert (q2 == 0x44).all()
+    mx.mx_quantize_dual_grouped(x2, good, k_cap=k_cap, q=q2)
+    torch.cuda.synchronize()
     # weight-gradient ranges: not 256-aligned, shorter than 256, past k_cap
     for bad, idx in (([0, 256, 600, 1024], 2), ([0, 256, 256, 768], 1), ([0, 256, 512, k_cap + 256], 3)):
         c2 = torch.full_like(c, 5.0)
