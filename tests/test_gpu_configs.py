@@ -1,10 +1,13 @@
 """Full-size parity on the five workloads (Qwen3-8B / Qwen3-30B-A3B layer shapes).
 
 Quantized bytes and rearranged scales are compared with the oracle byte for
-byte over every element; GEMM outputs on sampled entries (random positions
-plus rows/columns along the edges of C) against the oracle's double-precision
-entries, with the derived tolerance of tests/gpu_util.py.  The launches are
-the same ones bench.py times.
+byte over every element.  GEMM outputs are checked on a lattice that puts at
+least one entry in every 256 x 256 output tile (every expert's tiles for the
+grouped products) and reaches every 32 x 32 sub-tile position, plus random
+entries and the edges of C: each against the run-window model at the stated
+bar, with the count that also meets the stated bar against the oracle's
+exact result printed and kept in STATS.  The launches are the same ones
+bench.py times.
 """
 import numpy as np
 import pytest
@@ -12,10 +15,23 @@ import torch
 
 import mxsynth
 import oracle
-from gpu_util import (check_sampled, check_sampled_grouped, oracle_colwise_par,
-                      oracle_rowwise_par, sample_entries)
+from gpu_util import (check_sampled, check_sampled_grouped, lattice_entries, lattice_grouped,
+                      oracle_colwise_par, oracle_rowwise_par, sample_entries, stats_line)
 
 pytestmark = pytest.mark.gpu
+
+STATS = {}
+
+
+def _record(what: str, st: dict):
+    STATS[what] = st
+    print(stats_line(what, st), flush=True)
+
+
+def _dense_entries(rng, M, N):
+    r1, c1 = lattice_entries(rng, M, N)
+    r2, c2 = sample_entries(rng, M, N, n=512)
+    return np.concatenate([r1, r2]), np.concatenate([c1, c2])
 
 
 def _eq(gpu: torch.Tensor, ref: np.ndarray, what: str):
@@ -74,8 +90,8 @@ def test_dense_forward_m4608(gpu_lib, layer):
         C = mx.mx_gemm(q, mx.mx_scale_swizzle(s), wq, mx.mx_scale_swizzle(ws),
                        out_dtype=torch.bfloat16)
         assert C.shape == (spec.M, spec.N)
-        rows, cols = sample_entries(rng, spec.M, spec.N)
-        check_sampled(C, rows, cols, oq, os_, owq, ows, f"fwd {spec.name}")
+        rows, cols = _dense_entries(rng, spec.M, spec.N)
+        _record(f"fwd {spec.name}", check_sampled(C, rows, cols, oq, os_, owq, ows, f"fwd {spec.name}"))
         del C, wq, ws
 
 
@@ -98,8 +114,8 @@ def test_dense_backward_gate_up(gpu_lib, layer):
     _eq(wst, owst, "W colwise s")
     C = mx.mx_gemm(q, mx.mx_scale_swizzle(s), wqt, mx.mx_scale_swizzle(wst),
                    out_dtype=torch.bfloat16)
-    rows, cols = sample_entries(rng, 12288, 4096)
-    check_sampled(C, rows, cols, oq, os_, owqt, owst, "dgrad")
+    rows, cols = _dense_entries(rng, 12288, 4096)
+    _record("bwd dgrad", check_sampled(C, rows, cols, oq, os_, owqt, owst, "dgrad"))
     del C, q, s, wqt, wst
     # wgrad: M = 24576, N = 4096, K = 12288 tokens
     dqt, dst = mx.mx_quantize_colwise(dyd)
@@ -112,8 +128,8 @@ def test_dense_backward_gate_up(gpu_lib, layer):
     _eq(xst, oxst, "X colwise s")
     C = mx.mx_gemm(dqt, mx.mx_scale_swizzle(dst), xqt, mx.mx_scale_swizzle(xst),
                    out_dtype=torch.bfloat16)
-    rows, cols = sample_entries(rng, 24576, 4096)
-    check_sampled(C, rows, cols, odqt, odst, oxqt, oxst, "wgrad")
+    rows, cols = _dense_entries(rng, 24576, 4096)
+    _record("bwd wgrad", check_sampled(C, rows, cols, odqt, odst, oxqt, oxst, "wgrad"))
 
 
 def test_moe_grouped_qwen3_30b_a3b(gpu_lib):
@@ -135,11 +151,13 @@ def test_moe_grouped_qwen3_30b_a3b(gpu_lib):
         b_swz = torch.cat([mx.mx_scale_swizzle(ws[g * N:(g + 1) * N]) for g in range(G)])
         C = mx.mx_grouped_gemm(offd, q, mx.mx_scale_swizzle(s), wq.view(G, N, K), b_swz,
                                out_dtype=torch.bfloat16)
-        # every expert: its first and last row, plus random rows; random columns
+        # every tile of every expert (lattice), every expert's first and last
+        # row, random rows; random columns
         firsts = off[:-1][rows_per > 0]
         lasts = off[1:][rows_per > 0] - 1
-        rr = np.concatenate([firsts, lasts, rng.integers(0, int(off[-1]), size=1024)])
-        cc = rng.integers(0, N, size=rr.size)
-        check_sampled_grouped(C, rr, cc, off, oq, os_, owq.reshape(G, N, K),
-                              ows.reshape(G, N, K // 32), f"moe {name}")
+        rl, cl = lattice_grouped(rng, off, N)
+        rr = np.concatenate([rl, firsts, lasts, rng.integers(0, int(off[-1]), size=512)])
+        cc = np.concatenate([cl, rng.integers(0, N, size=rr.size - rl.size)])
+        _record(f"moe {name}", check_sampled_grouped(C, rr, cc, off, oq, os_, owq.reshape(G, N, K),
+                                                     ows.reshape(G, N, K // 32), f"moe {name}"))
         del C, q, s, wq, ws
