@@ -204,6 +204,14 @@ def build_workload(mx, torch, mxsynth):
     o["hq"] = torch.empty(M, 768, **u8)
     o["hswz"] = torch.empty(swz(M, 768 // 32), **u8)
     o["moe_out"] = torch.empty(ids.shape[0], 2048, **bf)
+    # one scratch buffer for every call that takes a workspace (split-tail
+    # GEMMs, the dispatch's chunk counts, the weight gradients' tile counter):
+    # the step runs on one stream, so the calls never overlap in time
+    gemm_ws = max(mx.mx_gemm_workspace_bytes(m, n, k) for m, n, k in
+                  ((4608, 6144, 4096), (4608, 4096, 4096), (4608, 24576, 4096), (4608, 4096, 12288),
+                   (12288, 4096, 24576), (24576, 4096, 12288)))
+    o["ws"] = torch.empty(max(gemm_ws, mx.mx_moe_dispatch_workspace_bytes(ids.shape[0], ids.shape[1], G),
+                              mx.mx_grouped_gemm_wgrad_workspace_bytes()), **u8)
     assert n_assign == M
     inputs = dict(W=W, xh=xh, xi=xi, dy=dy, x=xb, off=off, a_gu=a_gu, a_dn=a_dn,
                   w_gu=w_gu, w_dn=w_dn, dy_gu=dy_gu, dy_dn=dy_dn, M=M, k_cap=k_cap,
@@ -238,24 +246,24 @@ def step(mx, I, o, T):
     for name in ("xh", "xi"):
         T("quant_row", mx.mx_quantize_rowwise_swz, I[name], q=o[name + "_q"], s_swz=o[name + "_swz"])
     g = mx.mx_gemm
-    T("gemm", g, o["xh_q"], o["xh_swz"], o["qkv_q"], o["qkv_swz"], c=o["C_qkv"])
-    T("gemm", g, o["xh_q"], o["xh_swz"], o["o_q"], o["o_swz"], c=o["C_o"])
-    T("gemm", g, o["xh_q"], o["xh_swz"], o["gu_q"], o["gu_swz"], c=o["C_gu"])
-    T("gemm", g, o["xi_q"], o["xi_swz"], o["dn_q"], o["dn_swz"], c=o["C_dn"])
+    T("gemm", g, o["xh_q"], o["xh_swz"], o["qkv_q"], o["qkv_swz"], c=o["C_qkv"], workspace=o["ws"])
+    T("gemm", g, o["xh_q"], o["xh_swz"], o["o_q"], o["o_swz"], c=o["C_o"], workspace=o["ws"])
+    T("gemm", g, o["xh_q"], o["xh_swz"], o["gu_q"], o["gu_swz"], c=o["C_gu"], workspace=o["ws"])
+    T("gemm", g, o["xi_q"], o["xi_swz"], o["dn_q"], o["dn_swz"], c=o["C_dn"], workspace=o["ws"])
     # 3. dense backward of gate_up, 12288 tokens
     T("quant_dual", dq, I["dy"], q=o["dy_q"], s_swz=o["dy_swz"], qt=o["dyT_q"],
       st_swz=o["dyT_swz"])
     T("quant_col", cq, I["x"], o["xT_q"], o["xT_s"])
     T("swizzle", sw, o["xT_s"], o["xT_swz"])
-    T("gemm", g, o["dy_q"], o["dy_swz"], o["guT_q"], o["guT_swz"], c=o["C_dgrad"])
-    T("gemm", g, o["dyT_q"], o["dyT_swz"], o["xT_q"], o["xT_swz"], c=o["C_wgrad"])
+    T("gemm", g, o["dy_q"], o["dy_swz"], o["guT_q"], o["guT_swz"], c=o["C_dgrad"], workspace=o["ws"])
+    T("gemm", g, o["dyT_q"], o["dyT_swz"], o["xT_q"], o["xT_swz"], c=o["C_wgrad"], workspace=o["ws"])
     # 4. MoE layer: expert weights in both orientations, dispatch, gate_up,
     #    SwiGLU + quantize, down, combine
     for name, w in (("mgu", I["w_gu"]), ("mdn", I["w_dn"])):
         T("quant_dual", mx.mx_quantize_dual_experts, w, q=o[name + "_wq"], s_swz=o[name + "_wswz"],
           qt=o[name + "_wqt"], st_swz=o[name + "_wstswz"])
     T("moe_dispatch", mx.mx_moe_dispatch, I["x_tok"], I["ids"], I["w_gu"].shape[0],
-      offsets=o["moff"], src=o["msrc"], slot=o["mslot"], q=o["xq"], s_swz=o["xswz"])
+      offsets=o["moff"], src=o["msrc"], slot=o["mslot"], q=o["xq"], s_swz=o["xswz"], workspace=o["ws"])
     T("grouped_gemm", mx.mx_grouped_gemm, o["moff"], o["xq"], o["xswz"], o["mgu_wq"],
       o["mgu_wswz"], c=o["C_mgu"])
     T("swiglu", mx.mx_swiglu_quantize, o["C_mgu"], q=o["hq"], s_swz=o["hswz"], h=o["h"])
@@ -276,7 +284,7 @@ def step(mx, I, o, T):
         T("quant_col_grouped", mx.mx_quantize_colwise_grouped, a, I["off"], k_cap=k_cap,
           qt=o[name + "_xT"], st_swz=o[name + "_xTswz"], pad_offsets=o[name + "_pad2"])
         T("grouped_wgrad", mx.mx_grouped_gemm_wgrad, o[name + "_pad"], o[name + "_dyT"],
-          o[name + "_dyTswz"], o[name + "_xT"], o[name + "_xTswz"], c=o["dW_" + name])
+          o[name + "_dyTswz"], o[name + "_xT"], o[name + "_xTswz"], c=o["dW_" + name], workspace=o["ws"])
 
 
 def work_per_step(I):
@@ -416,8 +424,8 @@ def main():
     torch.cuda.set_device(0)
     I, o = build_workload(mx, torch, mxsynth)
     torch.cuda.synchronize()
-    # everything runs on one side stream, so that the library's per-stream
-    # workspace made by the warm-up steps is the one a captured step uses
+    # everything runs on one side stream (the step's calls share one
+    # workspace, so they must not overlap in time)
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
     stream_ctx = torch.cuda.stream(stream)

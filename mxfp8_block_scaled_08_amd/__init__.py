@@ -26,7 +26,8 @@ __all__ = [
     "mx_grouped_gemm", "mx_quantize_dual", "mx_quantize_dual_batch", "mx_quantize_dual_experts",
     "mx_moe_dispatch", "mx_moe_combine", "mx_grouped_k_capacity", "mx_quantize_colwise_grouped",
     "mx_grouped_gemm_wgrad", "mx_swiglu_quantize", "mx_quantize_rowwise_swz",
-    "mx_quantize_dual_grouped", "MX_OK", "MX_ERR_INVALID_ARG", "MX_ERR_SHAPE", "MX_ERR_ALIGN",
+    "mx_quantize_dual_grouped", "mx_gemm_workspace_bytes", "mx_moe_dispatch_workspace_bytes",
+    "mx_grouped_gemm_wgrad_workspace_bytes", "MX_OK", "MX_ERR_INVALID_ARG", "MX_ERR_SHAPE", "MX_ERR_ALIGN",
     "MX_ERR_OVERLAP", "MX_ERR_UNSUPPORTED", "MX_ERR_HIP", "MX_BF16", "MX_F32",
 ]
 
@@ -84,13 +85,17 @@ def load() -> ctypes.CDLL:
     L.mx_quantize_dual_batch.argtypes = [ctypes.c_void_p, ctypes.c_int, _vp]
     L.mx_quantize_dual_batch.restype = ctypes.c_int
     L.mx_moe_dispatch.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64,
-                                  _vp, _vp]
+                                  _vp, _vp, _i64, _vp]
+    L.mx_moe_dispatch_workspace_bytes.restype = _i64
+    L.mx_moe_dispatch_workspace_bytes.argtypes = [_i64, _i64, _i64]
     L.mx_moe_dispatch.restype = ctypes.c_int
     L.mx_moe_combine.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp]
     L.mx_moe_combine.restype = ctypes.c_int
     L.mx_gemm.restype = ctypes.c_int
     L.mx_gemm.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
-                          ctypes.c_int, _vp]
+                          ctypes.c_int, _vp, _i64, _vp]
+    L.mx_gemm_workspace_bytes.restype = _i64
+    L.mx_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64, ctypes.c_int]
     L.mx_grouped_gemm.restype = ctypes.c_int
     L.mx_grouped_gemm.argtypes = [_i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp,
                                   _i64, ctypes.c_int, _vp]
@@ -110,9 +115,24 @@ def load() -> ctypes.CDLL:
                                               _i64, _vp, _vp]
     L.mx_grouped_gemm_wgrad.restype = ctypes.c_int
     L.mx_grouped_gemm_wgrad.argtypes = [_i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
-                                        _vp, _vp, _i64, ctypes.c_int, _vp]
+                                        _vp, _vp, _i64, ctypes.c_int, _vp, _i64, _vp]
+    L.mx_grouped_gemm_wgrad_workspace_bytes.restype = _i64
+    L.mx_grouped_gemm_wgrad_workspace_bytes.argtypes = []
     _lib = L
     return L
+
+
+def _workspace(ws: Optional[torch.Tensor], need: int, device) -> Tuple[int, int]:
+    """(pointer, bytes) of the caller's workspace, or of a new uint8 tensor of
+    the size the library asked for (the caller keeps ownership: the tensor is
+    held by torch's allocator for the stream until the call's work is done)."""
+    if need <= 0 and ws is None:
+        return 0, 0
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    if not ws.is_cuda:
+        raise ValueError("workspace must be a device tensor")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
 
 
 def _status_name(st: int) -> str:
@@ -290,13 +310,15 @@ def mx_quantize_dual_batch(jobs, stream=None) -> None:
 def mx_moe_dispatch(x: torch.Tensor, topk_ids: torch.Tensor, num_experts: int,
                     offsets: Optional[torch.Tensor] = None, src: Optional[torch.Tensor] = None,
                     slot: Optional[torch.Tensor] = None, q: Optional[torch.Tensor] = None,
-                    s_swz: Optional[torch.Tensor] = None, stream=None):
+                    s_swz: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    stream=None):
     """Sort the routed rows by expert, gather and quantize them row-wise.
 
     x BF16 [tokens][hidden], topk_ids int32 [tokens][topk] -> (offsets int64
     [num_experts+1], src_token int32 [tokens*topk], slot int32 [tokens*topk],
     q uint8 [tokens*topk][hidden], s_swz uint8: rearranged scales); outputs
-    passed in are written in place."""
+    passed in are written in place.  workspace: device scratch of at least
+    mx_moe_dispatch_workspace_bytes bytes (a new tensor if None)."""
     tokens, hidden = x.shape
     if topk_ids.dim() != 2 or topk_ids.shape[0] != tokens or not topk_ids.is_contiguous():
         raise ValueError("topk_ids must be a contiguous [tokens][topk] tensor")
@@ -315,10 +337,11 @@ def mx_moe_dispatch(x: torch.Tensor, topk_ids: torch.Tensor, num_experts: int,
         s_swz = torch.empty(mx_scale_swizzled_bytes(n, hidden // 32), dtype=torch.uint8, device=dev)
     if offsets.numel() != num_experts + 1 or src.numel() != n or slot.numel() != n:
         raise ValueError("offsets, src and slot must have num_experts+1, n and n entries")
+    wp, wb = _workspace(workspace, mx_moe_dispatch_workspace_bytes(tokens, topk, num_experts), dev)
     st = load().mx_moe_dispatch(_dev(x, "x", torch.bfloat16), tokens, hidden, _ld(x, "x"),
                                 _dev(topk_ids, "topk_ids", torch.int32), topk, num_experts,
                                 _dev(offsets, "offsets"), _dev(src, "src"), _dev(slot, "slot"),
-                                _dev(q, "q"), _ld(q, "q"), _dev(s_swz, "s_swz"), _stream(stream))
+                                _dev(q, "q"), _ld(q, "q"), _dev(s_swz, "s_swz"), wp, wb, _stream(stream))
     _check("mx_moe_dispatch", st)
     return offsets, src, slot, q, s_swz
 
@@ -342,10 +365,26 @@ def mx_moe_combine(y: torch.Tensor, slot: torch.Tensor, weights: torch.Tensor,
 _OUT = {torch.bfloat16: MX_BF16, torch.float32: MX_F32}
 
 
+def mx_gemm_workspace_bytes(M: int, N: int, K: int, out_dtype: torch.dtype = torch.bfloat16) -> int:
+    """Device scratch mx_gemm needs for this shape (0: none), host-only."""
+    return load().mx_gemm_workspace_bytes(M, N, K, _OUT[out_dtype])
+
+
+def mx_moe_dispatch_workspace_bytes(tokens: int, topk: int, num_experts: int) -> int:
+    return load().mx_moe_dispatch_workspace_bytes(tokens, topk, num_experts)
+
+
+def mx_grouped_gemm_wgrad_workspace_bytes() -> int:
+    return load().mx_grouped_gemm_wgrad_workspace_bytes()
+
+
 def mx_gemm(a_q: torch.Tensor, a_s_swz: torch.Tensor, b_q: torch.Tensor,
             b_s_swz: torch.Tensor, c: Optional[torch.Tensor] = None,
-            out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
-    """C[M][N] = deq(A)[M][K] . deq(B)[N][K]^T (both operands K-contiguous)."""
+            out_dtype: torch.dtype = torch.bfloat16, workspace: Optional[torch.Tensor] = None,
+            stream=None) -> torch.Tensor:
+    """C[M][N] = deq(A)[M][K] . deq(B)[N][K]^T (both operands K-contiguous).
+    workspace: device scratch of at least mx_gemm_workspace_bytes bytes when
+    that is nonzero (a new tensor if None)."""
     a_q, b_q = _u8(a_q), _u8(b_q)
     M, K = a_q.shape
     N = b_q.shape[0]
@@ -355,10 +394,11 @@ def mx_gemm(a_q: torch.Tensor, a_s_swz: torch.Tensor, b_q: torch.Tensor,
         c = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
     if c.dtype not in _OUT:
         raise ValueError("c must be bfloat16 or float32")
+    wp, wb = _workspace(workspace, mx_gemm_workspace_bytes(M, N, K, c.dtype), a_q.device)
     st = load().mx_gemm(M, N, K, _dev(a_q, "a_q", torch.uint8), _ld(a_q, "a_q"),
                         _dev(a_s_swz, "a_s_swz", torch.uint8), _dev(b_q, "b_q", torch.uint8),
                         _ld(b_q, "b_q"), _dev(b_s_swz, "b_s_swz", torch.uint8),
-                        _dev(c, "c"), _ld(c, "c"), _OUT[c.dtype], _stream(stream))
+                        _dev(c, "c"), _ld(c, "c"), _OUT[c.dtype], wp, wb, _stream(stream))
     _check("mx_gemm", st)
     return c
 
@@ -459,9 +499,12 @@ def mx_quantize_colwise_grouped(x: torch.Tensor, group_offsets: torch.Tensor,
 
 def mx_grouped_gemm_wgrad(k_offsets: torch.Tensor, a_q: torch.Tensor, a_s_swz: torch.Tensor,
                           b_q: torch.Tensor, b_s_swz: torch.Tensor, c: Optional[torch.Tensor] = None,
-                          out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+                          out_dtype: torch.dtype = torch.bfloat16, workspace: Optional[torch.Tensor] = None,
+                          stream=None) -> torch.Tensor:
     """C [G][M][N]: C_g = A[:, r_g] B[:, r_g]^T over the column ranges
-    r_g = [k_offsets[g], k_offsets[g+1]) (the per-expert weight gradient)."""
+    r_g = [k_offsets[g], k_offsets[g+1]) (the per-expert weight gradient).
+    workspace: mx_grouped_gemm_wgrad_workspace_bytes() bytes of device scratch
+    (a new tensor if None)."""
     a_q, b_q = _u8(a_q), _u8(b_q)
     M, K = a_q.shape
     N, Kb = b_q.shape
@@ -482,7 +525,9 @@ def mx_grouped_gemm_wgrad(k_offsets: torch.Tensor, a_q: torch.Tensor, a_s_swz: t
                                       _dev(a_s_swz, "a_s_swz", torch.uint8),
                                       _dev(b_q, "b_q", torch.uint8), _ld(b_q, "b_q"),
                                       _dev(b_s_swz, "b_s_swz", torch.uint8), _dev(c, "c"),
-                                      c.stride(1), _OUT[c.dtype], _stream(stream))
+                                      c.stride(1), _OUT[c.dtype],
+                                      *_workspace(workspace, mx_grouped_gemm_wgrad_workspace_bytes(), a_q.device),
+                                      _stream(stream))
     _check("mx_grouped_gemm_wgrad", st)
     return c
 

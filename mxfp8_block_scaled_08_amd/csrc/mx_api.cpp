@@ -5,8 +5,12 @@
 // an invalid call writes nothing and returns a status naming the problem
 // (the paper "End-to-End MXFP8 Reinforcement Learning on Blackwell" found
 // five of its seven weight-sync failures silent, Table 10; errors here are
-// loud).  Nothing here allocates, synchronizes or reads device memory,
-// except the optional checks of device-resident offsets under MX_DEBUG.
+// loud).  Nothing here or in the launchers allocates device or host memory,
+// synchronizes or reads device memory; scratch memory (the split tail's
+// partial tiles, the dispatch's chunk counts, the weight gradient's tile
+// counter) is a workspace the caller passes, its size given by host-only
+// queries.  The one exception is the opt-in check of device-resident offsets
+// under MX_DEBUG, which waits for its result.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -59,6 +63,29 @@ int64_t extent(int64_t rows, int64_t used, int64_t ld, int64_t elem)
     if (rows <= 0 || used <= 0)
         return 0;
     return ((rows - 1) * ld + used) * elem;
+}
+
+// The caller's workspace: at least `need` bytes, `align`-aligned, not
+// overlapping any of the n buffers given (MX_OK when need is 0).
+mx_status check_workspace(const char *fn, const void *ws, int64_t ws_bytes, int64_t need, uintptr_t align,
+                          const void *const *bufs, const int64_t *lens, int n)
+{
+    if (ws_bytes < 0)
+        return fail(MX_ERR_INVALID_ARG, "%s: negative workspace_bytes", fn);
+    if (need <= 0)
+        return MX_OK;
+    if (!ws || ws_bytes < need)
+        return fail(MX_ERR_INVALID_ARG, "%s: needs a workspace of %lld bytes, got %lld at %p", fn,
+                    (long long)need, (long long)ws_bytes, ws);
+    if ((uintptr_t)ws % align != 0)
+        return fail(MX_ERR_ALIGN, "%s: workspace must be %d-byte aligned", fn, (int)align);
+    for (int i = 0; i < n; i++)
+        if (bufs[i] && lens[i] > 0) {
+            const uintptr_t a = (uintptr_t)ws, b = (uintptr_t)bufs[i];
+            if (a < b + (uintptr_t)lens[i] && b < a + (uintptr_t)need)
+                return fail(MX_ERR_OVERLAP, "%s: workspace overlaps buffer %d", fn, i);
+        }
+    return MX_OK;
 }
 
 int64_t swz_bytes(int64_t rows, int64_t kb)
@@ -356,7 +383,7 @@ mx_status mx_quantize_dual_experts(const void *x, int64_t num_experts, int64_t r
 mx_status mx_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
                           const int32_t *topk_ids, int64_t topk, int64_t num_experts,
                           int64_t *offsets, int32_t *src_token, int32_t *slot, void *q, int64_t ld_q,
-                          void *s_swz, void *stream)
+                          void *s_swz, void *workspace, int64_t workspace_bytes, void *stream)
 {
     const char *fn = "mx_moe_dispatch";
     if (tokens < 0 || hidden < 0 || topk < 1 || num_experts < 1)
@@ -396,10 +423,23 @@ mx_status mx_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t
         for (int k = i + 1; k < 7; k++)
             if ((i >= 2 || k >= 2) && overlap(bufs[i], lens[i], bufs[k], lens[k]))
                 return fail(MX_ERR_OVERLAP, "%s: buffers %d and %d overlap", fn, i, k);
+    const mx_status wst = check_workspace(fn, workspace, workspace_bytes,
+                                          mx::moe_dispatch_workspace_bytes(tokens, topk, num_experts), 4,
+                                          bufs, lens, 7);
+    if (wst != MX_OK)
+        return wst;
     return hip_status(mx::launch_moe_dispatch(x, tokens, hidden, ld_x, topk_ids, topk, num_experts,
-                                              offsets, src_token, slot, q, ld_q, s_swz,
+                                              offsets, src_token, slot, q, ld_q, s_swz, workspace,
                                               (hipStream_t)stream),
                       fn);
+}
+
+int64_t mx_moe_dispatch_workspace_bytes(int64_t tokens, int64_t topk, int64_t num_experts)
+{
+    if (tokens <= 0 || topk <= 0 || num_experts <= 0 || num_experts > mx::MOE_MAX_EXPERTS ||
+        tokens * topk >= ((int64_t)1 << 30))
+        return 0;
+    return mx::moe_dispatch_workspace_bytes(tokens, topk, num_experts);
 }
 
 int64_t mx_grouped_k_capacity(int64_t rows_total, int64_t num_groups)
@@ -506,8 +546,10 @@ mx_status mx_quantize_dual_grouped(const void *x, int64_t rows_total, int64_t co
             if ((i >= 2 || k >= 2) && overlap(bufs[i], lens[i], bufs[k], lens[k]))
                 return fail(MX_ERR_OVERLAP, "%s: buffers %d and %d overlap", fn, i, k);
     if (debug_checks()) {
+        // the row-wise output covers the rows of the experts only: under
+        // MX_DEBUG the offsets must also start at 0 and end at rows_total
         const mx_status dst =
-            debug_offsets(fn, "group_offsets", group_offsets, num_groups, rows_total, 1, 0, false, false, stream);
+            debug_offsets(fn, "group_offsets", group_offsets, num_groups, rows_total, 1, 0, true, true, stream);
         if (dst != MX_OK)
             return dst;
     }
@@ -642,9 +684,17 @@ static mx_status check_gemm_common(const char *fn, int64_t M, int64_t N, int64_t
     return MX_OK;
 }
 
+int64_t mx_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int c_dtype)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || (c_dtype != MX_BF16 && c_dtype != MX_F32))
+        return 0;
+    return mx::gemm_workspace_bytes(M, N, K, c_dtype, true);
+}
+
 mx_status mx_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t ld_a,
                   const void *a_s_swz, const void *b_q, int64_t ld_b, const void *b_s_swz,
-                  void *c, int64_t ld_c, int c_dtype, void *stream)
+                  void *c, int64_t ld_c, int c_dtype, void *workspace, int64_t workspace_bytes,
+                  void *stream)
 {
     const char *fn = "mx_gemm";
     mx_status st =
@@ -659,8 +709,15 @@ mx_status mx_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t ld_a
         overlap(c, ec, a_s_swz, swz_bytes(M, K / 32)) ||
         overlap(c, ec, b_s_swz, swz_bytes(N, K / 32)))
         return fail(MX_ERR_OVERLAP, "%s: C overlaps an input", fn);
+    const void *bufs[5] = {a_q, b_q, a_s_swz, b_s_swz, c};
+    const int64_t lens[5] = {extent(M, K, ld_a, 1), extent(N, K, ld_b, 1), swz_bytes(M, K / 32),
+                             swz_bytes(N, K / 32), ec};
+    const int64_t need = mx::gemm_workspace_bytes(M, N, K, c_dtype, mx::gemm_vec16(c, ld_c, c_dtype));
+    st = check_workspace(fn, workspace, workspace_bytes, need, 16, bufs, lens, 5);
+    if (st != MX_OK)
+        return st;
     return hip_status(mx::launch_gemm(M, N, K, a_q, ld_a, a_s_swz, b_q, ld_b, b_s_swz, c, ld_c,
-                                      c_dtype, (hipStream_t)stream),
+                                      c_dtype, workspace, (hipStream_t)stream),
                       fn);
 }
 
@@ -706,7 +763,8 @@ mx_status mx_grouped_gemm(int64_t num_groups, int64_t M_total, int64_t N, int64_
 mx_status mx_grouped_gemm_wgrad(int64_t num_groups, int64_t M, int64_t N, int64_t k_cap,
                                 const int64_t *k_offsets, const void *a_q, int64_t ld_a,
                                 const void *a_s_swz, const void *b_q, int64_t ld_b,
-                                const void *b_s_swz, void *c, int64_t ld_c, int c_dtype, void *stream)
+                                const void *b_s_swz, void *c, int64_t ld_c, int c_dtype, void *workspace,
+                                int64_t workspace_bytes, void *stream)
 {
     const char *fn = "mx_grouped_gemm_wgrad";
     if (num_groups < 1)
@@ -736,13 +794,21 @@ mx_status mx_grouped_gemm_wgrad(int64_t num_groups, int64_t M, int64_t N, int64_
         overlap(c, ec, a_s_swz, swz_bytes(M, k_cap / 32)) || overlap(c, ec, b_s_swz, swz_bytes(N, k_cap / 32)) ||
         overlap(c, ec, k_offsets, (num_groups + 1) * 8))
         return fail(MX_ERR_OVERLAP, "%s: C overlaps an input", fn);
+    const void *bufs[6] = {a_q, b_q, a_s_swz, b_s_swz, k_offsets, c};
+    const int64_t lens[6] = {extent(M, k_cap, ld_a, 1), extent(N, k_cap, ld_b, 1), swz_bytes(M, k_cap / 32),
+                             swz_bytes(N, k_cap / 32), (num_groups + 1) * 8, ec};
+    st = check_workspace(fn, workspace, workspace_bytes, mx::WGRAD_WORKSPACE_BYTES, 4, bufs, lens, 6);
+    if (st != MX_OK)
+        return st;
     if (debug_checks() &&
         (st = debug_offsets(fn, "k_offsets", k_offsets, num_groups, k_cap, 256, 256, false, false, stream)) != MX_OK)
         return st;
     return hip_status(mx::launch_grouped_gemm_wgrad(num_groups, M, N, k_cap, k_offsets, a_q, ld_a, a_s_swz,
-                                                    b_q, ld_b, b_s_swz, c, ld_c, c_dtype,
+                                                    b_q, ld_b, b_s_swz, c, ld_c, c_dtype, workspace,
                                                     (hipStream_t)stream),
                       fn);
 }
+
+int64_t mx_grouped_gemm_wgrad_workspace_bytes(void) { return mx::WGRAD_WORKSPACE_BYTES; }
 
 }  // extern "C"

@@ -11,9 +11,16 @@
 #include "mx_device.h"
 #include "mx_launch.h"
 
+#include <atomic>
 #include <climits>
 
 namespace mx {
+
+// Result words of the checks: a device array (no allocation), one word per
+// check in flight, taken round robin; each device holds its own copy, found
+// with hipGetSymbolAddress while that device is current.
+constexpr int DEBUG_SLOTS = 64;
+static __device__ __align__(256) int debug_flags[DEBUG_SLOTS];
 
 // One workgroup: entry g of off[0..G] fails when it is outside [0, total],
 // not a multiple of align, (first_zero) g == 0 and nonzero, (exact_end)
@@ -50,9 +57,12 @@ hipError_t check_offsets(const int64_t *off, int64_t G, int64_t total, int64_t a
                          bool first_zero, bool exact_end, hipStream_t stream, int64_t *first_bad)
 {
     *first_bad = -1;
-    int *flag = (int *)stream_workspace(stream, 256);
-    if (flag == nullptr)
-        return hipErrorOutOfMemory;
+    void *base = nullptr;
+    hipError_t e0 = hipGetSymbolAddress(&base, HIP_SYMBOL(debug_flags));
+    if (e0 != hipSuccess)
+        return e0;
+    static std::atomic<unsigned> next{0};
+    int *flag = (int *)base + next.fetch_add(1) % DEBUG_SLOTS;
     hipLaunchKernelGGL(check_offsets_kernel, dim3(1), dim3(256), 0, stream, off, G, total, align, min_len,
                        (int)first_zero, (int)exact_end, flag);
     hipError_t e = hipGetLastError();

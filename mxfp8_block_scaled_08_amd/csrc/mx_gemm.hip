@@ -48,8 +48,6 @@
 #include <algorithm>
 #include <cmath>
 #include <climits>
-#include <mutex>
-#include <vector>
 
 namespace mx {
 
@@ -966,6 +964,8 @@ static int vec16_ok(const void *c, int64_t ld_c, int c_dtype)
     return c_dtype == 0 && ((uintptr_t)c % 16 == 0) && (ld_c % 8 == 0);
 }
 
+bool gemm_vec16(const void *c, int64_t ld_c, int c_dtype) { return vec16_ok(c, ld_c, c_dtype) != 0; }
+
 // Bytes of a rearranged scale buffer: 32-row x 8-block tiles of 256 bytes.
 static int64_t scale_bytes(int64_t rows, int64_t K)
 {
@@ -990,57 +990,40 @@ static int cu_count()
     return cache[dev];
 }
 
-// Workspace (the split tail's partial tiles, the MoE permutation's counts):
-// one device buffer per (device, stream), allocated on first use and grown
-// when a call needs more, kept until the process ends.  Work on one stream
-// runs in order, so successive calls on a stream can share its buffer; calls
-// on different streams get different buffers.  A stream-ordered pool
-// allocation per call was tried first: on this runtime it blocked the host
-// until the stream caught up, which left the GPU idle behind every such call.
-// Growing waits for the stream (the old buffer may still be in use) before
-// freeing; allocation and growth happen outside graph capture only if the
-// first call on a stream is made outside it.
-void *stream_workspace(hipStream_t stream, size_t bytes)
+// Split-tail plan of a dense product.  With T tiles on P compute units the
+// last R = T mod P tiles form a partial round that leaves most units idle.
+// Each of them is cut into S K ranges (at most P / R, at most one per 256-K
+// group), one workgroup per range: the round then costs about 1/S of a
+// tile, plus writing and summing R * S partial tiles of 256 KiB.  A tile
+// costs ~1.7 us per 128-K stage and summing one partial ~0.065 us, so
+// S ~ sqrt(26 * stages / R) balances the two.  Only BF16 C stored by
+// whole-line stores (every tile full width) is split.  S depends on the
+// shape and the device's compute-unit count only, so the summation order
+// (and the bytes of C) is fixed per shape and device.
+struct SplitPlan {
+    int64_t rem = 0, S = 0;
+    int64_t bytes() const { return S >= 2 ? rem * S * (int64_t)(BM * BN * sizeof(float)) : 0; }
+};
+
+static SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int c_dtype, bool vec16, int64_t cus)
 {
-    struct Entry {
-        int dev;
-        hipStream_t stream;
-        void *ptr;
-        size_t bytes;
-    };
-    static std::mutex mu;
-    static std::vector<Entry> cache;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return nullptr;
-    std::lock_guard<std::mutex> lock(mu);
-    for (Entry &e : cache) {
-        if (e.dev != dev || e.stream != stream)
-            continue;
-        if (e.bytes >= bytes)
-            return e.ptr;
-        if (hipStreamSynchronize(stream) != hipSuccess)
-            return nullptr;
-        (void)hipFree(e.ptr);
-        e.ptr = nullptr;
-        e.bytes = 0;
-        const size_t want = std::max(bytes, (size_t)1 << 20);
-        if (hipMalloc(&e.ptr, want) != hipSuccess) {
-            (void)hipGetLastError();
-            e.ptr = nullptr;
-            return nullptr;
-        }
-        e.bytes = want;
-        return e.ptr;
+    SplitPlan sp;
+    if (M <= 0 || N <= 0 || K <= 0)
+        return sp;
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int64_t groups = (K / BK + 1) / 2;
+    const int64_t rem = tiles % cus;
+    if (rem > 0 && groups >= 2 && c_dtype == 0 && vec16 && N % BN == 0) {
+        const int64_t balance = std::max<int64_t>(2, (int64_t)std::sqrt(26.0 * 2 * groups / (double)rem));
+        sp.S = std::min<int64_t>(std::min<int64_t>(cus / rem, groups), balance);
+        sp.rem = rem;
     }
-    void *ptr = nullptr;
-    const size_t want = std::max(bytes, (size_t)1 << 20);
-    if (hipMalloc(&ptr, want) != hipSuccess) {
-        (void)hipGetLastError();
-        return nullptr;
-    }
-    cache.push_back(Entry{dev, stream, ptr, want});
-    return ptr;
+    return sp;
+}
+
+int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int c_dtype, bool vec16)
+{
+    return split_plan(M, N, K, c_dtype, vec16, cu_count()).bytes();
 }
 
 // Sums of the split tail: thread t of tile r's 16384 takes float4 t of the
@@ -1085,7 +1068,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemmParams p)
 
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t ld_a,
                        const void *a_s, const void *b_q, int64_t ld_b, const void *b_s,
-                       void *c, int64_t ld_c, int c_dtype, hipStream_t stream)
+                       void *c, int64_t ld_c, int c_dtype, void *ws, hipStream_t stream)
 {
     GemmParams p{};
     p.M = M;
@@ -1109,40 +1092,25 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t
     const int64_t cus = cu_count();
     p.dp_tiles = tiles;
     unsigned grid = (unsigned)std::min<int64_t>(tiles, cus);
-    // Split tail.  With T tiles on P compute units the last R = T mod P
-    // tiles form a partial round that leaves most units idle.  Cut each of
-    // them into S K ranges (at most P / R, at most one per 256-K group), one
-    // workgroup per range: the round then costs about 1/S of a tile, plus
-    // writing and summing R * S partial tiles of 256 KiB.  A tile costs
-    // ~1.7 us per 128-K stage and summing one partial ~0.065 us, so
-    // S ~ sqrt(26 * stages / R) balances the two.  Only BF16 C stored by
-    // whole-line stores (every tile full width) is split; without the
-    // workspace the call runs unsplit.
-    void *ws = nullptr;
-    const int64_t groups = (K / BK + 1) / 2;
-    const int64_t rem = tiles % cus;
-    if (rem > 0 && groups >= 2 && c_dtype == 0 && p.vec16 && N % BN == 0) {
-        const int64_t balance = std::max<int64_t>(2, (int64_t)std::sqrt(26.0 * 2 * groups / (double)rem));
-        const int64_t S = std::min<int64_t>(std::min<int64_t>(cus / rem, groups), balance);
-        const size_t part_bytes = (size_t)(rem * S) * (BM * BN * sizeof(float));
-        ws = S >= 2 ? stream_workspace(stream, part_bytes) : nullptr;
-        if (ws != nullptr) {
-            p.dp_tiles = tiles - rem;
-            p.split_tiles = (int)rem;
-            p.split_s = (int)S;
-            p.ws = (float *)ws;
-            grid = (unsigned)std::max<int64_t>(std::min<int64_t>(p.dp_tiles, cus), rem * S);
-        }
-        // (without a workspace the call runs unsplit)
+    // split tail (the caller's workspace holds the FP32 partial tiles; its
+    // size was checked against the plan before the launch)
+    const SplitPlan sp = split_plan(M, N, K, c_dtype, p.vec16 != 0, cus);
+    const bool split = sp.bytes() > 0;
+    if (split) {
+        p.dp_tiles = tiles - sp.rem;
+        p.split_tiles = (int)sp.rem;
+        p.split_s = (int)sp.S;
+        p.ws = (float *)ws;
+        grid = (unsigned)std::max<int64_t>(std::min<int64_t>(p.dp_tiles, cus), sp.rem * sp.S);
     }
-    if (ws != nullptr)
+    if (split)
         hipLaunchKernelGGL((mx_gemm_kernel<0, 0, true>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
     else if (c_dtype == 0)
         hipLaunchKernelGGL((mx_gemm_kernel<0, 0, false>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
     else
         hipLaunchKernelGGL((mx_gemm_kernel<0, 1, false>), dim3(grid), dim3(GM_THREADS), 0, stream, p);
     hipError_t err = hipGetLastError();
-    if (ws != nullptr) {
+    if (split) {
         if (err == hipSuccess) {
             hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)(p.split_tiles * (BM * BN / 4 / 256))),
                                dim3(256), 0, stream, p);
@@ -1198,7 +1166,7 @@ hipError_t launch_grouped_gemm_wgrad(int64_t G, int64_t M, int64_t N, int64_t K,
                                      const int64_t *k_offsets, const void *a_q, int64_t ld_a,
                                      const void *a_s, const void *b_q, int64_t ld_b,
                                      const void *b_s, void *c, int64_t ld_c, int c_dtype,
-                                     hipStream_t stream)
+                                     void *ws, hipStream_t stream)
 {
     GemmParams p{};
     p.M = M;
@@ -1222,9 +1190,7 @@ hipError_t launch_grouped_gemm_wgrad(int64_t G, int64_t M, int64_t N, int64_t K,
     p.vec16 = vec16_ok(c, ld_c, c_dtype);
     const int64_t tiles = G * p.tiles_m * p.tiles_n;
     const unsigned grid = (unsigned)std::min<int64_t>(tiles, cu_count());
-    p.counter = (int *)stream_workspace(stream, 256);
-    if (p.counter == nullptr)
-        return hipErrorOutOfMemory;
+    p.counter = (int *)ws;  // zeroed by a kernel (not a memset node), so replays of a captured call work
     hipLaunchKernelGGL(zero_counter_kernel, dim3(1), dim3(64), 0, stream, p.counter);
     if (c_dtype == 0)
         hipLaunchKernelGGL((mx_gemm_kernel<2, 0, false>), dim3(grid), dim3(GM_THREADS), 0, stream, p);

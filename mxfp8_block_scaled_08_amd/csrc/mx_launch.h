@@ -49,29 +49,41 @@ hipError_t launch_quantize_dual(const DualJob *jobs, int n, hipStream_t stream);
 hipError_t launch_scale_swizzle(const void *s, int64_t rows, int64_t kblocks, int64_t ld_s,
                                 void *s_swz, hipStream_t stream);
 
-// c_dtype: 0 = BF16, 1 = FP32 (the mx_dtype values).
+// Bytes of workspace a dense product needs for its split tail on the
+// current device (0: no split).  The split applies when the 256 x 256 tiles
+// leave a partial last round of compute units, C is BF16 and every tile is
+// full width with 16-byte stores (vec16: c 16-byte aligned, ld_c % 8 == 0,
+// N % 256 == 0).  Host-only: reads the device's compute-unit count.
+int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int c_dtype, bool vec16);
+// Whether C at c with leading dimension ld_c takes the full-line BF16 stores.
+bool gemm_vec16(const void *c, int64_t ld_c, int c_dtype);
+
+// c_dtype: 0 = BF16, 1 = FP32 (the mx_dtype values).  ws: at least
+// gemm_workspace_bytes(...) bytes, 16-byte aligned (may be null when that is 0).
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t ld_a,
                        const void *a_s, const void *b_q, int64_t ld_b, const void *b_s,
-                       void *c, int64_t ld_c, int c_dtype, hipStream_t stream);
+                       void *c, int64_t ld_c, int c_dtype, void *ws, hipStream_t stream);
 
 hipError_t launch_grouped_gemm(int64_t G, int64_t M_total, int64_t N, int64_t K,
                                const int64_t *offsets, const void *a_q, int64_t ld_a,
                                const void *a_s, const void *b_q, const void *b_s, void *c,
                                int64_t ld_c, int c_dtype, hipStream_t stream);
 
-// The current device's workspace for work on `stream`, at least `bytes`
-// long (null if it cannot be allocated): one buffer per (device, stream),
-// kept for reuse by later calls on that stream.
-void *stream_workspace(hipStream_t stream, size_t bytes);
-
 // MoE dispatch: stable order of the routed (token, expert) assignments by
 // expert, then the permuted rows gathered and quantized row-wise, scales in
 // the rearranged layout.  G <= MOE_MAX_EXPERTS, hidden % 256 == 0.
+// ws: moe_dispatch_workspace_bytes(...) bytes, 4-byte aligned (the
+// per-chunk expert counts; every byte is rewritten before it is read).
 constexpr int MOE_MAX_EXPERTS = 1024;
+constexpr int MOE_CHUNK = 256;  // routing assignments per counting workgroup
+inline int64_t moe_dispatch_workspace_bytes(int64_t tokens, int64_t topk, int64_t experts)
+{
+    return (tokens * topk + MOE_CHUNK - 1) / MOE_CHUNK * experts * 4;
+}
 hipError_t launch_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
                                const int32_t *topk_ids, int64_t topk, int64_t experts,
                                int64_t *offsets, int32_t *src_token, int32_t *slot, void *q,
-                               int64_t ld_q, void *s_swz, hipStream_t stream);
+                               int64_t ld_q, void *s_swz, void *ws, hipStream_t stream);
 
 // MoE combine: out[t] = sum_j weights[t][j] * y[slot[t][j]] (slots < 0 skipped).
 hipError_t launch_moe_combine(const void *y, int64_t tokens, int64_t hidden, int64_t ld_y,
@@ -93,12 +105,14 @@ hipError_t launch_quantize_colwise_grouped(const void *x, int64_t rows, int64_t 
 
 // Per-expert product along K: C_g = A[:, r_g] . B[:, r_g]^T for the column
 // ranges r_g = [k_offsets[g], k_offsets[g+1]), C_g at c + g * M * ld_c.
-// K % 256 == 0, G <= MOE_MAX_EXPERTS.
+// K % 256 == 0, G <= MOE_MAX_EXPERTS.  ws: WGRAD_WORKSPACE_BYTES, 4-byte
+// aligned (the tile counter, cleared by a kernel before the product).
+constexpr int64_t WGRAD_WORKSPACE_BYTES = 256;
 hipError_t launch_grouped_gemm_wgrad(int64_t G, int64_t M, int64_t N, int64_t K,
                                      const int64_t *k_offsets, const void *a_q, int64_t ld_a,
                                      const void *a_s, const void *b_q, int64_t ld_b,
                                      const void *b_s, void *c, int64_t ld_c, int c_dtype,
-                                     hipStream_t stream);
+                                     void *ws, hipStream_t stream);
 
 // SwiGLU of gu's halves ([0, F) gate, [F, 2F) up) fused with the row-wise
 // quantization of the BF16 result; h (BF16 [rows][ld_h]) stored when not
@@ -107,7 +121,7 @@ hipError_t launch_swiglu_quantize(const void *gu, int64_t rows, int64_t F, int64
                                   int64_t ld_h, void *q, int64_t ld_q, void *s_swz, hipStream_t stream);
 
 // Debug check of device offsets off[0..G] (see mx_debug.hip): waits for the
-// stream, then *first_bad = the first entry breaking the stated properties
+// stream (the one wait in the library, under MX_DEBUG only), then *first_bad = the first entry breaking the stated properties
 // (in [0, total], multiple of align, ranges at least min_len long,
 // off[0] == 0 if first_zero, off[G] == total if exact_end), or -1.
 hipError_t check_offsets(const int64_t *off, int64_t G, int64_t total, int64_t align, int64_t min_len,

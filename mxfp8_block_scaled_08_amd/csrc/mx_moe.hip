@@ -28,7 +28,7 @@
 
 namespace mx {
 
-constexpr int MOE_CHUNK = 256;
+// MOE_CHUNK (mx_launch.h): routing assignments per counting workgroup
 
 __global__ __launch_bounds__(MOE_CHUNK) void moe_count_kernel(const int32_t *__restrict__ ids, int64_t n,
                                                                int experts, int32_t *__restrict__ counts)
@@ -190,14 +190,11 @@ __global__ __launch_bounds__(MOE_Q_THREADS) void moe_gather_quantize_kernel(
 hipError_t launch_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
                                const int32_t *topk_ids, int64_t topk, int64_t experts,
                                int64_t *offsets, int32_t *src_token, int32_t *slot, void *q,
-                               int64_t ld_q, void *s_swz, hipStream_t stream)
+                               int64_t ld_q, void *s_swz, void *ws, hipStream_t stream)
 {
     const int64_t n = tokens * topk;
     const int64_t chunks = (n + MOE_CHUNK - 1) / MOE_CHUNK;
-    void *ws = stream_workspace(stream, (size_t)(chunks * experts) * sizeof(int32_t));
-    if (ws == nullptr)
-        return hipErrorOutOfMemory;
-    int32_t *counts = (int32_t *)ws;
+    int32_t *counts = (int32_t *)ws;  // [chunks][experts], every entry written by moe_count_kernel
     hipLaunchKernelGGL(moe_count_kernel, dim3((unsigned)chunks), dim3(MOE_CHUNK), 0, stream, topk_ids, n,
                        (int)experts, counts);
     hipLaunchKernelGGL(moe_scan_chunks_kernel, dim3((unsigned)experts), dim3(MOE_SCAN_THREADS), 0, stream,

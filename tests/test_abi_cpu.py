@@ -38,7 +38,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for n in names:
         assert hasattr(raw, n), f"{n} declared in include/mxfp8.h but not exported"
         assert hasattr(mx, n), f"{n} has no Python binding of the same name"
-    assert L.mx_abi_version() == 6
+    assert L.mx_abi_version() == 7
 
 
 def test_status_strings():
@@ -171,12 +171,12 @@ def test_gemm_validation():
     L = mx.load()
     g = L.mx_gemm
     ok_args = dict(M=64, N=64, K=256, a=FAKE, lda=256, sa=FAKE2, b=FAKE3, ldb=256, sb=FAKE4,
-                   c=FAKE4 + (1 << 20), ldc=64, dt=mx.MX_BF16)
+                   c=FAKE4 + (1 << 20), ldc=64, dt=mx.MX_BF16, ws=0, wsb=0)
 
     def call(**kw):
         a = dict(ok_args, **kw)
         return g(a["M"], a["N"], a["K"], a["a"], a["lda"], a["sa"], a["b"], a["ldb"], a["sb"],
-                 a["c"], a["ldc"], a["dt"], STREAM)
+                 a["c"], a["ldc"], a["dt"], a["ws"], a["wsb"], STREAM)
 
     assert call(K=96) == mx.MX_ERR_UNSUPPORTED
     assert call(K=100, lda=112, ldb=112) == mx.MX_ERR_SHAPE
@@ -193,6 +193,38 @@ def test_gemm_validation():
     assert call(c=FAKE + 128) == mx.MX_ERR_OVERLAP
     assert call(M=0) == mx.MX_OK
     assert call(N=0) == mx.MX_OK
+    assert call(wsb=-1) == mx.MX_ERR_INVALID_ARG
+
+
+WS = 1 << 36  # fake 256-byte aligned workspace address, far from the operands
+
+
+def test_gemm_workspace():
+    """The split tail's scratch comes from the caller: sized by a host-only
+    query, checked for size, alignment and overlap before any launch."""
+    L = mx.load()
+    q = L.mx_gemm_workspace_bytes
+    # 4608 x 4096: 18 x 16 = 288 tiles on 256 compute units (the count this
+    # build assumes without a device, and MI355X's) leave 32 tiles; K = 4096
+    # has 16 256-K groups: S = min(256 / 32, 16, max(2, floor(sqrt(26 * 2 * 16 / 32)))) = 5
+    assert q(4608, 4096, 4096, mx.MX_BF16) == 32 * 5 * 256 * 256 * 4
+    assert q(4608, 4096, 4096, mx.MX_F32) == 0          # FP32 C is never split
+    assert q(4096, 4096, 4096, mx.MX_BF16) == 0         # 256 tiles: whole rounds
+    assert q(4608, 4100, 4096, mx.MX_BF16) == 0         # ragged N: not split
+    assert q(4608, 4096, 256, mx.MX_BF16) == 0          # one 256-K group: nothing to split
+    assert q(0, 4096, 4096, mx.MX_BF16) == 0 and q(64, 64, 100, mx.MX_BF16) == 0
+    need = q(4608, 4096, 4096, mx.MX_BF16)
+    g = L.mx_gemm
+    M, N, K = 4608, 4096, 4096
+    args = lambda ws, wsb, c=FAKE4 + (1 << 20): (M, N, K, FAKE, K, FAKE2, FAKE3, K, FAKE4, c, N, mx.MX_BF16,
+                                                ws, wsb, STREAM)
+    assert g(*args(0, 0)) == mx.MX_ERR_INVALID_ARG
+    assert f"needs a workspace of {need} bytes" in _err(L)
+    assert g(*args(WS, need - 1)) == mx.MX_ERR_INVALID_ARG
+    assert g(*args(WS + 8, need)) == mx.MX_ERR_ALIGN
+    # the workspace over C, and over A's codes
+    assert g(*args(FAKE4 + (2 << 20), need)) == mx.MX_ERR_OVERLAP
+    assert g(*args(FAKE + 4096, need)) == mx.MX_ERR_OVERLAP
 
 
 def test_grouped_gemm_validation():
@@ -262,7 +294,8 @@ def test_grouped_gemm_wgrad_validation():
                          kw.get("off", FAKE), kw.get("a", FAKE2), kw.get("ld_a", 2048),
                          kw.get("a_s", FAKE2 + (1 << 24)), kw.get("b", FAKE3),
                          kw.get("ld_b", 2048), kw.get("b_s", FAKE3 + (1 << 24)),
-                         kw.get("c", FAKE4), kw.get("ld_c", 128), kw.get("dt", mx.MX_BF16), STREAM]
+                         kw.get("c", FAKE4), kw.get("ld_c", 128), kw.get("dt", mx.MX_BF16),
+                         kw.get("ws", WS), kw.get("wsb", 256), STREAM]
     assert f(*args(G=0)) == mx.MX_ERR_INVALID_ARG
     assert f(*args(G=2000)) == mx.MX_ERR_UNSUPPORTED
     assert f(*args(K=2048 + 128, ld_a=2304, ld_b=2304)) == mx.MX_ERR_SHAPE
@@ -281,8 +314,53 @@ def test_grouped_gemm_wgrad_validation():
     assert f(*args(G=1024, M=1 << 19, N=1 << 18, ld_c=1 << 18, K=256, ld_a=256, ld_b=256)) == \
         mx.MX_ERR_UNSUPPORTED
     assert "tiles" in _err(L)
+    # the tile counter lives in the caller's workspace
+    assert L.mx_grouped_gemm_wgrad_workspace_bytes() == 256
+    assert f(*args(ws=0, wsb=0)) == mx.MX_ERR_INVALID_ARG
+    assert "workspace of 256 bytes" in _err(L)
+    assert f(*args(wsb=255)) == mx.MX_ERR_INVALID_ARG
+    assert f(*args(ws=WS + 2)) == mx.MX_ERR_ALIGN
+    assert f(*args(ws=FAKE4 + 512)) == mx.MX_ERR_OVERLAP       # inside C
+    assert f(*args(ws=FAKE + 8)) == mx.MX_ERR_OVERLAP          # over the offsets
     # empty products succeed without a launch
     assert f(*args(M=0)) == mx.MX_OK
+
+
+def test_moe_dispatch_validation():
+    L = mx.load()
+    q = L.mx_moe_dispatch_workspace_bytes
+    # one int32 count per (256-assignment chunk, expert)
+    assert q(20480, 8, 128) == 640 * 128 * 4
+    assert q(1, 1, 1) == 4 and q(257, 1, 2) == 2 * 2 * 4
+    assert q(0, 8, 128) == 0 and q(10, 8, 2000) == 0
+    f = L.mx_moe_dispatch
+    T, H, TK, E = 1000, 256, 8, 16
+    need = q(T, TK, E)
+    # x, tokens, hidden, ld_x, topk_ids, topk, experts, offsets, src, slot, q, ld_q, s_swz, ws, wsb
+    base = dict(x=FAKE, T=T, H=H, ldx=H, ids=FAKE2, TK=TK, E=E, off=FAKE2 + (1 << 20),
+                src=FAKE2 + (2 << 20), slot=FAKE2 + (3 << 20), q=FAKE3, ldq=H, s=FAKE4, ws=WS, wsb=need)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["x"], a["T"], a["H"], a["ldx"], a["ids"], a["TK"], a["E"], a["off"], a["src"],
+                 a["slot"], a["q"], a["ldq"], a["s"], a["ws"], a["wsb"], STREAM)
+
+    assert call(T=-1) == mx.MX_ERR_INVALID_ARG
+    assert call(TK=0) == mx.MX_ERR_INVALID_ARG
+    assert call(H=100, ldx=112, ldq=112) == mx.MX_ERR_SHAPE
+    assert call(H=96, ldx=96, ldq=96) == mx.MX_ERR_UNSUPPORTED
+    assert call(E=2000) == mx.MX_ERR_UNSUPPORTED
+    assert call(ldq=128) == mx.MX_ERR_INVALID_ARG
+    assert call(q=0) == mx.MX_ERR_INVALID_ARG
+    assert call(x=FAKE + 8) == mx.MX_ERR_ALIGN
+    assert call(off=FAKE2 + (1 << 20) + 4) == mx.MX_ERR_ALIGN
+    assert call(src=FAKE3 + 64) == mx.MX_ERR_OVERLAP              # inside q
+    # the chunk counts live in the caller's workspace
+    assert call(ws=0, wsb=0) == mx.MX_ERR_INVALID_ARG
+    assert f"workspace of {need} bytes" in _err(L)
+    assert call(wsb=need - 4) == mx.MX_ERR_INVALID_ARG
+    assert call(ws=WS + 2) == mx.MX_ERR_ALIGN
+    assert call(ws=FAKE3 + 4096) == mx.MX_ERR_OVERLAP            # over q
 
 
 def test_quantize_dual_experts_validation():

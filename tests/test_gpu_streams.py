@@ -1,7 +1,9 @@
-"""Calls on different streams: each stream gets its own workspace, so a
-split-tail GEMM, a MoE dispatch and a weight gradient issued on two streams
-at once give the same bytes as the same calls on one stream.  The result of
-every call is deterministic, so the comparison is exact."""
+"""Calls on different streams: a split-tail GEMM, a MoE dispatch and a
+weight gradient issued on two streams at once, each call with its own
+workspace (the binding takes one from torch's allocator for the current
+stream when none is passed), give the same bytes as the same calls on one
+stream.  The result of every call is deterministic, so the comparison is
+exact."""
 import numpy as np
 import pytest
 import torch
@@ -44,7 +46,7 @@ def test_two_streams_match_one(gpu_lib):
     torch.cuda.synchronize()
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     outs = [mk(), mk()]
-    for rep in range(2):          # the first round also makes the streams' workspaces
+    for rep in range(2):
         for s, o in zip((s1, s2), outs):
             s.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(s):

@@ -6,9 +6,10 @@ rearranged scales, per-expert column-wise quantization and the weight
 gradient, plus a dense GEMM with a split tail -- is run eagerly, then captured
 into a graph on the same stream and replayed three times with eager work and
 synchronizations between the replays.  Every output is deterministic, so
-every replay must reproduce the eager bytes exactly.  The eager run comes
-first on the capture stream, so the library's per-stream workspace exists
-before capture (its set-up is the one step that must not be captured).
+every replay must reproduce the eager bytes exactly.  The calls that need
+scratch memory take one caller-owned workspace; the library holds no state,
+so a graph whose capture holds the very first calls of the process's stream
+(test_first_calls_inside_capture) replays as exactly.
 """
 import numpy as np
 import pytest
@@ -23,7 +24,7 @@ def _pass(mx, I, o):
     mx.mx_quantize_dual_experts(I["w_gu"], q=o["wgu_q"], s_swz=o["wgu_s"], qt=o["wgu_qt"], st_swz=o["wgu_st"])
     mx.mx_quantize_dual_experts(I["w_dn"], q=o["wdn_q"], s_swz=o["wdn_s"], qt=o["wdn_qt"], st_swz=o["wdn_st"])
     mx.mx_moe_dispatch(I["x"], I["ids"], I["G"], offsets=o["off"], src=o["src"], slot=o["slot"],
-                       q=o["xq"], s_swz=o["xs"])
+                       q=o["xq"], s_swz=o["xs"], workspace=I["ws"])
     mx.mx_grouped_gemm(o["off"], o["xq"], o["xs"], o["wgu_q"], o["wgu_s"], c=o["gu"])
     mx.mx_swiglu_quantize(o["gu"], q=o["hq"], s_swz=o["hs"], h=o["h"])
     mx.mx_grouped_gemm(o["off"], o["hq"], o["hs"], o["wdn_q"], o["wdn_s"], c=o["dn"])
@@ -34,14 +35,13 @@ def _pass(mx, I, o):
                                    pad_offsets=o["pad"])
     mx.mx_quantize_colwise_grouped(o["h"], o["off"], k_cap=I["k_cap"], qt=o["hT"], st_swz=o["hTs"],
                                    pad_offsets=o["pad2"])
-    mx.mx_grouped_gemm_wgrad(o["pad"], o["dyT"], o["dyTs"], o["hT"], o["hTs"], c=o["dw"])
+    mx.mx_grouped_gemm_wgrad(o["pad"], o["dyT"], o["dyTs"], o["hT"], o["hTs"], c=o["dw"], workspace=I["ws"])
     # a dense product whose tile count leaves a partial round: split tail
-    mx.mx_gemm(o["dyq"][:1280], o["dys"], o["wgu_qt"][0], o["wgu_st"], c=o["dense"])
+    mx.mx_gemm(o["dyq"][:1280], o["dys"], o["wgu_qt"][0], o["wgu_st"], c=o["dense"], workspace=I["ws"])
 
 
-def test_graph_replays_match_eager(gpu_lib):
-    mx = gpu_lib
-    dev = "cuda"
+def _setup(mx, dev="cuda"):
+    """Inputs I (with the shared workspace I["ws"]) and output buffers o."""
     T, H, F, G, k = 640, 512, 256, 8, 4
     rng = np.random.default_rng(9)
     ids = np.stack([rng.choice(G, size=k, replace=False) for _ in range(T)]).astype(np.int32)
@@ -71,33 +71,69 @@ def test_graph_replays_match_eager(gpu_lib):
              pad=torch.empty(G + 1, dtype=torch.int64, device=dev),
              pad2=torch.empty(G + 1, dtype=torch.int64, device=dev),
              dw=torch.empty(G, H, F, **bf), dense=torch.empty(1280, H, **bf))
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        _pass(mx, I, o)                     # eager, and the stream's workspace
-    torch.cuda.synchronize()
-    # only the bytes each call defines: the codes past pad[G] and the GEMM rows
-    # of unrouted assignments are not written by design
-    pend = int(o["pad"][-1])
-    def written(k_):
-        t = o[k_]
-        if k_ in ("dyT", "hT"):
-            return t[:, :pend]
-        if k_ in ("dyTs", "hTs"):                     # [32-row tiles][k_cap/256 tiles][256]
-            return t.view(-1, I["k_cap"] // 256, 256)[:, :pend // 256]
-        return t
+    assert mx.mx_gemm_workspace_bytes(1280, H, 2 * F) > 0, "the dense product must take the split tail"
+    I["ws"] = torch.empty(max(mx.mx_gemm_workspace_bytes(1280, H, 2 * F), mx.mx_moe_dispatch_workspace_bytes(T, k, G),
+                              mx.mx_grouped_gemm_wgrad_workspace_bytes()), **u8)
+    return I, o
 
+
+def _written(I, o, k_):
+    """Only the bytes each call defines: the codes past pad[G] and the GEMM
+    rows of unrouted assignments are not written by design."""
+    t = o[k_]
+    pend = int(o["pad"][-1])
+    if k_ in ("dyT", "hT"):
+        return t[:, :pend]
+    if k_ in ("dyTs", "hTs"):                     # [32-row tiles][k_cap/256 tiles][256]
+        return t.view(-1, I["k_cap"] // 256, 256)[:, :pend // 256]
+    return t
+
+
+def _replay_and_compare(g, I, o, ref):
     keys = list(o)
-    ref = {k_: written(k_).clone() for k_ in keys}
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=s):
-        _pass(mx, I, o)
     for rep in range(3):
         for k_ in keys:                     # eager work between replays: clobber the outputs
             o[k_].view(torch.uint8).fill_(0xA5)
+        I["ws"].fill_(0x5A)                 # and the workspace
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         for k_ in keys:
-            assert torch.equal(written(k_).contiguous().view(torch.uint8),
+            assert torch.equal(_written(I, o, k_).contiguous().view(torch.uint8),
                                ref[k_].contiguous().view(torch.uint8)), f"replay {rep}: {k_} differs"
+
+
+def test_graph_replays_match_eager(gpu_lib):
+    mx = gpu_lib
+    I, o = _setup(mx)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _pass(mx, I, o)                     # eager
+    torch.cuda.synchronize()
+    ref = {k_: _written(I, o, k_).clone() for k_ in o}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        _pass(mx, I, o)
+    _replay_and_compare(g, I, o, ref)
+
+
+def test_first_calls_inside_capture(gpu_lib):
+    """A fresh stream whose first library calls are made inside capture; the
+    eager reference runs afterwards on another stream with its own buffers."""
+    mx = gpu_lib
+    I, o = _setup(mx)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        _pass(mx, I, o)
+    I2, o2 = _setup(mx)
+    s2 = torch.cuda.Stream()
+    s2.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s2):
+        _pass(mx, I2, o2)
+    torch.cuda.synchronize()
+    ref = {k_: _written(I2, o2, k_).clone() for k_ in o2}
+    _replay_and_compare(g, I, o, ref)
