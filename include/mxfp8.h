@@ -322,6 +322,28 @@ mx_status mx_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t
                           void *s_swz, void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * mx_moe_dispatch for callers that cannot allocate any memory, not even a
+ * workspace (code under HIP graph capture that may not touch an allocator,
+ * tight serving loops, harnesses that forbid allocation): the same
+ * arguments, requirements and results without the workspace.  Its chunk
+ * counts live in a device array of MX_MOE_DISPATCH_NOALLOC_SCRATCH_BYTES
+ * (4 MiB) that the library holds on each GPU it runs on until the process
+ * ends; a call needing more, mx_moe_dispatch_workspace_bytes(tokens, topk,
+ * num_experts) > 4 MiB (e.g. beyond 262 144 tokens of top-8 over 128
+ * experts), returns MX_ERR_UNSUPPORTED without launching.  The first call on
+ * a device looks up that device's copy (no allocation, no wait).  Every call
+ * on one GPU uses the same array: calls that may run at the same time on
+ * one GPU (different streams, concurrent graph replays) race and give
+ * unspecified results; calls ordered on one stream do not.  Every count a
+ * call reads it has first written, so nothing needs clearing between calls.
+ */
+#define MX_MOE_DISPATCH_NOALLOC_SCRATCH_BYTES ((int64_t)4 << 20)
+mx_status mx_moe_dispatch_noalloc(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
+                                  const int32_t *topk_ids, int64_t topk, int64_t num_experts,
+                                  int64_t *offsets, int32_t *src_token, int32_t *slot, void *q,
+                                  int64_t ld_q, void *s_swz, void *stream);
+
+/*
  * The SwiGLU between the MoE expert projections (Qwen3's expert MLP; paper
  * Table 2: Qwen3-30B-A3B) fused with the row-wise quantization of its output,
  * the down projection's A operand (paper Figure 1: BF16 activations quantized

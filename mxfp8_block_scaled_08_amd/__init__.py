@@ -27,7 +27,7 @@ __all__ = [
     "mx_moe_dispatch", "mx_moe_combine", "mx_grouped_k_capacity", "mx_quantize_colwise_grouped",
     "mx_grouped_gemm_wgrad", "mx_swiglu_quantize", "mx_quantize_rowwise_swz",
     "mx_quantize_dual_grouped", "mx_gemm_workspace_bytes", "mx_moe_dispatch_workspace_bytes",
-    "mx_grouped_gemm_wgrad_workspace_bytes", "MX_OK", "MX_ERR_INVALID_ARG", "MX_ERR_SHAPE", "MX_ERR_ALIGN",
+    "mx_grouped_gemm_wgrad_workspace_bytes", "mx_moe_dispatch_noalloc", "MX_OK", "MX_ERR_INVALID_ARG", "MX_ERR_SHAPE", "MX_ERR_ALIGN",
     "MX_ERR_OVERLAP", "MX_ERR_UNSUPPORTED", "MX_ERR_HIP", "MX_BF16", "MX_F32",
 ]
 
@@ -86,6 +86,9 @@ def load() -> ctypes.CDLL:
     L.mx_quantize_dual_batch.restype = ctypes.c_int
     L.mx_moe_dispatch.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64,
                                   _vp, _vp, _i64, _vp]
+    L.mx_moe_dispatch_noalloc.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp,
+                                          _i64, _vp, _vp]
+    L.mx_moe_dispatch_noalloc.restype = ctypes.c_int
     L.mx_moe_dispatch_workspace_bytes.restype = _i64
     L.mx_moe_dispatch_workspace_bytes.argtypes = [_i64, _i64, _i64]
     L.mx_moe_dispatch.restype = ctypes.c_int
@@ -343,6 +346,27 @@ def mx_moe_dispatch(x: torch.Tensor, topk_ids: torch.Tensor, num_experts: int,
                                 _dev(offsets, "offsets"), _dev(src, "src"), _dev(slot, "slot"),
                                 _dev(q, "q"), _ld(q, "q"), _dev(s_swz, "s_swz"), wp, wb, _stream(stream))
     _check("mx_moe_dispatch", st)
+    return offsets, src, slot, q, s_swz
+
+
+def mx_moe_dispatch_noalloc(x: torch.Tensor, topk_ids: torch.Tensor, num_experts: int,
+                            offsets: torch.Tensor, src: torch.Tensor, slot: torch.Tensor,
+                            q: torch.Tensor, s_swz: torch.Tensor, stream=None):
+    """mx_moe_dispatch without a workspace (its chunk counts in the library's
+    device array): every output is passed in, so the call allocates nothing."""
+    tokens, hidden = x.shape
+    if topk_ids.dim() != 2 or topk_ids.shape[0] != tokens or not topk_ids.is_contiguous():
+        raise ValueError("topk_ids must be a contiguous [tokens][topk] tensor")
+    topk = topk_ids.shape[1]
+    n = tokens * topk
+    if offsets.numel() != num_experts + 1 or src.numel() != n or slot.numel() != n:
+        raise ValueError("offsets, src and slot must have num_experts+1, n and n entries")
+    st = load().mx_moe_dispatch_noalloc(_dev(x, "x", torch.bfloat16), tokens, hidden, _ld(x, "x"),
+                                        _dev(topk_ids, "topk_ids", torch.int32), topk, num_experts,
+                                        _dev(offsets, "offsets", torch.int64), _dev(src, "src", torch.int32),
+                                        _dev(slot, "slot", torch.int32), _dev(_u8(q), "q", torch.uint8),
+                                        _ld(q, "q"), _dev(_u8(s_swz), "s_swz", torch.uint8), _stream(stream))
+    _check("mx_moe_dispatch_noalloc", st)
     return offsets, src, slot, q, s_swz
 
 

@@ -380,12 +380,16 @@ mx_status mx_quantize_dual_experts(const void *x, int64_t num_experts, int64_t r
     return hip_status(mx::launch_quantize_dual(&dj, 1, (hipStream_t)stream), fn);
 }
 
-mx_status mx_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
-                          const int32_t *topk_ids, int64_t topk, int64_t num_experts,
-                          int64_t *offsets, int32_t *src_token, int32_t *slot, void *q, int64_t ld_q,
-                          void *s_swz, void *workspace, int64_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Arguments of the MoE dispatch (both entry points): MX_OK or the first problem.
+mx_status check_dispatch(const char *fn, const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
+                         const int32_t *topk_ids, int64_t topk, int64_t num_experts, int64_t *offsets,
+                         int32_t *src_token, int32_t *slot, void *q, int64_t ld_q, void *s_swz,
+                         const void **bufs, int64_t *lens)
 {
-    const char *fn = "mx_moe_dispatch";
     if (tokens < 0 || hidden < 0 || topk < 1 || num_experts < 1)
         return fail(MX_ERR_INVALID_ARG, "%s: need tokens, hidden >= 0, topk, num_experts >= 1", fn);
     if (hidden % 32 != 0)
@@ -416,20 +420,73 @@ mx_status mx_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t
     if (!aligned(topk_ids, 4) || !aligned(src_token, 4) || !aligned(slot, 4) || !aligned(offsets, 8))
         return fail(MX_ERR_ALIGN, "%s: index arrays need their natural alignment", fn);
     const int64_t n = tokens * topk;
-    const void *bufs[7] = {x, topk_ids, offsets, src_token, slot, q, s_swz};
-    const int64_t lens[7] = {extent(tokens, hidden, ld_x, 2), n * 4, (num_experts + 1) * 8, n * 4, n * 4,
-                             extent(n, hidden, ld_q, 1), swz_bytes(n, hidden / 32)};
+    const void *b7[7] = {x, topk_ids, offsets, src_token, slot, q, s_swz};
+    const int64_t l7[7] = {extent(tokens, hidden, ld_x, 2), n * 4, (num_experts + 1) * 8, n * 4, n * 4,
+                           extent(n, hidden, ld_q, 1), swz_bytes(n, hidden / 32)};
+    for (int i = 0; i < 7; i++) {
+        bufs[i] = b7[i];
+        lens[i] = l7[i];
+    }
     for (int i = 0; i < 7; i++)
         for (int k = i + 1; k < 7; k++)
             if ((i >= 2 || k >= 2) && overlap(bufs[i], lens[i], bufs[k], lens[k]))
                 return fail(MX_ERR_OVERLAP, "%s: buffers %d and %d overlap", fn, i, k);
-    const mx_status wst = check_workspace(fn, workspace, workspace_bytes,
-                                          mx::moe_dispatch_workspace_bytes(tokens, topk, num_experts), 4,
-                                          bufs, lens, 7);
-    if (wst != MX_OK)
-        return wst;
+    return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mx_status mx_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
+                          const int32_t *topk_ids, int64_t topk, int64_t num_experts,
+                          int64_t *offsets, int32_t *src_token, int32_t *slot, void *q, int64_t ld_q,
+                          void *s_swz, void *workspace, int64_t workspace_bytes, void *stream)
+{
+    const char *fn = "mx_moe_dispatch";
+    const void *bufs[7];
+    int64_t lens[7];
+    mx_status st = check_dispatch(fn, x, tokens, hidden, ld_x, topk_ids, topk, num_experts, offsets, src_token,
+                                  slot, q, ld_q, s_swz, bufs, lens);
+    if (st != MX_OK)
+        return st;
+    st = check_workspace(fn, workspace, workspace_bytes, mx::moe_dispatch_workspace_bytes(tokens, topk, num_experts),
+                         4, bufs, lens, 7);
+    if (st != MX_OK)
+        return st;
     return hip_status(mx::launch_moe_dispatch(x, tokens, hidden, ld_x, topk_ids, topk, num_experts,
                                               offsets, src_token, slot, q, ld_q, s_swz, workspace,
+                                              (hipStream_t)stream),
+                      fn);
+}
+
+mx_status mx_moe_dispatch_noalloc(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
+                                  const int32_t *topk_ids, int64_t topk, int64_t num_experts,
+                                  int64_t *offsets, int32_t *src_token, int32_t *slot, void *q, int64_t ld_q,
+                                  void *s_swz, void *stream)
+{
+    const char *fn = "mx_moe_dispatch_noalloc";
+    const void *bufs[7];
+    int64_t lens[7];
+    mx_status st = check_dispatch(fn, x, tokens, hidden, ld_x, topk_ids, topk, num_experts, offsets, src_token,
+                                  slot, q, ld_q, s_swz, bufs, lens);
+    if (st != MX_OK)
+        return st;
+    const int64_t need = mx::moe_dispatch_workspace_bytes(tokens, topk, num_experts);
+    static_assert(mx::MOE_NOALLOC_SCRATCH_BYTES == MX_MOE_DISPATCH_NOALLOC_SCRATCH_BYTES,
+                  "the header states the scratch size");
+    if (need > mx::MOE_NOALLOC_SCRATCH_BYTES)
+        return fail(MX_ERR_UNSUPPORTED,
+                    "%s: %lld tokens x top-%lld over %lld experts need %lld bytes of scratch, more than the "
+                    "%lld this entry point holds (use mx_moe_dispatch with a workspace)",
+                    fn, (long long)tokens, (long long)topk, (long long)num_experts, (long long)need,
+                    (long long)mx::MOE_NOALLOC_SCRATCH_BYTES);
+    void *scratch = nullptr;
+    const hipError_t e = mx::moe_noalloc_scratch(&scratch);
+    if (e != hipSuccess)
+        return fail(MX_ERR_HIP, "%s: device scratch lookup failed: %s", fn, hipGetErrorString(e));
+    return hip_status(mx::launch_moe_dispatch(x, tokens, hidden, ld_x, topk_ids, topk, num_experts,
+                                              offsets, src_token, slot, q, ld_q, s_swz, scratch,
                                               (hipStream_t)stream),
                       fn);
 }

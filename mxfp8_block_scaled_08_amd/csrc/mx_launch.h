@@ -85,6 +85,11 @@ hipError_t launch_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, in
                                int64_t *offsets, int32_t *src_token, int32_t *slot, void *q,
                                int64_t ld_q, void *s_swz, void *ws, hipStream_t stream);
 
+// The current device's copy of the dispatch's static scratch array
+// (MOE_NOALLOC_SCRATCH_BYTES), looked up once per device.
+constexpr int64_t MOE_NOALLOC_SCRATCH_BYTES = (int64_t)4 << 20;
+hipError_t moe_noalloc_scratch(void **ptr);
+
 // MoE combine: out[t] = sum_j weights[t][j] * y[slot[t][j]] (slots < 0 skipped).
 hipError_t launch_moe_combine(const void *y, int64_t tokens, int64_t hidden, int64_t ld_y,
                               const int32_t *slot, const float *weights, int64_t topk, void *out,

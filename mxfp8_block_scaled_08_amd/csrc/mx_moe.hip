@@ -24,6 +24,8 @@
 #include "mx_device.h"
 #include "mx_launch.h"
 
+#include <mutex>
+
 #include <algorithm>
 
 namespace mx {
@@ -185,6 +187,37 @@ __global__ __launch_bounds__(MOE_Q_THREADS) void moe_gather_quantize_kernel(
                 (uint8_t)c;
         }
     }
+}
+
+// Scratch of mx_moe_dispatch_noalloc: the chunk counts of the stable sort in
+// a device array instead of a caller's workspace, for callers that cannot
+// allocate.  Each device holds its own copy for the life of the process; in
+// host code `scratch` names a host-side stand-in, so the device address is
+// looked up (hipGetSymbolAddress) once per device, with that device
+// current, and only that address is handed to kernels.
+static __device__ __align__(256) int32_t scratch[MOE_NOALLOC_SCRATCH_BYTES / 4];
+
+hipError_t moe_noalloc_scratch(void **ptr)
+{
+    constexpr int MAX_DEVICES = 64;
+    static std::mutex mu;
+    static void *per_device[MAX_DEVICES];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= MAX_DEVICES)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (per_device[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        per_device[dev] = p;
+    }
+    *ptr = per_device[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,

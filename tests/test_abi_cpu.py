@@ -434,3 +434,32 @@ def test_quantize_dual_grouped_validation():
     assert call(k_cap=cap - 256, ld_qt=cap) == mx.MX_ERR_INVALID_ARG
     assert call(ld_q=1 << 24) == mx.MX_ERR_UNSUPPORTED
     assert call(ld_x=1 << 22) == mx.MX_ERR_UNSUPPORTED
+
+
+def test_moe_dispatch_noalloc_validation():
+    """The variant without a workspace checks its arguments like
+    mx_moe_dispatch and refuses routings whose chunk counts would not fit its
+    4 MiB device array, before any launch."""
+    L = mx.load()
+    f = L.mx_moe_dispatch_noalloc
+    H, TK = 256, 8
+
+    def call(T, E, **kw):
+        a = dict(x=FAKE, ids=FAKE2, off=FAKE2 + (64 << 20), src=FAKE2 + (128 << 20),
+                 slot=FAKE2 + (192 << 20), q=FAKE3, s=FAKE4)
+        a.update(kw)
+        return f(a["x"], T, H, H, a["ids"], TK, E, a["off"], a["src"], a["slot"], a["q"], H, a["s"], STREAM)
+
+    # 262 144 assignments over 1024 experts: 1024 chunks x 1024 x 4 bytes = 4 MiB
+    assert L.mx_moe_dispatch_workspace_bytes(32768, TK, 1024) == 4 << 20
+    # one chunk more does not fit
+    assert L.mx_moe_dispatch_workspace_bytes(32800, TK, 1024) > 4 << 20
+    assert call(32800, 1024) == mx.MX_ERR_UNSUPPORTED
+    assert "4194304" in _err(L) and "mx_moe_dispatch" in _err(L)
+    assert call(300000, 128) == mx.MX_ERR_UNSUPPORTED
+    # the same argument checks as mx_moe_dispatch
+    assert call(-1, 16) == mx.MX_ERR_INVALID_ARG
+    assert call(100, 2000) == mx.MX_ERR_UNSUPPORTED
+    assert call(100, 16, q=0) == mx.MX_ERR_INVALID_ARG
+    assert call(100, 16, x=FAKE + 8) == mx.MX_ERR_ALIGN
+    assert call(100, 16, src=FAKE3 + 64) == mx.MX_ERR_OVERLAP
