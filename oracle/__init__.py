@@ -4,11 +4,21 @@ TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import it; the library in
 ``mxfp8_block_scaled_08_amd`` never does and shares no code with it.
 
-The arithmetic lives in ``oracle/mx_oracle.c`` (plain scalar C, double
-precision); this module only marshals numpy arrays into it.  The sources it
-follows are named in the header of that file: the MXFP8 RL paper "End-to-End
-MXFP8 Reinforcement Learning on Blackwell" (Figure 1, Table 6, Table 10) for
-what the path computes, and the OCP MX v1.0 shared-scale rule for the bytes.
+The quantization, rearrangement, GEMM, per-expert column-wise and SwiGLU
+arithmetic lives in ``oracle/mx_oracle.c`` (plain scalar C, double
+precision); for those this module only marshals numpy arrays into it.  Two
+definitions are written here in plain numpy instead, because they are index
+work and one weighted sum rather than number formats: ``moe_dispatch`` (the
+stable sort of routed assignments by expert) and ``moe_combine`` (the
+weighted sum of each token's expert outputs, in double precision), plus the
+grouped padding offsets and capacity (integer arithmetic).  The sources
+followed are named in the header of the C file and beside each function: the
+MXFP8 RL paper "End-to-End MXFP8 Reinforcement Learning on Blackwell"
+(Figure 1, Table 2, Table 6, Table 10) for what the path computes, and the
+OCP MX v1.0 shared-scale rule for the bytes.  ``mx_oracle_ref.py`` is a
+second, independent implementation of the quantization, rearrangement and
+GEMM (numpy, different rounding route) that tests/test_oracle_agreement.py
+checks against this one.
 """
 import ctypes
 import os
