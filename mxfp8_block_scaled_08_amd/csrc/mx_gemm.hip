@@ -44,6 +44,7 @@
 // read from LDS while the matrix cores run the current one.
 #include "mx_device.h"
 #include "mx_launch.h"
+#include "mx_plan.h"
 
 #include <algorithm>
 #include <cmath>
@@ -990,36 +991,8 @@ static int cu_count()
     return cache[dev];
 }
 
-// Split-tail plan of a dense product.  With T tiles on P compute units the
-// last R = T mod P tiles form a partial round that leaves most units idle.
-// Each of them is cut into S K ranges (at most P / R, at most one per 256-K
-// group), one workgroup per range: the round then costs about 1/S of a
-// tile, plus writing and summing R * S partial tiles of 256 KiB.  A tile
-// costs ~1.7 us per 128-K stage and summing one partial ~0.065 us, so
-// S ~ sqrt(26 * stages / R) balances the two.  Only BF16 C stored by
-// whole-line stores (every tile full width) is split.  S depends on the
-// shape and the device's compute-unit count only, so the summation order
-// (and the bytes of C) is fixed per shape and device.
-struct SplitPlan {
-    int64_t rem = 0, S = 0;
-    int64_t bytes() const { return S >= 2 ? rem * S * (int64_t)(BM * BN * sizeof(float)) : 0; }
-};
-
-static SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int c_dtype, bool vec16, int64_t cus)
-{
-    SplitPlan sp;
-    if (M <= 0 || N <= 0 || K <= 0)
-        return sp;
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    const int64_t groups = (K / BK + 1) / 2;
-    const int64_t rem = tiles % cus;
-    if (rem > 0 && groups >= 2 && c_dtype == 0 && vec16 && N % BN == 0) {
-        const int64_t balance = std::max<int64_t>(2, (int64_t)std::sqrt(26.0 * 2 * groups / (double)rem));
-        sp.S = std::min<int64_t>(std::min<int64_t>(cus / rem, groups), balance);
-        sp.rem = rem;
-    }
-    return sp;
-}
+// the split-tail plan (mx_plan.h) takes the kernel's tile and stage sizes
+static_assert(PLAN_BM == BM && PLAN_BN == BN && PLAN_BK == BK, "plan and kernel tiles agree");
 
 int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int c_dtype, bool vec16)
 {
