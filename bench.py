@@ -352,50 +352,189 @@ def graph_replay(torch, mx, I, o, noop, steps):
 
 
 def cpu_baseline(torch, mxsynth, row_el, col_el, flops):
-    """The CPU oracle (single-threaded C, as it stands) on a bounded sample of
-    the same workload, extrapolated to the step's work in the metric's unit."""
+    """The CPU oracle (plain C, as it stands) on a bounded sample of the same
+    workload, extrapolated to the step's work in the metric's unit: on all the
+    host's usable cores (the sample split by rows over threads; the C calls
+    release the GIL), and on one thread beside it."""
+    import concurrent.futures as cf
+
     import numpy as np
     import oracle
 
+    threads = min(len(os.sched_getaffinity(0)), 16)
     t0 = time.perf_counter()
     w = mxsynth.normal_bf16((1024, 4096), 0.02, 2004, 0.001, 20.0)
     wb = mxsynth.bits(w)
-    t = time.perf_counter()
-    n_q = 0
-    while time.perf_counter() - t < 4.0:
-        oracle.quantize_rowwise(wb)
-        oracle.quantize_colwise(wb)
-        n_q += 1
-    q_time = time.perf_counter() - t
-    q_rate = n_q * wb.size / q_time * 2          # element-orientations per second
     xh = mxsynth.channel_outliers_bf16(64, 4096, 1.0, 3000, 0.005, 50.0)
     qa, sa = oracle.quantize_rowwise(mxsynth.bits(xh))
     qb, sb = oracle.quantize_rowwise(mxsynth.bits(
         mxsynth.normal_bf16((512, 4096), 0.02, 2000, 0.001, 20.0)))
-    t = time.perf_counter()
-    n_g = 0
     rows = np.repeat(np.arange(64), 512)
     cols = np.tile(np.arange(512), 64)
-    while time.perf_counter() - t < 8.0:
-        oracle.gemm_sampled(rows, cols, qa, sa, qb, sb)
-        n_g += 1
-    g_time = time.perf_counter() - t
-    g_rate = n_g * 2 * 64 * 512 * 4096 / g_time  # FLOP/s
-    step_s = (row_el + col_el) / q_rate + flops / g_rate
-    return {
-        "value": flops / step_s / 1e12,
-        "unit": "TFLOP/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": (f"row+column quantize of a 1024x4096 weight ({n_q} passes, {q_time:.1f} s: "
-                   f"{q_rate / 1e6:.1f} M element-orientations/s) and FP64 GEMM of a 64x512x4096 "
-                   f"slice of the forward qkv product ({n_g} passes, {g_time:.1f} s: "
-                   f"{g_rate / 1e9:.3f} GFLOP/s); step time extrapolated to the full step "
-                   f"({step_s:.0f} s), single thread"),
-        "wall_s": round(time.perf_counter() - t0, 1),
-        "host_cpu": platform.processor() or platform.machine(),
-        "host_nproc": os.cpu_count(),
-    }
+
+    def rates(n_threads, q_secs, g_secs):
+        q_parts = np.array_split(np.arange(wb.shape[0]), n_threads)
+
+        def quant(idx):
+            part = np.ascontiguousarray(wb[idx[0]:idx[-1] + 1])
+            oracle.quantize_rowwise(part)
+            oracle.quantize_colwise(part)
+
+        g_parts = np.array_split(np.arange(rows.size), n_threads)
+
+        def gemm(idx):
+            oracle.gemm_sampled(rows[idx], cols[idx], qa, sa, qb, sb)
+
+        with cf.ThreadPoolExecutor(max_workers=n_threads) as ex:
+            t, n_q = time.perf_counter(), 0
+            while time.perf_counter() - t < q_secs:
+                list(ex.map(quant, q_parts))
+                n_q += 1
+            q_time = time.perf_counter() - t
+            t, n_g = time.perf_counter(), 0
+            while time.perf_counter() - t < g_secs:
+                list(ex.map(gemm, g_parts))
+                n_g += 1
+            g_time = time.perf_counter() - t
+        q_rate = n_q * wb.size / q_time * 2          # element-orientations per second
+        g_rate = n_g * 2 * rows.size * 4096 / g_time  # FLOP/s
+        step_s = (row_el + col_el) / q_rate + flops / g_rate
+        return q_rate, g_rate, step_s, n_q, n_g, q_time, g_time
+
+    def record(n_threads, q_secs, g_secs):
+        q_rate, g_rate, step_s, n_q, n_g, q_time, g_time = rates(n_threads, q_secs, g_secs)
+        return {
+            "value": flops / step_s / 1e12,
+            "unit": "TFLOP/s",
+            "cores": n_threads,
+            "kind": "oracle",
+            "sample": (f"row+column quantize of a 1024x4096 weight ({n_q} passes, {q_time:.1f} s: "
+                       f"{q_rate / 1e6:.1f} M element-orientations/s) and FP64 GEMM of a 64x512x4096 "
+                       f"slice of the forward qkv product ({n_g} passes, {g_time:.1f} s: "
+                       f"{g_rate / 1e9:.3f} GFLOP/s), {n_threads} thread(s); step time extrapolated to "
+                       f"the full step ({step_s:.0f} s)"),
+        }
+
+    result = record(threads, 3.0, 5.0)
+    result["single_thread"] = record(1, 3.0, 5.0)
+    result["wall_s"] = round(time.perf_counter() - t0, 1)
+    result["host_cpu"] = platform.processor() or platform.machine()
+    result["host_nproc"] = os.cpu_count()
+    result["host_usable_cores"] = len(os.sched_getaffinity(0))
+    return result
+
+
+def _ulp_bf16(y):
+    import numpy as np
+    a = np.abs(y)
+    e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), -126)
+    return np.where(a > 0, np.ldexp(1.0, (e - 7).astype(int)), 2.0 ** -133)
+
+
+def oracle_parity(torch, mx, mxsynth, I, o):
+    """GEMM outputs of the timed step against the CPU oracle on bounded
+    samples (256 entries per product, every product of the step), and the
+    Tiny workload (128x256x256) in full: how many meet the stated bar
+    |C - C_ref| <= 1e-5 (|A||B|)_ij + 1 BF16 ulp, and the largest error beyond
+    the ulp allowance relative to (|A||B|)_ij.  The oracle sees the GPU's
+    quantized operands (their bytes are checked against the oracle by the
+    test suite)."""
+    import numpy as np
+    import oracle
+
+    rng = np.random.default_rng(77)
+
+    def host(t):
+        return t.cpu().numpy()
+
+    def unswz(buf, rows, kb):
+        return oracle.scale_unswizzle(host(buf), rows, kb)
+
+    def stats(got, ref, bnd):
+        err = np.abs(got - ref)
+        net = np.maximum(err - _ulp_bf16(ref), 0.0) / np.where(bnd > 0, bnd, np.inf)
+        return {"n": int(got.size), "within_stated": int((err <= 1e-5 * bnd + _ulp_bf16(ref)).sum()),
+                "max_err_over_bnd": float(net.max())}
+
+    def pairs(C, r, c, qa_rows, sa_rows, qb_rows, sb_rows):
+        n = len(r)
+        ref, bnd = oracle.gemm_sampled(np.arange(n), np.arange(n), qa_rows, sa_rows, qb_rows, sb_rows)
+        got = C[torch.from_numpy(np.asarray(r)).cuda(), torch.from_numpy(np.asarray(c)).cuda()]
+        return stats(got.float().cpu().numpy().astype(np.float64), ref, bnd)
+
+    out = {}
+    # Tiny: A[128x256] row-wise, B[256x256] column-wise, BF16 out, every output
+    A, B = mxsynth.tiny()
+    qa, sa = mx.mx_quantize_rowwise(A.cuda())
+    qbt, sbt = mx.mx_quantize_colwise(B.cuda())
+    C = mx.mx_gemm(qa, mx.mx_scale_swizzle(sa), qbt, mx.mx_scale_swizzle(sbt))
+    ref, bnd = oracle.gemm(host(qa), host(sa), host(qbt), host(sbt))
+    out["tiny"] = stats(C.float().cpu().numpy().astype(np.float64), ref, bnd)
+    # dense products of the step
+    dense = {"qkv": ("xh", "qkv", "C_qkv"), "o": ("xh", "o", "C_o"), "gate_up": ("xh", "gu", "C_gu"),
+             "down": ("xi", "dn", "C_dn"), "dgrad": ("dy", "guT", "C_dgrad"), "wgrad": ("dyT", "xT", "C_wgrad")}
+    for name, (an, bn, cn) in dense.items():
+        a_q, b_q, C = o[an + "_q"], o[bn + "_q"], o[cn]
+        M, K = a_q.shape
+        N = b_q.shape[0]
+        r, c = rng.integers(0, M, 256), rng.integers(0, N, 256)
+        sa_, sb_ = unswz(o[an + "_swz"], M, K // 32), unswz(o[bn + "_swz"], N, K // 32)
+        out[name] = pairs(C, r, c, host(a_q[torch.from_numpy(r).cuda()]), sa_[r],
+                          host(b_q[torch.from_numpy(c).cuda()]), sb_[c])
+    # row-grouped MoE products: forward gate_up / down, data gradients
+    G = I["w_gu"].shape[0]
+    grouped = {"moe_gate_up": ("moff", "xq", "xswz", "mgu_wq", "mgu_wswz", "C_mgu"),
+               "moe_down": ("moff", "hq", "hswz", "mdn_wq", "mdn_wswz", "C_mdn"),
+               "moe_dgrad_gate_up": (None, "mgu_dyq", "mgu_dyswz", "mgu_wqt", "mgu_wstswz", "dX_mgu"),
+               "moe_dgrad_down": (None, "mdn_dyq", "mdn_dyswz", "mdn_wqt", "mdn_wstswz", "dX_mdn")}
+    for name, (offn, an, asn, bn, bsn, cn) in grouped.items():
+        off = host(o[offn]) if offn else host(I["off"])
+        a_q, C = o[an], o[cn]
+        K = a_q.shape[1]
+        Gb, N, Kb = o[bn].shape
+        assert Gb == G and Kb == K
+        r = rng.integers(0, int(off[-1]), 256)
+        c = rng.integers(0, N, 256)
+        g = np.searchsorted(off, r, side="right") - 1
+        sa_ = unswz(o[asn], a_q.shape[0], K // 32)
+        per = mx.mx_scale_swizzled_bytes(N, K // 32)
+        bsw = host(o[bsn]).reshape(G, per)
+        sb_ = np.stack([oracle.scale_unswizzle(bsw[gi], N, K // 32)[ci] for gi, ci in zip(g, c)])
+        qb_rows = host(o[bn][torch.from_numpy(g).cuda(), torch.from_numpy(c).cuda()])
+        out[name] = pairs(C, r, c, host(a_q[torch.from_numpy(r).cuda()]), sa_[r], qb_rows, sb_)
+    # K-grouped MoE weight gradients: C_g over expert g's column range
+    for name, (an, bn, cn) in {"moe_wgrad_gate_up": ("mgu_dyT", "mgu_xT", "dW_mgu"),
+                               "moe_wgrad_down": ("mdn_dyT", "mdn_xT", "dW_mdn")}.items():
+        pad = host(o[an.split("_")[0] + "_pad"])
+        a_q, b_q, C = o[an], o[bn], o[cn]
+        Mw, kc = a_q.shape
+        Nw = b_q.shape[0]
+        g = rng.integers(0, G, 256)
+        i, j = rng.integers(0, Mw, 256), rng.integers(0, Nw, 256)
+        sa_, sb_ = unswz(o[an + "swz"], Mw, kc // 32), unswz(o[bn + "swz"], Nw, kc // 32)
+        qa_h, qb_h = host(a_q[torch.from_numpy(i).cuda()]), host(b_q[torch.from_numpy(j).cuda()])
+        refs, bnds = [], []
+        for e in range(256):
+            lo, hi = int(pad[g[e]]), int(pad[g[e] + 1])
+            rf, bd = oracle.gemm_sampled(np.zeros(1, np.int64), np.zeros(1, np.int64),
+                                         np.ascontiguousarray(qa_h[e:e + 1, lo:hi]),
+                                         np.ascontiguousarray(sa_[i[e]:i[e] + 1, lo // 32:hi // 32]),
+                                         np.ascontiguousarray(qb_h[e:e + 1, lo:hi]),
+                                         np.ascontiguousarray(sb_[j[e]:j[e] + 1, lo // 32:hi // 32]))
+            refs.append(rf[0])
+            bnds.append(bd[0])
+        got = C[torch.from_numpy(g).cuda(), torch.from_numpy(i).cuda(), torch.from_numpy(j).cuda()]
+        out[name] = stats(got.float().cpu().numpy().astype(np.float64), np.array(refs), np.array(bnds))
+    groups = {"tiny": ["tiny"], "dense_fwd_m4608": ["qkv", "o", "gate_up", "down"],
+              "dense_bwd_gate_up": ["dgrad", "wgrad"],
+              "moe_qwen3_30b_a3b": [k for k in out if k.startswith("moe_")]}
+    per_config = {}
+    for cfg, keys in groups.items():
+        per_config[cfg] = {"n": sum(out[k]["n"] for k in keys),
+                           "within_stated": sum(out[k]["within_stated"] for k in keys),
+                           "max_err_over_bnd": max(out[k]["max_err_over_bnd"] for k in keys)}
+    return {"bar": "|C - C_ref| <= 1e-5 (|A||B|)_ij + 1 BF16 ulp of C_ref (BF16 out)",
+            "per_config": per_config, "per_product": out}
 
 
 def main():
@@ -557,8 +696,11 @@ def main():
     if graph is not None:
         result["graph"] = graph
     if not args.no_cpu_baseline:
+        # the CPU-oracle leg: the oracle's speed on the host, and the step's
+        # GEMM outputs against it
         result["cpu_baseline"] = cpu_baseline(torch, mxsynth, row_el + dualg_el, col_el + colg_el + dualg_el,
                                               flops)
+        result["parity_vs_oracle"] = oracle_parity(torch, mx, mxsynth, I, o)
     print(json.dumps(result))
 
 
