@@ -26,29 +26,34 @@
 //
 // Tiling: a 256-thread workgroup (4 waves, 2x2) owns a 256x256 tile of C;
 // each wave owns 128x128 = 4x4 matrix-core tiles (256 FP32 accumulators per
-// lane, held in AGPRs).  K advances 128 per stage through two LDS buffers
-// (A and B: 256 rows x 128 bytes each, 64 KiB per stage) filled by direct
-// global->LDS loads (global_load_lds_dwordx4): no VGPR staging.  A stage is
-// two 64-K matrix-core steps; the loads of stage k+2 are issued in the middle
-// of stage k, as soon as every wave has read stage k's buffer, so a load has
-// about one stage of matrix-core time to land.
-// Each load instruction writes 1 KiB of LDS linearly by lane, so the lane's
-// global address picks which 16-byte chunk lands where: eight lanes fetch one
-// full 128-byte row (one cache line), and the eight chunks of a row are
-// XOR-permuted by (row >> 1) & 7.  A 16-byte LDS read is serviced 16 lanes at
-// a time, in the lane groups {0-3, 12-15, 20-27} and {4-11, 16-19, 28-31} of
-// each half-wave (measured with in-bounds probes and the LDS bank-conflict
-// counter), each cycle covering 64 banks = 256 bytes = two rows.  The eight
-// rows of each parity in a group differ in (row >> 1) & 7, so every lane of a
-// group gets its own 16-byte bank slot.  The fragments of the next step are
-// read from LDS while the matrix cores run the current one.
+// lane, held in AGPRs).  K advances 64 per stage (one matrix-core step)
+// through a ring of four LDS stages (A and B: 256 rows x 64 bytes each, 32
+// KiB per stage; 128 KiB in all), one barrier per stage.  Operands travel
+// in pairs of stages: the 128 bytes of a row that two stages need are one
+// cache line, loaded by one 16-byte-per-lane load instruction per 8 rows
+// into registers, and written to the ring two stages later, when both of
+// their ring stages are free.  Whole-line requests keep the load path's
+// request count at one per line (loading each 64-byte half on its own
+// doubled it and saturated the texture address unit), and staging through
+// registers lets a pair's loads go out while the ring is still full, spread
+// over the stage, with two stages of time to land.
+// In LDS the four 16-byte chunks of a 64-byte row are XOR-permuted by
+// (row >> 2) & 3.  A 16-byte LDS read is serviced 16 lanes at a time, in the
+// lane groups {0-3, 12-15, 20-27} and {4-11, 16-19, 28-31} of each half-wave
+// (measured with in-bounds probes and the LDS bank-conflict counter), each
+// cycle covering 64 banks = 256 bytes = four rows; the four rows of each
+// residue mod 4 in a group differ in (row >> 2) & 3, so every lane of a
+// group gets its own 16-byte bank slot.  The A fragments of the next stage
+// are read while the matrix cores run the current one; the B fragments one
+// sub-tile ahead.
 #include "mx_device.h"
 #include "mx_launch.h"
 #include "mx_plan.h"
 
 #include <algorithm>
-#include <cmath>
 #include <climits>
+#include <cmath>
+#include <type_traits>
 
 namespace mx {
 
@@ -56,12 +61,13 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int GM_THREADS = 256;
-constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int TM = 4, TN = 4;      // 32x32 sub-tiles per wave along M and N
+constexpr int BM = 256, BN = 256;
+constexpr int BK = 64;             // K bytes per stage: one matrix-core step
+constexpr int NBUF = 4;            // stages in the LDS ring (one 256-K group)
+constexpr int GM_THREADS = 256;    // 4 waves, one per SIMD, 2x2 over the tile
+constexpr int TM = 4, TN = 4;      // 32x32 sub-tiles per wave along M and N (128x128)
 constexpr int GROUP_M = 4;         // tile-rows walked together for L2 reuse
-constexpr int STAGE_BYTES = BM * BK;  // one operand, one stage (32 KiB)
-constexpr int DMA_PER_WAVE = STAGE_BYTES / 1024 / 4;  // 1 KiB per instruction, 4 waves
+constexpr int STAGE_BYTES = BM * BK;  // one operand, one stage (16 KiB)
 
 struct GemmParams {
     int64_t M, N, K;
@@ -93,7 +99,8 @@ struct GemmParams {
     int *counter;
 };
 
-__device__ __forceinline__ int chunk_perm(int row) { return (row >> 1) & 7; }
+// The 16-byte slot of a 64-byte LDS row that holds chunk c is c ^ chunk_perm(row).
+__device__ __forceinline__ int chunk_perm(int row) { return (row >> 2) & 3; }
 
 // Two FP32 -> packed BF16 (low half first), round to nearest even: one
 // v_cvt_pk_bf16_f32 on this target (NaN stays NaN).
@@ -103,8 +110,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t{lo, hi}), bf16x2_t));
 }
 
-typedef const void __attribute__((address_space(1))) *gptr_t;
-typedef void __attribute__((address_space(3))) *lptr_t;
 
 // Values every lane holds alike, moved to scalar registers.
 __device__ __forceinline__ int64_t uniform(int64_t x)
@@ -118,35 +123,53 @@ template <typename T> __device__ __forceinline__ const T *uniform(const T *x)
     return reinterpret_cast<const T *>(uniform((int64_t)(uintptr_t)x));
 }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
-#define MX_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+// A wave-uniform value the compiler must take as unknown at this point, so
+// that what it derives from it (a divisor's reciprocal) is formed where it is
+// used and not kept in vector registers across the main loop.
+__device__ __forceinline__ int64_t opaque(int64_t x)
+{
+    asm volatile("" : "+s"(x));
+    return x;
+}
 
-// The same wait with its bound picked by a wave-uniform value: at most
-// RELAXED operations outstanding when sel is zero, else at most STRICT
-// (RELAXED >= STRICT; the zero path jumps over the strict wait).
-#define MX_WAIT_VMCNT_SEL(sel, RELAXED, STRICT)                                                   \
-    asm volatile("s_cmp_eq_u32 %0, 0\n\t"                                                       \
-                 "s_cbranch_scc1 .Lmx_vm_relaxed%=\n\t"                                         \
-                 "s_waitcnt vmcnt(%2)\n"                                                         \
-                 ".Lmx_vm_relaxed%=:\n\t"                                                       \
-                 "s_waitcnt vmcnt(%1)" ::"s"(sel), "n"(RELAXED), "n"(STRICT) : "memory", "scc")
+// Tile t of a GROUP_M-row band walk over tiles_m x tiles_n tiles -> (m, n):
+// the bands of GROUP_M tile-rows are taken in turn, and within a band the
+// tiles column by column.  t < GROUP_M * tiles_n * ceil(tiles_m / GROUP_M)
+// and tiles_n < 2^21, so the in-band index fits 32 bits; the band height
+// (GROUP_M, less for the last band) is 1 to 4, divided by shifts or by the
+// exact multiply-high for 3.
+__device__ __forceinline__ void band_walk(int64_t t, int64_t tiles_m, int64_t tiles_n, int64_t &m,
+                                          int64_t &n)
+{
+    static_assert(GROUP_M == 4, "the band division below assumes bands of at most 4 tile-rows");
+    const int64_t per_band = opaque(GROUP_M * tiles_n);
+    const int64_t band = t / per_band;
+    const int64_t first_m = band * GROUP_M;
+    const uint32_t gm = (uint32_t)min(tiles_m - first_m, (int64_t)GROUP_M);
+    const uint32_t in = (uint32_t)(t - band * per_band);
+    const uint32_t q = gm == 4   ? in >> 2
+                       : gm == 2 ? in >> 1
+                       : gm == 1 ? in
+                                 : (uint32_t)(((uint64_t)in * 0xAAAAAAABull) >> 33);
+    m = first_m + (int64_t)(in - q * gm);
+    n = (int64_t)q;
+}
 
 // Workgroup barrier for the LDS ring.  __syncthreads() would also wait for
-// every outstanding vector-memory load (its release fence must cover the LDS
-// writes of the direct-to-LDS loads), draining the whole pipeline each step.
-// Here each wave waits only for its own LDS reads (so a buffer can be
-// refilled) and the loads of the stage about to be read were already waited
-// for with MX_WAIT_VMCNT; the "memory" clobber keeps the compiler from moving
-// LDS accesses across the barrier.
+// every outstanding vector-memory load (its release fence is conservative),
+// draining the register prefetch each stage.  The ring is only written and
+// read with LDS instructions, so each wave waits for its own LDS writes and
+// reads and then meets the others; the "memory" clobber keeps the compiler
+// from moving LDS accesses across the barrier.
 __device__ __forceinline__ void lds_ring_barrier()
 {
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
 }
 
-// Coordinates of one 256x256 output tile, and the stages of it a unit of
-// work covers: ns stages from stage kb (both even: whole 256-K groups).
+// Coordinates of one 256x256 output tile, and the 64-K stages of it a unit
+// of work covers: ns stages from stage kb (both multiples of 4: whole 256-K
+// groups).
 struct Tile {
     int64_t m0, n0, m_end;
     int64_t c_row;  // K-grouped: the row of C holding the tile's first row (g * M + m0)
@@ -168,19 +191,17 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
 {
     constexpr bool GROUPED = MODE == 1;
     constexpr bool KGROUPED = MODE == 2;
-    __shared__ __attribute__((aligned(1024))) uint8_t sA[2][STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t sB[2][STAGE_BYTES];
-    // per wave: the 32-row scale tiles of one 256-K group that hold its A rows
-    // (up to five: 2 KiB) and B rows (four: 1 KiB)
-    __shared__ __attribute__((aligned(1024))) uint8_t sS[4][3072];
+    constexpr int NW = 4, WN = 128;  // waves; columns of C per wave
+    __shared__ __attribute__((aligned(1024))) uint8_t sA[NBUF][STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sB[NBUF][STAGE_BYTES];
     // grouped: per expert g, its first m-tile number and its clamped row range
     // K-grouped: per expert g its stage range [s_lo[g], s_hi[g]), and s_pref[r]
     // the expert of rank r by decreasing stage count
     constexpr bool TABLE = GROUPED || KGROUPED;
     __shared__ int s_pref[TABLE ? GROUP_TABLE + 1 : 1];
     __shared__ int s_lo[TABLE ? GROUP_TABLE : 1], s_hi[TABLE ? GROUP_TABLE : 1];
-    __shared__ int s_wsum[4];
-    __shared__ int64_t s_next[KGROUPED ? 2 : 1];  // K-grouped: tiles taken ahead
+    __shared__ int s_wsum[NW];
+    __shared__ int64_t s_next[2];  // K-grouped: tiles taken ahead
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -191,7 +212,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     const int64_t N = p.N;
     const int64_t KT256 = (p.K + 255) / 256;  // scale words per 32-row tile
     const int KIT = (int)(p.K / BK);
-    const int KITP = (KIT + 1) & ~1;  // stages per tile, padded to whole 256-K groups
+    const int KITP = (KIT + 3) & ~3;  // stages per tile, padded to whole 256-K groups
 
     // ---- tile enumeration
     const bool table = !GROUPED || (p.G <= GROUP_TABLE && p.M < ((int64_t)1 << 31));
@@ -209,8 +230,8 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             const int64_t hi = min(max(p.offsets[g + 1], lo), p.K);
             const int glo = min((int)(lo / 256), KG - 1);
             const int ghi = min(max((int)((hi + 255) / 256), glo + 1), KG);
-            s_lo[g] = 2 * glo;
-            s_hi[g] = 2 * ghi;
+            s_lo[g] = 4 * glo;
+            s_hi[g] = 4 * ghi;
         }
         __syncthreads();
         // rank by decreasing stage count (ties by expert number): tiles are
@@ -259,8 +280,12 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             s_pref[g] = run;
             run += (s_hi[g] - s_lo[g] + BM - 1) / BM;
         }
-        if (tid == GM_THREADS - 1)
-            s_pref[G] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+        if (tid == GM_THREADS - 1) {
+            int tot = 0;
+            for (int w = 0; w < NW; w++)
+                tot += s_wsum[w];
+            s_pref[G] = tot;
+        }
         __syncthreads();
         ntiles = (int64_t)s_pref[G] * p.tiles_n;
     } else {
@@ -342,17 +367,13 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     auto coords = [&](int64_t pid) -> Tile {
         Tile c;
         if (KGROUPED) {
-            const int64_t per_expert = p.tiles_m * p.tiles_n;
+            const int64_t per_expert = opaque(p.tiles_m * p.tiles_n);
             const int64_t r = pid / per_expert;
             const int g = __builtin_amdgcn_readfirstlane(s_pref[r]);
-            const int64_t t = pid - r * per_expert;
-            const int64_t per_group = GROUP_M * p.tiles_n;
-            const int64_t grp = t / per_group;
-            const int64_t first_m = grp * GROUP_M;
-            const int64_t gm = min(p.tiles_m - first_m, (int64_t)GROUP_M);
-            const int64_t in = t - grp * per_group;
-            c.m0 = (first_m + in % gm) * BM;
-            c.n0 = (in / gm) * BN;
+            int64_t mt, nt;
+            band_walk(pid - r * per_expert, p.tiles_m, p.tiles_n, mt, nt);
+            c.m0 = mt * BM;
+            c.n0 = nt * BN;
             c.m_end = p.M;
             c.c_row = (int64_t)g * p.M + c.m0;
             c.b = p.b;
@@ -362,20 +383,18 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             return c;
         }
         if (!GROUPED) {
-            const int64_t per_group = GROUP_M * p.tiles_n;
-            const int64_t grp = pid / per_group;
-            const int64_t first_m = grp * GROUP_M;
-            const int64_t gm = min(p.tiles_m - first_m, (int64_t)GROUP_M);
-            const int64_t in = pid - grp * per_group;
-            c.m0 = (first_m + in % gm) * BM;
-            c.n0 = (in / gm) * BN;
+            int64_t mt, nt;
+            band_walk(pid, p.tiles_m, p.tiles_n, mt, nt);
+            c.m0 = mt * BM;
+            c.n0 = nt * BN;
             c.m_end = p.M;
             c.b = p.b;
             c.bs = p.bs;
             return c;
         }
-        const int64_t mt = pid / p.tiles_n;
-        c.n0 = (pid - mt * p.tiles_n) * BN;
+        const int64_t tn = opaque(p.tiles_n);
+        const int64_t mt = pid / tn;
+        c.n0 = (pid - mt * tn) * BN;
         int64_t g;
         if (table) {
             // first expert whose tiles end beyond mt, searching forward from
@@ -437,11 +456,11 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
         if (SPLIT && has_split && k == 0) {
             const int r = split_u / p.split_s, sidx = split_u - r * p.split_s;
             Tile c = coords(p.dp_tiles + r);
-            const int KG = KITP / 2;  // 256-K groups
+            const int KG = KITP / 4;  // 256-K groups
             const int g0 = (int)((int64_t)sidx * KG / p.split_s);
             const int g1 = (int)((int64_t)(sidx + 1) * KG / p.split_s);
-            c.kb = 2 * g0;
-            c.ns = 2 * (g1 - g0);
+            c.kb = 4 * g0;
+            c.ns = 4 * (g1 - g0);
             c.sp = split_u;
             return c;
         }
@@ -457,122 +476,107 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
         return c;
     };
 
-    // ---- direct-to-LDS plan.  Instruction i of this wave fills LDS rows
-    // 8*(8*wave + i) .. +8 of a stage; lane -> row + lane/8, slot lane%8,
-    // fetching global chunk slot ^ perm(row) of that row.  Rows past the
-    // operand (or past the expert, which are never stored) need no clamp:
-    // the tile's buffer range ends at the operand's last row and reads
-    // beyond it return zero.
-    uint32_t a_src[DMA_PER_WAVE], b_src[DMA_PER_WAVE];
+    // ---- operand loads.  Two consecutive stages of a tile (128 K: one
+    // 128-byte cache line of each row) of A and of B are loaded together
+    // into registers, 16 bytes per lane and instruction, and written to the
+    // LDS ring two stages later.  Instruction i of this wave covers rows
+    // 8*wave + 32*i .. +8 of an operand: lane -> row + lane/8, chunk lane%8
+    // of the row's 128 bytes, which belongs to stage chunk/4 of the pair.
+    // In LDS a stage holds 64 bytes of each of the 256 rows, row after row,
+    // chunk c of a row in slot (c & 3) ^ perm(row) (rows 32 apart share the
+    // permutation, so one offset register serves all eight instructions).
+    // Rows past the operand (or past the expert, which are never stored) need
+    // no clamp: the tile's buffer range ends at the operand's last row and
+    // reads beyond it return zero.
+    constexpr int PAIR_LOADS = 2 * (BM / 32);  // per wave: 8 of A, 8 of B
+    const int prow = 8 * wave + (lane >> 3);
+    const int pchunk = lane & 7;
+    const uint32_t a_src = (uint32_t)(prow * p.ld_a + pchunk * 16);
+    const uint32_t b_src = (uint32_t)(prow * p.ld_b + pchunk * 16);
+    const uint32_t a_step = (uint32_t)(32 * p.ld_a), b_step = (uint32_t)(32 * p.ld_b);
+    const uint32_t w_off = (uint32_t)((pchunk >> 2) * STAGE_BYTES + prow * BK +
+                                      (((pchunk & 3) ^ chunk_perm(prow)) * 16));
+    // Loads of stages st, st + 1 (st even) of tile T.  A pair past the end or
+    // of padding (live false) gets an empty range and loads zeros, which keeps
+    // the main loop branch-free.
+    // Loads of stages st, st + 1 (st even) of tile T, load q into R[q] (A
+    // rows for q < 8, then B rows).  A pair past the end or of padding (live
+    // false) gets an empty range and loads zeros, which keeps the main loop
+    // branch-free.  (32-bit sizes: row counts are below 2^29; a 64-bit
+    // compare would need a vector register for a uniform value.)
+    auto pair_load_one = [&](const Tile &T, int st, bool live, v4i *R, int q) {
+        const uint32_t ab = (uint32_t)min((int)(p.M - T.m0), BM) * (uint32_t)p.ld_a;
+        const uint32_t bb = (uint32_t)min((int)(N - T.n0), BN) * (uint32_t)p.ld_b;
+        const uint32_t koff = (uint32_t)(T.kb + st) * BK;
+        if (q < PAIR_LOADS / 2)
+            R[q] = __builtin_amdgcn_raw_buffer_load_b128(byte_range(p.a + T.m0 * p.ld_a, live ? ab : 0u),
+                                                         a_src + (uint32_t)q * a_step, koff, 0);
+        else
+            R[q] = __builtin_amdgcn_raw_buffer_load_b128(byte_range(T.b + T.n0 * p.ld_b, live ? bb : 0u),
+                                                         b_src + (uint32_t)(q - PAIR_LOADS / 2) * b_step, koff, 0);
+    };
+    auto pair_loads = [&](const Tile &T, int st, bool live, v4i *R) {
 #pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; i++) {
-        const int row = 8 * (DMA_PER_WAVE * wave + i) + (lane >> 3);
-        const int chunk = (lane & 7) ^ chunk_perm(row);
-        a_src[i] = (uint32_t)(row * p.ld_a + chunk * 16);
-        b_src[i] = (uint32_t)(row * p.ld_b + chunk * 16);
-    }
-    const uint32_t lds_a0 = (uint32_t)(uintptr_t)&sA[0][0];
-    const uint32_t lds_b0 = (uint32_t)(uintptr_t)&sB[0][0];
-    // Loads of stage st of tile T into buffer buf, in two halves (rows of
-    // instructions 0-3 and 4-7) so they can be issued at two points of a
-    // stage.  A stage past the end or a padding stage (live false) gets an
-    // empty range: its loads move no data and write zeros, which keeps the
-    // main loop branch-free.
-    auto dma_stage = [&](const Tile &T, int st, int buf, bool live, int half) {
-        const uint32_t ab = (uint32_t)(min(p.M - T.m0, (int64_t)BM) * p.ld_a);
-        const uint32_t bb = (uint32_t)(min(N - T.n0, (int64_t)BN) * p.ld_b);
-        const __amdgpu_buffer_rsrc_t ra = byte_range(p.a + T.m0 * p.ld_a, live ? ab : 0u);
-        const __amdgpu_buffer_rsrc_t rb = byte_range(T.b + T.n0 * p.ld_b, live ? bb : 0u);
-        const uint32_t koff = (uint32_t)(T.kb + st) * BK;  // scalar offset, added after the range check
-#pragma unroll
-        for (int i = half * (DMA_PER_WAVE / 2); i < (half + 1) * (DMA_PER_WAVE / 2); i++) {
-            const uint32_t off = (uint32_t)(buf * STAGE_BYTES + 1024 * (DMA_PER_WAVE * wave + i));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lptr_t)(uintptr_t)(lds_a0 + off), 16,
-                                                     a_src[i], koff, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lptr_t)(uintptr_t)(lds_b0 + off), 16,
-                                                     b_src[i], koff, 0, 0);
-        }
+        for (int q = 0; q < PAIR_LOADS; q++)
+            pair_load_one(T, st, live, R, q);
+    };
+    // write R[q] of a pair into ring stages t0, t0 + 1
+    auto pair_write_one = [&](int t0, const v4i *R, int q) {
+        uint8_t *base = q < PAIR_LOADS / 2 ? &sA[0][0] : &sB[0][0];
+        *reinterpret_cast<v4i *>(base + t0 * STAGE_BYTES + w_off + (q % (PAIR_LOADS / 2)) * 32 * BK) = R[q];
     };
 
-    // ---- scale words.  A group's word for a row sits in the row's 32-row
-    // scale tile (256 bytes per tile and group; tiles KT256 * 256 bytes
-    // apart).  The wave's 128 A rows lie in at most five consecutive tiles
-    // (four when the tile's first row is a multiple of 32, always so for B),
-    // so three 16-byte-per-lane direct-to-LDS loads bring a group's words:
-    // lane l fetches 16 bytes of tile l / 16 (the second A load covers tile 4
-    // with lanes 0-15; the other lanes are out of range and write zeros).
-    // The lane then reads its own word of sub-tile i from LDS at a per-tile
-    // base plus i * 256.  Rows past the operand fall outside the resource's
-    // range and read zero.
-    const uint32_t lds_s = (uint32_t)(uintptr_t)&sS[wave][0];
-    const int64_t stile = KT256 * 256;  // bytes per 32-row scale tile
-    const uint32_t s_v4 = (uint32_t)((lane >> 4) * stile + (lane & 15) * 16);
-    const uint32_t s_v1 = lane < 16 ? (uint32_t)(4 * stile + lane * 16) : 0xFFFFFFF0u;
-    // offset of the lane's A word of sub-tile 0 in the wave's region for
-    // tile T (sub-tile i adds i * 256; B words sit at 2048 + i * 256 + lane * 4)
-    auto scale_lanes = [&](const Tile &T) -> uint32_t {
+    // ---- scale words.  Per 256-K group the lane (h, r) supplies, for A
+    // sub-tile i, the word of row m0 + wm*128 + 32i + r: entry 32h + (row &
+    // 31) of the row's 32-row scale tile, whose group g sits at g * 256
+    // within the tile's KT256 * 256 bytes (likewise for B).  Each is one
+    // 4-byte load into a register, a group ahead.  Rows past the operand fall
+    // outside the resource's range and read zero.
+    const uint32_t stile = (uint32_t)(KT256 * 256);  // bytes per 32-row scale tile (below 2^32)
+    struct ScaleLanes {
+        uint32_t a, b;  // the lane's offsets for sub-tile 0 (sub-tile i adds i * stile)
+    };
+    auto scale_lanes = [&](const Tile &T) -> ScaleLanes {
         const int x = (int)(T.m0 & 31) + r32;
-        return (uint32_t)((x >> 5) * 256 + (h * 32 + (x & 31)) * 4);
+        const int ta = (int)(T.m0 >> 5) + wm * 4 + (x >> 5), tb = (int)(T.n0 >> 5) + wn * (WN / 32);
+        return ScaleLanes{(uint32_t)ta * stile + (uint32_t)((h * 32 + (x & 31)) * 4),
+                          (uint32_t)tb * stile + (uint32_t)((h * 32 + r32) * 4)};
     };
-    auto dma_scales = [&](const Tile &T, int group, bool live) {
-        const int64_t a_base = ((T.m0 + wm * 128) >> 5) * stile;
-        const int64_t b_base = ((T.n0 + wn * 128) >> 5) * stile;
-        const uint32_t a_bytes = live && a_base < p.as_bytes ? (uint32_t)(p.as_bytes - a_base) : 0u;
-        const uint32_t b_bytes = live && b_base < p.bs_bytes ? (uint32_t)(p.bs_bytes - b_base) : 0u;
-        const __amdgpu_buffer_rsrc_t rsa = byte_range(p.as + (live ? a_base : 0), a_bytes);
-        const __amdgpu_buffer_rsrc_t rsb = byte_range(T.bs + (live ? b_base : 0), b_bytes);
+    auto load_scales = [&](const Tile &T, const ScaleLanes &S, int group, bool live, uint32_t *xa,
+                           uint32_t *xb) {
+        const __amdgpu_buffer_rsrc_t rsa = byte_range(p.as, live ? p.as_bytes : 0u);
+        const __amdgpu_buffer_rsrc_t rsb = byte_range(T.bs, live ? p.bs_bytes : 0u);
         const uint32_t kw = (uint32_t)group * 256;  // scalar offset, within the row's scale tile
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lptr_t)(uintptr_t)lds_s, 16, s_v4, kw, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lptr_t)(uintptr_t)(lds_s + 1024), 16, s_v1,
-                                                 kw, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lptr_t)(uintptr_t)(lds_s + 2048), 16, s_v4,
-                                                 kw, 0, 0);
-    };
-    constexpr int SCALE_LOADS = 3;
-    constexpr int EPILOGUE_STORES = 2 * TM * TN;  // BF16 C, whole-width tile
-    static_assert(TN % 2 == 0, "BF16 stores pair adjacent sub-tiles");
-    static_assert(DMA_PER_WAVE + SCALE_LOADS + EPILOGUE_STORES <= 63, "vmcnt holds at most 63");
-    auto read_scales = [&](uint32_t a_rd_s, uint32_t *xa, uint32_t *xb) {
 #pragma unroll
         for (int i = 0; i < TM; i++)
-            xa[i] = *reinterpret_cast<const uint32_t *>(&sS[wave][a_rd_s + i * 256]);
+            xa[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsa, S.a + (uint32_t)i * stile, kw, 0);
 #pragma unroll
         for (int i = 0; i < TN; i++)
-            xb[i] = *reinterpret_cast<const uint32_t *>(&sS[wave][2048 + i * 256 + lane * 4]);
+            xb[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsb, S.b + (uint32_t)i * stile, kw, 0);
     };
+    static_assert(TN % 2 == 0, "BF16 stores pair adjacent sub-tiles");
 
-    // ---- per-lane LDS read offsets of the matrix-core fragments.  At step
-    // s (0, 1) of a stage the lane needs chunk 4s + h (bytes 0-15 of the
-    // operand) and chunk 4s + 2 + h (bytes 16-31) of its row.  Rows of the
-    // sub-tiles are 32 apart, which leaves chunk_perm unchanged, and the chunk
-    // bits are disjoint, so the four chunks sit at the step-0 offset XOR
-    // 64s + 32t.  One register per (s, t) and operand; the sub-tile is an
-    // immediate offset of the LDS read.
-    uint32_t a_rd[4], b_rd[4];
-    {
-        const uint32_t la0 = (uint32_t)((wm * 128 + r32) * BK + ((h ^ chunk_perm(r32)) * 16));
-        const uint32_t lb0 = (uint32_t)((wn * 128 + r32) * BK + ((h ^ chunk_perm(r32)) * 16));
-#pragma unroll
-        for (int x = 0; x < 4; x++) {
-            a_rd[x] = la0 ^ (32u * x);
-            b_rd[x] = lb0 ^ (32u * x);
-        }
-    }
-    auto read_frags = [&](int buf, int step, v8i *xa, v8i *xb) {
-        const uint8_t *A_ = &sA[buf][0];
-        const uint8_t *B_ = &sB[buf][0];
-#pragma unroll
-        for (int i = 0; i < TM; i++) {
-            const v4i lo = *reinterpret_cast<const v4i *>(A_ + a_rd[2 * step] + i * 32 * BK);
-            const v4i hi = *reinterpret_cast<const v4i *>(A_ + a_rd[2 * step + 1] + i * 32 * BK);
-            xa[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int i = 0; i < TN; i++) {
-            const v4i lo = *reinterpret_cast<const v4i *>(B_ + b_rd[2 * step] + i * 32 * BK);
-            const v4i hi = *reinterpret_cast<const v4i *>(B_ + b_rd[2 * step + 1] + i * 32 * BK);
-            xb[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
+    // ---- per-lane LDS read offsets of the matrix-core fragments.  The lane
+    // needs chunk h (bytes 0-15 of the operand) and chunk 2 + h (bytes
+    // 16-31) of its row's 64 bytes.  Rows of the sub-tiles are 32 apart,
+    // which leaves chunk_perm unchanged, and chunk 2 + h sits in the slot of
+    // chunk h XOR 2, so the second read is at the first offset XOR 32.  The
+    // sub-tile and the ring buffer are immediate offsets of the LDS read.
+    const uint32_t a_lo = (uint32_t)((wm * 128 + r32) * BK + ((h ^ chunk_perm(r32)) * 16));
+    const uint32_t b_lo = (uint32_t)((wn * WN + r32) * BK + ((h ^ chunk_perm(r32)) * 16));
+    const uint32_t a_hi = a_lo ^ 32u, b_hi = b_lo ^ 32u;
+    // A sub-tile i (rows wm*128 + 32i ..) and B sub-tile i of ring buffer buf
+    auto read_a = [&](int buf, int i) -> v8i {
+        const uint8_t *A_ = &sA[buf][0] + i * 32 * BK;
+        const v4i lo = *reinterpret_cast<const v4i *>(A_ + a_lo);
+        const v4i hi = *reinterpret_cast<const v4i *>(A_ + a_hi);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto read_b = [&](int buf, int i) -> v8i {
+        const uint8_t *B_ = &sB[buf][0] + i * 32 * BK;
+        const v4i lo = *reinterpret_cast<const v4i *>(B_ + b_lo);
+        const v4i hi = *reinterpret_cast<const v4i *>(B_ + b_hi);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
 
     v16f acc[TN][TM];
@@ -584,54 +588,55 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             for (int v = 0; v < 16; v++)
                 acc[i][j][v] = 0.0f;
 
-    // per-lane offsets of C within a tile: row wm*128 + j*32 + r32, columns
-    // from wn*128 + 4h (the sub-tile and register group add immediates)
+    // Per-lane offset of C within a tile for band j = 0: row wm*128 + r32,
+    // columns from wn*WN + 4h.  Band j adds j * c_band, wave-uniform (the
+    // sub-tile and register group add immediates), so one register serves
+    // every band.  The row offsets stay in the vector offset, which the
+    // buffer range check covers (the scalar offset is added after it).
     constexpr int CE = CT == 0 ? 2 : 4;  // bytes per C element
+    const uint32_t c_band = (uint32_t)(32 * p.ld_c * CE);
     // BF16 C is stored after three lane exchanges (see the epilogue): lane l
     // writes 8 columns, chunk k = ((l >> 5) & 1) | (((l >> 4) & 1) << 1) of
     // sub-tile pair half (l >> 3) & 1, of row l & 7 of an 8-row quarter of the
-    // pair's 32-row band; one base for rows 0-7 and one for rows 16-23.
-    uint32_t c_off[TM], c_off_hi[TM];
-#pragma unroll
-    for (int j = 0; j < TM; j++) {
-        if (CT == 0) {
-            const int row = wm * 128 + j * 32 + (lane & 7);
-            const int col = wn * 128 + ((lane >> 3) & 1) * 32 + (((lane >> 5) & 1) | (((lane >> 4) & 1) << 1)) * 8;
-            c_off[j] = (uint32_t)((row * p.ld_c + col) * CE);
-            c_off_hi[j] = (uint32_t)(((row + 16) * p.ld_c + col) * CE);
-        } else {
-            c_off[j] = (uint32_t)(((wm * 128 + j * 32 + r32) * p.ld_c + wn * 128 + 4 * h) * CE);
-            c_off_hi[j] = 0;
-        }
+    // pair's 32-row band (rows 0-7; rows 8-15, 16-23 and 24-31 add scalar
+    // offsets too).
+    uint32_t c_off;
+    if (CT == 0) {
+        const int row = wm * 128 + (lane & 7);
+        const int col = wn * WN + ((lane >> 3) & 1) * 32 + (((lane >> 5) & 1) | (((lane >> 4) & 1) << 1)) * 8;
+        c_off = (uint32_t)((row * p.ld_c + col) * CE);
+    } else {
+        c_off = (uint32_t)(((wm * 128 + r32) * p.ld_c + wn * WN + 4 * h) * CE);
     }
 
     // ---- the workgroup's stages: its units' stages numbered continuously,
-    // so the pipeline runs across units
+    // so the pipeline runs across units.  Every unit has a multiple of 4
+    // stages, so stage u of the sequence uses ring buffer u % 4, which is
+    // also its position t in its 256-K group.
     Tile cur = unit(0);
-    // (K-grouped: unknown in advance and not used)
-    const int64_t total = KGROUPED ? 0 : (my_units - has_split) * KITP + (has_split ? cur.ns : 0);
-    uint32_t cur_srd = scale_lanes(cur);
+    ScaleLanes cur_sl = scale_lanes(cur);
 
-    // prologue: scale words of the first group, stages 0 and 1 in flight
-    dma_scales(cur, cur.kb >> 1, true);
-    dma_stage(cur, 0, 0, cur.kb < KIT, 0);
-    dma_stage(cur, 0, 0, cur.kb < KIT, 1);
-    dma_stage(cur, 1, 1, cur.kb + 1 < KIT, 0);
-    dma_stage(cur, 1, 1, cur.kb + 1 < KIT, 1);
-    MX_WAIT_VMCNT(0);  // stages 0 and 1 (the first stage's wait is the relaxed one)
+    // prologue: stages 0 and 1 into the ring, stages 2 and 3 into registers,
+    // the first group's scale words; then stage 0's fragments
+    v4i R[PAIR_LOADS];
+    pair_loads(cur, 0, cur.kb < KIT, R);
+#pragma unroll
+    for (int q = 0; q < PAIR_LOADS; q++)
+        pair_write_one(0, R, q);
+    pair_loads(cur, 2, cur.kb + 2 < KIT, R);
+    uint32_t wa[TM], wb[TN], na[TM], nb[TN];
+    load_scales(cur, cur_sl, cur.kb >> 2, true, wa, wb);
     lds_ring_barrier();
-    uint32_t wa[TM], wb[TN];
-    read_scales(cur_srd, wa, wb);
-    v8i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
-    read_frags(0, 0, fa0, fb0);
+    // The A fragments of a stage are read during the previous stage (two
+    // register sets, alternating); the B fragments one sub-tile ahead: the
+    // first during the previous stage, sub-tile i + 1 while the instructions
+    // of sub-tile i run.
+    v8i fa0[TM], fa1[TM], fb_first;
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+        fa0[i] = read_a(0, i);
+    fb_first = read_b(0, 0);
 
-#define MX_MFMA_STEP(FA, FB, SHIFT, I0, I1)                                                  \
-    _Pragma("unroll") for (int i = (I0); i < (I1); i++) {                                    \
-        const int sbv = (int)(wb[i] >> (SHIFT));                                             \
-        _Pragma("unroll") for (int j = 0; j < TM; j++)                                       \
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                     \
-                FB[i], FA[j], acc[i][j], 0, 0, 0, sbv, 0, (int)(wa[j] >> (SHIFT)));          \
-    }
 
     // BF16 stores of one 32-row band j of the wave's C, sub-tile i in x[i].
     // Register group q of lane (h, r) holds columns 8q + 4h .. +3 of
@@ -650,7 +655,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     // with the default policy each round of tiles' output fills the
     // L2 and evicts the operand panels that the next round reuses;
     // streaming whole lines keeps them resident.
-    auto store_band = [&](const __amdgpu_buffer_rsrc_t &rc, int j, const v16f *x) {
+    auto store_band = [&](const __amdgpu_buffer_rsrc_t &rc, uint32_t cb, int j, const v16f *x) {
         const uint32_t row8 = (uint32_t)(8 * p.ld_c * CE);
         {
             uint32_t s1[TN][4], s2[TN][4];
@@ -698,55 +703,39 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                 }
                 const uint32_t col = (uint32_t)(i * 32 * CE);
                 constexpr int NT = 2;  // cache policy: non-temporal
+                const uint32_t o = cb + (uint32_t)j * c_band + col;
                 __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]},
-                                                       rc, c_off[j] + col, 0, NT);
+                                                       rc, o, 0, NT);
                 __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)y1[0], (int)y1[1], (int)y1[2], (int)y1[3]},
-                                                       rc, c_off[j] + row8 + col, 0, NT);
+                                                       rc, o + row8, 0, NT);
                 __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)x2[0], (int)x2[1], (int)x2[2], (int)x2[3]},
-                                                       rc, c_off_hi[j] + col, 0, NT);
+                                                       rc, o + 2 * row8, 0, NT);
                 __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)y2[0], (int)y2[1], (int)y2[2], (int)y2[3]},
-                                                       rc, c_off_hi[j] + row8 + col, 0, NT);
+                                                       rc, o + 3 * row8, 0, NT);
             }
         }
     };
 
-    // Stage gs uses buffer gs & 1 and scale bytes 2*(gs & 1) and 2*(gs & 1)+1
-    // of the current 256-K words (a tile has an even number of stages, so
-    // parity within the tile and overall agree).  On entry the step-0
-    // fragments are in fa0/fb0 and the loads of stage gs+1 are in flight.
-    //   1. Step 0 runs while step 1's fragments are read (one LDS read
-    //      between consecutive matrix-core instructions) and the scale words
-    //      of stage gs+2's group are requested.
-    //   2. Barrier: every wave is done with buffer gs & 1.  Half of step 1
-    //      runs while the first half of stage gs+2's loads goes into that
-    //      buffer.
-    //   3. Wait until this wave's loads of stage gs+1 have landed (all but
-    //      the 11 issued since its last one: vector-memory operations retire
-    //      in issue order) and barrier, so every wave's have.  The other half
-    //      of step 1 runs while the second half of stage gs+2's loads is
-    //      issued and stage gs+1's step-0 fragments and the scale words of
-    //      the next group are read.  Those words are kept on a group's last
-    //      stage (odd gs), when they belong to the group of stage gs+1; on an
-    //      even stage they are being rewritten and are discarded.  An odd
-    //      stage reloads the words of its own group, which leaves the bytes
-    //      unchanged.
-    // Spreading the loads over the stage keeps fewer of them waiting on the
-    // L1's outstanding-miss capacity at once: a load that cannot be accepted
-    // stalls the wave, and with it the matrix-core instructions behind it.
-    // Past the end the loads are empty and the fragment reads unused, so the
-    // body has no branches.  After a tile's last stage its accumulators are
-    // stored and cleared.
-    int64_t gs = 0;  // stages run so far (all tiles)
-    // The first stage of a tile waits for loads issued before the previous
-    // tile's stores.  Vector-memory operations retire in issue order, so its
-    // wait allows EPILOGUE_STORES more outstanding operations: the stores
-    // drain while that stage's matrix-core work runs, and only the second
-    // stage's wait (for loads issued after them) includes them.  That bound
-    // is exact after the BF16 whole-width stores and conservative after the
-    // FP32 ones (more stores); the other epilogue, and the prologue before
-    // the first tile, wait for all of the wave's operations instead.
+    // Stage u of the sequence (64 K) uses ring buffer u % 4 = t, its
+    // position in its 256-K group, and byte t of the group's scale words.
+    // On entry its fragments are in registers (set t & 1) and stage u+1 is
+    // in the ring for every wave.  While the stage's 16 matrix-core
+    // instructions run, the wave
+    //   - at even t, writes the pair of stages u+2, u+3 that it loaded at
+    //     stage u-2 into ring buffers (t+2) % 4 and (t+3) % 4 (their
+    //     fragments were read at stages u-3 and u-2, before the last
+    //     barrier), and loads the pair u+4, u+5 into the same registers, one
+    //     128-byte line of each row: the load path sees a steady stream of
+    //     whole-line requests, each with two stages' time to land;
+    //   - at t = 1, loads the next group's scale words;
+    //   - reads stage u+1's fragments into the other register set.
+    // A barrier then makes this wave's LDS writes and reads complete for
+    // every wave.  The compiler places the waits for the loads, which only
+    // feed registers.  Past the end the loads are empty (their range is) and
+    // the fragment reads unused, so the body has no branches.  After a
+    // unit's last stage its accumulators are stored and cleared.
     for (int64_t k = 0; k < my_units; k++) {
-        // the unit after this one (loaded during this unit's last two stages)
+        // the unit after this one (loaded during this unit's last group)
         bool nxt_ok;
         Tile nxt;
         if (KGROUPED) {
@@ -756,68 +745,83 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             nxt_ok = k + 1 < my_units;
             nxt = nxt_ok ? unit(k + 1) : cur;
         }
-        const uint32_t nxt_srd = scale_lanes(nxt);
-        for (int st = 0; st < cur.ns; st++, gs++) {
-            const int buf = (int)(gs & 1);
-            const int shift = 16 * buf;
-            // stage gs + 2: stage st + 2 of this unit, or the next unit's first two
-            const bool same = st + 2 < cur.ns;
-            const int st2 = same ? st + 2 : st + 2 - cur.ns;
-            const Tile ld = same ? cur : nxt;
-            const bool live = KGROUPED ? (same || nxt_ok) : gs + 2 < total;
-            // the group's first stage (K-grouped: units are whole 256-K groups)
-            const bool live_group = KGROUPED ? live : ((gs + 2) & ~(int64_t)1) < total;
-            // 1.
-            read_frags(buf, 1, fa1, fb1);
-            dma_scales(ld, (ld.kb + st2) >> 1, live_group);
-            MX_MFMA_STEP(fa0, fb0, shift, 0, TN)
+        const ScaleLanes nxt_sl = scale_lanes(nxt);
+        const int ng = cur.ns >> 2;  // 256-K groups of this unit
+        for (int gi = 0; gi < ng; gi++) {
+            // the next group: of this unit, or the next unit's first (every
+            // unit has at least one); it exists when it is in this unit or a
+            // next unit exists
+            const bool same = gi + 1 < ng;
+            const Tile &ld = same ? cur : nxt;
+            const ScaleLanes &ld_sl = same ? cur_sl : nxt_sl;
+            const int st4 = same ? 4 * (gi + 1) : 0;  // its first stage within ld
+            const bool live = same || nxt_ok;
+            auto stage = [&](auto T_) {
+                constexpr int t = decltype(T_)::value;
+                v8i *FA = (t & 1) ? fa1 : fa0, *NA = (t & 1) ? fa0 : fa1;
+                constexpr int nbuf = (t + 1) & 3;  // the next stage's buffer
+                const bool pl = live && ld.kb + st4 + t < KIT;
+                if (t == 1)
+                    load_scales(ld, ld_sl, (ld.kb + st4) >> 2, live, na, nb);
+                // Per B sub-tile i: read B sub-tile i + 1 (or the next
+                // stage's first) and the next stage's A sub-tile i, then at
+                // even t a quarter of the pair writes and loads, while the
+                // four matrix-core instructions of row i run.  LDS writes and
+                // reads stay in program order (the compiler cannot tell the
+                // ring buffers apart), so reads come first in each row.
+                v8i xb = fb_first;
 #pragma unroll
-            for (int q = 0; q < 3; q++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // matrix core
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // scale load
-            }
+                for (int i = 0; i < TN; i++) {
+                    const v8i xn = i + 1 < TN ? read_b(t, i + 1) : read_b(nbuf, 0);
+                    NA[i] = read_a(nbuf, i);
+                    if (t == 0 || t == 2) {
 #pragma unroll
-            for (int q = 0; q < TM * TN - 3; q++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            lds_ring_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-            // 2.
-            dma_stage(ld, st2, buf, live && ld.kb + st2 < KIT, 0);
-            MX_MFMA_STEP(fa1, fb1, shift + 8, 0, TN / 2)
+                        for (int q = 4 * i; q < 4 * i + 4; q++) {
+                            pair_write_one((t + 2) & 3, R, q);
+                            pair_load_one(ld, st4 + t, pl, R, q);
+                        }
+                    }
+                    const int sbv = (int)(wb[i] >> (8 * t));
 #pragma unroll
-            for (int q = 0; q < 8; q++) {  // 8 matrix-core, 8 loads
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-                __builtin_amdgcn_sched_group_barrier(0x010, 1, 1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // 3.
-            MX_WAIT_VMCNT_SEL(st, DMA_PER_WAVE + SCALE_LOADS + EPILOGUE_STORES, DMA_PER_WAVE + SCALE_LOADS);
-            asm volatile("s_barrier" ::: "memory");
-            __builtin_amdgcn_sched_barrier(0);
-            uint32_t na[TM], nb[TN];
-            read_scales(st + 1 < cur.ns ? cur_srd : nxt_srd, na, nb);
-            dma_stage(ld, st2, buf, live && ld.kb + st2 < KIT, 1);
-            read_frags(buf ^ 1, 0, fa0, fb0);
-            MX_MFMA_STEP(fa1, fb1, shift + 8, TN / 2, TN)
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);  // scale words
+                    for (int j = 0; j < TM; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            xb, FA[j], acc[i][j], 0, 0, 0, sbv, 0, (int)(wa[j] >> (8 * t)));
+                    xb = xn;
+                }
+                fb_first = xb;
 #pragma unroll
-            for (int q = 0; q < 8; q++) {  // 8 matrix-core, 8 loads, 16 LDS reads
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-                __builtin_amdgcn_sched_group_barrier(0x010, 1, 2);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
-            }
-            __builtin_amdgcn_sched_barrier(0);  // the selects wait for the words: keep them last
+                for (int i = 0; i < TN; i++) {  // per row: 4 matrix-core, 4 LDS reads (+ 4 writes, 4 loads)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    if (t == 1)
+                        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // scale words
 #pragma unroll
-            for (int i = 0; i < TM; i++)
-                wa[i] = buf ? na[i] : wa[i];
+                    for (int q = 0; q < 4; q++) {
+                        if (q > 0)
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        if (t == 0 || t == 2) {
+                            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                        }
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (t == 3) {
 #pragma unroll
-            for (int i = 0; i < TN; i++)
-                wb[i] = buf ? nb[i] : wb[i];
-            __builtin_amdgcn_sched_barrier(0);
+                    for (int i = 0; i < TM; i++)
+                        wa[i] = na[i];
+#pragma unroll
+                    for (int i = 0; i < TN; i++)
+                        wb[i] = nb[i];
+                }
+                lds_ring_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            stage(std::integral_constant<int, 0>{});
+            stage(std::integral_constant<int, 1>{});
+            stage(std::integral_constant<int, 2>{});
+            stage(std::integral_constant<int, 3>{});
         }
 
         // K-grouped: take the tile of unit k + 3 (its slot was last read at the
@@ -833,7 +837,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
         if (split_unit) {
             const __amdgpu_buffer_rsrc_t rw = byte_range(p.ws, (uint32_t)(p.split_tiles * p.split_s) *
                                                                    (uint32_t)(BM * BN * 4));
-            const uint32_t base = (uint32_t)cur.sp * (BM * BN * 4) + (uint32_t)(wave * (BM * BN / 4) + lane * 4) * 4;
+            const uint32_t base = (uint32_t)cur.sp * (BM * BN * 4) + (uint32_t)(wave * (BM * BN / NW) + lane * 4) * 4;
 #pragma unroll
             for (int i = 0; i < TN; i++)
 #pragma unroll
@@ -859,6 +863,10 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             const __amdgpu_buffer_rsrc_t rc =
                 byte_range((const uint8_t *)p.c + (c_row * p.ld_c + cur.n0) * CE,
                            rows_valid * (uint32_t)(p.ld_c * CE));
+            // the band offsets are formed here, per tile, not kept in
+            // registers across the main loop
+            uint32_t cb = c_off;
+            asm volatile("" : "+v"(cb));
             if (CT == 0) {
 #pragma unroll
                 for (int j = 0; j < TM; j++) {
@@ -866,7 +874,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
 #pragma unroll
                     for (int i = 0; i < TN; i++)
                         x[i] = acc[i][j];
-                    store_band(rc, j, x);
+                    store_band(rc, cb, j, x);
 #pragma unroll
                     for (int i = 0; i < TN; i++)
 #pragma unroll
@@ -884,8 +892,8 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                             const f4_t v{acc[i][j][4 * q + 0], acc[i][j][4 * q + 1],
                                          acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
                             __builtin_amdgcn_raw_buffer_store_b128(
-                                __builtin_bit_cast(v4i, v), rc, c_off[j] + (uint32_t)((i * 32 + 8 * q) * CE),
-                                0, 0);
+                                __builtin_bit_cast(v4i, v), rc,
+                                cb + (uint32_t)j * c_band + (uint32_t)((i * 32 + 8 * q) * CE), 0, 0);
                         }
 #pragma unroll
                         for (int v = 0; v < 16; v++)
@@ -903,7 +911,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                     if (m < cur.m_end) {
 #pragma unroll
                         for (int q = 0; q < 4; q++) {
-                            const int64_t n = cur.n0 + wn * 128 + i * 32 + 8 * q + 4 * h;
+                            const int64_t n = cur.n0 + wn * WN + i * 32 + 8 * q + 4 * h;
                             const float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
                             const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
                             if (CT == 0) {
@@ -935,23 +943,18 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                         acc[i][j][v] = 0.0f;
                 }
             }
-            MX_WAIT_VMCNT(0);  // a varying number of stores: the next wait cannot count them
         }
         // (a split-tail unit issues 64 stores, more than the next unit's
-        // relaxed first wait allows, so that wait still covers its loads)
+        // relaxed waits allow, so those waits still cover their loads)
         if (KGROUPED) {
             if (!nxt_ok)
                 break;
             t_nxt = uniform(s_next[k & 1]);  // the tile of unit k + 2
         }
         cur = nxt;
-        cur_srd = nxt_srd;
-        // re-read the next stage's step-0 fragments, so that the copy read in
-        // the last stage need not stay live across the stores
-        read_frags((int)(gs & 1), 0, fa0, fb0);
+        cur_sl = nxt_sl;
     }
-#undef MX_MFMA_STEP
-    MX_WAIT_VMCNT(0);  // no load may still write LDS when the workgroup ends
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // the prefetch past the end: let it land
 }
 
 static int vec_ok(const void *c, int64_t ld_c, int c_dtype)
@@ -992,7 +995,7 @@ static int cu_count()
 }
 
 // the split-tail plan (mx_plan.h) takes the kernel's tile and stage sizes
-static_assert(PLAN_BM == BM && PLAN_BN == BN && PLAN_BK == BK, "plan and kernel tiles agree");
+static_assert(PLAN_BM == BM && PLAN_BN == BN && PLAN_BK == 2 * BK, "plan and kernel tiles agree");
 
 int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int c_dtype, bool vec16)
 {
@@ -1006,15 +1009,18 @@ int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int c_dtype, bool 
 // wn*128 + 32i + 8q + 4(lane >> 5) .. +3.
 __global__ __launch_bounds__(256) void split_reduce_kernel(GemmParams p)
 {
+    constexpr int NW = 4;
+    constexpr int PER_WAVE = BM * BN / 4 / NW;  // float4 per wave region
     const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int r = (int)(gt >> 14);
     const int t = (int)(gt & 16383);
     if (r >= p.split_tiles)
         return;
-    const int wave = t >> 12, idx = (t >> 6) & 63, lane = t & 63;
+    const int wave = t / PER_WAVE, idx = (t % PER_WAVE) >> 6, lane = t & 63;
     const int q = idx & 3, j = (idx >> 2) & 3, i = idx >> 4;
+    static_assert(PER_WAVE / 64 == TN * TM * 4, "one float4 per lane per (sub-tile, group)");
     const int row = (wave & 1) * 128 + j * 32 + (lane & 31);
-    const int col = (wave >> 1) * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
+    const int col = (wave >> 1) * (32 * TN) + i * 32 + 8 * q + 4 * (lane >> 5);
     // tile dp_tiles + r: the kernel's tile order (GROUP_M tile-rows at a time)
     const int64_t pid = p.dp_tiles + r;
     const int64_t per_group = GROUP_M * p.tiles_n;

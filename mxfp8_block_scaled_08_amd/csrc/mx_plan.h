@@ -8,7 +8,7 @@
 
 namespace mx {
 
-constexpr int64_t PLAN_BM = 256, PLAN_BN = 256, PLAN_BK = 128;  // output tile, K stage
+constexpr int64_t PLAN_BM = 256, PLAN_BN = 256, PLAN_BK = 128;  // output tile; K per cost unit
 
 // With T tiles on P compute units the last R = T mod P tiles form a partial
 // round that leaves most units idle.  Each of them is cut into S K ranges (at
