@@ -480,25 +480,25 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     // 128-byte cache line of each row) of A and of B are loaded together
     // into registers, 16 bytes per lane and instruction, and written to the
     // LDS ring two stages later.  Instruction i of this wave covers rows
-    // 8*wave + 32*i .. +8 of an operand: lane -> row + lane/8, chunk lane%8
-    // of the row's 128 bytes, which belongs to stage chunk/4 of the pair.
-    // In LDS a stage holds 64 bytes of each of the 256 rows, row after row,
-    // chunk c of a row in slot (c & 3) ^ perm(row) (rows 32 apart share the
-    // permutation, so one offset register serves all eight instructions).
-    // Rows past the operand (or past the expert, which are never stored) need
-    // no clamp: the tile's buffer range ends at the operand's last row and
-    // reads beyond it return zero.
+    // 8*wave + 32*i .. +8 of an operand: lane l takes row (l & 31) / 4 of
+    // them and chunk (l & 3) + 4 * (l / 32) of the row's 128 bytes, so each
+    // half-wave holds one stage of the pair (one 64-byte half of every row)
+    // and writes it to its ring stage as 8 consecutive 64-byte LDS rows.  In
+    // LDS chunk c of a row sits in slot c ^ perm(row) (rows 32 apart share
+    // the permutation, so one offset register serves all eight
+    // instructions); a half-wave's 32 lanes then cover 8 rows x 4 slots,
+    // every 16-lane service group distinct 16-byte bank slots.  Rows past
+    // the operand (or past the expert, which are never stored) need no clamp:
+    // the tile's buffer range ends at the operand's last row and reads beyond
+    // it return zero.
     constexpr int PAIR_LOADS = 2 * (BM / 32);  // per wave: 8 of A, 8 of B
-    const int prow = 8 * wave + (lane >> 3);
-    const int pchunk = lane & 7;
+    const int prow = 8 * wave + ((lane & 31) >> 2);
+    const int pchunk = (lane & 3) + 4 * (lane >> 5);
     const uint32_t a_src = (uint32_t)(prow * p.ld_a + pchunk * 16);
     const uint32_t b_src = (uint32_t)(prow * p.ld_b + pchunk * 16);
     const uint32_t a_step = (uint32_t)(32 * p.ld_a), b_step = (uint32_t)(32 * p.ld_b);
-    const uint32_t w_off = (uint32_t)((pchunk >> 2) * STAGE_BYTES + prow * BK +
-                                      (((pchunk & 3) ^ chunk_perm(prow)) * 16));
-    // Loads of stages st, st + 1 (st even) of tile T.  A pair past the end or
-    // of padding (live false) gets an empty range and loads zeros, which keeps
-    // the main loop branch-free.
+    const uint32_t w_off = (uint32_t)((lane >> 5) * STAGE_BYTES + prow * BK +
+                                      (((lane & 3) ^ chunk_perm(prow)) * 16));
     // Loads of stages st, st + 1 (st even) of tile T, load q into R[q] (A
     // rows for q < 8, then B rows).  A pair past the end or of padding (live
     // false) gets an empty range and loads zeros, which keeps the main loop
