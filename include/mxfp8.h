@@ -452,7 +452,9 @@ mx_status mx_gemm(int64_t M, int64_t N, int64_t K, const void *a_q, int64_t ld_a
  *   b_s_swz  num_groups rearranged [N][K/32] scale buffers back to back,
  *            expert g at g * mx_scale_swizzled_bytes(N, K/32)
  *   c        [M_total][ld_c] of c_dtype
- * Same requirements as mx_gemm, plus num_groups >= 1.  The offsets live on
+ * Same requirements as mx_gemm, plus num_groups in 1..1024 (else
+ * MX_ERR_INVALID_ARG / MX_ERR_UNSUPPORTED: the kernel keeps a per-expert tile
+ * table in LDS).  The offsets live on
  * the device and are not read by the host; offsets that break the stated
  * properties give unspecified (but in-bounds) results.
  */

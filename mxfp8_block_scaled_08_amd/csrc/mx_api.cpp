@@ -786,9 +786,9 @@ mx_status mx_grouped_gemm(int64_t num_groups, int64_t M_total, int64_t N, int64_
     const char *fn = "mx_grouped_gemm";
     if (num_groups < 1)
         return fail(MX_ERR_INVALID_ARG, "%s: num_groups=%lld < 1", fn, (long long)num_groups);
-    if (num_groups > (1 << 20))
-        return fail(MX_ERR_UNSUPPORTED, "%s: num_groups=%lld too large", fn,
-                    (long long)num_groups);
+    if (num_groups > mx::MOE_MAX_EXPERTS)
+        return fail(MX_ERR_UNSUPPORTED, "%s: num_groups=%lld > %d", fn, (long long)num_groups,
+                    mx::MOE_MAX_EXPERTS);
     mx_status st = check_gemm_common(fn, M_total, N, K, a_q, ld_a, a_s_swz, b_q, K, b_s_swz, c,
                                      ld_c, c_dtype);
     if (st != MX_OK)

@@ -215,7 +215,6 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     const int KITP = (KIT + 3) & ~3;  // stages per tile, padded to whole 256-K groups
 
     // ---- tile enumeration
-    const bool table = !GROUPED || (p.G <= GROUP_TABLE && p.M < ((int64_t)1 << 31));
     int64_t ntiles;
     if (KGROUPED) {
         // Stage ranges, clamped so that every expert has at least one 256-K
@@ -249,7 +248,8 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
         ntiles = p.G * p.tiles_m * p.tiles_n;
     } else if (!GROUPED) {
         ntiles = p.tiles_m * p.tiles_n;
-    } else if (table) {
+    } else {
+        // (p.G <= GROUP_TABLE: the library takes at most that many experts)
         // each thread takes a contiguous run of experts; block-wide exclusive
         // scan of their m-tile counts (ceil(rows / BM))
         const int G = (int)p.G;
@@ -288,26 +288,6 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
         }
         __syncthreads();
         ntiles = (int64_t)s_pref[G] * p.tiles_n;
-    } else {
-        // too many experts for the table: count with a wave-wide scan over
-        // global memory (every wave computes the same total)
-        int64_t run = 0;
-        for (int64_t gb = 0; gb < p.G; gb += 64) {
-            const int64_t g = gb + lane;
-            int64_t cnt = 0;
-            if (g < p.G) {
-                const int64_t lo = min(max(p.offsets[g], (int64_t)0), p.M);
-                const int64_t hi = min(max(p.offsets[g + 1], lo), p.M);
-                cnt = (hi - lo + BM - 1) / BM;
-            }
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int64_t o = __shfl_xor(cnt, d, 64);
-                cnt += o;
-            }
-            run += cnt;
-        }
-        ntiles = run * p.tiles_n;
     }
     // Workgroups are dealt to the 8 XCDs in turn (workgroup b runs on XCD
     // b % 8), and each XCD has its own L2: give XCD x a contiguous eighth of
@@ -393,57 +373,26 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             return c;
         }
         const int64_t tn = opaque(p.tiles_n);
-        const int64_t mt = pid / tn;
-        c.n0 = (pid - mt * tn) * BN;
-        int64_t g;
-        if (table) {
-            // first expert whose tiles end beyond mt, searching forward from
-            // the last one found (a workgroup's tiles come in increasing
-            // order); pid < ntiles guarantees a hit, and the loop is bounded
-            // either way
-            const int G = (int)p.G;
-            if ((int64_t)s_pref[g_cur] > mt)
-                g_cur = 0;
-            int found = -1;
-            for (int gb = g_cur; gb < G && found < 0; gb += 64) {
-                const int gg = gb + lane;
-                const uint64_t m = __ballot(gg < G && (int64_t)s_pref[gg + 1] > mt);
-                if (m)
-                    found = gb + __builtin_ctzll(m);
-            }
-            g_cur = found < 0 ? G - 1 : found;
-            g = g_cur;
-            c.m0 = s_lo[g] + (mt - s_pref[g]) * BM;
-            c.m_end = s_hi[g];
-        } else {
-            int64_t run = 0;
-            g = -1;
-            for (int64_t gb = 0; gb < p.G && g < 0; gb += 64) {
-                const int64_t gg = gb + lane;
-                int64_t lo = 0, hi = 0;
-                if (gg < p.G) {
-                    lo = min(max(p.offsets[gg], (int64_t)0), p.M);
-                    hi = min(max(p.offsets[gg + 1], lo), p.M);
-                }
-                const int64_t cnt = (hi - lo + BM - 1) / BM;
-                int64_t incl = cnt;
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const int64_t o = __shfl_up(incl, d, 64);
-                    if (lane >= d)
-                        incl += o;
-                }
-                const int64_t excl = run + incl - cnt;
-                const uint64_t m = __ballot(cnt > 0 && mt >= excl && mt < excl + cnt);
-                if (m) {
-                    const int src = __builtin_ctzll(m);
-                    g = gb + src;
-                    c.m0 = __shfl(lo + (mt - excl) * BM, src, 64);
-                    c.m_end = __shfl(hi, src, 64);
-                }
-                run += __shfl(incl, 63, 64);
-            }
+        const int64_t mt64 = pid / tn;
+        c.n0 = (pid - mt64 * tn) * BN;
+        const int mt = (int)mt64;  // below 2^31 (so are the tile counts)
+        // first expert whose tiles end beyond mt, searching forward from the
+        // last one found (a workgroup's tiles come in increasing order); pid <
+        // ntiles guarantees a hit, and the loop is bounded either way
+        const int G = (int)p.G;
+        if (s_pref[g_cur] > mt)
+            g_cur = 0;
+        int found = -1;
+        for (int gb = g_cur; gb < G && found < 0; gb += 64) {
+            const int gg = gb + lane;
+            const uint64_t m = __ballot(gg < G && s_pref[gg + 1] > mt);
+            if (m)
+                found = gb + __builtin_ctzll(m);
         }
+        g_cur = found < 0 ? G - 1 : found;
+        int64_t g = g_cur;
+        c.m0 = s_lo[g] + (int64_t)(mt - s_pref[g]) * BM;
+        c.m_end = s_hi[g];
         c.m0 = uniform(c.m0);
         c.m_end = uniform(c.m_end);
         g = uniform(g);
@@ -727,7 +676,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     //     barrier), and loads the pair u+4, u+5 into the same registers, one
     //     128-byte line of each row: the load path sees a steady stream of
     //     whole-line requests, each with two stages' time to land;
-    //   - at t = 1, loads the next group's scale words;
+    //   - at t = 3, loads the next group's scale words (consumed at the next stage);
     //   - reads stage u+1's fragments into the other register set.
     // A barrier then makes this wave's LDS writes and reads complete for
     // every wave.  The compiler places the waits for the loads, which only
@@ -761,7 +710,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                 v8i *FA = (t & 1) ? fa1 : fa0, *NA = (t & 1) ? fa0 : fa1;
                 constexpr int nbuf = (t + 1) & 3;  // the next stage's buffer
                 const bool pl = live && ld.kb + st4 + t < KIT;
-                if (t == 1)
+                if (t == 3)
                     load_scales(ld, ld_sl, (ld.kb + st4) >> 2, live, na, nb);
                 // Per B sub-tile i: read B sub-tile i + 1 (or the next
                 // stage's first) and the next stage's A sub-tile i, then at
@@ -794,7 +743,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                    if (t == 1)
+                    if (t == 3)
                         __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // scale words
 #pragma unroll
                     for (int q = 0; q < 4; q++) {

@@ -236,6 +236,9 @@ def test_grouped_gemm_validation():
     assert f(*base[:4], 0, *base[5:]) == mx.MX_ERR_INVALID_ARG  # null offsets
     assert f(*base[:4], FAKE4 + (1 << 22) + 4, *base[5:]) == mx.MX_ERR_ALIGN
     assert f(*base[:3], 96, *base[4:]) == mx.MX_ERR_UNSUPPORTED
+    # the per-expert tile table holds 1024 experts
+    assert f(1025, *base[1:]) == mx.MX_ERR_UNSUPPORTED
+    assert "1025 > 1024" in _err(L)
     # C on top of the offsets array
     assert f(*base[:10], FAKE4 + (1 << 22) - 64, *base[11:]) == mx.MX_ERR_OVERLAP
     assert f(*base[:1], 0, *base[2:]) == mx.MX_OK
