@@ -170,10 +170,11 @@ __device__ __forceinline__ void lds_ring_barrier()
 // Coordinates of one 256x256 output tile, and the 64-K stages of it a unit
 // of work covers: ns stages from stage kb (both multiples of 4: whole 256-K
 // groups).
+// (32-bit fields: row and column counts are below 2^29, experts at most
+// 1024; a workgroup holds three tiles at a time in scalar registers.)
 struct Tile {
-    int64_t m0, n0, m_end;
-    int64_t c_row;  // K-grouped: the row of C holding the tile's first row (g * M + m0)
-    const uint8_t *b, *bs;  // B operand and its rearranged scales (per expert when grouped)
+    int m0, n0, m_end;
+    int g;  // expert (grouped modes), else 0
     int kb, ns;
     int sp;  // split-tail slot (tile * split_s + range), or -1 for a whole tile
 };
@@ -352,12 +353,10 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             const int g = __builtin_amdgcn_readfirstlane(s_pref[r]);
             int64_t mt, nt;
             band_walk(pid - r * per_expert, p.tiles_m, p.tiles_n, mt, nt);
-            c.m0 = mt * BM;
-            c.n0 = nt * BN;
-            c.m_end = p.M;
-            c.c_row = (int64_t)g * p.M + c.m0;
-            c.b = p.b;
-            c.bs = p.bs;
+            c.m0 = (int)(mt * BM);
+            c.n0 = (int)(nt * BN);
+            c.m_end = (int)p.M;
+            c.g = g;
             c.kb = __builtin_amdgcn_readfirstlane(s_lo[g]);
             c.ns = __builtin_amdgcn_readfirstlane(s_hi[g]) - c.kb;
             return c;
@@ -365,16 +364,15 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
         if (!GROUPED) {
             int64_t mt, nt;
             band_walk(pid, p.tiles_m, p.tiles_n, mt, nt);
-            c.m0 = mt * BM;
-            c.n0 = nt * BN;
-            c.m_end = p.M;
-            c.b = p.b;
-            c.bs = p.bs;
+            c.m0 = (int)(mt * BM);
+            c.n0 = (int)(nt * BN);
+            c.m_end = (int)p.M;
+            c.g = 0;
             return c;
         }
         const int64_t tn = opaque(p.tiles_n);
         const int64_t mt64 = pid / tn;
-        c.n0 = (pid - mt64 * tn) * BN;
+        c.n0 = (int)((pid - mt64 * tn) * BN);
         const int mt = (int)mt64;  // below 2^31 (so are the tile counts)
         // first expert whose tiles end beyond mt, searching forward from the
         // last one found (a workgroup's tiles come in increasing order); pid <
@@ -390,15 +388,19 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                 found = gb + __builtin_ctzll(m);
         }
         g_cur = found < 0 ? G - 1 : found;
-        int64_t g = g_cur;
-        c.m0 = s_lo[g] + (int64_t)(mt - s_pref[g]) * BM;
-        c.m_end = s_hi[g];
-        c.m0 = uniform(c.m0);
-        c.m_end = uniform(c.m_end);
-        g = uniform(g);
-        c.b = p.b + g * p.b_group_stride;
-        c.bs = p.bs + g * p.bs_group_stride;
+        const int g = g_cur;
+        c.m0 = __builtin_amdgcn_readfirstlane(s_lo[g] + (mt - s_pref[g]) * BM);
+        c.m_end = __builtin_amdgcn_readfirstlane(s_hi[g]);
+        c.g = __builtin_amdgcn_readfirstlane(g);
         return c;
+    };
+    // a tile's B operand and its rearranged scales (per expert when grouped
+    // by rows)
+    auto b_of = [&](const Tile &T) -> const uint8_t * {
+        return GROUPED ? p.b + (int64_t)T.g * p.b_group_stride : p.b;
+    };
+    auto bs_of = [&](const Tile &T) -> const uint8_t * {
+        return GROUPED ? p.bs + (int64_t)T.g * p.bs_group_stride : p.bs;
     };
     // unit k of this workgroup: its split-tail unit first, then whole tiles
     auto unit = [&](int64_t k) -> Tile {
@@ -458,10 +460,10 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
         const uint32_t bb = (uint32_t)min((int)(N - T.n0), BN) * (uint32_t)p.ld_b;
         const uint32_t koff = (uint32_t)(T.kb + st) * BK;
         if (q < PAIR_LOADS / 2)
-            R[q] = __builtin_amdgcn_raw_buffer_load_b128(byte_range(p.a + T.m0 * p.ld_a, live ? ab : 0u),
+            R[q] = __builtin_amdgcn_raw_buffer_load_b128(byte_range(p.a + (int64_t)T.m0 * p.ld_a, live ? ab : 0u),
                                                          a_src + (uint32_t)q * a_step, koff, 0);
         else
-            R[q] = __builtin_amdgcn_raw_buffer_load_b128(byte_range(T.b + T.n0 * p.ld_b, live ? bb : 0u),
+            R[q] = __builtin_amdgcn_raw_buffer_load_b128(byte_range(b_of(T) + (int64_t)T.n0 * p.ld_b, live ? bb : 0u),
                                                          b_src + (uint32_t)(q - PAIR_LOADS / 2) * b_step, koff, 0);
     };
     auto pair_loads = [&](const Tile &T, int st, bool live, v4i *R) {
@@ -494,8 +496,11 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     auto load_scales = [&](const Tile &T, const ScaleLanes &S, int group, bool live, uint32_t *xa,
                            uint32_t *xb) {
         const __amdgpu_buffer_rsrc_t rsa = byte_range(p.as, live ? p.as_bytes : 0u);
-        const __amdgpu_buffer_rsrc_t rsb = byte_range(T.bs, live ? p.bs_bytes : 0u);
-        const uint32_t kw = (uint32_t)group * 256;  // scalar offset, within the row's scale tile
+        const __amdgpu_buffer_rsrc_t rsb = byte_range(bs_of(T), live ? p.bs_bytes : 0u);
+        // scalar offset, within the row's scale tile (readfirstlane: the
+        // compiler may select the tile's fields in vector registers, and a
+        // vector soffset would become a loop over distinct values)
+        const uint32_t kw = __builtin_amdgcn_readfirstlane((uint32_t)group * 256);
 #pragma unroll
         for (int i = 0; i < TM; i++)
             xa[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsa, S.a + (uint32_t)i * stile, kw, 0);
@@ -573,6 +578,16 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     for (int q = 0; q < PAIR_LOADS; q++)
         pair_write_one(0, R, q);
     pair_loads(cur, 2, cur.kb + 2 < KIT, R);
+    // the unit after the current one (K-grouped: taken from the counter)
+    bool nxt_ok;
+    Tile nxt;
+    if (KGROUPED) {
+        nxt_ok = t_nxt < ntiles;
+        nxt = nxt_ok ? coords(t_nxt) : cur;
+    } else {
+        nxt_ok = 1 < my_units;
+        nxt = nxt_ok ? unit(1) : cur;
+    }
     uint32_t wa[TM], wb[TN], na[TM], nb[TN];
     load_scales(cur, cur_sl, cur.kb >> 2, true, wa, wb);
     lds_ring_barrier();
@@ -684,19 +699,10 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     // the fragment reads unused, so the body has no branches.  After a
     // unit's last stage its accumulators are stored and cleared.
     for (int64_t k = 0; k < my_units; k++) {
-        // the unit after this one (loaded during this unit's last group)
-        bool nxt_ok;
-        Tile nxt;
-        if (KGROUPED) {
-            nxt_ok = t_nxt < ntiles;
-            nxt = nxt_ok ? coords(t_nxt) : cur;
-        } else {
-            nxt_ok = k + 1 < my_units;
-            nxt = nxt_ok ? unit(k + 1) : cur;
-        }
+        // nxt: the unit after this one (loaded during this unit's last group)
         const ScaleLanes nxt_sl = scale_lanes(nxt);
         const int ng = cur.ns >> 2;  // 256-K groups of this unit
-        for (int gi = 0; gi < ng; gi++) {
+        auto group = [&](int gi) {
             // the next group: of this unit, or the next unit's first (every
             // unit has at least one); it exists when it is in this unit or a
             // next unit exists
@@ -710,6 +716,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                 v8i *FA = (t & 1) ? fa1 : fa0, *NA = (t & 1) ? fa0 : fa1;
                 constexpr int nbuf = (t + 1) & 3;  // the next stage's buffer
                 const bool pl = live && ld.kb + st4 + t < KIT;
+                constexpr bool pairs = t == 0 || t == 2;
                 if (t == 3)
                     load_scales(ld, ld_sl, (ld.kb + st4) >> 2, live, na, nb);
                 // Per B sub-tile i: read B sub-tile i + 1 (or the next
@@ -723,7 +730,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                 for (int i = 0; i < TN; i++) {
                     const v8i xn = i + 1 < TN ? read_b(t, i + 1) : read_b(nbuf, 0);
                     NA[i] = read_a(nbuf, i);
-                    if (t == 0 || t == 2) {
+                    if (pairs) {
 #pragma unroll
                         for (int q = 4 * i; q < 4 * i + 4; q++) {
                             pair_write_one((t + 2) & 3, R, q);
@@ -749,7 +756,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                     for (int q = 0; q < 4; q++) {
                         if (q > 0)
                             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        if (t == 0 || t == 2) {
+                        if (pairs) {
                             __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
                             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                         }
@@ -771,13 +778,27 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             stage(std::integral_constant<int, 1>{});
             stage(std::integral_constant<int, 2>{});
             stage(std::integral_constant<int, 3>{});
+        };
+        for (int gi = 0; gi < ng; gi++)
+            group(gi);
+        // the unit after the next one
+        bool nxt2_ok = false;
+        Tile nxt2 = nxt;
+        if (nxt_ok) {
+            if (KGROUPED) {
+                const int64_t t2 = uniform(s_next[k & 1]);  // the tile of unit k + 2
+                nxt2_ok = t2 < ntiles;
+                nxt2 = nxt2_ok ? coords(t2) : nxt;
+            } else {
+                nxt2_ok = k + 2 < my_units;
+                nxt2 = nxt2_ok ? unit(k + 2) : nxt;
+            }
+            // K-grouped: take the tile of unit k + 3 (its slot was last read
+            // at the end of unit k - 1, before this unit's barriers)
+            if (KGROUPED && tid == 0)
+                s_next[(k + 1) & 1] =
+                    P + __hip_atomic_fetch_add(p.counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-
-        // K-grouped: take the tile of unit k + 3 (its slot was last read at the
-        // end of unit k - 1, before this unit's barriers)
-        if (KGROUPED && tid == 0)
-            s_next[(k + 1) & 1] =
-                P + __hip_atomic_fetch_add(p.counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // ---- split-tail unit (BF16 C, whole-width tiles only): its FP32
         // partial tile goes to its workspace slot, lane-major per sub-tile
         // and register group (64 lanes x 16 bytes per store, whole lines,
@@ -807,10 +828,11 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             // whole-width tile: buffer stores relative to the tile's first
             // element; the range ends after the tile's last valid row, so the
             // stores of rows past it (past M, or past the expert) are dropped
-            const uint32_t rows_valid = (uint32_t)min(cur.m_end - cur.m0, (int64_t)BM);
-            const int64_t c_row = KGROUPED ? cur.c_row : cur.m0;
+            const uint32_t rows_valid = (uint32_t)min(cur.m_end - cur.m0, BM);
+            // K-grouped: expert g's C starts at row g * M
+            const int64_t c_row = (KGROUPED ? (int64_t)cur.g * p.M : 0) + cur.m0;
             const __amdgpu_buffer_rsrc_t rc =
-                byte_range((const uint8_t *)p.c + (c_row * p.ld_c + cur.n0) * CE,
+                byte_range((const uint8_t *)p.c + (c_row * p.ld_c + (int64_t)cur.n0) * CE,
                            rows_valid * (uint32_t)(p.ld_c * CE));
             // the band offsets are formed here, per tile, not kept in
             // registers across the main loop
@@ -856,7 +878,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
 #pragma unroll
                 for (int j = 0; j < TM; j++) {
                     const int64_t m = cur.m0 + wm * 128 + j * 32 + r32;
-                    const int64_t mc = m + (KGROUPED ? cur.c_row - cur.m0 : 0);  // row of C
+                    const int64_t mc = m + (KGROUPED ? (int64_t)cur.g * p.M : 0);  // row of C
                     if (m < cur.m_end) {
 #pragma unroll
                         for (int q = 0; q < 4; q++) {
@@ -893,15 +915,12 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                 }
             }
         }
-        // (a split-tail unit issues 64 stores, more than the next unit's
-        // relaxed waits allow, so those waits still cover their loads)
-        if (KGROUPED) {
-            if (!nxt_ok)
-                break;
-            t_nxt = uniform(s_next[k & 1]);  // the tile of unit k + 2
-        }
+        if (!nxt_ok)
+            break;
         cur = nxt;
         cur_sl = nxt_sl;
+        nxt = nxt2;
+        nxt_ok = nxt2_ok;
     }
     __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // the prefetch past the end: let it land
 }
