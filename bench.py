@@ -132,15 +132,11 @@ def build_workload(mx, torch, mxsynth):
     # weight sync outputs: row-wise into the fused forward operands, column-wise
     # into the fused backward operand of gate_up
     o["qkv_q"] = torch.empty(6144, 4096, **u8)
-    o["qkv_s"] = torch.empty(6144, 128, **u8)
-    o["o_q"], o["o_s"] = torch.empty(4096, 4096, **u8), torch.empty(4096, 128, **u8)
+    o["o_q"] = torch.empty(4096, 4096, **u8)
     o["gu_q"] = torch.empty(24576, 4096, **u8)
-    o["gu_s"] = torch.empty(24576, 128, **u8)
-    o["dn_q"], o["dn_s"] = torch.empty(4096, 12288, **u8), torch.empty(4096, 384, **u8)
+    o["dn_q"] = torch.empty(4096, 12288, **u8)
     o["guT_q"] = torch.empty(4096, 24576, **u8)
-    o["guT_s"] = torch.empty(4096, 768, **u8)
-    o["colT"] = {n: (torch.empty(W[n].shape[1], W[n].shape[0], **u8),
-                     torch.empty(W[n].shape[1], W[n].shape[0] // 32, **u8))
+    o["colT"] = {n: torch.empty(W[n].shape[1], W[n].shape[0], **u8)
                  for n in ("q", "k", "v", "o", "down")}
     for name, (r, c) in (("qkv", (6144, 4096)), ("o", (4096, 4096)), ("gu", (24576, 4096)),
                          ("dn", (4096, 12288)), ("guT", (4096, 24576))):
@@ -150,13 +146,12 @@ def build_workload(mx, torch, mxsynth):
     # activations
     for name, x in (("xh", xh), ("xi", xi)):
         o[name + "_q"] = torch.empty(x.shape, **u8)
-        o[name + "_s"] = torch.empty(x.shape[0], x.shape[1] // 32, **u8)
         o[name + "_swz"] = torch.empty(swz(x.shape[0], x.shape[1] // 32), **u8)
-    o["dy_q"], o["dy_s"] = torch.empty(12288, 24576, **u8), torch.empty(12288, 768, **u8)
+    o["dy_q"] = torch.empty(12288, 24576, **u8)
     o["dy_swz"] = torch.empty(swz(12288, 768), **u8)
-    o["dyT_q"], o["dyT_s"] = torch.empty(24576, 12288, **u8), torch.empty(24576, 384, **u8)
+    o["dyT_q"] = torch.empty(24576, 12288, **u8)
     o["dyT_swz"] = torch.empty(swz(24576, 384), **u8)
-    o["xT_q"], o["xT_s"] = torch.empty(4096, 12288, **u8), torch.empty(4096, 384, **u8)
+    o["xT_q"] = torch.empty(4096, 12288, **u8)
     o["xT_swz"] = torch.empty(swz(4096, 384), **u8)
     M = int(off[-1].item())
     G = w_gu.shape[0]
@@ -172,7 +167,6 @@ def build_workload(mx, torch, mxsynth):
         # backward: dY [M][N] row-wise (data gradient), dY and the forward
         # input column-wise per expert (weight gradient)
         o[name + "_dyq"] = torch.empty(M, N, **u8)
-        o[name + "_dys"] = torch.empty(M, N // 32, **u8)
         o[name + "_dyswz"] = torch.empty(swz(M, N // 32), **u8)
         o[name + "_dyT"] = torch.empty(N, k_cap, **u8)
         o[name + "_dyTswz"] = torch.empty(swz(N, k_cap // 32), **u8)
@@ -222,7 +216,6 @@ def build_workload(mx, torch, mxsynth):
 def step(mx, I, o, T):
     """One pass of the hot path; T(category, fn, ...) times each launch."""
     W = I["W"]
-    cq, sw = mx.mx_quantize_colwise, mx.mx_scale_swizzle
     # 1. weight sync: both orientations of every weight in one pass each, the
     #    row-wise codes into the fused forward operands (q, k, v stacked; gate,
     #    up stacked) and the column-wise ones into the backward operands (gate
@@ -232,19 +225,19 @@ def step(mx, I, o, T):
     jobs = []
     for name, r0, r1 in (("q", 0, 4096), ("k", 4096, 5120), ("v", 5120, 6144)):
         jobs.append(dict(x=W[name], q=o["qkv_q"][r0:r1], s_swz=o["qkv_swz"][(r0 // 32) * t16 * 256:],
-                         s_tiles=t16, qt=o["colT"][name][0], st_swz=o["colT_swz"][name]))
-    jobs.append(dict(x=W["o"], q=o["o_q"], s_swz=o["o_swz"], qt=o["colT"]["o"][0],
+                         s_tiles=t16, qt=o["colT"][name], st_swz=o["colT_swz"][name]))
+    jobs.append(dict(x=W["o"], q=o["o_q"], s_swz=o["o_swz"], qt=o["colT"]["o"],
                      st_swz=o["colT_swz"]["o"]))
     for name, r0, r1 in (("gate", 0, 12288), ("up", 12288, 24576)):
         jobs.append(dict(x=W[name], q=o["gu_q"][r0:r1], s_swz=o["gu_swz"][(r0 // 32) * t16 * 256:],
                          s_tiles=t16, qt=o["guT_q"][:, r0:r1],
                          st_swz=o["guT_swz"][(r0 // 256) * 256:], st_tiles=24576 // 256))
-    jobs.append(dict(x=W["down"], q=o["dn_q"], s_swz=o["dn_swz"], qt=o["colT"]["down"][0],
+    jobs.append(dict(x=W["down"], q=o["dn_q"], s_swz=o["dn_swz"], qt=o["colT"]["down"],
                      st_swz=o["colT_swz"]["down"]))
     T("quant_dual", mx.mx_quantize_dual_batch, jobs)
-    # 2. dense forward, M = 4608
-    for name in ("xh", "xi"):
-        T("quant_row", mx.mx_quantize_rowwise_swz, I[name], q=o[name + "_q"], s_swz=o[name + "_swz"])
+    # 2. dense forward, M = 4608: both activations in one launch
+    T("quant_row", mx.mx_quantize_rowwise_swz_batch,
+      [dict(x=I[name], q=o[name + "_q"], s_swz=o[name + "_swz"]) for name in ("xh", "xi")])
     g = mx.mx_gemm
     T("gemm", g, o["xh_q"], o["xh_swz"], o["qkv_q"], o["qkv_swz"], c=o["C_qkv"], workspace=o["ws"])
     T("gemm", g, o["xh_q"], o["xh_swz"], o["o_q"], o["o_swz"], c=o["C_o"], workspace=o["ws"])
@@ -253,8 +246,7 @@ def step(mx, I, o, T):
     # 3. dense backward of gate_up, 12288 tokens
     T("quant_dual", dq, I["dy"], q=o["dy_q"], s_swz=o["dy_swz"], qt=o["dyT_q"],
       st_swz=o["dyT_swz"])
-    T("quant_col", cq, I["x"], o["xT_q"], o["xT_s"])
-    T("swizzle", sw, o["xT_s"], o["xT_swz"])
+    T("quant_col", mx.mx_quantize_colwise_swz, I["x"], qt=o["xT_q"], st_swz=o["xT_swz"])
     T("gemm", g, o["dy_q"], o["dy_swz"], o["guT_q"], o["guT_swz"], c=o["C_dgrad"], workspace=o["ws"])
     T("gemm", g, o["dyT_q"], o["dyT_swz"], o["xT_q"], o["xT_swz"], c=o["C_wgrad"], workspace=o["ws"])
     # 4. MoE layer: expert weights in both orientations, dispatch, gate_up,
@@ -616,7 +608,7 @@ def main():
                              "GB/s": col_only * QUANT_BYTES_PER_ELEMENT / (T.totals["quant_col"] / K) / 1e6},
         "quantize_dual": {"ms": T.totals["quant_dual"] / K,
                           "GB/s": dual_el * DUAL_BYTES_PER_ELEMENT / (T.totals["quant_dual"] / K) / 1e6},
-        "scale_swizzle": {"ms": T.totals["swizzle"] / K, "launches": T.counts["swizzle"] // K},
+        "scale_swizzle": {"launches": T.counts.get("swizzle", 0) // K},
         "moe_dispatch": {
             "ms": T.totals["moe_dispatch"] / K,
             "GB/s": w["disp_el"] * QUANT_BYTES_PER_ELEMENT / (T.totals["moe_dispatch"] / K) / 1e6},

@@ -12,6 +12,9 @@
  *
  *   mx_quantize_rowwise   BF16 -> E4M3 + E8M0, 32-element blocks along rows
  *   mx_quantize_colwise   BF16 -> E4M3 + E8M0, 32-element blocks down columns
+ *                         (the _swz forms write the scales in the GEMM's
+ *                         layout; mx_quantize_rowwise_swz_batch: several
+ *                         tensors in one launch)
  *   mx_scale_swizzle      E8M0 [rows][kblocks] -> the GEMM's scale layout
  *   mx_quantize_dual      both orientations from one read, scales already in
  *                         the GEMM's layout (mx_quantize_dual_batch: several
@@ -92,7 +95,7 @@
 extern "C" {
 #endif
 
-#define MXFP8_ABI_VERSION 7
+#define MXFP8_ABI_VERSION 8
 
 typedef enum mx_status {
     MX_OK = 0,
@@ -155,6 +158,29 @@ mx_status mx_quantize_rowwise_swz(const void *x, int64_t rows, int64_t cols, int
                                   int64_t ld_q, void *s_swz, int64_t s_tiles, void *stream);
 
 /*
+ * Several mx_quantize_rowwise_swz jobs in one launch: the activations of a
+ * layer's forward products (the paper's Table 6 times "MXFP8 quantization"
+ * as a kernel category of its own; a launch per tensor leaves a partial
+ * wave of workgroups each time).  jobs is a HOST array of n_jobs (0..8)
+ * descriptors, read before the call returns; each job has the meaning and
+ * requirements of mx_quantize_rowwise_swz's arguments and is validated
+ * before anything is launched (messages name the job).  A job's input must
+ * not overlap another job's outputs (else MX_ERR_OVERLAP); jobs may write
+ * disjoint parts of one output buffer, overlapping writes by two jobs give
+ * unspecified bytes there.  Every job's bytes equal mx_quantize_rowwise_swz's.
+ */
+#define MX_ROWWISE_MAX_JOBS 8
+typedef struct mx_rowwise_job {
+    const void *x;
+    int64_t rows, cols, ld_x;
+    void *q;
+    int64_t ld_q;
+    void *s_swz;
+    int64_t s_tiles;
+} mx_rowwise_job;
+mx_status mx_quantize_rowwise_swz_batch(const mx_rowwise_job *jobs, int n_jobs, void *stream);
+
+/*
  * Column-wise quantization (one 32x1 block per 32 consecutive elements of a
  * column), written TRANSPOSED so that every GEMM operand is K-contiguous:
  *   x   BF16  [rows][ld_x]   input, row-major
@@ -168,6 +194,28 @@ mx_status mx_quantize_rowwise_swz(const void *x, int64_t rows, int64_t cols, int
  */
 mx_status mx_quantize_colwise(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
                               void *qt, int64_t ld_qt, void *st, int64_t ld_st, void *stream);
+
+/*
+ * Column-wise quantization with the scales written straight into the GEMM's
+ * rearranged layout: mx_quantize_colwise followed by mx_scale_swizzle of its
+ * st, in one pass (the "MXFP8 quantization" and "scale rearrangement" of the
+ * paper's Table 6 fused for a backward operand that is not also needed
+ * row-wise, e.g. an activation kept for the weight gradient).
+ *   qt      = mx_quantize_colwise's qt
+ *   st_swz  the scales ([cols][rows/32]) rearranged: tile (ct, rt) (scale
+ *           rows 32ct.., blocks 8rt..) at byte offset (ct*st_tiles + rt)*256;
+ *           with st_tiles = rows/256 the buffer equals mx_scale_swizzle of
+ *           mx_quantize_colwise's st, every byte written.  A larger st_tiles,
+ *           with st_swz advanced to the block's first tile, writes into the
+ *           rearranged buffer of a larger operand (as mx_quantize_dual).
+ * Requirements: rows % 32 == 0 and cols % 8 == 0 (else MX_ERR_SHAPE); rows %
+ * 256 == 0 and cols % 32 == 0 (else MX_ERR_UNSUPPORTED: whole scale tiles);
+ * ld_x >= cols, ld_qt >= rows, st_tiles >= rows/256 (else
+ * MX_ERR_INVALID_ARG); x and qt 16-byte aligned with ld_x % 8 == 0 and
+ * ld_qt % 16 == 0 (else MX_ERR_ALIGN); no overlap (else MX_ERR_OVERLAP).
+ */
+mx_status mx_quantize_colwise_swz(const void *x, int64_t rows, int64_t cols, int64_t ld_x, void *qt,
+                                  int64_t ld_qt, void *st_swz, int64_t st_tiles, void *stream);
 
 /*
  * Size in bytes of the rearranged scale buffer for a [rows][kblocks] scale

@@ -26,6 +26,7 @@ __all__ = [
     "mx_grouped_gemm", "mx_quantize_dual", "mx_quantize_dual_batch", "mx_quantize_dual_experts",
     "mx_moe_dispatch", "mx_moe_combine", "mx_grouped_k_capacity", "mx_quantize_colwise_grouped",
     "mx_grouped_gemm_wgrad", "mx_swiglu_quantize", "mx_quantize_rowwise_swz",
+    "mx_quantize_rowwise_swz_batch", "mx_quantize_colwise_swz",
     "mx_quantize_dual_grouped", "mx_gemm_workspace_bytes", "mx_moe_dispatch_workspace_bytes",
     "mx_grouped_gemm_wgrad_workspace_bytes", "mx_moe_dispatch_noalloc", "MX_OK", "MX_ERR_INVALID_ARG", "MX_ERR_SHAPE", "MX_ERR_ALIGN",
     "MX_ERR_OVERLAP", "MX_ERR_UNSUPPORTED", "MX_ERR_HIP", "MX_BF16", "MX_F32",
@@ -107,6 +108,10 @@ def load() -> ctypes.CDLL:
                                            _i64, _vp, _vp]
     L.mx_quantize_rowwise_swz.restype = ctypes.c_int
     L.mx_quantize_rowwise_swz.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp]
+    L.mx_quantize_colwise_swz.restype = ctypes.c_int
+    L.mx_quantize_colwise_swz.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp]
+    L.mx_quantize_rowwise_swz_batch.restype = ctypes.c_int
+    L.mx_quantize_rowwise_swz_batch.argtypes = [ctypes.c_void_p, ctypes.c_int, _vp]
     L.mx_swiglu_quantize.restype = ctypes.c_int
     L.mx_swiglu_quantize.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]
     L.mx_quantize_dual_experts.restype = ctypes.c_int
@@ -599,6 +604,49 @@ def mx_quantize_rowwise_swz(x: torch.Tensor, q: Optional[torch.Tensor] = None,
                                         _dev(s_swz, "s_swz", torch.uint8), s_tiles, _stream(stream))
     _check("mx_quantize_rowwise_swz", st)
     return q, s_swz
+
+
+class _RowJob(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("ld_x", ctypes.c_int64), ("q", ctypes.c_void_p), ("ld_q", ctypes.c_int64),
+                ("s_swz", ctypes.c_void_p), ("s_tiles", ctypes.c_int64)]
+
+
+def mx_quantize_rowwise_swz_batch(jobs, stream=None) -> None:
+    """Several mx_quantize_rowwise_swz in one launch.  jobs: a sequence of dicts
+    with the device tensors x, q, s_swz and optionally s_tiles (the meaning of
+    mx_quantize_rowwise_swz's arguments); outputs are written in place."""
+    arr = (_RowJob * max(len(jobs), 1))()
+    for i, j in enumerate(jobs):
+        x = j["x"]
+        rows, cols = x.shape
+        q, s_swz = _u8(j["q"]), _u8(j["s_swz"])
+        arr[i] = _RowJob(_dev(x, "x", torch.bfloat16), rows, cols, _ld(x, "x"),
+                         _dev(q, "q", torch.uint8), _ld(q, "q"),
+                         _dev(s_swz, "s_swz", torch.uint8), j.get("s_tiles", cols // 256))
+    st = load().mx_quantize_rowwise_swz_batch(ctypes.cast(arr, ctypes.c_void_p), len(jobs), _stream(stream))
+    _check("mx_quantize_rowwise_swz_batch", st)
+
+
+def mx_quantize_colwise_swz(x: torch.Tensor, qt: Optional[torch.Tensor] = None,
+                            st_swz: Optional[torch.Tensor] = None, st_tiles: Optional[int] = None,
+                            stream=None):
+    """BF16 x[rows][cols] -> (qt [cols][rows], st_swz): column-wise MXFP8,
+    transposed, with the scales stored in the GEMM's rearranged layout."""
+    rows, cols = x.shape
+    dev = x.device
+    if qt is None:
+        qt = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+    if st_tiles is None:
+        st_tiles = rows // 256
+    if st_swz is None:
+        st_swz = torch.empty(mx_scale_swizzled_bytes(cols, rows // 32), dtype=torch.uint8, device=dev)
+    qt, st_swz = _u8(qt), _u8(st_swz)
+    st = load().mx_quantize_colwise_swz(_dev(x, "x", torch.bfloat16), rows, cols, _ld(x, "x"),
+                                        _dev(qt, "qt", torch.uint8), _ld(qt, "qt"),
+                                        _dev(st_swz, "st_swz", torch.uint8), st_tiles, _stream(stream))
+    _check("mx_quantize_colwise_swz", st)
+    return qt, st_swz
 
 
 def mx_quantize_dual_grouped(x: torch.Tensor, group_offsets: torch.Tensor, k_cap: Optional[int] = None,

@@ -174,35 +174,85 @@ mx_status mx_quantize_rowwise(const void *x, int64_t rows, int64_t cols, int64_t
                       fn);
 }
 
+// Checks of one row-wise job with rearranged scales; `who` names it in messages.
+static mx_status check_rowwise_swz(const char *who, const mx_rowwise_job &j)
+{
+    const int64_t rows = j.rows, cols = j.cols;
+    if (rows < 0 || cols < 0)
+        return fail(MX_ERR_INVALID_ARG, "%s: negative size rows=%lld cols=%lld", who, (long long)rows,
+                    (long long)cols);
+    if (cols % 32 != 0)
+        return fail(MX_ERR_SHAPE, "%s: cols=%lld is not a multiple of the 32-element block", who,
+                    (long long)cols);
+    if (cols % 256 != 0)
+        return fail(MX_ERR_UNSUPPORTED, "%s: cols=%lld: this build needs cols %% 256 == 0", who,
+                    (long long)cols);
+    if (j.ld_x < cols || j.ld_q < cols || j.s_tiles < cols / 256)
+        return fail(MX_ERR_INVALID_ARG, "%s: ld_x=%lld, ld_q=%lld or s_tiles=%lld too small", who,
+                    (long long)j.ld_x, (long long)j.ld_q, (long long)j.s_tiles);
+    if (rows == 0 || cols == 0)
+        return MX_OK;
+    if (!j.x || !j.q || !j.s_swz)
+        return fail(MX_ERR_INVALID_ARG, "%s: null pointer", who);
+    if (!aligned(j.x, 16) || !aligned(j.q, 8) || j.ld_x % 8 != 0 || j.ld_q % 8 != 0)
+        return fail(MX_ERR_ALIGN, "%s: x needs 16-byte aligned rows (ld_x %% 8), q 8-byte (ld_q %% 8)", who);
+    const int64_t ex = extent(rows, cols, j.ld_x, 2), eq = extent(rows, cols, j.ld_q, 1);
+    const int64_t es = (((rows + 31) / 32 - 1) * j.s_tiles + cols / 256) * 256;
+    if (overlap(j.x, ex, j.q, eq) || overlap(j.x, ex, j.s_swz, es) || overlap(j.q, eq, j.s_swz, es))
+        return fail(MX_ERR_OVERLAP, "%s: input and outputs must not overlap", who);
+    return MX_OK;
+}
+
 mx_status mx_quantize_rowwise_swz(const void *x, int64_t rows, int64_t cols, int64_t ld_x, void *q,
                                   int64_t ld_q, void *s_swz, int64_t s_tiles, void *stream)
 {
     const char *fn = "mx_quantize_rowwise_swz";
-    if (rows < 0 || cols < 0)
-        return fail(MX_ERR_INVALID_ARG, "%s: negative size rows=%lld cols=%lld", fn, (long long)rows,
-                    (long long)cols);
-    if (cols % 32 != 0)
-        return fail(MX_ERR_SHAPE, "%s: cols=%lld is not a multiple of the 32-element block", fn,
-                    (long long)cols);
-    if (cols % 256 != 0)
-        return fail(MX_ERR_UNSUPPORTED, "%s: cols=%lld: this build needs cols %% 256 == 0", fn,
-                    (long long)cols);
-    if (ld_x < cols || ld_q < cols || s_tiles < cols / 256)
-        return fail(MX_ERR_INVALID_ARG, "%s: ld_x=%lld, ld_q=%lld or s_tiles=%lld too small", fn,
-                    (long long)ld_x, (long long)ld_q, (long long)s_tiles);
+    const mx_status st = check_rowwise_swz(fn, mx_rowwise_job{x, rows, cols, ld_x, q, ld_q, s_swz, s_tiles});
+    if (st != MX_OK)
+        return st;
     if (rows == 0 || cols == 0)
         return ok();
-    if (!x || !q || !s_swz)
-        return fail(MX_ERR_INVALID_ARG, "%s: null pointer", fn);
-    if (!aligned(x, 16) || !aligned(q, 8) || ld_x % 8 != 0 || ld_q % 8 != 0)
-        return fail(MX_ERR_ALIGN, "%s: x needs 16-byte aligned rows (ld_x %% 8), q 8-byte (ld_q %% 8)", fn);
-    const int64_t ex = extent(rows, cols, ld_x, 2), eq = extent(rows, cols, ld_q, 1);
-    const int64_t es = (((rows + 31) / 32 - 1) * s_tiles + cols / 256) * 256;
-    if (overlap(x, ex, q, eq) || overlap(x, ex, s_swz, es) || overlap(q, eq, s_swz, es))
-        return fail(MX_ERR_OVERLAP, "%s: input and outputs must not overlap", fn);
     return hip_status(mx::launch_quantize_rowwise_swz(x, rows, cols, ld_x, q, ld_q, s_swz, s_tiles,
                                                       (hipStream_t)stream),
                       fn);
+}
+
+mx_status mx_quantize_rowwise_swz_batch(const mx_rowwise_job *jobs, int n_jobs, void *stream)
+{
+    const char *fn = "mx_quantize_rowwise_swz_batch";
+    if (n_jobs < 0 || n_jobs > MX_ROWWISE_MAX_JOBS)
+        return fail(MX_ERR_INVALID_ARG, "%s: n_jobs=%d outside 0..%d", fn, n_jobs, MX_ROWWISE_MAX_JOBS);
+    if (n_jobs == 0)
+        return ok();
+    if (!jobs)
+        return fail(MX_ERR_INVALID_ARG, "%s: null job array", fn);
+    static_assert(MX_ROWWISE_MAX_JOBS == mx::QR_MAX_JOBS, "job limits differ");
+    mx::RowJob rj[MX_ROWWISE_MAX_JOBS];
+    int n = 0;
+    for (int i = 0; i < n_jobs; i++) {
+        char who[96];
+        snprintf(who, sizeof who, "%s: job %d", fn, i);
+        const mx_status st = check_rowwise_swz(who, jobs[i]);
+        if (st != MX_OK)
+            return st;
+        const mx_rowwise_job &a = jobs[i];
+        if (a.rows == 0 || a.cols == 0)
+            continue;
+        // a job's input must not be written by another job
+        const int64_t ex = extent(a.rows, a.cols, a.ld_x, 2);
+        for (int k = 0; k < n_jobs; k++) {
+            const mx_rowwise_job &b = jobs[k];
+            if (k == i || b.rows == 0 || b.cols == 0)
+                continue;
+            const int64_t es = (((b.rows + 31) / 32 - 1) * b.s_tiles + b.cols / 256) * 256;
+            if (overlap(a.x, ex, b.q, extent(b.rows, b.cols, b.ld_q, 1)) || overlap(a.x, ex, b.s_swz, es))
+                return fail(MX_ERR_OVERLAP, "%s: job %d's input overlaps job %d's outputs", fn, i, k);
+        }
+        rj[n++] = mx::RowJob{a.x, a.rows, a.cols, a.ld_x, a.q, a.ld_q, a.s_swz, a.s_tiles};
+    }
+    if (n == 0)
+        return ok();
+    return hip_status(mx::launch_quantize_rowwise_batch(rj, n, (hipStream_t)stream), fn);
 }
 
 mx_status mx_quantize_colwise(const void *x, int64_t rows, int64_t cols, int64_t ld_x, void *qt,
@@ -234,6 +284,41 @@ mx_status mx_quantize_colwise(const void *x, int64_t rows, int64_t cols, int64_t
         return fail(MX_ERR_OVERLAP, "%s: input and outputs overlap", fn);
     return hip_status(mx::launch_quantize_colwise(x, rows, cols, ld_x, qt, ld_qt, st, ld_st,
                                                   (hipStream_t)stream),
+                      fn);
+}
+
+mx_status mx_quantize_colwise_swz(const void *x, int64_t rows, int64_t cols, int64_t ld_x, void *qt,
+                                  int64_t ld_qt, void *st_swz, int64_t st_tiles, void *stream)
+{
+    const char *fn = "mx_quantize_colwise_swz";
+    if (rows < 0 || cols < 0)
+        return fail(MX_ERR_INVALID_ARG, "%s: negative size rows=%lld cols=%lld", fn,
+                    (long long)rows, (long long)cols);
+    if (rows % 32 != 0)
+        return fail(MX_ERR_SHAPE, "%s: rows=%lld is not a multiple of the 32-element block", fn,
+                    (long long)rows);
+    if (cols % 8 != 0)
+        return fail(MX_ERR_SHAPE, "%s: cols=%lld is not a multiple of 8", fn, (long long)cols);
+    if (rows % 256 != 0 || cols % 32 != 0)
+        return fail(MX_ERR_UNSUPPORTED,
+                    "%s: rows=%lld, cols=%lld: this build needs rows %% 256 == 0 and cols %% 32 == 0", fn,
+                    (long long)rows, (long long)cols);
+    if (ld_x < cols || ld_qt < rows || st_tiles < rows / 256)
+        return fail(MX_ERR_INVALID_ARG, "%s: ld_x=%lld, ld_qt=%lld or st_tiles=%lld too small", fn,
+                    (long long)ld_x, (long long)ld_qt, (long long)st_tiles);
+    if (rows == 0 || cols == 0)
+        return ok();
+    if (!x || !qt || !st_swz)
+        return fail(MX_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!aligned(x, 16) || !aligned(qt, 16) || ld_x % 8 != 0 || ld_qt % 16 != 0)
+        return fail(MX_ERR_ALIGN,
+                    "%s: x and qt need 16-byte aligned rows (ld_x %% 8, ld_qt %% 16)", fn);
+    const int64_t ex = extent(rows, cols, ld_x, 2), eq = extent(cols, rows, ld_qt, 1);
+    const int64_t es = ((cols / 32 - 1) * st_tiles + rows / 256) * 256;
+    if (overlap(x, ex, qt, eq) || overlap(x, ex, st_swz, es) || overlap(qt, eq, st_swz, es))
+        return fail(MX_ERR_OVERLAP, "%s: input and outputs overlap", fn);
+    return hip_status(mx::launch_quantize_colwise_swz(x, rows, cols, ld_x, qt, ld_qt, st_swz, st_tiles,
+                                                      (hipStream_t)stream),
                       fn);
 }
 

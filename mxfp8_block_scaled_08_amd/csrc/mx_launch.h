@@ -22,6 +22,28 @@ hipError_t launch_quantize_colwise(const void *x, int64_t rows, int64_t cols, in
                                    void *qt, int64_t ld_qt, void *st, int64_t ld_st,
                                    hipStream_t stream);
 
+// Column-wise with the scales ([cols][rows/32]) stored in the rearranged
+// layout (tile (ct, rt) at st_swz + (ct * st_tiles + rt) * 256);
+// rows % 256 == 0, cols % 32 == 0.
+hipError_t launch_quantize_colwise_swz(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                                       void *qt, int64_t ld_qt, void *st_swz, int64_t st_tiles,
+                                       hipStream_t stream);
+
+// One tensor of a batched row-wise quantization with rearranged scales
+// (tile (rt, kt) at s_swz + (rt * s_tiles + kt) * 256); cols % 256 == 0.
+struct RowJob {
+    const void *x;
+    int64_t rows, cols, ld_x;
+    void *q;
+    int64_t ld_q;
+    void *s_swz;
+    int64_t s_tiles;
+};
+constexpr int QR_MAX_JOBS = 8;
+
+// n in 1..QR_MAX_JOBS jobs, one launch; empty jobs are allowed.
+hipError_t launch_quantize_rowwise_batch(const RowJob *jobs, int n, hipStream_t stream);
+
 // One tensor of a dual (row-wise + column-wise) quantization.  s_swz /
 // st_swz: tile (0, 0) of its rearranged scales; tile (rt, kt) at
 // + (rt * s_tiles + kt) * 256 (st_tiles likewise).

@@ -24,14 +24,15 @@ namespace mx {
 constexpr int QR_THREADS = 256;
 constexpr int QR_UNROLL = 4;
 
+// The units base, base + QR_THREADS, .. (QR_UNROLL of them) of one tensor.
 template <bool CONTIG, bool SWZ>
-__global__ __launch_bounds__(QR_THREADS) void quantize_rowwise_kernel(
-    const uint16_t *__restrict__ x, int64_t ld_x, uint8_t *__restrict__ q, int64_t ld_q,
-    uint8_t *__restrict__ s, int64_t ld_s, int64_t units, uint32_t units_per_row)
+__device__ __forceinline__ void quantize_rowwise_units(const uint16_t *__restrict__ x, int64_t ld_x,
+                                                       uint8_t *__restrict__ q, int64_t ld_q,
+                                                       uint8_t *__restrict__ s, int64_t ld_s,
+                                                       int64_t units, uint32_t units_per_row,
+                                                       int64_t base)
 {
-    const int64_t per_block = (int64_t)QR_THREADS * QR_UNROLL;
-    for (int64_t base = (int64_t)blockIdx.x * per_block + threadIdx.x; base < units;
-         base += (int64_t)gridDim.x * per_block) {
+    {
         uint4 v[QR_UNROLL];
         int64_t xo[QR_UNROLL];
 #pragma unroll
@@ -88,6 +89,39 @@ __global__ __launch_bounds__(QR_THREADS) void quantize_rowwise_kernel(
     }
 }
 
+template <bool CONTIG, bool SWZ>
+__global__ __launch_bounds__(QR_THREADS) void quantize_rowwise_kernel(
+    const uint16_t *__restrict__ x, int64_t ld_x, uint8_t *__restrict__ q, int64_t ld_q,
+    uint8_t *__restrict__ s, int64_t ld_s, int64_t units, uint32_t units_per_row)
+{
+    const int64_t per_block = (int64_t)QR_THREADS * QR_UNROLL;
+    for (int64_t base = (int64_t)blockIdx.x * per_block + threadIdx.x; base < units;
+         base += (int64_t)gridDim.x * per_block)
+        quantize_rowwise_units<CONTIG, SWZ>(x, ld_x, q, ld_q, s, ld_s, units, units_per_row, base);
+}
+
+// Several tensors in one launch, scales rearranged: job j takes workgroups
+// first[j] .. first[j+1] - 1, each QR_THREADS * QR_UNROLL units of its
+// tensor (the forward activations of a layer in one launch instead of one
+// small launch each).
+struct RowBatch {
+    RowJob job[QR_MAX_JOBS];
+    int64_t first[QR_MAX_JOBS + 1];
+    int n;
+};
+
+__global__ __launch_bounds__(QR_THREADS) void quantize_rowwise_batch_kernel(RowBatch B)
+{
+    int j = 0;
+    while (j + 1 < B.n && (int64_t)blockIdx.x >= B.first[j + 1])
+        j++;
+    const RowJob &J = B.job[j];
+    const int64_t units = J.rows * (J.cols / 8);
+    const int64_t base = ((int64_t)blockIdx.x - B.first[j]) * (QR_THREADS * QR_UNROLL) + threadIdx.x;
+    quantize_rowwise_units<false, true>((const uint16_t *)J.x, J.ld_x, (uint8_t *)J.q, J.ld_q,
+                                        (uint8_t *)J.s_swz, J.s_tiles, units, (uint32_t)(J.cols / 8), base);
+}
+
 // ---------------------------------------------------------------------------
 // Column-wise: a block is 32 consecutive rows of one column, and the output is
 // transposed (qt[col][row], st[col][row / 32]).  No LDS: each wave covers a
@@ -117,6 +151,10 @@ constexpr int QC_TILE_C = 256;
 constexpr int QC_WIDE = 32;
 constexpr int QC_GROUP_R = 32;
 
+// SWZ: each scale byte goes straight to its place in the rearranged layout
+// of the [cols][rows/32] scales (ld_st then holds the tiles per 32-column
+// tile row), which saves the separate rearrangement pass.
+template <bool SWZ>
 __global__ __launch_bounds__(QC_THREADS) void quantize_colwise_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     uint8_t *__restrict__ qt, int64_t ld_qt, uint8_t *__restrict__ st, int64_t ld_st,
@@ -187,8 +225,14 @@ __global__ __launch_bounds__(QC_THREADS) void quantize_colwise_kernel(
             o[k] = nan_block_select(cvt_x4(p01, p23, sc), c);
         }
         *reinterpret_cast<uint4 *>(qt + (c0 + j) * ld_qt + r0) = make_uint4(o[0], o[1], o[2], o[3]);
-        if (half == 0)
-            st[(c0 + j) * ld_st + (r0 >> 5)] = (uint8_t)c;
+        if (half == 0) {
+            const int64_t col = c0 + j, b = r0 >> 5;  // scale row and 32-element block
+            if (SWZ)
+                st[((col >> 5) * ld_st + (b >> 3)) * 256 + (32 * (b & 1) + (col & 31)) * 4 + ((b & 7) >> 1)] =
+                    (uint8_t)c;
+            else
+                st[col * ld_st + b] = (uint8_t)c;
+        }
     }
 }
 
@@ -496,9 +540,43 @@ hipError_t launch_quantize_colwise(const void *x, int64_t rows, int64_t cols, in
     int64_t blocks = tiles_r * tiles_c;
     if (tiles_c >= QC_WIDE)
         blocks = (blocks + 7) / 8 * 8;
-    hipLaunchKernelGGL(quantize_colwise_kernel, dim3((unsigned)blocks), dim3(QC_THREADS), 0,
+    hipLaunchKernelGGL(quantize_colwise_kernel<false>, dim3((unsigned)blocks), dim3(QC_THREADS), 0,
                        stream, (const uint16_t *)x, rows, cols, ld_x, (uint8_t *)qt, ld_qt,
                        (uint8_t *)st, ld_st, tiles_r, tiles_c);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_colwise_swz(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
+                                       void *qt, int64_t ld_qt, void *st_swz, int64_t st_tiles,
+                                       hipStream_t stream)
+{
+    const int64_t tiles_c = (cols + QC_TILE_C - 1) / QC_TILE_C;
+    const int64_t tiles_r = (rows + QC_TILE_R - 1) / QC_TILE_R;
+    int64_t blocks = tiles_r * tiles_c;
+    if (tiles_c >= QC_WIDE)
+        blocks = (blocks + 7) / 8 * 8;
+    hipLaunchKernelGGL(quantize_colwise_kernel<true>, dim3((unsigned)blocks), dim3(QC_THREADS), 0,
+                       stream, (const uint16_t *)x, rows, cols, ld_x, (uint8_t *)qt, ld_qt,
+                       (uint8_t *)st_swz, st_tiles, tiles_r, tiles_c);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_rowwise_batch(const RowJob *jobs, int n, hipStream_t stream)
+{
+    RowBatch B{};
+    B.n = n;
+    int64_t blocks = 0;
+    const int64_t per_block = (int64_t)QR_THREADS * QR_UNROLL;
+    for (int j = 0; j < n; j++) {
+        B.job[j] = jobs[j];
+        B.first[j] = blocks;
+        blocks += (jobs[j].rows * (jobs[j].cols / 8) + per_block - 1) / per_block;
+    }
+    B.first[n] = blocks;
+    if (blocks == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(quantize_rowwise_batch_kernel, dim3((unsigned)blocks), dim3(QR_THREADS), 0,
+                       stream, B);
     return hipGetLastError();
 }
 

@@ -31,6 +31,9 @@ hipError_t launch_quantize_rowwise_swz(const void *, int64_t, int64_t, int64_t, 
                                        hipStream_t) { return hit(); }
 hipError_t launch_quantize_colwise(const void *, int64_t, int64_t, int64_t, void *, int64_t, void *, int64_t,
                                    hipStream_t) { return hit(); }
+hipError_t launch_quantize_colwise_swz(const void *, int64_t, int64_t, int64_t, void *, int64_t, void *, int64_t,
+                                       hipStream_t) { return hit(); }
+hipError_t launch_quantize_rowwise_batch(const RowJob *, int, hipStream_t) { return hit(); }
 hipError_t launch_quantize_dual(const DualJob *, int, hipStream_t) { return hit(); }
 hipError_t launch_scale_swizzle(const void *, int64_t, int64_t, int64_t, void *, hipStream_t) { return hit(); }
 int64_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int c_dtype, bool vec16)

@@ -38,7 +38,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for n in names:
         assert hasattr(raw, n), f"{n} declared in include/mxfp8.h but not exported"
         assert hasattr(mx, n), f"{n} has no Python binding of the same name"
-    assert L.mx_abi_version() == 7
+    assert L.mx_abi_version() == 8
 
 
 def test_status_strings():
@@ -415,6 +415,59 @@ def test_quantize_rowwise_swz_validation():
     assert f(FAKE, 64, 512, 512, FAKE + 1024, 512, FAKE3, 2, STREAM) == mx.MX_ERR_OVERLAP
     assert f(0, 64, 512, 512, FAKE2, 512, FAKE3, 2, STREAM) == mx.MX_ERR_INVALID_ARG
     assert f(FAKE, 0, 512, 512, FAKE2, 512, FAKE3, 2, STREAM) == mx.MX_OK
+
+
+def test_quantize_rowwise_swz_batch_validation():
+    L = mx.load()
+    f = L.mx_quantize_rowwise_swz_batch
+    J = mx._RowJob
+    good = (FAKE, 64, 512, 512, FAKE2, 512, FAKE3, 2)
+    arr = (J * 3)(J(*good), J(*good), J(*good))
+    assert f(ctypes.cast(arr, ctypes.c_void_p), 9, STREAM) == mx.MX_ERR_INVALID_ARG
+    assert "0..8" in _err(L)
+    assert f(ctypes.cast(arr, ctypes.c_void_p), -1, STREAM) == mx.MX_ERR_INVALID_ARG
+    assert f(None, 2, STREAM) == mx.MX_ERR_INVALID_ARG
+    assert f(None, 0, STREAM) == mx.MX_OK
+    for i, v, code in ((2, 48, mx.MX_ERR_SHAPE), (2, 288, mx.MX_ERR_UNSUPPORTED), (7, 1, mx.MX_ERR_INVALID_ARG),
+                       (1, -1, mx.MX_ERR_INVALID_ARG), (0, FAKE + 8, mx.MX_ERR_ALIGN),
+                       (4, FAKE + 1024, mx.MX_ERR_OVERLAP), (6, 0, mx.MX_ERR_INVALID_ARG)):
+        bad = list(good)
+        bad[i] = v
+        if i == 2:
+            bad[3] = bad[5] = v
+        arr[1] = J(*bad)
+        assert f(ctypes.cast(arr, ctypes.c_void_p), 3, STREAM) == code, (i, v)
+        assert "job 1" in _err(L)
+    arr[1] = J(*good)
+    other = list(good)
+    other[0] = 0x180000000                           # job 2 reads ...
+    other[6] = FAKE + 4096                           # ... and writes its scales into job 0's input
+    arr[2] = J(*other)
+    assert f(ctypes.cast(arr, ctypes.c_void_p), 3, STREAM) == mx.MX_ERR_OVERLAP
+    assert "job 0" in _err(L)
+    empty = list(good)
+    empty[1] = 0
+    arr[0] = arr[1] = arr[2] = J(*empty)
+    assert f(ctypes.cast(arr, ctypes.c_void_p), 3, STREAM) == mx.MX_OK
+
+
+def test_quantize_colwise_swz_validation():
+    L = mx.load()
+    f = L.mx_quantize_colwise_swz
+    # x, rows, cols, ld_x, qt, ld_qt, st_swz, st_tiles
+    assert f(FAKE, 48, 64, 64, FAKE2, 48, FAKE3, 1, STREAM) == mx.MX_ERR_SHAPE
+    assert f(FAKE, 256, 60, 64, FAKE2, 256, FAKE3, 1, STREAM) == mx.MX_ERR_SHAPE
+    assert f(FAKE, 288, 64, 64, FAKE2, 288, FAKE3, 2, STREAM) == mx.MX_ERR_UNSUPPORTED
+    assert f(FAKE, 256, 40, 40, FAKE2, 256, FAKE3, 1, STREAM) == mx.MX_ERR_UNSUPPORTED
+    assert f(FAKE, 512, 64, 64, FAKE2, 512, FAKE3, 1, STREAM) == mx.MX_ERR_INVALID_ARG  # st_tiles
+    assert f(FAKE, 512, 64, 64, FAKE2, 256, FAKE3, 2, STREAM) == mx.MX_ERR_INVALID_ARG  # ld_qt
+    assert f(FAKE, -256, 64, 64, FAKE2, 512, FAKE3, 2, STREAM) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE, 512, 64, 64, FAKE2 + 8, 512, FAKE3, 2, STREAM) == mx.MX_ERR_ALIGN
+    assert f(FAKE, 512, 64, 64, FAKE2, 520, FAKE3, 2, STREAM) == mx.MX_ERR_ALIGN
+    assert f(FAKE, 512, 64, 64, FAKE + 4096, 512, FAKE3, 2, STREAM) == mx.MX_ERR_OVERLAP
+    assert f(FAKE, 512, 64, 64, FAKE2, 512, FAKE2 + 512, 2, STREAM) == mx.MX_ERR_OVERLAP
+    assert f(FAKE, 512, 64, 64, FAKE2, 512, 0, 2, STREAM) == mx.MX_ERR_INVALID_ARG
+    assert f(FAKE, 0, 64, 64, FAKE2, 0, FAKE3, 0, STREAM) == mx.MX_OK
 
 
 def test_quantize_dual_grouped_validation():

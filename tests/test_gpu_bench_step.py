@@ -93,7 +93,7 @@ def test_bench_step_matches_oracle(gpu_lib):
     _row(o["o_q"], o["o_swz"], bits(W["o"]), "o")
     _row(o["dn_q"], o["dn_swz"], bits(W["down"]), "down")
     for n in ("q", "k", "v", "o", "down"):
-        _col(o["colT"][n][0], o["colT_swz"][n], bits(W[n]), n)
+        _col(o["colT"][n], o["colT_swz"][n], bits(W[n]), n)
     print("activations", flush=True)
     oxh = _row(o["xh_q"], o["xh_swz"], bits(I["xh"]), "X (hidden)")
     _row(o["xi_q"], o["xi_swz"], bits(I["xi"]), "X (intermediate)")

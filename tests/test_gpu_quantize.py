@@ -260,3 +260,120 @@ def test_rowwise_swz_into_larger_operand(gpu_lib):
     oq, os_ = oracle.quantize_rowwise(mxsynth.bits(cat))
     assert np.array_equal(q.cpu().numpy(), oq)
     assert np.array_equal(s_swz.cpu().numpy(), oracle.scale_swizzle(os_))
+
+
+@pytest.mark.parametrize("rows,cols", [(256, 32), (512, 96), (768, 264 + 8 * 3),
+                                       (4096, 1024), (4608, 4096),
+                                       # 32+ column tiles (the per-XCD tile order), a ragged
+                                       # last column tile and tile-row group
+                                       (1280, 8192), (256, 16416)])
+def test_colwise_swz_matches_oracle(gpu_lib, rows, cols):
+    """Column-wise codes and the rearranged scales in one pass: the codes
+    equal the oracle's column-wise codes and the scale buffer equals the
+    oracle's rearrangement of its column-wise scales, every byte."""
+    mx = gpu_lib
+    x = mxsynth.normal_bf16((rows, cols), 1.0, seed=3 * rows + cols, outlier_frac=0.005, outlier_mul=50.0)
+    qt, st_swz = mx.mx_quantize_colwise_swz(bf16_dev(x))
+    torch.cuda.synchronize()
+    from gpu_util import oracle_colwise_par
+    oqt, ost = oracle_colwise_par(mxsynth.bits(x))
+    assert np.array_equal(qt.cpu().numpy(), oqt)
+    assert st_swz.numel() == mx.mx_scale_swizzled_bytes(cols, rows // 32)
+    assert np.array_equal(st_swz.cpu().numpy(), oracle.scale_swizzle(ost))
+
+
+def test_colwise_swz_strided_and_into_larger_operand(gpu_lib):
+    """A strided input, and two tensors stacked along K (= their rows) written
+    into one operand with st_tiles of the larger K: the result equals the
+    column-wise quantization of the stacked tensor; bytes past the codes'
+    columns are untouched."""
+    mx = gpu_lib
+    a = mxsynth.normal_bf16((256, 96), 1.0, seed=11)
+    b = mxsynth.normal_bf16((512, 96), 2.0, seed=12)
+    cat = torch.cat([a, b], dim=0)
+    xbuf = torch.zeros(512, 136, dtype=torch.bfloat16, device="cuda")
+    xbuf[:, :96] = b.cuda()
+    kt = 768 // 256
+    qbuf = torch.full((96, 800), 0x11, dtype=torch.uint8, device="cuda")
+    st_swz = torch.full((mx.mx_scale_swizzled_bytes(96, 24),), 0xEE, dtype=torch.uint8, device="cuda")
+    mx.mx_quantize_colwise_swz(a.cuda(), qt=qbuf[:, :256], st_swz=st_swz, st_tiles=kt)
+    mx.mx_quantize_colwise_swz(xbuf[:, :96], qt=qbuf[:, 256:768], st_swz=st_swz[256:], st_tiles=kt)
+    torch.cuda.synchronize()
+    oqt, ost = oracle.quantize_colwise(mxsynth.bits(cat))
+    assert np.array_equal(qbuf[:, :768].cpu().numpy(), oqt)
+    assert (qbuf[:, 768:] == 0x11).all()
+    assert np.array_equal(st_swz.cpu().numpy(), oracle.scale_swizzle(ost))
+
+
+def _rowwise_swz_ref(x: torch.Tensor):
+    """Oracle codes and scale buffer of mx_quantize_rowwise_swz (rows past the
+    tensor in its last 32-row tile excepted: compared through unswizzle)."""
+    from gpu_util import oracle_rowwise_par
+    return oracle_rowwise_par(mxsynth.bits(x))
+
+
+def _check_rowwise_swz(q: torch.Tensor, s_swz: torch.Tensor, x: torch.Tensor):
+    rows, cols = x.shape
+    oq, os_ = _rowwise_swz_ref(x)
+    assert np.array_equal(q.cpu().numpy(), oq)
+    got = s_swz.cpu().numpy()
+    if rows % 32 == 0:
+        assert np.array_equal(got, oracle.scale_swizzle(os_))
+    else:
+        assert np.array_equal(oracle.scale_unswizzle(got, rows, cols // 32), os_)
+
+
+def test_rowwise_swz_batch_layer_activations(gpu_lib):
+    """The two activations of a dense layer's forward products (4608 tokens:
+    hidden 4096, intermediate 12288) in one launch, every byte against the
+    oracle."""
+    mx = gpu_lib
+    xs = [mxsynth.normal_bf16((4608, 4096), 1.0, seed=21, outlier_frac=0.005, outlier_mul=50.0),
+          mxsynth.normal_bf16((4608, 12288), 0.5, seed=22, outlier_frac=0.005, outlier_mul=50.0)]
+    jobs = []
+    for x in xs:
+        r, c = x.shape
+        jobs.append({"x": bf16_dev(x), "q": torch.empty(r, c, dtype=torch.uint8, device="cuda"),
+                     "s_swz": torch.full((mx.mx_scale_swizzled_bytes(r, c // 32),), 0xEE, dtype=torch.uint8,
+                                         device="cuda")})
+    mx.mx_quantize_rowwise_swz_batch(jobs)
+    torch.cuda.synchronize()
+    for x, j in zip(xs, jobs):
+        _check_rowwise_swz(j["q"], j["s_swz"], x)
+
+
+def test_rowwise_swz_batch_ragged_jobs(gpu_lib):
+    """Eight jobs of mixed, ragged shapes (one empty, one strided, two writing
+    side by side into one operand), each equal to the oracle."""
+    mx = gpu_lib
+    shapes = [(37, 512), (0, 256), (256, 768), (1, 256), (1000, 4096), (33, 12288)]
+    xs = [mxsynth.normal_bf16(s, 1.0, seed=40 + i, outlier_frac=0.01, outlier_mul=50.0)
+          for i, s in enumerate(shapes)]
+    jobs = []
+    for x in xs:
+        r, c = x.shape
+        jobs.append({"x": bf16_dev(x), "q": torch.empty(r, c, dtype=torch.uint8, device="cuda"),
+                     "s_swz": torch.full((max(mx.mx_scale_swizzled_bytes(r, c // 32), 1),), 0xEE,
+                                         dtype=torch.uint8, device="cuda")})
+    # the strided one: job 2 reads a view of a wider buffer and writes into a wider q
+    xbuf = torch.zeros(256, 1024, dtype=torch.bfloat16, device="cuda")
+    xbuf[:, :768] = xs[2].cuda()
+    qbuf = torch.full((256, 1024), 0x11, dtype=torch.uint8, device="cuda")
+    jobs[2]["x"], jobs[2]["q"] = xbuf[:, :768], qbuf[:, :768]
+    # two halves of one [64][768] operand along K
+    a = mxsynth.normal_bf16((64, 512), 1.0, seed=50)
+    b = mxsynth.normal_bf16((64, 256), 1.0, seed=51)
+    cat = torch.cat([a, b], dim=1)
+    qc = torch.empty(64, 768, dtype=torch.uint8, device="cuda")
+    sc = torch.full((mx.mx_scale_swizzled_bytes(64, 24),), 0xEE, dtype=torch.uint8, device="cuda")
+    jobs.append({"x": a.cuda(), "q": qc[:, :512], "s_swz": sc, "s_tiles": 3})
+    jobs.append({"x": b.cuda(), "q": qc[:, 512:], "s_swz": sc[512:], "s_tiles": 3})
+    assert len(jobs) == 8
+    mx.mx_quantize_rowwise_swz_batch(jobs)
+    torch.cuda.synchronize()
+    for i, x in enumerate(xs):
+        if x.shape[0] == 0:
+            continue
+        _check_rowwise_swz(jobs[i]["q"], jobs[i]["s_swz"], x)
+    assert (qbuf[:, 768:] == 0x11).all()
+    _check_rowwise_swz(qc, sc, cat)
