@@ -57,7 +57,34 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES between two device buffers (a plain copy of known "
                          "size, for scaling the HBM byte counters) and exit")
+    ap.add_argument("--hbm-probe", action="store_true",
+                    help="only time plain device copies and reads of 1 GiB (what this GPU's HBM "
+                         "delivers to simple streaming kernels) and exit")
     return ap.parse_args()
+
+
+def hbm_probe(torch):
+    """Best-of-10 bandwidth of plain streaming kernels over 1 GiB buffers:
+    the runtime's device-to-device copy, an elementwise copy (torch's vectorized
+    kernel) and a read-only reduction; read + written bytes / time."""
+    n = 1 << 30
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    out = {}
+    cases = (("runtime device copy", lambda: b.copy_(a), 2 * n),
+             ("elementwise copy (x * 1)", lambda: torch.mul(a, 1.0, out=b), 2 * n),
+             ("read-only reduction (sum)", lambda: a.sum(), n))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name, fn, traffic in cases:
+        best = float("inf")
+        for _ in range(11):
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        out[name] = {"us": round(best * 1e3, 1), "GB/s": round(traffic / (best * 1e-3) / 1e9, 1)}
+    return out
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_hbm_traffic_qwen3_layer.md")
@@ -546,6 +573,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n}))
+        return
+    if args.hbm_probe:
+        torch.cuda.set_device(0)
+        print(json.dumps({"hbm_probe_1GiB": hbm_probe(torch)}))
         return
 
     import mxfp8_block_scaled_08_amd as mx

@@ -78,6 +78,32 @@ __device__ __forceinline__ uint32_t nan_block_select(uint32_t codes, uint32_t c)
 }
 
 typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
+typedef unsigned v2u_t __attribute__((ext_vector_type(2)));
+
+// Streaming accesses: a pass over far more data than L2 and the Infinity
+// Cache hold, each input byte read once and each output byte written once,
+// with the non-temporal cache policy (the nt bit; STREAM is the same policy
+// as the cache-policy operand of buffer accesses), whose lines are evicted
+// first.  Measured on the layer pass: the elementwise passes run faster with
+// it, and so do the products that follow them, since the passes' outputs are
+// written back to HBM while they run instead of being evicted, dirty, from
+// the Infinity Cache by the product's own reads.
+constexpr int STREAM = 2;
+
+__device__ __forceinline__ uint4 ld_stream(const void *p)
+{
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const v4u_t *>(p)));
+}
+
+__device__ __forceinline__ void st_stream(void *p, uint4 v)
+{
+    __builtin_nontemporal_store(__builtin_bit_cast(v4u_t, v), reinterpret_cast<v4u_t *>(p));
+}
+
+__device__ __forceinline__ void st_stream(void *p, uint2 v)
+{
+    __builtin_nontemporal_store(__builtin_bit_cast(v2u_t, v), reinterpret_cast<v2u_t *>(p));
+}
 
 // Buffer resource for a byte range: uniform base and size in SGPRs, so each
 // lane supplies only a 32-bit offset.  Word 3 selects 32-bit data format

@@ -167,6 +167,8 @@ __global__ __launch_bounds__(MOE_Q_THREADS) void moe_gather_quantize_kernel(
         uint4 w = make_uint4(0, 0, 0, 0);
         if (live) {
             const int64_t t = src_token[row];
+            // a plain load: each token's row is read once per routed copy,
+            // and the copies after the first can hit in L2 or the Infinity Cache
             w = *reinterpret_cast<const uint4 *>(x + t * ld_x + cu * 8);
         }
         uint32_t m = pk_max_u16(pk_max_u16(mag2(w.x), mag2(w.y)), pk_max_u16(mag2(w.z), mag2(w.w)));
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(MOE_Q_THREADS) void moe_gather_quantize_kernel(
         uint2 out;
         out.x = nan_block_select(cvt_x4(w.x, w.y, sc), c);
         out.y = nan_block_select(cvt_x4(w.z, w.w, sc), c);
-        *reinterpret_cast<uint2 *>(q + row * ld_q + cu * 8) = out;
+        st_stream(q + row * ld_q + cu * 8, out);
         if ((threadIdx.x & 3) == 0) {
             const int64_t b = cu >> 2;  // 32-element block of the row
             s_swz[((row >> 5) * kt + (b >> 3)) * 256 + (32 * (b & 1) + (row & 31)) * 4 + ((b & 7) >> 1)] =
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t *__rest
 #pragma unroll
             for (int j = 0; j < K; j++)
                 v[j] = (p[j] >= 0 && p[j] < rows_y)
-                           ? *reinterpret_cast<const uint4 *>(y + (int64_t)p[j] * ld_y + cu * 8)
+                           ? ld_stream(y + (int64_t)p[j] * ld_y + cu * 8)
                            : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
             for (int j = 0; j < K; j++)
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t *__rest
                 if (p < 0 || p >= rows_y)  // unrouted, or not a row of y
                     continue;
                 combine_acc(acc, weights[t * topk + j],
-                            *reinterpret_cast<const uint4 *>(y + (int64_t)p * ld_y + cu * 8));
+                            ld_stream(y + (int64_t)p * ld_y + cu * 8));
             }
         }
         typedef float f2_t __attribute__((ext_vector_type(2)));
@@ -306,7 +308,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t *__rest
 #pragma unroll
         for (int k = 0; k < 4; k++)
             o[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t{acc[2 * k], acc[2 * k + 1]}), bf16x2_t));
-        *reinterpret_cast<uint4 *>(out + t * ld_out + cu * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+        st_stream(out + t * ld_out + cu * 8, make_uint4(o[0], o[1], o[2], o[3]));
     }
 }
 
@@ -351,8 +353,8 @@ __global__ __launch_bounds__(256) void swiglu_quantize_kernel(
         const bool live = u < units;
         uint4 gw = make_uint4(0, 0, 0, 0), uw = make_uint4(0, 0, 0, 0);
         if (live) {
-            gw = *reinterpret_cast<const uint4 *>(gu + row * ld_gu + cu * 8);
-            uw = *reinterpret_cast<const uint4 *>(gu + row * ld_gu + F + cu * 8);
+            gw = ld_stream(gu + row * ld_gu + cu * 8);
+            uw = ld_stream(gu + row * ld_gu + F + cu * 8);
         }
         const uint32_t gs[4] = {gw.x, gw.y, gw.z, gw.w}, us[4] = {uw.x, uw.y, uw.z, uw.w};
         uint32_t hw[4];
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(256) void swiglu_quantize_kernel(
             hw[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t{hv[0], hv[1]}), bf16x2_t));
         }
         if (live && h != nullptr)
-            *reinterpret_cast<uint4 *>(h + row * ld_h + cu * 8) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            st_stream(h + row * ld_h + cu * 8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
         uint32_t m = pk_max_u16(pk_max_u16(mag2(hw[0]), mag2(hw[1])), pk_max_u16(mag2(hw[2]), mag2(hw[3])));
         m = max(m & 0xFFFFu, m >> 16);
         m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
@@ -382,7 +384,7 @@ __global__ __launch_bounds__(256) void swiglu_quantize_kernel(
         uint2 out;
         out.x = nan_block_select(cvt_x4(hw[0], hw[1], sc), c);
         out.y = nan_block_select(cvt_x4(hw[2], hw[3], sc), c);
-        *reinterpret_cast<uint2 *>(q + row * ld_q + cu * 8) = out;
+        st_stream(q + row * ld_q + cu * 8, out);
         if ((threadIdx.x & 3) == 0) {
             const int64_t b = cu >> 2;  // 32-element block of the row
             s_swz[((row >> 5) * kt + (b >> 3)) * 256 + (32 * (b & 1) + (row & 31)) * 4 + ((b & 7) >> 1)] =

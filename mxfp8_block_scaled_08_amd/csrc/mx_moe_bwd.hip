@@ -127,7 +127,7 @@ __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
     uint4 v[16];
 #pragma unroll
     for (int i = 0; i < 16; i++)
-        v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff + i * vstep, 0, 0));
+        v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff + i * vstep, 0, STREAM));
     // column-wise maxima (per column, the lane's 16 rows) and, with ROW, the
     // row-wise ones (per row, the lane's 8 columns) in one pass, each
     // magnitude used by both as soon as it is formed
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
                 o[k] = nan_block_select(cvt_x4(p01, p23, sc), c);
             }
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u_t, make_uint4(o[0], o[1], o[2], o[3])), rq,
-                                                   qoff, (int)(j * ld_qt), 0);
+                                                   qoff, (int)(j * ld_qt), STREAM);
             if (half == 0) {
                 // rearranged row = column wc*64 + cg*8 + j of the tile, block wr*4 + rb
                 const int col = wc * 64 + cg * 8 + j, blk = wr * 4 + rb;
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
             const int r = idx >> 4, ch = idx & 15;
             __builtin_amdgcn_raw_buffer_store_b128(
                 __builtin_bit_cast(v4u_t, *reinterpret_cast<const uint4 *>(&lds_q[r * QG_TILE + ch * 16])), rr,
-                (uint32_t)(r * ld_q + ch * 16), 0, 0);
+                (uint32_t)(r * ld_q + ch * 16), 0, STREAM);
         }
         // scales: blocks 2t + h of the row go to byte t of word h
         if (tid < QG_TILE && tid < valid) {

@@ -46,7 +46,7 @@ __device__ __forceinline__ void quantize_rowwise_units(const uint16_t *__restric
                 xo[i] = row * ld_x + cu * 8;
             }
             if (u < units)
-                v[i] = *reinterpret_cast<const uint4 *>(x + xo[i]);
+                v[i] = ld_stream(x + xo[i]);
             else
                 v[i] = make_uint4(0, 0, 0, 0);
         }
@@ -82,7 +82,7 @@ __device__ __forceinline__ void quantize_rowwise_units(const uint16_t *__restric
                     so = row * ld_s + (cu >> 2);
                 }
             }
-            *reinterpret_cast<uint2 *>(q + qo) = out;
+            st_stream(q + qo, out);
             if ((threadIdx.x & 3) == 0)
                 s[so] = (uint8_t)c;
         }
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(QC_THREADS) void quantize_colwise_kernel(
     uint4 v[16];
 #pragma unroll
     for (int i = 0; i < 16; i++)
-        v[i] = *reinterpret_cast<const uint4 *>(src + i * ld_x);
+        v[i] = ld_stream(src + i * ld_x);
     // packed maxima of columns (0,1), (2,3), (4,5), (6,7)
     uint32_t m[4] = {0, 0, 0, 0};
 #pragma unroll
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(QC_THREADS) void quantize_colwise_kernel(
             const uint32_t p23 = __builtin_amdgcn_perm(wd, wc, sel);  // rows 4k+2, 4k+3
             o[k] = nan_block_select(cvt_x4(p01, p23, sc), c);
         }
-        *reinterpret_cast<uint4 *>(qt + (c0 + j) * ld_qt + r0) = make_uint4(o[0], o[1], o[2], o[3]);
+        st_stream(qt + (c0 + j) * ld_qt + r0, make_uint4(o[0], o[1], o[2], o[3]));
         if (half == 0) {
             const int64_t col = c0 + j, b = r0 >> 5;  // scale row and 32-element block
             if (SWZ)
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(QD_THREADS) void quantize_dual_kernel(DualBatch B)
     uint4 v[16];
 #pragma unroll
     for (int i = 0; i < 16; i++)
-        v[i] = *reinterpret_cast<const uint4 *>(src + i * ld_x);
+        v[i] = ld_stream(src + i * ld_x);
     // column-wise maxima (per column, the lane's 16 rows) and row-wise ones
     // (per row, the lane's 8 columns) in one pass, each magnitude used by
     // both as soon as it is formed (two passes keep all 64 magnitudes live)
@@ -378,7 +378,7 @@ __global__ __launch_bounds__(QD_THREADS) void quantize_dual_kernel(DualBatch B)
                 o[k] = nan_block_select(cvt_x4(p01, p23, sc), c);
             }
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u_t, make_uint4(o[0], o[1], o[2], o[3])), rq,
-                                                   qoff, (int)(j * ld_qt), 0);
+                                                   qoff, (int)(j * ld_qt), STREAM);
             if (half == 0) {
                 // rearranged row = column wc*64 + cg*8 + j of the tile, block wr*4 + rb
                 const int col = wc * 64 + cg * 8 + j, blk = wr * 4 + rb;
@@ -417,7 +417,7 @@ __global__ __launch_bounds__(QD_THREADS) void quantize_dual_kernel(DualBatch B)
             if (C0 + ch * 16 < cols)
                 __builtin_amdgcn_raw_buffer_store_b128(
                     __builtin_bit_cast(v4u_t, *reinterpret_cast<const uint4 *>(&lds_q[r * QD_TILE + ch * 16])), rr,
-                    (uint32_t)(r * ld_q + ch * 16), 0, 0);
+                    (uint32_t)(r * ld_q + ch * 16), 0, STREAM);
         }
     }
     // thread -> word tid & 63 of rearranged tile tid >> 6 (its 32-row tile
