@@ -884,6 +884,10 @@ mx_status mx_grouped_gemm(int64_t num_groups, int64_t M_total, int64_t N, int64_
         return fail(MX_ERR_INVALID_ARG, "%s: null group_offsets", fn);
     if (!aligned(group_offsets, 8))
         return fail(MX_ERR_ALIGN, "%s: group_offsets must be 8-byte aligned", fn);
+    // tile numbers are formed in 32 bits: the experts' row tiles (at most one
+    // partial tile each) times the column tiles
+    if (((M_total + 255) / 256 + num_groups) * ((N + 255) / 256) >= ((int64_t)1 << 31))
+        return fail(MX_ERR_UNSUPPORTED, "%s: more than 2^31 - 1 output tiles", fn);
     const int64_t ce = c_dtype == MX_BF16 ? 2 : 4;
     const int64_t ec = extent(M_total, N, ld_c, ce);
     const int64_t eb = num_groups * N * K;

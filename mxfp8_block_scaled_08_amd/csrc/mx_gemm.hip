@@ -348,8 +348,8 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
     auto coords = [&](int64_t pid) -> Tile {
         Tile c;
         if (KGROUPED) {
-            const int64_t per_expert = opaque(p.tiles_m * p.tiles_n);
-            const int64_t r = pid / per_expert;
+            const uint32_t per_expert = (uint32_t)opaque(p.tiles_m * p.tiles_n);
+            const int64_t r = (uint32_t)pid / per_expert;  // (32-bit: tile numbers are below 2^31)
             const int g = __builtin_amdgcn_readfirstlane(s_pref[r]);
             int64_t mt, nt;
             band_walk(pid - r * per_expert, p.tiles_m, p.tiles_n, mt, nt);
@@ -370,10 +370,11 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
             c.g = 0;
             return c;
         }
-        const int64_t tn = opaque(p.tiles_n);
-        const int64_t mt64 = pid / tn;
-        c.n0 = (int)((pid - mt64 * tn) * BN);
-        const int mt = (int)mt64;  // below 2^31 (so are the tile counts)
+        // (32-bit: tile numbers and counts are below 2^31)
+        const uint32_t tn = (uint32_t)opaque(p.tiles_n), pid32 = (uint32_t)pid;
+        const uint32_t mt32 = pid32 / tn;
+        c.n0 = (int)((pid32 - mt32 * tn) * BN);
+        const int mt = (int)mt32;
         // first expert whose tiles end beyond mt, searching forward from the
         // last one found (a workgroup's tiles come in increasing order); pid <
         // ntiles guarantees a hit, and the loop is bounded either way
@@ -824,7 +825,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void mx_gemm_kernel(GemmParams p)
                     for (int v = 0; v < 16; v++)
                         acc[i][j][v] = 0.0f;
                 }
-        } else         if ((CT == 0 ? p.vec16 : p.vec_store) && cur.n0 + BN <= N) {
+        } else if ((CT == 0 ? p.vec16 : p.vec_store) && cur.n0 + BN <= N) {
             // whole-width tile: buffer stores relative to the tile's first
             // element; the range ends after the tile's last valid row, so the
             // stores of rows past it (past M, or past the expert) are dropped

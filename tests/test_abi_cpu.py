@@ -242,6 +242,9 @@ def test_grouped_gemm_validation():
     # C on top of the offsets array
     assert f(*base[:10], FAKE4 + (1 << 22) - 64, *base[11:]) == mx.MX_ERR_OVERLAP
     assert f(*base[:1], 0, *base[2:]) == mx.MX_OK
+    # tile numbers are 32-bit: 2^28 rows x 2^21 columns is 2^33 tiles
+    assert f(4, 1 << 28, 1 << 21, 256, *base[4:11], 1 << 21, *base[12:]) == mx.MX_ERR_UNSUPPORTED
+    assert "2^31" in _err(L)
 
 
 def test_python_binding_fails_loudly_without_device_tensors():
