@@ -60,7 +60,52 @@ def parse():
     ap.add_argument("--hbm-probe", action="store_true",
                     help="only time plain device copies and reads of 1 GiB (what this GPU's HBM "
                          "delivers to simple streaming kernels) and exit")
+    ap.add_argument("--library-compare", type=int, default=0, metavar="CALLS",
+                    help="only run the 12288x4096x24576 product (the dense data gradient) CALLS "
+                         "times back to back with this library's MX GEMM and with torch's "
+                         "hipBLASLt FP8 GEMM (per-tensor scales, no block scales), twice each, "
+                         "print per-call times and exit (context for the matrix-core counters)")
     return ap.parse_args()
+
+
+def library_compare(torch, mx, calls):
+    """Back-to-back sequences of one dense product, this library's MX GEMM and
+    hipBLASLt's per-tensor-scaled FP8 GEMM (torch._scaled_mm) on the same E4M3
+    codes, alternating ours, hipBLASLt, ours, hipBLASLt; per sequence the
+    per-call times (HIP events) and the median of its second half, after the
+    clock has settled."""
+    M, N, K = 12288, 4096, 24576
+    g = torch.Generator(device="cuda").manual_seed(0)
+
+    def operand(rows, std):
+        x = (torch.randn(rows, K, device="cuda", generator=g) * std).to(torch.bfloat16)
+        q, s = mx.mx_quantize_rowwise(x)
+        return q, mx.mx_scale_swizzle(s)
+
+    a, sa = operand(M, 1.0)
+    b, sb = operand(N, 0.02)
+    c = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(1, mx.mx_gemm_workspace_bytes(M, N, K)), dtype=torch.uint8, device="cuda")
+    a8, b8 = a.view(torch.float8_e4m3fn), b.view(torch.float8_e4m3fn)
+    one = torch.ones((), device="cuda")
+    fns = {"mx_gemm (MX block scales)": lambda: mx.mx_gemm(a, sa, b, sb, c=c, workspace=ws),
+           "hipBLASLt torch._scaled_mm (per-tensor scales)":
+               lambda: torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)}
+    out = []
+    for name in list(fns) * 2:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(calls + 1)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(calls):
+            fns[name]()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        t = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(calls)]
+        half = sorted(t[calls // 2:])
+        med = half[len(half) // 2]
+        out.append({"kernel": name, "us": [round(x, 1) for x in t], "median_second_half_us": round(med, 1),
+                    "frac_of_5PF": round(2 * M * N * K / (med * 1e-6) / 5e15, 3)})
+    return {"product": f"{M}x{N}x{K}", "sequences": out}
 
 
 def hbm_probe(torch):
@@ -577,6 +622,12 @@ def main():
     if args.hbm_probe:
         torch.cuda.set_device(0)
         print(json.dumps({"hbm_probe_1GiB": hbm_probe(torch)}))
+        return
+    if args.library_compare:
+        import mxfp8_block_scaled_08_amd as mx
+        mx.load()
+        torch.cuda.set_device(0)
+        print(json.dumps({"library_compare": library_compare(torch, mx, args.library_compare)}))
         return
 
     import mxfp8_block_scaled_08_amd as mx
