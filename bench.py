@@ -370,12 +370,17 @@ def work_per_step(I):
              + 2 * 4608 * 4096 * 12288 + 2 * 12288 * 4096 * 24576 + 2 * 24576 * 4096 * 12288)
     grouped = 2 * (2 * M * 1536 * 2048 + 2 * M * 2048 * 768)   # forward + data gradient
     wgrad = 2 * M * 1536 * 2048 + 2 * M * 2048 * 768
-    disp_el = M * 2048           # routed rows gathered and quantized
+    disp_el = M * 2048           # routed rows quantized and written
+    # dispatch traffic: each token row read once, every routed row written
+    # (codes + scales), the routing ids read and the slot / source-token
+    # indices written
+    disp_bytes = (I["x_tok"].numel() * 2 + disp_el * (1 + 1 / 32)
+                  + I["ids"].numel() * 4 * 3)
     swiglu_el = M * 768          # SwiGLU outputs, quantized
     comb_el = I["x_tok"].numel()  # combined outputs
     return dict(row_el=row_el, col_el=col_el, dual_el=dual_el, colg_el=colg_el, dualg_el=dualg_el,
                 dense=dense,
-                grouped=grouped, wgrad=wgrad, disp_el=disp_el, swiglu_el=swiglu_el,
+                grouped=grouped, wgrad=wgrad, disp_el=disp_el, disp_bytes=disp_bytes, swiglu_el=swiglu_el,
                 comb_el=comb_el, topk=I["ids"].shape[1])
 
 
@@ -693,7 +698,7 @@ def main():
         "scale_swizzle": {"launches": T.counts.get("swizzle", 0) // K},
         "moe_dispatch": {
             "ms": T.totals["moe_dispatch"] / K,
-            "GB/s": w["disp_el"] * QUANT_BYTES_PER_ELEMENT / (T.totals["moe_dispatch"] / K) / 1e6},
+            "GB/s": w["disp_bytes"] / (T.totals["moe_dispatch"] / K) / 1e6},
         "swiglu_quantize": {
             "ms": T.totals["swiglu"] / K,
             "GB/s": w["swiglu_el"] * (4 + 2 + QUANT_BYTES_PER_ELEMENT - 2) / (T.totals["swiglu"] / K) / 1e6},

@@ -16,11 +16,15 @@
 // LDS.  The scan runs as one workgroup per expert over its chunks, then one
 // over the experts' totals.  Expert ids outside [0, experts) are not routed (slot -1).
 //
-// Gather + quantize.  Row i of the permuted operand is the quantized row of
-// token src_token[i]: the row-wise kernel's lane layout (8 BF16 per lane,
+// Quantize + scatter.  Row i of the permuted operand is the quantized row of
+// token src_token[i].  All routed copies of a token are the same bytes, so the
+// kernel goes token by token: it reads each token row once (non-temporal) and
+// quantizes it once, with the row-wise kernel's lane layout (8 BF16 per lane,
 // four lanes per 32-element block, DPP quad maximum, CDNA4's scaled
-// conversion) with the source row looked up per unit, and each block's scale
-// byte stored at its place in the GEMM's rearranged layout.
+// conversion).  It then stores the codes and each block's scale byte, at its
+// place in the GEMM's rearranged layout, to every row the token's
+// assignments were placed at.  The operand's reads fall from one token row
+// per routed copy (8 per token) to one per token.
 #include "mx_device.h"
 #include "mx_launch.h"
 
@@ -150,27 +154,23 @@ __global__ __launch_bounds__(MOE_CHUNK) void moe_place_kernel(const int32_t *__r
 
 constexpr int MOE_Q_THREADS = 256;
 
-// Unit u = 8 consecutive elements of permuted row u / upr; rows at or past
-// offsets[experts] (the routed count) are not written.
-__global__ __launch_bounds__(MOE_Q_THREADS) void moe_gather_quantize_kernel(
-    const uint16_t *__restrict__ x, int64_t ld_x, const int32_t *__restrict__ src_token,
-    const int64_t *__restrict__ routed_end, uint8_t *__restrict__ q, int64_t ld_q,
-    uint8_t *__restrict__ s_swz, int64_t units, uint32_t upr, int64_t kt)
+// Unit u = 8 consecutive elements of token row u / upr.  The row is read
+// and quantized once; its codes and scale bytes go to every row of the
+// permuted operand the token is routed to (slot[t * topk + j], j < topk;
+// -1 for an assignment that is not routed).  Those rows are exactly
+// [0, offsets[experts]); the rest are not written.
+__global__ __launch_bounds__(MOE_Q_THREADS) void moe_scatter_quantize_kernel(
+    const uint16_t *__restrict__ x, int64_t ld_x, const int32_t *__restrict__ slot, int topk,
+    uint8_t *__restrict__ q, int64_t ld_q, uint8_t *__restrict__ s_swz, int64_t units, uint32_t upr,
+    int64_t kt)
 {
-    const int64_t routed = *routed_end;
     for (int64_t u = (int64_t)blockIdx.x * MOE_Q_THREADS + threadIdx.x; u - (threadIdx.x & 3) < units;
          u += (int64_t)gridDim.x * MOE_Q_THREADS) {
         // upr is a multiple of 32, so a quad shares its row
-        const int64_t row = u / upr;
-        const int64_t cu = u - row * upr;
-        const bool live = u < units && row < routed;
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (live) {
-            const int64_t t = src_token[row];
-            // a plain load: each token's row is read once per routed copy,
-            // and the copies after the first can hit in L2 or the Infinity Cache
-            w = *reinterpret_cast<const uint4 *>(x + t * ld_x + cu * 8);
-        }
+        const int64_t t = u / upr;
+        const int64_t cu = u - t * upr;
+        const bool live = u < units;
+        const uint4 w = live ? ld_stream(x + t * ld_x + cu * 8) : make_uint4(0, 0, 0, 0);
         uint32_t m = pk_max_u16(pk_max_u16(mag2(w.x), mag2(w.y)), pk_max_u16(mag2(w.z), mag2(w.w)));
         m = max(m & 0xFFFFu, m >> 16);
         m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
@@ -182,11 +182,15 @@ __global__ __launch_bounds__(MOE_Q_THREADS) void moe_gather_quantize_kernel(
         uint2 out;
         out.x = nan_block_select(cvt_x4(w.x, w.y, sc), c);
         out.y = nan_block_select(cvt_x4(w.z, w.w, sc), c);
-        st_stream(q + row * ld_q + cu * 8, out);
-        if ((threadIdx.x & 3) == 0) {
-            const int64_t b = cu >> 2;  // 32-element block of the row
-            s_swz[((row >> 5) * kt + (b >> 3)) * 256 + (32 * (b & 1) + (row & 31)) * 4 + ((b & 7) >> 1)] =
-                (uint8_t)c;
+        const int64_t b = cu >> 2;  // 32-element block of the row
+        const int64_t s_in = ((b >> 3) * 256) + 32 * (b & 1) * 4 + ((b & 7) >> 1);
+        for (int j = 0; j < topk; j++) {
+            const int64_t row = slot[t * topk + j];
+            if (row < 0)
+                continue;
+            st_stream(q + row * ld_q + cu * 8, out);
+            if ((threadIdx.x & 3) == 0)
+                s_swz[(row >> 5) * kt * 256 + s_in + (row & 31) * 4] = (uint8_t)c;
         }
     }
 }
@@ -239,11 +243,11 @@ hipError_t launch_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, in
     hipLaunchKernelGGL(moe_place_kernel, dim3((unsigned)chunks), dim3(MOE_CHUNK), 0, stream, topk_ids, n,
                        (int)topk, (int)experts, counts, (const int64_t *)offsets, src_token, slot);
     const uint32_t upr = (uint32_t)(hidden / 8);
-    const int64_t units = n * upr;
+    const int64_t units = tokens * upr;
     const int64_t per_pass = (int64_t)MOE_Q_THREADS;
     const int64_t blocks = std::min<int64_t>((units + per_pass - 1) / per_pass, 65536);
-    hipLaunchKernelGGL(moe_gather_quantize_kernel, dim3((unsigned)blocks), dim3(MOE_Q_THREADS), 0, stream,
-                       (const uint16_t *)x, ld_x, src_token, offsets + experts, (uint8_t *)q, ld_q,
+    hipLaunchKernelGGL(moe_scatter_quantize_kernel, dim3((unsigned)blocks), dim3(MOE_Q_THREADS), 0, stream,
+                       (const uint16_t *)x, ld_x, (const int32_t *)slot, (int)topk, (uint8_t *)q, ld_q,
                        (uint8_t *)s_swz, units, upr, (hidden / 32 + 7) / 8);
     return hipGetLastError();
 }
