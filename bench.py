@@ -266,7 +266,6 @@ def build_workload(mx, torch, mxsynth):
     o["xswz"] = torch.empty(swz(M, 2048 // 32), **u8)
     o["msrc"] = torch.empty(n_assign, dtype=torch.int32, device=dev)
     o["mslot"] = torch.empty(n_assign, dtype=torch.int32, device=dev)
-    o["h"] = torch.empty(M, 768, **bf)
     o["hq"] = torch.empty(M, 768, **u8)
     o["hswz"] = torch.empty(swz(M, 768 // 32), **u8)
     o["moe_out"] = torch.empty(ids.shape[0], 2048, **bf)
@@ -330,14 +329,18 @@ def step(mx, I, o, T):
       offsets=o["moff"], src=o["msrc"], slot=o["mslot"], q=o["xq"], s_swz=o["xswz"], workspace=o["ws"])
     T("grouped_gemm", mx.mx_grouped_gemm, o["moff"], o["xq"], o["xswz"], o["mgu_wq"],
       o["mgu_wswz"], c=o["C_mgu"])
-    T("swiglu", mx.mx_swiglu_quantize, o["C_mgu"], q=o["hq"], s_swz=o["hswz"], h=o["h"])
+    # h = SwiGLU(gate, up) quantized row-wise (the down projection's A) and per
+    # expert column-wise (its weight gradient's operand) from one read; h
+    # itself is never written
+    T("swiglu", mx.mx_swiglu_quantize_dual_grouped, o["C_mgu"], o["moff"], k_cap=I["k_cap"], q=o["hq"],
+      s_swz=o["hswz"], qt=o["mdn_xT"], st_swz=o["mdn_xTswz"], pad_offsets=o["mdn_pad2"])
     T("grouped_gemm", mx.mx_grouped_gemm, o["moff"], o["hq"], o["hswz"], o["mdn_wq"],
       o["mdn_wswz"], c=o["C_mdn"])
     T("moe_combine", mx.mx_moe_combine, o["C_mdn"], o["mslot"], I["rw"], out=o["moe_out"])
     # 5. MoE expert backward: data gradient grouped over rows, weight gradient
     #    grouped over each expert's token range
     k_cap = I["k_cap"]
-    for name, a, dyp in (("mgu", I["a_gu"], I["dy_gu"]), ("mdn", o["h"], I["dy_dn"])):
+    for name, a, dyp in (("mgu", I["a_gu"], I["dy_gu"]), ("mdn", None, I["dy_dn"])):
         # dY row-wise (data gradient) and per expert column-wise (weight
         # gradient) from one read
         T("quant_dual_grouped", mx.mx_quantize_dual_grouped, dyp, I["off"], k_cap=k_cap,
@@ -345,8 +348,9 @@ def step(mx, I, o, T):
           pad_offsets=o[name + "_pad"])
         T("grouped_gemm", mx.mx_grouped_gemm, I["off"], o[name + "_dyq"], o[name + "_dyswz"],
           o[name + "_wqt"], o[name + "_wstswz"], c=o["dX_" + name])
-        T("quant_col_grouped", mx.mx_quantize_colwise_grouped, a, I["off"], k_cap=k_cap,
-          qt=o[name + "_xT"], st_swz=o[name + "_xTswz"], pad_offsets=o[name + "_pad2"])
+        if a is not None:  # (down's operand came from the SwiGLU pass)
+            T("quant_col_grouped", mx.mx_quantize_colwise_grouped, a, I["off"], k_cap=k_cap,
+              qt=o[name + "_xT"], st_swz=o[name + "_xTswz"], pad_offsets=o[name + "_pad2"])
         T("grouped_wgrad", mx.mx_grouped_gemm_wgrad, o[name + "_pad"], o[name + "_dyT"],
           o[name + "_dyTswz"], o[name + "_xT"], o[name + "_xTswz"], c=o["dW_" + name], workspace=o["ws"])
 
@@ -363,6 +367,7 @@ def work_per_step(I):
     col_el = dual_el + I["x"].numel()                            # + wgrad activation operand
     # per-expert column-wise operands of the MoE weight gradients
     colg_el = I["a_gu"].numel() + I["a_dn"].numel()
+    colg_gu_el = I["a_gu"].numel()   # down's (the SwiGLU output) is quantized in the SwiGLU pass
     # MoE output gradients: row-wise and per-expert column-wise from one read
     dualg_el = I["dy_gu"].numel() + I["dy_dn"].numel()
     M = I["M"]
@@ -378,7 +383,8 @@ def work_per_step(I):
                   + I["ids"].numel() * 4 * 3)
     swiglu_el = M * 768          # SwiGLU outputs, quantized
     comb_el = I["x_tok"].numel()  # combined outputs
-    return dict(row_el=row_el, col_el=col_el, dual_el=dual_el, colg_el=colg_el, dualg_el=dualg_el,
+    return dict(row_el=row_el, col_el=col_el, dual_el=dual_el, colg_el=colg_el, colg_gu_el=colg_gu_el,
+                dualg_el=dualg_el,
                 dense=dense,
                 grouped=grouped, wgrad=wgrad, disp_el=disp_el, disp_bytes=disp_bytes, swiglu_el=swiglu_el,
                 comb_el=comb_el, topk=I["ids"].shape[1])
@@ -680,7 +686,7 @@ def main():
     flops = dense + grouped + wgrad
     K = args.steps
     row_only, col_only = row_el - dual_el, col_el - dual_el
-    q_bytes = ((row_only + col_only + colg_el) * QUANT_BYTES_PER_ELEMENT
+    q_bytes = ((row_only + col_only + w["colg_gu_el"]) * QUANT_BYTES_PER_ELEMENT
                + (dual_el + dualg_el) * DUAL_BYTES_PER_ELEMENT)
     qt = (T.totals.get("quant_row", 0) + T.totals.get("quant_col", 0)
           + T.totals.get("quant_dual", 0) + T.totals.get("quant_col_grouped", 0)
@@ -701,7 +707,8 @@ def main():
             "GB/s": w["disp_bytes"] / (T.totals["moe_dispatch"] / K) / 1e6},
         "swiglu_quantize": {
             "ms": T.totals["swiglu"] / K,
-            "GB/s": w["swiglu_el"] * (4 + 2 + QUANT_BYTES_PER_ELEMENT - 2) / (T.totals["swiglu"] / K) / 1e6},
+            # gate and up read (4 B), h quantized in both orientations
+            "GB/s": w["swiglu_el"] * (4 + 2 * (QUANT_BYTES_PER_ELEMENT - 2)) / (T.totals["swiglu"] / K) / 1e6},
         "moe_combine": {
             "ms": T.totals["moe_combine"] / K,
             "GB/s": w["comb_el"] * (2 * w["topk"] + 2) / (T.totals["moe_combine"] / K) / 1e6},
@@ -710,7 +717,7 @@ def main():
             "GB/s": dualg_el * DUAL_BYTES_PER_ELEMENT / (T.totals["quant_dual_grouped"] / K) / 1e6},
         "quantize_colwise_grouped": {
             "ms": T.totals["quant_col_grouped"] / K,
-            "GB/s": colg_el * QUANT_BYTES_PER_ELEMENT / (T.totals["quant_col_grouped"] / K) / 1e6},
+            "GB/s": w["colg_gu_el"] * QUANT_BYTES_PER_ELEMENT / (T.totals["quant_col_grouped"] / K) / 1e6},
         "dense_gemm": {"ms": gemm_ms, "TFLOP/s": dense / gemm_ms / 1e9},
         "grouped_gemm": {"ms": ggemm_ms, "TFLOP/s": grouped / ggemm_ms / 1e9},
         "grouped_wgrad": {"ms": wg_ms, "TFLOP/s": wgrad / wg_ms / 1e9},

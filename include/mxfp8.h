@@ -95,7 +95,7 @@
 extern "C" {
 #endif
 
-#define MXFP8_ABI_VERSION 8
+#define MXFP8_ABI_VERSION 9
 
 typedef enum mx_status {
     MX_OK = 0,
@@ -580,6 +580,32 @@ mx_status mx_quantize_dual_grouped(const void *x, int64_t rows_total, int64_t co
                                    const int64_t *group_offsets, int64_t num_groups, int64_t *pad_offsets,
                                    void *q, int64_t ld_q, void *s_swz, void *qt, int64_t ld_qt, int64_t k_cap,
                                    void *st_swz, void *stream);
+
+/*
+ * The MoE layer's activation between its expert projections, quantized for
+ * both of its uses from one read (paper Table 2: Qwen3-30B-A3B; Figure 1:
+ * MXFP8 GEMMs in the forward and backward passes).  h = SwiGLU of the
+ * gate/up output, exactly as mx_swiglu_quantize forms it, is quantized:
+ *   - row-wise: the down projection's A operand;
+ *   - per expert column-wise: the down projection's weight-gradient operand,
+ *     as mx_quantize_colwise_grouped lays it out.
+ * h itself is never written.  So mx_swiglu_quantize followed by
+ * mx_quantize_dual_grouped of its h gives the same bytes, without h's
+ * round trip through memory.
+ *   gu     BF16 [rows_total][ld_gu]: gate in columns [0, F), up in [F, 2F)
+ * group_offsets, num_groups, pad_offsets, qt, ld_qt, k_cap and st_swz are as
+ * for mx_quantize_colwise_grouped, with cols = F.  q, ld_q and s_swz are as
+ * for mx_quantize_dual_grouped: q holds rows_total rows of F codes.  As
+ * there, only the rows of the experts are written to q and s_swz.
+ * Requirements: F % 32 == 0 (else MX_ERR_SHAPE) and F % 256 == 0 (else
+ * MX_ERR_UNSUPPORTED); ld_gu >= 2F, ld_q >= F, ld_qt >= k_cap (else
+ * MX_ERR_INVALID_ARG); the rest as mx_quantize_dual_grouped, with gu in
+ * place of x.
+ */
+mx_status mx_swiglu_quantize_dual_grouped(const void *gu, int64_t rows_total, int64_t F, int64_t ld_gu,
+                                          const int64_t *group_offsets, int64_t num_groups, int64_t *pad_offsets,
+                                          void *q, int64_t ld_q, void *s_swz, void *qt, int64_t ld_qt,
+                                          int64_t k_cap, void *st_swz, void *stream);
 
 /*
  * MoE weight gradient, product side (paper Table 8, update_actor; Table 2):

@@ -27,7 +27,7 @@ __all__ = [
     "mx_moe_dispatch", "mx_moe_combine", "mx_grouped_k_capacity", "mx_quantize_colwise_grouped",
     "mx_grouped_gemm_wgrad", "mx_swiglu_quantize", "mx_quantize_rowwise_swz",
     "mx_quantize_rowwise_swz_batch", "mx_quantize_colwise_swz",
-    "mx_quantize_dual_grouped", "mx_gemm_workspace_bytes", "mx_moe_dispatch_workspace_bytes",
+    "mx_quantize_dual_grouped", "mx_swiglu_quantize_dual_grouped", "mx_gemm_workspace_bytes", "mx_moe_dispatch_workspace_bytes",
     "mx_grouped_gemm_wgrad_workspace_bytes", "mx_moe_dispatch_noalloc", "MX_OK", "MX_ERR_INVALID_ARG", "MX_ERR_SHAPE", "MX_ERR_ALIGN",
     "MX_ERR_OVERLAP", "MX_ERR_UNSUPPORTED", "MX_ERR_HIP", "MX_BF16", "MX_F32",
 ]
@@ -106,6 +106,9 @@ def load() -> ctypes.CDLL:
     L.mx_quantize_dual_grouped.restype = ctypes.c_int
     L.mx_quantize_dual_grouped.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
                                            _i64, _vp, _vp]
+    L.mx_swiglu_quantize_dual_grouped.restype = ctypes.c_int
+    L.mx_swiglu_quantize_dual_grouped.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp,
+                                                  _i64, _i64, _vp, _vp]
     L.mx_quantize_rowwise_swz.restype = ctypes.c_int
     L.mx_quantize_rowwise_swz.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp]
     L.mx_quantize_colwise_swz.restype = ctypes.c_int
@@ -682,4 +685,42 @@ def mx_quantize_dual_grouped(x: torch.Tensor, group_offsets: torch.Tensor, k_cap
                                          _dev(qt, "qt", torch.uint8), _ld(qt, "qt"), k_cap,
                                          _dev(st_swz, "st_swz", torch.uint8), _stream(stream))
     _check("mx_quantize_dual_grouped", st)
+    return q, s_swz, qt, st_swz, pad_offsets
+
+
+def mx_swiglu_quantize_dual_grouped(gu: torch.Tensor, group_offsets: torch.Tensor, k_cap: Optional[int] = None,
+                                    q: Optional[torch.Tensor] = None, s_swz: Optional[torch.Tensor] = None,
+                                    qt: Optional[torch.Tensor] = None, st_swz: Optional[torch.Tensor] = None,
+                                    pad_offsets: Optional[torch.Tensor] = None, stream=None):
+    """gu [rows][2F] BF16 (gate, then up), rows sorted by expert -> (q [rows][F],
+    s_swz, qt [F][k_cap], st_swz, pad_offsets): h = SwiGLU(gate, up) quantized
+    row-wise and per expert column-wise from one read, h never written (see
+    mx_swiglu_quantize_dual_grouped in the header)."""
+    rows, two_f = gu.shape
+    F = two_f // 2
+    G = group_offsets.numel() - 1
+    if group_offsets.dtype != torch.int64 or G < 1:
+        raise ValueError("group_offsets must be int64 with G+1 entries, G >= 1")
+    if k_cap is None:
+        k_cap = mx_grouped_k_capacity(rows, G)
+    dev = gu.device
+    if q is None:
+        q = torch.empty((rows, F), dtype=torch.uint8, device=dev)
+    if s_swz is None:
+        s_swz = torch.empty(max(mx_scale_swizzled_bytes(rows, F // 32), 1), dtype=torch.uint8, device=dev)
+    if qt is None:
+        qt = torch.empty((F, k_cap), dtype=torch.uint8, device=dev)
+    if st_swz is None:
+        st_swz = torch.empty(mx_scale_swizzled_bytes(F, k_cap // 32), dtype=torch.uint8, device=dev)
+    if pad_offsets is None:
+        pad_offsets = torch.empty(G + 1, dtype=torch.int64, device=dev)
+    q, s_swz, qt, st_swz = _u8(q), _u8(s_swz), _u8(qt), _u8(st_swz)
+    st = load().mx_swiglu_quantize_dual_grouped(_dev(gu, "gu", torch.bfloat16), rows, F, _ld(gu, "gu"),
+                                                _dev(group_offsets, "group_offsets", torch.int64), G,
+                                                _dev(pad_offsets, "pad_offsets", torch.int64),
+                                                _dev(q, "q", torch.uint8), _ld(q, "q"),
+                                                _dev(s_swz, "s_swz", torch.uint8),
+                                                _dev(qt, "qt", torch.uint8), _ld(qt, "qt"), k_cap,
+                                                _dev(st_swz, "st_swz", torch.uint8), _stream(stream))
+    _check("mx_swiglu_quantize_dual_grouped", st)
     return q, s_swz, qt, st_swz, pad_offsets

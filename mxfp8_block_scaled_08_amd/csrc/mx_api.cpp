@@ -702,6 +702,66 @@ mx_status mx_quantize_dual_grouped(const void *x, int64_t rows_total, int64_t co
                       fn);
 }
 
+mx_status mx_swiglu_quantize_dual_grouped(const void *gu, int64_t rows_total, int64_t F, int64_t ld_gu,
+                                          const int64_t *group_offsets, int64_t num_groups, int64_t *pad_offsets,
+                                          void *q, int64_t ld_q, void *s_swz, void *qt, int64_t ld_qt,
+                                          int64_t k_cap, void *st_swz, void *stream)
+{
+    const char *fn = "mx_swiglu_quantize_dual_grouped";
+    if (rows_total < 0 || F < 1 || num_groups < 1)
+        return fail(MX_ERR_INVALID_ARG, "%s: need rows_total >= 0, F >= 1, num_groups >= 1", fn);
+    if (num_groups > mx::MOE_MAX_EXPERTS)
+        return fail(MX_ERR_UNSUPPORTED, "%s: num_groups=%lld > %d", fn, (long long)num_groups,
+                    mx::MOE_MAX_EXPERTS);
+    if (F % 32 != 0)
+        return fail(MX_ERR_SHAPE, "%s: F=%lld is not a multiple of 32", fn, (long long)F);
+    if (F % 256 != 0)
+        return fail(MX_ERR_UNSUPPORTED, "%s: F=%lld: this build needs F %% 256 == 0", fn, (long long)F);
+    if (k_cap % 256 != 0 || k_cap < mx_grouped_k_capacity(rows_total, num_groups))
+        return fail(MX_ERR_INVALID_ARG,
+                    "%s: k_cap=%lld must be a multiple of 256 and at least "
+                    "mx_grouped_k_capacity(rows_total, num_groups) = %lld",
+                    fn, (long long)k_cap, (long long)mx_grouped_k_capacity(rows_total, num_groups));
+    if (ld_gu < 2 * F || ld_qt < k_cap || ld_q < F)
+        return fail(MX_ERR_INVALID_ARG, "%s: leading dimension too small (ld_gu=%lld ld_q=%lld ld_qt=%lld)", fn,
+                    (long long)ld_gu, (long long)ld_q, (long long)ld_qt);
+    if ((!gu && rows_total > 0) || (!q && rows_total > 0) || (!s_swz && rows_total > 0) || !group_offsets ||
+        !pad_offsets || !qt || !st_swz)
+        return fail(MX_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!aligned(gu, 16) || ld_gu % 8 != 0 || !aligned(qt, 16) || ld_qt % 16 != 0 || !aligned(st_swz, 4) ||
+        !aligned(q, 16) || ld_q % 16 != 0 || !aligned(s_swz, 4) || !aligned(group_offsets, 8) ||
+        !aligned(pad_offsets, 8))
+        return fail(MX_ERR_ALIGN,
+                    "%s: gu, q and qt need 16-byte aligned rows (ld_gu %% 8, ld_q %% 16, ld_qt %% 16), "
+                    "s_swz and st_swz 4 bytes, the offsets 8 bytes",
+                    fn);
+    if (k_cap / 256 * (F / 256) >= ((int64_t)1 << 31) || ld_gu >= ((int64_t)1 << 22) ||
+        ld_qt >= ((int64_t)1 << 24) || ld_q >= ((int64_t)1 << 24))
+        return fail(MX_ERR_UNSUPPORTED,
+                    "%s: operand too large for this build (ld_gu < 2^22, ld_q and ld_qt < 2^24)", fn);
+    const void *bufs[7] = {gu, group_offsets, pad_offsets, qt, st_swz, q, s_swz};
+    const int64_t lens[7] = {rows_total > 0 ? extent(rows_total, 2 * F, ld_gu, 2) : 0, (num_groups + 1) * 8,
+                             (num_groups + 1) * 8, extent(F, k_cap, ld_qt, 1), swz_bytes(F, k_cap / 32),
+                             extent(rows_total, F, ld_q, 1), swz_bytes(rows_total, F / 32)};
+    for (int i = 0; i < 7; i++)
+        for (int k = i + 1; k < 7; k++)
+            if ((i >= 2 || k >= 2) && overlap(bufs[i], lens[i], bufs[k], lens[k]))
+                return fail(MX_ERR_OVERLAP, "%s: buffers %d and %d overlap", fn, i, k);
+    if (debug_checks()) {
+        // the row-wise output covers the rows of the experts only: under
+        // MX_DEBUG the offsets must also start at 0 and end at rows_total
+        const mx_status dst =
+            debug_offsets(fn, "group_offsets", group_offsets, num_groups, rows_total, 1, 0, true, true, stream);
+        if (dst != MX_OK)
+            return dst;
+    }
+    return hip_status(mx::launch_quantize_colwise_grouped(gu, rows_total, F, ld_gu, group_offsets, num_groups,
+                                                          pad_offsets, qt, ld_qt, k_cap, st_swz,
+                                                          (hipStream_t)stream, rows_total > 0 ? q : nullptr,
+                                                          ld_q, s_swz, rows_total > 0),
+                      fn);
+}
+
 mx_status mx_swiglu_quantize(const void *gu, int64_t rows, int64_t F, int64_t ld_gu, void *h, int64_t ld_h,
                              void *q, int64_t ld_q, void *s_swz, void *stream)
 {

@@ -112,6 +112,26 @@ __device__ __forceinline__ void st_stream(void *p, uint2 v)
 // dropped.  Callers pass values that every lane holds alike; reading them
 // from the first lane says so to the compiler, which would otherwise wrap
 // each access in a loop over the distinct values it cannot rule out.
+// SwiGLU of two packed BF16 pairs (gate g, up u; element 0 in the low half):
+// h = g * sigmoid(g) * u in FP32, the sigmoid taken from exp(-|g|) (no
+// overflow for any g; the library exp, subnormal results kept), rounded to
+// BF16 by the hardware's nearest-even conversion.  One definition for every
+// kernel that forms h, so they agree bit for bit.
+__device__ __forceinline__ uint32_t swiglu_bf16x2(uint32_t gs, uint32_t us)
+{
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    float hv[2];
+#pragma unroll
+    for (int e = 0; e < 2; e++) {
+        const float g = __builtin_bit_cast(float, e ? (gs & 0xFFFF0000u) : (gs << 16));
+        const float v = __builtin_bit_cast(float, e ? (us & 0xFFFF0000u) : (us << 16));
+        const float t = expf(-fabsf(g));
+        const float sig = (g >= 0.0f ? 1.0f : t) / (1.0f + t);
+        hv[e] = g * sig * v;
+    }
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t{hv[0], hv[1]}), bf16x2_t));
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void *base, uint32_t bytes)
 {
     const uint64_t b = (uint64_t)(uintptr_t)base;

@@ -123,12 +123,13 @@ hipError_t launch_moe_combine(const void *y, int64_t tokens, int64_t hidden, int
 // k_cap % 256 == 0 and at least the capacity for rows and G.
 // With q non-null, also the row-wise quantization of the same rows (q at
 // [rows][ld_q], scales rearranged with cols/256 tiles per 32-row tile row);
-// cols % 256 == 0 then.
+// cols % 256 == 0 then.  With swiglu (q non-null), x is a gate/up output
+// [rows][ld_x] with ld_x >= 2 cols and the rows quantized are its SwiGLU.
 hipError_t launch_quantize_colwise_grouped(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
                                           const int64_t *offsets, int64_t G, int64_t *pad,
                                           void *qt, int64_t ld_qt, int64_t k_cap, void *st_swz,
                                           hipStream_t stream, void *q = nullptr, int64_t ld_q = 0,
-                                          void *s_swz = nullptr);
+                                          void *s_swz = nullptr, bool swiglu = false);
 
 // Per-expert product along K: C_g = A[:, r_g] . B[:, r_g]^T for the column
 // ranges r_g = [k_offsets[g], k_offsets[g+1]), C_g at c + g * M * ld_c.

@@ -348,7 +348,6 @@ __global__ __launch_bounds__(256) void swiglu_quantize_kernel(
     uint8_t *__restrict__ q, int64_t ld_q, uint8_t *__restrict__ s_swz, int64_t units, uint32_t upr,
     int64_t kt)
 {
-    typedef float f2_t __attribute__((ext_vector_type(2)));
     for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u - (threadIdx.x & 3) < units;
          u += (int64_t)gridDim.x * 256) {
         // upr is a multiple of 4, so a quad shares its row
@@ -360,21 +359,8 @@ __global__ __launch_bounds__(256) void swiglu_quantize_kernel(
             gw = ld_stream(gu + row * ld_gu + cu * 8);
             uw = ld_stream(gu + row * ld_gu + F + cu * 8);
         }
-        const uint32_t gs[4] = {gw.x, gw.y, gw.z, gw.w}, us[4] = {uw.x, uw.y, uw.z, uw.w};
-        uint32_t hw[4];
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            float hv[2];
-#pragma unroll
-            for (int e = 0; e < 2; e++) {
-                const float g = __builtin_bit_cast(float, e ? (gs[k] & 0xFFFF0000u) : (gs[k] << 16));
-                const float v = __builtin_bit_cast(float, e ? (us[k] & 0xFFFF0000u) : (us[k] << 16));
-                const float t = expf(-fabsf(g));  // the library exp: subnormal results kept
-                const float sig = (g >= 0.0f ? 1.0f : t) / (1.0f + t);
-                hv[e] = g * sig * v;
-            }
-            hw[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t{hv[0], hv[1]}), bf16x2_t));
-        }
+        const uint32_t hw[4] = {swiglu_bf16x2(gw.x, uw.x), swiglu_bf16x2(gw.y, uw.y), swiglu_bf16x2(gw.z, uw.z),
+                                swiglu_bf16x2(gw.w, uw.w)};
         if (live && h != nullptr)
             st_stream(h + row * ld_h + cu * 8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
         uint32_t m = pk_max_u16(pk_max_u16(mag2(hw[0]), mag2(hw[1])), pk_max_u16(mag2(hw[2]), mag2(hw[3])));

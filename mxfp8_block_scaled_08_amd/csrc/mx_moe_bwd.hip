@@ -79,7 +79,13 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void pad_offsets_kernel(const int6
 // row's eight scale bytes as the two 4-byte words they form in the
 // rearranged layout (rows of an expert start anywhere, so a row's scales do
 // not fill whole tiles).
-template <bool ROW>
+// SWIGLU: x is the gate/up projection output [rows][ld_x] (gate in columns
+// [0, cols), up in [cols, 2 cols)) and the tile quantizes h = SwiGLU(gate,
+// up) (swiglu_bf16x2, the same h as mx_swiglu_quantize's), formed in
+// registers from one load of each half: the MoE down projection's row-wise A
+// operand and its weight gradient's per-expert column-wise operand, with h
+// itself never written.
+template <bool ROW, bool SWIGLU>
 __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     const int64_t *__restrict__ offsets, const int64_t *__restrict__ pad, int G,
@@ -125,9 +131,22 @@ __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
     const uint32_t voff = active ? (uint32_t)(rl0 * ld_x + c0) * 2u : 0x80000000u;
     const uint32_t vstep = active ? (uint32_t)ld_x * 2u : 0u;
     uint4 v[16];
+    if (SWIGLU) {
+        // the up half: cols * 2 bytes further along the row (an inactive
+        // lane's offset stays past the range)
+        const uint32_t uoff = (uint32_t)(cols * 2);
 #pragma unroll
-    for (int i = 0; i < 16; i++)
-        v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff + i * vstep, 0, STREAM));
+        for (int i = 0; i < 16; i++) {
+            const uint4 g = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff + i * vstep, 0, STREAM));
+            const uint4 u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff + i * vstep + uoff, 0, STREAM));
+            v[i] = make_uint4(swiglu_bf16x2(g.x, u.x), swiglu_bf16x2(g.y, u.y), swiglu_bf16x2(g.z, u.z),
+                              swiglu_bf16x2(g.w, u.w));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+            v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff + i * vstep, 0, STREAM));
+    }
     // column-wise maxima (per column, the lane's 16 rows) and, with ROW, the
     // row-wise ones (per row, the lane's 8 columns) in one pass, each
     // magnitude used by both as soon as it is formed
@@ -247,7 +266,7 @@ __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
 hipError_t launch_quantize_colwise_grouped(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
                                           const int64_t *offsets, int64_t G, int64_t *pad,
                                           void *qt, int64_t ld_qt, int64_t k_cap, void *st_swz,
-                                          hipStream_t stream, void *q, int64_t ld_q, void *s_swz)
+                                          hipStream_t stream, void *q, int64_t ld_q, void *s_swz, bool swiglu)
 {
     hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, stream, offsets, (int)G,
                        rows, k_cap, pad);
@@ -259,13 +278,18 @@ hipError_t launch_quantize_colwise_grouped(const void *x, int64_t rows, int64_t 
     const int64_t blocks = tiles_r * tiles_c;
     if (blocks == 0)
         return hipSuccess;
-    if (q != nullptr)
-        hipLaunchKernelGGL((quantize_colwise_grouped_kernel<true>), dim3((unsigned)blocks), dim3(QG_THREADS), 0,
+    if (swiglu)
+        hipLaunchKernelGGL((quantize_colwise_grouped_kernel<true, true>), dim3((unsigned)blocks), dim3(QG_THREADS), 0,
+                           stream, (const uint16_t *)x, rows, cols, ld_x, offsets, (const int64_t *)pad, (int)G,
+                           (uint8_t *)qt, ld_qt, (uint8_t *)st_swz, k_cap / QG_TILE, tiles_c, (uint8_t *)q, ld_q,
+                           (uint8_t *)s_swz, cols / 256);
+    else if (q != nullptr)
+        hipLaunchKernelGGL((quantize_colwise_grouped_kernel<true, false>), dim3((unsigned)blocks), dim3(QG_THREADS), 0,
                            stream, (const uint16_t *)x, rows, cols, ld_x, offsets, (const int64_t *)pad, (int)G,
                            (uint8_t *)qt, ld_qt, (uint8_t *)st_swz, k_cap / QG_TILE, tiles_c, (uint8_t *)q, ld_q,
                            (uint8_t *)s_swz, cols / 256);
     else
-        hipLaunchKernelGGL((quantize_colwise_grouped_kernel<false>), dim3((unsigned)blocks), dim3(QG_THREADS), 0,
+        hipLaunchKernelGGL((quantize_colwise_grouped_kernel<false, false>), dim3((unsigned)blocks), dim3(QG_THREADS), 0,
                            stream, (const uint16_t *)x, rows, cols, ld_x, offsets, (const int64_t *)pad, (int)G,
                            (uint8_t *)qt, ld_qt, (uint8_t *)st_swz, k_cap / QG_TILE, tiles_c, nullptr,
                            (int64_t)0, nullptr, (int64_t)0);

@@ -61,7 +61,7 @@ hipError_t launch_moe_combine(const void *, int64_t, int64_t, int64_t, const int
                               void *, int64_t, hipStream_t) { return hit(); }
 hipError_t launch_quantize_colwise_grouped(const void *, int64_t, int64_t, int64_t, const int64_t *, int64_t,
                                           int64_t *, void *, int64_t, int64_t, void *, hipStream_t, void *,
-                                          int64_t, void *) { return hit(); }
+                                          int64_t, void *, bool) { return hit(); }
 hipError_t launch_grouped_gemm_wgrad(int64_t, int64_t, int64_t, int64_t, const int64_t *, const void *, int64_t,
                                      const void *, const void *, int64_t, const void *, void *, int64_t, int,
                                      void *ws, hipStream_t) { return hit(ws); }

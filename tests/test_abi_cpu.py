@@ -38,7 +38,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for n in names:
         assert hasattr(raw, n), f"{n} declared in include/mxfp8.h but not exported"
         assert hasattr(mx, n), f"{n} has no Python binding of the same name"
-    assert L.mx_abi_version() == 8
+    assert L.mx_abi_version() == 9
 
 
 def test_status_strings():
@@ -493,6 +493,40 @@ def test_quantize_dual_grouped_validation():
     assert call(k_cap=cap - 256, ld_qt=cap) == mx.MX_ERR_INVALID_ARG
     assert call(ld_q=1 << 24) == mx.MX_ERR_UNSUPPORTED
     assert call(ld_x=1 << 22) == mx.MX_ERR_UNSUPPORTED
+
+
+def test_swiglu_quantize_dual_grouped_validation():
+    """The fused SwiGLU + row-wise + per-expert column-wise quantization checks
+    its arguments like mx_quantize_dual_grouped, with the gate/up input twice
+    as wide as the quantized h, before any launch."""
+    L = mx.load()
+    f = L.mx_swiglu_quantize_dual_grouped
+    cap = L.mx_grouped_k_capacity(1000, 4)
+    # gu, rows, F, ld_gu, offsets, G, pad, q, ld_q, s_swz, qt, ld_qt, k_cap, st_swz
+    base = dict(gu=FAKE, rows=1000, F=256, ld_gu=512, off=FAKE2, G=4, pad=FAKE2 + 4096, q=FAKE3,
+                ld_q=256, s=FAKE3 + (1 << 24), qt=FAKE4, ld_qt=cap, k_cap=cap, st=FAKE4 + (1 << 24))
+    order = ["gu", "rows", "F", "ld_gu", "off", "G", "pad", "q", "ld_q", "s", "qt", "ld_qt", "k_cap", "st"]
+    call = lambda **kw: f(*[kw.get(k, base[k]) for k in order], STREAM)
+    assert call(ld_gu=256) == mx.MX_ERR_INVALID_ARG         # the up half does not fit
+    assert call(F=288, ld_gu=576, ld_q=288) == mx.MX_ERR_UNSUPPORTED
+    assert call(F=48, ld_gu=96, ld_q=48) == mx.MX_ERR_SHAPE
+    assert call(F=0) == mx.MX_ERR_INVALID_ARG
+    assert call(rows=-1) == mx.MX_ERR_INVALID_ARG
+    assert call(G=0) == mx.MX_ERR_INVALID_ARG
+    assert call(G=1025) == mx.MX_ERR_UNSUPPORTED
+    assert call(ld_q=128) == mx.MX_ERR_INVALID_ARG
+    assert call(q=0) == mx.MX_ERR_INVALID_ARG
+    assert call(gu=0) == mx.MX_ERR_INVALID_ARG
+    assert call(gu=FAKE + 8) == mx.MX_ERR_ALIGN
+    assert call(ld_gu=516) == mx.MX_ERR_ALIGN
+    assert call(q=FAKE3 + 8) == mx.MX_ERR_ALIGN
+    assert call(s=FAKE3 + (1 << 24) + 2) == mx.MX_ERR_ALIGN
+    assert call(s=FAKE3 + 1000) == mx.MX_ERR_OVERLAP        # row-wise scales inside the codes
+    assert call(q=FAKE + 4096) == mx.MX_ERR_OVERLAP         # codes inside the input
+    assert call(k_cap=cap - 256, ld_qt=cap) == mx.MX_ERR_INVALID_ARG
+    assert call(ld_q=1 << 24) == mx.MX_ERR_UNSUPPORTED
+    assert call(ld_gu=1 << 22) == mx.MX_ERR_UNSUPPORTED
+    assert "ld_gu" in mx.mx_last_error()
 
 
 def test_moe_dispatch_noalloc_validation():

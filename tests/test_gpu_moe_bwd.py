@@ -282,6 +282,55 @@ def test_dual_grouped_matches_oracle(gpu_lib, sizes, cols):
                           oracle.scale_swizzle(ost).reshape(-1, KT, 256)[:, :pend // 256])
 
 
+@pytest.mark.parametrize("sizes,F", [([37], 256), ([0, 37, 256, 300, 5], 512), ([513, 0, 255, 1, 31], 768),
+                                     ([0, 0], 256)])
+def test_swiglu_dual_grouped_matches_composition_and_oracle(gpu_lib, sizes, F):
+    """h = SwiGLU(gate, up) quantized row-wise and per expert column-wise from
+    one read of the gate/up output, h never written.  The result is byte-equal
+    to mx_swiglu_quantize (its h and row-wise output) followed by
+    mx_quantize_dual_grouped of that h.  Each output also equals the oracle's
+    quantization of that h; h itself is pinned against the oracle's SwiGLU in
+    tests/test_gpu_swiglu.py.  Gate values far out on both sides, zeros and
+    negative zeros are planted."""
+    mx = gpu_lib
+    off = _offsets(sizes)
+    rows = int(off[-1])
+    gu = mxsynth.normal_bf16((rows, 2 * F), 1.0, seed=900 + rows + F, outlier_frac=0.01, outlier_mul=100.0)
+    gb = mxsynth.bits(gu).copy()
+    if rows:
+        rng = np.random.default_rng(rows + F)
+        for v in (0xC2C8, 0x4248, 0x0000, 0x8000, 0xC1A0, 0x42B2, 0xC2B2):   # -100, 50, 0, -0, -20, 89, -89
+            gb[rng.integers(0, rows, 8), rng.integers(0, F, 8)] = v
+    gu_d = mxsynth.from_bits(gb).cuda() if rows else torch.empty((0, 2 * F), dtype=torch.bfloat16, device="cuda")
+    off_d = torch.from_numpy(off).cuda()
+    q, s_swz, qt, st_swz, pad = mx.mx_swiglu_quantize_dual_grouped(gu_d, off_d)
+    h = torch.empty((rows, F), dtype=torch.bfloat16, device="cuda")
+    if rows:
+        q1, s1, h = mx.mx_swiglu_quantize(gu_d, want_h=True)
+    cq, cs, cqt, cst, cpad = mx.mx_quantize_dual_grouped(h, off_d)
+    torch.cuda.synchronize()
+    k_cap = qt.shape[1]
+    assert k_cap == cqt.shape[1]
+    assert torch.equal(pad, cpad)
+    pend = int(pad[-1])
+    KT = k_cap // 256
+    assert torch.equal(qt[:, :pend], cqt[:, :pend])
+    assert torch.equal(st_swz.view(-1, KT, 256)[:, :pend // 256], cst.view(-1, KT, 256)[:, :pend // 256])
+    hb = mxsynth.bits(h.cpu())
+    oqt, ost, opad = oracle.quantize_colwise_grouped(hb, off, k_cap)
+    assert np.array_equal(pad.cpu().numpy(), opad)
+    assert np.array_equal(qt.cpu().numpy()[:, :pend], oqt[:, :pend])
+    assert np.array_equal(st_swz.cpu().numpy().reshape(-1, KT, 256)[:, :pend // 256],
+                          oracle.scale_swizzle(ost).reshape(-1, KT, 256)[:, :pend // 256])
+    if rows:
+        assert torch.equal(q, cq) and torch.equal(q, q1)
+        us = oracle.scale_unswizzle(s_swz.cpu().numpy(), rows, F // 32)
+        assert np.array_equal(us, oracle.scale_unswizzle(s1.cpu().numpy(), rows, F // 32))
+        oq, os_ = oracle.quantize_rowwise(hb)
+        assert np.array_equal(q.cpu().numpy(), oq)
+        assert np.array_equal(us, os_)
+
+
 @pytest.mark.parametrize("row_wise", [False, True])
 def test_grouped_quantizers_strided_views(gpu_lib, row_wise):
     """x a column slice of a wider BF16 tensor (ld_x > cols), and the codes
