@@ -114,7 +114,8 @@ __device__ __forceinline__ void st_stream(void *p, uint2 v)
 // each access in a loop over the distinct values it cannot rule out.
 // SwiGLU of two packed BF16 pairs (gate g, up u; element 0 in the low half):
 // h = g * sigmoid(g) * u in FP32, the sigmoid taken from exp(-|g|) (no
-// overflow for any g; the library exp, subnormal results kept), rounded to
+// overflow for any g; the library exp, subnormal results kept) and the
+// hardware reciprocal of 1 + exp(-|g|) (in [1, 2]: within 1 ulp), rounded to
 // BF16 by the hardware's nearest-even conversion.  One definition for every
 // kernel that forms h, so they agree bit for bit.
 __device__ __forceinline__ uint32_t swiglu_bf16x2(uint32_t gs, uint32_t us)
@@ -126,7 +127,7 @@ __device__ __forceinline__ uint32_t swiglu_bf16x2(uint32_t gs, uint32_t us)
         const float g = __builtin_bit_cast(float, e ? (gs & 0xFFFF0000u) : (gs << 16));
         const float v = __builtin_bit_cast(float, e ? (us & 0xFFFF0000u) : (us << 16));
         const float t = expf(-fabsf(g));
-        const float sig = (g >= 0.0f ? 1.0f : t) / (1.0f + t);
+        const float sig = (g >= 0.0f ? 1.0f : t) * __builtin_amdgcn_rcpf(1.0f + t);
         hv[e] = g * sig * v;
     }
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t{hv[0], hv[1]}), bf16x2_t));
