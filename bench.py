@@ -325,8 +325,11 @@ def step(mx, I, o, T):
     for name, w in (("mgu", I["w_gu"]), ("mdn", I["w_dn"])):
         T("quant_dual", mx.mx_quantize_dual_experts, w, q=o[name + "_wq"], s_swz=o[name + "_wswz"],
           qt=o[name + "_wqt"], st_swz=o[name + "_wstswz"])
-    T("moe_dispatch", mx.mx_moe_dispatch, I["x_tok"], I["ids"], I["w_gu"].shape[0],
-      offsets=o["moff"], src=o["msrc"], slot=o["mslot"], q=o["xq"], s_swz=o["xswz"], workspace=o["ws"])
+    # the dispatched rows quantized row-wise (gate_up's A) and per expert
+    # column-wise (gate_up's weight-gradient operand) from one gather
+    T("moe_dispatch", mx.mx_moe_dispatch_dual_grouped, I["x_tok"], I["ids"], I["w_gu"].shape[0],
+      k_cap=I["k_cap"], offsets=o["moff"], src=o["msrc"], slot=o["mslot"], q=o["xq"], s_swz=o["xswz"],
+      pad_offsets=o["mgu_pad2"], qt=o["mgu_xT"], st_swz=o["mgu_xTswz"], workspace=o["ws"])
     T("grouped_gemm", mx.mx_grouped_gemm, o["moff"], o["xq"], o["xswz"], o["mgu_wq"],
       o["mgu_wswz"], c=o["C_mgu"])
     # h = SwiGLU(gate, up) quantized row-wise (the down projection's A) and per
@@ -340,7 +343,7 @@ def step(mx, I, o, T):
     # 5. MoE expert backward: data gradient grouped over rows, weight gradient
     #    grouped over each expert's token range
     k_cap = I["k_cap"]
-    for name, a, dyp in (("mgu", I["a_gu"], I["dy_gu"]), ("mdn", None, I["dy_dn"])):
+    for name, dyp in (("mgu", I["dy_gu"]), ("mdn", I["dy_dn"])):
         # dY row-wise (data gradient) and per expert column-wise (weight
         # gradient) from one read
         T("quant_dual_grouped", mx.mx_quantize_dual_grouped, dyp, I["off"], k_cap=k_cap,
@@ -348,9 +351,8 @@ def step(mx, I, o, T):
           pad_offsets=o[name + "_pad"])
         T("grouped_gemm", mx.mx_grouped_gemm, I["off"], o[name + "_dyq"], o[name + "_dyswz"],
           o[name + "_wqt"], o[name + "_wstswz"], c=o["dX_" + name])
-        if a is not None:  # (down's operand came from the SwiGLU pass)
-            T("quant_col_grouped", mx.mx_quantize_colwise_grouped, a, I["off"], k_cap=k_cap,
-              qt=o[name + "_xT"], st_swz=o[name + "_xTswz"], pad_offsets=o[name + "_pad2"])
+        # the weight gradient's other operand (X for gate_up, h for down) was
+        # quantized per expert column-wise in the forward (dispatch, SwiGLU)
         T("grouped_wgrad", mx.mx_grouped_gemm_wgrad, o[name + "_pad"], o[name + "_dyT"],
           o[name + "_dyTswz"], o[name + "_xT"], o[name + "_xTswz"], c=o["dW_" + name], workspace=o["ws"])
 
@@ -367,7 +369,7 @@ def work_per_step(I):
     col_el = dual_el + I["x"].numel()                            # + wgrad activation operand
     # per-expert column-wise operands of the MoE weight gradients
     colg_el = I["a_gu"].numel() + I["a_dn"].numel()
-    colg_gu_el = I["a_gu"].numel()   # down's (the SwiGLU output) is quantized in the SwiGLU pass
+    colg_gu_el = 0   # both per-expert column-wise operands are quantized in the forward passes
     # MoE output gradients: row-wise and per-expert column-wise from one read
     dualg_el = I["dy_gu"].numel() + I["dy_dn"].numel()
     M = I["M"]
@@ -376,10 +378,12 @@ def work_per_step(I):
     grouped = 2 * (2 * M * 1536 * 2048 + 2 * M * 2048 * 768)   # forward + data gradient
     wgrad = 2 * M * 1536 * 2048 + 2 * M * 2048 * 768
     disp_el = M * 2048           # routed rows quantized and written
-    # dispatch traffic: each token row read once, every routed row written
-    # (codes + scales), the routing ids read and the slot / source-token
-    # indices written
+    # dispatch traffic: each token row read once (the gathers of its other
+    # routed copies hit in cache), every routed row written row-wise and the
+    # per-expert column-wise operand written (codes + scales), the routing ids
+    # read and the slot / source-token indices written
     disp_bytes = (I["x_tok"].numel() * 2 + disp_el * (1 + 1 / 32)
+                  + 2048 * I["k_cap"] * (1 + 1 / 32)   # the per-expert column-wise operand
                   + I["ids"].numel() * 4 * 3)
     swiglu_el = M * 768          # SwiGLU outputs, quantized
     comb_el = I["x_tok"].numel()  # combined outputs
@@ -715,9 +719,6 @@ def main():
         "quantize_dual_grouped": {
             "ms": T.totals["quant_dual_grouped"] / K,
             "GB/s": dualg_el * DUAL_BYTES_PER_ELEMENT / (T.totals["quant_dual_grouped"] / K) / 1e6},
-        "quantize_colwise_grouped": {
-            "ms": T.totals["quant_col_grouped"] / K,
-            "GB/s": w["colg_gu_el"] * QUANT_BYTES_PER_ELEMENT / (T.totals["quant_col_grouped"] / K) / 1e6},
         "dense_gemm": {"ms": gemm_ms, "TFLOP/s": dense / gemm_ms / 1e9},
         "grouped_gemm": {"ms": ggemm_ms, "TFLOP/s": grouped / ggemm_ms / 1e9},
         "grouped_wgrad": {"ms": wg_ms, "TFLOP/s": wgrad / wg_ms / 1e9},

@@ -370,6 +370,36 @@ mx_status mx_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t
                           void *s_swz, void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * mx_moe_dispatch that also writes the dispatched rows quantized per expert
+ * column-wise: the gate_up projection's weight-gradient operand, laid out as
+ * mx_quantize_colwise_grouped lays out a [tokens*topk][hidden] operand with
+ * group_offsets = the dispatch's offsets (paper Table 2: Qwen3-30B-A3B, 128
+ * experts; Figure 1: the forward's BF16 activations quantized for the MXFP8
+ * GEMMs of both passes).  Each permuted row is read from its token's row of
+ * x once and quantized both ways, so the permuted BF16 rows never exist in
+ * memory.  Arguments and results as mx_moe_dispatch, plus
+ *   pad_offsets  DEVICE int64 [num_experts + 1] out, as
+ *                mx_quantize_colwise_grouped's (the weight gradient's
+ *                k_offsets)
+ *   qt, ld_qt, k_cap, st_swz  as mx_quantize_colwise_grouped's, with cols =
+ *                hidden and rows_total = tokens*topk (k_cap at least
+ *                mx_grouped_k_capacity(tokens*topk, num_experts))
+ * q and s_swz hold the same bytes as mx_moe_dispatch's.  Requirements: those
+ * of mx_moe_dispatch, plus k_cap % 256 == 0, k_cap at least that capacity and
+ * ld_qt >= k_cap (else MX_ERR_INVALID_ARG); qt 16-byte aligned rows (ld_qt %
+ * 16), st_swz and s_swz 4-byte and pad_offsets 8-byte aligned (else
+ * MX_ERR_ALIGN); x below 2^31 bytes, ld_x < 2^22, ld_q and ld_qt < 2^24 (else
+ * MX_ERR_UNSUPPORTED); no output overlapping an input, another output or the
+ * workspace (else MX_ERR_OVERLAP).  Workspace as mx_moe_dispatch.
+ */
+mx_status mx_moe_dispatch_dual_grouped(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
+                                      const int32_t *topk_ids, int64_t topk, int64_t num_experts,
+                                      int64_t *offsets, int32_t *src_token, int32_t *slot, void *q,
+                                      int64_t ld_q, void *s_swz, int64_t *pad_offsets, void *qt, int64_t ld_qt,
+                                      int64_t k_cap, void *st_swz, void *workspace, int64_t workspace_bytes,
+                                      void *stream);
+
+/*
  * mx_moe_dispatch for callers that cannot allocate any memory, not even a
  * workspace (code under HIP graph capture that may not touch an allocator,
  * tight serving loops, harnesses that forbid allocation): the same

@@ -24,7 +24,7 @@ __all__ = [
     "MxError", "load", "lib_path", "mx_abi_version", "mx_status_string", "mx_last_error", "mx_quantize_rowwise",
     "mx_quantize_colwise", "mx_scale_swizzled_bytes", "mx_scale_swizzle", "mx_gemm",
     "mx_grouped_gemm", "mx_quantize_dual", "mx_quantize_dual_batch", "mx_quantize_dual_experts",
-    "mx_moe_dispatch", "mx_moe_combine", "mx_grouped_k_capacity", "mx_quantize_colwise_grouped",
+    "mx_moe_dispatch", "mx_moe_dispatch_dual_grouped", "mx_moe_combine", "mx_grouped_k_capacity", "mx_quantize_colwise_grouped",
     "mx_grouped_gemm_wgrad", "mx_swiglu_quantize", "mx_quantize_rowwise_swz",
     "mx_quantize_rowwise_swz_batch", "mx_quantize_colwise_swz",
     "mx_quantize_dual_grouped", "mx_swiglu_quantize_dual_grouped", "mx_gemm_workspace_bytes", "mx_moe_dispatch_workspace_bytes",
@@ -93,6 +93,9 @@ def load() -> ctypes.CDLL:
     L.mx_moe_dispatch_workspace_bytes.restype = _i64
     L.mx_moe_dispatch_workspace_bytes.argtypes = [_i64, _i64, _i64]
     L.mx_moe_dispatch.restype = ctypes.c_int
+    L.mx_moe_dispatch_dual_grouped.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64,
+                                               _vp, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp]
+    L.mx_moe_dispatch_dual_grouped.restype = ctypes.c_int
     L.mx_moe_combine.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp]
     L.mx_moe_combine.restype = ctypes.c_int
     L.mx_gemm.restype = ctypes.c_int
@@ -355,6 +358,54 @@ def mx_moe_dispatch(x: torch.Tensor, topk_ids: torch.Tensor, num_experts: int,
                                 _dev(q, "q"), _ld(q, "q"), _dev(s_swz, "s_swz"), wp, wb, _stream(stream))
     _check("mx_moe_dispatch", st)
     return offsets, src, slot, q, s_swz
+
+
+def mx_moe_dispatch_dual_grouped(x: torch.Tensor, topk_ids: torch.Tensor, num_experts: int,
+                                 k_cap: Optional[int] = None, offsets: Optional[torch.Tensor] = None,
+                                 src: Optional[torch.Tensor] = None, slot: Optional[torch.Tensor] = None,
+                                 q: Optional[torch.Tensor] = None, s_swz: Optional[torch.Tensor] = None,
+                                 pad_offsets: Optional[torch.Tensor] = None, qt: Optional[torch.Tensor] = None,
+                                 st_swz: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                                 stream=None):
+    """mx_moe_dispatch that also quantizes the dispatched rows per expert
+    column-wise (the gate_up weight gradient's operand) from the same reads.
+    Returns (offsets, src_token, slot, q, s_swz, pad_offsets, qt [hidden][k_cap],
+    st_swz); outputs passed in are written in place."""
+    tokens, hidden = x.shape
+    if topk_ids.dim() != 2 or topk_ids.shape[0] != tokens or not topk_ids.is_contiguous():
+        raise ValueError("topk_ids must be a contiguous [tokens][topk] tensor")
+    topk = topk_ids.shape[1]
+    n = tokens * topk
+    dev = x.device
+    if k_cap is None:
+        k_cap = mx_grouped_k_capacity(n, num_experts)
+    if offsets is None:
+        offsets = torch.empty(num_experts + 1, dtype=torch.int64, device=dev)
+    if src is None:
+        src = torch.empty(n, dtype=torch.int32, device=dev)
+    if slot is None:
+        slot = torch.empty(n, dtype=torch.int32, device=dev)
+    if q is None:
+        q = torch.empty((n, hidden), dtype=torch.uint8, device=dev)
+    if s_swz is None:
+        s_swz = torch.empty(mx_scale_swizzled_bytes(n, hidden // 32), dtype=torch.uint8, device=dev)
+    if pad_offsets is None:
+        pad_offsets = torch.empty(num_experts + 1, dtype=torch.int64, device=dev)
+    if qt is None:
+        qt = torch.empty((hidden, k_cap), dtype=torch.uint8, device=dev)
+    if st_swz is None:
+        st_swz = torch.empty(mx_scale_swizzled_bytes(hidden, k_cap // 32), dtype=torch.uint8, device=dev)
+    if offsets.numel() != num_experts + 1 or src.numel() != n or slot.numel() != n:
+        raise ValueError("offsets, src and slot must have num_experts+1, n and n entries")
+    q, s_swz, qt, st_swz = _u8(q), _u8(s_swz), _u8(qt), _u8(st_swz)
+    wp, wb = _workspace(workspace, mx_moe_dispatch_workspace_bytes(tokens, topk, num_experts), dev)
+    st = load().mx_moe_dispatch_dual_grouped(
+        _dev(x, "x", torch.bfloat16), tokens, hidden, _ld(x, "x"), _dev(topk_ids, "topk_ids", torch.int32), topk,
+        num_experts, _dev(offsets, "offsets"), _dev(src, "src"), _dev(slot, "slot"), _dev(q, "q"), _ld(q, "q"),
+        _dev(s_swz, "s_swz"), _dev(pad_offsets, "pad_offsets", torch.int64), _dev(qt, "qt"), _ld(qt, "qt"), k_cap,
+        _dev(st_swz, "st_swz"), wp, wb, _stream(stream))
+    _check("mx_moe_dispatch_dual_grouped", st)
+    return offsets, src, slot, q, s_swz, pad_offsets, qt, st_swz
 
 
 def mx_moe_dispatch_noalloc(x: torch.Tensor, topk_ids: torch.Tensor, num_experts: int,

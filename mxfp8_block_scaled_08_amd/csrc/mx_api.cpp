@@ -545,6 +545,63 @@ mx_status mx_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t
                       fn);
 }
 
+mx_status mx_moe_dispatch_dual_grouped(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
+                                      const int32_t *topk_ids, int64_t topk, int64_t num_experts,
+                                      int64_t *offsets, int32_t *src_token, int32_t *slot, void *q,
+                                      int64_t ld_q, void *s_swz, int64_t *pad_offsets, void *qt, int64_t ld_qt,
+                                      int64_t k_cap, void *st_swz, void *workspace, int64_t workspace_bytes,
+                                      void *stream)
+{
+    const char *fn = "mx_moe_dispatch_dual_grouped";
+    const void *bufs[10];
+    int64_t lens[10];
+    mx_status st = check_dispatch(fn, x, tokens, hidden, ld_x, topk_ids, topk, num_experts, offsets, src_token,
+                                  slot, q, ld_q, s_swz, bufs, lens);
+    if (st != MX_OK)
+        return st;
+    const int64_t n = tokens * topk;
+    if (k_cap % 256 != 0 || k_cap < mx_grouped_k_capacity(n, num_experts))
+        return fail(MX_ERR_INVALID_ARG,
+                    "%s: k_cap=%lld must be a multiple of 256 and at least "
+                    "mx_grouped_k_capacity(tokens * topk, num_experts) = %lld",
+                    fn, (long long)k_cap, (long long)mx_grouped_k_capacity(n, num_experts));
+    if (ld_qt < k_cap)
+        return fail(MX_ERR_INVALID_ARG, "%s: ld_qt=%lld < k_cap=%lld", fn, (long long)ld_qt, (long long)k_cap);
+    if (!pad_offsets || !qt || !st_swz)
+        return fail(MX_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!aligned(qt, 16) || ld_qt % 16 != 0 || !aligned(st_swz, 4) || !aligned(pad_offsets, 8) ||
+        !aligned(s_swz, 4))
+        return fail(MX_ERR_ALIGN, "%s: qt needs 16-byte aligned rows (ld_qt %% 16), the scales 4 bytes, "
+                                  "pad_offsets 8 bytes", fn);
+    // the gathered rows' offsets into x, the row-wise codes' into q, the
+    // column-wise codes' into qt and the grouped tiles are formed in 32 bits
+    if (extent(tokens, hidden, ld_x, 2) >= ((int64_t)1 << 31) || ld_x >= ((int64_t)1 << 22) ||
+        ld_q >= ((int64_t)1 << 24) || ld_qt >= ((int64_t)1 << 24) ||
+        k_cap / 256 * (hidden / 256) >= ((int64_t)1 << 31))
+        return fail(MX_ERR_UNSUPPORTED,
+                    "%s: operand too large for this build (x below 2^31 bytes, ld_x < 2^22, ld_q and ld_qt < 2^24)",
+                    fn);
+    bufs[7] = pad_offsets;
+    lens[7] = (num_experts + 1) * 8;
+    bufs[8] = qt;
+    lens[8] = extent(hidden, k_cap, ld_qt, 1);
+    bufs[9] = st_swz;
+    lens[9] = swz_bytes(hidden, k_cap / 32);
+    for (int i = 7; i < 10; i++)
+        for (int k = 0; k < i; k++)
+            if (overlap(bufs[i], lens[i], bufs[k], lens[k]))
+                return fail(MX_ERR_OVERLAP, "%s: buffers %d and %d overlap", fn, i, k);
+    st = check_workspace(fn, workspace, workspace_bytes, mx::moe_dispatch_workspace_bytes(tokens, topk, num_experts),
+                         4, bufs, lens, 10);
+    if (st != MX_OK)
+        return st;
+    return hip_status(mx::launch_moe_dispatch_dual_grouped(x, tokens, hidden, ld_x, topk_ids, topk, num_experts,
+                                                           offsets, src_token, slot, q, ld_q, s_swz, pad_offsets,
+                                                           qt, ld_qt, k_cap, st_swz, workspace,
+                                                           (hipStream_t)stream),
+                      fn);
+}
+
 mx_status mx_moe_dispatch_noalloc(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
                                   const int32_t *topk_ids, int64_t topk, int64_t num_experts,
                                   int64_t *offsets, int32_t *src_token, int32_t *slot, void *q, int64_t ld_q,

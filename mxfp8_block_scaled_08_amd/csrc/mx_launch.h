@@ -106,6 +106,16 @@ hipError_t launch_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, in
                                const int32_t *topk_ids, int64_t topk, int64_t experts,
                                int64_t *offsets, int32_t *src_token, int32_t *slot, void *q,
                                int64_t ld_q, void *s_swz, void *ws, hipStream_t stream);
+// The dispatch's ordering as launch_moe_dispatch, then the permuted rows
+// (row p = token src_token[p] of x) quantized row-wise into q / s_swz and per
+// expert column-wise into qt / st_swz / pad (launch_quantize_colwise_grouped
+// over rows_total = tokens * topk with the dispatch's offsets); tokens * ld_x
+// * 2 < 2^31.
+hipError_t launch_moe_dispatch_dual_grouped(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
+                                            const int32_t *topk_ids, int64_t topk, int64_t experts,
+                                            int64_t *offsets, int32_t *src_token, int32_t *slot, void *q,
+                                            int64_t ld_q, void *s_swz, int64_t *pad, void *qt, int64_t ld_qt,
+                                            int64_t k_cap, void *st_swz, void *ws, hipStream_t stream);
 
 // The current device's copy of the dispatch's static scratch array
 // (MOE_NOALLOC_SCRATCH_BYTES), looked up once per device.
@@ -125,11 +135,14 @@ hipError_t launch_moe_combine(const void *y, int64_t tokens, int64_t hidden, int
 // [rows][ld_q], scales rearranged with cols/256 tiles per 32-row tile row);
 // cols % 256 == 0 then.  With swiglu (q non-null), x is a gate/up output
 // [rows][ld_x] with ld_x >= 2 cols and the rows quantized are its SwiGLU.
+// With src (q non-null), row p is row src[p] of x, whose x_bytes (< 2^31)
+// bytes hold the token rows.
 hipError_t launch_quantize_colwise_grouped(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
                                           const int64_t *offsets, int64_t G, int64_t *pad,
                                           void *qt, int64_t ld_qt, int64_t k_cap, void *st_swz,
                                           hipStream_t stream, void *q = nullptr, int64_t ld_q = 0,
-                                          void *s_swz = nullptr, bool swiglu = false);
+                                          void *s_swz = nullptr, bool swiglu = false,
+                                          const int32_t *src = nullptr, int64_t x_bytes = 0);
 
 // Per-expert product along K: C_g = A[:, r_g] . B[:, r_g]^T for the column
 // ranges r_g = [k_offsets[g], k_offsets[g+1]), C_g at c + g * M * ld_c.

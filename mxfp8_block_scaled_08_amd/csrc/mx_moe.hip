@@ -226,10 +226,11 @@ hipError_t moe_noalloc_scratch(void **ptr)
     return hipSuccess;
 }
 
-hipError_t launch_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
-                               const int32_t *topk_ids, int64_t topk, int64_t experts,
-                               int64_t *offsets, int32_t *src_token, int32_t *slot, void *q,
-                               int64_t ld_q, void *s_swz, void *ws, hipStream_t stream)
+// The dispatch's ordering: offsets, src_token and slot (four small kernels,
+// the chunk counts in ws).
+static void launch_dispatch_order(const int32_t *topk_ids, int64_t tokens, int64_t topk, int64_t experts,
+                                  int64_t *offsets, int32_t *src_token, int32_t *slot, void *ws,
+                                  hipStream_t stream)
 {
     const int64_t n = tokens * topk;
     const int64_t chunks = (n + MOE_CHUNK - 1) / MOE_CHUNK;
@@ -242,6 +243,14 @@ hipError_t launch_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, in
                        offsets);
     hipLaunchKernelGGL(moe_place_kernel, dim3((unsigned)chunks), dim3(MOE_CHUNK), 0, stream, topk_ids, n,
                        (int)topk, (int)experts, counts, (const int64_t *)offsets, src_token, slot);
+}
+
+hipError_t launch_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
+                               const int32_t *topk_ids, int64_t topk, int64_t experts,
+                               int64_t *offsets, int32_t *src_token, int32_t *slot, void *q,
+                               int64_t ld_q, void *s_swz, void *ws, hipStream_t stream)
+{
+    launch_dispatch_order(topk_ids, tokens, topk, experts, offsets, src_token, slot, ws, stream);
     const uint32_t upr = (uint32_t)(hidden / 8);
     const int64_t units = tokens * upr;
     const int64_t per_pass = (int64_t)MOE_Q_THREADS;
@@ -250,6 +259,21 @@ hipError_t launch_moe_dispatch(const void *x, int64_t tokens, int64_t hidden, in
                        (const uint16_t *)x, ld_x, (const int32_t *)slot, (int)topk, (uint8_t *)q, ld_q,
                        (uint8_t *)s_swz, units, upr, (hidden / 32 + 7) / 8);
     return hipGetLastError();
+}
+
+hipError_t launch_moe_dispatch_dual_grouped(const void *x, int64_t tokens, int64_t hidden, int64_t ld_x,
+                                            const int32_t *topk_ids, int64_t topk, int64_t experts,
+                                            int64_t *offsets, int32_t *src_token, int32_t *slot, void *q,
+                                            int64_t ld_q, void *s_swz, int64_t *pad, void *qt, int64_t ld_qt,
+                                            int64_t k_cap, void *st_swz, void *ws, hipStream_t stream)
+{
+    launch_dispatch_order(topk_ids, tokens, topk, experts, offsets, src_token, slot, ws, stream);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    return launch_quantize_colwise_grouped(x, tokens * topk, hidden, ld_x, offsets, experts, pad, qt, ld_qt,
+                                           k_cap, st_swz, stream, q, ld_q, s_swz, false, src_token,
+                                           tokens * ld_x * 2);
 }
 
 // Combine: thread -> 8 consecutive columns of one token; the token's slots in

@@ -79,22 +79,32 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void pad_offsets_kernel(const int6
 // row's eight scale bytes as the two 4-byte words they form in the
 // rearranged layout (rows of an expert start anywhere, so a row's scales do
 // not fill whole tiles).
-// SWIGLU: x is the gate/up projection output [rows][ld_x] (gate in columns
-// [0, cols), up in [cols, 2 cols)) and the tile quantizes h = SwiGLU(gate,
-// up) (swiglu_bf16x2, the same h as mx_swiglu_quantize's), formed in
-// registers from one load of each half: the MoE down projection's row-wise A
-// operand and its weight gradient's per-expert column-wise operand, with h
-// itself never written.
-template <bool ROW, bool SWIGLU>
+// LOAD selects where the tile's BF16 rows come from:
+//  - QG_PLAIN: rows [src0, src0 + valid) of x.
+//  - QG_SWIGLU: x is the gate/up projection output [rows][ld_x] (gate in
+//    columns [0, cols), up in [cols, 2 cols)) and the tile quantizes h =
+//    SwiGLU(gate, up) (swiglu_bf16x2, the same h as mx_swiglu_quantize's),
+//    formed in registers from one load of each half: the MoE down
+//    projection's row-wise A operand and its weight gradient's per-expert
+//    column-wise operand, with h itself never written.
+//  - QG_GATHER: row p of the operand is row src[p] of x (the token
+//    activations, x_bytes bytes in all): the MoE dispatch's permuted rows,
+//    quantized row-wise (the gate_up projection's A operand) and per expert
+//    column-wise (its weight gradient's operand) without the permuted BF16
+//    rows ever being written.
+constexpr int QG_PLAIN = 0, QG_SWIGLU = 1, QG_GATHER = 2;
+template <bool ROW, int LOAD>
 __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, int64_t ld_x,
     const int64_t *__restrict__ offsets, const int64_t *__restrict__ pad, int G,
     uint8_t *__restrict__ qt, int64_t ld_qt, uint8_t *__restrict__ st_swz, int64_t st_tiles,
-    int64_t tiles_c, uint8_t *__restrict__ q, int64_t ld_q, uint8_t *__restrict__ s_swz, int64_t s_tiles)
+    int64_t tiles_c, uint8_t *__restrict__ q, int64_t ld_q, uint8_t *__restrict__ s_swz, int64_t s_tiles,
+    const int32_t *__restrict__ src, uint32_t x_bytes)
 {
     __shared__ uint32_t lds_st[8 * 64];
     __shared__ __attribute__((aligned(16))) uint8_t lds_q[ROW ? QG_TILE * QG_TILE : 1];  // row-wise codes
     __shared__ uint8_t lds_rs[ROW ? QG_TILE * 8 : 1];  // row-wise scale bytes, 8 per row
+    __shared__ __attribute__((aligned(16))) int32_t lds_src[LOAD == QG_GATHER ? QG_TILE : 1];  // the tile's tokens
     const int64_t tr = blockIdx.x / tiles_c, tc = blockIdx.x - tr * tiles_c;
     const int64_t P0 = tr * QG_TILE;  // first padded column (row of the padded operand)
     // The expert whose range holds P0 is the last g with pad[g] <= P0; the
@@ -131,7 +141,23 @@ __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
     const uint32_t voff = active ? (uint32_t)(rl0 * ld_x + c0) * 2u : 0x80000000u;
     const uint32_t vstep = active ? (uint32_t)ld_x * 2u : 0u;
     uint4 v[16];
-    if (SWIGLU) {
+    if (LOAD == QG_GATHER) {
+        // each row from its token: the tile's 256 token numbers are loaded
+        // once (one coalesced load) into LDS; one range over all of x (below
+        // 2^31 bytes), rows past the tile's valid ones and inactive lanes at
+        // an offset past it (they read zero).  Plain loads: every token row
+        // is read by each of its routed copies' tiles.
+        if (tid < QG_TILE)
+            lds_src[tid] = tid < valid ? src[src0 + tid] : -1;
+        __syncthreads();
+        const __amdgpu_buffer_rsrc_t rg = byte_range(x, x_bytes);
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const int32_t t = lds_src[rl0 + i];
+            const uint32_t off = (active && t >= 0) ? (uint32_t)((int64_t)t * ld_x + c0) * 2u : 0xFFFFFFF0u;
+            v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0));
+        }
+    } else if (LOAD == QG_SWIGLU) {
         // the up half: cols * 2 bytes further along the row (an inactive
         // lane's offset stays past the range)
         const uint32_t uoff = (uint32_t)(cols * 2);
@@ -266,7 +292,8 @@ __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
 hipError_t launch_quantize_colwise_grouped(const void *x, int64_t rows, int64_t cols, int64_t ld_x,
                                           const int64_t *offsets, int64_t G, int64_t *pad,
                                           void *qt, int64_t ld_qt, int64_t k_cap, void *st_swz,
-                                          hipStream_t stream, void *q, int64_t ld_q, void *s_swz, bool swiglu)
+                                          hipStream_t stream, void *q, int64_t ld_q, void *s_swz, bool swiglu,
+                                          const int32_t *src, int64_t x_bytes)
 {
     hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(MOE_MAX_EXPERTS), 0, stream, offsets, (int)G,
                        rows, k_cap, pad);
@@ -278,21 +305,26 @@ hipError_t launch_quantize_colwise_grouped(const void *x, int64_t rows, int64_t 
     const int64_t blocks = tiles_r * tiles_c;
     if (blocks == 0)
         return hipSuccess;
-    if (swiglu)
-        hipLaunchKernelGGL((quantize_colwise_grouped_kernel<true, true>), dim3((unsigned)blocks), dim3(QG_THREADS), 0,
-                           stream, (const uint16_t *)x, rows, cols, ld_x, offsets, (const int64_t *)pad, (int)G,
-                           (uint8_t *)qt, ld_qt, (uint8_t *)st_swz, k_cap / QG_TILE, tiles_c, (uint8_t *)q, ld_q,
-                           (uint8_t *)s_swz, cols / 256);
+    if (src != nullptr)
+        hipLaunchKernelGGL((quantize_colwise_grouped_kernel<true, QG_GATHER>), dim3((unsigned)blocks),
+                           dim3(QG_THREADS), 0, stream, (const uint16_t *)x, rows, cols, ld_x, offsets,
+                           (const int64_t *)pad, (int)G, (uint8_t *)qt, ld_qt, (uint8_t *)st_swz, k_cap / QG_TILE,
+                           tiles_c, (uint8_t *)q, ld_q, (uint8_t *)s_swz, cols / 256, src, (uint32_t)x_bytes);
+    else if (swiglu)
+        hipLaunchKernelGGL((quantize_colwise_grouped_kernel<true, QG_SWIGLU>), dim3((unsigned)blocks),
+                           dim3(QG_THREADS), 0, stream, (const uint16_t *)x, rows, cols, ld_x, offsets,
+                           (const int64_t *)pad, (int)G, (uint8_t *)qt, ld_qt, (uint8_t *)st_swz, k_cap / QG_TILE,
+                           tiles_c, (uint8_t *)q, ld_q, (uint8_t *)s_swz, cols / 256, nullptr, 0u);
     else if (q != nullptr)
-        hipLaunchKernelGGL((quantize_colwise_grouped_kernel<true, false>), dim3((unsigned)blocks), dim3(QG_THREADS), 0,
-                           stream, (const uint16_t *)x, rows, cols, ld_x, offsets, (const int64_t *)pad, (int)G,
-                           (uint8_t *)qt, ld_qt, (uint8_t *)st_swz, k_cap / QG_TILE, tiles_c, (uint8_t *)q, ld_q,
-                           (uint8_t *)s_swz, cols / 256);
+        hipLaunchKernelGGL((quantize_colwise_grouped_kernel<true, QG_PLAIN>), dim3((unsigned)blocks),
+                           dim3(QG_THREADS), 0, stream, (const uint16_t *)x, rows, cols, ld_x, offsets,
+                           (const int64_t *)pad, (int)G, (uint8_t *)qt, ld_qt, (uint8_t *)st_swz, k_cap / QG_TILE,
+                           tiles_c, (uint8_t *)q, ld_q, (uint8_t *)s_swz, cols / 256, nullptr, 0u);
     else
-        hipLaunchKernelGGL((quantize_colwise_grouped_kernel<false, false>), dim3((unsigned)blocks), dim3(QG_THREADS), 0,
-                           stream, (const uint16_t *)x, rows, cols, ld_x, offsets, (const int64_t *)pad, (int)G,
-                           (uint8_t *)qt, ld_qt, (uint8_t *)st_swz, k_cap / QG_TILE, tiles_c, nullptr,
-                           (int64_t)0, nullptr, (int64_t)0);
+        hipLaunchKernelGGL((quantize_colwise_grouped_kernel<false, QG_PLAIN>), dim3((unsigned)blocks),
+                           dim3(QG_THREADS), 0, stream, (const uint16_t *)x, rows, cols, ld_x, offsets,
+                           (const int64_t *)pad, (int)G, (uint8_t *)qt, ld_qt, (uint8_t *)st_swz, k_cap / QG_TILE,
+                           tiles_c, nullptr, (int64_t)0, nullptr, (int64_t)0, nullptr, 0u);
     return hipGetLastError();
 }
 

@@ -52,6 +52,10 @@ hipError_t launch_grouped_gemm(int64_t, int64_t, int64_t, int64_t, const int64_t
 hipError_t launch_moe_dispatch(const void *, int64_t, int64_t, int64_t, const int32_t *, int64_t, int64_t,
                                int64_t *, int32_t *, int32_t *, void *, int64_t, void *, void *ws,
                                hipStream_t) { return hit(ws); }
+hipError_t launch_moe_dispatch_dual_grouped(const void *, int64_t, int64_t, int64_t, const int32_t *, int64_t,
+                                            int64_t, int64_t *, int32_t *, int32_t *, void *, int64_t, void *,
+                                            int64_t *, void *, int64_t, int64_t, void *, void *ws,
+                                            hipStream_t) { return hit(ws); }
 hipError_t moe_noalloc_scratch(void **ptr)
 {
     *ptr = (void *)(uintptr_t)0x5000000000ull;  // a fake device address, never dereferenced
@@ -61,7 +65,7 @@ hipError_t launch_moe_combine(const void *, int64_t, int64_t, int64_t, const int
                               void *, int64_t, hipStream_t) { return hit(); }
 hipError_t launch_quantize_colwise_grouped(const void *, int64_t, int64_t, int64_t, const int64_t *, int64_t,
                                           int64_t *, void *, int64_t, int64_t, void *, hipStream_t, void *,
-                                          int64_t, void *, bool) { return hit(); }
+                                          int64_t, void *, bool, const int32_t *, int64_t) { return hit(); }
 hipError_t launch_grouped_gemm_wgrad(int64_t, int64_t, int64_t, int64_t, const int64_t *, const void *, int64_t,
                                      const void *, const void *, int64_t, const void *, void *, int64_t, int,
                                      void *ws, hipStream_t) { return hit(ws); }

@@ -529,6 +529,50 @@ def test_swiglu_quantize_dual_grouped_validation():
     assert "ld_gu" in mx.mx_last_error()
 
 
+def test_moe_dispatch_dual_grouped_validation():
+    """The dispatch that also writes the per-expert column-wise operand checks
+    mx_moe_dispatch's arguments and the grouped operand's (capacity, alignment,
+    overlap, the 32-bit offset bounds) before any launch."""
+    L = mx.load()
+    f = L.mx_moe_dispatch_dual_grouped
+    T, H, TK, E = 1000, 256, 8, 16
+    need = L.mx_moe_dispatch_workspace_bytes(T, TK, E)
+    cap = L.mx_grouped_k_capacity(T * TK, E)
+    # x, tokens, hidden, ld_x, topk_ids, topk, experts, offsets, src, slot, q, ld_q, s_swz,
+    # pad, qt, ld_qt, k_cap, st_swz, ws, wsb
+    base = dict(x=FAKE, T=T, H=H, ldx=H, ids=FAKE2, TK=TK, E=E, off=FAKE2 + (1 << 20),
+                src=FAKE2 + (2 << 20), slot=FAKE2 + (3 << 20), q=FAKE3, ldq=H, s=FAKE4,
+                pad=FAKE2 + (4 << 20), qt=FAKE3 + (64 << 20), ldqt=cap, kcap=cap, st=FAKE4 + (64 << 20),
+                ws=WS, wsb=need)
+    order = ["x", "T", "H", "ldx", "ids", "TK", "E", "off", "src", "slot", "q", "ldq", "s", "pad", "qt", "ldqt",
+             "kcap", "st", "ws", "wsb"]
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(*[a[k] for k in order], STREAM)
+
+    assert call(T=-1) == mx.MX_ERR_INVALID_ARG
+    assert call(H=96, ldx=96, ldq=96) == mx.MX_ERR_UNSUPPORTED
+    assert call(E=2000) == mx.MX_ERR_UNSUPPORTED
+    assert call(q=0) == mx.MX_ERR_INVALID_ARG
+    assert call(kcap=cap - 256, ldqt=cap) == mx.MX_ERR_INVALID_ARG
+    assert call(kcap=cap + 128, ldqt=cap + 128) == mx.MX_ERR_INVALID_ARG
+    assert call(ldqt=cap - 16) == mx.MX_ERR_INVALID_ARG
+    assert call(qt=0) == mx.MX_ERR_INVALID_ARG
+    assert call(pad=0) == mx.MX_ERR_INVALID_ARG
+    assert call(qt=FAKE3 + (64 << 20) + 8) == mx.MX_ERR_ALIGN
+    assert call(ldqt=cap + 8) == mx.MX_ERR_ALIGN
+    assert call(st=FAKE4 + (64 << 20) + 2) == mx.MX_ERR_ALIGN
+    assert call(pad=FAKE2 + (4 << 20) + 4) == mx.MX_ERR_ALIGN
+    assert call(qt=FAKE3) == mx.MX_ERR_OVERLAP                    # column-wise codes over q
+    assert call(pad=FAKE2 + (1 << 20)) == mx.MX_ERR_OVERLAP       # pad over offsets
+    assert call(ws=FAKE3 + (64 << 20)) == mx.MX_ERR_OVERLAP       # workspace over qt
+    far = 1 << 40  # a fake x far from the other buffers, so only the size rules apply
+    assert call(x=far, ldx=1 << 22) == mx.MX_ERR_UNSUPPORTED
+    assert call(x=far, ldx=1 << 21) == mx.MX_ERR_UNSUPPORTED   # x of 4 GiB: past 32-bit offsets
+    assert "x below 2^31" in mx.mx_last_error()
+
+
 def test_moe_dispatch_noalloc_validation():
     """The variant without a workspace checks its arguments like
     mx_moe_dispatch and refuses routings whose chunk counts would not fit its

@@ -121,6 +121,7 @@ def test_bench_step_matches_oracle(gpu_lib):
     _eq(o["msrc"], src, "dispatch source tokens")
     _eq(o["mslot"], slot, "dispatch slots")
     _row(o["xq"], o["xswz"], bits(I["x_tok"])[src], "dispatched rows")
+    src_rows, M_rows = src, ids.size
     print("MoE backward", flush=True)
     off = I["off"].cpu().numpy()          # the same expert sizes as the routing
     k_cap = I["k_cap"]
@@ -136,7 +137,13 @@ def test_bench_step_matches_oracle(gpu_lib):
     c = np.concatenate([cl, rng.integers(0, 2048, r.size - rl.size)])
     check_sampled_grouped(o["dX_mgu"], r, c, off, odq[0], odq[1], ogu_qt, ogu_st, "MoE gate_up dgrad")
     del odq, ogu_qt, ogu_st
-    ob = _grouped_col(o["mgu_xT"], o["mgu_xTswz"], o["mgu_pad2"], bits(I["a_gu"]), off, k_cap, "X_gu")
+    # gate_up's weight-gradient operand: the dispatched rows, quantized per
+    # expert column-wise by the dispatch itself
+    routed = int(off[-1])
+    xg = np.zeros((M_rows, 2048), np.uint16)
+    xg[:routed] = bits(I["x_tok"])[src_rows[:routed]]
+    ob = _grouped_col(o["mgu_xT"], o["mgu_xTswz"], o["mgu_pad2"], xg, off, k_cap, "X_gu")
+    del xg
     # weight gradient of gate_up: every 256 x 256 tile of every expert
     gs, rs, cs = lattice_wgrad(rng, G, 1536, 2048)
     check_sampled_wgrad(o["dW_mgu"], gs, rs, cs, oa[2], oa[0], oa[1], ob[0], ob[1], "MoE gate_up wgrad")

@@ -65,6 +65,75 @@ def test_dispatch_qwen3_moe_routing(gpu_lib):
         assert torch.equal(a, b)
 
 
+def _check_dispatch_dual_grouped(mx, x_bits, ids, G, what, par=False):
+    """mx_moe_dispatch_dual_grouped: the dispatch outputs byte-equal to
+    mx_moe_dispatch's, and the per-expert column-wise operand byte-equal to
+    mx_quantize_colwise_grouped of the permuted BF16 rows and to the oracle's."""
+    T, H = x_bits.shape
+    xd = bf16_dev(mxsynth.from_bits(x_bits))
+    idd = torch.from_numpy(ids).cuda()
+    out = mx.mx_moe_dispatch_dual_grouped(xd, idd, G)
+    ref = mx.mx_moe_dispatch(xd, idd, G)
+    off, src = out[0], out[1]
+    routed = int(off[-1].item())
+    for a, b, name in zip(out[:5], ref, ("offsets", "src_token", "slot", "q", "s_swz")):
+        if name == "src_token":
+            a, b = a[:routed], b[:routed]
+        elif name == "q":
+            a, b = a[:routed], b[:routed]
+        elif name == "s_swz":
+            n = T * ids.shape[1]
+            a = torch.from_numpy(oracle.scale_unswizzle(a.cpu().numpy(), n, H // 32)[:routed])
+            b = torch.from_numpy(oracle.scale_unswizzle(b.cpu().numpy(), n, H // 32)[:routed])
+        assert torch.equal(a.cpu(), b.cpu()), f"{what}: {name}"
+    pad, qt, st_swz = out[5], out[6], out[7]
+    k_cap = qt.shape[1]
+    rows_total = T * ids.shape[1]
+    # the same operand from the permuted BF16 rows (rows past the routed count
+    # are in no expert)
+    perm = torch.zeros((rows_total, H), dtype=torch.bfloat16, device="cuda")
+    perm[:routed] = xd[src[:routed].long()]
+    cqt, cst, cpad = mx.mx_quantize_colwise_grouped(perm, off, k_cap=k_cap)
+    torch.cuda.synchronize()
+    assert torch.equal(pad, cpad), f"{what}: pad offsets"
+    pend = int(pad[-1].item())
+    KT = k_cap // 256
+    assert torch.equal(qt[:, :pend], cqt[:, :pend]), f"{what}: column-wise codes"
+    assert torch.equal(st_swz.view(-1, KT, 256)[:, :pend // 256], cst.view(-1, KT, 256)[:, :pend // 256]), \
+        f"{what}: column-wise scales"
+    ooff, osrc, _ = oracle.moe_dispatch(ids, G)
+    pb = x_bits[osrc[:routed]]   # the permuted rows of the experts (the oracle takes exactly those)
+    if par:
+        return out
+    oqt, ost, opad = oracle.quantize_colwise_grouped(pb, ooff, k_cap)
+    assert np.array_equal(pad.cpu().numpy(), opad), f"{what}: oracle pad"
+    assert np.array_equal(qt.cpu().numpy()[:, :pend], oqt[:, :pend]), f"{what}: oracle column-wise codes"
+    assert np.array_equal(st_swz.cpu().numpy().reshape(-1, KT, 256)[:, :pend // 256],
+                          oracle.scale_swizzle(ost).reshape(-1, KT, 256)[:, :pend // 256]), \
+        f"{what}: oracle column-wise scales"
+    return out
+
+
+@pytest.mark.parametrize("T,H,k,G,invalid", [(1, 256, 1, 1, 0), (37, 256, 3, 5, 0), (1000, 512, 8, 16, 0),
+                                             (999, 768, 4, 33, 40), (300, 256, 2, 1024, 7)])
+def test_dispatch_dual_grouped_matches_dispatch_and_oracle(gpu_lib, T, H, k, G, invalid):
+    rng = np.random.default_rng(T + H + k + G + 1)
+    x = mxsynth.bits(mxsynth.normal_bf16((T, H), 1.0, T + 2, 0.01, 30.0))
+    ids = _routing(rng, T, k, G, invalid)
+    _check_dispatch_dual_grouped(gpu_lib, x, ids, G, f"dual-grouped dispatch T{T} H{H} k{k} G{G}")
+
+
+def test_dispatch_dual_grouped_qwen3_moe_routing(gpu_lib):
+    """The MoE layer's routing (20480 tokens, top-8 of 128 experts) on the
+    gate_up input width 2048: the 163840 permuted rows quantized both ways,
+    byte-equal to mx_moe_dispatch and to mx_quantize_colwise_grouped of the
+    permuted rows (the latter pinned against the oracle at this size in
+    tests/test_gpu_moe_bwd.py)."""
+    ids, _ = mxsynth.moe_routing()
+    x = mxsynth.bits(mxsynth.normal_bf16((mxsynth.MOE_TOKENS, mxsynth.MOE_HIDDEN), 1.0, 5201))
+    _check_dispatch_dual_grouped(gpu_lib, x, ids, mxsynth.MOE_EXPERTS, "qwen3 routing", par=True)
+
+
 def test_dispatch_feeds_grouped_gemm(gpu_lib):
     """Dispatch -> grouped GEMM (the dispatched operand, scales and offsets used
     as they are) -> combine, against the oracle's dispatch, grouped product and
