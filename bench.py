@@ -191,6 +191,7 @@ def build_workload(mx, torch, mxsynth):
     xh, xi = mxsynth.dense_fwd_activations(device=dev)
     dy, xb = mxsynth.dense_bwd_inputs(device=dev)
     rows_per, a_gu, a_dn, w_gu, w_dn = mxsynth.moe_inputs(device=dev)
+    del a_gu, a_dn  # the MoE pass starts from x_tok and the SwiGLU output instead
     dy_gu, dy_dn = mxsynth.moe_bwd_grads(device=dev)
     off = torch.from_numpy(mxsynth.offsets_from_rows(rows_per)).to(dev)
     ids, rw = mxsynth.moe_routing()
@@ -228,7 +229,7 @@ def build_workload(mx, torch, mxsynth):
     M = int(off[-1].item())
     G = w_gu.shape[0]
     k_cap = mx.mx_grouped_k_capacity(M, G)
-    for name, a, w, dyp in (("mgu", a_gu, w_gu, dy_gu), ("mdn", a_dn, w_dn, dy_dn)):
+    for name, w in (("mgu", w_gu), ("mdn", w_dn)):
         G, N, K = w.shape
         # expert weights, both orientations: [G][N][K] and [G][K][N], scales
         # rearranged per expert, back to back
@@ -278,7 +279,7 @@ def build_workload(mx, torch, mxsynth):
     o["ws"] = torch.empty(max(gemm_ws, mx.mx_moe_dispatch_workspace_bytes(ids.shape[0], ids.shape[1], G),
                               mx.mx_grouped_gemm_wgrad_workspace_bytes()), **u8)
     assert n_assign == M
-    inputs = dict(W=W, xh=xh, xi=xi, dy=dy, x=xb, off=off, a_gu=a_gu, a_dn=a_dn,
+    inputs = dict(W=W, xh=xh, xi=xi, dy=dy, x=xb, off=off,
                   w_gu=w_gu, w_dn=w_dn, dy_gu=dy_gu, dy_dn=dy_dn, M=M, k_cap=k_cap,
                   x_tok=x_tok, ids=ids, rw=rw)
     return inputs, o
@@ -368,8 +369,11 @@ def work_per_step(I):
     row_el = dual_el + I["xh"].numel() + I["xi"].numel()         # + forward activations
     col_el = dual_el + I["x"].numel()                            # + wgrad activation operand
     # per-expert column-wise operands of the MoE weight gradients
-    colg_el = I["a_gu"].numel() + I["a_dn"].numel()
-    colg_gu_el = 0   # both per-expert column-wise operands are quantized in the forward passes
+    # per-expert column-wise operands of the MoE weight gradients: the
+    # dispatched rows (2048 columns) and the SwiGLU output (768), both
+    # quantized in the forward passes from rows they already read
+    colg_el = I["M"] * (2048 + 768)
+    colg_gu_el = 0
     # MoE output gradients: row-wise and per-expert column-wise from one read
     dualg_el = I["dy_gu"].numel() + I["dy_dn"].numel()
     M = I["M"]
