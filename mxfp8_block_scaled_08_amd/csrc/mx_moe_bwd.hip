@@ -151,22 +151,44 @@ __global__ __launch_bounds__(QG_THREADS) void quantize_colwise_grouped_kernel(
             lds_src[tid] = tid < valid ? src[src0 + tid] : -1;
         __syncthreads();
         const __amdgpu_buffer_rsrc_t rg = byte_range(x, x_bytes);
+        // the lane's 16 token numbers in four 16-byte LDS reads (rl0 is a
+        // multiple of 16), so the 16 row loads issue back to back
+        int32_t tk[16];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const int4 w = reinterpret_cast<const int4 *>(lds_src + rl0)[k];
+            tk[4 * k] = w.x;
+            tk[4 * k + 1] = w.y;
+            tk[4 * k + 2] = w.z;
+            tk[4 * k + 3] = w.w;
+        }
 #pragma unroll
         for (int i = 0; i < 16; i++) {
-            const int32_t t = lds_src[rl0 + i];
+            const int32_t t = tk[i];
             const uint32_t off = (active && t >= 0) ? (uint32_t)((int64_t)t * ld_x + c0) * 2u : 0xFFFFFFF0u;
             v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0));
         }
     } else if (LOAD == QG_SWIGLU) {
         // the up half: cols * 2 bytes further along the row (an inactive
-        // lane's offset stays past the range)
-        const uint32_t uoff = (uint32_t)(cols * 2);
+        // lane's offset stays past the range).  Two batches of 8 rows, each
+        // issuing its 16 loads before any arithmetic (the barrier keeps the
+        // scheduler from interleaving them): all 32 at once would not fit
+        // the register budget of two workgroups per CU, and loads issued
+        // row by row between the SwiGLU arithmetic left 2-5 in flight
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const uint4 g = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff + i * vstep, 0, STREAM));
-            const uint4 u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff + i * vstep + uoff, 0, STREAM));
-            v[i] = make_uint4(swiglu_bf16x2(g.x, u.x), swiglu_bf16x2(g.y, u.y), swiglu_bf16x2(g.z, u.z),
-                              swiglu_bf16x2(g.w, u.w));
+        for (int b8 = 0; b8 < 16; b8 += 8) {
+            const uint32_t uoff = (uint32_t)(cols * 2);
+            uint4 g[8], u[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                g[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff + (b8 + i) * vstep, 0, STREAM));
+                u[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, voff + (b8 + i) * vstep + uoff, 0, STREAM));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                v[b8 + i] = make_uint4(swiglu_bf16x2(g[i].x, u[i].x), swiglu_bf16x2(g[i].y, u[i].y),
+                                       swiglu_bf16x2(g[i].z, u[i].z), swiglu_bf16x2(g[i].w, u[i].w));
         }
     } else {
 #pragma unroll

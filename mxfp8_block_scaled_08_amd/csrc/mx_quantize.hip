@@ -301,15 +301,14 @@ __global__ __launch_bounds__(QD_THREADS) void quantize_dual_kernel(DualBatch B)
     const int cg = lane & 7, half = (lane >> 3) & 1, rb = lane >> 4;
     int64_t tr, tc;
     if (tiles_c >= QC_WIDE) {
+        // XCD x (block b on XCD b mod 8) takes the x-th contiguous eighth of
+        // the tiles in row-major order (against the column-wise kernel's
+        // tile-row-fastest groups: 250 -> 244 us on a 12288 x 24576 tensor)
         const int64_t t = (b & 7) * (nb >> 3) + (b >> 3);
         if (t >= tiles_r * tiles_c)
             return;
-        const int64_t per_group = QC_GROUP_R * tiles_c;
-        const int64_t grp = t / per_group, first = grp * QC_GROUP_R;
-        const int64_t gr = min(tiles_r - first, (int64_t)QC_GROUP_R);
-        const int64_t in = t - grp * per_group;
-        tr = first + in % gr;
-        tc = in / gr;
+        tr = t / tiles_c;
+        tc = t - tr * tiles_c;
     } else {
         tr = b / tiles_c;
         tc = b - tr * tiles_c;
